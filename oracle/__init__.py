@@ -1,0 +1,236 @@
+"""CPU oracle for the 2D-Gaussian tile rasterizer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never imports, links or calls it, and it never
+imports the product path.
+
+``liboracle.so`` is built from ``oracle.c`` (plain C, fp64 values, fp32 cutoff
+decision, OpenMP over pixels) by :func:`build`.  The wrappers below only
+marshal numpy arrays; every piece of arithmetic is in ``oracle.c``, whose
+header states the definitions and the pages they come from.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, a library normal density, exact rational arithmetic for the
+fp32 cutoff, numpy's stable sort for the bin order, central finite
+differences, torch's Adam).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+TILE = 16
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-Wno-unused-function", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+    lib.oracle_cutoff_exponent.argtypes = [P, i32, i32, P]
+    lib.oracle_cutoff_exponent.restype = ctypes.c_float
+    lib.oracle_const.argtypes = [i32]
+    lib.oracle_const.restype = ctypes.c_float
+    lib.oracle_footprint.argtypes = [i32, i32, i64, P, P, P, P]
+    lib.oracle_footprint.restype = i64
+    lib.oracle_bin.argtypes = [i32, i32, i64, P, P, P, P, P, P, i64]
+    lib.oracle_bin.restype = i64
+    lib.oracle_box_leaks.argtypes = [i32, i32, i64, P]
+    lib.oracle_box_leaks.restype = i64
+    lib.oracle_cutoff_margin.argtypes = [i32, i32, i64, P]
+    lib.oracle_cutoff_margin.restype = ctypes.c_double
+    lib.oracle_render_sum.argtypes = [i32, i32, i64, P, P, i64, i32, P, P]
+    lib.oracle_render_sum.restype = None
+    lib.oracle_grad_sum.argtypes = [i32, i32, i64, P, P, i32, P, P]
+    lib.oracle_grad_sum.restype = None
+    lib.oracle_render_alpha.argtypes = [i32, i32, i64, P, P, P, P, i64, P, P, P, P, P]
+    lib.oracle_render_alpha.restype = None
+    lib.oracle_grad_alpha.argtypes = [i32, i32, i64, P, P, P, P, P, P, P, P, P]
+    lib.oracle_grad_alpha.restype = None
+    lib.oracle_loss_l2.argtypes = [i64, P, P, P]
+    lib.oracle_loss_l2.restype = ctypes.c_double
+    lib.oracle_adam.argtypes = [i64, i32, P, P, P, P, P, ctypes.c_double, ctypes.c_double,
+                                ctypes.c_double, i32]
+    lib.oracle_adam.restype = None
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def constants() -> dict:
+    """The fp32 constants of the cutoff decision, as the oracle defines them."""
+    lib = _load()
+    return {"scale": lib.oracle_const(0), "e9": lib.oracle_const(1), "logit_max": lib.oracle_const(2)}
+
+
+def cutoff_exponent(param, i: int, j: int):
+    """fp32 exponent e = (a dx)^2 + (b dx + c dy)^2 at pixel (i, j), and (mx, my, a, b, c)."""
+    par = _f64(param).reshape(8)
+    abc = np.zeros(5, np.float32)
+    e = _load().oracle_cutoff_exponent(_p(par), int(i), int(j), _p(abc))
+    return np.float32(e), abc
+
+
+def footprint(W, H, params, logit=None):
+    """Per-Gaussian pixel box [N,4] = (j0, i0, j1, i1) (-1s: none) and tile count [N]."""
+    par = _f64(params).reshape(-1, 8)
+    n = par.shape[0]
+    box = np.zeros((n, 4), np.int32)
+    cnt = np.zeros(n, np.uint32)
+    _load().oracle_footprint(W, H, n, _p(par), _p(_f64(logit)), _p(box), _p(cnt))
+    return box, cnt
+
+
+def bin(W, H, params, logit=None):
+    """Binning by definition: dict(offsets, keys, vals, ranges, M)."""
+    par = _f64(params).reshape(-1, 8)
+    n = par.shape[0]
+    _, cnt = footprint(W, H, par, logit)
+    M = int(cnt.astype(np.int64).sum())
+    tx, ty = -(-W // TILE), -(-H // TILE)
+    offsets = np.zeros(n + 1, np.uint32)
+    keys = np.zeros(max(M, 1), np.uint32)
+    vals = np.zeros(max(M, 1), np.uint32)
+    ranges = np.zeros((tx * ty, 2), np.uint32)
+    got = _load().oracle_bin(W, H, n, _p(par), _p(_f64(logit)), _p(offsets), _p(keys), _p(vals),
+                             _p(ranges), M)
+    assert got == M
+    return {"offsets": offsets, "keys": keys[:M], "vals": vals[:M], "ranges": ranges, "M": M,
+            "counts": cnt}
+
+
+def box_leaks(W, H, params) -> int:
+    par = _f64(params).reshape(-1, 8)
+    return int(_load().oracle_box_leaks(W, H, par.shape[0], _p(par)))
+
+
+def cutoff_margin(W, H, params) -> float:
+    par = _f64(params).reshape(-1, 8)
+    return float(_load().oracle_cutoff_margin(W, H, par.shape[0], _p(par)))
+
+
+def _pix(pixels):
+    if pixels is None:
+        return None
+    return np.ascontiguousarray(pixels, dtype=np.int32).reshape(-1, 2)
+
+
+def render_sum(W, H, params, pixels=None, cutoff=True):
+    """Sum image.  pixels: None (all, returns [3,H,W]) or int [P,2] of (row, col) (returns [3,P]).
+    Returns (image, sabs) with sabs = sum_n |c| w (the error-metric scale)."""
+    par = _f64(params).reshape(-1, 8)
+    pix = _pix(pixels)
+    npix = W * H if pix is None else pix.shape[0]
+    out = np.zeros((3, npix))
+    sabs = np.zeros((3, npix))
+    _load().oracle_render_sum(W, H, par.shape[0], _p(par), _p(pix), npix, int(bool(cutoff)), _p(out),
+                              _p(sabs))
+    if pix is None:
+        return out.reshape(3, H, W), sabs.reshape(3, H, W)
+    return out, sabs
+
+
+def grad_sum(W, H, params, dL_dI, cutoff=True):
+    """(dparams [N,8], abs-sum [N,8]) for L = <dL_dI, I>."""
+    par = _f64(params).reshape(-1, 8)
+    G = _f64(dL_dI).reshape(3, H, W)
+    n = par.shape[0]
+    d = np.zeros((n, 8))
+    a = np.zeros((n, 8))
+    _load().oracle_grad_sum(W, H, n, _p(par), _p(G), int(bool(cutoff)), _p(d), _p(a))
+    return d, a
+
+
+def render_alpha(W, H, params, logit, bg, pixels=None, force_last=None):
+    """Alpha image.  Returns dict(image, t_final, last, ambiguous); shapes [3,H,W]/[H,W] for all
+    pixels or [3,P]/[P] for a pixel list.  last = index of the last Gaussian composited (-1: none)."""
+    par = _f64(params).reshape(-1, 8)
+    lg = _f64(logit).reshape(-1)
+    b = _f64(bg).reshape(3)
+    pix = _pix(pixels)
+    npix = W * H if pix is None else pix.shape[0]
+    fl = None if force_last is None else np.ascontiguousarray(force_last, dtype=np.int64).reshape(npix)
+    out = np.zeros((3, npix))
+    tf = np.zeros(npix)
+    last = np.zeros(npix, np.int64)
+    amb = np.zeros(npix, np.int32)
+    _load().oracle_render_alpha(W, H, par.shape[0], _p(par), _p(lg), _p(b), _p(pix), npix, _p(fl),
+                                _p(out), _p(tf), _p(last), _p(amb))
+    if pix is None:
+        return {"image": out.reshape(3, H, W), "t_final": tf.reshape(H, W),
+                "last": last.reshape(H, W), "ambiguous": amb.reshape(H, W)}
+    return {"image": out, "t_final": tf, "last": last, "ambiguous": amb}
+
+
+def grad_alpha(W, H, params, logit, bg, dL_dI, force_last=None):
+    """(dparams [N,8], dlogit [N], dbg [3], abs-sum [N,9]) for L = <dL_dI, C>."""
+    par = _f64(params).reshape(-1, 8)
+    lg = _f64(logit).reshape(-1)
+    b = _f64(bg).reshape(3)
+    G = _f64(dL_dI).reshape(3, H, W)
+    n = par.shape[0]
+    fl = None if force_last is None else np.ascontiguousarray(force_last, dtype=np.int64).reshape(H * W)
+    d = np.zeros((n, 8))
+    dl = np.zeros(n)
+    dbg = np.zeros(3)
+    a = np.zeros((n, 9))
+    _load().oracle_grad_alpha(W, H, n, _p(par), _p(lg), _p(b), _p(G), _p(fl), _p(d), _p(dl), _p(dbg),
+                              _p(a))
+    return d, dl, dbg, a
+
+
+def loss_l2(image, target):
+    """(L, dL/dI) with L = mean (I - T)^2."""
+    img = _f64(image)
+    tgt = _f64(target)
+    g = np.zeros_like(img)
+    L = _load().oracle_loss_l2(img.size, _p(img), _p(tgt), _p(g))
+    return float(L), g
+
+
+def adam(p, g, m, v, lr, step, beta1=0.9, beta2=0.999, eps=1e-8):
+    """One Adam step in fp64 on [rows, row_len] arrays (updated copies returned)."""
+    p = _f64(p).copy()
+    m = _f64(m).copy()
+    v = _f64(v).copy()
+    g = _f64(g)
+    rows, row_len = p.shape
+    lr = _f64(lr).reshape(row_len)
+    _load().oracle_adam(rows, row_len, _p(p), _p(g), _p(m), _p(v), _p(lr), beta1, beta2, eps, int(step))
+    return p, m, v

@@ -1,0 +1,541 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for tile-based 2D-Gaussian rasterization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP library: every quantity here is written out from its definition.
+ *
+ * What it computes (sources are the pages' text, cited by page title and
+ * section; the pages print no formulas, so each definition below is the
+ * plainest reading that their text supports):
+ *
+ *  - "GaussianImage" (Overview): an image is a set of 2D Gaussians with 8
+ *    parameters each (position, covariance, colour) and it is rendered by
+ *    accumulated summation.  Here params[n] = (mux, muy, l11, l21, l22,
+ *    cr, cg, cb) with the covariance Sigma = L L^T, L = [[l11,0],[l21,l22]]
+ *    (the Cholesky form of the "gaussianimage_cholesky" scripts), and
+ *      I_k(p) = sum_n c_{n,k} exp(-q_n(p)/2),  q = d^T Sigma^-1 d, d = p - mu,
+ *    over the Gaussians whose 3-sigma cutoff admits pixel p.  Pixel (row i,
+ *    col j) samples the point (j+0.5, i+0.5).
+ *  - "Drawing with Gaussians" (Overview, 2D fitting): the variant in which the
+ *    Gaussians are alpha-composited over a trainable background:
+ *      alpha_n = o_n w_n, C = sum_n c_n alpha_n T_n + T_final bg,
+ *      T_1 = 1, T_{n+1} = T_n (1 - alpha_n), in Gaussian index order, stopping
+ *    after the first Gaussian that drives T below 1e-4.
+ *    o_n = sigmoid(min(lambda_n, ln 999)).
+ *  - "FlashImgs" (Commands, train --loss l2): the L2 (mean squared error)
+ *    fitting loss, and the Adam optimiser named by the fvdb page
+ *    (GaussianSplatOptimizer) with textbook defaults.
+ *  - fvdb page (GaussianSplatReconstructionConfig, tile_size): 16x16 tiles;
+ *    (eps_2d): a small pixel pad on the screen-space bounding box.
+ *
+ * The cutoff decision is made in fp32 (the kernel's precision) by the exact
+ * operation sequence stated in cutoff_setup()/cutoff_in(); every value
+ * (weights, images, gradients) is computed in fp64 from the definitions
+ * above, using the 2x2 adjugate for Sigma^-1 and matrix calculus for the
+ * derivatives.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORACLE_TILE 16
+#define LOG2E_D 1.44269504088896340736
+
+/* ------------------------------------------------------------------------ */
+/* fp32 cutoff decision (the one place where floating point decides an      */
+/* integer: whether a pair is summed, and which tiles a Gaussian lands in). */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int ok;            /* 0: culled (non-finite or singular), contributes nothing */
+    float mx, my;      /* mean, fp32 */
+    float a, b, c;     /* rows of L^-1 scaled by sqrt(log2(e)/2): e = (a dx)^2 + (b dx + c dy)^2 */
+    int j0, j1, i0, i1;/* inclusive pixel box of the 3-sigma cutoff (j: column, i: row); empty if j0 > j1 */
+} cutoff32;
+
+/* fp32 constants, each the fp32 value nearest its definition. */
+static float c_scale(void) { return (float)sqrt(0.5 * LOG2E_D); }  /* sqrt(log2(e)/2) */
+static float c_e9(void)    { return (float)(4.5 * LOG2E_D); }      /* 9 * log2(e)/2   */
+static float c_lmax(void)  { return (float)log(999.0); }           /* logit(0.999)    */
+
+static cutoff32 cutoff_setup(const double *pd, const double *logit, int W, int H)
+{
+    cutoff32 s;
+    memset(&s, 0, sizeof s);
+    float p[8];
+    for (int k = 0; k < 8; ++k) {
+        p[k] = (float)pd[k];
+        if (!isfinite(p[k])) return s;
+    }
+    if (logit && !isfinite((float)*logit)) return s;
+    const float l11 = p[2], l21 = p[3], l22 = p[4];
+    if (l11 == 0.0f || l22 == 0.0f) return s;
+    float i11 = 1.0f / l11;      /* built with -ffp-contract=off: each fp32 rounding as written */
+    float i22 = 1.0f / l22;
+    float t = l21 * i11;
+    float k = -(t * i22);
+    if (!isfinite(i11) || !isfinite(i22) || !isfinite(k)) return s;
+    const float S = c_scale();
+    float a = i11 * S, b = k * S, c = i22 * S;
+    s.a = a; s.b = b; s.c = c;
+    s.mx = p[0]; s.my = p[1];
+    /* 3-sigma half-extents of the ellipse q <= 9 plus a 1/256 px pad */
+    float sx = 3.0f * fabsf(l11);
+    float rx = sx + 0.00390625f;
+    float l22sq = l22 * l22;
+    float syy = fmaf(l21, l21, l22sq);
+    float sy = 3.0f * sqrtf(syy);
+    float ry = sy + 0.00390625f;
+    float cx = s.mx - 0.5f, cy = s.my - 0.5f;
+    float fj0 = ceilf(cx - rx), fj1 = floorf(cx + rx);
+    float fi0 = ceilf(cy - ry), fi1 = floorf(cy + ry);
+    fj0 = fmaxf(fj0, 0.0f); fi0 = fmaxf(fi0, 0.0f);
+    fj1 = fminf(fj1, (float)(W - 1)); fi1 = fminf(fi1, (float)(H - 1));
+    s.ok = 1;
+    if (!(fj0 <= fj1) || !(fi0 <= fi1)) { s.j0 = 1; s.j1 = 0; s.i0 = 1; s.i1 = 0; return s; }
+    s.j0 = (int)fj0; s.j1 = (int)fj1; s.i0 = (int)fi0; s.i1 = (int)fi1;
+    return s;
+}
+
+/* The fp32 decision for pixel (i, j): returns 1 iff the pair is summed. */
+static int cutoff_in(const cutoff32 *s, int i, int j)
+{
+    if (!s->ok) return 0;
+    float px = (float)j + 0.5f, py = (float)i + 0.5f;
+    float dx = px - s->mx, dy = py - s->my;
+    float u = s->a * dx;
+    float t = s->b * dx;
+    float v = fmaf(s->c, dy, t);
+    float uu = u * u;
+    float e = fmaf(v, v, uu);
+    return e <= c_e9();
+}
+
+/* Exposed for the pins: the fp32 exponent e at pixel (i, j) and the setup. */
+float oracle_cutoff_exponent(const double *param, int i, int j, float *abc_out /*[5]: mx,my,a,b,c*/)
+{
+    cutoff32 s = cutoff_setup(param, NULL, 1 << 20, 1 << 20);
+    if (abc_out) { abc_out[0] = s.mx; abc_out[1] = s.my; abc_out[2] = s.a; abc_out[3] = s.b; abc_out[4] = s.c; }
+    if (!s.ok) return NAN;
+    float px = (float)j + 0.5f, py = (float)i + 0.5f;
+    float dx = px - s.mx, dy = py - s.my;
+    float u = s.a * dx;
+    float t = s.b * dx;
+    float v = fmaf(s.c, dy, t);
+    float uu = u * u;
+    return fmaf(v, v, uu);
+}
+
+float oracle_const(int which)
+{
+    switch (which) {
+    case 0: return c_scale();
+    case 1: return c_e9();
+    case 2: return c_lmax();
+    default: return NAN;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp64 values                                                              */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    double mx, my, l11, l21, l22, c[3];
+    double sxx, sxy, syy, det;     /* Sigma = L L^T and its determinant */
+    double pxx, pxy, pyy;          /* Sigma^-1 by the adjugate */
+    double o;                      /* opacity (alpha variant) */
+    int clamped;                   /* lambda >= ln 999: o held at its clamp */
+} gauss64;
+
+static gauss64 gauss_setup(const double *p, const double *logit)
+{
+    gauss64 g;
+    g.mx = p[0]; g.my = p[1]; g.l11 = p[2]; g.l21 = p[3]; g.l22 = p[4];
+    g.c[0] = p[5]; g.c[1] = p[6]; g.c[2] = p[7];
+    g.sxx = g.l11 * g.l11;
+    g.sxy = g.l11 * g.l21;
+    g.syy = g.l21 * g.l21 + g.l22 * g.l22;
+    g.det = (g.l11 * g.l22) * (g.l11 * g.l22);   /* det(L L^T) = det(L)^2 */
+    g.pxx = g.syy / g.det;
+    g.pxy = -g.sxy / g.det;
+    g.pyy = g.sxx / g.det;
+    g.o = 1.0; g.clamped = 0;
+    if (logit) {
+        double lam = *logit;
+        double lmax = (double)c_lmax();
+        if (lam >= lmax) { lam = lmax; g.clamped = 1; }
+        g.o = 1.0 / (1.0 + exp(-lam));
+    }
+    return g;
+}
+
+/* q = d^T Sigma^-1 d at the pixel centre */
+static double gauss_q(const gauss64 *g, int i, int j, double *dx_out, double *dy_out)
+{
+    double dx = (j + 0.5) - g->mx, dy = (i + 0.5) - g->my;
+    if (dx_out) *dx_out = dx;
+    if (dy_out) *dy_out = dy;
+    return g->pxx * dx * dx + 2.0 * g->pxy * dx * dy + g->pyy * dy * dy;
+}
+
+/* Derivatives of q w.r.t. (mux, muy, l11, l21, l22), by matrix calculus:
+ *   dq/dmu = -2 Sigma^-1 d,
+ *   dq/dL  = -2 Sigma^-1 d d^T Sigma^-1 L  (lower-triangular entries). */
+static void gauss_dq(const gauss64 *g, double dx, double dy, double dq[5])
+{
+    double zx = g->pxx * dx + g->pxy * dy;   /* z = Sigma^-1 d */
+    double zy = g->pxy * dx + g->pyy * dy;
+    dq[0] = -2.0 * zx;
+    dq[1] = -2.0 * zy;
+    /* (z z^T L)_{r,c} = z_r * (z^T L)_c ; (z^T L) = (zx l11 + zy l21, zy l22) */
+    double zl0 = zx * g->l11 + zy * g->l21;
+    double zl1 = zy * g->l22;
+    dq[2] = -2.0 * zx * zl0;   /* entry (0,0): l11 */
+    dq[3] = -2.0 * zy * zl0;   /* entry (1,0): l21 */
+    dq[4] = -2.0 * zy * zl1;   /* entry (1,1): l22 */
+}
+
+/* ------------------------------------------------------------------------ */
+/* Binning by definition                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Per-Gaussian inclusive pixel box (j0,i0,j1,i1; -1s when culled or empty)
+ * and tile count.  Returns the number of culled Gaussians. */
+int64_t oracle_footprint(int W, int H, int64_t n, const double *params, const double *logit,
+                         int32_t *pix_box, uint32_t *counts)
+{
+    int64_t culled = 0;
+    for (int64_t g = 0; g < n; ++g) {
+        cutoff32 s = cutoff_setup(params + 8 * g, logit ? logit + g : NULL, W, H);
+        if (!s.ok) ++culled;
+        if (!s.ok || s.j0 > s.j1 || s.i0 > s.i1) {
+            if (pix_box) { pix_box[4*g+0] = -1; pix_box[4*g+1] = -1; pix_box[4*g+2] = -1; pix_box[4*g+3] = -1; }
+            counts[g] = 0;
+            continue;
+        }
+        if (pix_box) { pix_box[4*g+0] = s.j0; pix_box[4*g+1] = s.i0; pix_box[4*g+2] = s.j1; pix_box[4*g+3] = s.i1; }
+        int tx0 = s.j0 / ORACLE_TILE, tx1 = s.j1 / ORACLE_TILE;
+        int ty0 = s.i0 / ORACLE_TILE, ty1 = s.i1 / ORACLE_TILE;
+        counts[g] = (uint32_t)((tx1 - tx0 + 1) * (ty1 - ty0 + 1));
+    }
+    return culled;
+}
+
+/* Tile lists by definition: tile t's list is every Gaussian whose tile box
+ * holds t, in ascending index order; the lists are concatenated in tile order.
+ * offsets[n] = instances emitted by Gaussians before n (offsets[N] = M).
+ * Returns M, or -(M) - 1 when M exceeds cap (nothing written to keys/vals). */
+int64_t oracle_bin(int W, int H, int64_t n, const double *params, const double *logit,
+                   uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, int64_t cap)
+{
+    const int tx = (W + ORACLE_TILE - 1) / ORACLE_TILE, ty = (H + ORACLE_TILE - 1) / ORACLE_TILE;
+    const int64_t T = (int64_t)tx * ty;
+    int32_t *box = (int32_t *)malloc(sizeof(int32_t) * 4 * (n > 0 ? n : 1));
+    uint32_t *cnt = (uint32_t *)malloc(sizeof(uint32_t) * (n > 0 ? n : 1));
+    oracle_footprint(W, H, n, params, logit, box, cnt);
+    int64_t M = 0;
+    for (int64_t g = 0; g < n; ++g) { offsets[g] = (uint32_t)M; M += cnt[g]; }
+    offsets[n] = (uint32_t)M;
+    if (M > cap) { free(box); free(cnt); return -M - 1; }
+    int64_t pos = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        int ttx = (int)(t % tx), tty = (int)(t / tx);
+        ranges[2*t] = (uint32_t)pos;
+        for (int64_t g = 0; g < n; ++g) {
+            if (cnt[g] == 0) continue;
+            int tx0 = box[4*g+0] / ORACLE_TILE, ty0 = box[4*g+1] / ORACLE_TILE;
+            int tx1 = box[4*g+2] / ORACLE_TILE, ty1 = box[4*g+3] / ORACLE_TILE;
+            if (ttx >= tx0 && ttx <= tx1 && tty >= ty0 && tty <= ty1) {
+                keys[pos] = (uint32_t)t; vals[pos] = (uint32_t)g; ++pos;
+            }
+        }
+        ranges[2*t+1] = (uint32_t)pos;
+        if (ranges[2*t] == ranges[2*t+1]) { ranges[2*t] = 0; ranges[2*t+1] = 0; }
+    }
+    free(box); free(cnt);
+    return M;
+}
+
+/* Counts pairs whose fp32 cutoff admits the pixel although the pixel lies
+ * outside the Gaussian's pixel box (a non-conservative box).  Brute force. */
+int64_t oracle_box_leaks(int W, int H, int64_t n, const double *params)
+{
+    int64_t leaks = 0;
+    #pragma omp parallel for reduction(+:leaks) schedule(dynamic, 64)
+    for (int64_t g = 0; g < n; ++g) {
+        cutoff32 s = cutoff_setup(params + 8 * g, NULL, W, H);
+        if (!s.ok) continue;
+        for (int i = 0; i < H; ++i)
+            for (int j = 0; j < W; ++j)
+                if (cutoff_in(&s, i, j) && !(j >= s.j0 && j <= s.j1 && i >= s.i0 && i <= s.i1)) ++leaks;
+    }
+    return leaks;
+}
+
+/* Smallest |e - E9| over all pairs (how far every decision is from flipping). */
+double oracle_cutoff_margin(int W, int H, int64_t n, const double *params)
+{
+    double m = INFINITY;
+    const double e9 = (double)c_e9();
+    for (int64_t g = 0; g < n; ++g) {
+        cutoff32 s = cutoff_setup(params + 8 * g, NULL, W, H);
+        if (!s.ok) continue;
+        for (int i = 0; i < H; ++i)
+            for (int j = 0; j < W; ++j) {
+                float e = oracle_cutoff_exponent(params + 8 * g, i, j, NULL);
+                double d = fabs((double)e - e9);
+                if (d < m) m = d;
+            }
+    }
+    return m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Renders                                                                  */
+/* ------------------------------------------------------------------------ */
+
+static void pixel_of(const int32_t *pix, int64_t p, int W, int *i, int *j)
+{
+    if (pix) { *i = pix[2*p]; *j = pix[2*p+1]; }
+    else { *i = (int)(p / W); *j = (int)(p % W); }
+}
+
+/* Accumulated-sum image at npix pixels (pix = NULL: every pixel, row-major).
+ * out[k*npix + p] = I_k(p); sabs[k*npix + p] = sum_n |c_{n,k}| w_n(p).
+ * cutoff = 0 sums every Gaussian at every pixel (test-only: no 3-sigma cut). */
+void oracle_render_sum(int W, int H, int64_t n, const double *params, const int32_t *pix, int64_t npix,
+                       int cutoff, double *out, double *sabs)
+{
+    cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
+    gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
+    for (int64_t g = 0; g < n; ++g) { cs[g] = cutoff_setup(params + 8*g, NULL, W, H); gs[g] = gauss_setup(params + 8*g, NULL); }
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npix; ++p) {
+        int i, j; pixel_of(pix, p, W, &i, &j);
+        double acc[3] = {0, 0, 0}, aab[3] = {0, 0, 0};
+        for (int64_t g = 0; g < n; ++g) {
+            if (!cs[g].ok) continue;
+            if (cutoff && !cutoff_in(&cs[g], i, j)) continue;
+            double w = exp(-0.5 * gauss_q(&gs[g], i, j, NULL, NULL));
+            for (int k = 0; k < 3; ++k) { acc[k] += gs[g].c[k] * w; aab[k] += fabs(gs[g].c[k]) * w; }
+        }
+        for (int k = 0; k < 3; ++k) { out[k*npix + p] = acc[k]; if (sabs) sabs[k*npix + p] = aab[k]; }
+    }
+    free(cs); free(gs);
+}
+
+/* Gradient of L = sum_{k,p} G_k(p) I_k(p) for the sum image (G = dL/dI at
+ * every pixel, [3,H,W]).  dparams[n,8] and, if given, the per-entry sum of
+ * |per-pair contribution| aabs[n,8]. */
+void oracle_grad_sum(int W, int H, int64_t n, const double *params, const double *G, int cutoff,
+                     double *dparams, double *aabs)
+{
+    const int nt = omp_get_max_threads();
+    cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
+    gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
+    for (int64_t g = 0; g < n; ++g) { cs[g] = cutoff_setup(params + 8*g, NULL, W, H); gs[g] = gauss_setup(params + 8*g, NULL); }
+    double *part = (double *)calloc((size_t)nt * 16 * (n > 0 ? n : 1), sizeof(double));
+    const int64_t HW = (int64_t)H * W;
+    #pragma omp parallel
+    {
+        double *mine = part + (size_t)omp_get_thread_num() * 16 * (n > 0 ? n : 1);
+        #pragma omp for schedule(dynamic, 4)
+        for (int i = 0; i < H; ++i)
+            for (int j = 0; j < W; ++j) {
+                const double gk[3] = {G[(int64_t)i*W + j], G[HW + (int64_t)i*W + j], G[2*HW + (int64_t)i*W + j]};
+                for (int64_t g = 0; g < n; ++g) {
+                    if (!cs[g].ok) continue;
+                    if (cutoff && !cutoff_in(&cs[g], i, j)) continue;
+                    double dx, dy;
+                    double q = gauss_q(&gs[g], i, j, &dx, &dy);
+                    double w = exp(-0.5 * q);
+                    double gc = gk[0]*gs[g].c[0] + gk[1]*gs[g].c[1] + gk[2]*gs[g].c[2];
+                    double dq[5];
+                    gauss_dq(&gs[g], dx, dy, dq);
+                    double contrib[8];
+                    for (int t = 0; t < 5; ++t) contrib[t] = gc * w * (-0.5) * dq[t];
+                    for (int k = 0; k < 3; ++k) contrib[5+k] = gk[k] * w;
+                    for (int t = 0; t < 8; ++t) { mine[16*g + t] += contrib[t]; mine[16*g + 8 + t] += fabs(contrib[t]); }
+                }
+            }
+    }
+    for (int64_t g = 0; g < n; ++g)
+        for (int t = 0; t < 8; ++t) {
+            double s = 0, a = 0;
+            for (int th = 0; th < nt; ++th) { s += part[(size_t)th*16*n + 16*g + t]; a += part[(size_t)th*16*n + 16*g + 8 + t]; }
+            dparams[8*g + t] = s;
+            if (aabs) aabs[8*g + t] = a;
+        }
+    free(part); free(cs); free(gs);
+}
+
+/* Alpha-composited image.  For each pixel the Gaussians are visited in index
+ * order; a Gaussian whose cutoff admits the pixel has alpha = o w and adds
+ * c alpha T; then T <- T (1 - alpha); after the first Gaussian that leaves
+ * T < 1e-4 the pixel stops.  C += T bg.
+ *  out[3,npix], t_final[npix], last[npix] = index of the last Gaussian
+ *  composited (-1 if none), ambiguous[npix] = 1 when some transmittance met
+ *  by the stop test lies within 1e-3 (relative) of 1e-4, so fp32 rounding may
+ *  move the stop by one Gaussian.  force_last (may be NULL): per pixel,
+ *  stop after this Gaussian index instead of testing T (>= n: never stop,
+ *  -1: composite nothing). */
+void oracle_render_alpha(int W, int H, int64_t n, const double *params, const double *logit, const double *bg,
+                         const int32_t *pix, int64_t npix, const int64_t *force_last,
+                         double *out, double *t_final, int64_t *last, int32_t *ambiguous)
+{
+    cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
+    gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
+    for (int64_t g = 0; g < n; ++g) { cs[g] = cutoff_setup(params + 8*g, logit + g, W, H); gs[g] = gauss_setup(params + 8*g, logit + g); }
+    const double thr = 1e-4, band = 1e-3;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npix; ++p) {
+        int i, j; pixel_of(pix, p, W, &i, &j);
+        double C[3] = {0, 0, 0}, T = 1.0;
+        int64_t lst = -1; int amb = 0;
+        int64_t fl = force_last ? force_last[p] : 0;
+        if (!(force_last && fl < 0)) {
+            for (int64_t g = 0; g < n; ++g) {
+                if (!cs[g].ok || !cutoff_in(&cs[g], i, j)) continue;
+                double w = exp(-0.5 * gauss_q(&gs[g], i, j, NULL, NULL));
+                double al = gs[g].o * w;
+                for (int k = 0; k < 3; ++k) C[k] += gs[g].c[k] * al * T;
+                T *= (1.0 - al);
+                lst = g;
+                if (force_last) { if (g >= fl) break; continue; }
+                if (fabs(T - thr) <= band * thr) amb = 1;
+                if (T < thr) break;
+            }
+        }
+        for (int k = 0; k < 3; ++k) out[k*npix + p] = C[k] + T * bg[k];
+        if (t_final) t_final[p] = T;
+        if (last) last[p] = lst;
+        if (ambiguous) ambiguous[p] = amb;
+    }
+    free(cs); free(gs);
+}
+
+/* Gradient of L = sum G_k(p) C_k(p) for the alpha image at every pixel, with
+ * each pixel's stopping point held fixed (force_last as above, or the oracle's
+ * own stop when NULL).  dparams[n,8], dlogit[n], dbg[3]; aabs[n,9] (8 params +
+ * logit) is the per-entry sum of |per-pair contribution|.  The suffix sums are
+ * formed directly from the stored contributors (no division). */
+void oracle_grad_alpha(int W, int H, int64_t n, const double *params, const double *logit, const double *bg,
+                       const double *G, const int64_t *force_last,
+                       double *dparams, double *dlogit, double *dbg, double *aabs)
+{
+    const int nt = omp_get_max_threads();
+    cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
+    gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
+    for (int64_t g = 0; g < n; ++g) { cs[g] = cutoff_setup(params + 8*g, logit + g, W, H); gs[g] = gauss_setup(params + 8*g, logit + g); }
+    const size_t stride = 20;   /* 9 sums + 9 abs sums + pad */
+    double *part = (double *)calloc((size_t)nt * stride * (n > 0 ? n : 1), sizeof(double));
+    double *pbg = (double *)calloc((size_t)nt * 3, sizeof(double));
+    const int64_t HW = (int64_t)H * W;
+    const double thr = 1e-4;
+    #pragma omp parallel
+    {
+        const int th = omp_get_thread_num();
+        double *mine = part + (size_t)th * stride * (n > 0 ? n : 1);
+        int64_t cap = 64;
+        int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * cap);
+        double *wv = (double *)malloc(sizeof(double) * cap);
+        double *Tv = (double *)malloc(sizeof(double) * cap);
+        #pragma omp for schedule(dynamic, 4)
+        for (int64_t p = 0; p < HW; ++p) {
+            int i = (int)(p / W), j = (int)(p % W);
+            const double gk[3] = {G[p], G[HW + p], G[2*HW + p]};
+            /* forward: collect contributors */
+            int64_t K = 0; double T = 1.0;
+            int64_t fl = force_last ? force_last[p] : 0;
+            if (!(force_last && fl < 0)) {
+                for (int64_t g = 0; g < n; ++g) {
+                    if (!cs[g].ok || !cutoff_in(&cs[g], i, j)) continue;
+                    double w = exp(-0.5 * gauss_q(&gs[g], i, j, NULL, NULL));
+                    if (K == cap) {
+                        cap *= 2;
+                        idx = (int64_t *)realloc(idx, sizeof(int64_t) * cap);
+                        wv = (double *)realloc(wv, sizeof(double) * cap);
+                        Tv = (double *)realloc(Tv, sizeof(double) * cap);
+                    }
+                    idx[K] = g; wv[K] = w; Tv[K] = T; ++K;
+                    T *= (1.0 - gs[g].o * w);
+                    if (force_last) { if (g >= fl) break; continue; }
+                    if (T < thr) break;
+                }
+            }
+            /* dC/dbg = T_final */
+            for (int k = 0; k < 3; ++k) pbg[3*th + k] += gk[k] * T;
+            /* backward: S_m = sum_{r>m} c_r alpha_r T_r + T_final bg, per channel */
+            double S[3] = {T * bg[0], T * bg[1], T * bg[2]};
+            for (int64_t m = K - 1; m >= 0; --m) {
+                const gauss64 *gg = &gs[idx[m]];
+                double w = wv[m], Tm = Tv[m], al = gg->o * w;
+                double dC_dal = 0.0;   /* sum_k G_k dC_k/dalpha */
+                for (int k = 0; k < 3; ++k) dC_dal += gk[k] * (Tm * gg->c[k] - S[k] / (1.0 - al));
+                double contrib[9];
+                double dx, dy;
+                gauss_q(gg, i, j, &dx, &dy);
+                double dq[5];
+                gauss_dq(gg, dx, dy, dq);
+                /* alpha = o w, w = exp(-q/2) */
+                for (int t = 0; t < 5; ++t) contrib[t] = dC_dal * gg->o * w * (-0.5) * dq[t];
+                for (int k = 0; k < 3; ++k) contrib[5+k] = gk[k] * al * Tm;
+                contrib[8] = gg->clamped ? 0.0 : dC_dal * w * gg->o * (1.0 - gg->o);
+                double *dst = mine + stride * idx[m];
+                for (int t = 0; t < 9; ++t) { dst[t] += contrib[t]; dst[9 + t] += fabs(contrib[t]); }
+                for (int k = 0; k < 3; ++k) S[k] += gg->c[k] * al * Tm;
+            }
+        }
+        free(idx); free(wv); free(Tv);
+    }
+    for (int64_t g = 0; g < n; ++g) {
+        for (int t = 0; t < 9; ++t) {
+            double s = 0, a = 0;
+            for (int th = 0; th < nt; ++th) { s += part[(size_t)th*stride*n + stride*g + t]; a += part[(size_t)th*stride*n + stride*g + 9 + t]; }
+            if (t < 8) dparams[8*g + t] = s; else dlogit[g] = s;
+            if (aabs) aabs[9*g + t] = a;
+        }
+    }
+    for (int k = 0; k < 3; ++k) { double s = 0; for (int th = 0; th < nt; ++th) s += pbg[3*th + k]; dbg[k] = s; }
+    free(part); free(pbg); free(cs); free(gs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Loss and optimiser                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* L = mean (I - T)^2 over all m entries; grad (may be NULL) = dL/dI. */
+double oracle_loss_l2(int64_t m, const double *img, const double *tgt, double *grad)
+{
+    double s = 0.0;
+    for (int64_t e = 0; e < m; ++e) {
+        double d = img[e] - tgt[e];
+        s += d * d;
+        if (grad) grad[e] = 2.0 * d / (double)m;
+    }
+    return m > 0 ? s / (double)m : 0.0;
+}
+
+/* One Adam step (bias-corrected, no weight decay) on rows x row_len entries,
+ * lr per slot of the row; step t >= 1. */
+void oracle_adam(int64_t rows, int row_len, double *p, const double *g, double *m, double *v,
+                 const double *lr, double b1, double b2, double eps, int step)
+{
+    const double bc1 = 1.0 - pow(b1, step), bc2 = 1.0 - pow(b2, step);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int s = 0; s < row_len; ++s) {
+            int64_t e = r * row_len + s;
+            m[e] = b1 * m[e] + (1.0 - b1) * g[e];
+            v[e] = b2 * v[e] + (1.0 - b2) * g[e] * g[e];
+            double mh = m[e] / bc1, vh = v[e] / bc2;
+            p[e] -= lr[s] * mh / (sqrt(vh) + eps);
+        }
+}
+
+int oracle_threads(void) { return omp_get_max_threads(); }
