@@ -66,7 +66,7 @@ def _load():
     lib.oracle_render_sum.restype = None
     lib.oracle_grad_sum.argtypes = [i32, i32, i64, P, P, i32, P, P]
     lib.oracle_grad_sum.restype = None
-    lib.oracle_render_alpha.argtypes = [i32, i32, i64, P, P, P, P, i64, P, P, P, P, P]
+    lib.oracle_render_alpha.argtypes = [i32, i32, i64, P, P, P, P, i64, P, P, P, P, P, P]
     lib.oracle_render_alpha.restype = None
     lib.oracle_grad_alpha.argtypes = [i32, i32, i64, P, P, P, P, P, P, P, P, P]
     lib.oracle_grad_alpha.restype = None
@@ -178,8 +178,9 @@ def grad_sum(W, H, params, dL_dI, cutoff=True):
 
 
 def render_alpha(W, H, params, logit, bg, pixels=None, force_last=None):
-    """Alpha image.  Returns dict(image, t_final, last, ambiguous); shapes [3,H,W]/[H,W] for all
-    pixels or [3,P]/[P] for a pixel list.  last = index of the last Gaussian composited (-1: none)."""
+    """Alpha image.  Returns dict(image, sabs, t_final, last, ambiguous); shapes [3,H,W]/[H,W] for
+    all pixels or [3,P]/[P] for a pixel list.  last = index of the last Gaussian composited (-1:
+    none); sabs = sum |c| alpha T + T |bg| (error-metric scale)."""
     par = _f64(params).reshape(-1, 8)
     lg = _f64(logit).reshape(-1)
     b = _f64(bg).reshape(3)
@@ -190,12 +191,13 @@ def render_alpha(W, H, params, logit, bg, pixels=None, force_last=None):
     tf = np.zeros(npix)
     last = np.zeros(npix, np.int64)
     amb = np.zeros(npix, np.int32)
+    sabs = np.zeros((3, npix))
     _load().oracle_render_alpha(W, H, par.shape[0], _p(par), _p(lg), _p(b), _p(pix), npix, _p(fl),
-                                _p(out), _p(tf), _p(last), _p(amb))
+                                _p(out), _p(tf), _p(last), _p(amb), _p(sabs))
     if pix is None:
-        return {"image": out.reshape(3, H, W), "t_final": tf.reshape(H, W),
+        return {"image": out.reshape(3, H, W), "sabs": sabs.reshape(3, H, W), "t_final": tf.reshape(H, W),
                 "last": last.reshape(H, W), "ambiguous": amb.reshape(H, W)}
-    return {"image": out, "t_final": tf, "last": last, "ambiguous": amb}
+    return {"image": out, "sabs": sabs, "t_final": tf, "last": last, "ambiguous": amb}
 
 
 def grad_alpha(W, H, params, logit, bg, dL_dI, force_last=None):

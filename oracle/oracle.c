@@ -349,6 +349,7 @@ void oracle_grad_sum(int W, int H, int64_t n, const double *params, const double
         for (int i = 0; i < H; ++i)
             for (int j = 0; j < W; ++j) {
                 const double gk[3] = {G[(int64_t)i*W + j], G[HW + (int64_t)i*W + j], G[2*HW + (int64_t)i*W + j]};
+                if (gk[0] == 0.0 && gk[1] == 0.0 && gk[2] == 0.0) continue;   /* contributes exactly 0 */
                 for (int64_t g = 0; g < n; ++g) {
                     if (!cs[g].ok) continue;
                     if (cutoff && !cutoff_in(&cs[g], i, j)) continue;
@@ -384,10 +385,11 @@ void oracle_grad_sum(int W, int H, int64_t n, const double *params, const double
  *  by the stop test lies within 1e-3 (relative) of 1e-4, so fp32 rounding may
  *  move the stop by one Gaussian.  force_last (may be NULL): per pixel,
  *  stop after this Gaussian index instead of testing T (>= n: never stop,
- *  -1: composite nothing). */
+ *  -1: composite nothing).  sabs (may be NULL): per channel
+ *  sum_n |c_n| alpha_n T_n + T |bg|, the scale of the error metric. */
 void oracle_render_alpha(int W, int H, int64_t n, const double *params, const double *logit, const double *bg,
                          const int32_t *pix, int64_t npix, const int64_t *force_last,
-                         double *out, double *t_final, int64_t *last, int32_t *ambiguous)
+                         double *out, double *t_final, int64_t *last, int32_t *ambiguous, double *sabs)
 {
     cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
     gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
@@ -396,7 +398,7 @@ void oracle_render_alpha(int W, int H, int64_t n, const double *params, const do
     #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t p = 0; p < npix; ++p) {
         int i, j; pixel_of(pix, p, W, &i, &j);
-        double C[3] = {0, 0, 0}, T = 1.0;
+        double C[3] = {0, 0, 0}, A[3] = {0, 0, 0}, T = 1.0;
         int64_t lst = -1; int amb = 0;
         int64_t fl = force_last ? force_last[p] : 0;
         if (!(force_last && fl < 0)) {
@@ -404,7 +406,7 @@ void oracle_render_alpha(int W, int H, int64_t n, const double *params, const do
                 if (!cs[g].ok || !cutoff_in(&cs[g], i, j)) continue;
                 double w = exp(-0.5 * gauss_q(&gs[g], i, j, NULL, NULL));
                 double al = gs[g].o * w;
-                for (int k = 0; k < 3; ++k) C[k] += gs[g].c[k] * al * T;
+                for (int k = 0; k < 3; ++k) { C[k] += gs[g].c[k] * al * T; A[k] += fabs(gs[g].c[k]) * al * T; }
                 T *= (1.0 - al);
                 lst = g;
                 if (force_last) { if (g >= fl) break; continue; }
@@ -412,7 +414,10 @@ void oracle_render_alpha(int W, int H, int64_t n, const double *params, const do
                 if (T < thr) break;
             }
         }
-        for (int k = 0; k < 3; ++k) out[k*npix + p] = C[k] + T * bg[k];
+        for (int k = 0; k < 3; ++k) {
+            out[k*npix + p] = C[k] + T * bg[k];
+            if (sabs) sabs[k*npix + p] = A[k] + T * fabs(bg[k]);
+        }
         if (t_final) t_final[p] = T;
         if (last) last[p] = lst;
         if (ambiguous) ambiguous[p] = amb;
@@ -450,6 +455,7 @@ void oracle_grad_alpha(int W, int H, int64_t n, const double *params, const doub
         for (int64_t p = 0; p < HW; ++p) {
             int i = (int)(p / W), j = (int)(p % W);
             const double gk[3] = {G[p], G[HW + p], G[2*HW + p]};
+            if (gk[0] == 0.0 && gk[1] == 0.0 && gk[2] == 0.0) continue;   /* contributes exactly 0 */
             /* forward: collect contributors */
             int64_t K = 0; double T = 1.0;
             int64_t fl = force_last ? force_last[p] : 0;

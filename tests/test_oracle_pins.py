@@ -310,6 +310,8 @@ def test_alpha_one_and_two_gaussians(orc):
         ref = a1 * p[0, 5 + k] + (1 - a1) * a2 * p[1, 5 + k] + (1 - a1) * (1 - a2) * bg[k]
         np.testing.assert_allclose(r2["image"][k], ref, rtol=1e-12)
     np.testing.assert_allclose(r2["t_final"], (1 - a1) * (1 - a2), rtol=1e-12)
+    # with non-negative colours and background the error-metric scale is the image itself
+    np.testing.assert_allclose(r2["sabs"], r2["image"], rtol=1e-14)
     # order matters where both overlap
     r3 = orc.render_alpha(W, H, p[::-1], lg[::-1], bg)
     both = in1 & in2
