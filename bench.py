@@ -1,0 +1,274 @@
+"""Benchmark: 768x512 synthetic target, 50,000 2D Gaussians, accumulated-sum rendering.
+
+One "step" is the whole hot path on the GPU: gi_preprocess -> gi_bin_sort -> gi_render_fwd ->
+gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared).  `value` is fwd+bwd training
+steps per second on one MI355X with every input resident in HBM.  Also reported: render FPS
+(preprocess + bin/sort + raster), cached-raster FPS (raster only, binning reused), per-kernel
+times from HIP events on the launch stream, the roofline of the dominant kernel, and the CPU
+oracle timed on a bounded pixel sample of the same workload.
+
+usage: python bench.py [--gpus 1] [--steps 2800] [--warmup 50] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "render FPS + fwd+bwd steps/s, 768×512 × 50K 2D Gaussians; % FP32 VALU peak"
+PEAK_FP32 = 157.3          # TFLOP/s, MI355X FP32 vector (AMD published)
+PEAK_HBM = 8000.0          # GB/s
+FLOP_FWD = 17              # per binned pair: dx, dy 2; cutoff exponent 7; scale + exp2 2; 3 colour FMA 6
+FLOP_BWD = 32              # per binned pair (recompute 11, colour/h 9, mean/conic partials 11, reduce 1)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def binned_pairs(W, H, ranges):
+    """sum over tiles of (list length) x (in-image pixels of the tile)."""
+    tx = -(-W // 16)
+    T = ranges.shape[0]
+    t = np.arange(T)
+    x0, y0 = (t % tx) * 16, (t // tx) * 16
+    npx = np.minimum(16, W - x0) * np.minimum(16, H - y0)
+    ln = ranges[:, 1].astype(np.int64) - ranges[:, 0].astype(np.int64)
+    return int((ln * npx).sum())
+
+
+def evaluated_pairs(W, H, keys, vals, pixbox):
+    """Pairs the forward kernel evaluates: 64 per (list entry, 8x8 quadrant its box overlaps)."""
+    tx = -(-W // 16)
+    k = keys.astype(np.int64)
+    b = pixbox[vals.astype(np.int64)].astype(np.int64)
+    x0, y0 = (k % tx) * 16, (k // tx) * 16
+    tot = 0
+    for q in range(4):
+        qx, qy = x0 + (q & 1) * 8, y0 + (q >> 1) * 8
+        ov = (b[:, 0] <= qx + 7) & (b[:, 2] >= qx) & (b[:, 1] <= qy + 7) & (b[:, 3] >= qy)
+        tot += int(ov.sum())
+    return tot * 64
+
+
+def kernel_source_hash(name):
+    src = os.path.join(ROOT, "rasterizer_gaussian_raster_amd", "csrc", name)
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file, kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        e = d.get(kernel_name)
+        if e and e.get("source_sha256_16") == kernel_source_hash(kernel_file):
+            return float(e["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+    return None
+
+
+def cpu_baseline(wl, params, target_seconds=12.0):
+    """The oracle (brute force over all N Gaussians per pixel, fp64) on a bounded pixel sample:
+    sum render + analytic gradient of the same pixels, extrapolated to one full-frame step."""
+    import oracle
+    W, H = wl.width, wl.height
+    p64 = params.astype(np.float64)
+    rng = np.random.default_rng(12345)
+
+    def run(npix):
+        idx = rng.choice(W * H, size=npix, replace=False)
+        pix = np.stack([idx // W, idx % W], 1).astype(np.int32)
+        G = np.zeros((3, H, W))
+        G[:, pix[:, 0], pix[:, 1]] = rng.normal(size=(3, npix))
+        t0 = time.perf_counter()
+        oracle.render_sum(W, H, p64, pixels=pix)
+        oracle.grad_sum(W, H, p64, G)
+        return time.perf_counter() - t0
+
+    run(64)                                    # load + warm
+    probe = 256
+    tp = run(probe)
+    npix = int(min(W * H, max(probe, probe * target_seconds / max(tp, 1e-6))))
+    t = run(npix)
+    per_frame = t * (W * H) / npix
+    return {"value": 1.0 / per_frame, "unit": "fwd+bwd steps/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{npix} random pixels of the {W}x{H} frame, all {params.shape[0]} Gaussians per pixel "
+                      f"(render + gradient), {t:.1f} s, extrapolated linearly to the full frame",
+            "seconds": round(t, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2800)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="kodak_768x512_50k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rasterizer_gaussian_raster_amd import gi, synth
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter, Raster
+
+    gi.load()
+    wlname = args.workload
+    w = synth.make_workload(wlname)
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    dev = torch.device("cuda:0")
+    target = torch.from_numpy(w["target"]).to(dev)
+    params = torch.from_numpy(w["params"]).to(dev)
+    if wl.mode != "sum":
+        raise SystemExit("bench.py times the accumulated-sum workloads")
+    log(f"[bench] {wlname}: {W}x{H}, N={wl.n}, steps={args.steps}, warmup={args.warmup}")
+
+    if args.copy_calibration:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 256 MiB device-to-device copies")
+
+    # ---------------- training step (the whole hot path) ----------------
+    fit = Fitter(target, params, capacity_slack=2.0)
+    r = fit.raster
+    for _ in range(args.warmup):
+        fit.step()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        # events bracket the raster kernels on the stream they are launched on
+        rr = fit.raster
+        rr.preprocess(fit.params)
+        rr.bin(sync=False)
+        ev[k][0].record()
+        rr.forward()
+        ev[k][1].record()
+        gi.gi_loss_l2(fit.target.numel(), rr.image, fit.target, fit.dL, fit.loss, fit.loss_ws)
+        ev[k][2].record()
+        rr.backward(fit.dL, fit.grad)
+        ev[k][3].record()
+        fit.step_count += 1
+        gi.gi_adam_step(fit.n, 8, fit.params, fit.grad, fit.m, fit.v, fit.lr, fit.betas[0], fit.betas[1],
+                        fit.eps, fit.step_count, 1)
+    torch.cuda.synchronize()
+    t_train = time.perf_counter() - t0
+    fwd_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)])
+    bwd_ms = np.array([ev[k][2].elapsed_time(ev[k][3]) for k in range(args.steps)])
+    M_now = int(r.d_num.cpu().item()) & 0xFFFFFFFF
+    assert M_now <= r.capacity, "tile-pair capacity exceeded during the timed run"
+    ms_step = 1e3 * t_train / args.steps
+    final_loss = float(fit.loss.item())
+    log(f"[bench] train: {ms_step:.4f} ms/step, fwd {np.median(fwd_ms)*1e3:.1f} us, "
+        f"bwd {np.median(bwd_ms)*1e3:.1f} us, loss {final_loss:.4e}")
+
+    # ---------------- render-only: preprocess + bin/sort + raster ----------------
+    rend = Raster(W, H, wl.n)
+    rend.preprocess(fit.params)
+    M = rend.bin(sync=True)
+    rend.set_capacity(int(M * 1.5) + 4096)
+    reps = max(50, args.steps // 4)
+    for _ in range(10):
+        rend.render(fit.params, sync=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rend.render(fit.params, sync=False)
+    torch.cuda.synchronize()
+    t_render = (time.perf_counter() - t0) / reps
+    # cached raster: binning reused
+    for _ in range(10):
+        rend.forward()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rend.forward()
+    torch.cuda.synchronize()
+    t_cached = (time.perf_counter() - t0) / reps
+    log(f"[bench] render {t_render*1e6:.1f} us ({1/t_render:.0f} FPS), cached raster {t_cached*1e6:.1f} us")
+
+    # ---------------- work counts of the timed problem ----------------
+    rend.preprocess(fit.params)
+    M = rend.bin(sync=True)
+    torch.cuda.synchronize()
+    ranges = rend.ranges.cpu().numpy().view(np.uint32)
+    keys = rend.keys.cpu().numpy().view(np.uint32)[:M]
+    vals = rend.vals.cpu().numpy().view(np.uint32)[:M]
+    pixbox = rend.pixbox.cpu().numpy().view(np.uint16)
+    pairs = binned_pairs(W, H, ranges)
+    evald = evaluated_pairs(W, H, keys, vals, pixbox)
+    fwd_s = float(np.mean(fwd_ms)) * 1e-3
+    bwd_s = float(np.mean(bwd_ms)) * 1e-3
+    fwd_tf = FLOP_FWD * pairs / fwd_s / 1e12
+    bwd_tf = FLOP_BWD * pairs / bwd_s / 1e12
+
+    def roof(name, kfile, kname, tf, secs):
+        traffic = load_traffic(kfile, kname)
+        return {"bound": "alu", "kernel": kname, "achieved": round(tf, 3), "peak": PEAK_FP32,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32, 4),
+                "traffic": traffic, "avg_launch_us": round(secs * 1e6, 2)}
+
+    roof_fwd = roof("fwd", "k_raster_sum.hip", "k_render_sum_fwd", fwd_tf, fwd_s)
+    roof_bwd = roof("bwd", "k_raster_sum.hip", "k_render_sum_bwd", bwd_tf, bwd_s)
+    dominant = roof_bwd if bwd_s >= fwd_s else roof_fwd
+
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "fwd+bwd steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wlname, "width": W, "height": H, "gaussians": wl.n, "mode": "sum",
+                   "tiles": int(rend.T), "tile_pairs": int(M), "binned_pixel_pairs": pairs,
+                   "evaluated_pixel_pairs_fwd": evald},
+        "render_fps": round(1.0 / t_render, 1),
+        "mpix_per_s": round(W * H / t_render / 1e6, 1),
+        "cached_raster_fps": round(1.0 / t_cached, 1),
+        "fit_seconds_2800_steps": round(2800 * ms_step / 1e3, 3),
+        "final_loss": final_loss,
+        "kernels_us": {"render_fwd": round(fwd_s * 1e6, 2), "render_bwd": round(bwd_s * 1e6, 2)},
+        "roofline": dominant,
+        "roofline_fwd": roof_fwd,
+        "roofline_bwd": roof_bwd,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a pixel sample ...")
+        out["cpu_baseline"] = cpu_baseline(wl, w["params"])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * gi.h -- C ABI of libgi.so: tile-based rasterization of 2D Gaussians on
+ * AMD Instinct MI355X (gfx950), forward and backward, with a fused Adam step.
+ *
+ * Method (as the pages state it; they print no formulas, the readings are
+ * given with each call):
+ *   - "GaussianImage" (Overview): an image is represented by 2D Gaussians of
+ *     8 parameters each -- position, covariance, colour -- and rendered by
+ *     accumulated summation.  The covariance is held as a Cholesky factor
+ *     (the "gaussianimage_cholesky" scripts of its quick start).
+ *   - "Drawing with Gaussians" (Overview, 2D fitting): anisotropic 2D
+ *     Gaussians alpha-composited over a trainable background; covariance from
+ *     a lower-triangular L (MLX-specific notes).
+ *   - "FlashImgs" (Commands: train, --loss l2; Python API): image fitting with
+ *     an L2 loss, rendering and training kernels behind tensor-level calls.
+ *   - fvdb radiance_fields page (GaussianSplatReconstructionConfig: tile_size
+ *     = 16, eps_2d bounding-box padding; GaussianSplatOptimizer: Adam).
+ *
+ * Conventions shared by every call
+ *   - Pointers marked "device" are device memory (hipMalloc, or a torch CUDA
+ *     tensor's data pointer) owned by the caller; the library never allocates,
+ *     frees or retains them, and keeps no global state.  "host" pointers are
+ *     read synchronously during the call.
+ *   - `stream` is a hipStream_t (NULL: the legacy default stream).  Every call
+ *     only enqueues work on it and returns; results are ready when the stream
+ *     reaches them.  Calls on different streams that share buffers race.
+ *   - Arguments are checked before anything is enqueued; a bad argument
+ *     returns GI_ERR_INVALID_ARG and enqueues nothing.  A failed launch returns
+ *     GI_ERR_HIP.  gi_status_string() names a status.
+ *   - float arrays are IEEE fp32; device arrays must be 16-byte aligned.
+ *   - Pixel (row i, column j) samples the point (j + 0.5, i + 0.5); images are
+ *     planar [3][H][W] (channel, row, column).  Tiles are 16x16 pixels, tile
+ *     id = ty * ceil(W/16) + tx.  1 <= W, H <= 32768.
+ *
+ * Gaussian parameters ("params", device float [n][8]):
+ *     mux, muy, l11, l21, l22, cr, cg, cb
+ *   mean in pixels; covariance Sigma = L L^T with L = [[l11, 0], [l21, l22]]
+ *   (signs free, det Sigma = (l11 l22)^2); colour = weighted colour (the
+ *   Gaussian's peak amplitude; opacity is folded into it in the sum mode).
+ *   Alpha mode adds "logit" (device float [n]): o = sigmoid(min(logit, ln 999)).
+ *
+ * Cutoff (the 3-sigma rule; its fp32 evaluation is part of the contract so
+ * that binning and pixel coverage are reproducible bit for bit):
+ *     i11 = 1/l11, i22 = 1/l22, k = -((l21*i11)*i22)            (L^-1 rows)
+ *     a = i11*S, b = k*S, c = i22*S,   S = fp32(sqrt(log2(e)/2))
+ *     dx = (j+0.5) - mux, dy = (i+0.5) - muy
+ *     u = a*dx, t = b*dx, v = fma(c, dy, t), e = fma(v, v, u*u)
+ *     the pair (Gaussian, pixel) contributes iff e <= fp32(4.5*log2(e)),
+ *   i.e. iff d^T Sigma^-1 d <= 9 up to fp32 rounding; its weight is
+ *   w = exp(-d^T Sigma^-1 d / 2) = 2^-e.  A Gaussian with a non-finite
+ *   parameter (or logit), l11 == 0, l22 == 0, or non-finite i11/i22/k is
+ *   culled: it covers no tile and no pixel, and its gradient is 0.
+ */
+#ifndef GI_H
+#define GI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GI_OK = 0,
+    GI_ERR_INVALID_ARG = 1,
+    GI_ERR_HIP = 2,
+    GI_ERR_CAPACITY = 3
+} gi_status;
+
+typedef enum {
+    GI_MODE_SUM = 0,     /* accumulated summation ("GaussianImage", Overview)            */
+    GI_MODE_ALPHA = 1    /* front-to-back alpha over a background ("Drawing with Gaussians") */
+} gi_mode;
+
+typedef struct {
+    int32_t width;       /* W, pixels */
+    int32_t height;      /* H, pixels */
+    int32_t mode;        /* gi_mode */
+    int32_t reserved;    /* must be 0 */
+} gi_desc;
+
+/* Name of a status code (static string). */
+const char *gi_status_string(gi_status s);
+
+/* Library version, e.g. "gi 1.0 gfx950". */
+const char *gi_version(void);
+
+/* Number of 16x16 tiles, ceil(W/16)*ceil(H/16); 0 for an invalid desc. */
+int64_t gi_num_tiles(const gi_desc *desc);
+
+/*
+ * gi_preprocess -- per-Gaussian set-up for binning and rasterization.
+ *   Reading of "GaussianImage" (8 parameters, Cholesky covariance) and the
+ *   fvdb config's eps_2d (pixel padding of the screen-space box).
+ *
+ *   n        number of Gaussians, 0 <= n < 2^31.
+ *   params   device float [n][8], as above.
+ *   logit    device float [n] (alpha mode) or NULL (sum mode).
+ *   records  device float [n][8] out: mux, muy, a, b, c, cr, cg, cb
+ *            (a, b, c as in the cutoff rule; zeros for a culled Gaussian).
+ *   opacity  device float [n] out (alpha mode): o = 1/(1+exp(-min(logit, ln 999)));
+ *            NULL in sum mode.
+ *   pixbox   device uint16 [n][4] out: j0, i0, j1, i1, the inclusive pixel box
+ *            of the 3-sigma ellipse, clipped to the image:
+ *              rx = 3|l11| + 1/256, ry = 3 sqrt(fma(l21, l21, l22*l22)) + 1/256,
+ *              j0 = max(0, ceil((mux-0.5) - rx)), j1 = min(W-1, floor((mux-0.5) + rx)),
+ *              i0, i1 likewise with muy, ry (fp32).  An empty box (off-image or
+ *              culled) is written as (1, 1, 0, 0).
+ *   counts   device uint32 [n] out: tiles covered, (j1/16 - j0/16 + 1)(i1/16 - i0/16 + 1),
+ *            0 for an empty box.
+ */
+gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                        float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
+                        void *stream);
+
+/*
+ * gi_bin_sort -- tile lists: every (tile, Gaussian) pair of the pixel boxes,
+ *   ordered by tile and, within a tile, by ascending Gaussian index.  Pairs are
+ *   emitted per Gaussian in (index, tile row, tile column) order and sorted by
+ *   tile id with a stable LSD radix sort, so each tile's list is in index order
+ *   (the summation order of the sum image and the front-to-back order of the
+ *   alpha image).  Reading: tile binning is what the FlashImgs viewer calls
+ *   "tile-binned compute" (Web viewer) with fvdb's 16-pixel tiles.
+ *
+ *   pixbox, counts  from gi_preprocess (device).
+ *   offsets   device uint32 [n+1] out: exclusive prefix sum of counts; offsets[n] = M.
+ *   keys      device uint32 [capacity] out: tile id of pair m (m < M), ascending.
+ *   vals      device uint32 [capacity] out: Gaussian index of pair m.
+ *   ranges    device uint32 [T][2] out: [start, end) of tile t in keys/vals;
+ *             (0, 0) for a tile with no pair.
+ *   capacity  length of keys/vals, 0 <= capacity < 2^31.
+ *   d_num     device uint32 [1] out: M (saturated at 2^32-1).  When M > capacity
+ *             no pair is written, every range is (0, 0) and *d_num still holds M.
+ *   h_num     host int64 [1] or NULL.  If given, the call waits for the stream,
+ *             stores M there, and returns GI_ERR_CAPACITY when M > capacity;
+ *             if NULL the call never waits and overflow shows only in *d_num.
+ *   workspace device scratch of at least gi_bin_sort_workspace_bytes() bytes,
+ *             256-byte aligned; its contents need no initialisation and are
+ *             garbage afterwards.
+ */
+size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity);
+gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, const uint32_t *counts,
+                      uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges,
+                      int64_t capacity, uint32_t *d_num, int64_t *h_num,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gi_render_fwd -- rasterize the binned Gaussians into an image.
+ *   Sum mode ("GaussianImage", accumulated summation):
+ *       I_k(p) = sum over the tile's list, in list order, of c_k * 2^-e
+ *     over pairs admitted by the cutoff; no background, no clamping.  The fp32
+ *     sum is formed in list order, so the image is bitwise reproducible.
+ *   Alpha mode ("Drawing with Gaussians", alpha-composited over a background):
+ *       alpha = o * 2^-e, C_k += c_k * alpha * T, T -= alpha * T, in list order;
+ *     after the first Gaussian that leaves T < 1e-4 the pixel stops;
+ *       image_k = C_k + T * background_k.
+ *
+ *   n                 number of Gaussians given to gi_preprocess.
+ *   records, opacity, pixbox  from gi_preprocess (opacity NULL in sum mode);
+ *                     the pixel boxes let each 8x8 quadrant of a tile skip the
+ *                     Gaussians that cannot reach it (no effect on the result).
+ *   ranges, vals      from gi_bin_sort.
+ *   background device float [3] (alpha mode) or NULL.
+ *   image      device float [3][H][W] out.
+ *   t_final    device float [H][W] out (alpha mode): final T; NULL in sum mode.
+ *   last       device uint32 [H][W] out (alpha mode): one past the list position
+ *              (index into vals) of the last Gaussian composited at the pixel, or
+ *              the tile's range start if none; NULL in sum mode.
+ */
+gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
+                        const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                        const float *background, float *image, float *t_final, uint32_t *last,
+                        void *stream);
+
+/*
+ * gi_render_bwd -- gradients of a scalar loss L given dL/dimage.
+ *   Reading of "Drawing with Gaussians" (fused rasterization kernels with
+ *   custom VJPs): the exact derivative of gi_render_fwd's image, with the
+ *   cutoff held fixed (almost-everywhere derivative) and, in alpha mode, each
+ *   pixel's stopping point held fixed.  Per admitted pair with w = 2^-e:
+ *     sum:   dL/dc_k += g_k w,  dL/dw = sum_k g_k c_k
+ *     alpha: dL/dc_k += g_k alpha T_j,
+ *            dL/dalpha = sum_k g_k (T_j c_k - S_k / (1 - alpha)),
+ *            S_k = sum over later contributors of c alpha T, plus T_final bg_k,
+ *            dL/dlogit += dL/dalpha * w * o (1 - o)  (0 when logit >= ln 999),
+ *            dL/dbg_k += g_k T_final.
+ *     w -> (mean, L) through d^T Sigma^-1 d.
+ *
+ *   records, opacity, pixbox, ranges, vals, background, t_final, last: as given to /
+ *             produced by gi_render_fwd for the same inputs (alpha-only ones
+ *             NULL in sum mode).
+ *   logit     device float [n] (alpha mode, for the clamp test) or NULL.
+ *   dL_dimage device float [3][H][W].
+ *   dparams   device float [n][8], ACCUMULATED (+=) in the params layout.
+ *   dlogit    device float [n], accumulated (alpha mode) or NULL.
+ *   dbackground device float [3], accumulated (alpha mode) or NULL.
+ *   Accumulation uses fp32 atomics: the order of additions, hence the last
+ *   bits of the gradients, may vary from run to run.
+ */
+gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
+                        const float *logit, const uint16_t *pixbox, const uint32_t *ranges,
+                        const uint32_t *vals,
+                        const float *background, const float *t_final, const uint32_t *last,
+                        const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                        void *stream);
+
+/*
+ * gi_loss_l2 -- L = mean over the 3HW entries of (image - target)^2 and
+ *   dL/dimage = 2 (image - target) / (3HW)  ("FlashImgs", --loss l2).
+ *   count      number of entries (3*H*W), >= 1.
+ *   dL_dimage  device float [count] out (may be NULL).
+ *   d_loss     device float [1] out (may be NULL); summed in fp64 per block and
+ *              over blocks in a fixed order (reproducible).
+ *   workspace  device scratch of gi_loss_workspace_bytes(count) bytes.
+ */
+size_t gi_loss_workspace_bytes(int64_t count);
+gi_status gi_loss_l2(int64_t count, const float *image, const float *target, float *dL_dimage,
+                     float *d_loss, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gi_adam_step -- one fused Adam step over rows x row_len fp32 entries
+ *   (fvdb GaussianSplatOptimizer: Adam; "Drawing with Gaussians": fused
+ *   optimizer kernels).  With t = step >= 1:
+ *     m = b1 m + (1-b1) g,  v = b2 v + (1-b2) g^2,
+ *     p -= lr[slot] * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps),
+ *   slot = column within the row; no weight decay.  zero_grad != 0 also sets
+ *   g = 0 afterwards (ready for the next accumulation).
+ *   p, g, m, v  device float [rows][row_len], updated in place.
+ *   lr          host float [row_len], 1 <= row_len <= 16.
+ */
+gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v,
+                       const float *lr, float beta1, float beta2, float eps, int32_t step,
+                       int32_t zero_grad, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GI_H */

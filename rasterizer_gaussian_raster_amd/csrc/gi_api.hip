@@ -1,0 +1,148 @@
+// gi_api.hip -- the extern "C" entry points declared in include/gi.h: argument
+// checks, launch of the gfx950 kernels on the caller's stream, status codes.
+#include <hip/hip_runtime.h>
+
+#include "../../include/gi.h"
+#include "gi_launch.hpp"
+
+namespace {
+
+constexpr int kMaxDim = 32768;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+bool desc_ok(const gi_desc *d) {
+    return d && d->width >= 1 && d->height >= 1 && d->width <= kMaxDim && d->height <= kMaxDim &&
+           (d->mode == GI_MODE_SUM || d->mode == GI_MODE_ALPHA) && d->reserved == 0;
+}
+
+gi_status hip_status(hipError_t e) { return e == hipSuccess ? GI_OK : GI_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *gi_status_string(gi_status s) {
+    switch (s) {
+    case GI_OK: return "GI_OK";
+    case GI_ERR_INVALID_ARG: return "GI_ERR_INVALID_ARG";
+    case GI_ERR_HIP: return "GI_ERR_HIP";
+    case GI_ERR_CAPACITY: return "GI_ERR_CAPACITY";
+    default: return "GI_UNKNOWN_STATUS";
+    }
+}
+
+const char *gi_version(void) { return "gi 1.0 gfx950"; }
+
+int64_t gi_num_tiles(const gi_desc *desc) {
+    if (!desc_ok(desc)) return 0;
+    return (int64_t)((desc->width + 15) / 16) * ((desc->height + 15) / 16);
+}
+
+gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, const float *logit, float *records,
+                        float *opacity, uint16_t *pixbox, uint32_t *counts, void *stream) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    const bool alpha = desc->mode == GI_MODE_ALPHA;
+    if (n > 0) {
+        if (!params || !records || !pixbox || !counts) return GI_ERR_INVALID_ARG;
+        if (!aligned16(params) || !aligned16(records) || !aligned16(pixbox) || !aligned16(counts))
+            return GI_ERR_INVALID_ARG;
+        if (alpha != (logit != nullptr) || alpha != (opacity != nullptr)) return GI_ERR_INVALID_ARG;
+    }
+    return hip_status(gi::launch_preprocess((int)n, desc->width, desc->height, params, logit, records, opacity,
+                                            pixbox, counts, as_stream(stream)));
+}
+
+size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return 0;
+    return gi::make_bin_plan((int)n, desc->width, desc->height, capacity).bytes;
+}
+
+gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, const uint32_t *counts,
+                      uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, int64_t capacity,
+                      uint32_t *d_num, int64_t *h_num, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31))
+        return GI_ERR_INVALID_ARG;
+    if (!offsets || !ranges || !d_num || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!pixbox || !counts)) return GI_ERR_INVALID_ARG;
+    if (capacity > 0 && (!keys || !vals)) return GI_ERR_INVALID_ARG;
+    const gi::BinPlan plan = gi::make_bin_plan((int)n, desc->width, desc->height, capacity);
+    if (workspace_bytes < plan.bytes) return GI_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, d_num, workspace, s);
+    if (e != hipSuccess) return GI_ERR_HIP;
+    if (h_num) {
+        unsigned long long total = 0;
+        e = hipMemcpyAsync(&total, gi::bin_total_ptr(workspace), sizeof(total), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return GI_ERR_HIP;
+        *h_num = (int64_t)total;
+        if ((int64_t)total > capacity) return GI_ERR_CAPACITY;
+    }
+    return GI_OK;
+}
+
+gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
+                        const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                        const float *background, float *image, float *t_final, uint32_t *last, void *stream) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!ranges || !vals || !image || !aligned16(image)) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    if (desc->mode == GI_MODE_SUM) {
+        if (opacity || background || t_final || last) return GI_ERR_INVALID_ARG;
+        return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, vals,
+                                                    image, s));
+    }
+    if (!background || !t_final || !last || (n > 0 && !opacity)) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_render_alpha_fwd(desc->width, desc->height, records, opacity, pixbox, ranges,
+                                                  vals, background, image, t_final, last, s));
+}
+
+gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
+                        const float *logit, const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                        const float *background, const float *t_final, const uint32_t *last,
+                        const float *dL_dimage, float *dparams, float *dlogit, float *dbackground, void *stream) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!ranges || !vals || !dL_dimage) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !pixbox || !dparams || !aligned16(records))) return GI_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    if (desc->mode == GI_MODE_SUM) {
+        if (opacity || logit || background || t_final || last || dlogit || dbackground) return GI_ERR_INVALID_ARG;
+        return hip_status(gi::launch_render_sum_bwd(desc->width, desc->height, records, pixbox, ranges, vals,
+                                                    dL_dimage, dparams, s));
+    }
+    if (!background || !t_final || !last || (n > 0 && (!opacity || !logit))) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_render_alpha_bwd(desc->width, desc->height, records, opacity, logit, pixbox,
+                                                  ranges, vals, background, t_final, last, dL_dimage, dparams,
+                                                  dlogit, dbackground, s));
+}
+
+size_t gi_loss_workspace_bytes(int64_t count) { return count < 1 ? 0 : gi::loss_workspace_bytes(count); }
+
+gi_status gi_loss_l2(int64_t count, const float *image, const float *target, float *dL_dimage, float *d_loss,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (count < 1 || !image || !target || !workspace) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::loss_workspace_bytes(count) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+        return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_loss_l2(count, image, target, dL_dimage, d_loss, workspace, as_stream(stream)));
+}
+
+gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v, const float *lr,
+                       float beta1, float beta2, float eps, int32_t step, int32_t zero_grad, void *stream) {
+    if (rows < 0 || row_len < 1 || row_len > 16 || step < 1 || !lr) return GI_ERR_INVALID_ARG;
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps >= 0.0f))
+        return GI_ERR_INVALID_ARG;
+    if (rows > 0) {
+        if (!p || !g || !m || !v) return GI_ERR_INVALID_ARG;
+        if (row_len % 4 == 0 && (!aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v)))
+            return GI_ERR_INVALID_ARG;
+    }
+    return hip_status(gi::launch_adam(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_grad,
+                                      as_stream(stream)));
+}
+
+}  // extern "C"

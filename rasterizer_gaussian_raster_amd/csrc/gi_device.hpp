@@ -1,0 +1,58 @@
+// gi_device.hpp -- device-side helpers shared by the gfx950 kernels of libgi.
+//
+// Wave64 only (CDNA4).  Cross-lane reductions use DPP row operations and the
+// gfx9 row broadcasts, which stay inside the VALU (no LDS round trip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gi {
+
+constexpr int kTile = 16;            // tile edge, pixels (fvdb config: tile_size = 16)
+constexpr int kWave = 64;
+
+// fp32 constants of the cutoff rule, each the fp32 value nearest its definition.
+constexpr float kScale = 0x1.b2da4ep-1f;   // sqrt(log2(e) / 2)
+constexpr float kE9 = 0x1.9f7f06p+2f;      // 9 * log2(e) / 2: e <= kE9  <=>  q <= 9
+constexpr float kLogitMax = 0x1.ba0846p+2f;// ln(999): opacity clamp at 0.999
+constexpr float kTmin = 1e-4f;             // alpha mode: stop once T < kTmin
+constexpr float kLn2 = 0x1.62e430p-1f;     // ln 2
+constexpr float kPad = 0.00390625f;        // 1/256 px pad of the pixel box
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+__device__ __forceinline__ uint64_t lanes_below() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// 2^x with the hardware transcendental (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND_CTRL = false>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, BANK_MASK, BOUND_CTRL));
+}
+
+// Sum over the 64 lanes, returned uniform (read from lane 63).
+__device__ __forceinline__ float wave_total(float x) {
+    x += dpp_f<0xb1>(x);
+    x += dpp_f<0x4e>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
+    x += dpp_f<0x142, 0xa>(x);
+    x += dpp_f<0x143, 0xc>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// XCD-aware block -> work-item map: the hardware deals consecutive workgroups
+// round-robin over the 8 XCDs; give each XCD a contiguous run of work items so
+// neighbouring tiles (which share Gaussians) hit the same L2.  The grid must
+// be a multiple of 8 blocks; the map is then a bijection of [0, nblocks).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    const int per = nblocks >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace gi

@@ -1,0 +1,56 @@
+// gi_launch.hpp -- host-side launchers of the gfx950 kernels (internal to libgi).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gi {
+
+// k_preprocess.hip
+hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
+                             float *opacity, uint16_t *pixbox, uint32_t *counts, hipStream_t s);
+
+// k_binning.hip
+struct BinPlan {
+    int n, W, H, tiles_x, ntiles;
+    int64_t capacity;
+    int passes;            // LSD passes (0 when there is a single tile)
+    int bits[4];           // digit width of each pass
+    int nb_g;              // Gaussian groups of 256 (emission blocks)
+    int nbs;               // sort blocks of kSortChunk keys over the capacity
+    size_t off_part, off_kalt, off_valt, off_table, off_tsp, bytes;
+};
+BinPlan make_bin_plan(int n, int W, int H, int64_t capacity);
+hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
+                           uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *d_num, void *ws,
+                           hipStream_t s);
+// device address of the 64-bit instance total inside the workspace
+const void *bin_total_ptr(const void *ws);
+
+// k_raster_sum.hip
+hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
+                                 const uint32_t *ranges, const uint32_t *vals, float *image, hipStream_t s);
+hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
+                                 const uint32_t *ranges, const uint32_t *vals, const float *dL_dimage,
+                                 float *dparams, hipStream_t s);
+
+// k_raster_alpha.hip
+hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
+                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                                   const float *background, float *image, float *t_final, uint32_t *last,
+                                   hipStream_t s);
+hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
+                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                                   const float *background, const float *t_final, const uint32_t *last,
+                                   const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                                   hipStream_t s);
+
+// k_optim.hip
+size_t loss_workspace_bytes(int64_t count);
+hipError_t launch_loss_l2(int64_t count, const float *image, const float *target, float *dL_dimage, float *d_loss,
+                          void *ws, hipStream_t s);
+hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, float *v, const float *lr,
+                       float beta1, float beta2, float eps, int step, int zero_grad, hipStream_t s);
+
+}  // namespace gi

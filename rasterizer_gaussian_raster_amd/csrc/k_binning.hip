@@ -1,0 +1,380 @@
+// k_binning.hip -- tile lists from per-Gaussian pixel boxes.
+//
+//   1. k_group_sums   : per 256-Gaussian group, sum of tile counts (u64).
+//   2. k_group_scan   : one workgroup scans the group sums -> group bases, M.
+//   3. k_emit         : per group, offsets[] and one (tile id, index) pair per
+//                       covered tile, emitted in (index, tile row, tile column)
+//                       order; the group's pairs are spread evenly over its
+//                       256 lanes by a binary search in LDS (no lane walks a
+//                       large Gaussian alone).
+//   4. LSD radix sort on the tile id, 1..8-bit digits per pass (as many passes
+//      as the id needs), each pass = digit counts per 4096-key block ->
+//      exclusive scan of the digit-major count table -> stable scatter, where
+//      each key's rank among equal digits is found with wave ballots in key
+//      order, so the sort is stable and each tile list ends up in ascending
+//      Gaussian index.
+//   5. k_ranges       : per tile, [start, end) by binary search of the sorted ids.
+//
+// Binning is the tile-binned scheme of the FlashImgs viewer ("Web viewer":
+// tile-binned compute) with fvdb's 16-pixel tiles (tile_size).  All steps are
+// HBM/latency bound: ~20 B per pair per sort pass, 12 B per Gaussian to emit.
+#include "gi_device.hpp"
+#include "gi_launch.hpp"
+
+namespace gi {
+
+constexpr int kSortThreads = 256;
+constexpr int kSortIters = 16;
+constexpr int kSortChunk = kSortThreads * kSortIters;   // keys per sort block
+constexpr int kScanItems = 16;
+constexpr int kScanChunk = 256 * kScanItems;           // table entries per scan block
+
+struct BinHeader {
+    unsigned long long total;   // M, 64-bit
+    uint32_t m_eff;             // M if M <= capacity, else 0 (nothing emitted or sorted)
+    uint32_t pad[13];
+};
+
+// ---------------------------------------------------------------------------
+// block-wide exclusive scan (NT threads, wave64)
+// ---------------------------------------------------------------------------
+template <typename T, int NT>
+__device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T inc = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        T y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += y;
+    }
+    if (lane == 63) smem[wave] = inc;
+    __syncthreads();
+    T off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const T sw = smem[w];
+        off += (w < wave) ? sw : T(0);
+        tot += sw;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + inc - x;
+}
+
+// ---------------------------------------------------------------------------
+// 1-3: counts -> offsets -> emitted pairs
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_group_sums(int n, const uint32_t *__restrict__ counts,
+                                                    unsigned long long *__restrict__ part) {
+    __shared__ unsigned long long sm[4];
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    unsigned long long c = g < n ? counts[g] : 0ull;
+    unsigned long long tot;
+    block_exclusive_scan<unsigned long long, 256>(c, sm, &tot);
+    if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+// One workgroup of 1024: exclusive scan of the group sums in place; publishes M.
+__global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long long capacity,
+                                                     unsigned long long *__restrict__ part,
+                                                     BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
+                                                     uint32_t *__restrict__ d_num) {
+    __shared__ unsigned long long sm[16];
+    const int per = (ngroups + 1023) / 1024;
+    const int beg = threadIdx.x * per;
+    unsigned long long s = 0;
+    for (int i = 0; i < per; ++i)
+        if (beg + i < ngroups) s += part[beg + i];
+    unsigned long long tot;
+    unsigned long long run = block_exclusive_scan<unsigned long long, 1024>(s, sm, &tot);
+    for (int i = 0; i < per; ++i)
+        if (beg + i < ngroups) {
+            const unsigned long long v = part[beg + i];
+            part[beg + i] = run;
+            run += v;
+        }
+    if (threadIdx.x == 0) {
+        hdr->total = tot;
+        hdr->m_eff = (tot <= (unsigned long long)capacity) ? (uint32_t)tot : 0u;
+        const uint32_t sat = tot > 0xffffffffull ? 0xffffffffu : (uint32_t)tot;
+        *d_num = sat;
+        offsets[n] = sat;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_emit(int n, int tiles_x, const uint32_t *__restrict__ counts,
+                                              const uint2 *__restrict__ pixbox,
+                                              const unsigned long long *__restrict__ part,
+                                              const BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
+                                              uint32_t *__restrict__ keys, uint32_t *__restrict__ vals) {
+    __shared__ uint32_t excl[257];
+    __shared__ uint2 box[256];
+    __shared__ uint32_t sm[4];
+    const int tid = threadIdx.x;
+    const int g = blockIdx.x * 256 + tid;
+    const uint32_t c = g < n ? counts[g] : 0u;
+    uint32_t tot;
+    const uint32_t local = block_exclusive_scan<uint32_t, 256>(c, sm, &tot);
+    const unsigned long long base = part[blockIdx.x];
+    if (g < n) {
+        const unsigned long long o = base + local;
+        offsets[g] = o > 0xffffffffull ? 0xffffffffu : (uint32_t)o;
+    }
+    if (hdr->m_eff != hdr->total || tot == 0) return;   // overflow (or nothing to emit): uniform
+    excl[tid] = local;
+    if (tid == 0) excl[256] = tot;
+    box[tid] = g < n ? pixbox[g] : make_uint2(0u, 0u);
+    __syncthreads();
+    const uint32_t b32 = (uint32_t)base;
+    for (uint32_t idx = tid; idx < tot; idx += 256) {
+        int lo = 0, hi = 256;                 // excl[lo] <= idx < excl[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (excl[mid] <= idx) lo = mid; else hi = mid;
+        }
+        const uint32_t r = idx - excl[lo];
+        const uint2 bx = box[lo];
+        const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
+        const uint32_t tx1 = (bx.y & 0xffffu) >> 4;
+        const uint32_t wt = tx1 - tx0 + 1;
+        const uint32_t q = r / wt, rem = r - q * wt;
+        keys[b32 + idx] = (ty0 + q) * (uint32_t)tiles_x + tx0 + rem;
+        vals[b32 + idx] = (uint32_t)(blockIdx.x * 256 + lo);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4: stable LSD radix sort pass
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint32_t *__restrict__ keys,
+                                                             const BinHeader *__restrict__ hdr, int shift,
+                                                             int bits, uint32_t *__restrict__ table, int nbs) {
+    __shared__ uint32_t h[256];
+    const int radix = 1 << bits;
+    const int tid = threadIdx.x;
+    if (tid < radix) h[tid] = 0;
+    __syncthreads();
+    const uint32_t M = hdr->m_eff;
+    const uint32_t base = blockIdx.x * (uint32_t)kSortChunk;
+    for (int it = 0; it < kSortIters; ++it) {
+        const uint32_t idx = base + it * kSortThreads + tid;
+        if (idx < M) atomicAdd(&h[(keys[idx] >> shift) & (radix - 1)], 1u);
+    }
+    __syncthreads();
+    if (tid < radix) table[(size_t)tid * nbs + blockIdx.x] = h[tid];
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(const uint32_t *__restrict__ kin,
+                                                               const uint32_t *__restrict__ vin,
+                                                               uint32_t *__restrict__ kout,
+                                                               uint32_t *__restrict__ vout,
+                                                               const BinHeader *__restrict__ hdr, int shift,
+                                                               int bits, const uint32_t *__restrict__ table,
+                                                               int nbs) {
+    __shared__ uint32_t run[256];          // next output slot per digit
+    __shared__ uint32_t wcnt[4][256];      // per wave: keys of each digit in this round
+    const uint32_t M = hdr->m_eff;
+    const uint32_t base = blockIdx.x * (uint32_t)kSortChunk;
+    if (base >= M) return;
+    const int radix = 1 << bits;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid < radix) run[tid] = table[(size_t)tid * nbs + blockIdx.x];
+    for (int i = tid; i < 4 * 256; i += kSortThreads) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const uint64_t below = lanes_below();
+    for (int it = 0; it < kSortIters; ++it) {
+        const uint32_t rbase = base + it * kSortThreads;
+        if (rbase >= M) break;                                  // uniform
+        const uint32_t idx = rbase + tid;
+        const bool valid = idx < M;
+        const uint32_t key = valid ? kin[idx] : 0u;
+        const uint32_t val = valid ? vin[idx] : 0u;
+        const uint32_t d = (key >> shift) & (uint32_t)(radix - 1);
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < bits; ++bit) {
+            const bool on = (d >> bit) & 1u;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & below);
+        const bool leader = valid && (peers >> lane) == 1ull;   // highest lane of the digit group
+        if (leader) wcnt[wave][d] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t pos = run[d] + rank;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
+            kout[pos] = key;
+            vout[pos] = val;
+        }
+        __syncthreads();
+        if (tid < radix) {
+            run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+            wcnt[0][tid] = 0; wcnt[1][tid] = 0; wcnt[2][tid] = 0; wcnt[3][tid] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+// exclusive scan of a u32 array in place: one workgroup when it is short,
+// otherwise reduce -> scan of block sums -> rescan with offsets.
+__global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, int count) {
+    __shared__ uint32_t sm[16];
+    const int per = (count + 1023) / 1024;
+    const int beg = threadIdx.x * per;
+    uint32_t s = 0;
+    for (int i = 0; i < per; ++i)
+        if (beg + i < count) s += a[beg + i];
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan<uint32_t, 1024>(s, sm, &tot);
+    for (int i = 0; i < per; ++i)
+        if (beg + i < count) {
+            const uint32_t v = a[beg + i];
+            a[beg + i] = run;
+            run += v;
+        }
+}
+
+__global__ __launch_bounds__(256) void k_scan_reduce(const uint32_t *__restrict__ a, int count,
+                                                     uint32_t *__restrict__ sums) {
+    __shared__ uint32_t sm[4];
+    const int beg = blockIdx.x * kScanChunk + threadIdx.x * kScanItems;
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i)
+        if (beg + i < count) s += a[beg + i];
+    uint32_t tot;
+    block_exclusive_scan<uint32_t, 256>(s, sm, &tot);
+    if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(256) void k_scan_down(uint32_t *__restrict__ a, int count,
+                                                   const uint32_t *__restrict__ sums) {
+    __shared__ uint32_t sm[4];
+    const int beg = blockIdx.x * kScanChunk + threadIdx.x * kScanItems;
+    uint32_t v[kScanItems];
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        v[i] = (beg + i < count) ? a[beg + i] : 0u;
+        s += v[i];
+    }
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan<uint32_t, 256>(s, sm, &tot) + sums[blockIdx.x];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i)
+        if (beg + i < count) {
+            a[beg + i] = run;
+            run += v[i];
+        }
+}
+
+static hipError_t scan_u32(uint32_t *a, int count, uint32_t *sums, hipStream_t s) {
+    if (count <= 32768) {
+        k_scan_single<<<1, 1024, 0, s>>>(a, count);
+        return hipGetLastError();
+    }
+    const int nb = (count + kScanChunk - 1) / kScanChunk;
+    k_scan_reduce<<<nb, 256, 0, s>>>(a, count, sums);
+    k_scan_single<<<1, 1024, 0, s>>>(sums, nb);
+    k_scan_down<<<nb, 256, 0, s>>>(a, count, sums);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 5: tile ranges
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lower_bound_u32(const uint32_t *__restrict__ a, uint32_t n, uint32_t x) {
+    uint32_t lo = 0, hi = n;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void k_ranges(const uint32_t *__restrict__ keys, const BinHeader *__restrict__ hdr,
+                                                int ntiles, uint2 *__restrict__ ranges) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= ntiles) return;
+    const uint32_t M = hdr->m_eff;
+    const uint32_t lo = lower_bound_u32(keys, M, (uint32_t)t);
+    const uint32_t hi = lower_bound_u32(keys, M, (uint32_t)t + 1u);
+    ranges[t] = hi > lo ? make_uint2(lo, hi) : make_uint2(0u, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
+    BinPlan p{};
+    p.n = n; p.W = W; p.H = H;
+    p.tiles_x = (W + kTile - 1) / kTile;
+    const int tiles_y = (H + kTile - 1) / kTile;
+    p.ntiles = p.tiles_x * tiles_y;
+    p.capacity = capacity;
+    int B = 0;
+    while ((1ll << B) < (long long)p.ntiles) ++B;          // key bits: ids in [0, ntiles)
+    p.passes = (B + 7) / 8;
+    for (int i = 0; i < 4; ++i) p.bits[i] = 0;
+    if (p.passes > 0) {
+        const int w = (B + p.passes - 1) / p.passes;
+        int left = B;
+        for (int i = 0; i < p.passes; ++i) { p.bits[i] = left < w ? left : w; left -= p.bits[i]; }
+    }
+    p.nb_g = (n + 255) / 256;
+    p.nbs = (int)((capacity + kSortChunk - 1) / kSortChunk);
+    size_t off = align256(sizeof(BinHeader));
+    p.off_part = off; off = align256(off + sizeof(unsigned long long) * (size_t)(p.nb_g > 0 ? p.nb_g : 1));
+    p.off_kalt = off; off = align256(off + sizeof(uint32_t) * (size_t)(capacity > 0 ? capacity : 1));
+    p.off_valt = off; off = align256(off + sizeof(uint32_t) * (size_t)(capacity > 0 ? capacity : 1));
+    const size_t table = (size_t)256 * (size_t)(p.nbs > 0 ? p.nbs : 1);
+    p.off_table = off; off = align256(off + sizeof(uint32_t) * table);
+    p.off_tsp = off; off = align256(off + sizeof(uint32_t) * ((table + kScanChunk - 1) / kScanChunk + 1));
+    p.bytes = off;
+    return p;
+}
+
+const void *bin_total_ptr(const void *ws) { return &static_cast<const BinHeader *>(ws)->total; }
+
+hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
+                           uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *d_num, void *ws,
+                           hipStream_t s) {
+    char *w = static_cast<char *>(ws);
+    BinHeader *hdr = reinterpret_cast<BinHeader *>(w);
+    unsigned long long *part = reinterpret_cast<unsigned long long *>(w + p.off_part);
+    uint32_t *kalt = reinterpret_cast<uint32_t *>(w + p.off_kalt);
+    uint32_t *valt = reinterpret_cast<uint32_t *>(w + p.off_valt);
+    uint32_t *table = reinterpret_cast<uint32_t *>(w + p.off_table);
+    uint32_t *tsp = reinterpret_cast<uint32_t *>(w + p.off_tsp);
+
+    if (p.nb_g > 0) k_group_sums<<<p.nb_g, 256, 0, s>>>(p.n, counts, part);
+    k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
+    // Emit into the buffer that the last pass reads from, so the result lands in keys/vals.
+    uint32_t *ek = (p.passes & 1) ? kalt : keys;
+    uint32_t *ev = (p.passes & 1) ? valt : vals;
+    if (p.nb_g > 0)
+        k_emit<<<p.nb_g, 256, 0, s>>>(p.n, p.tiles_x, counts, reinterpret_cast<const uint2 *>(pixbox), part, hdr,
+                                      offsets, ek, ev);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    uint32_t *srck = ek, *srcv = ev;
+    uint32_t *dstk = (srck == keys) ? kalt : keys, *dstv = (srcv == vals) ? valt : vals;
+    int shift = 0;
+    for (int pass = 0; pass < p.passes && p.nbs > 0; ++pass) {
+        const int bits = p.bits[pass];
+        k_sort_count<<<p.nbs, kSortThreads, 0, s>>>(srck, hdr, shift, bits, table, p.nbs);
+        e = scan_u32(table, (1 << bits) * p.nbs, tsp, s);
+        if (e != hipSuccess) return e;
+        k_sort_scatter<<<p.nbs, kSortThreads, 0, s>>>(srck, srcv, dstk, dstv, hdr, shift, bits, table, p.nbs);
+        shift += bits;
+        uint32_t *tk = srck, *tv = srcv;
+        srck = dstk; srcv = dstv; dstk = tk; dstv = tv;
+    }
+    if (p.ntiles > 0)
+        k_ranges<<<(p.ntiles + 255) / 256, 256, 0, s>>>(keys, hdr, p.ntiles, reinterpret_cast<uint2 *>(ranges));
+    return hipGetLastError();
+}
+
+}  // namespace gi

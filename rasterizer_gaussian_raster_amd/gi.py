@@ -1,0 +1,156 @@
+"""ctypes binding of libgi.so (include/gi.h): one Python function per C entry point.
+
+Argument marshalling only: tensors are passed as device pointers, the current
+torch stream as the hipStream_t, and a non-OK status raises GiError.  Every
+computation happens in the HIP kernels behind the C ABI.  There is no fallback:
+if libgi.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgi.so")
+
+GI_OK, GI_ERR_INVALID_ARG, GI_ERR_HIP, GI_ERR_CAPACITY = 0, 1, 2, 3
+MODE_SUM, MODE_ALPHA = 0, 1
+TILE = 16
+
+_lib = None
+
+
+class GiError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status) if _lib else status}")
+
+
+class gi_desc(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("height", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def desc(width: int, height: int, mode: int = MODE_SUM) -> gi_desc:
+    return gi_desc(int(width), int(height), int(mode), 0)
+
+
+def load():
+    """Open libgi.so (built by rasterizer_gaussian_raster_amd.build); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m rasterizer_gaussian_raster_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, D = ctypes.c_void_p, ctypes.POINTER(gi_desc)
+    i64, i32, f32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    sigs = {
+        "gi_status_string": ([i32], ctypes.c_char_p),
+        "gi_version": ([], ctypes.c_char_p),
+        "gi_num_tiles": ([D], i64),
+        "gi_preprocess": ([D, i64, P, P, P, P, P, P, P], i32),
+        "gi_bin_sort_workspace_bytes": ([D, i64, i64], sz),
+        "gi_bin_sort": ([D, i64, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
+        "gi_render_fwd": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
+        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P], i32),
+        "gi_loss_workspace_bytes": ([i64], sz),
+        "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
+        "gi_adam_step": ([i64, i32, P, P, P, P, P, f32, f32, f32, i32, i32, P], i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        if not t.is_cuda:
+            raise ValueError("device tensor expected")
+        if not t.is_contiguous():
+            raise ValueError("contiguous tensor expected")
+        return ctypes.c_void_p(t.data_ptr())
+    return ctypes.c_void_p(int(t))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(st: int, what: str):
+    if st != GI_OK:
+        raise GiError(st, what)
+
+
+def status_string(st: int) -> str:
+    return load().gi_status_string(int(st)).decode()
+
+
+def version() -> str:
+    return load().gi_version().decode()
+
+
+def num_tiles(d: gi_desc) -> int:
+    return int(load().gi_num_tiles(ctypes.byref(d)))
+
+
+def gi_preprocess(d, n, params, logit, records, opacity, pixbox, counts, stream=None):
+    _check(load().gi_preprocess(ctypes.byref(d), int(n), _ptr(params), _ptr(logit), _ptr(records),
+                                _ptr(opacity), _ptr(pixbox), _ptr(counts), _stream(stream)), "gi_preprocess")
+
+
+def gi_bin_sort_workspace_bytes(d, n, capacity) -> int:
+    return int(load().gi_bin_sort_workspace_bytes(ctypes.byref(d), int(n), int(capacity)))
+
+
+def gi_bin_sort(d, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
+                sync_count=False, stream=None):
+    """Returns M (host int) when sync_count, else None.  Raises GiError(GI_ERR_CAPACITY) on overflow
+    when sync_count."""
+    h = ctypes.c_int64(-1)
+    st = load().gi_bin_sort(ctypes.byref(d), int(n), _ptr(pixbox), _ptr(counts), _ptr(offsets), _ptr(keys),
+                            _ptr(vals), _ptr(ranges), int(capacity), _ptr(d_num),
+                            ctypes.byref(h) if sync_count else None, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gi_bin_sort")
+    return int(h.value) if sync_count else None
+
+
+def gi_render_fwd(d, n, records, opacity, pixbox, ranges, vals, background, image, t_final, last, stream=None):
+    _check(load().gi_render_fwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(pixbox),
+                                _ptr(ranges), _ptr(vals), _ptr(background), _ptr(image), _ptr(t_final),
+                                _ptr(last), _stream(stream)), "gi_render_fwd")
+
+
+def gi_render_bwd(d, n, records, opacity, logit, pixbox, ranges, vals, background, t_final, last, dL_dimage,
+                  dparams, dlogit, dbackground, stream=None):
+    _check(load().gi_render_bwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(logit),
+                                _ptr(pixbox), _ptr(ranges), _ptr(vals), _ptr(background), _ptr(t_final),
+                                _ptr(last), _ptr(dL_dimage), _ptr(dparams), _ptr(dlogit), _ptr(dbackground),
+                                _stream(stream)), "gi_render_bwd")
+
+
+def gi_loss_workspace_bytes(count) -> int:
+    return int(load().gi_loss_workspace_bytes(int(count)))
+
+
+def gi_loss_l2(count, image, target, dL_dimage, d_loss, workspace, stream=None):
+    _check(load().gi_loss_l2(int(count), _ptr(image), _ptr(target), _ptr(dL_dimage), _ptr(d_loss),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gi_loss_l2")
+
+
+def gi_adam_step(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_grad, stream=None):
+    lr_arr = (ctypes.c_float * int(row_len))(*[float(x) for x in lr])
+    _check(load().gi_adam_step(int(rows), int(row_len), _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr_arr,
+                               float(beta1), float(beta2), float(eps), int(step), int(zero_grad),
+                               _stream(stream)), "gi_adam_step")

@@ -1,0 +1,163 @@
+"""Buffers and call sequence for rendering and fitting with libgi.
+
+Torch provides device memory and the stream; every step below is one call of
+the C ABI (through :mod:`.gi`):
+
+  render : gi_preprocess -> gi_bin_sort -> gi_render_fwd
+  fit    : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
+
+uint32/uint16 device arrays are held in int32/int16 tensors (same bytes).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import gi
+
+# Default per-slot learning rates (pixels for the mean and the Cholesky factor,
+# colour units for the colours).
+DEFAULT_LR = (0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005)
+
+
+class Raster:
+    """Device buffers for one (W, H, n, mode) problem."""
+
+    def __init__(self, width, height, n, mode=gi.MODE_SUM, capacity=None, device="cuda"):
+        self.W, self.H, self.n, self.mode = int(width), int(height), int(n), int(mode)
+        self.desc = gi.desc(self.W, self.H, self.mode)
+        self.T = gi.num_tiles(self.desc)
+        self.device = device
+        alpha = self.mode == gi.MODE_ALPHA
+        dev = torch.device(device)
+        self.records = torch.empty((max(self.n, 1), 8), dtype=torch.float32, device=dev)
+        self.opacity = torch.empty(max(self.n, 1), dtype=torch.float32, device=dev) if alpha else None
+        self.pixbox = torch.empty((max(self.n, 1), 4), dtype=torch.int16, device=dev)
+        self.counts = torch.empty(max(self.n, 1), dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(self.n + 1, dtype=torch.int32, device=dev)
+        self.ranges = torch.empty((max(self.T, 1), 2), dtype=torch.int32, device=dev)
+        self.d_num = torch.empty(1, dtype=torch.int32, device=dev)
+        self.image = torch.empty((3, self.H, self.W), dtype=torch.float32, device=dev)
+        self.t_final = torch.empty((self.H, self.W), dtype=torch.float32, device=dev) if alpha else None
+        self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev) if alpha else None
+        self.capacity = 0
+        self.keys = self.vals = self.ws = None
+        self.M = None
+        if capacity is not None:
+            self.set_capacity(capacity)
+
+    def set_capacity(self, capacity):
+        capacity = int(capacity)
+        dev = torch.device(self.device)
+        self.capacity = capacity
+        self.keys = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+        self.vals = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+        nbytes = gi.gi_bin_sort_workspace_bytes(self.desc, self.n, capacity)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    # -- steps ---------------------------------------------------------------------------------
+    def preprocess(self, params, logit=None, stream=None):
+        gi.gi_preprocess(self.desc, self.n, params, logit, self.records, self.opacity, self.pixbox, self.counts,
+                         stream)
+
+    def bin(self, sync=False, slack=1.25, stream=None):
+        """Bin and sort.  sync: read M back (one host wait) and grow the buffers if needed."""
+        if self.keys is None:
+            self.set_capacity(max(1024, 4 * self.n))
+            sync = True
+        if not sync:
+            gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
+                           self.ranges, self.capacity, self.d_num, self.ws, sync_count=False, stream=stream)
+            return None
+        try:
+            M = gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
+                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream)
+        except gi.GiError as e:
+            if e.status != gi.GI_ERR_CAPACITY:
+                raise
+            M = int(self.d_num.cpu().view(torch.int32).item()) & 0xFFFFFFFF
+            self.set_capacity(int(M * slack) + 1024)
+            M = gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
+                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream)
+        self.M = M
+        return M
+
+    def forward(self, background=None, stream=None):
+        gi.gi_render_fwd(self.desc, self.n, self.records, self.opacity, self.pixbox, self.ranges, self.vals,
+                         background, self.image, self.t_final, self.last, stream)
+        return self.image
+
+    def backward(self, dL_dimage, dparams, logit=None, background=None, dlogit=None, dbackground=None,
+                 stream=None):
+        gi.gi_render_bwd(self.desc, self.n, self.records, self.opacity, logit, self.pixbox, self.ranges,
+                         self.vals, background, self.t_final, self.last, dL_dimage, dparams, dlogit,
+                         dbackground, stream)
+
+    def render(self, params, logit=None, background=None, sync=True):
+        self.preprocess(params, logit)
+        self.bin(sync=sync)
+        return self.forward(background)
+
+
+class Fitter:
+    """Fits Gaussians to a target image with L2 loss and Adam (all steps in libgi)."""
+
+    def __init__(self, target, params, logit=None, background=None, lr=DEFAULT_LR, lr_logit=0.05, lr_bg=0.01,
+                 betas=(0.9, 0.999), eps=1e-8, capacity_slack=1.5):
+        self.target = target.contiguous()
+        _, H, W = self.target.shape
+        self.params = params.contiguous().clone()
+        self.n = self.params.shape[0]
+        alpha = logit is not None
+        self.raster = Raster(W, H, self.n, gi.MODE_ALPHA if alpha else gi.MODE_SUM, device=self.params.device)
+        dev = self.params.device
+        self.grad = torch.zeros_like(self.params)
+        self.m = torch.zeros_like(self.params)
+        self.v = torch.zeros_like(self.params)
+        self.logit = logit.contiguous().clone() if alpha else None
+        self.bg = background.contiguous().clone() if alpha else None
+        if alpha:
+            self.g_logit, self.m_logit, self.v_logit = (torch.zeros_like(self.logit) for _ in range(3))
+            self.g_bg, self.m_bg, self.v_bg = (torch.zeros(4, dtype=torch.float32, device=dev) for _ in range(3))
+            self.bg4 = torch.zeros(4, dtype=torch.float32, device=dev)
+            self.bg4[:3] = self.bg
+        self.lr, self.lr_logit, self.lr_bg = tuple(lr), lr_logit, lr_bg
+        self.betas, self.eps = betas, eps
+        self.dL = torch.empty_like(self.target)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.loss_ws = torch.empty(gi.gi_loss_workspace_bytes(self.target.numel()), dtype=torch.uint8, device=dev)
+        self.step_count = 0
+        self.slack = capacity_slack
+        # size the tile-pair buffers once, with room for the Gaussians to spread
+        self.raster.preprocess(self.params, self.logit)
+        M = self.raster.bin(sync=True)
+        self.raster.set_capacity(int(M * capacity_slack) + 4096)
+
+    def check_capacity(self):
+        """Host wait: grow the pair buffers when the last binning came near (or over) capacity."""
+        M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
+        if M > 0.8 * self.raster.capacity:
+            self.raster.set_capacity(int(M * self.slack) + 4096)
+            return True
+        return False
+
+    def step(self):
+        r = self.raster
+        bg = self.bg4 if self.logit is not None else None
+        r.preprocess(self.params, self.logit)
+        r.bin(sync=False)
+        r.forward(bg)
+        gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
+        if self.logit is None:
+            r.backward(self.dL, self.grad)
+        else:
+            r.backward(self.dL, self.grad, logit=self.logit, background=bg, dlogit=self.g_logit,
+                       dbackground=self.g_bg)
+        self.step_count += 1
+        b1, b2 = self.betas
+        gi.gi_adam_step(self.n, 8, self.params, self.grad, self.m, self.v, self.lr, b1, b2, self.eps,
+                        self.step_count, 1)
+        if self.logit is not None:
+            gi.gi_adam_step(self.n, 1, self.logit, self.g_logit, self.m_logit, self.v_logit, [self.lr_logit],
+                            b1, b2, self.eps, self.step_count, 1)
+            gi.gi_adam_step(1, 4, self.bg4, self.g_bg, self.m_bg, self.v_bg, [self.lr_bg] * 3 + [0.0],
+                            b1, b2, self.eps, self.step_count, 1)

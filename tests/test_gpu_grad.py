@@ -1,0 +1,139 @@
+"""GPU backward vs the oracle's analytic gradients (<= 1e-4 under the |contribution|-weighted
+metric), sum and alpha modes, small cases and full-size workloads with a sparse dL/dI."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (GRAD_TOL, dev, gpu_last_to_index, grad_error, pixel_tile_start, require_gpu,
+                      sample_pixels, u32)
+from rasterizer_gaussian_raster_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _grad_sum(W, H, params, G):
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    r = Raster(W, H, params.shape[0])
+    r.render(dev(params))
+    dp = torch.zeros((params.shape[0], 8), dtype=torch.float32, device="cuda")
+    r.backward(dev(G.astype(np.float32)), dp)
+    torch.cuda.synchronize()
+    return dp.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed,W,H,n,sig,margin", [
+    (151, 16, 16, 5, (1.0, 5.0), 0),
+    (152, 64, 64, 256, (0.5, 6.0), 0),
+    (153, 100, 37, 600, (0.3, 12.0), 20),
+    (154, 17, 33, 80, (0.3, 8.0), 10),
+    (155, 257, 129, 1500, (0.3, 40.0), 50),
+])
+def test_sum_grad_random(seed, W, H, n, sig, margin):
+    require_gpu()
+    import oracle
+    p = synth.random_case(seed, W, H, n, sigma=sig, margin=margin)
+    G = np.random.default_rng(seed).normal(size=(3, H, W)).astype(np.float32)
+    got = _grad_sum(W, H, p, G)
+    ref, A = oracle.grad_sum(W, H, p.astype(np.float64), G.astype(np.float64))
+    err = grad_error(got, ref, A)
+    print(f"sum grad {W}x{H} n={n}: max rel err {err:.3e}")
+    assert err <= GRAD_TOL
+
+
+@pytest.mark.parametrize("name,nrand,ntiles", [("tiny_fit_64x64", 0, 0), ("kodak_768x512_50k", 4096, 8),
+                                               ("div2k_1020x678_70k", 2048, 4)])
+def test_sum_grad_workloads(name, nrand, ntiles):
+    """Every Gaussian's gradient at full size; dL/dI is nonzero on sampled pixels only."""
+    require_gpu()
+    import oracle
+    w = synth.make_workload(name)
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    rng = np.random.default_rng(wl.seed + 50)
+    if nrand == 0:
+        G = rng.normal(size=(3, H, W)).astype(np.float32)
+    else:
+        G = np.zeros((3, H, W), np.float32)
+        pix = sample_pixels(W, H, nrand, ntiles, seed=wl.seed + 60)
+        G[:, pix[:, 0], pix[:, 1]] = rng.normal(size=(3, len(pix)))
+    got = _grad_sum(W, H, w["params"], G)
+    ref, A = oracle.grad_sum(W, H, w["params"].astype(np.float64), G.astype(np.float64))
+    err = grad_error(got, ref, A)
+    print(f"{name} grad: max rel err {err:.3e}")
+    assert err <= GRAD_TOL
+
+
+def test_sum_grad_culled_rows_are_zero():
+    require_gpu()
+    W, H = 48, 40
+    p = synth.random_case(161, W, H, 30)
+    p[0, 0] = np.nan
+    p[1, 2] = 0.0
+    p[2, 6] = np.inf
+    G = np.ones((3, H, W), np.float32)
+    got = _grad_sum(W, H, p, G)
+    assert np.all(got[:3] == 0)
+    assert np.all(np.isfinite(got))
+
+
+# ------------------------------------------------------------------------------------------------
+# alpha mode
+# ------------------------------------------------------------------------------------------------
+
+def _alpha_case_grad(W, H, p, lg, bg, G):
+    import oracle
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    n = p.shape[0]
+    r = Raster(W, H, n, gi.MODE_ALPHA)
+    P, L, B = dev(p), dev(lg), dev(bg)
+    r.render(P, L, B)
+    dp = torch.zeros((n, 8), dtype=torch.float32, device="cuda")
+    dl = torch.zeros(n, dtype=torch.float32, device="cuda")
+    db = torch.zeros(3, dtype=torch.float32, device="cuda")
+    r.backward(dev(G.astype(np.float32)), dp, logit=L, background=B, dlogit=dl, dbackground=db)
+    torch.cuda.synchronize()
+    vals = u32(r.vals)[: r.M].astype(np.int64)
+    ranges = u32(r.ranges).astype(np.int64)
+    yy, xx = np.mgrid[0:H, 0:W]
+    pix = np.stack([yy.ravel(), xx.ravel()], 1)
+    last = u32(r.last).astype(np.int64).reshape(-1)
+    fl = gpu_last_to_index(last, vals, pixel_tile_start(W, ranges, pix))
+    ref, rl, rb, A = oracle.grad_alpha(W, H, p.astype(np.float64), lg.astype(np.float64), bg.astype(np.float64),
+                                       G.astype(np.float64), force_last=fl)
+    got = np.concatenate([dp.cpu().numpy(), dl.cpu().numpy()[:, None]], 1)
+    err = grad_error(got, np.concatenate([ref, rl[:, None]], 1), A)
+    tf = r.t_final.cpu().numpy()
+    abg = np.abs(G.astype(np.float64) * tf[None]).sum(axis=(1, 2))
+    berr = np.max(np.abs(db.cpu().numpy() - rb) / np.maximum(abg, 1e-30))
+    print(f"alpha grad {W}x{H} n={n}: max rel err {err:.3e}, bg rel err {berr:.3e}")
+    assert err <= GRAD_TOL
+    assert berr <= GRAD_TOL
+
+
+@pytest.mark.parametrize("seed,W,H,n", [(171, 16, 16, 6), (172, 64, 64, 256), (173, 100, 37, 400)])
+def test_alpha_grad_random(seed, W, H, n):
+    require_gpu()
+    p, lg, bg = synth.random_case(seed, W, H, n, sigma=(0.5, 8.0), alpha=True, margin=10)
+    G = np.random.default_rng(seed).normal(size=(3, H, W)).astype(np.float32)
+    _alpha_case_grad(W, H, p, lg, bg, G)
+
+
+def test_alpha_grad_termination_stress():
+    require_gpu()
+    rng = np.random.default_rng(181)
+    n = 600
+    W = H = 48
+    p = np.zeros((n, 8), np.float32)
+    p[:, 0] = rng.uniform(0, W, n)
+    p[:, 1] = rng.uniform(0, H, n)
+    p[:, 2] = rng.uniform(4, 12, n)
+    p[:, 3] = rng.normal(0, 0.5, n)
+    p[:, 4] = rng.uniform(4, 12, n)
+    p[:, 5:] = rng.uniform(0, 1, (n, 3))
+    o = rng.uniform(0.5, 0.95, n)
+    lg = np.log(o / (1 - o)).astype(np.float32)
+    lg[:5] = 9.0                       # clamped opacity: zero logit gradient
+    bg = np.array([0.2, 0.4, 0.6], np.float32)
+    G = rng.normal(size=(3, H, W)).astype(np.float32)
+    _alpha_case_grad(W, H, p, lg, bg, G)
