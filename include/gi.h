@@ -228,9 +228,11 @@ gi_status gi_loss_l2(int64_t count, const float *image, const float *target, flo
  *   g = 0 afterwards (ready for the next accumulation).
  *   p, g, m, v  device float [rows][row_len], updated in place.
  *   lr          host float [row_len], 1 <= row_len <= 16.
+ *   beta1, beta2, eps  host doubles: 1 - beta and the bias corrections are formed
+ *               in double before rounding to fp32 (1 - 0.999f is 1.3e-5 off 0.001).
  */
 gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v,
-                       const float *lr, float beta1, float beta2, float eps, int32_t step,
+                       const float *lr, double beta1, double beta2, double eps, int32_t step,
                        int32_t zero_grad, void *stream);
 
 #ifdef __cplusplus

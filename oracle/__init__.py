@@ -64,11 +64,11 @@ def _load():
     lib.oracle_cutoff_margin.restype = ctypes.c_double
     lib.oracle_render_sum.argtypes = [i32, i32, i64, P, P, i64, i32, P, P]
     lib.oracle_render_sum.restype = None
-    lib.oracle_grad_sum.argtypes = [i32, i32, i64, P, P, i32, P, P]
+    lib.oracle_grad_sum.argtypes = [i32, i32, i64, P, P, i32, P, P, P]
     lib.oracle_grad_sum.restype = None
     lib.oracle_render_alpha.argtypes = [i32, i32, i64, P, P, P, P, i64, P, P, P, P, P, P]
     lib.oracle_render_alpha.restype = None
-    lib.oracle_grad_alpha.argtypes = [i32, i32, i64, P, P, P, P, P, P, P, P, P]
+    lib.oracle_grad_alpha.argtypes = [i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_grad_alpha.restype = None
     lib.oracle_loss_l2.argtypes = [i64, P, P, P]
     lib.oracle_loss_l2.restype = ctypes.c_double
@@ -166,15 +166,17 @@ def render_sum(W, H, params, pixels=None, cutoff=True):
     return out, sabs
 
 
-def grad_sum(W, H, params, dL_dI, cutoff=True):
-    """(dparams [N,8], abs-sum [N,8]) for L = <dL_dI, I>."""
+def grad_sum(W, H, params, dL_dI, cutoff=True, with_cond=False):
+    """(dparams [N,8], abs-sum [N,8]) for L = <dL_dI, I>; with_cond also returns the running-error
+    scale [N,8] (inner sums of each contribution taken over absolute values)."""
     par = _f64(params).reshape(-1, 8)
     G = _f64(dL_dI).reshape(3, H, W)
     n = par.shape[0]
     d = np.zeros((n, 8))
     a = np.zeros((n, 8))
-    _load().oracle_grad_sum(W, H, n, _p(par), _p(G), int(bool(cutoff)), _p(d), _p(a))
-    return d, a
+    c = np.zeros((n, 8))
+    _load().oracle_grad_sum(W, H, n, _p(par), _p(G), int(bool(cutoff)), _p(d), _p(a), _p(c))
+    return (d, a, c) if with_cond else (d, a)
 
 
 def render_alpha(W, H, params, logit, bg, pixels=None, force_last=None):
@@ -200,8 +202,9 @@ def render_alpha(W, H, params, logit, bg, pixels=None, force_last=None):
     return {"image": out, "sabs": sabs, "t_final": tf, "last": last, "ambiguous": amb}
 
 
-def grad_alpha(W, H, params, logit, bg, dL_dI, force_last=None):
-    """(dparams [N,8], dlogit [N], dbg [3], abs-sum [N,9]) for L = <dL_dI, C>."""
+def grad_alpha(W, H, params, logit, bg, dL_dI, force_last=None, with_cond=False):
+    """(dparams [N,8], dlogit [N], dbg [3], abs-sum [N,9]) for L = <dL_dI, C>; with_cond also
+    returns the running-error scale [N,9]."""
     par = _f64(params).reshape(-1, 8)
     lg = _f64(logit).reshape(-1)
     b = _f64(bg).reshape(3)
@@ -212,9 +215,10 @@ def grad_alpha(W, H, params, logit, bg, dL_dI, force_last=None):
     dl = np.zeros(n)
     dbg = np.zeros(3)
     a = np.zeros((n, 9))
+    c = np.zeros((n, 9))
     _load().oracle_grad_alpha(W, H, n, _p(par), _p(lg), _p(b), _p(G), _p(fl), _p(d), _p(dl), _p(dbg),
-                              _p(a))
-    return d, dl, dbg, a
+                              _p(a), _p(c))
+    return (d, dl, dbg, a, c) if with_cond else (d, dl, dbg, a)
 
 
 def loss_l2(image, target):

@@ -187,6 +187,21 @@ static double gauss_q(const gauss64 *g, int i, int j, double *dx_out, double *dy
 /* Derivatives of q w.r.t. (mux, muy, l11, l21, l22), by matrix calculus:
  *   dq/dmu = -2 Sigma^-1 d,
  *   dq/dL  = -2 Sigma^-1 d d^T Sigma^-1 L  (lower-triangular entries). */
+/* The same derivatives with every inner sum replaced by the sum of the absolute
+ * values of its terms (a running-error scale for fp32 evaluations of dq). */
+static void gauss_dq_abs(const gauss64 *g, double dx, double dy, double dqa[5])
+{
+    double zx = fabs(g->pxx * dx) + fabs(g->pxy * dy);
+    double zy = fabs(g->pxy * dx) + fabs(g->pyy * dy);
+    dqa[0] = 2.0 * zx;
+    dqa[1] = 2.0 * zy;
+    double zl0 = zx * fabs(g->l11) + zy * fabs(g->l21);
+    double zl1 = zy * fabs(g->l22);
+    dqa[2] = 2.0 * zx * zl0;
+    dqa[3] = 2.0 * zy * zl0;
+    dqa[4] = 2.0 * zy * zl1;
+}
+
 static void gauss_dq(const gauss64 *g, double dx, double dy, double dq[5])
 {
     double zx = g->pxx * dx + g->pxy * dy;   /* z = Sigma^-1 d */
@@ -332,19 +347,21 @@ void oracle_render_sum(int W, int H, int64_t n, const double *params, const int3
 
 /* Gradient of L = sum_{k,p} G_k(p) I_k(p) for the sum image (G = dL/dI at
  * every pixel, [3,H,W]).  dparams[n,8] and, if given, the per-entry sum of
- * |per-pair contribution| aabs[n,8]. */
+ * |per-pair contribution| aabs[n,8] and the running-error scale acond[n,8]:
+ * the same sum with every inner sum of a contribution (g.c, Sigma^-1 d, ...)
+ * taken over absolute values. */
 void oracle_grad_sum(int W, int H, int64_t n, const double *params, const double *G, int cutoff,
-                     double *dparams, double *aabs)
+                     double *dparams, double *aabs, double *acond)
 {
     const int nt = omp_get_max_threads();
     cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
     gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
     for (int64_t g = 0; g < n; ++g) { cs[g] = cutoff_setup(params + 8*g, NULL, W, H); gs[g] = gauss_setup(params + 8*g, NULL); }
-    double *part = (double *)calloc((size_t)nt * 16 * (n > 0 ? n : 1), sizeof(double));
+    double *part = (double *)calloc((size_t)nt * 24 * (n > 0 ? n : 1), sizeof(double));
     const int64_t HW = (int64_t)H * W;
     #pragma omp parallel
     {
-        double *mine = part + (size_t)omp_get_thread_num() * 16 * (n > 0 ? n : 1);
+        double *mine = part + (size_t)omp_get_thread_num() * 24 * (n > 0 ? n : 1);
         #pragma omp for schedule(dynamic, 4)
         for (int i = 0; i < H; ++i)
             for (int j = 0; j < W; ++j) {
@@ -359,19 +376,31 @@ void oracle_grad_sum(int W, int H, int64_t n, const double *params, const double
                     double gc = gk[0]*gs[g].c[0] + gk[1]*gs[g].c[1] + gk[2]*gs[g].c[2];
                     double dq[5];
                     gauss_dq(&gs[g], dx, dy, dq);
-                    double contrib[8];
-                    for (int t = 0; t < 5; ++t) contrib[t] = gc * w * (-0.5) * dq[t];
-                    for (int k = 0; k < 3; ++k) contrib[5+k] = gk[k] * w;
-                    for (int t = 0; t < 8; ++t) { mine[16*g + t] += contrib[t]; mine[16*g + 8 + t] += fabs(contrib[t]); }
+                    double dqa[5];
+                    gauss_dq_abs(&gs[g], dx, dy, dqa);
+                    double gca = fabs(gk[0]*gs[g].c[0]) + fabs(gk[1]*gs[g].c[1]) + fabs(gk[2]*gs[g].c[2]);
+                    double contrib[8], cond[8];
+                    for (int t = 0; t < 5; ++t) { contrib[t] = gc * w * (-0.5) * dq[t]; cond[t] = gca * w * 0.5 * dqa[t]; }
+                    for (int k = 0; k < 3; ++k) { contrib[5+k] = gk[k] * w; cond[5+k] = fabs(contrib[5+k]); }
+                    for (int t = 0; t < 8; ++t) {
+                        mine[24*g + t] += contrib[t];
+                        mine[24*g + 8 + t] += fabs(contrib[t]);
+                        mine[24*g + 16 + t] += cond[t];
+                    }
                 }
             }
     }
     for (int64_t g = 0; g < n; ++g)
         for (int t = 0; t < 8; ++t) {
-            double s = 0, a = 0;
-            for (int th = 0; th < nt; ++th) { s += part[(size_t)th*16*n + 16*g + t]; a += part[(size_t)th*16*n + 16*g + 8 + t]; }
+            double s = 0, a = 0, c = 0;
+            for (int th = 0; th < nt; ++th) {
+                s += part[(size_t)th*24*n + 24*g + t];
+                a += part[(size_t)th*24*n + 24*g + 8 + t];
+                c += part[(size_t)th*24*n + 24*g + 16 + t];
+            }
             dparams[8*g + t] = s;
             if (aabs) aabs[8*g + t] = a;
+            if (acond) acond[8*g + t] = c;
         }
     free(part); free(cs); free(gs);
 }
@@ -428,17 +457,18 @@ void oracle_render_alpha(int W, int H, int64_t n, const double *params, const do
 /* Gradient of L = sum G_k(p) C_k(p) for the alpha image at every pixel, with
  * each pixel's stopping point held fixed (force_last as above, or the oracle's
  * own stop when NULL).  dparams[n,8], dlogit[n], dbg[3]; aabs[n,9] (8 params +
- * logit) is the per-entry sum of |per-pair contribution|.  The suffix sums are
- * formed directly from the stored contributors (no division). */
+ * logit) is the per-entry sum of |per-pair contribution| and acond[n,9] the
+ * running-error scale (inner sums over absolute values, as in oracle_grad_sum).
+ * The suffix sums are formed directly from the stored contributors (no division). */
 void oracle_grad_alpha(int W, int H, int64_t n, const double *params, const double *logit, const double *bg,
                        const double *G, const int64_t *force_last,
-                       double *dparams, double *dlogit, double *dbg, double *aabs)
+                       double *dparams, double *dlogit, double *dbg, double *aabs, double *acond)
 {
     const int nt = omp_get_max_threads();
     cutoff32 *cs = (cutoff32 *)malloc(sizeof(cutoff32) * (n > 0 ? n : 1));
     gauss64 *gs = (gauss64 *)malloc(sizeof(gauss64) * (n > 0 ? n : 1));
     for (int64_t g = 0; g < n; ++g) { cs[g] = cutoff_setup(params + 8*g, logit + g, W, H); gs[g] = gauss_setup(params + 8*g, logit + g); }
-    const size_t stride = 20;   /* 9 sums + 9 abs sums + pad */
+    const size_t stride = 28;   /* 9 sums + 9 abs sums + 9 running-error scales + pad */
     double *part = (double *)calloc((size_t)nt * stride * (n > 0 ? n : 1), sizeof(double));
     double *pbg = (double *)calloc((size_t)nt * 3, sizeof(double));
     const int64_t HW = (int64_t)H * W;
@@ -479,33 +509,47 @@ void oracle_grad_alpha(int W, int H, int64_t n, const double *params, const doub
             for (int k = 0; k < 3; ++k) pbg[3*th + k] += gk[k] * T;
             /* backward: S_m = sum_{r>m} c_r alpha_r T_r + T_final bg, per channel */
             double S[3] = {T * bg[0], T * bg[1], T * bg[2]};
+            double Sa[3] = {T * fabs(bg[0]), T * fabs(bg[1]), T * fabs(bg[2])};
             for (int64_t m = K - 1; m >= 0; --m) {
                 const gauss64 *gg = &gs[idx[m]];
                 double w = wv[m], Tm = Tv[m], al = gg->o * w;
-                double dC_dal = 0.0;   /* sum_k G_k dC_k/dalpha */
-                for (int k = 0; k < 3; ++k) dC_dal += gk[k] * (Tm * gg->c[k] - S[k] / (1.0 - al));
-                double contrib[9];
+                double dC_dal = 0.0, dC_dal_a = 0.0;   /* sum_k G_k dC_k/dalpha, and over |terms| */
+                for (int k = 0; k < 3; ++k) {
+                    dC_dal += gk[k] * (Tm * gg->c[k] - S[k] / (1.0 - al));
+                    dC_dal_a += fabs(gk[k]) * (Tm * fabs(gg->c[k]) + Sa[k] / (1.0 - al));
+                }
+                double contrib[9], cond[9];
                 double dx, dy;
                 gauss_q(gg, i, j, &dx, &dy);
-                double dq[5];
+                double dq[5], dqa[5];
                 gauss_dq(gg, dx, dy, dq);
+                gauss_dq_abs(gg, dx, dy, dqa);
                 /* alpha = o w, w = exp(-q/2) */
-                for (int t = 0; t < 5; ++t) contrib[t] = dC_dal * gg->o * w * (-0.5) * dq[t];
-                for (int k = 0; k < 3; ++k) contrib[5+k] = gk[k] * al * Tm;
+                for (int t = 0; t < 5; ++t) {
+                    contrib[t] = dC_dal * gg->o * w * (-0.5) * dq[t];
+                    cond[t] = dC_dal_a * gg->o * w * 0.5 * dqa[t];
+                }
+                for (int k = 0; k < 3; ++k) { contrib[5+k] = gk[k] * al * Tm; cond[5+k] = fabs(contrib[5+k]); }
                 contrib[8] = gg->clamped ? 0.0 : dC_dal * w * gg->o * (1.0 - gg->o);
+                cond[8] = gg->clamped ? 0.0 : dC_dal_a * w * gg->o * (1.0 - gg->o);
                 double *dst = mine + stride * idx[m];
-                for (int t = 0; t < 9; ++t) { dst[t] += contrib[t]; dst[9 + t] += fabs(contrib[t]); }
-                for (int k = 0; k < 3; ++k) S[k] += gg->c[k] * al * Tm;
+                for (int t = 0; t < 9; ++t) { dst[t] += contrib[t]; dst[9 + t] += fabs(contrib[t]); dst[18 + t] += cond[t]; }
+                for (int k = 0; k < 3; ++k) { S[k] += gg->c[k] * al * Tm; Sa[k] += fabs(gg->c[k]) * al * Tm; }
             }
         }
         free(idx); free(wv); free(Tv);
     }
     for (int64_t g = 0; g < n; ++g) {
         for (int t = 0; t < 9; ++t) {
-            double s = 0, a = 0;
-            for (int th = 0; th < nt; ++th) { s += part[(size_t)th*stride*n + stride*g + t]; a += part[(size_t)th*stride*n + stride*g + 9 + t]; }
+            double s = 0, a = 0, c = 0;
+            for (int th = 0; th < nt; ++th) {
+                s += part[(size_t)th*stride*n + stride*g + t];
+                a += part[(size_t)th*stride*n + stride*g + 9 + t];
+                c += part[(size_t)th*stride*n + stride*g + 18 + t];
+            }
             if (t < 8) dparams[8*g + t] = s; else dlogit[g] = s;
             if (aabs) aabs[9*g + t] = a;
+            if (acond) acond[9*g + t] = c;
         }
     }
     for (int k = 0; k < 3; ++k) { double s = 0; for (int th = 0; th < nt; ++th) s += pbg[3*th + k]; dbg[k] = s; }

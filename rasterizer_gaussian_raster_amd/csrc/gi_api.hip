@@ -132,9 +132,9 @@ gi_status gi_loss_l2(int64_t count, const float *image, const float *target, flo
 }
 
 gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v, const float *lr,
-                       float beta1, float beta2, float eps, int32_t step, int32_t zero_grad, void *stream) {
+                       double beta1, double beta2, double eps, int32_t step, int32_t zero_grad, void *stream) {
     if (rows < 0 || row_len < 1 || row_len > 16 || step < 1 || !lr) return GI_ERR_INVALID_ARG;
-    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps >= 0.0f))
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0))
         return GI_ERR_INVALID_ARG;
     if (rows > 0) {
         if (!p || !g || !m || !v) return GI_ERR_INVALID_ARG;

@@ -51,6 +51,6 @@ size_t loss_workspace_bytes(int64_t count);
 hipError_t launch_loss_l2(int64_t count, const float *image, const float *target, float *dL_dimage, float *d_loss,
                           void *ws, hipStream_t s);
 hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, float *v, const float *lr,
-                       float beta1, float beta2, float eps, int step, int zero_grad, hipStream_t s);
+                       double beta1, double beta2, double eps, int step, int zero_grad, hipStream_t s);
 
 }  // namespace gi

@@ -1,7 +1,10 @@
 // k_binning.hip -- tile lists from per-Gaussian pixel boxes.
 //
-//   1. k_group_sums   : per 256-Gaussian group, sum of tile counts (u64).
-//   2. k_group_scan   : one workgroup scans the group sums -> group bases, M.
+//   1. k_group_sums   : per 256-Gaussian group, sum of tile counts (u64); clears
+//                       the tile ranges.
+//   2. k_group_scan   : one workgroup scans the group sums -> group bases, M
+//                       (only for more than 2048 groups; below that each emit
+//                       workgroup adds up the sums before it itself).
 //   3. k_emit         : per group, offsets[] and one (tile id, index) pair per
 //                       covered tile, emitted in (index, tile row, tile column)
 //                       order; the group's pairs are spread evenly over its
@@ -13,7 +16,8 @@
 //      each key's rank among equal digits is found with wave ballots in key
 //      order, so the sort is stable and each tile list ends up in ascending
 //      Gaussian index.
-//   5. k_ranges       : per tile, [start, end) by binary search of the sorted ids.
+//   5. k_ranges       : one thread per sorted pair marks where each tile's run
+//                       starts and ends.
 //
 // Binning is the tile-binned scheme of the FlashImgs viewer ("Web viewer":
 // tile-binned compute) with fvdb's 16-pixel tiles (tile_size).  All steps are
@@ -24,7 +28,8 @@
 namespace gi {
 
 constexpr int kSortThreads = 256;
-constexpr int kSortIters = 16;
+constexpr int kSortIters = 4;
+constexpr int kMaxRedundantGroups = 2048;              // emit sums the group totals itself up to this
 constexpr int kSortChunk = kSortThreads * kSortIters;   // keys per sort block
 constexpr int kScanItems = 16;
 constexpr int kScanChunk = 256 * kScanItems;           // table entries per scan block
@@ -64,9 +69,13 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *t
 // ---------------------------------------------------------------------------
 // 1-3: counts -> offsets -> emitted pairs
 // ---------------------------------------------------------------------------
+// Also clears the tile ranges (tiles that receive no pair keep (0, 0)).
 __global__ __launch_bounds__(256) void k_group_sums(int n, const uint32_t *__restrict__ counts,
-                                                    unsigned long long *__restrict__ part) {
+                                                    unsigned long long *__restrict__ part, int ntiles,
+                                                    uint2 *__restrict__ ranges) {
     __shared__ unsigned long long sm[4];
+    for (int t = blockIdx.x * 256 + threadIdx.x; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
+    if (n == 0) return;
     const int g = blockIdx.x * 256 + threadIdx.x;
     unsigned long long c = g < n ? counts[g] : 0ull;
     unsigned long long tot;
@@ -102,25 +111,54 @@ __global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long lo
     }
 }
 
-__global__ __launch_bounds__(256) void k_emit(int n, int tiles_x, const uint32_t *__restrict__ counts,
+// part[] holds either the exclusive group bases (scanned by k_group_scan) or, when
+// `redundant`, the raw group sums: then every block adds up the sums before it
+// (and all of them for M) itself, and block 0 publishes M -- one launch fewer.
+__global__ __launch_bounds__(256) void k_emit(int n, int ngroups, int redundant, long long capacity, int tiles_x,
+                                              const uint32_t *__restrict__ counts,
                                               const uint2 *__restrict__ pixbox,
                                               const unsigned long long *__restrict__ part,
-                                              const BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
+                                              BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
+                                              uint32_t *__restrict__ d_num,
                                               uint32_t *__restrict__ keys, uint32_t *__restrict__ vals) {
     __shared__ uint32_t excl[257];
     __shared__ uint2 box[256];
     __shared__ uint32_t sm[4];
+    __shared__ unsigned long long sm64[8];
     const int tid = threadIdx.x;
     const int g = blockIdx.x * 256 + tid;
     const uint32_t c = g < n ? counts[g] : 0u;
     uint32_t tot;
     const uint32_t local = block_exclusive_scan<uint32_t, 256>(c, sm, &tot);
-    const unsigned long long base = part[blockIdx.x];
+    unsigned long long base, total;
+    if (redundant) {
+        unsigned long long before = 0, all = 0;
+        for (int i = tid; i < ngroups; i += 256) {
+            const unsigned long long v = part[i];
+            all += v;
+            before += i < (int)blockIdx.x ? v : 0ull;
+        }
+        unsigned long long tb, ta;
+        block_exclusive_scan<unsigned long long, 256>(before, sm64, &tb);
+        block_exclusive_scan<unsigned long long, 256>(all, sm64 + 4, &ta);
+        base = tb;
+        total = ta;
+        if (blockIdx.x == 0 && tid == 0) {
+            hdr->total = total;
+            hdr->m_eff = (total <= (unsigned long long)capacity) ? (uint32_t)total : 0u;
+            const uint32_t sat = total > 0xffffffffull ? 0xffffffffu : (uint32_t)total;
+            *d_num = sat;
+            offsets[n] = sat;
+        }
+    } else {
+        base = part[blockIdx.x];
+        total = hdr->total;
+    }
     if (g < n) {
         const unsigned long long o = base + local;
         offsets[g] = o > 0xffffffffull ? 0xffffffffu : (uint32_t)o;
     }
-    if (hdr->m_eff != hdr->total || tot == 0) return;   // overflow (or nothing to emit): uniform
+    if (total > (unsigned long long)capacity || tot == 0) return;   // overflow (or nothing to emit): uniform
     excl[tid] = local;
     if (tid == 0) excl[256] = tot;
     box[tid] = g < n ? pixbox[g] : make_uint2(0u, 0u);
@@ -283,23 +321,16 @@ static hipError_t scan_u32(uint32_t *a, int count, uint32_t *sums, hipStream_t s
 // ---------------------------------------------------------------------------
 // 5: tile ranges
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t lower_bound_u32(const uint32_t *__restrict__ a, uint32_t n, uint32_t x) {
-    uint32_t lo = 0, hi = n;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
+// One thread per sorted pair: the first and last pair of each tile's run write
+// its start and end (the ranges were cleared by k_group_sums).
 __global__ __launch_bounds__(256) void k_ranges(const uint32_t *__restrict__ keys, const BinHeader *__restrict__ hdr,
-                                                int ntiles, uint2 *__restrict__ ranges) {
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    if (t >= ntiles) return;
+                                                uint32_t *__restrict__ ranges) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
     const uint32_t M = hdr->m_eff;
-    const uint32_t lo = lower_bound_u32(keys, M, (uint32_t)t);
-    const uint32_t hi = lower_bound_u32(keys, M, (uint32_t)t + 1u);
-    ranges[t] = hi > lo ? make_uint2(lo, hi) : make_uint2(0u, 0u);
+    if (i >= M) return;
+    const uint32_t k = keys[i];
+    if (i == 0 || keys[i - 1] != k) ranges[2 * k] = i;
+    if (i + 1 == M || keys[i + 1] != k) ranges[2 * k + 1] = i + 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -349,14 +380,16 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     uint32_t *table = reinterpret_cast<uint32_t *>(w + p.off_table);
     uint32_t *tsp = reinterpret_cast<uint32_t *>(w + p.off_tsp);
 
-    if (p.nb_g > 0) k_group_sums<<<p.nb_g, 256, 0, s>>>(p.n, counts, part);
-    k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
+    k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, 256, 0, s>>>(p.n, counts, part, p.ntiles,
+                                                         reinterpret_cast<uint2 *>(ranges));
+    const int redundant = p.nb_g > 0 && p.nb_g <= kMaxRedundantGroups;
+    if (!redundant) k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
     // Emit into the buffer that the last pass reads from, so the result lands in keys/vals.
     uint32_t *ek = (p.passes & 1) ? kalt : keys;
     uint32_t *ev = (p.passes & 1) ? valt : vals;
     if (p.nb_g > 0)
-        k_emit<<<p.nb_g, 256, 0, s>>>(p.n, p.tiles_x, counts, reinterpret_cast<const uint2 *>(pixbox), part, hdr,
-                                      offsets, ek, ev);
+        k_emit<<<p.nb_g, 256, 0, s>>>(p.n, p.nb_g, redundant, (long long)p.capacity, p.tiles_x, counts,
+                                      reinterpret_cast<const uint2 *>(pixbox), part, hdr, offsets, d_num, ek, ev);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint32_t *srck = ek, *srcv = ev;
@@ -372,8 +405,8 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
         uint32_t *tk = srck, *tv = srcv;
         srck = dstk; srcv = dstv; dstk = tk; dstv = tv;
     }
-    if (p.ntiles > 0)
-        k_ranges<<<(p.ntiles + 255) / 256, 256, 0, s>>>(keys, hdr, p.ntiles, reinterpret_cast<uint2 *>(ranges));
+    if (p.capacity > 0)
+        k_ranges<<<(unsigned)((p.capacity + 255) / 256), 256, 0, s>>>(keys, hdr, ranges);
     return hipGetLastError();
 }
 

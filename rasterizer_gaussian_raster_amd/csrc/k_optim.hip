@@ -63,13 +63,13 @@ hipError_t launch_loss_l2(int64_t count, const float *image, const float *target
 
 struct AdamArgs {
     float lr[16];
-    float b1, b2, eps, inv_bc1, inv_sqrt_bc2;
+    float b1, omb1, b2, omb2, eps, inv_bc1, inv_sqrt_bc2;   // omb = 1 - beta, formed in double
     int row_len;
 };
 
 __device__ __forceinline__ void adam_one(float &p, float &g, float &m, float &v, float lr, const AdamArgs &a) {
-    m = fmaf(a.b1, m, (1.0f - a.b1) * g);
-    v = fmaf(a.b2, v, (1.0f - a.b2) * g * g);
+    m = fmaf(a.b1, m, a.omb1 * g);
+    v = fmaf(a.b2, v, a.omb2 * g * g);
     const float den = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
     p -= lr * (m * a.inv_bc1) / den;
 }
@@ -106,14 +106,16 @@ __global__ __launch_bounds__(256) void k_adam1(int64_t n, float *__restrict__ p,
 }
 
 hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, float *v, const float *lr,
-                       float beta1, float beta2, float eps, int step, int zero_grad, hipStream_t s) {
+                       double beta1, double beta2, double eps, int step, int zero_grad, hipStream_t s) {
     AdamArgs a{};
     for (int i = 0; i < row_len; ++i) a.lr[i] = lr[i];
-    a.b1 = beta1;
-    a.b2 = beta2;
-    a.eps = eps;
-    a.inv_bc1 = (float)(1.0 / (1.0 - pow((double)beta1, (double)step)));
-    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow((double)beta2, (double)step)));
+    a.b1 = (float)beta1;
+    a.omb1 = (float)(1.0 - beta1);
+    a.b2 = (float)beta2;
+    a.omb2 = (float)(1.0 - beta2);
+    a.eps = (float)eps;
+    a.inv_bc1 = (float)(1.0 / (1.0 - pow(beta1, (double)step)));
+    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(beta2, (double)step)));
     a.row_len = row_len;
     const int64_t n = rows * row_len;
     if (n == 0) return hipSuccess;

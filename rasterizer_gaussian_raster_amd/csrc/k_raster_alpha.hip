@@ -3,7 +3,7 @@
 // over a trainable background; fused kernels with custom VJPs) and its backward.
 //
 // Layout as the sum forward: one workgroup per 16x16 tile, wave w owns the 8x8
-// quadrant (w & 1, w >> 1), one pixel per lane, the tile list staged 256 at a
+// quadrant (w & 1, w >> 1), one pixel per lane, the tile list staged 128 at a
 // time and compacted per quadrant in list order.  A Gaussian dropped for a
 // quadrant has alpha = 0 at every pixel there, so T and C are unchanged by it:
 // compaction keeps the results bit for bit.
@@ -27,6 +27,8 @@ namespace gi {
 
 struct AlphaRec { float4 p, q, r; };   // p = (mux, muy, a, b), q = (c, cr, cg, cb), r = (o, pos, so, g)
 
+constexpr int kBatch = 128;           // list entries staged per round (24 KB of LDS per workgroup)
+
 __device__ __forceinline__ uint32_t quadrant_mask(uint2 bx, int x0, int y0) {
     const int j0 = bx.x & 0xffff, i0 = bx.x >> 16, j1 = bx.y & 0xffff, i1 = bx.y >> 16;
     uint32_t qm = 0;
@@ -38,8 +40,8 @@ __device__ __forceinline__ uint32_t quadrant_mask(uint2 bx, int x0, int y0) {
     return qm;
 }
 
-// Stage list entries [lo, hi) (hi - lo <= 256) into the per-quadrant lists; returns this wave's count.
-__device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[256], int (*wq)[4], uint32_t lo, uint32_t hi, int x0,
+// Stage list entries [lo, hi) (hi - lo <= kBatch) into the per-quadrant lists; returns this wave's count.
+__device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4], uint32_t lo, uint32_t hi, int x0,
                                            int y0, const float4 *__restrict__ records,
                                            const float *__restrict__ opacity, const float *__restrict__ logit,
                                            const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
@@ -47,16 +49,15 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[256], int (*wq)[4], u
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t idx = lo + tid;
     uint32_t qm = 0;
-    AlphaRec r;
-    r.p = r.q = r.r = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (idx < hi) {
+    float4 rp = make_float4(0.f, 0.f, 0.f, 0.f), rq = rp, rr = rp;
+    if (tid < kBatch && idx < hi) {
         const uint32_t g = vals[idx];
-        r.p = records[2 * g];
-        r.q = records[2 * g + 1];
+        rp = records[2 * g];
+        rq = records[2 * g + 1];
         const float o = opacity[g];
         float so = 0.0f;
         if (logit) so = logit[g] < kLogitMax ? o * (1.0f - o) : 0.0f;
-        r.r = make_float4(o, __uint_as_float(idx), so, __uint_as_float(g));
+        rr = make_float4(o, __uint_as_float(idx), so, __uint_as_float(g));
         qm = quadrant_mask(pixbox[g], x0, y0);
     }
     uint32_t rank[4];
@@ -72,7 +73,9 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[256], int (*wq)[4], u
         if ((qm >> q) & 1u) {
             int off = rank[q];
             for (int w = 0; w < wave; ++w) off += wq[w][q];
-            lst[q][off] = r;
+            lst[q][off].p = rp;
+            lst[q][off].q = rq;
+            lst[q][off].r = rr;
         }
     }
     const int cnt = __builtin_amdgcn_readfirstlane(wq[0][wave] + wq[1][wave] + wq[2][wave] + wq[3][wave]);
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
                                                           const float *__restrict__ bg,
                                                           float *__restrict__ image, float *__restrict__ t_final,
                                                           uint32_t *__restrict__ last) {
-    __shared__ AlphaRec lst[4][256];
+    __shared__ AlphaRec lst[4][kBatch];
     __shared__ int wq[4][4];
     __shared__ int wdone[4];
     const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -105,8 +108,8 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
     uint32_t lst_end = rg.x;
     bool done = false;
 
-    for (uint32_t base = rg.x; base < rg.y; base += 256) {
-        const uint32_t hi = rg.y - base > 256u ? base + 256u : rg.y;
+    for (uint32_t base = rg.x; base < rg.y; base += kBatch) {
+        const uint32_t hi = rg.y - base > (uint32_t)kBatch ? base + kBatch : rg.y;
         const int cnt = stage_alpha(lst, wq, base, hi, x0, y0, records, opacity, nullptr, pixbox, vals, below);
         const AlphaRec *L = lst[wave];
         for (int k = 0; k < cnt; ++k) {
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                                                           const float *__restrict__ dL,
                                                           float *__restrict__ dparams, float *__restrict__ dlogit,
                                                           float *__restrict__ dbg) {
-    __shared__ AlphaRec lst[4][256];
+    __shared__ AlphaRec lst[4][kBatch];
     __shared__ int wq[4][4];
     __shared__ uint32_t wmax[4];
     __shared__ float wbg[4][3];
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
     const float is = 1.0f / kScale;
 
     for (uint32_t hi = bend0; hi > rg.x;) {
-        const uint32_t lo = hi - rg.x > 256u ? hi - 256u : rg.x;
+        const uint32_t lo = hi - rg.x > (uint32_t)kBatch ? hi - kBatch : rg.x;
         __syncthreads();                                   // previous batch fully consumed
         const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, records, opacity, logit, pixbox, vals, below);
         const AlphaRec *L = lst[wave];

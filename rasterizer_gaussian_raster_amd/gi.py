@@ -46,7 +46,7 @@ def load():
         raise RuntimeError(f"{LIB_PATH} is not built; run python -m rasterizer_gaussian_raster_amd.build")
     lib = ctypes.CDLL(LIB_PATH)
     P, D = ctypes.c_void_p, ctypes.POINTER(gi_desc)
-    i64, i32, f32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    i64, i32, f64, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
     sigs = {
         "gi_status_string": ([i32], ctypes.c_char_p),
         "gi_version": ([], ctypes.c_char_p),
@@ -58,7 +58,7 @@ def load():
         "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_workspace_bytes": ([i64], sz),
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
-        "gi_adam_step": ([i64, i32, P, P, P, P, P, f32, f32, f32, i32, i32, P], i32),
+        "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)

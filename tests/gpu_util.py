@@ -2,7 +2,8 @@
 
 Image metric: max over (channel, pixel) of |I_gpu - I_ref| / S, S = the oracle's sum of
 |colour| x weight at that pixel (0/0 counts as 0; S = 0 requires I_gpu == 0 exactly).
-Gradient metric: |g_gpu - g_ref| / A per entry, A = the oracle's sum over pairs of |contribution|.
+Gradient metric: |g_gpu - g_ref| / C per entry, C = the oracle's running-error scale (sum over
+pairs of each contribution with its inner sums taken over absolute values).
 """
 import numpy as np
 import pytest

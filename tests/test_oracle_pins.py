@@ -489,3 +489,23 @@ def test_adam_matches_torch(orc):
         q, m, v = orc.adam(q, g, m, v, lr, step)
         ref = np.stack([c.detach().numpy() for c in cols], 1)
         np.testing.assert_allclose(q, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_running_error_scale(orc):
+    """acond >= sum |contribution| always; equal when no inner sum can cancel (axis-aligned
+    Gaussians, non-negative dL/dI and colours)."""
+    W, H = 40, 36
+    p = synth.random_case(31, W, H, 12, sigma=(1.0, 6.0)).astype(np.float64)
+    G = np.random.default_rng(31).normal(size=(3, H, W))
+    _, a, c = orc.grad_sum(W, H, p, G, with_cond=True)
+    assert np.all(c >= a * (1 - 1e-12))
+    q = p.copy()
+    q[:, 3] = 0.0
+    q[:, 2:5] = np.abs(q[:, 2:5])
+    q[:, 5:] = np.abs(q[:, 5:])
+    _, a2, c2 = orc.grad_sum(W, H, q, np.abs(G), with_cond=True)
+    np.testing.assert_allclose(c2, a2, rtol=1e-12, atol=0)
+    p, lg, bg = synth.random_case(32, W, H, 12, sigma=(1.0, 6.0), alpha=True)
+    _, _, _, a3, c3 = orc.grad_alpha(W, H, p.astype(np.float64), lg.astype(np.float64), bg.astype(np.float64), G,
+                                     with_cond=True)
+    assert np.all(c3 >= a3 * (1 - 1e-12))
