@@ -187,23 +187,31 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
  *            dL/dbg_k += g_k T_final.
  *     w -> (mean, L) through d^T Sigma^-1 d.
  *
- *   records, opacity, pixbox, ranges, vals, background, t_final, last: as given to /
- *             produced by gi_render_fwd for the same inputs (alpha-only ones
- *             NULL in sum mode).
+ *   records, opacity, pixbox: from gi_preprocess (opacity NULL in sum mode).
+ *   offsets, ranges, vals, capacity: from / as given to gi_bin_sort.
  *   logit     device float [n] (alpha mode, for the clamp test) or NULL.
+ *   background, t_final, last: as given to / produced by gi_render_fwd (alpha
+ *             mode; NULL in sum mode).
  *   dL_dimage device float [3][H][W].
  *   dparams   device float [n][8], ACCUMULATED (+=) in the params layout.
  *   dlogit    device float [n], accumulated (alpha mode) or NULL.
  *   dbackground device float [3], accumulated (alpha mode) or NULL.
- *   Accumulation uses fp32 atomics: the order of additions, hence the last
- *   bits of the gradients, may vary from run to run.
+ *   workspace device scratch of gi_render_bwd_workspace_bytes() bytes, 256-byte
+ *             aligned, no initialisation needed.
+ *   Each (Gaussian, tile) pair's gradient is formed in the tile's workgroup
+ *   (the contributions of one pair are combined with LDS atomics, whose order
+ *   may vary in the last bits) and stored at the pair's emission slot
+ *   offsets[n] + (position of the tile in n's tile rectangle); a second kernel
+ *   adds each Gaussian's slots in that fixed order.  No global atomics.  If
+ *   gi_bin_sort overflowed (M > capacity) nothing is accumulated.
  */
+size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity);
 gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
-                        const float *logit, const uint16_t *pixbox, const uint32_t *ranges,
-                        const uint32_t *vals,
+                        const float *logit, const uint16_t *pixbox, const uint32_t *offsets,
+                        const uint32_t *ranges, const uint32_t *vals, int64_t capacity,
                         const float *background, const float *t_final, const uint32_t *last,
                         const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
-                        void *stream);
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gi_loss_l2 -- L = mean over the 3HW entries of (image - target)^2 and

@@ -102,23 +102,43 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
                                                   vals, background, image, t_final, last, s));
 }
 
+size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return 0;
+    return gi::make_bwd_plan(desc->width, desc->height, capacity).bytes;
+}
+
 gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
-                        const float *logit, const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                        const float *logit, const uint16_t *pixbox, const uint32_t *offsets,
+                        const uint32_t *ranges, const uint32_t *vals, int64_t capacity,
                         const float *background, const float *t_final, const uint32_t *last,
-                        const float *dL_dimage, float *dparams, float *dlogit, float *dbackground, void *stream) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
-    if (!ranges || !vals || !dL_dimage) return GI_ERR_INVALID_ARG;
-    if (n > 0 && (!records || !pixbox || !dparams || !aligned16(records))) return GI_ERR_INVALID_ARG;
+                        const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31))
+        return GI_ERR_INVALID_ARG;
+    if (!offsets || !ranges || !vals || !dL_dimage || !workspace || !aligned256(workspace))
+        return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !pixbox || !dparams || !aligned16(records) || !aligned16(dparams)))
+        return GI_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
+    const int W = desc->width, H = desc->height;
+    const int ntiles = (int)gi_num_tiles(desc);
+    hipError_t e;
     if (desc->mode == GI_MODE_SUM) {
         if (opacity || logit || background || t_final || last || dlogit || dbackground) return GI_ERR_INVALID_ARG;
-        return hip_status(gi::launch_render_sum_bwd(desc->width, desc->height, records, pixbox, ranges, vals,
-                                                    dL_dimage, dparams, s));
+        e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, vals, capacity, dL_dimage, workspace, s);
+        if (e == hipSuccess)
+            e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 0, dparams, nullptr,
+                                       nullptr, s);
+        return hip_status(e);
     }
     if (!background || !t_final || !last || (n > 0 && (!opacity || !logit))) return GI_ERR_INVALID_ARG;
-    return hip_status(gi::launch_render_alpha_bwd(desc->width, desc->height, records, opacity, logit, pixbox,
-                                                  ranges, vals, background, t_final, last, dL_dimage, dparams,
-                                                  dlogit, dbackground, s));
+    e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, vals, capacity,
+                                    background, t_final, last, dL_dimage, workspace, s);
+    if (e == hipSuccess)
+        e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 1, dparams, dlogit,
+                                   dbackground, s);
+    return hip_status(e);
 }
 
 size_t gi_loss_workspace_bytes(int64_t count) { return count < 1 ? 0 : gi::loss_workspace_bytes(count); }

@@ -55,4 +55,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return (bid & 7) * per + (bid >> 3);
 }
 
+// Emission slot of the pair (Gaussian g, tile (tx, ty)): offsets[g] plus the
+// tile's row-major position in g's tile rectangle (box = packed pixel box).
+__device__ __forceinline__ uint32_t emit_slot(uint32_t off_g, uint2 box, int tx, int ty) {
+    const int tx0 = (int)(box.x & 0xffffu) >> 4, ty0 = (int)(box.x >> 16) >> 4;
+    const int tx1 = (int)(box.y & 0xffffu) >> 4;
+    return off_g + (uint32_t)((ty - ty0) * (tx1 - tx0 + 1) + (tx - tx0));
+}
+
 }  // namespace gi

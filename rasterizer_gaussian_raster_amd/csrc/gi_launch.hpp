@@ -31,9 +31,23 @@ const void *bin_total_ptr(const void *ws);
 // k_raster_sum.hip
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *ranges, const uint32_t *vals, float *image, hipStream_t s);
+
+// Backward workspace: per (Gaussian, tile) gradient at its emission slot.
+struct BwdPlan {
+    size_t off_part;    // float4 [capacity][2]: dmux, dmuy, dl11, dl21 | dl22, dcr, dcg, dcb
+    size_t off_logit;   // float [capacity]: dlogit (alpha)
+    size_t off_bg;      // float4 [ntiles]: dbackground per tile (alpha)
+    size_t bytes;
+};
+BwdPlan make_bwd_plan(int W, int H, int64_t capacity);
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *vals, const float *dL_dimage,
-                                 float *dparams, hipStream_t s);
+                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *vals,
+                                 int64_t capacity, const float *dL_dimage, void *ws, hipStream_t s);
+// Adds each Gaussian's slots (offsets[g] .. offsets[g+1]) in order to dparams / dlogit, and the
+// per-tile background partials to dbackground.
+hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
+                              const void *ws, int alpha, float *dparams, float *dlogit, float *dbackground,
+                              hipStream_t s);
 
 // k_raster_alpha.hip
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
@@ -41,9 +55,9 @@ hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const flo
                                    const float *background, float *image, float *t_final, uint32_t *last,
                                    hipStream_t s);
 hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
-                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
-                                   const float *background, const float *t_final, const uint32_t *last,
-                                   const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                                   const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
+                                   const uint32_t *vals, int64_t capacity, const float *background,
+                                   const float *t_final, const uint32_t *last, const float *dL_dimage, void *ws,
                                    hipStream_t s);
 
 // k_optim.hip

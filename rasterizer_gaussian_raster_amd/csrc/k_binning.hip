@@ -255,20 +255,26 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(const uint32_t *_
 
 // exclusive scan of a u32 array in place: one workgroup when it is short,
 // otherwise reduce -> scan of block sums -> rescan with offsets.
+// count <= 1024 * kScanSingleItems; every thread's loads are issued together.
+constexpr int kScanSingleItems = 32;
 __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, int count) {
     __shared__ uint32_t sm[16];
     const int per = (count + 1023) / 1024;
     const int beg = threadIdx.x * per;
+    uint32_t v[kScanSingleItems];
     uint32_t s = 0;
-    for (int i = 0; i < per; ++i)
-        if (beg + i < count) s += a[beg + i];
+#pragma unroll
+    for (int i = 0; i < kScanSingleItems; ++i) {
+        v[i] = (i < per && beg + i < count) ? a[beg + i] : 0u;
+        s += v[i];
+    }
     uint32_t tot;
     uint32_t run = block_exclusive_scan<uint32_t, 1024>(s, sm, &tot);
-    for (int i = 0; i < per; ++i)
-        if (beg + i < count) {
-            const uint32_t v = a[beg + i];
+#pragma unroll
+    for (int i = 0; i < kScanSingleItems; ++i)
+        if (i < per && beg + i < count) {
             a[beg + i] = run;
-            run += v;
+            run += v[i];
         }
 }
 
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(256) void k_scan_down(uint32_t *__restrict__ a, int
 }
 
 static hipError_t scan_u32(uint32_t *a, int count, uint32_t *sums, hipStream_t s) {
-    if (count <= 32768) {
+    if (count <= 1024 * kScanSingleItems) {
         k_scan_single<<<1, 1024, 0, s>>>(a, count);
         return hipGetLastError();
     }

@@ -18,8 +18,9 @@
 // colour behind it (S_k = later contributions + T_final bg_k), so
 //   dL/dalpha_j = T_j (g . c_j) - gS / (1 - alpha_j),  gS += (g . c_j) alpha_j T_j.
 // The 9 per-pixel contributions of a Gaussian are summed over the wave with
-// DPP row ops and broadcasts, then added with fp32 atomics (skipped when no
-// pixel of the wave is covered).
+// DPP row ops and broadcasts (skipped when no pixel of the wave is covered),
+// the four quadrants' sums meet in LDS, and each list entry stores its
+// gradient at its emission slot for the per-Gaussian gather.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
 
@@ -41,11 +42,13 @@ __device__ __forceinline__ uint32_t quadrant_mask(uint2 bx, int x0, int y0) {
 }
 
 // Stage list entries [lo, hi) (hi - lo <= kBatch) into the per-quadrant lists; returns this wave's count.
+// Backward only (offsets != nullptr): also the entry's emission slot -> eslot[tid].
 __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4], uint32_t lo, uint32_t hi, int x0,
                                            int y0, const float4 *__restrict__ records,
                                            const float *__restrict__ opacity, const float *__restrict__ logit,
                                            const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
-                                           uint64_t below) {
+                                           uint64_t below, const uint32_t *__restrict__ offsets = nullptr,
+                                           uint32_t *eslot = nullptr) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t idx = lo + tid;
     uint32_t qm = 0;
@@ -58,7 +61,9 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4]
         float so = 0.0f;
         if (logit) so = logit[g] < kLogitMax ? o * (1.0f - o) : 0.0f;
         rr = make_float4(o, __uint_as_float(idx), so, __uint_as_float(g));
-        qm = quadrant_mask(pixbox[g], x0, y0);
+        const uint2 bx = pixbox[g];
+        qm = quadrant_mask(bx, x0, y0);
+        if (offsets) eslot[tid] = emit_slot(offsets[g], bx, x0 / kTile, y0 / kTile);
     }
     uint32_t rank[4];
 #pragma unroll
@@ -131,7 +136,8 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
                 done = T < kTmin;
             }
         }
-        if (lane == 0) wdone[wave] = (__ballot(!done) == 0);
+        const bool wave_done = __ballot(!done) == 0;        // all lanes vote (outside any branch)
+        if (lane == 0) wdone[wave] = wave_done;
         if (hi >= rg.y) break;
         __syncthreads();
         if (wdone[0] && wdone[1] && wdone[2] && wdone[3]) break;   // uniform
@@ -151,18 +157,21 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                                                           const float *__restrict__ opacity,
                                                           const float *__restrict__ logit,
                                                           const uint2 *__restrict__ pixbox,
+                                                          const uint32_t *__restrict__ offsets,
                                                           const uint2 *__restrict__ ranges,
-                                                          const uint32_t *__restrict__ vals,
+                                                          const uint32_t *__restrict__ vals, uint32_t capacity,
                                                           const float *__restrict__ bg,
                                                           const float *__restrict__ t_final,
                                                           const uint32_t *__restrict__ last,
                                                           const float *__restrict__ dL,
-                                                          float *__restrict__ dparams, float *__restrict__ dlogit,
-                                                          float *__restrict__ dbg) {
+                                                          float4 *__restrict__ part, float *__restrict__ part_l,
+                                                          float4 *__restrict__ part_bg) {
     __shared__ AlphaRec lst[4][kBatch];
     __shared__ int wq[4][4];
     __shared__ uint32_t wmax[4];
     __shared__ float wbg[4][3];
+    __shared__ float acc[kBatch][9];          // per staged entry: dmux, dmuy, dl11, dl21, dl22, dc (3), dlogit
+    __shared__ uint32_t eslot[kBatch];
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
         gg = dL[o + plane];
         gb = dL[o + 2 * plane];
     }
-    // dL/dbg_k = sum_p g_k T_final
+    // dL/dbg_k = sum_p g_k T_final: one partial per tile
     {
         const float sr = wave_total(gr * T), sg = wave_total(gg * T), sb = wave_total(gb * T);
         if (lane == 0) { wbg[wave][0] = sr; wbg[wave][1] = sg; wbg[wave][2] = sb; }
@@ -193,11 +202,21 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
         if (lane == 0) wmax[wave] = m;
     }
     __syncthreads();
-    if (dbg && tid < 3) {
-        const float s = wbg[0][tid] + wbg[1][tid] + wbg[2][tid] + wbg[3][tid];
-        if (s != 0.0f) atomicAdd(dbg + tid, s);
-    }
+    if (tid == 0)
+        part_bg[t] = make_float4(((wbg[0][0] + wbg[1][0]) + wbg[2][0]) + wbg[3][0],
+                                 ((wbg[0][1] + wbg[1][1]) + wbg[2][1]) + wbg[3][1],
+                                 ((wbg[0][2] + wbg[1][2]) + wbg[2][2]) + wbg[3][2], 0.f);
     const uint32_t bend0 = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    // entries behind every pixel's stop contribute nothing: their slots get zeros
+    for (uint32_t idx = bend0 + tid; idx < rg.y; idx += 256) {
+        const uint32_t g = vals[idx];
+        const uint32_t slot = emit_slot(offsets[g], pixbox[g], x0 / kTile, y0 / kTile);
+        if (slot < capacity) {
+            part[2 * (size_t)slot] = make_float4(0.f, 0.f, 0.f, 0.f);
+            part[2 * (size_t)slot + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            part_l[slot] = 0.f;
+        }
+    }
     float gS = T * fmaf(gb, bg[2], fmaf(gg, bg[1], gr * bg[0]));
     const float k2 = 2.0f * kLn2;
     const float is = 1.0f / kScale;
@@ -205,7 +224,12 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
     for (uint32_t hi = bend0; hi > rg.x;) {
         const uint32_t lo = hi - rg.x > (uint32_t)kBatch ? hi - kBatch : rg.x;
         __syncthreads();                                   // previous batch fully consumed
-        const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, records, opacity, logit, pixbox, vals, below);
+        if (tid < kBatch) {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) acc[tid][k] = 0.0f;
+        }
+        const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, records, opacity, logit, pixbox, vals, below,
+                                    offsets, eslot);
         const AlphaRec *L = lst[wave];
         for (int k = cnt - 1; k >= 0; --k) {
             const float4 A = L[k].p, B = L[k].q, R = L[k].r;
@@ -244,10 +268,9 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
             const float Cr = wave_total(dcr), Cg = wave_total(dcg), Cb = wave_total(dcb);
             const float Dl = wave_total(dlg);
             if (lane == 0) {
-                const uint32_t g = __float_as_uint(R.w);
                 const float a = A.z, b = A.w, c = B.x;
                 const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                float *d = dparams + 8 * (size_t)g;
+                float *d = acc[pos - lo];
                 atomicAdd(d + 0, k2 * fmaf(a, Hu, b * Hv));
                 atomicAdd(d + 1, k2 * c * Hv);
                 atomicAdd(d + 2, -is * fmaf(a * a, da, a * b * db));
@@ -256,7 +279,16 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                 atomicAdd(d + 5, Cr);
                 atomicAdd(d + 6, Cg);
                 atomicAdd(d + 7, Cb);
-                if (dlogit) atomicAdd(dlogit + g, Dl);
+                atomicAdd(d + 8, Dl);
+            }
+        }
+        __syncthreads();
+        if (tid < kBatch && lo + tid < hi) {
+            const uint32_t slot = eslot[tid];
+            if (slot < capacity) {
+                part[2 * (size_t)slot] = make_float4(acc[tid][0], acc[tid][1], acc[tid][2], acc[tid][3]);
+                part[2 * (size_t)slot + 1] = make_float4(acc[tid][4], acc[tid][5], acc[tid][6], acc[tid][7]);
+                part_l[slot] = acc[tid][8];
             }
         }
         hi = lo;
@@ -278,15 +310,18 @@ hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const flo
 }
 
 hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
-                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
-                                   const float *background, const float *t_final, const uint32_t *last,
-                                   const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                                   const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
+                                   const uint32_t *vals, int64_t capacity, const float *background,
+                                   const float *t_final, const uint32_t *last, const float *dL_dimage, void *ws,
                                    hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
+    const BwdPlan p = make_bwd_plan(W, H, capacity);
+    char *w = static_cast<char *>(ws);
     k_render_alpha_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity, logit,
-        reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), vals, background, t_final,
-        last, dL_dimage, dparams, dlogit, dbackground);
+        reinterpret_cast<const uint2 *>(pixbox), offsets, reinterpret_cast<const uint2 *>(ranges), vals,
+        (uint32_t)capacity, background, t_final, last, dL_dimage, reinterpret_cast<float4 *>(w + p.off_part),
+        reinterpret_cast<float *>(w + p.off_logit), reinterpret_cast<float4 *>(w + p.off_bg));
     return hipGetLastError();
 }
 

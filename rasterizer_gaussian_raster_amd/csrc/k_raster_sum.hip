@@ -136,13 +136,14 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
 __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
+                                                        const uint32_t *__restrict__ offsets,
                                                         const uint2 *__restrict__ ranges,
-                                                        const uint32_t *__restrict__ vals,
+                                                        const uint32_t *__restrict__ vals, uint32_t capacity,
                                                         const float *__restrict__ dL,
-                                                        float *__restrict__ dparams) {
+                                                        float4 *__restrict__ part) {
     __shared__ float4 gp[256];                    // dL/dI of the tile's pixels, row-major
     __shared__ SumRec ent[256];                   // staged list entries
-    __shared__ uint32_t eg[256];                  // their Gaussian indices
+    __shared__ uint32_t eg[256];                  // their emission slots
     __shared__ float acc[256][9];                 // per-entry gradient (params layout), padded row
     __shared__ uint16_t items[256 * 16];          // entry | block << 8
     __shared__ uint32_t sm[4];
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
     const uint2 rg = ranges[t];
     if (rg.x == rg.y) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
+    const int tx = t % tiles_x, ty = t / tiles_x;
+    const int x0 = tx * kTile, y0 = ty * kTile;
     {
         const int xi = x0 + (tid & 15), yi = y0 + (tid >> 4);
         float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -170,8 +172,8 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
             const uint32_t g = vals[idx];
             ent[tid].p = records[2 * g];
             ent[tid].q = records[2 * g + 1];
-            eg[tid] = g;
             const uint2 bx = pixbox[g];
+            eg[tid] = emit_slot(offsets[g], bx, tx, ty);
             const int j0 = max((int)(bx.x & 0xffff) - x0, 0), j1 = min((int)(bx.y & 0xffff) - x0, 15);
             const int i0 = max((int)(bx.x >> 16) - y0, 0), i1 = min((int)(bx.y >> 16) - y0, 15);
             bx0 = (uint32_t)j0 >> 2;
@@ -245,18 +247,95 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
         }
         __syncthreads();
         if (idx < rg.y) {
-            float *d = dparams + 8 * (size_t)eg[tid];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float v = acc[tid][k];
-                if (v != 0.0f) atomicAdd(d + k, v);
+            const uint32_t slot = eg[tid];
+            if (slot < capacity) {
+                part[2 * (size_t)slot] = make_float4(acc[tid][0], acc[tid][1], acc[tid][2], acc[tid][3]);
+                part[2 * (size_t)slot + 1] = make_float4(acc[tid][4], acc[tid][5], acc[tid][6], acc[tid][7]);
             }
         }
         if (base + 256 < rg.y) __syncthreads();   // the next batch reuses ent / acc / items
     }
 }
 
+// One thread per Gaussian: its pairs' partial gradients sit at offsets[g] ..
+// offsets[g+1] in emission order; add them in that order (reproducible).
+__global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const uint32_t *__restrict__ offsets,
+                                                     uint32_t capacity, const float4 *__restrict__ part,
+                                                     const float *__restrict__ part_l,
+                                                     const float4 *__restrict__ part_bg,
+                                                     float *__restrict__ dparams, float *__restrict__ dlogit,
+                                                     float *__restrict__ dbg) {
+    if (offsets[n] > capacity) return;                  // binning overflowed: nothing was rendered
+    if (dbg && blockIdx.x == 0) {
+        __shared__ float4 sm[256];
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int t = threadIdx.x; t < ntiles; t += 256) {
+            const float4 v = part_bg[t];
+            s.x += v.x; s.y += v.y; s.z += v.z;
+        }
+        sm[threadIdx.x] = s;
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if (threadIdx.x < o) {
+                sm[threadIdx.x].x += sm[threadIdx.x + o].x;
+                sm[threadIdx.x].y += sm[threadIdx.x + o].y;
+                sm[threadIdx.x].z += sm[threadIdx.x + o].z;
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) { dbg[0] += sm[0].x; dbg[1] += sm[0].y; dbg[2] += sm[0].z; }
+    }
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= n) return;
+    const uint32_t o0 = offsets[g], o1 = offsets[g + 1];
+    if (o1 == o0) return;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    float l = 0.f;
+    for (uint32_t q = o0; q < o1; ++q) {
+        const float4 u = part[2 * (size_t)q], v = part[2 * (size_t)q + 1];
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+        b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+        if (part_l) l += part_l[q];
+    }
+    float4 *d = reinterpret_cast<float4 *>(dparams) + 2 * (size_t)g;
+    float4 d0 = d[0], d1 = d[1];
+    d0.x += a.x; d0.y += a.y; d0.z += a.z; d0.w += a.w;
+    d1.x += b.x; d1.y += b.y; d1.z += b.z; d1.w += b.w;
+    d[0] = d0;
+    d[1] = d1;
+    if (dlogit) dlogit[g] += l;
+}
+
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdPlan make_bwd_plan(int W, int H, int64_t capacity) {
+    const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+    const size_t cap = (size_t)(capacity > 0 ? capacity : 1);
+    BwdPlan p{};
+    size_t off = 0;
+    p.off_part = off; off = align256(off + 32 * cap);
+    p.off_logit = off; off = align256(off + 4 * cap);
+    p.off_bg = off; off = align256(off + 16 * (size_t)ntiles);
+    p.bytes = off;
+    return p;
+}
+
+hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
+                              const void *ws, int alpha, float *dparams, float *dlogit, float *dbackground,
+                              hipStream_t s) {
+    if (n == 0 && !(alpha && dbackground)) return hipSuccess;
+    const BwdPlan p = make_bwd_plan(W, H, capacity);
+    const char *w = static_cast<const char *>(ws);
+    const int nb = (n + 255) / 256;
+    k_grad_gather<<<nb > 0 ? nb : 1, 256, 0, s>>>(
+        n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(w + p.off_part),
+        alpha ? reinterpret_cast<const float *>(w + p.off_logit) : nullptr,
+        reinterpret_cast<const float4 *>(w + p.off_bg), dparams, alpha ? dlogit : nullptr,
+        alpha ? dbackground : nullptr);
+    return hipGetLastError();
+}
 
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *ranges, const uint32_t *vals, float *image, hipStream_t s) {
@@ -269,14 +348,14 @@ hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint1
 }
 
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *vals, const float *dL_dimage,
-                                 float *dparams, hipStream_t s) {
+                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *vals,
+                                 int64_t capacity, const float *dL_dimage, void *ws, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
-    k_render_sum_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles,
-                                                          reinterpret_cast<const float4 *>(records),
-                                                          reinterpret_cast<const uint2 *>(pixbox),
-                                                          reinterpret_cast<const uint2 *>(ranges), vals,
-                                                          dL_dimage, dparams);
+    const BwdPlan p = make_bwd_plan(W, H, capacity);
+    k_render_sum_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(
+        W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
+        offsets, reinterpret_cast<const uint2 *>(ranges), vals, (uint32_t)capacity, dL_dimage,
+        reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part));
     return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ def load():
         "gi_bin_sort_workspace_bytes": ([D, i64, i64], sz),
         "gi_bin_sort": ([D, i64, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gi_render_fwd": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
-        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P], i32),
+        "gi_render_bwd_workspace_bytes": ([D, i64, i64], sz),
+        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P, P, sz, P], i32),
         "gi_loss_workspace_bytes": ([i64], sz),
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
@@ -131,12 +132,17 @@ def gi_render_fwd(d, n, records, opacity, pixbox, ranges, vals, background, imag
                                 _ptr(last), _stream(stream)), "gi_render_fwd")
 
 
-def gi_render_bwd(d, n, records, opacity, logit, pixbox, ranges, vals, background, t_final, last, dL_dimage,
-                  dparams, dlogit, dbackground, stream=None):
+def gi_render_bwd_workspace_bytes(d, n, capacity) -> int:
+    return int(load().gi_render_bwd_workspace_bytes(ctypes.byref(d), int(n), int(capacity)))
+
+
+def gi_render_bwd(d, n, records, opacity, logit, pixbox, offsets, ranges, vals, capacity, background, t_final,
+                  last, dL_dimage, dparams, dlogit, dbackground, workspace, stream=None):
     _check(load().gi_render_bwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(logit),
-                                _ptr(pixbox), _ptr(ranges), _ptr(vals), _ptr(background), _ptr(t_final),
-                                _ptr(last), _ptr(dL_dimage), _ptr(dparams), _ptr(dlogit), _ptr(dbackground),
-                                _stream(stream)), "gi_render_bwd")
+                                _ptr(pixbox), _ptr(offsets), _ptr(ranges), _ptr(vals), int(capacity),
+                                _ptr(background), _ptr(t_final), _ptr(last), _ptr(dL_dimage), _ptr(dparams),
+                                _ptr(dlogit), _ptr(dbackground), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)), "gi_render_bwd")
 
 
 def gi_loss_workspace_bytes(count) -> int:

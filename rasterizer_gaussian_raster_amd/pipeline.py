@@ -40,7 +40,7 @@ class Raster:
         self.t_final = torch.empty((self.H, self.W), dtype=torch.float32, device=dev) if alpha else None
         self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev) if alpha else None
         self.capacity = 0
-        self.keys = self.vals = self.ws = None
+        self.keys = self.vals = self.ws = self.bwd_ws = None
         self.M = None
         if capacity is not None:
             self.set_capacity(capacity)
@@ -53,6 +53,7 @@ class Raster:
         self.vals = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
         nbytes = gi.gi_bin_sort_workspace_bytes(self.desc, self.n, capacity)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.bwd_ws = None                      # sized on first backward (capacity-dependent)
 
     # -- steps ---------------------------------------------------------------------------------
     def preprocess(self, params, logit=None, stream=None):
@@ -88,9 +89,12 @@ class Raster:
 
     def backward(self, dL_dimage, dparams, logit=None, background=None, dlogit=None, dbackground=None,
                  stream=None):
-        gi.gi_render_bwd(self.desc, self.n, self.records, self.opacity, logit, self.pixbox, self.ranges,
-                         self.vals, background, self.t_final, self.last, dL_dimage, dparams, dlogit,
-                         dbackground, stream)
+        if self.bwd_ws is None:
+            nbytes = gi.gi_render_bwd_workspace_bytes(self.desc, self.n, self.capacity)
+            self.bwd_ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device(self.device))
+        gi.gi_render_bwd(self.desc, self.n, self.records, self.opacity, logit, self.pixbox, self.offsets,
+                         self.ranges, self.vals, self.capacity, background, self.t_final, self.last, dL_dimage,
+                         dparams, dlogit, dbackground, self.bwd_ws, stream)
 
     def render(self, params, logit=None, background=None, sync=True):
         self.preprocess(params, logit)
