@@ -255,27 +255,55 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(const uint32_t *_
 
 // exclusive scan of a u32 array in place: one workgroup when it is short,
 // otherwise reduce -> scan of block sums -> rescan with offsets.
-// count <= 1024 * kScanSingleItems; every thread's loads are issued together.
+// count <= 1024 * kScanSingleItems.  Element r * 1024 + i lives in thread i's
+// register v[r] (coalesced loads, all issued together); its exclusive prefix is
+// the totals of rows before r plus the prefix of row r over threads before i.
 constexpr int kScanSingleItems = 32;
 __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, int count) {
-    __shared__ uint32_t sm[16];
-    const int per = (count + 1023) / 1024;
-    const int beg = threadIdx.x * per;
-    uint32_t v[kScanSingleItems];
-    uint32_t s = 0;
+    __shared__ uint32_t wsum[16][kScanSingleItems + 1];   // [wave][row] totals
+    __shared__ uint32_t rowpre[kScanSingleItems];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rows = (count + 1023) / 1024;
+    uint32_t v[kScanSingleItems], inc[kScanSingleItems];
 #pragma unroll
-    for (int i = 0; i < kScanSingleItems; ++i) {
-        v[i] = (i < per && beg + i < count) ? a[beg + i] : 0u;
-        s += v[i];
+    for (int r = 0; r < kScanSingleItems; ++r) {
+        const int e = r * 1024 + tid;
+        v[r] = (r < rows && e < count) ? a[e] : 0u;
     }
-    uint32_t tot;
-    uint32_t run = block_exclusive_scan<uint32_t, 1024>(s, sm, &tot);
 #pragma unroll
-    for (int i = 0; i < kScanSingleItems; ++i)
-        if (i < per && beg + i < count) {
-            a[beg + i] = run;
-            run += v[i];
+    for (int r = 0; r < kScanSingleItems; ++r) {
+        if (r >= rows) break;
+        uint32_t x = v[r];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
         }
+        inc[r] = x;
+        if (lane == 63) wsum[wave][r] = x;
+    }
+    __syncthreads();
+    if (tid < 64) {            // one wave: row totals -> exclusive prefix over rows
+        uint32_t tot = 0;
+        if (tid < rows)
+            for (int w = 0; w < 16; ++w) tot += wsum[w][tid];
+        uint32_t x = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (tid < rows) rowpre[tid] = x - tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kScanSingleItems; ++r) {
+        if (r >= rows) break;
+        uint32_t o = rowpre[r] + inc[r] - v[r];
+        for (int w = 0; w < wave; ++w) o += wsum[w][r];
+        const int e = r * 1024 + tid;
+        if (e < count) a[e] = o;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_scan_reduce(const uint32_t *__restrict__ a, int count,

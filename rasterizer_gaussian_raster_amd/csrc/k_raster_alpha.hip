@@ -18,9 +18,11 @@
 // colour behind it (S_k = later contributions + T_final bg_k), so
 //   dL/dalpha_j = T_j (g . c_j) - gS / (1 - alpha_j),  gS += (g . c_j) alpha_j T_j.
 // The 9 per-pixel contributions of a Gaussian are summed over the wave with
-// DPP row ops and broadcasts (skipped when no pixel of the wave is covered),
-// the four quadrants' sums meet in LDS, and each list entry stores its
-// gradient at its emission slot for the per-Gaussian gather.
+// DPP row ops and broadcasts (skipped when no pixel of the wave is covered) and
+// written over the entry's slot in the wave's own quadrant list; each list
+// entry then adds its four quadrant results in quadrant order and stores the
+// gradient at its emission slot for the per-Gaussian gather.  No atomics: the
+// gradients are bitwise reproducible.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
 
@@ -42,13 +44,14 @@ __device__ __forceinline__ uint32_t quadrant_mask(uint2 bx, int x0, int y0) {
 }
 
 // Stage list entries [lo, hi) (hi - lo <= kBatch) into the per-quadrant lists; returns this wave's count.
-// Backward only (offsets != nullptr): also the entry's emission slot -> eslot[tid].
+// Backward only (offsets != nullptr): also the entry's emission slot -> eslot[tid]
+// and its position in each quadrant list -> qpos[tid][q] (0xff: not in that list).
 __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4], uint32_t lo, uint32_t hi, int x0,
                                            int y0, const float4 *__restrict__ records,
                                            const float *__restrict__ opacity, const float *__restrict__ logit,
                                            const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
                                            uint64_t below, const uint32_t *__restrict__ offsets = nullptr,
-                                           uint32_t *eslot = nullptr) {
+                                           uint32_t *eslot = nullptr, uint8_t (*qpos)[4] = nullptr) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t idx = lo + tid;
     uint32_t qm = 0;
@@ -81,6 +84,9 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4]
             lst[q][off].p = rp;
             lst[q][off].q = rq;
             lst[q][off].r = rr;
+            if (qpos) qpos[tid][q] = (uint8_t)off;
+        } else if (qpos && tid < kBatch) {
+            qpos[tid][q] = 0xff;
         }
     }
     const int cnt = __builtin_amdgcn_readfirstlane(wq[0][wave] + wq[1][wave] + wq[2][wave] + wq[3][wave]);
@@ -170,8 +176,8 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
     __shared__ int wq[4][4];
     __shared__ uint32_t wmax[4];
     __shared__ float wbg[4][3];
-    __shared__ float acc[kBatch][9];          // per staged entry: dmux, dmuy, dl11, dl21, dl22, dc (3), dlogit
     __shared__ uint32_t eslot[kBatch];
+    __shared__ uint8_t qpos[kBatch][4];
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -224,12 +230,8 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
     for (uint32_t hi = bend0; hi > rg.x;) {
         const uint32_t lo = hi - rg.x > (uint32_t)kBatch ? hi - kBatch : rg.x;
         __syncthreads();                                   // previous batch fully consumed
-        if (tid < kBatch) {
-#pragma unroll
-            for (int k = 0; k < 9; ++k) acc[tid][k] = 0.0f;
-        }
         const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, records, opacity, logit, pixbox, vals, below,
-                                    offsets, eslot);
+                                    offsets, eslot, qpos);
         const AlphaRec *L = lst[wave];
         for (int k = cnt - 1; k >= 0; --k) {
             const float4 A = L[k].p, B = L[k].q, R = L[k].r;
@@ -240,7 +242,15 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
             const float v = fmaf(B.x, dy, tb);
             const float e = fmaf(v, v, u * u);
             const bool act = pos < lp && e <= kE9;
-            if (__ballot(act) == 0) continue;              // uniform
+            float *res = reinterpret_cast<float *>(&lst[wave][k]);   // this wave is done reading entry k
+            if (__ballot(act) == 0) {                                  // uniform
+                if (lane == 0) {
+                    lst[wave][k].p = make_float4(0.f, 0.f, 0.f, 0.f);
+                    lst[wave][k].q = make_float4(0.f, 0.f, 0.f, 0.f);
+                    res[8] = 0.0f;
+                }
+                continue;
+            }
             float dcr = 0.f, dcg = 0.f, dcb = 0.f, hu = 0.f, hv = 0.f, hudx = 0.f, hvdx = 0.f, hvdy = 0.f, dlg = 0.f;
             if (act) {
                 const float w = exp2_hw(-e);
@@ -270,25 +280,31 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
             if (lane == 0) {
                 const float a = A.z, b = A.w, c = B.x;
                 const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                float *d = acc[pos - lo];
-                atomicAdd(d + 0, k2 * fmaf(a, Hu, b * Hv));
-                atomicAdd(d + 1, k2 * c * Hv);
-                atomicAdd(d + 2, -is * fmaf(a * a, da, a * b * db));
-                atomicAdd(d + 3, -is * (a * c * db));
-                atomicAdd(d + 4, -is * fmaf(b * c, db, c * c * dc));
-                atomicAdd(d + 5, Cr);
-                atomicAdd(d + 6, Cg);
-                atomicAdd(d + 7, Cb);
-                atomicAdd(d + 8, Dl);
+                lst[wave][k].p = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv, -is * fmaf(a * a, da, a * b * db),
+                                             -is * (a * c * db));
+                lst[wave][k].q = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
+                res[8] = Dl;
             }
         }
         __syncthreads();
-        if (tid < kBatch && lo + tid < hi) {
+        if (tid < kBatch && lo + tid < hi) {      // quadrant results of this entry, added in quadrant order
+            float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+            float sl = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = qpos[tid][q];
+                if (k != 0xff) {
+                    const float4 u0 = lst[q][k].p, u1 = lst[q][k].q;
+                    s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
+                    s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+                    sl += lst[q][k].r.x;
+                }
+            }
             const uint32_t slot = eslot[tid];
             if (slot < capacity) {
-                part[2 * (size_t)slot] = make_float4(acc[tid][0], acc[tid][1], acc[tid][2], acc[tid][3]);
-                part[2 * (size_t)slot + 1] = make_float4(acc[tid][4], acc[tid][5], acc[tid][6], acc[tid][7]);
-                part_l[slot] = acc[tid][8];
+                part[2 * (size_t)slot] = s0;
+                part[2 * (size_t)slot + 1] = s1;
+                part_l[slot] = sl;
             }
         }
         hi = lo;

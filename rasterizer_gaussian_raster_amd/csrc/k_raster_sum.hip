@@ -16,13 +16,15 @@
 // Backward (work items).  The tile is cut into 16 blocks of 4x4 pixels; every
 // list entry yields one work item per block its pixel box overlaps (about 0.4
 // of the binned pairs at the benchmark shapes), and the items are packed 64
-// per wave, one per lane, so no lane idles on a short list and no pair outside
-// the box is evaluated.  A lane walks its block's 16 pixels (dL/dI staged in
+// per wave, one per lane, block-major so that a wave's lanes share their
+// block's dL/dI (LDS broadcasts), no lane idles on a short list and no pair
+// outside the box is evaluated.  A lane walks its block's 16 pixels (dL/dI staged in
 // LDS), keeping the Gaussian's partial gradient in registers with the
 // column-invariant factors (dx, u, b dx, u^2) hoisted; the chain rule from the
-// scaled rows of L^-1 (a, b, c) to (l11, l21, l22) is applied per item, the
-// items of an entry meet in LDS float atomics, and each entry then adds its 8
-// values to dparams with fp32 global atomics.
+// scaled rows of L^-1 (a, b, c) to (l11, l21, l22) is applied per item, each
+// entry adds up its items in a fixed order and stores its 8 values at its
+// emission slot for the per-Gaussian gather: no atomics anywhere, so the
+// gradients are bitwise reproducible.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
 
@@ -31,29 +33,6 @@ namespace gi {
 struct SumRec { float4 p, q; };   // p = (mux, muy, a, b), q = (c, cr, cg, cb)
 
 constexpr int kFwdBatch = 128;    // list entries staged per round (16 KB of LDS: 8+ workgroups per CU)
-
-// exclusive scan over the 256 threads of a workgroup (wave shuffles + one LDS step)
-__device__ __forceinline__ uint32_t block_exclusive_scan_u32(uint32_t x, uint32_t *sm, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += y;
-    }
-    if (lane == 63) sm[wave] = inc;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t s = sm[w];
-        off += (w < wave) ? s : 0u;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return off + inc - x;
-}
 
 __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
@@ -132,7 +111,16 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
     }
 }
 
-// Backward work item: one (list entry, 4x4 pixel block) pair per lane.
+// Backward work item: one (list entry, 4x4 pixel block) pair per thread.  Items
+// are laid out block-major (all entries overlapping block 0 in list order, then
+// block 1, ...), so the lanes of a wave mostly share one block and their dL/dI
+// reads from LDS are broadcasts.  Items run in rounds of 256 (one per thread);
+// each writes its 8 values to an LDS slot, then every entry adds its own items
+// in block order -- no atomics, and the result does not depend on timing.
+constexpr int kBwdBatch = 128;                    // list entries staged per round
+constexpr int kGpStride = 17;                     // padded LDS row of the tile's dL/dI (float4)
+constexpr uint16_t kNoItem = 0xffff;
+
 __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
@@ -141,12 +129,13 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                                                         const uint32_t *__restrict__ vals, uint32_t capacity,
                                                         const float *__restrict__ dL,
                                                         float4 *__restrict__ part) {
-    __shared__ float4 gp[256];                    // dL/dI of the tile's pixels, row-major
-    __shared__ SumRec ent[256];                   // staged list entries
-    __shared__ uint32_t eg[256];                  // their emission slots
-    __shared__ float acc[256][9];                 // per-entry gradient (params layout), padded row
-    __shared__ uint16_t items[256 * 16];          // entry | block << 8
-    __shared__ uint32_t sm[4];
+    __shared__ float4 gp[kTile * kGpStride];      // dL/dI of the tile's pixels
+    __shared__ SumRec ent[kBwdBatch];             // staged list entries
+    __shared__ uint16_t items[kBwdBatch * 16];    // entry | block << 8, block-major
+    __shared__ uint16_t ipos[kBwdBatch][16];      // item index of (entry, block), kNoItem if none
+    __shared__ float4 ipart[256][2];              // this round's item results
+    __shared__ uint32_t wcnt[4][16];              // per wave: entries overlapping each block
+    __shared__ uint32_t bstart[17];               // block-major start of each block's items
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     if (t >= ntiles) return;
     const uint2 rg = ranges[t];
@@ -161,99 +150,124 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
             const size_t o = (size_t)yi * W + xi, plane = (size_t)W * H;
             g = make_float4(dL[o], dL[o + plane], dL[o + 2 * plane], 0.f);
         }
-        gp[tid] = g;
+        gp[(tid >> 4) * kGpStride + (tid & 15)] = g;
     }
+    const uint64_t below = lanes_below();
     const float k2 = 2.0f * kLn2;
     const float is = 1.0f / kScale;
-    for (uint32_t base = rg.x; base < rg.y; base += 256) {
+    for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
         const uint32_t idx = base + tid;
-        uint32_t nit = 0, bx0 = 0, by0 = 0, wb = 1;
-        if (idx < rg.y) {
+        const bool staged = tid < kBwdBatch && idx < rg.y;
+        int bx0 = 4, bx1 = -1, by0 = 4, by1 = -1;         // block rectangle (empty when not staged)
+        uint32_t slot = 0xffffffffu;
+        if (staged) {
             const uint32_t g = vals[idx];
             ent[tid].p = records[2 * g];
             ent[tid].q = records[2 * g + 1];
             const uint2 bx = pixbox[g];
-            eg[tid] = emit_slot(offsets[g], bx, tx, ty);
-            const int j0 = max((int)(bx.x & 0xffff) - x0, 0), j1 = min((int)(bx.y & 0xffff) - x0, 15);
-            const int i0 = max((int)(bx.x >> 16) - y0, 0), i1 = min((int)(bx.y >> 16) - y0, 15);
-            bx0 = (uint32_t)j0 >> 2;
-            by0 = (uint32_t)i0 >> 2;
-            wb = ((uint32_t)j1 >> 2) - bx0 + 1;
-            nit = wb * (((uint32_t)i1 >> 2) - by0 + 1);
+            slot = emit_slot(offsets[g], bx, tx, ty);
+            bx0 = max((int)(bx.x & 0xffff) - x0, 0) >> 2;
+            bx1 = min((int)(bx.y & 0xffff) - x0, 15) >> 2;
+            by0 = max((int)(bx.x >> 16) - y0, 0) >> 2;
+            by1 = min((int)(bx.y >> 16) - y0, 15) >> 2;
         }
+        // block-major item positions: per block, ballot over the wave, then waves in order
 #pragma unroll
-        for (int k = 0; k < 9; ++k) acc[tid][k] = 0.0f;
-        uint32_t nitems;
-        const uint32_t off = block_exclusive_scan_u32(nit, sm, &nitems);
-        for (uint32_t k = 0; k < nit; ++k) {
-            const uint32_t q = k / wb;
-            const uint32_t blk = (by0 + q) * 4 + bx0 + (k - q * wb);
-            items[off + k] = (uint16_t)(tid | (blk << 8));
+        for (int b = 0; b < 16; ++b) {
+            const bool in = (b & 3) >= bx0 && (b & 3) <= bx1 && (b >> 2) >= by0 && (b >> 2) <= by1;
+            const uint64_t m = __ballot(in);
+            if (lane == 0) wcnt[wave][b] = (uint32_t)__popcll(m);
         }
         __syncthreads();
-        for (uint32_t cb = (uint32_t)wave * 64; cb < nitems; cb += 256) {
-            const uint32_t it = cb + lane;
-            const bool active = it < nitems;
-            const uint32_t code = active ? items[it] : 0u;
-            const uint32_t e = code & 0xffu, blk = code >> 8;
-            const int lx = (int)(blk & 3u) * 4, ly = (int)(blk >> 2) * 4;
-            const float4 A = ent[e].p, B = ent[e].q;
-            float dy[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
-            float Hu = 0.f, Hv = 0.f, Hudx = 0.f, Hvdx = 0.f, Hvdy = 0.f, Cr = 0.f, Cg = 0.f, Cb = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float dx = ((float)(x0 + lx + c) + 0.5f) - A.x;
-                const float u = A.z * dx;
-                const float tb = A.w * dx;
-                const float uu = u * u;
-                float ch = 0.f, chv = 0.f;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const float4 gv = gp[(ly + rr) * kTile + lx + c];
-                    const float v = fmaf(B.x, dy[rr], tb);
-                    const float ee = fmaf(v, v, uu);
-                    const float w = (active && ee <= kE9) ? exp2_hw(-ee) : 0.0f;
-                    Cr = fmaf(gv.x, w, Cr);
-                    Cg = fmaf(gv.y, w, Cg);
-                    Cb = fmaf(gv.z, w, Cb);
-                    const float h = fmaf(gv.z, B.w, fmaf(gv.y, B.z, gv.x * B.y)) * w;
-                    const float hv = h * v;
-                    ch += h;
-                    chv += hv;
-                    Hvdy = fmaf(hv, dy[rr], Hvdy);
-                }
-                Hu = fmaf(u, ch, Hu);
-                Hudx = fmaf(u * dx, ch, Hudx);
-                Hv += chv;
-                Hvdx = fmaf(dx, chv, Hvdx);
+        if (tid == 0) {
+            uint32_t run = 0;
+            for (int b = 0; b < 16; ++b) {
+                bstart[b] = run;
+                run += wcnt[0][b] + wcnt[1][b] + wcnt[2][b] + wcnt[3][b];
             }
-            if (active && (Cr != 0.f || Cg != 0.f || Cb != 0.f || Hu != 0.f || Hv != 0.f)) {
+            bstart[16] = run;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const bool in = (b & 3) >= bx0 && (b & 3) <= bx1 && (b >> 2) >= by0 && (b >> 2) <= by1;
+            const uint64_t m = __ballot(in);               // same vote as above
+            if (in) {
+                uint32_t o = bstart[b] + (uint32_t)__popcll(m & below);
+                for (int w = 0; w < wave; ++w) o += wcnt[w][b];
+                items[o] = (uint16_t)(tid | (b << 8));
+                ipos[tid][b] = (uint16_t)o;
+            } else if (tid < kBwdBatch) {
+                ipos[tid][b] = kNoItem;
+            }
+        }
+        const uint32_t nitems = bstart[16];
+        float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // this thread's entry
+        for (uint32_t rb = 0; rb < nitems; rb += 256) {
+            __syncthreads();                                // items / ipos written; ipart free
+            const uint32_t it = rb + tid;
+            if (it < nitems) {
+                const uint32_t code = items[it];
+                const uint32_t e = code & 0xffu, blk = code >> 8;
+                const int lx = (int)(blk & 3u) * 4, ly = (int)(blk >> 2) * 4;
+                const float4 A = ent[e].p, B = ent[e].q;
+                float dy[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
+                float Hu = 0.f, Hv = 0.f, Hudx = 0.f, Hvdx = 0.f, Hvdy = 0.f, Cr = 0.f, Cg = 0.f, Cb = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float dx = ((float)(x0 + lx + c) + 0.5f) - A.x;
+                    const float u = A.z * dx;
+                    const float tb = A.w * dx;
+                    const float uu = u * u;
+                    float ch = 0.f, chv = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const float4 gv = gp[(ly + rr) * kGpStride + lx + c];
+                        const float v = fmaf(B.x, dy[rr], tb);
+                        const float ee = fmaf(v, v, uu);
+                        const float w = ee <= kE9 ? exp2_hw(-ee) : 0.0f;
+                        Cr = fmaf(gv.x, w, Cr);
+                        Cg = fmaf(gv.y, w, Cg);
+                        Cb = fmaf(gv.z, w, Cb);
+                        const float h = fmaf(gv.z, B.w, fmaf(gv.y, B.z, gv.x * B.y)) * w;
+                        const float hv = h * v;
+                        ch += h;
+                        chv += hv;
+                        Hvdy = fmaf(hv, dy[rr], Hvdy);
+                    }
+                    Hu = fmaf(u, ch, Hu);
+                    Hudx = fmaf(u * dx, ch, Hudx);
+                    Hv += chv;
+                    Hvdx = fmaf(dx, chv, Hvdx);
+                }
                 // e = u^2 + v^2, w = 2^-e: dL/de = -ln2 h, summed through (Hu, Hv, ...); then
                 // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22).
                 const float a = A.z, b = A.w, c = B.x;
                 const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                float *d = acc[e];
-                atomicAdd(d + 0, k2 * fmaf(a, Hu, b * Hv));
-                atomicAdd(d + 1, k2 * c * Hv);
-                atomicAdd(d + 2, -is * fmaf(a * a, da, a * b * db));
-                atomicAdd(d + 3, -is * (a * c * db));
-                atomicAdd(d + 4, -is * fmaf(b * c, db, c * c * dc));
-                atomicAdd(d + 5, Cr);
-                atomicAdd(d + 6, Cg);
-                atomicAdd(d + 7, Cb);
+                ipart[tid][0] = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv, -is * fmaf(a * a, da, a * b * db),
+                                            -is * (a * c * db));
+                ipart[tid][1] = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
+            }
+            __syncthreads();                                // round's results visible
+            if (staged) {
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    const uint32_t p = ipos[tid][b];
+                    if (p != kNoItem && p - rb < 256u) {
+                        const float4 u0 = ipart[p - rb][0], u1 = ipart[p - rb][1];
+                        acc0.x += u0.x; acc0.y += u0.y; acc0.z += u0.z; acc0.w += u0.w;
+                        acc1.x += u1.x; acc1.y += u1.y; acc1.z += u1.z; acc1.w += u1.w;
+                    }
+                }
             }
         }
-        __syncthreads();
-        if (idx < rg.y) {
-            const uint32_t slot = eg[tid];
-            if (slot < capacity) {
-                part[2 * (size_t)slot] = make_float4(acc[tid][0], acc[tid][1], acc[tid][2], acc[tid][3]);
-                part[2 * (size_t)slot + 1] = make_float4(acc[tid][4], acc[tid][5], acc[tid][6], acc[tid][7]);
-            }
+        if (staged && slot < capacity) {
+            part[2 * (size_t)slot] = acc0;
+            part[2 * (size_t)slot + 1] = acc1;
         }
-        if (base + 256 < rg.y) __syncthreads();   // the next batch reuses ent / acc / items
+        if (base + kBwdBatch < rg.y) __syncthreads();   // the next batch reuses ent / items / ipos
     }
 }
 

@@ -147,3 +147,33 @@ def test_alpha_grad_termination_stress():
     bg = np.array([0.2, 0.4, 0.6], np.float32)
     G = rng.normal(size=(3, H, W)).astype(np.float32)
     _alpha_case_grad(W, H, p, lg, bg, G)
+
+
+def test_backward_is_bitwise_reproducible():
+    """No atomics: per-pair gradients formed in a fixed order and gathered in emission order."""
+    require_gpu()
+    w = synth.make_workload("kodak_768x512_50k")
+    G = np.random.default_rng(5).normal(size=(3, 512, 768)).astype(np.float32)
+    a = _grad_sum(768, 512, w["params"], G)
+    b = _grad_sum(768, 512, w["params"], G)
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_alpha_backward_is_bitwise_reproducible():
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    p, lg, bg = synth.random_case(191, 300, 200, 4000, sigma=(0.5, 16.0), alpha=True)
+    G = np.random.default_rng(6).normal(size=(3, 200, 300)).astype(np.float32)
+    outs = []
+    for _ in range(2):
+        r = Raster(300, 200, p.shape[0], gi.MODE_ALPHA)
+        P, L, B = dev(p), dev(lg), dev(bg)
+        r.render(P, L, B)
+        dp = torch.zeros((p.shape[0], 8), dtype=torch.float32, device="cuda")
+        dl = torch.zeros(p.shape[0], dtype=torch.float32, device="cuda")
+        db = torch.zeros(3, dtype=torch.float32, device="cuda")
+        r.backward(dev(G), dp, logit=L, background=B, dlogit=dl, dbackground=db)
+        torch.cuda.synchronize()
+        outs.append(np.concatenate([dp.cpu().numpy().ravel(), dl.cpu().numpy(), db.cpu().numpy()]))
+    np.testing.assert_array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
