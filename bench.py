@@ -1,7 +1,8 @@
 """Benchmark: 768x512 synthetic target, 50,000 2D Gaussians, accumulated-sum rendering.
 
-One "step" is the whole hot path on the GPU: gi_preprocess -> gi_bin_sort -> gi_render_fwd ->
-gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared).  `value` is fwd+bwd training
+One "step" is the whole hot path on the GPU: gi_preprocess -> gi_bin_sort -> gi_render_fwd_l2
+(forward raster + L2 loss gradient) -> gi_loss_reduce -> gi_render_bwd -> gi_adam_step_pairs (gather
+of the per-pair gradients + Adam).  `value` is fwd+bwd training
 steps per second on one MI355X with every input resident in HBM.  Also reported: render FPS
 (preprocess + bin/sort + raster), cached-raster FPS (raster only, binning reused), per-kernel
 times from HIP events on the launch stream, the roofline of the dominant kernel, and the CPU
@@ -161,20 +162,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        # events bracket the raster kernels on the stream they are launched on
-        rr = fit.raster
-        rr.preprocess(fit.params)
-        rr.bin(sync=False)
-        ev[k][0].record()
-        rr.forward()
-        ev[k][1].record()
-        gi.gi_loss_l2(fit.target.numel(), rr.image, fit.target, fit.dL, fit.loss, fit.loss_ws)
-        ev[k][2].record()
-        rr.backward(fit.dL, fit.grad)
-        ev[k][3].record()
-        fit.step_count += 1
-        gi.gi_adam_step(fit.n, 8, fit.params, fit.grad, fit.m, fit.v, fit.lr, fit.betas[0], fit.betas[1],
-                        fit.eps, fit.step_count, 1)
+        fit.step(ev[k])       # events bracket the raster kernels on the stream they are launched on
     torch.cuda.synchronize()
     t_train = time.perf_counter() - t0
     fwd_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)])
@@ -232,7 +220,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32, 4),
                 "traffic": traffic, "avg_launch_us": round(secs * 1e6, 2)}
 
-    roof_fwd = roof("fwd", "k_raster_sum.hip", "k_render_sum_fwd", fwd_tf, fwd_s)
+    roof_fwd = roof("fwd", "k_raster_sum.hip", "k_render_sum_fwd<true>", fwd_tf, fwd_s)
     roof_bwd = roof("bwd", "k_raster_sum.hip", "k_render_sum_bwd", bwd_tf, bwd_s)
     dominant = roof_bwd if bwd_s >= fwd_s else roof_fwd
 

@@ -174,6 +174,25 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
                         void *stream);
 
 /*
+ * gi_render_fwd_l2 -- gi_render_fwd (sum mode) fused with the L2 loss of
+ *   "FlashImgs" (train --loss l2): besides the image it writes
+ *     dL_dimage = 2 (image - target) / (3 W H)
+ *   and loss_partials[t] = sum over tile t's pixels and channels of
+ *   (image - target)^2 (fp32, a fixed order); gi_loss_reduce turns the partials
+ *   into the loss.  Same image bits as gi_render_fwd.
+ *   target      device float [3][H][W].
+ *   dL_dimage   device float [3][H][W] out.
+ *   loss_partials device float [T] out (T = gi_num_tiles).
+ */
+gi_status gi_render_fwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
+                           const uint32_t *ranges, const uint32_t *vals, const float *target,
+                           float *image, float *dL_dimage, float *loss_partials, void *stream);
+
+/* d_loss (device float [1]) = (sum of the nparts partials, in fp64, fixed order) / count. */
+gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t count, float *d_loss,
+                         void *stream);
+
+/*
  * gi_render_bwd -- gradients of a scalar loss L given dL/dimage.
  *   Reading of "Drawing with Gaussians" (fused rasterization kernels with
  *   custom VJPs): the exact derivative of gi_render_fwd's image, with the
@@ -193,7 +212,9 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
  *   background, t_final, last: as given to / produced by gi_render_fwd (alpha
  *             mode; NULL in sum mode).
  *   dL_dimage device float [3][H][W].
- *   dparams   device float [n][8], ACCUMULATED (+=) in the params layout.
+ *   dparams   device float [n][8], ACCUMULATED (+=) in the params layout; in sum
+ *             mode it may be NULL, which leaves the per-pair gradients in the
+ *             workspace for gi_adam_step_pairs (no gather pass).
  *   dlogit    device float [n], accumulated (alpha mode) or NULL.
  *   dbackground device float [3], accumulated (alpha mode) or NULL.
  *   workspace device scratch of gi_render_bwd_workspace_bytes() bytes, 256-byte
@@ -242,6 +263,21 @@ gi_status gi_loss_l2(int64_t count, const float *image, const float *target, flo
 gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v,
                        const float *lr, double beta1, double beta2, double eps, int32_t step,
                        int32_t zero_grad, void *stream);
+
+/*
+ * gi_adam_step_pairs -- gi_adam_step (rows of 8, sum mode) whose gradient is
+ *   read straight from the per-pair slots that gi_render_bwd(dparams = NULL)
+ *   left in its workspace: each Gaussian's slots offsets[g] .. offsets[g+1]
+ *   are added in emission order (the gather) and the Adam update applied in
+ *   the same pass.  Same arguments as gi_render_bwd for the slots (desc, n,
+ *   offsets, capacity, workspace) and as gi_adam_step for the update (p, m, v
+ *   device float [n][8]; lr host float [8]).  A binning overflow gives a zero
+ *   gradient.
+ */
+gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
+                             const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
+                             const float *lr, double beta1, double beta2, double eps, int32_t step,
+                             void *stream);
 
 #ifdef __cplusplus
 }

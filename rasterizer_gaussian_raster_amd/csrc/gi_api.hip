@@ -95,11 +95,27 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
     if (desc->mode == GI_MODE_SUM) {
         if (opacity || background || t_final || last) return GI_ERR_INVALID_ARG;
         return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, vals,
-                                                    image, s));
+                                                    image, nullptr, nullptr, nullptr, s));
     }
     if (!background || !t_final || !last || (n > 0 && !opacity)) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_render_alpha_fwd(desc->width, desc->height, records, opacity, pixbox, ranges,
                                                   vals, background, image, t_final, last, s));
+}
+
+gi_status gi_render_fwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
+                           const uint32_t *ranges, const uint32_t *vals, const float *target, float *image,
+                           float *dL_dimage, float *loss_partials, void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!ranges || !vals || !image || !target || !dL_dimage || !loss_partials || !aligned16(image))
+        return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, vals, image,
+                                                target, dL_dimage, loss_partials, as_stream(stream)));
+}
+
+gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t count, float *d_loss, void *stream) {
+    if (nparts < 1 || nparts >= (1ll << 31) || count < 1 || !loss_partials || !d_loss) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_loss_reduce((int)nparts, loss_partials, count, d_loss, as_stream(stream)));
 }
 
 size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
@@ -118,7 +134,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     if (!offsets || !ranges || !vals || !dL_dimage || !workspace || !aligned256(workspace))
         return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
-    if (n > 0 && (!records || !pixbox || !dparams || !aligned16(records) || !aligned16(dparams)))
+    if (n > 0 && (!records || !pixbox || !aligned16(records) || (dparams && !aligned16(dparams))))
         return GI_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     const int W = desc->width, H = desc->height;
@@ -127,11 +143,12 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     if (desc->mode == GI_MODE_SUM) {
         if (opacity || logit || background || t_final || last || dlogit || dbackground) return GI_ERR_INVALID_ARG;
         e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, vals, capacity, dL_dimage, workspace, s);
-        if (e == hipSuccess)
+        if (e == hipSuccess && dparams)
             e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 0, dparams, nullptr,
                                        nullptr, s);
         return hip_status(e);
     }
+    if (n > 0 && !dparams) return GI_ERR_INVALID_ARG;
     if (!background || !t_final || !last || (n > 0 && (!opacity || !logit))) return GI_ERR_INVALID_ARG;
     e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, vals, capacity,
                                     background, t_final, last, dL_dimage, workspace, s);
@@ -149,6 +166,20 @@ gi_status gi_loss_l2(int64_t count, const float *image, const float *target, flo
     if (workspace_bytes < gi::loss_workspace_bytes(count) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
         return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_loss_l2(count, image, target, dL_dimage, d_loss, workspace, as_stream(stream)));
+}
+
+gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
+                             const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
+                             const float *lr, double beta1, double beta2, double eps, int32_t step, void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+        capacity >= (1ll << 31) || step < 1 || !lr)
+        return GI_ERR_INVALID_ARG;
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0)) return GI_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!p || !m || !v || !aligned16(p) || !aligned16(m) || !aligned16(v))) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_adam_pairs((int)n, desc->width, desc->height, offsets, capacity, workspace, p, m, v,
+                                            lr, beta1, beta2, eps, step, as_stream(stream)));
 }
 
 gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v, const float *lr,

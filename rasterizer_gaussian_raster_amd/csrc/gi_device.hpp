@@ -46,6 +46,25 @@ __device__ __forceinline__ float wave_total(float x) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND_CTRL = false>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, BANK_MASK, BOUND_CTRL);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP (all lanes active): three
+// row_shr steps give sums of 4, then row_shr 4 / 8 on the upper banks finish
+// each 16-lane row, and the row_bcast 15 / 31 steps carry rows into rows.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+    uint32_t v = x + dpp_u<0x111, 0xf, 0xf, true>(x);      // row_shr:1
+    v += dpp_u<0x112, 0xf, 0xf, true>(x);                   // row_shr:2
+    v += dpp_u<0x113, 0xf, 0xf, true>(x);                   // row_shr:3
+    v += dpp_u<0x114, 0xf, 0xe>(v);                         // row_shr:4, lanes 4..15 of each row
+    v += dpp_u<0x118, 0xf, 0xc>(v);                         // row_shr:8, lanes 8..15 of each row
+    v += dpp_u<0x142, 0xa>(v);                              // row_bcast:15 into rows 1 and 3
+    v += dpp_u<0x143, 0xc>(v);                              // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // XCD-aware block -> work-item map: the hardware deals consecutive workgroups
 // round-robin over the 8 XCDs; give each XCD a contiguous run of work items so
 // neighbouring tiles (which share Gaussians) hit the same L2.  The grid must

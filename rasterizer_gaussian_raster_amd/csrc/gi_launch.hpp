@@ -30,7 +30,12 @@ const void *bin_total_ptr(const void *ws);
 
 // k_raster_sum.hip
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *vals, float *image, hipStream_t s);
+                                 const uint32_t *ranges, const uint32_t *vals, float *image, const float *target,
+                                 float *dL_dimage, float *loss_partials, hipStream_t s);
+hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, float *d_loss, hipStream_t s);
+hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
+                             float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
+                             hipStream_t s);
 
 // Backward workspace: per (Gaussian, tile) gradient at its emission slot.
 struct BwdPlan {

@@ -43,15 +43,24 @@ struct BinHeader {
 // ---------------------------------------------------------------------------
 // block-wide exclusive scan (NT threads, wave64)
 // ---------------------------------------------------------------------------
-template <typename T, int NT>
-__device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <typename T>
+__device__ __forceinline__ T wave_scan_any(T x) {
+    const int lane = threadIdx.x & 63;
     T inc = x;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
         T y = __shfl_up(inc, d, 64);
         if (lane >= d) inc += y;
     }
+    return inc;
+}
+template <>
+__device__ __forceinline__ uint32_t wave_scan_any<uint32_t>(uint32_t x) { return wave_scan_incl(x); }
+
+template <typename T, int NT>
+__device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const T inc = wave_scan_any<T>(x);
     if (lane == 63) smem[wave] = inc;
     __syncthreads();
     T off = 0, tot = 0;
@@ -257,10 +266,11 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(const uint32_t *_
 // otherwise reduce -> scan of block sums -> rescan with offsets.
 // count <= 1024 * kScanSingleItems.  Element r * 1024 + i lives in thread i's
 // register v[r] (coalesced loads, all issued together); its exclusive prefix is
-// the totals of rows before r plus the prefix of row r over threads before i.
+// the totals of rows before r, plus the row-r totals of waves before thread i's
+// wave, plus the DPP wave scan within the wave.
 constexpr int kScanSingleItems = 32;
 __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, int count) {
-    __shared__ uint32_t wsum[16][kScanSingleItems + 1];   // [wave][row] totals
+    __shared__ uint32_t wsum[16][kScanSingleItems];     // [wave][row] totals -> exclusive over waves
     __shared__ uint32_t rowpre[kScanSingleItems];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rows = (count + 1023) / 1024;
@@ -273,36 +283,31 @@ __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, 
 #pragma unroll
     for (int r = 0; r < kScanSingleItems; ++r) {
         if (r >= rows) break;
-        uint32_t x = v[r];
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t y = __shfl_up(x, d, 64);
-            if (lane >= d) x += y;
-        }
-        inc[r] = x;
-        if (lane == 63) wsum[wave][r] = x;
+        inc[r] = wave_scan_incl(v[r]);
+        if (lane == 63) wsum[wave][r] = inc[r];
     }
     __syncthreads();
-    if (tid < 64) {            // one wave: row totals -> exclusive prefix over rows
-        uint32_t tot = 0;
-        if (tid < rows)
-            for (int w = 0; w < 16; ++w) tot += wsum[w][tid];
-        uint32_t x = tot;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t y = __shfl_up(x, d, 64);
-            if (lane >= d) x += y;
+    if (tid < rows) {                     // one thread per row: exclusive over waves, row total
+        uint32_t run = 0;
+        for (int w = 0; w < 16; ++w) {
+            const uint32_t x = wsum[w][tid];
+            wsum[w][tid] = run;
+            run += x;
         }
+        rowpre[tid] = run;
+    }
+    __syncthreads();
+    if (tid < 64) {                       // one wave: exclusive over rows
+        const uint32_t tot = tid < rows ? rowpre[tid] : 0u;
+        const uint32_t x = wave_scan_incl(tot);
         if (tid < rows) rowpre[tid] = x - tot;
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kScanSingleItems; ++r) {
         if (r >= rows) break;
-        uint32_t o = rowpre[r] + inc[r] - v[r];
-        for (int w = 0; w < wave; ++w) o += wsum[w][r];
         const int e = r * 1024 + tid;
-        if (e < count) a[e] = o;
+        if (e < count) a[e] = rowpre[r] + wsum[wave][r] + inc[r] - v[r];
     }
 }
 

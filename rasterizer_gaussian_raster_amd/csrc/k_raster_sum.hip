@@ -34,12 +34,18 @@ struct SumRec { float4 p, q; };   // p = (mux, muy, a, b), q = (c, cr, cg, cb)
 
 constexpr int kFwdBatch = 128;    // list entries staged per round (16 KB of LDS: 8+ workgroups per CU)
 
+// L2 = true also forms the L2 loss gradient 2 (I - T) / (3 W H) from the target
+// and each tile's sum of squared residuals (reduced over the tile in a fixed order).
+template <bool L2>
 __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
                                                         const uint2 *__restrict__ ranges,
                                                         const uint32_t *__restrict__ vals,
-                                                        float *__restrict__ image) {
+                                                        float *__restrict__ image,
+                                                        const float *__restrict__ target,
+                                                        float *__restrict__ dL, float gscale,
+                                                        float *__restrict__ loss_part) {
     __shared__ SumRec lst[4][kFwdBatch];
     __shared__ int wq[4][4];                      // [wave][quadrant]: staged count this batch
     const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -103,12 +109,42 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
         }
         if (base + kFwdBatch < rg.y) __syncthreads();   // the next batch reuses lst / wq
     }
+    float sq = 0.0f;
     if (pxi < W && pyi < H) {
         const size_t o = (size_t)pyi * W + pxi, plane = (size_t)W * H;
         image[o] = ar;
         image[o + plane] = ag;
         image[o + 2 * plane] = ab;
+        if (L2) {
+            const float rr = ar - target[o], rgr = ag - target[o + plane], rbr = ab - target[o + 2 * plane];
+            dL[o] = gscale * rr;
+            dL[o + plane] = gscale * rgr;
+            dL[o + 2 * plane] = gscale * rbr;
+            sq = fmaf(rbr, rbr, fmaf(rgr, rgr, rr * rr));
+        }
     }
+    if (L2) {
+        __shared__ float wsq[4];
+        const float ws = wave_total(sq);
+        if (lane == 0) wsq[wave] = ws;
+        __syncthreads();
+        if (tid == 0) loss_part[t] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
+    }
+}
+
+// Sum of the per-tile partials in a fixed order, divided by the entry count.
+__global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__restrict__ part, double inv_count,
+                                                     float *__restrict__ loss) {
+    __shared__ double sm[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *loss = (float)(sm[0] * inv_count);
 }
 
 // Backward work item: one (list entry, 4x4 pixel block) pair per thread.  Items
@@ -320,6 +356,48 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
     if (dlogit) dlogit[g] += l;
 }
 
+// Adam on each Gaussian's 8 parameters with the gradient gathered from its
+// pairs' slots (offsets[g] .. offsets[g+1], emission order): the gather and
+// the optimizer in one pass, no gradient array.
+struct AdamPairArgs {
+    float lr[8];
+    float b1, omb1, b2, omb2, eps, inv_bc1, inv_sqrt_bc2;
+};
+
+__device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, float lr, const AdamPairArgs &a) {
+    m = fmaf(a.b1, m, a.omb1 * g);
+    v = fmaf(a.b2, v, a.omb2 * g * g);
+    p -= lr * (m * a.inv_bc1) / (sqrtf(v) * a.inv_sqrt_bc2 + a.eps);
+}
+
+__global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
+                                                    const float4 *__restrict__ part, float4 *__restrict__ p,
+                                                    float4 *__restrict__ m, float4 *__restrict__ v, AdamPairArgs a) {
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= n) return;
+    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    if (offsets[n] <= capacity) {                 // else binning overflowed: zero gradient
+        const uint32_t o0 = offsets[g], o1 = offsets[g + 1];
+        for (uint32_t q = o0; q < o1; ++q) {
+            const float4 u = part[2 * (size_t)q], w = part[2 * (size_t)q + 1];
+            g0.x += u.x; g0.y += u.y; g0.z += u.z; g0.w += u.w;
+            g1.x += w.x; g1.y += w.y; g1.z += w.z; g1.w += w.w;
+        }
+    }
+    float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
+    adam1(P0.x, g0.x, M0.x, V0.x, a.lr[0], a);
+    adam1(P0.y, g0.y, M0.y, V0.y, a.lr[1], a);
+    adam1(P0.z, g0.z, M0.z, V0.z, a.lr[2], a);
+    adam1(P0.w, g0.w, M0.w, V0.w, a.lr[3], a);
+    adam1(P1.x, g1.x, M1.x, V1.x, a.lr[4], a);
+    adam1(P1.y, g1.y, M1.y, V1.y, a.lr[5], a);
+    adam1(P1.z, g1.z, M1.z, V1.z, a.lr[6], a);
+    adam1(P1.w, g1.w, M1.w, V1.w, a.lr[7], a);
+    p[2 * g] = P0; p[2 * g + 1] = P1;
+    m[2 * g] = M0; m[2 * g + 1] = M1;
+    v[2 * g] = V0; v[2 * g + 1] = V1;
+}
+
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -334,6 +412,26 @@ BwdPlan make_bwd_plan(int W, int H, int64_t capacity) {
     p.off_bg = off; off = align256(off + 16 * (size_t)ntiles);
     p.bytes = off;
     return p;
+}
+
+hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
+                             float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
+                             hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const BwdPlan pl = make_bwd_plan(W, H, capacity);
+    AdamPairArgs a{};
+    for (int i = 0; i < 8; ++i) a.lr[i] = lr[i];
+    a.b1 = (float)beta1;
+    a.omb1 = (float)(1.0 - beta1);
+    a.b2 = (float)beta2;
+    a.omb2 = (float)(1.0 - beta2);
+    a.eps = (float)eps;
+    a.inv_bc1 = (float)(1.0 / (1.0 - pow(beta1, (double)step)));
+    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(beta2, (double)step)));
+    k_adam_pairs<<<(n + 255) / 256, 256, 0, s>>>(
+        n, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(static_cast<const char *>(ws) + pl.off_part),
+        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a);
+    return hipGetLastError();
 }
 
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
@@ -352,12 +450,25 @@ hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *o
 }
 
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *vals, float *image, hipStream_t s) {
+                                 const uint32_t *ranges, const uint32_t *vals, float *image, const float *target,
+                                 float *dL_dimage, float *loss_partials, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
-    k_render_sum_fwd<<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles,
-                                                          reinterpret_cast<const float4 *>(records),
-                                                          reinterpret_cast<const uint2 *>(pixbox),
-                                                          reinterpret_cast<const uint2 *>(ranges), vals, image);
+    const float4 *rec = reinterpret_cast<const float4 *>(records);
+    const uint2 *bx = reinterpret_cast<const uint2 *>(pixbox);
+    const uint2 *rg = reinterpret_cast<const uint2 *>(ranges);
+    if (target) {
+        const float gscale = (float)(2.0 / (3.0 * (double)W * (double)H));
+        k_render_sum_fwd<true><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, vals, image,
+                                                                     target, dL_dimage, gscale, loss_partials);
+    } else {
+        k_render_sum_fwd<false><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, vals,
+                                                                      image, nullptr, nullptr, 0.0f, nullptr);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, float *d_loss, hipStream_t s) {
+    k_loss_reduce<<<1, 256, 0, s>>>(nparts, partials, 1.0 / (double)count, d_loss);
     return hipGetLastError();
 }
 

@@ -60,6 +60,9 @@ def load():
         "gi_loss_workspace_bytes": ([i64], sz),
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
+        "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P], i32),
+        "gi_loss_reduce": ([i64, P, i64, P, P], i32),
+        "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -160,3 +163,22 @@ def gi_adam_step(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_gr
     _check(load().gi_adam_step(int(rows), int(row_len), _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr_arr,
                                float(beta1), float(beta2), float(eps), int(step), int(zero_grad),
                                _stream(stream)), "gi_adam_step")
+
+
+def gi_render_fwd_l2(d, n, records, pixbox, ranges, vals, target, image, dL_dimage, loss_partials, stream=None):
+    _check(load().gi_render_fwd_l2(ctypes.byref(d), int(n), _ptr(records), _ptr(pixbox), _ptr(ranges), _ptr(vals),
+                                   _ptr(target), _ptr(image), _ptr(dL_dimage), _ptr(loss_partials),
+                                   _stream(stream)), "gi_render_fwd_l2")
+
+
+def gi_loss_reduce(nparts, loss_partials, count, d_loss, stream=None):
+    _check(load().gi_loss_reduce(int(nparts), _ptr(loss_partials), int(count), _ptr(d_loss), _stream(stream)),
+           "gi_loss_reduce")
+
+
+def gi_adam_step_pairs(d, n, offsets, capacity, workspace, p, m, v, lr, beta1, beta2, eps, step, stream=None):
+    lr_arr = (ctypes.c_float * 8)(*[float(x) for x in lr])
+    _check(load().gi_adam_step_pairs(ctypes.byref(d), int(n), _ptr(offsets), int(capacity), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _ptr(p), _ptr(m), _ptr(v),
+                                     lr_arr, float(beta1), float(beta2), float(eps), int(step), _stream(stream)),
+           "gi_adam_step_pairs")

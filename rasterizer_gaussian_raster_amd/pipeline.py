@@ -4,7 +4,9 @@ Torch provides device memory and the stream; every step below is one call of
 the C ABI (through :mod:`.gi`):
 
   render : gi_preprocess -> gi_bin_sort -> gi_render_fwd
-  fit    : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
+  fit (sum mode)   : gi_preprocess -> gi_bin_sort -> gi_render_fwd_l2 -> gi_loss_reduce
+                     -> gi_render_bwd (pair gradients left in its workspace) -> gi_adam_step_pairs
+  fit (alpha mode) : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
 
 uint32/uint16 device arrays are held in int32/int16 tensors (same bytes).
 """
@@ -39,6 +41,7 @@ class Raster:
         self.image = torch.empty((3, self.H, self.W), dtype=torch.float32, device=dev)
         self.t_final = torch.empty((self.H, self.W), dtype=torch.float32, device=dev) if alpha else None
         self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev) if alpha else None
+        self.loss_partials = torch.empty(max(self.T, 1), dtype=torch.float32, device=dev)
         self.capacity = 0
         self.keys = self.vals = self.ws = self.bwd_ws = None
         self.M = None
@@ -87,8 +90,14 @@ class Raster:
                          background, self.image, self.t_final, self.last, stream)
         return self.image
 
+    def forward_l2(self, target, dL_dimage, stream=None):
+        gi.gi_render_fwd_l2(self.desc, self.n, self.records, self.pixbox, self.ranges, self.vals, target, self.image,
+                            dL_dimage, self.loss_partials, stream)
+        return self.image
+
     def backward(self, dL_dimage, dparams, logit=None, background=None, dlogit=None, dbackground=None,
                  stream=None):
+        """dparams=None (sum mode): leave the per-pair gradients in the workspace for adam_pairs."""
         if self.bwd_ws is None:
             nbytes = gi.gi_render_bwd_workspace_bytes(self.desc, self.n, self.capacity)
             self.bwd_ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device(self.device))
@@ -135,33 +144,53 @@ class Fitter:
         self.raster.preprocess(self.params, self.logit)
         M = self.raster.bin(sync=True)
         self.raster.set_capacity(int(M * capacity_slack) + 4096)
+        self.raster.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(self.raster.desc, self.n,
+                                                                          self.raster.capacity),
+                                         dtype=torch.uint8, device=dev)
 
     def check_capacity(self):
         """Host wait: grow the pair buffers when the last binning came near (or over) capacity."""
         M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
         if M > 0.8 * self.raster.capacity:
             self.raster.set_capacity(int(M * self.slack) + 4096)
+            self.raster.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(self.raster.desc, self.n,
+                                                                              self.raster.capacity),
+                                             dtype=torch.uint8, device=self.params.device)
             return True
         return False
 
-    def step(self):
+    def step(self, events=None):
+        """One training step.  events: optional 4 torch events recorded around the raster kernels
+        (before/after forward, before/after backward) on the current stream."""
         r = self.raster
-        bg = self.bg4 if self.logit is not None else None
+        ev = events if events is not None else (None,) * 4
+        if self.logit is None:
+            r.preprocess(self.params)
+            r.bin(sync=False)
+            ev[0] is not None and ev[0].record()
+            r.forward_l2(self.target, self.dL)
+            ev[1] is not None and ev[1].record()
+            gi.gi_loss_reduce(r.T, r.loss_partials, self.target.numel(), self.loss)
+            ev[2] is not None and ev[2].record()
+            r.backward(self.dL, None)
+            ev[3] is not None and ev[3].record()
+            self.step_count += 1
+            b1, b2 = self.betas
+            gi.gi_adam_step_pairs(r.desc, self.n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v,
+                                  self.lr, b1, b2, self.eps, self.step_count)
+            return
+        bg = self.bg4
         r.preprocess(self.params, self.logit)
         r.bin(sync=False)
         r.forward(bg)
         gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
-        if self.logit is None:
-            r.backward(self.dL, self.grad)
-        else:
-            r.backward(self.dL, self.grad, logit=self.logit, background=bg, dlogit=self.g_logit,
-                       dbackground=self.g_bg)
+        r.backward(self.dL, self.grad, logit=self.logit, background=bg, dlogit=self.g_logit,
+                   dbackground=self.g_bg)
         self.step_count += 1
         b1, b2 = self.betas
         gi.gi_adam_step(self.n, 8, self.params, self.grad, self.m, self.v, self.lr, b1, b2, self.eps,
                         self.step_count, 1)
-        if self.logit is not None:
-            gi.gi_adam_step(self.n, 1, self.logit, self.g_logit, self.m_logit, self.v_logit, [self.lr_logit],
-                            b1, b2, self.eps, self.step_count, 1)
-            gi.gi_adam_step(1, 4, self.bg4, self.g_bg, self.m_bg, self.v_bg, [self.lr_bg] * 3 + [0.0],
-                            b1, b2, self.eps, self.step_count, 1)
+        gi.gi_adam_step(self.n, 1, self.logit, self.g_logit, self.m_logit, self.v_logit, [self.lr_logit],
+                        b1, b2, self.eps, self.step_count, 1)
+        gi.gi_adam_step(1, 4, self.bg4, self.g_bg, self.m_bg, self.v_bg, [self.lr_bg] * 3 + [0.0],
+                        b1, b2, self.eps, self.step_count, 1)
