@@ -30,6 +30,7 @@ namespace gi {
 constexpr int kSortThreads = 256;
 constexpr int kSortIters = 4;
 constexpr int kMaxRedundantGroups = 2048;              // emit sums the group totals itself up to this
+constexpr int kMaxRawTable = 0;                        // scatter forms its digit offsets itself up to this (off: slower)
 constexpr int kSortChunk = kSortThreads * kSortIters;   // keys per sort block
 constexpr int kScanItems = 16;
 constexpr int kScanChunk = 256 * kScanItems;           // table entries per scan block
@@ -211,21 +212,42 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint32_t *__r
     if (tid < radix) table[(size_t)tid * nbs + blockIdx.x] = h[tid];
 }
 
+// `counts_raw`: the table holds the digit counts themselves (no scan pass ran);
+// each block then forms its own offsets: thread d adds digit d's counts over the
+// blocks in use (those before this one, and all of them for the digit total),
+// and a block scan over the digit totals gives each digit's start.
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(const uint32_t *__restrict__ kin,
                                                                const uint32_t *__restrict__ vin,
                                                                uint32_t *__restrict__ kout,
                                                                uint32_t *__restrict__ vout,
                                                                const BinHeader *__restrict__ hdr, int shift,
                                                                int bits, const uint32_t *__restrict__ table,
-                                                               int nbs) {
+                                                               int nbs, int counts_raw) {
     __shared__ uint32_t run[256];          // next output slot per digit
     __shared__ uint32_t wcnt[4][256];      // per wave: keys of each digit in this round
+    __shared__ uint32_t sm[4];
     const uint32_t M = hdr->m_eff;
     const uint32_t base = blockIdx.x * (uint32_t)kSortChunk;
     if (base >= M) return;
     const int radix = 1 << bits;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (tid < radix) run[tid] = table[(size_t)tid * nbs + blockIdx.x];
+    if (counts_raw) {
+        const int used = (int)((M + kSortChunk - 1) / kSortChunk);
+        uint32_t before = 0, total = 0;
+        if (tid < radix) {
+            const uint32_t *row = table + (size_t)tid * nbs;
+            for (int b = 0; b < used; ++b) {
+                const uint32_t c = row[b];
+                total += c;
+                before += b < (int)blockIdx.x ? c : 0u;
+            }
+        }
+        uint32_t all;
+        const uint32_t start = block_exclusive_scan<uint32_t, kSortThreads>(total, sm, &all);
+        if (tid < radix) run[tid] = start + before;
+    } else if (tid < radix) {
+        run[tid] = table[(size_t)tid * nbs + blockIdx.x];
+    }
     for (int i = tid; i < 4 * 256; i += kSortThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const uint64_t below = lanes_below();
@@ -437,9 +459,12 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     for (int pass = 0; pass < p.passes && p.nbs > 0; ++pass) {
         const int bits = p.bits[pass];
         k_sort_count<<<p.nbs, kSortThreads, 0, s>>>(srck, hdr, shift, bits, table, p.nbs);
-        e = scan_u32(table, (1 << bits) * p.nbs, tsp, s);
-        if (e != hipSuccess) return e;
-        k_sort_scatter<<<p.nbs, kSortThreads, 0, s>>>(srck, srcv, dstk, dstv, hdr, shift, bits, table, p.nbs);
+        const int raw = (1 << bits) * p.nbs <= kMaxRawTable;
+        if (!raw) {
+            e = scan_u32(table, (1 << bits) * p.nbs, tsp, s);
+            if (e != hipSuccess) return e;
+        }
+        k_sort_scatter<<<p.nbs, kSortThreads, 0, s>>>(srck, srcv, dstk, dstv, hdr, shift, bits, table, p.nbs, raw);
         shift += bits;
         uint32_t *tk = srck, *tv = srcv;
         srck = dstk; srcv = dstv; dstk = tk; dstv = tv;
