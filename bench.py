@@ -81,7 +81,7 @@ def load_traffic(kernel_file, kernel_name):
     return None
 
 
-def cpu_baseline(wl, params, target_seconds=12.0):
+def cpu_baseline(wl, params, target_seconds=15.0):
     """The oracle (brute force over all N Gaussians per pixel, fp64) on a bounded pixel sample:
     sum render + analytic gradient of the same pixels, extrapolated to one full-frame step."""
     import oracle
@@ -100,10 +100,12 @@ def cpu_baseline(wl, params, target_seconds=12.0):
         return time.perf_counter() - t0
 
     run(64)                                    # load + warm
-    probe = 256
-    tp = run(probe)
-    npix = int(min(W * H, max(probe, probe * target_seconds / max(tp, 1e-6))))
+    npix = 256
     t = run(npix)
+    # grow the sample until it holds most of the time budget (small samples are overhead-bound)
+    while t < 0.6 * target_seconds and npix < W * H:
+        npix = int(min(W * H, npix * min(16.0, max(2.0, target_seconds / max(t, 1e-3)))))
+        t = run(npix)
     per_frame = t * (W * H) / npix
     return {"value": 1.0 / per_frame, "unit": "fwd+bwd steps/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{npix} random pixels of the {W}x{H} frame, all {params.shape[0]} Gaussians per pixel "
