@@ -15,10 +15,15 @@ hipError_t launch_preprocess(int n, int W, int H, const float *params, const flo
 struct BinPlan {
     int n, W, H, tiles_x, ntiles;
     int64_t capacity;
-    int passes;            // LSD passes (0 when there is a single tile)
+    int passes;            // LSD passes (>= 1; a single tile takes one 0-bit pass)
     int bits[4];           // digit width of each pass
-    int nb_g;              // Gaussian groups of 256 (emission blocks)
-    int nbs;               // sort blocks of kSortChunk keys over the capacity
+    int nb_g;              // Gaussian groups of 256
+    int redundant_groups;  // group bases summed by each block (no group-scan kernel)
+    int seg_groups, nseg;  // groups per first-pass segment, number of segments
+    int pass_lanes;        // keys per lane in the later passes' blocks (4, 8 or 16)
+    int nbs;               // sort blocks of 256 * pass_lanes keys over the capacity (later passes)
+    int ncols_cap[4];      // digit-table columns of each pass
+    int table_redundant[4];// digit table read raw by every block (no scan kernel)
     size_t off_part, off_kalt, off_valt, off_table, off_tsp, bytes;
 };
 BinPlan make_bin_plan(int n, int W, int H, int64_t capacity);

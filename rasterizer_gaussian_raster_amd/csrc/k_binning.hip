@@ -1,39 +1,49 @@
 // k_binning.hip -- tile lists from per-Gaussian pixel boxes.
 //
-//   1. k_group_sums   : per 256-Gaussian group, sum of tile counts (u64); clears
-//                       the tile ranges.
-//   2. k_group_scan   : one workgroup scans the group sums -> group bases, M
-//                       (only for more than 2048 groups; below that each emit
-//                       workgroup adds up the sums before it itself).
-//   3. k_emit         : per group, offsets[] and one (tile id, index) pair per
-//                       covered tile, emitted in (index, tile row, tile column)
-//                       order; the group's pairs are spread evenly over its
-//                       256 lanes by a binary search in LDS (no lane walks a
-//                       large Gaussian alone).
-//   4. LSD radix sort on the tile id, 1..8-bit digits per pass (as many passes
-//      as the id needs), each pass = digit counts per 4096-key block ->
-//      exclusive scan of the digit-major count table -> stable scatter, where
-//      each key's rank among equal digits is found with wave ballots in key
-//      order, so the sort is stable and each tile list ends up in ascending
-//      Gaussian index.
-//   5. k_ranges       : one thread per sorted pair marks where each tile's run
-//                       starts and ends.
+// Every Gaussian g covers a rectangle of tiles; its pairs (tile id, g) are
+// numbered in (index, tile row, tile column) order, pair m of g sitting at
+// emission slot offsets[g] + m.  A stable LSD radix sort on the tile id then
+// leaves each tile's list in ascending Gaussian index.
+//
+//   1. k_group_sums : per 256-Gaussian group, the sum of tile counts (u64);
+//                     clears the tile ranges.
+//   2. k_group_scan : one workgroup scans the group sums (only for more than
+//                     2048 groups; below that every block of step 3 adds up the
+//                     sums before it itself).
+//   3. k_count0     : per segment of 1 or 4 groups: offsets[], M, and the
+//                     histogram of the first digit over the segment's pairs.
+//                     The pairs are never written in emission order: they are
+//                     regenerated from the pixel boxes wherever they are needed
+//                     (a binary search in LDS spreads a group's pairs evenly over
+//                     its 256 lanes, so no lane walks a large Gaussian alone).
+//   4. k_scatter0   : first sort pass, straight from the regenerated pairs.
+//   5. k_count / k_scatter : further passes over blocks of 1024-4096 keys.
+//   6. k_ranges     : marks where each tile's run starts and ends.
+//
+// Each scatter block ranks up to 4096 keys at a time: every wave takes a
+// contiguous span of the chunk and finds the rank of each key among the equal
+// digits of its span with wave ballots (in key order, hence stable); the chunk
+// is then reordered by digit in LDS and written out in runs, so consecutive
+// lanes store to consecutive addresses.  Digit tables of up to ~20K entries are
+// never scanned by a kernel of their own: each scatter block adds up the
+// entries it needs itself.
 //
 // Binning is the tile-binned scheme of the FlashImgs viewer ("Web viewer":
 // tile-binned compute) with fvdb's 16-pixel tiles (tile_size).  All steps are
-// HBM/latency bound: ~20 B per pair per sort pass, 12 B per Gaussian to emit.
+// HBM or latency bound: ~20 B per pair per sort pass after the first.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
 
 namespace gi {
 
-constexpr int kSortThreads = 256;
-constexpr int kSortIters = 4;
-constexpr int kMaxRedundantGroups = 2048;              // emit sums the group totals itself up to this
-constexpr int kMaxRawTable = 0;                        // scatter forms its digit offsets itself up to this (off: slower)
-constexpr int kSortChunk = kSortThreads * kSortIters;   // keys per sort block
+constexpr int kBT = 256;                       // threads per binning block
+constexpr int kPerLane = 16;                   // keys per lane per chunk (at most)
+constexpr int kChunk = kBT * kPerLane;         // keys per first-pass chunk
+constexpr int kMaxRedundantGroups = 2048;      // count0 adds up the group sums itself up to this
+constexpr int kMaxRedundantTable = 32768;      // digit tables up to this are not scanned ...
+constexpr int64_t kMaxRedundantReads = 8 << 20;// ... when all blocks together read at most this many entries
 constexpr int kScanItems = 16;
-constexpr int kScanChunk = 256 * kScanItems;           // table entries per scan block
+constexpr int kScanChunk = 256 * kScanItems;   // table entries per scan block
 
 struct BinHeader {
     unsigned long long total;   // M, 64-bit
@@ -76,21 +86,244 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *t
     return off + inc - x;
 }
 
+__device__ __forceinline__ uint32_t sat32(unsigned long long x) { return x > 0xffffffffull ? 0xffffffffu : (uint32_t)x; }
+
 // ---------------------------------------------------------------------------
-// 1-3: counts -> offsets -> emitted pairs
+// pair regeneration: a segment's exclusive scan of tile counts and its boxes in LDS
 // ---------------------------------------------------------------------------
-// Also clears the tile ranges (tiles that receive no pair keep (0, 0)).
-__global__ __launch_bounds__(256) void k_group_sums(int n, const uint32_t *__restrict__ counts,
+template <int S>
+struct SegLds {
+    uint32_t excl[S + 1];
+    uint2 box[S];
+};
+
+// Pair `idx` (< excl[ns]) of a segment of ns Gaussians: its tile id and the
+// segment-local index of its Gaussian (the last l with excl[l] <= idx, which
+// never names a Gaussian without tiles).
+template <int S>
+__device__ __forceinline__ void regen_pair(const SegLds<S> &G, int ns, uint32_t idx, int tiles_x, uint32_t &key,
+                                           int &lo) {
+    int l = 0;
+#pragma unroll
+    for (int step = S >> 1; step > 0; step >>= 1)
+        if (l + step < ns && G.excl[l + step] <= idx) l += step;
+    const uint32_t r = idx - G.excl[l];
+    const uint2 bx = G.box[l];
+    const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
+    const uint32_t tx1 = (bx.y & 0xffffu) >> 4;
+    const uint32_t wt = tx1 - tx0 + 1;
+    const uint32_t q = r / wt, rem = r - q * wt;
+    key = (ty0 + q) * (uint32_t)tiles_x + tx0 + rem;
+    lo = l;
+}
+
+// ---------------------------------------------------------------------------
+// digit bases of one sort block
+// ---------------------------------------------------------------------------
+// Table layouts: "redundant" = [column][radix] raw counts (radix >= 4), read
+// by every block; "scanned" = [radix][ncols_cap], exclusive-scanned in place
+// beforehand.  Every column up to ncols_cap is written (zeros past M).
+struct BaseLds {
+    uint4 part_b[kBT], part_t[kBT];
+    uint32_t sm[4];
+};
+
+// Per-thread partial sums of the table entries this block needs, loaded in one
+// round (split from digit_finish so the loads overlap the caller's own).
+struct DigitAcc {
+    uint4 b, t;      // redundant: sums over the thread's columns (before `me`, all) of 4 digits
+    uint32_t x;      // scanned: the block's base of digit tid
+};
+
+__device__ __forceinline__ DigitAcc digit_load(const uint32_t *__restrict__ table, int redundant, int ncols_cap,
+                                               int me, int bits) {
+    const int tid = threadIdx.x;
+    DigitAcc a;
+    a.b = make_uint4(0u, 0u, 0u, 0u);
+    a.t = a.b;
+    a.x = 0u;
+    if (!redundant) {
+        if (tid < (1 << bits)) a.x = table[(size_t)tid * ncols_cap + me];
+        return a;
+    }
+    // uint4 q of column c holds digits 4*(q mod Q) .. +3, Q = radix/4 (divides 256):
+    // thread t always reads the same 4 digits, from columns t/Q, t/Q + 256/Q, ...
+    const int lq = bits - 2;
+    const int g4 = tid & ((1 << lq) - 1);
+    const int cstep = kBT >> lq;
+    const uint4 *t4 = reinterpret_cast<const uint4 *>(table);
+    // batches of 16 loads, all in flight together (at most 2 batches: the table
+    // holds <= kMaxRedundantTable entries, 1024 per column step)
+    for (int c0 = tid >> lq; c0 < ncols_cap; c0 += 16 * cstep) {
+        uint4 v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int c = c0 + k * cstep;
+            v[k] = c < ncols_cap ? t4[((size_t)c << lq) + g4] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int c = c0 + k * cstep;
+            a.t.x += v[k].x; a.t.y += v[k].y; a.t.z += v[k].z; a.t.w += v[k].w;
+            if (c < me) { a.b.x += v[k].x; a.b.y += v[k].y; a.b.z += v[k].z; a.b.w += v[k].w; }
+        }
+    }
+    return a;
+}
+
+// gbase[d] = first output position of this block's keys of digit d.
+__device__ __forceinline__ void digit_finish(const DigitAcc &a, int redundant, int bits, uint32_t *gbase,
+                                             BaseLds &B) {
+    const int tid = threadIdx.x, radix = 1 << bits;
+    if (!redundant) {
+        if (tid < radix) gbase[tid] = a.x;
+        __syncthreads();
+        return;
+    }
+    const int q = radix >> 2;
+    B.part_b[tid] = a.b;
+    B.part_t[tid] = a.t;
+    __syncthreads();
+    for (int s = kBT >> 1; s >= q; s >>= 1) {          // fold threads with equal tid mod q
+        if (tid < s) {
+            const uint4 ob = B.part_b[tid + s], ot = B.part_t[tid + s];
+            uint4 &mb = B.part_b[tid], &mt = B.part_t[tid];
+            mb.x += ob.x; mb.y += ob.y; mb.z += ob.z; mb.w += ob.w;
+            mt.x += ot.x; mt.y += ot.y; mt.z += ot.z; mt.w += ot.w;
+        }
+        __syncthreads();
+    }
+    uint32_t b = 0, t = 0;
+    if (tid < radix) {
+        b = reinterpret_cast<const uint32_t *>(B.part_b)[tid];    // uint4 (d>>2), component (d&3)
+        t = reinterpret_cast<const uint32_t *>(B.part_t)[tid];
+    }
+    uint32_t all;
+    const uint32_t start = block_exclusive_scan<uint32_t, kBT>(t, B.sm, &all);
+    if (tid < radix) gbase[tid] = start + b;
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// one chunk of a stable scatter
+// ---------------------------------------------------------------------------
+template <int PL>
+struct ChunkLds {
+    uint32_t cnt[4][256];     // per wave: keys of each digit so far -> wave's first local slot
+    uint32_t dstart[256];     // chunk-local first slot of each digit
+    uint32_t gbase[256];      // global position of the block's next key of each digit
+    uint32_t sk[kBT * PL], sv[kBT * PL];
+    uint32_t sm[4];
+};
+
+// Scatters the chunk's `cc` keys to kout/vout at gbase[digit] + (rank of the
+// key among the chunk's keys of its digit), then advances gbase past the chunk.
+// Key i sits in lane i % 64 of wave i / span, register (i % span) / 64, for
+// the `span` (a multiple of 64, span * 4 >= cc) the caller loaded with.
+// Entered and left by all threads with LDS in a settled state.
+template <int PL>
+__device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span, int shift, int bits,
+                                              const uint32_t (&key)[PL], const uint32_t (&val)[PL],
+                                              uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                              uint32_t cap) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << bits;
+    const uint32_t dmask = (uint32_t)(radix - 1);
+    if (tid < radix) { L.cnt[0][tid] = 0u; L.cnt[1][tid] = 0u; L.cnt[2][tid] = 0u; L.cnt[3][tid] = 0u; }
+    __syncthreads();
+    const int iters = span >> 6;                          // <= PL; guards on `it` are uniform
+    const uint64_t below = lanes_below();
+    uint32_t rk[PL];
+#pragma unroll
+    for (int it = 0; it < PL; ++it) {
+        if (it >= iters) continue;
+        const int idx = wave * span + it * 64 + lane;
+        const bool valid = idx < cc;
+        const uint32_t d = (key[it] >> shift) & dmask;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < bits; ++b) {
+            const bool on = (d >> b) & 1u;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        const uint32_t before = valid ? L.cnt[wave][d] : 0u;
+        rk[it] = before + (uint32_t)__popcll(peers & below);
+        if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    if (tid < radix) { c0 = L.cnt[0][tid]; c1 = L.cnt[1][tid]; c2 = L.cnt[2][tid]; c3 = L.cnt[3][tid]; }
+    const uint32_t tot = c0 + c1 + c2 + c3;
+    uint32_t all;
+    const uint32_t ds = block_exclusive_scan<uint32_t, kBT>(tot, L.sm, &all);
+    if (tid < radix) {
+        L.dstart[tid] = ds;
+        L.cnt[0][tid] = ds;
+        L.cnt[1][tid] = ds + c0;
+        L.cnt[2][tid] = ds + c0 + c1;
+        L.cnt[3][tid] = ds + c0 + c1 + c2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < PL; ++it) {
+        if (it >= iters) continue;
+        const int idx = wave * span + it * 64 + lane;
+        if (idx < cc) {
+            const uint32_t lp = L.cnt[wave][(key[it] >> shift) & dmask] + rk[it];
+            if (lp < (uint32_t)(kBT * PL)) {
+                L.sk[lp] = key[it];
+                L.sv[lp] = val[it];
+            }
+        }
+    }
+    __syncthreads();
+    for (int j = tid; j < cc; j += kBT) {
+        const uint32_t k = L.sk[j];
+        const uint32_t d = (k >> shift) & dmask;
+        const uint32_t pos = L.gbase[d] + (uint32_t)j - L.dstart[d];
+        if (pos < cap) {                                  // holds by construction; keeps a bad table in bounds
+            kout[pos] = k;
+            vout[pos] = L.sv[j];
+        }
+    }
+    __syncthreads();
+    if (tid < radix) L.gbase[tid] += tot;
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// 1-2: group sums
+// ---------------------------------------------------------------------------
+// Also clears the tile ranges (tiles that receive no pair keep (0, 0)); with
+// n == 0 it publishes M = 0 itself.
+__global__ __launch_bounds__(kBT) void k_group_sums(int n, const uint32_t *__restrict__ counts,
                                                     unsigned long long *__restrict__ part, int ntiles,
-                                                    uint2 *__restrict__ ranges) {
+                                                    uint2 *__restrict__ ranges, BinHeader *__restrict__ hdr,
+                                                    uint32_t *__restrict__ offsets, uint32_t *__restrict__ d_num) {
     __shared__ unsigned long long sm[4];
-    for (int t = blockIdx.x * 256 + threadIdx.x; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
-    if (n == 0) return;
-    const int g = blockIdx.x * 256 + threadIdx.x;
+    for (int t = blockIdx.x * kBT + threadIdx.x; t < ntiles; t += gridDim.x * kBT) ranges[t] = make_uint2(0u, 0u);
+    if (n == 0) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            hdr->total = 0ull;
+            hdr->m_eff = 0u;
+            *d_num = 0u;
+            offsets[0] = 0u;
+        }
+        return;
+    }
+    const int g = blockIdx.x * kBT + threadIdx.x;
     unsigned long long c = g < n ? counts[g] : 0ull;
     unsigned long long tot;
-    block_exclusive_scan<unsigned long long, 256>(c, sm, &tot);
+    block_exclusive_scan<unsigned long long, kBT>(c, sm, &tot);
     if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+__device__ __forceinline__ void publish_total(unsigned long long tot, long long capacity, int n,
+                                              BinHeader *hdr, uint32_t *offsets, uint32_t *d_num) {
+    hdr->total = tot;
+    hdr->m_eff = (tot <= (unsigned long long)capacity) ? (uint32_t)tot : 0u;
+    *d_num = sat32(tot);
+    offsets[n] = sat32(tot);
 }
 
 // One workgroup of 1024: exclusive scan of the group sums in place; publishes M.
@@ -112,184 +345,220 @@ __global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long lo
             part[beg + i] = run;
             run += v;
         }
-    if (threadIdx.x == 0) {
-        hdr->total = tot;
-        hdr->m_eff = (tot <= (unsigned long long)capacity) ? (uint32_t)tot : 0u;
-        const uint32_t sat = tot > 0xffffffffull ? 0xffffffffu : (uint32_t)tot;
-        *d_num = sat;
-        offsets[n] = sat;
-    }
+    if (threadIdx.x == 0) publish_total(tot, capacity, n, hdr, offsets, d_num);
 }
 
-// part[] holds either the exclusive group bases (scanned by k_group_scan) or, when
-// `redundant`, the raw group sums: then every block adds up the sums before it
-// (and all of them for M) itself, and block 0 publishes M -- one launch fewer.
-__global__ __launch_bounds__(256) void k_emit(int n, int ngroups, int redundant, long long capacity, int tiles_x,
-                                              const uint32_t *__restrict__ counts,
-                                              const uint2 *__restrict__ pixbox,
-                                              const unsigned long long *__restrict__ part,
-                                              BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
-                                              uint32_t *__restrict__ d_num,
-                                              uint32_t *__restrict__ keys, uint32_t *__restrict__ vals) {
-    __shared__ uint32_t excl[257];
-    __shared__ uint2 box[256];
+// ---------------------------------------------------------------------------
+// 3: offsets + first-digit histogram per segment
+// ---------------------------------------------------------------------------
+// part[] holds the raw group sums when `redundant` (then block b adds up the
+// sums before its first group, and all of them for M, itself; block 0
+// publishes M), else the exclusive group bases from k_group_scan.
+__global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_groups, int redundant,
+                                                long long capacity, int tiles_x, int bits, int table_redundant,
+                                                int ncols_cap, const uint32_t *__restrict__ counts,
+                                                const uint2 *__restrict__ pixbox,
+                                                const unsigned long long *__restrict__ part,
+                                                BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
+                                                uint32_t *__restrict__ d_num, uint32_t *__restrict__ table) {
+    __shared__ SegLds<kBT> G;
+    __shared__ uint32_t hist[256];
     __shared__ uint32_t sm[4];
     __shared__ unsigned long long sm64[8];
     const int tid = threadIdx.x;
-    const int g = blockIdx.x * 256 + tid;
-    const uint32_t c = g < n ? counts[g] : 0u;
-    uint32_t tot;
-    const uint32_t local = block_exclusive_scan<uint32_t, 256>(c, sm, &tot);
+    const int radix = 1 << bits;
+    const uint32_t dmask = (uint32_t)(radix - 1);
+    if (tid < radix) hist[tid] = 0u;
+    const int g0 = blockIdx.x * seg_groups;
+    const int g1 = min(g0 + seg_groups, ngroups);
+    // the first group's inputs, loaded together with the group sums
+    int gid = g0 * kBT + tid;
+    uint32_t c = gid < n ? counts[gid] : 0u;
+    uint2 bx = gid < n ? pixbox[gid] : make_uint2(0u, 0u);
     unsigned long long base, total;
     if (redundant) {
         unsigned long long before = 0, all = 0;
-        for (int i = tid; i < ngroups; i += 256) {
-            const unsigned long long v = part[i];
-            all += v;
-            before += i < (int)blockIdx.x ? v : 0ull;
+        unsigned long long v[kMaxRedundantGroups / kBT];
+#pragma unroll
+        for (int k = 0; k < kMaxRedundantGroups / kBT; ++k) {
+            const int i = tid + k * kBT;
+            v[k] = i < ngroups ? part[i] : 0ull;
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxRedundantGroups / kBT; ++k) {
+            all += v[k];
+            before += tid + k * kBT < g0 ? v[k] : 0ull;
         }
         unsigned long long tb, ta;
-        block_exclusive_scan<unsigned long long, 256>(before, sm64, &tb);
-        block_exclusive_scan<unsigned long long, 256>(all, sm64 + 4, &ta);
+        block_exclusive_scan<unsigned long long, kBT>(before, sm64, &tb);
+        block_exclusive_scan<unsigned long long, kBT>(all, sm64 + 4, &ta);
         base = tb;
         total = ta;
-        if (blockIdx.x == 0 && tid == 0) {
-            hdr->total = total;
-            hdr->m_eff = (total <= (unsigned long long)capacity) ? (uint32_t)total : 0u;
-            const uint32_t sat = total > 0xffffffffull ? 0xffffffffu : (uint32_t)total;
-            *d_num = sat;
-            offsets[n] = sat;
-        }
+        if (blockIdx.x == 0 && tid == 0) publish_total(total, capacity, n, hdr, offsets, d_num);
     } else {
-        base = part[blockIdx.x];
+        base = part[g0];
         total = hdr->total;
     }
-    if (g < n) {
-        const unsigned long long o = base + local;
-        offsets[g] = o > 0xffffffffull ? 0xffffffffu : (uint32_t)o;
-    }
-    if (total > (unsigned long long)capacity || tot == 0) return;   // overflow (or nothing to emit): uniform
-    excl[tid] = local;
-    if (tid == 0) excl[256] = tot;
-    box[tid] = g < n ? pixbox[g] : make_uint2(0u, 0u);
-    __syncthreads();
-    const uint32_t b32 = (uint32_t)base;
-    for (uint32_t idx = tid; idx < tot; idx += 256) {
-        int lo = 0, hi = 256;                 // excl[lo] <= idx < excl[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (excl[mid] <= idx) lo = mid; else hi = mid;
+    const bool emit = total <= (unsigned long long)capacity;
+    for (int g = g0; g < g1; ++g) {
+        if (g > g0) {
+            gid = g * kBT + tid;
+            c = gid < n ? counts[gid] : 0u;
+            bx = gid < n ? pixbox[gid] : make_uint2(0u, 0u);
         }
-        const uint32_t r = idx - excl[lo];
-        const uint2 bx = box[lo];
-        const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
-        const uint32_t tx1 = (bx.y & 0xffffu) >> 4;
-        const uint32_t wt = tx1 - tx0 + 1;
-        const uint32_t q = r / wt, rem = r - q * wt;
-        keys[b32 + idx] = (ty0 + q) * (uint32_t)tiles_x + tx0 + rem;
-        vals[b32 + idx] = (uint32_t)(blockIdx.x * 256 + lo);
+        uint32_t tot;
+        const uint32_t local = block_exclusive_scan<uint32_t, kBT>(c, sm, &tot);
+        if (gid < n) offsets[gid] = sat32(base + local);
+        if (emit && tot > 0) {                                    // uniform
+            G.excl[tid] = local;
+            if (tid == 0) G.excl[kBT] = tot;
+            G.box[tid] = bx;
+            __syncthreads();
+            const int ns = min(kBT, n - g * kBT);
+            for (uint32_t idx = tid; idx < tot; idx += kBT) {
+                uint32_t key;
+                int lo;
+                regen_pair<kBT>(G, ns, idx, tiles_x, key, lo);
+                atomicAdd(&hist[key & dmask], 1u);
+            }
+            __syncthreads();
+        }
+        base += tot;
+    }
+    __syncthreads();
+    if (tid < radix) {
+        if (table_redundant) table[(size_t)blockIdx.x * radix + tid] = hist[tid];
+        else table[(size_t)tid * ncols_cap + blockIdx.x] = hist[tid];
     }
 }
 
 // ---------------------------------------------------------------------------
-// 4: stable LSD radix sort pass
+// 4: first sort pass from the regenerated pairs (segments of 256 * SG Gaussians)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint32_t *__restrict__ keys,
-                                                             const BinHeader *__restrict__ hdr, int shift,
-                                                             int bits, uint32_t *__restrict__ table, int nbs) {
+template <int SG>
+__global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int bits, int table_redundant, int ncols_cap,
+                                                  const uint2 *__restrict__ pixbox,
+                                                  const uint32_t *__restrict__ offsets,
+                                                  const BinHeader *__restrict__ hdr,
+                                                  const uint32_t *__restrict__ table, uint32_t *__restrict__ kout,
+                                                  uint32_t *__restrict__ vout) {
+    constexpr int S = kBT * SG;
+    __shared__ SegLds<S> G;
+    __shared__ ChunkLds<kPerLane> L;
+    __shared__ BaseLds B;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int first = blockIdx.x * S;
+    const int ns = min(S, n - first);
+    // One round of loads: the segment's offsets and boxes, M, the digit table.
+    uint32_t o[SG];
+    uint2 bx[SG];
+#pragma unroll
+    for (int r = 0; r < SG; ++r) {
+        const int i = r * kBT + tid;
+        o[r] = i < ns ? offsets[first + i] : 0u;
+        bx[r] = i < ns ? pixbox[first + i] : make_uint2(0u, 0u);
+    }
+    const uint32_t o0 = offsets[first];
+    const uint32_t oend = offsets[first + ns];       // the next segment's first slot, or M
+    const uint32_t M = hdr->m_eff;
+    const DigitAcc acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
+    if (M == 0u) return;                              // overflow or no pair (then offsets may saturate): uniform
+#pragma unroll
+    for (int r = 0; r < SG; ++r) {
+        const int i = r * kBT + tid;
+        if (i < ns) {
+            G.excl[i] = o[r] - o0;
+            G.box[i] = bx[r];
+        }
+    }
+    if (tid == 0) G.excl[ns] = oend - o0;
+    digit_finish(acc, table_redundant, bits, L.gbase, B);   // its barriers publish G
+    const uint32_t tot = oend - o0;
+    for (uint32_t cs = 0; cs < tot; cs += kChunk) {
+        const int cc = (int)min((uint32_t)kChunk, tot - cs);
+        const int span = ((cc + kBT - 1) / kBT) * 64;
+        const int iters = span >> 6;
+        uint32_t key[kPerLane], val[kPerLane];
+#pragma unroll
+        for (int it = 0; it < kPerLane; ++it) {
+            if (it < iters) {                                     // uniform
+                const int idx = wave * span + it * 64 + lane;
+                int lo;
+                regen_pair<S>(G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
+                val[it] = (uint32_t)(first + lo);
+            }
+        }
+        scatter_chunk(L, cc, span, 0, bits, key, val, kout, vout, M);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 5: further passes over blocks of 256 * PL keys
+// ---------------------------------------------------------------------------
+template <int PL>
+__global__ __launch_bounds__(kBT) void k_count(const uint32_t *__restrict__ keys, const BinHeader *__restrict__ hdr,
+                                               int shift, int bits, int table_redundant, int ncols_cap,
+                                               uint32_t *__restrict__ table) {
+    constexpr int CH = kBT * PL;
     __shared__ uint32_t h[256];
     const int radix = 1 << bits;
     const int tid = threadIdx.x;
-    if (tid < radix) h[tid] = 0;
+    if (tid < radix) h[tid] = 0u;
     __syncthreads();
     const uint32_t M = hdr->m_eff;
-    const uint32_t base = blockIdx.x * (uint32_t)kSortChunk;
-    for (int it = 0; it < kSortIters; ++it) {
-        const uint32_t idx = base + it * kSortThreads + tid;
-        if (idx < M) atomicAdd(&h[(keys[idx] >> shift) & (radix - 1)], 1u);
+    const uint32_t base = blockIdx.x * (uint32_t)CH;
+    if (base < M) {                                               // uniform
+        uint32_t k[PL];
+#pragma unroll
+        for (int it = 0; it < PL; ++it) {
+            const uint32_t idx = base + it * kBT + tid;
+            k[it] = keys[idx < M ? idx : M - 1];
+        }
+#pragma unroll
+        for (int it = 0; it < PL; ++it)
+            if (base + it * kBT + tid < M) atomicAdd(&h[(k[it] >> shift) & (radix - 1)], 1u);
     }
     __syncthreads();
-    if (tid < radix) table[(size_t)tid * nbs + blockIdx.x] = h[tid];
+    if (tid < radix) {                                            // zero columns past M too
+        if (table_redundant) table[(size_t)blockIdx.x * radix + tid] = h[tid];
+        else table[(size_t)tid * ncols_cap + blockIdx.x] = h[tid];
+    }
 }
 
-// `counts_raw`: the table holds the digit counts themselves (no scan pass ran);
-// each block then forms its own offsets: thread d adds digit d's counts over the
-// blocks in use (those before this one, and all of them for the digit total),
-// and a block scan over the digit totals gives each digit's start.
-__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(const uint32_t *__restrict__ kin,
-                                                               const uint32_t *__restrict__ vin,
-                                                               uint32_t *__restrict__ kout,
-                                                               uint32_t *__restrict__ vout,
-                                                               const BinHeader *__restrict__ hdr, int shift,
-                                                               int bits, const uint32_t *__restrict__ table,
-                                                               int nbs, int counts_raw) {
-    __shared__ uint32_t run[256];          // next output slot per digit
-    __shared__ uint32_t wcnt[4][256];      // per wave: keys of each digit in this round
-    __shared__ uint32_t sm[4];
-    const uint32_t M = hdr->m_eff;
-    const uint32_t base = blockIdx.x * (uint32_t)kSortChunk;
-    if (base >= M) return;
-    const int radix = 1 << bits;
+template <int PL>
+__global__ __launch_bounds__(kBT) void k_scatter(const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin,
+                                                 uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                                 const BinHeader *__restrict__ hdr, int shift, int bits,
+                                                 int table_redundant, int ncols_cap,
+                                                 const uint32_t *__restrict__ table) {
+    constexpr int CH = kBT * PL, SPAN = PL * 64;
+    __shared__ ChunkLds<PL> L;
+    __shared__ BaseLds B;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (counts_raw) {
-        const int used = (int)((M + kSortChunk - 1) / kSortChunk);
-        uint32_t before = 0, total = 0;
-        if (tid < radix) {
-            const uint32_t *row = table + (size_t)tid * nbs;
-            for (int b = 0; b < used; ++b) {
-                const uint32_t c = row[b];
-                total += c;
-                before += b < (int)blockIdx.x ? c : 0u;
-            }
-        }
-        uint32_t all;
-        const uint32_t start = block_exclusive_scan<uint32_t, kSortThreads>(total, sm, &all);
-        if (tid < radix) run[tid] = start + before;
-    } else if (tid < radix) {
-        run[tid] = table[(size_t)tid * nbs + blockIdx.x];
+    const uint32_t base = blockIdx.x * (uint32_t)CH;
+    const uint32_t M = hdr->m_eff;
+    if (base >= M) return;                                        // uniform
+    // the block's keys and the digit table in one round of loads
+    uint32_t key[PL], val[PL];
+#pragma unroll
+    for (int it = 0; it < PL; ++it) {
+        const uint32_t idx = base + wave * SPAN + it * 64 + lane;
+        const uint32_t ii = idx < M ? idx : M - 1;
+        key[it] = kin[ii];
+        val[it] = vin[ii];
     }
-    for (int i = tid; i < 4 * 256; i += kSortThreads) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-    const uint64_t below = lanes_below();
-    for (int it = 0; it < kSortIters; ++it) {
-        const uint32_t rbase = base + it * kSortThreads;
-        if (rbase >= M) break;                                  // uniform
-        const uint32_t idx = rbase + tid;
-        const bool valid = idx < M;
-        const uint32_t key = valid ? kin[idx] : 0u;
-        const uint32_t val = valid ? vin[idx] : 0u;
-        const uint32_t d = (key >> shift) & (uint32_t)(radix - 1);
-        uint64_t peers = __ballot(valid);
-        for (int bit = 0; bit < bits; ++bit) {
-            const bool on = (d >> bit) & 1u;
-            const uint64_t m = __ballot(on);
-            peers &= on ? m : ~m;
-        }
-        const uint32_t rank = (uint32_t)__popcll(peers & below);
-        const bool leader = valid && (peers >> lane) == 1ull;   // highest lane of the digit group
-        if (leader) wcnt[wave][d] = (uint32_t)__popcll(peers);
-        __syncthreads();
-        if (valid) {
-            uint32_t pos = run[d] + rank;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
-            kout[pos] = key;
-            vout[pos] = val;
-        }
-        __syncthreads();
-        if (tid < radix) {
-            run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
-            wcnt[0][tid] = 0; wcnt[1][tid] = 0; wcnt[2][tid] = 0; wcnt[3][tid] = 0;
-        }
-        __syncthreads();
-    }
+    const DigitAcc acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
+    digit_finish(acc, table_redundant, bits, L.gbase, B);
+    const int cc = (int)min((uint32_t)CH, M - base);
+    scatter_chunk(L, cc, SPAN, shift, bits, key, val, kout, vout, M);
 }
 
-// exclusive scan of a u32 array in place: one workgroup when it is short,
-// otherwise reduce -> scan of block sums -> rescan with offsets.
-// count <= 1024 * kScanSingleItems.  Element r * 1024 + i lives in thread i's
-// register v[r] (coalesced loads, all issued together); its exclusive prefix is
-// the totals of rows before r, plus the row-r totals of waves before thread i's
-// wave, plus the DPP wave scan within the wave.
+// ---------------------------------------------------------------------------
+// exclusive scan of a u32 array in place (large digit tables): one workgroup
+// when it is short, otherwise reduce -> scan of block sums -> rescan.
+// count <= 1024 * kScanSingleItems for the single form.  Element r * 1024 + i
+// lives in thread i's register v[r] (coalesced loads, all issued together).
+// ---------------------------------------------------------------------------
 constexpr int kScanSingleItems = 32;
 __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, int count) {
     __shared__ uint32_t wsum[16][kScanSingleItems];     // [wave][row] totals -> exclusive over waves
@@ -380,18 +649,32 @@ static hipError_t scan_u32(uint32_t *a, int count, uint32_t *sums, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
-// 5: tile ranges
+// 6: tile ranges
 // ---------------------------------------------------------------------------
-// One thread per sorted pair: the first and last pair of each tile's run write
-// its start and end (the ranges were cleared by k_group_sums).
+// Four sorted pairs per thread: a key that differs from its predecessor opens
+// its tile's run and closes the predecessor's (the ranges were cleared by
+// k_group_sums).
 __global__ __launch_bounds__(256) void k_ranges(const uint32_t *__restrict__ keys, const BinHeader *__restrict__ hdr,
-                                                uint32_t *__restrict__ ranges) {
-    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+                                                uint32_t ntiles, uint32_t *__restrict__ ranges) {
+    const uint32_t i0 = (blockIdx.x * 256u + threadIdx.x) * 4u;
     const uint32_t M = hdr->m_eff;
-    if (i >= M) return;
-    const uint32_t k = keys[i];
-    if (i == 0 || keys[i - 1] != k) ranges[2 * k] = i;
-    if (i + 1 == M || keys[i + 1] != k) ranges[2 * k + 1] = i + 1;
+    if (i0 >= M) return;
+    uint32_t k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = min(keys[i0 + j < M ? i0 + j : M - 1], ntiles - 1);   // ids are < ntiles
+    uint32_t prev = i0 > 0 ? min(keys[i0 - 1], ntiles - 1) : 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t i = i0 + j;
+        if (i < M) {
+            if (k[j] != prev) {
+                ranges[2 * k[j]] = i;
+                if (i > 0) ranges[2 * prev + 1] = i;
+            }
+            if (i + 1 == M) ranges[2 * k[j] + 1] = M;
+            prev = k[j];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -408,20 +691,34 @@ BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
     p.capacity = capacity;
     int B = 0;
     while ((1ll << B) < (long long)p.ntiles) ++B;          // key bits: ids in [0, ntiles)
-    p.passes = (B + 7) / 8;
+    p.passes = B == 0 ? 1 : (B + 7) / 8;                    // a single tile still takes one (copying) pass
     for (int i = 0; i < 4; ++i) p.bits[i] = 0;
-    if (p.passes > 0) {
+    {
         const int w = (B + p.passes - 1) / p.passes;
         int left = B;
         for (int i = 0; i < p.passes; ++i) { p.bits[i] = left < w ? left : w; left -= p.bits[i]; }
     }
     p.nb_g = (n + 255) / 256;
-    p.nbs = (int)((capacity + kSortChunk - 1) / kSortChunk);
+    p.redundant_groups = p.nb_g > 0 && p.nb_g <= kMaxRedundantGroups;
+    p.seg_groups = p.nb_g <= kMaxRedundantGroups ? 1 : 4;
+    p.nseg = (p.nb_g + p.seg_groups - 1) / p.seg_groups;
+    // later passes: smaller blocks when the pair buffer is small, so the launch still fills the chip
+    p.pass_lanes = capacity <= (1ll << 19) ? 4 : capacity <= (1ll << 22) ? 8 : 16;
+    const int64_t chunk = (int64_t)kBT * p.pass_lanes;
+    p.nbs = (int)((capacity + chunk - 1) / chunk);
+    size_t table = 1;
+    for (int i = 0; i < p.passes; ++i) {
+        const int cols = i == 0 ? p.nseg : p.nbs;
+        p.ncols_cap[i] = cols;
+        const size_t entries = ((size_t)1 << p.bits[i]) * (size_t)(cols > 0 ? cols : 1);
+        p.table_redundant[i] = p.bits[i] >= 2 && entries <= (size_t)kMaxRedundantTable &&
+                               (int64_t)entries * cols <= kMaxRedundantReads;
+        if (entries > table) table = entries;
+    }
     size_t off = align256(sizeof(BinHeader));
     p.off_part = off; off = align256(off + sizeof(unsigned long long) * (size_t)(p.nb_g > 0 ? p.nb_g : 1));
     p.off_kalt = off; off = align256(off + sizeof(uint32_t) * (size_t)(capacity > 0 ? capacity : 1));
     p.off_valt = off; off = align256(off + sizeof(uint32_t) * (size_t)(capacity > 0 ? capacity : 1));
-    const size_t table = (size_t)256 * (size_t)(p.nbs > 0 ? p.nbs : 1);
     p.off_table = off; off = align256(off + sizeof(uint32_t) * table);
     p.off_tsp = off; off = align256(off + sizeof(uint32_t) * ((table + kScanChunk - 1) / kScanChunk + 1));
     p.bytes = off;
@@ -440,37 +737,51 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     uint32_t *valt = reinterpret_cast<uint32_t *>(w + p.off_valt);
     uint32_t *table = reinterpret_cast<uint32_t *>(w + p.off_table);
     uint32_t *tsp = reinterpret_cast<uint32_t *>(w + p.off_tsp);
+    const uint2 *box = reinterpret_cast<const uint2 *>(pixbox);
 
-    k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, 256, 0, s>>>(p.n, counts, part, p.ntiles,
-                                                         reinterpret_cast<uint2 *>(ranges));
-    const int redundant = p.nb_g > 0 && p.nb_g <= kMaxRedundantGroups;
-    if (!redundant) k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
-    // Emit into the buffer that the last pass reads from, so the result lands in keys/vals.
-    uint32_t *ek = (p.passes & 1) ? kalt : keys;
-    uint32_t *ev = (p.passes & 1) ? valt : vals;
-    if (p.nb_g > 0)
-        k_emit<<<p.nb_g, 256, 0, s>>>(p.n, p.nb_g, redundant, (long long)p.capacity, p.tiles_x, counts,
-                                      reinterpret_cast<const uint2 *>(pixbox), part, hdr, offsets, d_num, ek, ev);
+    k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, part, p.ntiles,
+                                                         reinterpret_cast<uint2 *>(ranges), hdr, offsets, d_num);
+    if (p.n == 0) return hipGetLastError();
+    if (!p.redundant_groups)
+        k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
+    k_count0<<<p.nseg, kBT, 0, s>>>(p.n, p.nb_g, p.seg_groups, p.redundant_groups, (long long)p.capacity,
+                                    p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], counts, box, part,
+                                    hdr, offsets, d_num, table);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    uint32_t *srck = ek, *srcv = ev;
-    uint32_t *dstk = (srck == keys) ? kalt : keys, *dstv = (srcv == vals) ? valt : vals;
-    int shift = 0;
-    for (int pass = 0; pass < p.passes && p.nbs > 0; ++pass) {
-        const int bits = p.bits[pass];
-        k_sort_count<<<p.nbs, kSortThreads, 0, s>>>(srck, hdr, shift, bits, table, p.nbs);
-        const int raw = (1 << bits) * p.nbs <= kMaxRawTable;
-        if (!raw) {
-            e = scan_u32(table, (1 << bits) * p.nbs, tsp, s);
+    if (e != hipSuccess || p.capacity == 0) return e;
+    // pass i writes keys/vals when an even number of passes follow it
+    auto dst_k = [&](int i) { return ((p.passes - 1 - i) & 1) ? kalt : keys; };
+    auto dst_v = [&](int i) { return ((p.passes - 1 - i) & 1) ? valt : vals; };
+    if (!p.table_redundant[0]) {
+        e = scan_u32(table, (1 << p.bits[0]) * p.ncols_cap[0], tsp, s);
+        if (e != hipSuccess) return e;
+    }
+    if (p.seg_groups == 1)
+        k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box,
+                                             offsets, hdr, table, dst_k(0), dst_v(0));
+    else
+        k_scatter0<4><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box,
+                                             offsets, hdr, table, dst_k(0), dst_v(0));
+    int shift = p.bits[0];
+    for (int i = 1; i < p.passes; ++i) {
+        const uint32_t *sk = dst_k(i - 1), *sv = dst_v(i - 1);
+        const int b = p.bits[i], tr = p.table_redundant[i], nc = p.ncols_cap[i];
+        if (p.pass_lanes == 4) k_count<4><<<p.nbs, kBT, 0, s>>>(sk, hdr, shift, b, tr, nc, table);
+        else if (p.pass_lanes == 8) k_count<8><<<p.nbs, kBT, 0, s>>>(sk, hdr, shift, b, tr, nc, table);
+        else k_count<16><<<p.nbs, kBT, 0, s>>>(sk, hdr, shift, b, tr, nc, table);
+        if (!tr) {
+            e = scan_u32(table, (1 << b) * nc, tsp, s);
             if (e != hipSuccess) return e;
         }
-        k_sort_scatter<<<p.nbs, kSortThreads, 0, s>>>(srck, srcv, dstk, dstv, hdr, shift, bits, table, p.nbs, raw);
-        shift += bits;
-        uint32_t *tk = srck, *tv = srcv;
-        srck = dstk; srcv = dstv; dstk = tk; dstv = tv;
+        if (p.pass_lanes == 4)
+            k_scatter<4><<<p.nbs, kBT, 0, s>>>(sk, sv, dst_k(i), dst_v(i), hdr, shift, b, tr, nc, table);
+        else if (p.pass_lanes == 8)
+            k_scatter<8><<<p.nbs, kBT, 0, s>>>(sk, sv, dst_k(i), dst_v(i), hdr, shift, b, tr, nc, table);
+        else
+            k_scatter<16><<<p.nbs, kBT, 0, s>>>(sk, sv, dst_k(i), dst_v(i), hdr, shift, b, tr, nc, table);
+        shift += p.bits[i];
     }
-    if (p.capacity > 0)
-        k_ranges<<<(unsigned)((p.capacity + 255) / 256), 256, 0, s>>>(keys, hdr, ranges);
+    k_ranges<<<(unsigned)((p.capacity + 1023) / 1024), 256, 0, s>>>(keys, hdr, (uint32_t)p.ntiles, ranges);
     return hipGetLastError();
 }
 

@@ -137,6 +137,14 @@ def test_bin_long_tile_list():
     assert got["ranges"][0, 1] - got["ranges"][0, 0] == n
 
 
+def test_bin_large_boxes():
+    """Groups of 256 Gaussians with far more pairs than one 4096-key sort chunk."""
+    require_gpu()
+    p = synth.random_case(11, 640, 600, 700, sigma=(20.0, 150.0), margin=100)
+    got = _check_bin(640, 600, p)
+    assert got["M"] > 40 * 4096
+
+
 def test_bin_capacity_overflow():
     require_gpu()
     from rasterizer_gaussian_raster_amd import gi
