@@ -27,6 +27,14 @@ __device__ __forceinline__ uint64_t lanes_below() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// Orders a wave's LDS writes before its later LDS reads by other lanes of the
+// same wave (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // 2^x with the hardware transcendental (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -15,10 +15,11 @@
 //
 // Backward (work items).  The tile is cut into 16 blocks of 4x4 pixels; every
 // list entry yields one work item per block its pixel box overlaps (about 0.4
-// of the binned pairs at the benchmark shapes), and the items are packed 64
-// per wave, one per lane, block-major so that a wave's lanes share their
-// block's dL/dI (LDS broadcasts), no lane idles on a short list and no pair
-// outside the box is evaluated.  A lane walks its block's 16 pixels (dL/dI staged in
+// of the binned pairs at the benchmark shapes).  Each wave takes a quarter of
+// the tile's entries and packs their items 64 per round, one per lane, entry
+// by entry (no lane idles on a short list and no pair outside the box is
+// evaluated); after the tile's dL/dI is in LDS the waves never wait for one
+// another.  A lane walks its block's 16 pixels (dL/dI staged in
 // LDS), keeping the Gaussian's partial gradient in registers with the
 // column-invariant factors (dx, u, b dx, u^2) hoisted; the chain rule from the
 // scaled rows of L^-1 (a, b, c) to (l11, l21, l22) is applied per item, each
@@ -153,9 +154,11 @@ __global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__
 // reads from LDS are broadcasts.  Items run in rounds of 256 (one per thread);
 // each writes its 8 values to an LDS slot, then every entry adds its own items
 // in block order -- no atomics, and the result does not depend on timing.
-constexpr int kBwdBatch = 128;                    // list entries staged per round
-constexpr int kGpStride = 17;                     // padded LDS row of the tile's dL/dI (float4)
-constexpr uint16_t kNoItem = 0xffff;
+constexpr int kBwdBatch = 128;                    // list entries per block round, split over the 4 waves
+constexpr int kWaveEnt = kBwdBatch / 4;           // entries a wave takes per round (at most)
+constexpr int kGpStride = 17;                     // padded LDS run of one 4x4 block's dL/dI (float4):
+                                                  // the 16 blocks' pixels at one offset span all
+                                                  // 8 bank groups (at most 2-way conflicts)
 
 __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
@@ -165,13 +168,10 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                                                         const uint32_t *__restrict__ vals, uint32_t capacity,
                                                         const float *__restrict__ dL,
                                                         float4 *__restrict__ part) {
-    __shared__ float4 gp[kTile * kGpStride];      // dL/dI of the tile's pixels
-    __shared__ SumRec ent[kBwdBatch];             // staged list entries
-    __shared__ uint16_t items[kBwdBatch * 16];    // entry | block << 8, block-major
-    __shared__ uint16_t ipos[kBwdBatch][16];      // item index of (entry, block), kNoItem if none
-    __shared__ float4 ipart[256][2];              // this round's item results
-    __shared__ uint32_t wcnt[4][16];              // per wave: entries overlapping each block
-    __shared__ uint32_t bstart[17];               // block-major start of each block's items
+    __shared__ float4 gp[16 * kGpStride];               // dL/dI of the tile's pixels, block by block
+    __shared__ float4 entp[4][kWaveEnt], entq[4][kWaveEnt];   // per wave: its staged entries (p, q)
+    __shared__ uint16_t items[4][kWaveEnt * 16];        // per wave: entry | block << 8, entry-major
+    __shared__ float4 ipart[4][2][64];                  // per wave: this round's item results
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     if (t >= ntiles) return;
     const uint2 rg = ranges[t];
@@ -179,27 +179,28 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tx = t % tiles_x, ty = t / tiles_x;
     const int x0 = tx * kTile, y0 = ty * kTile;
-    {
-        const int xi = x0 + (tid & 15), yi = y0 + (tid >> 4);
-        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (xi < W && yi < H) {
-            const size_t o = (size_t)yi * W + xi, plane = (size_t)W * H;
-            g = make_float4(dL[o], dL[o + plane], dL[o + 2 * plane], 0.f);
-        }
-        gp[(tid >> 4) * kGpStride + (tid & 15)] = g;
-    }
-    const uint64_t below = lanes_below();
     const float k2 = 2.0f * kLn2;
     const float is = 1.0f / kScale;
-    for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
-        const uint32_t idx = base + tid;
-        const bool staged = tid < kBwdBatch && idx < rg.y;
-        int bx0 = 4, bx1 = -1, by0 = 4, by1 = -1;         // block rectangle (empty when not staged)
-        uint32_t slot = 0xffffffffu;
-        if (staged) {
-            const uint32_t g = vals[idx];
-            ent[tid].p = records[2 * g];
-            ent[tid].q = records[2 * g + 1];
+
+    // This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
+    auto share = [&](uint32_t base, uint32_t &e0, uint32_t &ne) {
+        const uint32_t nb = min((uint32_t)kBwdBatch, rg.y - base);
+        const uint32_t q = (nb + 3) >> 2;
+        e0 = base + (uint32_t)wave * q;
+        const uint32_t end = base + nb;
+        ne = e0 < end ? min(q, end - e0) : 0u;
+    };
+    // Stages lane `lane`'s entry of the share: its record in LDS, its emission slot
+    // and the rectangle of 4x4 blocks its pixel box overlaps (empty when none).
+    int bx0, bx1, by0, by1;
+    uint32_t slot;
+    auto stage = [&](uint32_t e0, uint32_t ne) {
+        bx0 = 4; bx1 = -1; by0 = 4; by1 = -1;
+        slot = 0xffffffffu;
+        if ((uint32_t)lane < ne) {
+            const uint32_t g = vals[e0 + lane];
+            entp[wave][lane] = records[2 * g];
+            entq[wave][lane] = records[2 * g + 1];
             const uint2 bx = pixbox[g];
             slot = emit_slot(offsets[g], bx, tx, ty);
             bx0 = max((int)(bx.x & 0xffff) - x0, 0) >> 2;
@@ -207,46 +208,51 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
             by0 = max((int)(bx.x >> 16) - y0, 0) >> 2;
             by1 = min((int)(bx.y >> 16) - y0, 15) >> 2;
         }
-        // block-major item positions: per block, ballot over the wave, then waves in order
-#pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            const bool in = (b & 3) >= bx0 && (b & 3) <= bx1 && (b >> 2) >= by0 && (b >> 2) <= by1;
-            const uint64_t m = __ballot(in);
-            if (lane == 0) wcnt[wave][b] = (uint32_t)__popcll(m);
+    };
+
+    // dL/dI loads and the first share's staging go out together; one workgroup
+    // barrier publishes the tile's dL/dI, everything after it is wave-local.
+    uint32_t e0, ne;
+    share(rg.x, e0, ne);
+    float4 gv0 = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+        const int xi = x0 + (tid & 15), yi = y0 + (tid >> 4);
+        if (xi < W && yi < H) {
+            const size_t o = (size_t)yi * W + xi, plane = (size_t)W * H;
+            gv0 = make_float4(dL[o], dL[o + plane], dL[o + 2 * plane], 0.f);
         }
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t run = 0;
-            for (int b = 0; b < 16; ++b) {
-                bstart[b] = run;
-                run += wcnt[0][b] + wcnt[1][b] + wcnt[2][b] + wcnt[3][b];
-            }
-            bstart[16] = run;
+    }
+    stage(e0, ne);
+    // pixel (x, y) of the tile: block (y/4)*4 + x/4, offset (y%4)*4 + x%4
+    gp[(((tid >> 6) << 2) | ((tid & 15) >> 2)) * kGpStride + (((tid >> 4) & 3) << 2) + (tid & 3)] = gv0;
+    __syncthreads();
+
+    for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
+        if (base != rg.x) {
+            share(base, e0, ne);
+            stage(e0, ne);
         }
-        __syncthreads();
-#pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            const bool in = (b & 3) >= bx0 && (b & 3) <= bx1 && (b >> 2) >= by0 && (b >> 2) <= by1;
-            const uint64_t m = __ballot(in);               // same vote as above
-            if (in) {
-                uint32_t o = bstart[b] + (uint32_t)__popcll(m & below);
-                for (int w = 0; w < wave; ++w) o += wcnt[w][b];
-                items[o] = (uint16_t)(tid | (b << 8));
-                ipos[tid][b] = (uint16_t)o;
-            } else if (tid < kBwdBatch) {
-                ipos[tid][b] = kNoItem;
-            }
+        if (ne == 0) continue;                              // wave-uniform; no workgroup barrier below
+        // entry-major item positions: lane e's items are [s_e, s_e + n_e), blocks in
+        // ascending order (row-major over its rectangle)
+        const uint32_t n_e = (uint32_t)(lane) < ne ? (uint32_t)((bx1 - bx0 + 1) * (by1 - by0 + 1)) : 0u;
+        const uint32_t incl = wave_scan_incl(n_e);
+        const uint32_t s_e = incl - n_e;
+        const uint32_t nitems = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        {
+            uint32_t o = s_e;
+            for (int by = by0; by <= by1; ++by)
+                for (int bx = bx0; bx <= bx1; ++bx) items[wave][o++] = (uint16_t)(lane | ((by * 4 + bx) << 8));
         }
-        const uint32_t nitems = bstart[16];
-        float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // this thread's entry
-        for (uint32_t rb = 0; rb < nitems; rb += 256) {
-            __syncthreads();                                // items / ipos written; ipart free
-            const uint32_t it = rb + tid;
+        wave_sync();
+        float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // this lane's entry
+        for (uint32_t rb = 0; rb < nitems; rb += 64) {
+            const uint32_t it = rb + lane;
             if (it < nitems) {
-                const uint32_t code = items[it];
+                const uint32_t code = items[wave][it];
                 const uint32_t e = code & 0xffu, blk = code >> 8;
                 const int lx = (int)(blk & 3u) * 4, ly = (int)(blk >> 2) * 4;
-                const float4 A = ent[e].p, B = ent[e].q;
+                const float4 A = entp[wave][e], B = entq[wave][e];
                 float dy[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                     float ch = 0.f, chv = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        const float4 gv = gp[(ly + rr) * kGpStride + lx + c];
+                        const float4 gv = gp[blk * kGpStride + rr * 4 + c];
                         const float v = fmaf(B.x, dy[rr], tb);
                         const float ee = fmaf(v, v, uu);
                         const float w = ee <= kE9 ? exp2_hw(-ee) : 0.0f;
@@ -282,28 +288,26 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                 // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22).
                 const float a = A.z, b = A.w, c = B.x;
                 const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                ipart[tid][0] = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv, -is * fmaf(a * a, da, a * b * db),
-                                            -is * (a * c * db));
-                ipart[tid][1] = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
+                ipart[wave][0][lane] = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv,
+                                                   -is * fmaf(a * a, da, a * b * db), -is * (a * c * db));
+                ipart[wave][1][lane] = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
             }
-            __syncthreads();                                // round's results visible
-            if (staged) {
-#pragma unroll
-                for (int b = 0; b < 16; ++b) {
-                    const uint32_t p = ipos[tid][b];
-                    if (p != kNoItem && p - rb < 256u) {
-                        const float4 u0 = ipart[p - rb][0], u1 = ipart[p - rb][1];
-                        acc0.x += u0.x; acc0.y += u0.y; acc0.z += u0.z; acc0.w += u0.w;
-                        acc1.x += u1.x; acc1.y += u1.y; acc1.z += u1.z; acc1.w += u1.w;
-                    }
-                }
+            wave_sync();
+            // each entry adds its items of this round in order: blocks ascending
+            // whatever the rounds are, so the sum is reproducible
+            const uint32_t lo = max(s_e, rb), hi = min(s_e + n_e, rb + 64u);
+            for (uint32_t p = lo; p < hi; ++p) {
+                const float4 u0 = ipart[wave][0][p - rb], u1 = ipart[wave][1][p - rb];
+                acc0.x += u0.x; acc0.y += u0.y; acc0.z += u0.z; acc0.w += u0.w;
+                acc1.x += u1.x; acc1.y += u1.y; acc1.z += u1.z; acc1.w += u1.w;
             }
+            wave_sync();                                    // ipart is rewritten next round
         }
-        if (staged && slot < capacity) {
+        if ((uint32_t)lane < ne && slot < capacity) {
             part[2 * (size_t)slot] = acc0;
             part[2 * (size_t)slot + 1] = acc1;
         }
-        if (base + kBwdBatch < rg.y) __syncthreads();   // the next batch reuses ent / items / ipos
+        wave_sync();                                        // ent / items are rewritten next batch
     }
 }
 
