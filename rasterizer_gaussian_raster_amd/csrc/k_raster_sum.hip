@@ -311,6 +311,27 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
     }
 }
 
+// Adds the pair slots q in [o0, o1) (part[2q], part[2q + 1]) into (a, b) in
+// ascending q; four slots are loaded at a time so that their latencies overlap.
+__device__ __forceinline__ void gather_slots(const float4 *__restrict__ part, uint32_t o0, uint32_t o1, float4 &a,
+                                             float4 &b) {
+    for (uint32_t q = o0; q < o1; q += 4) {
+        float4 u[4], w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t qq = min(q + (uint32_t)k, o1 - 1u);     // in range; repeats are not added
+            u[k] = part[2 * (size_t)qq];
+            w[k] = part[2 * (size_t)qq + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (q + (uint32_t)k < o1) {
+                a.x += u[k].x; a.y += u[k].y; a.z += u[k].z; a.w += u[k].w;
+                b.x += w[k].x; b.y += w[k].y; b.z += w[k].z; b.w += w[k].w;
+            }
+    }
+}
+
 // One thread per Gaussian: its pairs' partial gradients sit at offsets[g] ..
 // offsets[g+1] in emission order; add them in that order (reproducible).
 __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const uint32_t *__restrict__ offsets,
@@ -343,16 +364,13 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
     if (g >= n) return;
     const uint32_t o0 = offsets[g], o1 = offsets[g + 1];
     if (o1 == o0) return;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    float l = 0.f;
-    for (uint32_t q = o0; q < o1; ++q) {
-        const float4 u = part[2 * (size_t)q], v = part[2 * (size_t)q + 1];
-        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
-        b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
-        if (part_l) l += part_l[q];
-    }
     float4 *d = reinterpret_cast<float4 *>(dparams) + 2 * (size_t)g;
     float4 d0 = d[0], d1 = d[1];
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    gather_slots(part, o0, o1, a, b);
+    float l = 0.f;
+    if (part_l)
+        for (uint32_t q = o0; q < o1; ++q) l += part_l[q];
     d0.x += a.x; d0.y += a.y; d0.z += a.z; d0.w += a.w;
     d1.x += b.x; d1.y += b.y; d1.z += b.z; d1.w += b.w;
     d[0] = d0;
@@ -379,16 +397,9 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
                                                     float4 *__restrict__ m, float4 *__restrict__ v, AdamPairArgs a) {
     const int g = blockIdx.x * 256 + threadIdx.x;
     if (g >= n) return;
-    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
-    if (offsets[n] <= capacity) {                 // else binning overflowed: zero gradient
-        const uint32_t o0 = offsets[g], o1 = offsets[g + 1];
-        for (uint32_t q = o0; q < o1; ++q) {
-            const float4 u = part[2 * (size_t)q], w = part[2 * (size_t)q + 1];
-            g0.x += u.x; g0.y += u.y; g0.z += u.z; g0.w += u.w;
-            g1.x += w.x; g1.y += w.y; g1.z += w.z; g1.w += w.w;
-        }
-    }
     float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
+    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    if (offsets[n] <= capacity) gather_slots(part, offsets[g], offsets[g + 1], g0, g1);   // else: zero gradient
     adam1(P0.x, g0.x, M0.x, V0.x, a.lr[0], a);
     adam1(P0.y, g0.y, M0.y, V0.y, a.lr[1], a);
     adam1(P0.z, g0.z, M0.z, V0.z, a.lr[2], a);
