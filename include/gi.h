@@ -129,6 +129,14 @@ gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, con
  *   vals      device uint32 [capacity] out: Gaussian index of pair m.
  *   ranges    device uint32 [T][2] out: [start, end) of tile t in keys/vals;
  *             (0, 0) for a tile with no pair.
+ *   tile_order device uint32 [T] out, or NULL: the tiles by decreasing list
+ *             length (lengths of 1023 or more count as equal; ties in no
+ *             particular order).  Passed to the raster calls it makes them take
+ *             long lists first, which balances the CUs when the whole grid of
+ *             tiles is resident at once (a few thousand tiles); it never changes
+ *             a result.  Costs one single-workgroup launch; an order from an
+ *             earlier binning is as valid (any permutation of the tiles is),
+ *             so a caller may refresh it only now and then.
  *   capacity  length of keys/vals, 0 <= capacity < 2^31.
  *   d_num     device uint32 [1] out: M (saturated at 2^32-1).  When M > capacity
  *             no pair is written, every range is (0, 0) and *d_num still holds M.
@@ -142,7 +150,7 @@ gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, con
 size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity);
 gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, const uint32_t *counts,
                       uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges,
-                      int64_t capacity, uint32_t *d_num, int64_t *h_num,
+                      uint32_t *tile_order, int64_t capacity, uint32_t *d_num, int64_t *h_num,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -161,6 +169,7 @@ gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, co
  *                     the pixel boxes let each 8x8 quadrant of a tile skip the
  *                     Gaussians that cannot reach it (no effect on the result).
  *   ranges, vals      from gi_bin_sort.
+ *   tile_order        from gi_bin_sort, or NULL (tiles in index order).
  *   background device float [3] (alpha mode) or NULL.
  *   image      device float [3][H][W] out.
  *   t_final    device float [H][W] out (alpha mode): final T; NULL in sum mode.
@@ -169,7 +178,8 @@ gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, co
  *              the tile's range start if none; NULL in sum mode.
  */
 gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
-                        const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
+                        const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *tile_order,
+                        const uint32_t *vals,
                         const float *background, float *image, float *t_final, uint32_t *last,
                         void *stream);
 
@@ -185,8 +195,9 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
  *   loss_partials device float [T] out (T = gi_num_tiles).
  */
 gi_status gi_render_fwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
-                           const uint32_t *ranges, const uint32_t *vals, const float *target,
-                           float *image, float *dL_dimage, float *loss_partials, void *stream);
+                           const uint32_t *ranges, const uint32_t *tile_order, const uint32_t *vals,
+                           const float *target, float *image, float *dL_dimage, float *loss_partials,
+                           void *stream);
 
 /* d_loss (device float [1]) = (sum of the nparts partials, in fp64, fixed order) / count. */
 gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t count, float *d_loss,
@@ -208,6 +219,7 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
  *
  *   records, opacity, pixbox: from gi_preprocess (opacity NULL in sum mode).
  *   offsets, ranges, vals, capacity: from / as given to gi_bin_sort.
+ *   tile_order from gi_bin_sort, or NULL (tiles in index order).
  *   logit     device float [n] (alpha mode, for the clamp test) or NULL.
  *   background, t_final, last: as given to / produced by gi_render_fwd (alpha
  *             mode; NULL in sum mode).
@@ -219,17 +231,18 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
  *   dbackground device float [3], accumulated (alpha mode) or NULL.
  *   workspace device scratch of gi_render_bwd_workspace_bytes() bytes, 256-byte
  *             aligned, no initialisation needed.
- *   Each (Gaussian, tile) pair's gradient is formed in the tile's workgroup
- *   (the contributions of one pair are combined with LDS atomics, whose order
- *   may vary in the last bits) and stored at the pair's emission slot
- *   offsets[n] + (position of the tile in n's tile rectangle); a second kernel
- *   adds each Gaussian's slots in that fixed order.  No global atomics.  If
- *   gi_bin_sort overflowed (M > capacity) nothing is accumulated.
+ *   Each (Gaussian, tile) pair's gradient is formed in the tile's workgroup,
+ *   its per-pixel terms added in a fixed order, and stored at the pair's
+ *   emission slot offsets[g] + (position of the tile in g's tile rectangle); a
+ *   second pass adds each Gaussian's slots in that order.  No atomics: the
+ *   gradients are bitwise reproducible.  If gi_bin_sort overflowed
+ *   (M > capacity) nothing is accumulated.
  */
 size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity);
 gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
                         const float *logit, const uint16_t *pixbox, const uint32_t *offsets,
-                        const uint32_t *ranges, const uint32_t *vals, int64_t capacity,
+                        const uint32_t *ranges, const uint32_t *tile_order, const uint32_t *vals,
+                        int64_t capacity,
                         const float *background, const float *t_final, const uint32_t *last,
                         const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
                         void *workspace, size_t workspace_bytes, void *stream);
@@ -273,11 +286,17 @@ gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float 
  *   offsets, capacity, workspace) and as gi_adam_step for the update (p, m, v
  *   device float [n][8]; lr host float [8]).  A binning overflow gives a zero
  *   gradient.
+ *   d_step    device int32 [1] or NULL.  If given, the step t is read from it on
+ *             the device (and `step` is ignored; t < 1 counts as 1), so that one
+ *             captured graph of a training step stays right on every replay
+ *             when the caller advances *d_step in the same graph.  The bias
+ *             corrections 1/(1-b1^t), 1/sqrt(1-b2^t) are formed on the device in
+ *             fp64 either way (the same bits for the same t).
  */
 gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
                              const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
                              const float *lr, double beta1, double beta2, double eps, int32_t step,
-                             void *stream);
+                             const int32_t *d_step, void *stream);
 
 #ifdef __cplusplus
 }

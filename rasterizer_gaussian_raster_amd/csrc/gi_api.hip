@@ -62,8 +62,9 @@ size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capac
 }
 
 gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, const uint32_t *counts,
-                      uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, int64_t capacity,
-                      uint32_t *d_num, int64_t *h_num, void *workspace, size_t workspace_bytes, void *stream) {
+                      uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
+                      int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace, size_t workspace_bytes,
+                      void *stream) {
     if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31))
         return GI_ERR_INVALID_ARG;
     if (!offsets || !ranges || !d_num || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
@@ -72,7 +73,8 @@ gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, co
     const gi::BinPlan plan = gi::make_bin_plan((int)n, desc->width, desc->height, capacity);
     if (workspace_bytes < plan.bytes) return GI_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
-    hipError_t e = gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, d_num, workspace, s);
+    hipError_t e =
+        gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, tile_order, d_num, workspace, s);
     if (e != hipSuccess) return GI_ERR_HIP;
     if (h_num) {
         unsigned long long total = 0;
@@ -86,31 +88,33 @@ gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, co
 }
 
 gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
-                        const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
-                        const float *background, float *image, float *t_final, uint32_t *last, void *stream) {
+                        const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *tile_order,
+                        const uint32_t *vals, const float *background, float *image, float *t_final, uint32_t *last,
+                        void *stream) {
     if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
     if (!ranges || !vals || !image || !aligned16(image)) return GI_ERR_INVALID_ARG;
     if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     if (desc->mode == GI_MODE_SUM) {
         if (opacity || background || t_final || last) return GI_ERR_INVALID_ARG;
-        return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, vals,
-                                                    image, nullptr, nullptr, nullptr, s));
+        return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, tile_order,
+                                                    vals, image, nullptr, nullptr, nullptr, s));
     }
     if (!background || !t_final || !last || (n > 0 && !opacity)) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_render_alpha_fwd(desc->width, desc->height, records, opacity, pixbox, ranges,
-                                                  vals, background, image, t_final, last, s));
+                                                  tile_order, vals, background, image, t_final, last, s));
 }
 
 gi_status gi_render_fwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
-                           const uint32_t *ranges, const uint32_t *vals, const float *target, float *image,
-                           float *dL_dimage, float *loss_partials, void *stream) {
+                           const uint32_t *ranges, const uint32_t *tile_order, const uint32_t *vals,
+                           const float *target, float *image, float *dL_dimage, float *loss_partials,
+                           void *stream) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
     if (!ranges || !vals || !image || !target || !dL_dimage || !loss_partials || !aligned16(image))
         return GI_ERR_INVALID_ARG;
     if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
-    return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, vals, image,
-                                                target, dL_dimage, loss_partials, as_stream(stream)));
+    return hip_status(gi::launch_render_sum_fwd(desc->width, desc->height, records, pixbox, ranges, tile_order,
+                                                vals, image, target, dL_dimage, loss_partials, as_stream(stream)));
 }
 
 gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t count, float *d_loss, void *stream) {
@@ -125,7 +129,7 @@ size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t cap
 
 gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
                         const float *logit, const uint16_t *pixbox, const uint32_t *offsets,
-                        const uint32_t *ranges, const uint32_t *vals, int64_t capacity,
+                        const uint32_t *ranges, const uint32_t *tile_order, const uint32_t *vals, int64_t capacity,
                         const float *background, const float *t_final, const uint32_t *last,
                         const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
                         void *workspace, size_t workspace_bytes, void *stream) {
@@ -142,7 +146,8 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     hipError_t e;
     if (desc->mode == GI_MODE_SUM) {
         if (opacity || logit || background || t_final || last || dlogit || dbackground) return GI_ERR_INVALID_ARG;
-        e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, vals, capacity, dL_dimage, workspace, s);
+        e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, tile_order, vals, capacity, dL_dimage,
+                                      workspace, s);
         if (e == hipSuccess && dparams)
             e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 0, dparams, nullptr,
                                        nullptr, s);
@@ -150,7 +155,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     }
     if (n > 0 && !dparams) return GI_ERR_INVALID_ARG;
     if (!background || !t_final || !last || (n > 0 && (!opacity || !logit))) return GI_ERR_INVALID_ARG;
-    e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, vals, capacity,
+    e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, tile_order, vals, capacity,
                                     background, t_final, last, dL_dimage, workspace, s);
     if (e == hipSuccess)
         e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 1, dparams, dlogit,
@@ -170,16 +175,17 @@ gi_status gi_loss_l2(int64_t count, const float *image, const float *target, flo
 
 gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
                              const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
-                             const float *lr, double beta1, double beta2, double eps, int32_t step, void *stream) {
+                             const float *lr, double beta1, double beta2, double eps, int32_t step,
+                             const int32_t *d_step, void *stream) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
-        capacity >= (1ll << 31) || step < 1 || !lr)
+        capacity >= (1ll << 31) || (!d_step && step < 1) || !lr)
         return GI_ERR_INVALID_ARG;
     if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0)) return GI_ERR_INVALID_ARG;
     if (!offsets || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
     if (n > 0 && (!p || !m || !v || !aligned16(p) || !aligned16(m) || !aligned16(v))) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_adam_pairs((int)n, desc->width, desc->height, offsets, capacity, workspace, p, m, v,
-                                            lr, beta1, beta2, eps, step, as_stream(stream)));
+                                            lr, beta1, beta2, eps, step, d_step, as_stream(stream)));
 }
 
 gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v, const float *lr,

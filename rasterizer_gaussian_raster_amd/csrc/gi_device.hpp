@@ -35,6 +35,14 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Adam's bias corrections for step t (t < 1 is taken as 1), formed in fp64 and
+// rounded once: 1/(1 - b1^t) and 1/sqrt(1 - b2^t).
+__device__ __forceinline__ void adam_bias(double b1, double b2, int t, float &inv_bc1, float &inv_sqrt_bc2) {
+    const double td = (double)(t < 1 ? 1 : t);
+    inv_bc1 = (float)(1.0 / (1.0 - pow(b1, td)));
+    inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(b2, td)));
+}
+
 // 2^x with the hardware transcendental (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -80,6 +88,14 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     const int per = nblocks >> 3;
     return (bid & 7) * per + (bid >> 3);
+}
+
+// The tile workgroup `bid` of `nblocks` takes: order[bid] when a tile order is
+// given (longest list first; workgroups past the tiles get none), else the
+// XCD-aware map of bid.
+__device__ __forceinline__ int tile_of(int bid, int nblocks, int ntiles, const uint32_t *order) {
+    if (order) return bid < ntiles ? (int)order[bid] : ntiles;
+    return xcd_remap(bid, nblocks);
 }
 
 // Emission slot of the pair (Gaussian g, tile (tx, ty)): offsets[g] plus the

@@ -28,19 +28,19 @@ struct BinPlan {
 };
 BinPlan make_bin_plan(int n, int W, int H, int64_t capacity);
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
-                           uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *d_num, void *ws,
-                           hipStream_t s);
+                           uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
+                           void *ws, hipStream_t s);
 // device address of the 64-bit instance total inside the workspace
 const void *bin_total_ptr(const void *ws);
 
 // k_raster_sum.hip
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *vals, float *image, const float *target,
-                                 float *dL_dimage, float *loss_partials, hipStream_t s);
+                                 const uint32_t *ranges, const uint32_t *order, const uint32_t *vals, float *image,
+                                 const float *target, float *dL_dimage, float *loss_partials, hipStream_t s);
 hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, float *d_loss, hipStream_t s);
 hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
                              float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
-                             hipStream_t s);
+                             const int32_t *d_step, hipStream_t s);
 
 // Backward workspace: per (Gaussian, tile) gradient at its emission slot.
 struct BwdPlan {
@@ -51,8 +51,9 @@ struct BwdPlan {
 };
 BwdPlan make_bwd_plan(int W, int H, int64_t capacity);
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *vals,
-                                 int64_t capacity, const float *dL_dimage, void *ws, hipStream_t s);
+                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
+                                 const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
+                                 hipStream_t s);
 // Adds each Gaussian's slots (offsets[g] .. offsets[g+1]) in order to dparams / dlogit, and the
 // per-tile background partials to dbackground.
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
@@ -61,12 +62,13 @@ hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *o
 
 // k_raster_alpha.hip
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
-                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
-                                   const float *background, float *image, float *t_final, uint32_t *last,
-                                   hipStream_t s);
+                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *order,
+                                   const uint32_t *vals, const float *background, float *image, float *t_final,
+                                   uint32_t *last, hipStream_t s);
 hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
                                    const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
-                                   const uint32_t *vals, int64_t capacity, const float *background,
+                                   const uint32_t *order, const uint32_t *vals, int64_t capacity,
+                                   const float *background,
                                    const float *t_final, const uint32_t *last, const float *dL_dimage, void *ws,
                                    hipStream_t s);
 

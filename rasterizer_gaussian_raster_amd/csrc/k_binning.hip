@@ -19,6 +19,10 @@
 //   4. k_scatter0   : first sort pass, straight from the regenerated pairs.
 //   5. k_count / k_scatter : further passes over blocks of 1024-4096 keys.
 //   6. k_ranges     : marks where each tile's run starts and ends.
+//   7. k_tile_order : (optional) the tiles by decreasing list length, the order
+//                     in which the raster kernels should take them: long lists
+//                     first spread the work evenly over the CUs when the whole
+//                     grid is resident at once.
 //
 // Each scatter block ranks up to 4096 keys at a time: every wave takes a
 // contiguous span of the chunk and finds the rank of each key among the equal
@@ -678,6 +682,38 @@ __global__ __launch_bounds__(256) void k_ranges(const uint32_t *__restrict__ key
 }
 
 // ---------------------------------------------------------------------------
+// 7: tile order (longest list first)
+// ---------------------------------------------------------------------------
+// A counting sort of the tiles by list length, one workgroup of 1024: lengths
+// of 1023 or more share the first bucket, and tiles of equal bucket land in no
+// particular order (the order only schedules work: every tile's results are
+// its own, whatever the order).
+__global__ __launch_bounds__(1024) void k_tile_order(const uint2 *__restrict__ ranges, int ntiles,
+                                                     uint32_t *__restrict__ order) {
+    __shared__ uint32_t hist[1024];
+    __shared__ uint32_t sm[16];
+    const int tid = threadIdx.x;
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int t = tid; t < ntiles; t += 1024) {
+        const uint2 r = ranges[t];
+        const uint32_t len = r.y > r.x ? r.y - r.x : 0u;
+        atomicAdd(&hist[1023u - min(len, 1023u)], 1u);
+    }
+    __syncthreads();
+    const uint32_t h = hist[tid];
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<uint32_t, 1024>(h, sm, &tot);
+    hist[tid] = ex;
+    __syncthreads();
+    for (int t = tid; t < ntiles; t += 1024) {
+        const uint2 r = ranges[t];
+        const uint32_t len = r.y > r.x ? r.y - r.x : 0u;
+        order[atomicAdd(&hist[1023u - min(len, 1023u)], 1u)] = (uint32_t)t;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -728,8 +764,8 @@ BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
 const void *bin_total_ptr(const void *ws) { return &static_cast<const BinHeader *>(ws)->total; }
 
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
-                           uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *d_num, void *ws,
-                           hipStream_t s) {
+                           uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
+                           void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
     BinHeader *hdr = reinterpret_cast<BinHeader *>(w);
     unsigned long long *part = reinterpret_cast<unsigned long long *>(w + p.off_part);
@@ -738,17 +774,26 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     uint32_t *table = reinterpret_cast<uint32_t *>(w + p.off_table);
     uint32_t *tsp = reinterpret_cast<uint32_t *>(w + p.off_tsp);
     const uint2 *box = reinterpret_cast<const uint2 *>(pixbox);
+    // ranges, then the tile order when one is asked for (also for n == 0 or capacity == 0)
+    auto finish = [&]() -> hipError_t {
+        if (p.capacity > 0)
+            k_ranges<<<(unsigned)((p.capacity + 1023) / 1024), 256, 0, s>>>(keys, hdr, (uint32_t)p.ntiles, ranges);
+        if (tile_order)
+            k_tile_order<<<1, 1024, 0, s>>>(reinterpret_cast<const uint2 *>(ranges), p.ntiles, tile_order);
+        return hipGetLastError();
+    };
 
     k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, part, p.ntiles,
                                                          reinterpret_cast<uint2 *>(ranges), hdr, offsets, d_num);
-    if (p.n == 0) return hipGetLastError();
+    if (p.n == 0) return finish();
     if (!p.redundant_groups)
         k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
     k_count0<<<p.nseg, kBT, 0, s>>>(p.n, p.nb_g, p.seg_groups, p.redundant_groups, (long long)p.capacity,
                                     p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], counts, box, part,
                                     hdr, offsets, d_num, table);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.capacity == 0) return e;
+    if (e != hipSuccess) return e;
+    if (p.capacity == 0) return finish();
     // pass i writes keys/vals when an even number of passes follow it
     auto dst_k = [&](int i) { return ((p.passes - 1 - i) & 1) ? kalt : keys; };
     auto dst_v = [&](int i) { return ((p.passes - 1 - i) & 1) ? valt : vals; };
@@ -781,8 +826,7 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
             k_scatter<16><<<p.nbs, kBT, 0, s>>>(sk, sv, dst_k(i), dst_v(i), hdr, shift, b, tr, nc, table);
         shift += p.bits[i];
     }
-    k_ranges<<<(unsigned)((p.capacity + 1023) / 1024), 256, 0, s>>>(keys, hdr, (uint32_t)p.ntiles, ranges);
-    return hipGetLastError();
+    return finish();
 }
 
 }  // namespace gi

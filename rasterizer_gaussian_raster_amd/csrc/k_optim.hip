@@ -63,15 +63,22 @@ hipError_t launch_loss_l2(int64_t count, const float *image, const float *target
 
 struct AdamArgs {
     float lr[16];
-    float b1, omb1, b2, omb2, eps, inv_bc1, inv_sqrt_bc2;   // omb = 1 - beta, formed in double
+    float b1, omb1, b2, omb2, eps;   // omb = 1 - beta, formed in double
+    double b1d, b2d;                 // for the bias corrections
+    int step;
     int row_len;
 };
 
-__device__ __forceinline__ void adam_one(float &p, float &g, float &m, float &v, float lr, const AdamArgs &a) {
+struct AdamBias {
+    float inv_bc1, inv_sqrt_bc2;
+};
+
+__device__ __forceinline__ void adam_one(float &p, float &g, float &m, float &v, float lr, const AdamArgs &a,
+                                         const AdamBias &c) {
     m = fmaf(a.b1, m, a.omb1 * g);
     v = fmaf(a.b2, v, a.omb2 * g * g);
-    const float den = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
-    p -= lr * (m * a.inv_bc1) / den;
+    const float den = sqrtf(v) * c.inv_sqrt_bc2 + a.eps;
+    p -= lr * (m * c.inv_bc1) / den;
 }
 
 // 4 consecutive scalars per thread (row_len divisible by 4, 16-byte aligned arrays).
@@ -81,11 +88,13 @@ __global__ __launch_bounds__(256) void k_adam4(int64_t n4, float4 *__restrict__ 
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
     float4 P = p[i], G = g[i], Mm = m[i], V = v[i];
+    AdamBias c;
+    adam_bias(a.b1d, a.b2d, a.step, c.inv_bc1, c.inv_sqrt_bc2);
     const int s0 = (int)((i * 4) % a.row_len);
-    adam_one(P.x, G.x, Mm.x, V.x, a.lr[s0 + 0], a);
-    adam_one(P.y, G.y, Mm.y, V.y, a.lr[s0 + 1], a);
-    adam_one(P.z, G.z, Mm.z, V.z, a.lr[s0 + 2], a);
-    adam_one(P.w, G.w, Mm.w, V.w, a.lr[s0 + 3], a);
+    adam_one(P.x, G.x, Mm.x, V.x, a.lr[s0 + 0], a, c);
+    adam_one(P.y, G.y, Mm.y, V.y, a.lr[s0 + 1], a, c);
+    adam_one(P.z, G.z, Mm.z, V.z, a.lr[s0 + 2], a, c);
+    adam_one(P.w, G.w, Mm.w, V.w, a.lr[s0 + 3], a, c);
     p[i] = P;
     m[i] = Mm;
     v[i] = V;
@@ -98,7 +107,9 @@ __global__ __launch_bounds__(256) void k_adam1(int64_t n, float *__restrict__ p,
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float P = p[i], G = g[i], Mm = m[i], V = v[i];
-    adam_one(P, G, Mm, V, a.lr[i % a.row_len], a);
+    AdamBias c;
+    adam_bias(a.b1d, a.b2d, a.step, c.inv_bc1, c.inv_sqrt_bc2);
+    adam_one(P, G, Mm, V, a.lr[i % a.row_len], a, c);
     p[i] = P;
     m[i] = Mm;
     v[i] = V;
@@ -114,8 +125,9 @@ hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, 
     a.b2 = (float)beta2;
     a.omb2 = (float)(1.0 - beta2);
     a.eps = (float)eps;
-    a.inv_bc1 = (float)(1.0 / (1.0 - pow(beta1, (double)step)));
-    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(beta2, (double)step)));
+    a.b1d = beta1;
+    a.b2d = beta2;
+    a.step = step;
     a.row_len = row_len;
     const int64_t n = rows * row_len;
     if (n == 0) return hipSuccess;

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
                                                           const float4 *__restrict__ records,
                                                           const float *__restrict__ opacity,
                                                           const uint2 *__restrict__ pixbox,
-                                                          const uint2 *__restrict__ ranges,
+                                                          const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
                                                           const uint32_t *__restrict__ vals,
                                                           const float *__restrict__ bg,
                                                           float *__restrict__ image, float *__restrict__ t_final,
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
     __shared__ AlphaRec lst[4][kBatch];
     __shared__ int wq[4][4];
     __shared__ int wdone[4];
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                                                           const float *__restrict__ logit,
                                                           const uint2 *__restrict__ pixbox,
                                                           const uint32_t *__restrict__ offsets,
-                                                          const uint2 *__restrict__ ranges,
+                                                          const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
                                                           const uint32_t *__restrict__ vals, uint32_t capacity,
                                                           const float *__restrict__ bg,
                                                           const float *__restrict__ t_final,
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
     __shared__ float wbg[4][3];
     __shared__ uint32_t eslot[kBatch];
     __shared__ uint8_t qpos[kBatch][4];
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
@@ -314,20 +314,21 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
 
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
-                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *vals,
-                                   const float *background, float *image, float *t_final, uint32_t *last,
-                                   hipStream_t s) {
+                                   const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *order,
+                                   const uint32_t *vals, const float *background, float *image, float *t_final,
+                                   uint32_t *last, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     k_render_alpha_fwd<<<padded_tiles(ntiles), 256, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity,
-        reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), vals, background, image,
-        t_final, last);
+        reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), order, vals, background,
+        image, t_final, last);
     return hipGetLastError();
 }
 
 hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
                                    const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
-                                   const uint32_t *vals, int64_t capacity, const float *background,
+                                   const uint32_t *order, const uint32_t *vals, int64_t capacity,
+                                   const float *background,
                                    const float *t_final, const uint32_t *last, const float *dL_dimage, void *ws,
                                    hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
@@ -335,7 +336,7 @@ hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const flo
     char *w = static_cast<char *>(ws);
     k_render_alpha_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity, logit,
-        reinterpret_cast<const uint2 *>(pixbox), offsets, reinterpret_cast<const uint2 *>(ranges), vals,
+        reinterpret_cast<const uint2 *>(pixbox), offsets, reinterpret_cast<const uint2 *>(ranges), order, vals,
         (uint32_t)capacity, background, t_final, last, dL_dimage, reinterpret_cast<float4 *>(w + p.off_part),
         reinterpret_cast<float *>(w + p.off_logit), reinterpret_cast<float4 *>(w + p.off_bg));
     return hipGetLastError();

@@ -41,7 +41,7 @@ template <bool L2>
 __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
-                                                        const uint2 *__restrict__ ranges,
+                                                        const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
                                                         const uint32_t *__restrict__ vals,
                                                         float *__restrict__ image,
                                                         const float *__restrict__ target,
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
                                                         float *__restrict__ loss_part) {
     __shared__ SumRec lst[4][kFwdBatch];
     __shared__ int wq[4][4];                      // [wave][quadrant]: staged count this batch
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
                                                         const uint32_t *__restrict__ offsets,
-                                                        const uint2 *__restrict__ ranges,
+                                                        const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
                                                         const uint32_t *__restrict__ vals, uint32_t capacity,
                                                         const float *__restrict__ dL,
                                                         float4 *__restrict__ part) {
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
     __shared__ float4 entp[4][kWaveEnt], entq[4][kWaveEnt];   // per wave: its staged entries (p, q)
     __shared__ uint16_t items[4][kWaveEnt * 16];        // per wave: entry | block << 8, entry-major
     __shared__ float4 ipart[4][2][64];                  // per wave: this round's item results
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const uint2 rg = ranges[t];
     if (rg.x == rg.y) return;
@@ -383,13 +383,17 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
 // the optimizer in one pass, no gradient array.
 struct AdamPairArgs {
     float lr[8];
-    float b1, omb1, b2, omb2, eps, inv_bc1, inv_sqrt_bc2;
+    float b1, omb1, b2, omb2, eps;
+    double b1d, b2d;                 // for the bias corrections
+    int step;                        // used when d_step is NULL
+    const int32_t *d_step;           // device step count (graph replays), or NULL
 };
 
-__device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, float lr, const AdamPairArgs &a) {
+__device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, float lr, const AdamPairArgs &a,
+                                      float inv_bc1, float inv_sqrt_bc2) {
     m = fmaf(a.b1, m, a.omb1 * g);
     v = fmaf(a.b2, v, a.omb2 * g * g);
-    p -= lr * (m * a.inv_bc1) / (sqrtf(v) * a.inv_sqrt_bc2 + a.eps);
+    p -= lr * (m * inv_bc1) / (sqrtf(v) * inv_sqrt_bc2 + a.eps);
 }
 
 __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
@@ -399,15 +403,18 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
     if (g >= n) return;
     float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
     float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    const int t = a.d_step ? *a.d_step : a.step;
     if (offsets[n] <= capacity) gather_slots(part, offsets[g], offsets[g + 1], g0, g1);   // else: zero gradient
-    adam1(P0.x, g0.x, M0.x, V0.x, a.lr[0], a);
-    adam1(P0.y, g0.y, M0.y, V0.y, a.lr[1], a);
-    adam1(P0.z, g0.z, M0.z, V0.z, a.lr[2], a);
-    adam1(P0.w, g0.w, M0.w, V0.w, a.lr[3], a);
-    adam1(P1.x, g1.x, M1.x, V1.x, a.lr[4], a);
-    adam1(P1.y, g1.y, M1.y, V1.y, a.lr[5], a);
-    adam1(P1.z, g1.z, M1.z, V1.z, a.lr[6], a);
-    adam1(P1.w, g1.w, M1.w, V1.w, a.lr[7], a);
+    float c1, c2;
+    adam_bias(a.b1d, a.b2d, t, c1, c2);
+    adam1(P0.x, g0.x, M0.x, V0.x, a.lr[0], a, c1, c2);
+    adam1(P0.y, g0.y, M0.y, V0.y, a.lr[1], a, c1, c2);
+    adam1(P0.z, g0.z, M0.z, V0.z, a.lr[2], a, c1, c2);
+    adam1(P0.w, g0.w, M0.w, V0.w, a.lr[3], a, c1, c2);
+    adam1(P1.x, g1.x, M1.x, V1.x, a.lr[4], a, c1, c2);
+    adam1(P1.y, g1.y, M1.y, V1.y, a.lr[5], a, c1, c2);
+    adam1(P1.z, g1.z, M1.z, V1.z, a.lr[6], a, c1, c2);
+    adam1(P1.w, g1.w, M1.w, V1.w, a.lr[7], a, c1, c2);
     p[2 * g] = P0; p[2 * g + 1] = P1;
     m[2 * g] = M0; m[2 * g + 1] = M1;
     v[2 * g] = V0; v[2 * g + 1] = V1;
@@ -431,7 +438,7 @@ BwdPlan make_bwd_plan(int W, int H, int64_t capacity) {
 
 hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
                              float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
-                             hipStream_t s) {
+                             const int32_t *d_step, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
     AdamPairArgs a{};
@@ -441,8 +448,10 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
     a.b2 = (float)beta2;
     a.omb2 = (float)(1.0 - beta2);
     a.eps = (float)eps;
-    a.inv_bc1 = (float)(1.0 / (1.0 - pow(beta1, (double)step)));
-    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(beta2, (double)step)));
+    a.b1d = beta1;
+    a.b2d = beta2;
+    a.step = step;
+    a.d_step = d_step;
     k_adam_pairs<<<(n + 255) / 256, 256, 0, s>>>(
         n, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(static_cast<const char *>(ws) + pl.off_part),
         reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a);
@@ -465,18 +474,18 @@ hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *o
 }
 
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *vals, float *image, const float *target,
-                                 float *dL_dimage, float *loss_partials, hipStream_t s) {
+                                 const uint32_t *ranges, const uint32_t *order, const uint32_t *vals, float *image,
+                                 const float *target, float *dL_dimage, float *loss_partials, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const float4 *rec = reinterpret_cast<const float4 *>(records);
     const uint2 *bx = reinterpret_cast<const uint2 *>(pixbox);
     const uint2 *rg = reinterpret_cast<const uint2 *>(ranges);
     if (target) {
         const float gscale = (float)(2.0 / (3.0 * (double)W * (double)H));
-        k_render_sum_fwd<true><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, vals, image,
-                                                                     target, dL_dimage, gscale, loss_partials);
+        k_render_sum_fwd<true><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, order, vals,
+                                                                     image, target, dL_dimage, gscale, loss_partials);
     } else {
-        k_render_sum_fwd<false><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, vals,
+        k_render_sum_fwd<false><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, order, vals,
                                                                       image, nullptr, nullptr, 0.0f, nullptr);
     }
     return hipGetLastError();
@@ -488,13 +497,14 @@ hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, 
 }
 
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *vals,
-                                 int64_t capacity, const float *dL_dimage, void *ws, hipStream_t s) {
+                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
+                                 const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
+                                 hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     k_render_sum_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
-        offsets, reinterpret_cast<const uint2 *>(ranges), vals, (uint32_t)capacity, dL_dimage,
+        offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, dL_dimage,
         reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part));
     return hipGetLastError();
 }

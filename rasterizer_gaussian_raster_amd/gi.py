@@ -53,16 +53,16 @@ def load():
         "gi_num_tiles": ([D], i64),
         "gi_preprocess": ([D, i64, P, P, P, P, P, P, P], i32),
         "gi_bin_sort_workspace_bytes": ([D, i64, i64], sz),
-        "gi_bin_sort": ([D, i64, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
-        "gi_render_fwd": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
+        "gi_bin_sort": ([D, i64, P, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
+        "gi_render_fwd": ([D, i64, P, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_render_bwd_workspace_bytes": ([D, i64, i64], sz),
-        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P, P, sz, P], i32),
+        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P, P, sz, P], i32),
         "gi_loss_workspace_bytes": ([i64], sz),
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
-        "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P], i32),
+        "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
-        "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P], i32),
+        "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -84,8 +84,14 @@ def _ptr(t):
     return ctypes.c_void_p(int(t))
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
+    """hipStream_t of `stream` (a torch stream or a raw handle); None: torch's current stream."""
     if stream is None:
+        if _raw_stream is not None:      # the raw handle without building a Stream object
+            return ctypes.c_void_p(_raw_stream(torch.cuda.current_device()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
@@ -117,22 +123,23 @@ def gi_bin_sort_workspace_bytes(d, n, capacity) -> int:
 
 
 def gi_bin_sort(d, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
-                sync_count=False, stream=None):
+                sync_count=False, stream=None, tile_order=None):
     """Returns M (host int) when sync_count, else None.  Raises GiError(GI_ERR_CAPACITY) on overflow
     when sync_count."""
     h = ctypes.c_int64(-1)
     st = load().gi_bin_sort(ctypes.byref(d), int(n), _ptr(pixbox), _ptr(counts), _ptr(offsets), _ptr(keys),
-                            _ptr(vals), _ptr(ranges), int(capacity), _ptr(d_num),
+                            _ptr(vals), _ptr(ranges), _ptr(tile_order), int(capacity), _ptr(d_num),
                             ctypes.byref(h) if sync_count else None, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gi_bin_sort")
     return int(h.value) if sync_count else None
 
 
-def gi_render_fwd(d, n, records, opacity, pixbox, ranges, vals, background, image, t_final, last, stream=None):
+def gi_render_fwd(d, n, records, opacity, pixbox, ranges, vals, background, image, t_final, last, stream=None,
+                  tile_order=None):
     _check(load().gi_render_fwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(pixbox),
-                                _ptr(ranges), _ptr(vals), _ptr(background), _ptr(image), _ptr(t_final),
-                                _ptr(last), _stream(stream)), "gi_render_fwd")
+                                _ptr(ranges), _ptr(tile_order), _ptr(vals), _ptr(background), _ptr(image),
+                                _ptr(t_final), _ptr(last), _stream(stream)), "gi_render_fwd")
 
 
 def gi_render_bwd_workspace_bytes(d, n, capacity) -> int:
@@ -140,9 +147,10 @@ def gi_render_bwd_workspace_bytes(d, n, capacity) -> int:
 
 
 def gi_render_bwd(d, n, records, opacity, logit, pixbox, offsets, ranges, vals, capacity, background, t_final,
-                  last, dL_dimage, dparams, dlogit, dbackground, workspace, stream=None):
+                  last, dL_dimage, dparams, dlogit, dbackground, workspace, stream=None, tile_order=None):
     _check(load().gi_render_bwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(logit),
-                                _ptr(pixbox), _ptr(offsets), _ptr(ranges), _ptr(vals), int(capacity),
+                                _ptr(pixbox), _ptr(offsets), _ptr(ranges), _ptr(tile_order), _ptr(vals),
+                                int(capacity),
                                 _ptr(background), _ptr(t_final), _ptr(last), _ptr(dL_dimage), _ptr(dparams),
                                 _ptr(dlogit), _ptr(dbackground), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)), "gi_render_bwd")
@@ -165,8 +173,10 @@ def gi_adam_step(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_gr
                                _stream(stream)), "gi_adam_step")
 
 
-def gi_render_fwd_l2(d, n, records, pixbox, ranges, vals, target, image, dL_dimage, loss_partials, stream=None):
-    _check(load().gi_render_fwd_l2(ctypes.byref(d), int(n), _ptr(records), _ptr(pixbox), _ptr(ranges), _ptr(vals),
+def gi_render_fwd_l2(d, n, records, pixbox, ranges, vals, target, image, dL_dimage, loss_partials, stream=None,
+                     tile_order=None):
+    _check(load().gi_render_fwd_l2(ctypes.byref(d), int(n), _ptr(records), _ptr(pixbox), _ptr(ranges),
+                                   _ptr(tile_order), _ptr(vals),
                                    _ptr(target), _ptr(image), _ptr(dL_dimage), _ptr(loss_partials),
                                    _stream(stream)), "gi_render_fwd_l2")
 
@@ -176,9 +186,12 @@ def gi_loss_reduce(nparts, loss_partials, count, d_loss, stream=None):
            "gi_loss_reduce")
 
 
-def gi_adam_step_pairs(d, n, offsets, capacity, workspace, p, m, v, lr, beta1, beta2, eps, step, stream=None):
+def gi_adam_step_pairs(d, n, offsets, capacity, workspace, p, m, v, lr, beta1, beta2, eps, step, stream=None,
+                       d_step=None):
+    """d_step: optional device int32 [1] holding the step (read on the device; `step` is then ignored)."""
     lr_arr = (ctypes.c_float * 8)(*[float(x) for x in lr])
     _check(load().gi_adam_step_pairs(ctypes.byref(d), int(n), _ptr(offsets), int(capacity), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _ptr(p), _ptr(m), _ptr(v),
-                                     lr_arr, float(beta1), float(beta2), float(eps), int(step), _stream(stream)),
+                                     lr_arr, float(beta1), float(beta2), float(eps), int(step), _ptr(d_step),
+                                     _stream(stream)),
            "gi_adam_step_pairs")

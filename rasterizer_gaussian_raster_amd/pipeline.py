@@ -8,6 +8,10 @@ the C ABI (through :mod:`.gi`):
                      -> gi_render_bwd (pair gradients left in its workspace) -> gi_adam_step_pairs
   fit (alpha mode) : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
 
+Fitter.capture() records the sum-mode step as HIP graphs (torch.cuda.CUDAGraph over the same
+calls on the capture stream); step() then replays one graph per step: a single launch instead of a
+dozen, so the host no longer paces the GPU.  Adam then reads its step count from device memory.
+
 uint32/uint16 device arrays are held in int32/int16 tensors (same bytes).
 """
 from __future__ import annotations
@@ -19,6 +23,14 @@ from . import gi
 # Default per-slot learning rates (pixels for the mean and the Cholesky factor,
 # colour units for the colours).
 DEFAULT_LR = (0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005)
+
+# Up to this many tiles the raster kernels take the tiles longest list first
+# (gi_bin_sort's tile_order): the whole grid is then resident on the chip at once
+# and the order is what balances the CUs.  Larger grids balance themselves.  The
+# order is a schedule, not data: one from an earlier binning is as valid, so a fit
+# refreshes it every ORDER_EVERY steps only.
+ORDER_MAX_TILES = 8192
+ORDER_EVERY = 16
 
 
 class Raster:
@@ -42,6 +54,9 @@ class Raster:
         self.t_final = torch.empty((self.H, self.W), dtype=torch.float32, device=dev) if alpha else None
         self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev) if alpha else None
         self.loss_partials = torch.empty(max(self.T, 1), dtype=torch.float32, device=dev)
+        self.order = (torch.empty(max(self.T, 1), dtype=torch.int32, device=dev)
+                      if self.T <= ORDER_MAX_TILES else None)
+        self.has_order = False          # an order has been written (by any earlier binning)
         self.capacity = 0
         self.keys = self.vals = self.ws = self.bwd_ws = None
         self.M = None
@@ -59,40 +74,52 @@ class Raster:
         self.bwd_ws = None                      # sized on first backward (capacity-dependent)
 
     # -- steps ---------------------------------------------------------------------------------
+    def _order(self):
+        return self.order if self.has_order else None
+
     def preprocess(self, params, logit=None, stream=None):
         gi.gi_preprocess(self.desc, self.n, params, logit, self.records, self.opacity, self.pixbox, self.counts,
                          stream)
 
-    def bin(self, sync=False, slack=1.25, stream=None):
-        """Bin and sort.  sync: read M back (one host wait) and grow the buffers if needed."""
+    def bin(self, sync=False, slack=1.25, stream=None, order=None):
+        """Bin and sort.  sync: read M back (one host wait) and grow the buffers if needed.
+        order: also (re)write the tile order; default: only when none has been written yet."""
+        if order is None:
+            order = not self.has_order
+        tile_order = self.order if order else None
+        if tile_order is not None:
+            self.has_order = True
         if self.keys is None:
             self.set_capacity(max(1024, 4 * self.n))
             sync = True
         if not sync:
             gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
-                           self.ranges, self.capacity, self.d_num, self.ws, sync_count=False, stream=stream)
+                           self.ranges, self.capacity, self.d_num, self.ws, sync_count=False, stream=stream,
+                           tile_order=tile_order)
             return None
         try:
             M = gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
-                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream)
+                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream,
+                               tile_order=tile_order)
         except gi.GiError as e:
             if e.status != gi.GI_ERR_CAPACITY:
                 raise
             M = int(self.d_num.cpu().view(torch.int32).item()) & 0xFFFFFFFF
             self.set_capacity(int(M * slack) + 1024)
             M = gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
-                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream)
+                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream,
+                               tile_order=tile_order)
         self.M = M
         return M
 
     def forward(self, background=None, stream=None):
         gi.gi_render_fwd(self.desc, self.n, self.records, self.opacity, self.pixbox, self.ranges, self.vals,
-                         background, self.image, self.t_final, self.last, stream)
+                         background, self.image, self.t_final, self.last, stream, tile_order=self._order())
         return self.image
 
     def forward_l2(self, target, dL_dimage, stream=None):
         gi.gi_render_fwd_l2(self.desc, self.n, self.records, self.pixbox, self.ranges, self.vals, target, self.image,
-                            dL_dimage, self.loss_partials, stream)
+                            dL_dimage, self.loss_partials, stream, tile_order=self._order())
         return self.image
 
     def backward(self, dL_dimage, dparams, logit=None, background=None, dlogit=None, dbackground=None,
@@ -103,7 +130,7 @@ class Raster:
             self.bwd_ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device(self.device))
         gi.gi_render_bwd(self.desc, self.n, self.records, self.opacity, logit, self.pixbox, self.offsets,
                          self.ranges, self.vals, self.capacity, background, self.t_final, self.last, dL_dimage,
-                         dparams, dlogit, dbackground, self.bwd_ws, stream)
+                         dparams, dlogit, dbackground, self.bwd_ws, stream, tile_order=self._order())
 
     def render(self, params, logit=None, background=None, sync=True):
         self.preprocess(params, logit)
@@ -139,6 +166,8 @@ class Fitter:
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self.loss_ws = torch.empty(gi.gi_loss_workspace_bytes(self.target.numel()), dtype=torch.uint8, device=dev)
         self.step_count = 0
+        self.graphs = None
+        self.d_step = None
         self.slack = capacity_slack
         # size the tile-pair buffers once, with room for the Gaussians to spread
         self.raster.preprocess(self.params, self.logit)
@@ -152,6 +181,7 @@ class Fitter:
         """Host wait: grow the pair buffers when the last binning came near (or over) capacity."""
         M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
         if M > 0.8 * self.raster.capacity:
+            self.graphs = None              # the captured graphs hold the old buffers: capture() again
             self.raster.set_capacity(int(M * self.slack) + 4096)
             self.raster.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(self.raster.desc, self.n,
                                                                               self.raster.capacity),
@@ -159,29 +189,63 @@ class Fitter:
             return True
         return False
 
+    def _sum_step(self, order, ev=(None,) * 4, d_step=None):
+        """The sum-mode step's calls.  d_step: device step counter, advanced here (graph mode)."""
+        r = self.raster
+        r.preprocess(self.params)
+        r.bin(sync=False, order=order)
+        ev[0] is not None and ev[0].record()
+        r.forward_l2(self.target, self.dL)
+        ev[1] is not None and ev[1].record()
+        gi.gi_loss_reduce(r.T, r.loss_partials, self.target.numel(), self.loss)
+        ev[2] is not None and ev[2].record()
+        r.backward(self.dL, None)
+        ev[3] is not None and ev[3].record()
+        if d_step is not None:
+            d_step.add_(1)
+        b1, b2 = self.betas
+        gi.gi_adam_step_pairs(r.desc, self.n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v,
+                              self.lr, b1, b2, self.eps, self.step_count + 1, d_step=d_step)
+
+    def capture(self, warmup=2):
+        """Record the sum-mode step as two HIP graphs (with and without the tile-order refresh).  The
+        `warmup` steps run first (real steps) on a side stream, as graph capture asks."""
+        if self.logit is not None:
+            raise ValueError("graph capture is for the sum mode")
+        dev = self.params.device
+        self.d_step = torch.full((1,), self.step_count, dtype=torch.int32, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                self._sum_step(self.step_count % ORDER_EVERY == 0, d_step=self.d_step)
+                self.step_count += 1
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graphs = {}
+        for order in (False, True):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._sum_step(order, d_step=self.d_step)
+            graphs[order] = g
+        torch.cuda.synchronize(dev)
+        self.graphs = graphs
+
     def step(self, events=None):
         """One training step.  events: optional 4 torch events recorded around the raster kernels
-        (before/after forward, before/after backward) on the current stream."""
-        r = self.raster
-        ev = events if events is not None else (None,) * 4
-        if self.logit is None:
-            r.preprocess(self.params)
-            r.bin(sync=False)
-            ev[0] is not None and ev[0].record()
-            r.forward_l2(self.target, self.dL)
-            ev[1] is not None and ev[1].record()
-            gi.gi_loss_reduce(r.T, r.loss_partials, self.target.numel(), self.loss)
-            ev[2] is not None and ev[2].record()
-            r.backward(self.dL, None)
-            ev[3] is not None and ev[3].record()
+        (before/after forward, before/after backward) on the current stream (eager steps only)."""
+        if self.graphs is not None:
+            self.graphs[self.step_count % ORDER_EVERY == 0].replay()
             self.step_count += 1
-            b1, b2 = self.betas
-            gi.gi_adam_step_pairs(r.desc, self.n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v,
-                                  self.lr, b1, b2, self.eps, self.step_count)
+            return
+        r = self.raster
+        if self.logit is None:
+            self._sum_step(self.step_count % ORDER_EVERY == 0, events if events is not None else (None,) * 4)
+            self.step_count += 1
             return
         bg = self.bg4
         r.preprocess(self.params, self.logit)
-        r.bin(sync=False)
+        r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0)
         r.forward(bg)
         gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
         r.backward(self.dL, self.grad, logit=self.logit, background=bg, dlogit=self.g_logit,
