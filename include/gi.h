@@ -118,7 +118,7 @@ gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, con
  * gi_bin_sort -- tile lists: every (tile, Gaussian) pair of the pixel boxes,
  *   ordered by tile and, within a tile, by ascending Gaussian index.  Pairs are
  *   emitted per Gaussian in (index, tile row, tile column) order and sorted by
- *   tile id with a stable LSD radix sort, so each tile's list is in index order
+ *   tile id with a stable radix sort, so each tile's list is in index order
  *   (the summation order of the sum image and the front-to-back order of the
  *   alpha image).  Reading: tile binning is what the FlashImgs viewer calls
  *   "tile-binned compute" (Web viewer) with fvdb's 16-pixel tiles.
@@ -152,6 +152,21 @@ gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, co
                       uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges,
                       uint32_t *tile_order, int64_t capacity, uint32_t *d_num, int64_t *h_num,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gi_preprocess_bin_sort -- gi_preprocess followed by gi_bin_sort on the same
+ *   stream, with identical outputs, in one call that saves a launch: the
+ *   preprocess kernel also writes the per-group pair totals the binning would
+ *   otherwise compute in a kernel of its own and clears ranges.  Arguments as in
+ *   the two calls (the preprocess outputs pixbox and counts are written and then
+ *   read by the binning); the same errors, checked before anything is launched.
+ *   workspace must hold gi_bin_sort_workspace_bytes() bytes.
+ */
+gi_status gi_preprocess_bin_sort(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                                 float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
+                                 uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges,
+                                 uint32_t *tile_order, int64_t capacity, uint32_t *d_num, int64_t *h_num,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gi_render_fwd -- rasterize the binned Gaussians into an image.
@@ -229,6 +244,11 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
  *             workspace for gi_adam_step_pairs (no gather pass).
  *   dlogit    device float [n], accumulated (alpha mode) or NULL.
  *   dbackground device float [3], accumulated (alpha mode) or NULL.
+ *   loss_partials, loss_count, d_loss (sum mode, optional): when d_loss is not
+ *             NULL, a spare workgroup of the same launch also does what
+ *             gi_loss_reduce(T, loss_partials, loss_count, d_loss) does (the
+ *             partials of gi_render_fwd_l2; one launch fewer per training step);
+ *             NULL in alpha mode.
  *   workspace device scratch of gi_render_bwd_workspace_bytes() bytes, 256-byte
  *             aligned, no initialisation needed.
  *   Each (Gaussian, tile) pair's gradient is formed in the tile's workgroup,
@@ -245,6 +265,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
                         int64_t capacity,
                         const float *background, const float *t_final, const uint32_t *last,
                         const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                        const float *loss_partials, int64_t loss_count, float *d_loss,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -42,18 +42,49 @@ int64_t gi_num_tiles(const gi_desc *desc) {
     return (int64_t)((desc->width + 15) / 16) * ((desc->height + 15) / 16);
 }
 
-gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, const float *logit, float *records,
-                        float *opacity, uint16_t *pixbox, uint32_t *counts, void *stream) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+bool preprocess_args_ok(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                        const float *records, const float *opacity, const uint16_t *pixbox, const uint32_t *counts) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return false;
     const bool alpha = desc->mode == GI_MODE_ALPHA;
     if (n > 0) {
-        if (!params || !records || !pixbox || !counts) return GI_ERR_INVALID_ARG;
-        if (!aligned16(params) || !aligned16(records) || !aligned16(pixbox) || !aligned16(counts))
-            return GI_ERR_INVALID_ARG;
-        if (alpha != (logit != nullptr) || alpha != (opacity != nullptr)) return GI_ERR_INVALID_ARG;
+        if (!params || !records || !pixbox || !counts) return false;
+        if (!aligned16(params) || !aligned16(records) || !aligned16(pixbox) || !aligned16(counts)) return false;
+        if (alpha != (logit != nullptr) || alpha != (opacity != nullptr)) return false;
     }
+    return true;
+}
+
+bool bin_args_ok(const gi_desc *desc, int64_t n, const uint16_t *pixbox, const uint32_t *counts,
+                 const uint32_t *offsets, const uint32_t *keys, const uint32_t *vals, const uint32_t *ranges,
+                 int64_t capacity, const uint32_t *d_num, const void *workspace, size_t workspace_bytes) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return false;
+    if (!offsets || !ranges || !d_num || !workspace || !aligned256(workspace)) return false;
+    if (n > 0 && (!pixbox || !counts)) return false;
+    if (capacity > 0 && (!keys || !vals)) return false;
+    return workspace_bytes >= gi::make_bin_plan((int)n, desc->width, desc->height, capacity).bytes;
+}
+
+// M back to the host (one wait on the stream) and the overflow status.
+gi_status read_total(const void *workspace, int64_t capacity, int64_t *h_num, hipStream_t s) {
+    unsigned long long total = 0;
+    hipError_t e = hipMemcpyAsync(&total, gi::bin_total_ptr(workspace), sizeof(total), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return GI_ERR_HIP;
+    *h_num = (int64_t)total;
+    return (int64_t)total > capacity ? GI_ERR_CAPACITY : GI_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, const float *logit, float *records,
+                        float *opacity, uint16_t *pixbox, uint32_t *counts, void *stream) {
+    if (!preprocess_args_ok(desc, n, params, logit, records, opacity, pixbox, counts)) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_preprocess((int)n, desc->width, desc->height, params, logit, records, opacity,
-                                            pixbox, counts, as_stream(stream)));
+                                            pixbox, counts, nullptr, nullptr, as_stream(stream)));
 }
 
 size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
@@ -65,26 +96,35 @@ gi_status gi_bin_sort(const gi_desc *desc, int64_t n, const uint16_t *pixbox, co
                       uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
                       int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace, size_t workspace_bytes,
                       void *stream) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31))
+    if (!bin_args_ok(desc, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
+                     workspace_bytes))
         return GI_ERR_INVALID_ARG;
-    if (!offsets || !ranges || !d_num || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
-    if (n > 0 && (!pixbox || !counts)) return GI_ERR_INVALID_ARG;
-    if (capacity > 0 && (!keys || !vals)) return GI_ERR_INVALID_ARG;
     const gi::BinPlan plan = gi::make_bin_plan((int)n, desc->width, desc->height, capacity);
-    if (workspace_bytes < plan.bytes) return GI_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
-    hipError_t e =
-        gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, tile_order, d_num, workspace, s);
+    if (gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, tile_order, d_num, workspace, s) !=
+        hipSuccess)
+        return GI_ERR_HIP;
+    return h_num ? read_total(workspace, capacity, h_num, s) : GI_OK;
+}
+
+gi_status gi_preprocess_bin_sort(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                                 float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
+                                 uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges,
+                                 uint32_t *tile_order, int64_t capacity, uint32_t *d_num, int64_t *h_num,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (!preprocess_args_ok(desc, n, params, logit, records, opacity, pixbox, counts) ||
+        !bin_args_ok(desc, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
+                     workspace_bytes))
+        return GI_ERR_INVALID_ARG;
+    const gi::BinPlan plan = gi::make_bin_plan((int)n, desc->width, desc->height, capacity);
+    hipStream_t s = as_stream(stream);
+    hipError_t e = gi::launch_preprocess((int)n, desc->width, desc->height, params, logit, records, opacity,
+                                         pixbox, counts, gi::bin_group_sums(plan, workspace), ranges, s);
+    if (e == hipSuccess)
+        e = gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, tile_order, d_num, workspace, s,
+                                true);
     if (e != hipSuccess) return GI_ERR_HIP;
-    if (h_num) {
-        unsigned long long total = 0;
-        e = hipMemcpyAsync(&total, gi::bin_total_ptr(workspace), sizeof(total), hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return GI_ERR_HIP;
-        *h_num = (int64_t)total;
-        if ((int64_t)total > capacity) return GI_ERR_CAPACITY;
-    }
-    return GI_OK;
+    return h_num ? read_total(workspace, capacity, h_num, s) : GI_OK;
 }
 
 gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
@@ -132,9 +172,11 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
                         const uint32_t *ranges, const uint32_t *tile_order, const uint32_t *vals, int64_t capacity,
                         const float *background, const float *t_final, const uint32_t *last,
                         const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
+                        const float *loss_partials, int64_t loss_count, float *d_loss,
                         void *workspace, size_t workspace_bytes, void *stream) {
     if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31))
         return GI_ERR_INVALID_ARG;
+    if (d_loss && (desc->mode != GI_MODE_SUM || !loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;
     if (!offsets || !ranges || !vals || !dL_dimage || !workspace || !aligned256(workspace))
         return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
@@ -147,7 +189,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     if (desc->mode == GI_MODE_SUM) {
         if (opacity || logit || background || t_final || last || dlogit || dbackground) return GI_ERR_INVALID_ARG;
         e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, tile_order, vals, capacity, dL_dimage,
-                                      workspace, s);
+                                      workspace, loss_partials, loss_count, d_loss, s);
         if (e == hipSuccess && dparams)
             e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 0, dparams, nullptr,
                                        nullptr, s);

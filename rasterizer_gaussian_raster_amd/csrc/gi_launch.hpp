@@ -8,15 +8,21 @@
 namespace gi {
 
 // k_preprocess.hip
+// group_sums / ranges (or NULL): the binning's group sums and cleared ranges (gi_preprocess_bin_sort).
 hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
-                             float *opacity, uint16_t *pixbox, uint32_t *counts, hipStream_t s);
+                             float *opacity, uint16_t *pixbox, uint32_t *counts, unsigned long long *group_sums,
+                             uint32_t *ranges, hipStream_t s);
 
 // k_binning.hip
 struct BinPlan {
     int n, W, H, tiles_x, ntiles;
     int64_t capacity;
-    int passes;            // LSD passes (>= 1; a single tile takes one 0-bit pass)
+    int order_kind;        // 0: one pass (<= 8 key bits); 1: high digit, then buckets (<= 16); 2: LSD
+    int passes;            // sort passes over all pairs (>= 1; a single tile takes one 0-bit pass)
     int bits[4];           // digit width of each pass
+    int shift0;            // first pass: digit = (key >> shift0) & (2^bits[0] - 1)
+    int lo_bits;           // bucket pass: low digit width (order_kind 1)
+    int bucket_lanes;      // bucket pass: keys per lane per chunk (4, 8 or 16)
     int nb_g;              // Gaussian groups of 256
     int redundant_groups;  // group bases summed by each block (no group-scan kernel)
     int seg_groups, nseg;  // groups per first-pass segment, number of segments
@@ -24,12 +30,15 @@ struct BinPlan {
     int nbs;               // sort blocks of 256 * pass_lanes keys over the capacity (later passes)
     int ncols_cap[4];      // digit-table columns of each pass
     int table_redundant[4];// digit table read raw by every block (no scan kernel)
-    size_t off_part, off_kalt, off_valt, off_table, off_tsp, bytes;
+    size_t off_part, off_kalt, off_valt, off_table, off_tsp, off_bstart, bytes;
 };
 BinPlan make_bin_plan(int n, int W, int H, int64_t capacity);
+// groups_done: the preprocess kernel already wrote the group sums and cleared the ranges.
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
-                           void *ws, hipStream_t s);
+                           void *ws, hipStream_t s, bool groups_done = false);
+// device address of the group sums inside the bin workspace
+unsigned long long *bin_group_sums(const BinPlan &p, void *ws);
 // device address of the 64-bit instance total inside the workspace
 const void *bin_total_ptr(const void *ws);
 
@@ -53,7 +62,7 @@ BwdPlan make_bwd_plan(int W, int H, int64_t capacity);
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
-                                 hipStream_t s);
+                                 const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s);
 // Adds each Gaussian's slots (offsets[g] .. offsets[g+1]) in order to dparams / dlogit, and the
 // per-tile background partials to dbackground.
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,

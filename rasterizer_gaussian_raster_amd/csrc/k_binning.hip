@@ -2,8 +2,8 @@
 //
 // Every Gaussian g covers a rectangle of tiles; its pairs (tile id, g) are
 // numbered in (index, tile row, tile column) order, pair m of g sitting at
-// emission slot offsets[g] + m.  A stable LSD radix sort on the tile id then
-// leaves each tile's list in ascending Gaussian index.
+// emission slot offsets[g] + m.  A stable radix sort on the tile id then leaves
+// each tile's list in ascending Gaussian index.
 //
 //   1. k_group_sums : per 256-Gaussian group, the sum of tile counts (u64);
 //                     clears the tile ranges.
@@ -14,23 +14,31 @@
 //                     histogram of the first digit over the segment's pairs.
 //                     The pairs are never written in emission order: they are
 //                     regenerated from the pixel boxes wherever they are needed
-//                     (a binary search in LDS spreads a group's pairs evenly over
-//                     its 256 lanes, so no lane walks a large Gaussian alone).
+//                     (each thread walks its own Gaussian's tiles; when some
+//                     Gaussian of the segment covers more than 64 tiles, a
+//                     binary search in LDS spreads the pairs over the lanes).
 //   4. k_scatter0   : first sort pass, straight from the regenerated pairs.
-//   5. k_count / k_scatter : further passes over blocks of 1024-4096 keys.
-//   6. k_ranges     : marks where each tile's run starts and ends.
-//   7. k_tile_order : (optional) the tiles by decreasing list length, the order
+//   Then, by the number B of key bits and the size of the pair buffer:
+//     B <= 8         : that pass sorted the whole key; its workgroup 0 writes
+//                      the tile ranges from the digit starts.
+//     B <= 16, small : the first pass took the high digit; k_bucket_sort, one
+//                      workgroup per high digit, sorts its bucket by the low
+//                      digit and writes the bucket's tile ranges from its counts.
+//     otherwise      : LSD -- the first pass took the low digit, k_count /
+//                      k_scatter take the next ones over blocks of 1024-4096
+//                      keys, and k_ranges marks where each run starts and ends.
+//   5. k_tile_order : (optional) the tiles by decreasing list length, the order
 //                     in which the raster kernels should take them: long lists
 //                     first spread the work evenly over the CUs when the whole
 //                     grid is resident at once.
 //
-// Each scatter block ranks up to 4096 keys at a time: every wave takes a
-// contiguous span of the chunk and finds the rank of each key among the equal
-// digits of its span with wave ballots (in key order, hence stable); the chunk
-// is then reordered by digit in LDS and written out in runs, so consecutive
-// lanes store to consecutive addresses.  Digit tables of up to ~20K entries are
-// never scanned by a kernel of their own: each scatter block adds up the
-// entries it needs itself.
+// Each scatter ranks up to 4096 keys at a time: every wave takes a contiguous
+// span of the chunk and finds the rank of each key among the equal digits of
+// its span with wave ballots (in key order, hence stable); the chunk is then
+// reordered by digit in LDS and written out in runs, so consecutive lanes store
+// to consecutive addresses.  Digit tables of up to 32K entries are never
+// scanned by a kernel of their own: each scatter block adds up the entries it
+// needs itself.
 //
 // Binning is the tile-binned scheme of the FlashImgs viewer ("Web viewer":
 // tile-binned compute) with fvdb's 16-pixel tiles (tile_size).  All steps are
@@ -48,6 +56,8 @@ constexpr int kMaxRedundantTable = 32768;      // digit tables up to this are no
 constexpr int64_t kMaxRedundantReads = 8 << 20;// ... when all blocks together read at most this many entries
 constexpr int kScanItems = 16;
 constexpr int kScanChunk = 256 * kScanItems;   // table entries per scan block
+constexpr uint32_t kDirectMax = 64;            // a thread emits its Gaussian's pairs itself up to this many tiles
+constexpr int64_t kMaxBucketCapacity = 1 << 21; // bucket pass for pair buffers up to this (larger: LSD passes)
 
 struct BinHeader {
     unsigned long long total;   // M, 64-bit
@@ -359,7 +369,8 @@ __global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long lo
 // sums before its first group, and all of them for M, itself; block 0
 // publishes M), else the exclusive group bases from k_group_scan.
 __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_groups, int redundant,
-                                                long long capacity, int tiles_x, int bits, int table_redundant,
+                                                long long capacity, int tiles_x, int shift, int bits,
+                                                int table_redundant,
                                                 int ncols_cap, const uint32_t *__restrict__ counts,
                                                 const uint2 *__restrict__ pixbox,
                                                 const unsigned long long *__restrict__ part,
@@ -413,7 +424,16 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
         uint32_t tot;
         const uint32_t local = block_exclusive_scan<uint32_t, kBT>(c, sm, &tot);
         if (gid < n) offsets[gid] = sat32(base + local);
-        if (emit && tot > 0) {                                    // uniform
+        const bool big = __syncthreads_or(c > kDirectMax);
+        if (emit && tot > 0 && !big) {                            // uniform: each thread its own tiles
+            const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
+            const uint32_t wt = ((bx.y & 0xffffu) >> 4) - tx0 + 1;
+            uint32_t row = ty0 * (uint32_t)tiles_x + tx0, col = 0;
+            for (uint32_t k = 0; k < c; ++k) {
+                atomicAdd(&hist[((row + col) >> shift) & dmask], 1u);
+                if (++col == wt) { col = 0; row += (uint32_t)tiles_x; }
+            }
+        } else if (emit && tot > 0) {                             // uniform: pairs spread over the lanes
             G.excl[tid] = local;
             if (tid == 0) G.excl[kBT] = tot;
             G.box[tid] = bx;
@@ -423,7 +443,7 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
                 uint32_t key;
                 int lo;
                 regen_pair<kBT>(G, ns, idx, tiles_x, key, lo);
-                atomicAdd(&hist[key & dmask], 1u);
+                atomicAdd(&hist[(key >> shift) & dmask], 1u);
             }
             __syncthreads();
         }
@@ -440,12 +460,16 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
 // 4: first sort pass from the regenerated pairs (segments of 256 * SG Gaussians)
 // ---------------------------------------------------------------------------
 template <int SG>
-__global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int bits, int table_redundant, int ncols_cap,
-                                                  const uint2 *__restrict__ pixbox,
+// Workgroup 0 also publishes where each digit's run starts (bucket_start[d],
+// d <= radix, the last one M) for the bucket pass, and, when this pass sorts
+// the whole key (ranges != NULL), the tile ranges themselves.
+__global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift, int bits, int table_redundant,
+                                                  int ncols_cap, const uint2 *__restrict__ pixbox,
                                                   const uint32_t *__restrict__ offsets,
                                                   const BinHeader *__restrict__ hdr,
                                                   const uint32_t *__restrict__ table, uint32_t *__restrict__ kout,
-                                                  uint32_t *__restrict__ vout) {
+                                                  uint32_t *__restrict__ vout, uint32_t *__restrict__ bucket_start,
+                                                  uint2 *__restrict__ ranges, int ntiles) {
     constexpr int S = kBT * SG;
     __shared__ SegLds<S> G;
     __shared__ ChunkLds<kPerLane> L;
@@ -454,12 +478,13 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int bits, 
     const int first = blockIdx.x * S;
     const int ns = min(S, n - first);
     // One round of loads: the segment's offsets and boxes, M, the digit table.
-    uint32_t o[SG];
+    uint32_t o[SG], o1[SG];
     uint2 bx[SG];
 #pragma unroll
     for (int r = 0; r < SG; ++r) {
         const int i = r * kBT + tid;
         o[r] = i < ns ? offsets[first + i] : 0u;
+        o1[r] = i < ns ? offsets[first + i + 1] : 0u;
         bx[r] = i < ns ? pixbox[first + i] : make_uint2(0u, 0u);
     }
     const uint32_t o0 = offsets[first];
@@ -476,23 +501,67 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int bits, 
         }
     }
     if (tid == 0) G.excl[ns] = oend - o0;
+    uint32_t cmax = 0;
+#pragma unroll
+    for (int r = 0; r < SG; ++r) cmax = max(cmax, o1[r] - o[r]);
+    const bool big = __syncthreads_or(cmax > kDirectMax);   // else each thread emits its own pairs
     digit_finish(acc, table_redundant, bits, L.gbase, B);   // its barriers publish G
+    if (blockIdx.x == 0) {
+        const int radix = 1 << bits;
+        if (tid < radix) bucket_start[tid] = L.gbase[tid];
+        if (tid == 0) bucket_start[radix] = M;
+        if (ranges && tid < radix && tid < ntiles) {
+            const uint32_t a = L.gbase[tid], e = tid + 1 < radix ? L.gbase[tid + 1] : M;
+            ranges[tid] = e > a ? make_uint2(a, e) : make_uint2(0u, 0u);
+        }
+    }
     const uint32_t tot = oend - o0;
     for (uint32_t cs = 0; cs < tot; cs += kChunk) {
         const int cc = (int)min((uint32_t)kChunk, tot - cs);
         const int span = ((cc + kBT - 1) / kBT) * 64;
         const int iters = span >> 6;
         uint32_t key[kPerLane], val[kPerLane];
+        if (!big) {                                               // uniform
+            // each thread writes its Gaussians' pairs of this chunk into the staging arrays
 #pragma unroll
-        for (int it = 0; it < kPerLane; ++it) {
-            if (it < iters) {                                     // uniform
-                const int idx = wave * span + it * 64 + lane;
-                int lo;
-                regen_pair<S>(G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
-                val[it] = (uint32_t)(first + lo);
+            for (int r = 0; r < SG; ++r) {
+                const int i = r * kBT + tid;
+                if (i >= ns) continue;
+                const uint32_t e0 = o[r] - o0, e1 = o1[r] - o0;
+                const uint32_t lo = max(e0, cs), hi = min(e1, cs + (uint32_t)cc);
+                if (lo >= hi) continue;
+                const uint32_t tx0 = (bx[r].x & 0xffffu) >> 4, ty0 = (bx[r].x >> 16) >> 4;
+                const uint32_t wt = ((bx[r].y & 0xffffu) >> 4) - tx0 + 1;
+                uint32_t q = (lo - e0) / wt, col = (lo - e0) - q * wt;
+                uint32_t row = (ty0 + q) * (uint32_t)tiles_x + tx0;
+                for (uint32_t x = lo; x < hi; ++x) {
+                    L.sk[x - cs] = row + col;
+                    L.sv[x - cs] = (uint32_t)(first + i);
+                    if (++col == wt) { col = 0; row += (uint32_t)tiles_x; }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kPerLane; ++it) {
+                if (it < iters) {                                 // uniform
+                    const int idx = wave * span + it * 64 + lane;
+                    const int q = idx < cc ? idx : cc - 1;
+                    key[it] = L.sk[q];
+                    val[it] = L.sv[q];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < kPerLane; ++it) {
+                if (it < iters) {                                 // uniform
+                    const int idx = wave * span + it * 64 + lane;
+                    int lo;
+                    regen_pair<S>(G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
+                    val[it] = (uint32_t)(first + lo);
+                }
             }
         }
-        scatter_chunk(L, cc, span, 0, bits, key, val, kout, vout, M);
+        scatter_chunk(L, cc, span, shift, bits, key, val, kout, vout, M);
     }
 }
 
@@ -558,6 +627,67 @@ __global__ __launch_bounds__(kBT) void k_scatter(const uint32_t *__restrict__ ki
 }
 
 // ---------------------------------------------------------------------------
+// 5': second pass of the most-significant-digit order (keys up to 16 bits)
+// ---------------------------------------------------------------------------
+// One workgroup per bucket (pairs whose tile ids share the high digit, in
+// emission order after the first pass): it counts the low digits, writes the
+// ranges of the bucket's 2^lo tiles straight from those counts, and scatters
+// the bucket stably by the low digit, 256 * PL pairs at a time.
+template <int PL>
+__global__ __launch_bounds__(kBT) void k_bucket_sort(const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin,
+                                                     uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                                     const BinHeader *__restrict__ hdr,
+                                                     const uint32_t *__restrict__ bucket_start, int lo_bits,
+                                                     int ntiles, uint2 *__restrict__ ranges) {
+    constexpr int CH = kBT * PL;
+    __shared__ ChunkLds<PL> L;
+    __shared__ uint32_t hist[256];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << lo_bits;
+    const uint32_t M = hdr->m_eff;
+    const uint32_t s0 = M ? bucket_start[blockIdx.x] : 0u, s1 = M ? bucket_start[blockIdx.x + 1] : 0u;
+    if (tid < radix) hist[tid] = 0u;
+    __syncthreads();
+    for (uint32_t base = s0; base < s1; base += CH) {            // uniform
+        uint32_t k[PL];
+#pragma unroll
+        for (int it = 0; it < PL; ++it) {
+            const uint32_t idx = base + it * kBT + tid;
+            k[it] = kin[idx < s1 ? idx : s1 - 1];
+        }
+#pragma unroll
+        for (int it = 0; it < PL; ++it)
+            if (base + it * kBT + tid < s1) atomicAdd(&hist[k[it] & (uint32_t)(radix - 1)], 1u);
+    }
+    __syncthreads();
+    const uint32_t c = tid < radix ? hist[tid] : 0u;
+    uint32_t all;
+    const uint32_t ex = block_exclusive_scan<uint32_t, kBT>(c, L.sm, &all);
+    if (tid < radix) {
+        const int t = (blockIdx.x << lo_bits) + tid;
+        if (t < ntiles) ranges[t] = c ? make_uint2(s0 + ex, s0 + ex + c) : make_uint2(0u, 0u);
+        L.gbase[tid] = s0 + ex;
+    }
+    __syncthreads();
+    for (uint32_t base = s0; base < s1; base += CH) {            // uniform
+        const int cc = (int)min((uint32_t)CH, s1 - base);
+        const int span = ((cc + kBT - 1) / kBT) * 64;
+        const int iters = span >> 6;
+        uint32_t key[PL], val[PL];
+#pragma unroll
+        for (int it = 0; it < PL; ++it) {
+            if (it < iters) {
+                const int idx = wave * span + it * 64 + lane;
+                const uint32_t q = base + (uint32_t)(idx < cc ? idx : cc - 1);
+                key[it] = kin[q];
+                val[it] = vin[q];
+            }
+        }
+        scatter_chunk(L, cc, span, 0, lo_bits, key, val, kout, vout, M);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // exclusive scan of a u32 array in place (large digit tables): one workgroup
 // when it is short, otherwise reduce -> scan of block sums -> rescan.
 // count <= 1024 * kScanSingleItems for the single form.  Element r * 1024 + i
@@ -577,9 +707,10 @@ __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, 
     }
 #pragma unroll
     for (int r = 0; r < kScanSingleItems; ++r) {
-        if (r >= rows) break;
-        inc[r] = wave_scan_incl(v[r]);
-        if (lane == 63) wsum[wave][r] = inc[r];
+        if (r < rows) {                   // uniform over the block
+            inc[r] = wave_scan_incl(v[r]);
+            if (lane == 63) wsum[wave][r] = inc[r];
+        }
     }
     __syncthreads();
     if (tid < rows) {                     // one thread per row: exclusive over waves, row total
@@ -600,9 +731,8 @@ __global__ __launch_bounds__(1024) void k_scan_single(uint32_t *__restrict__ a, 
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kScanSingleItems; ++r) {
-        if (r >= rows) break;
         const int e = r * 1024 + tid;
-        if (e < count) a[e] = rowpre[r] + wsum[wave][r] + inc[r] - v[r];
+        if (r < rows && e < count) a[e] = rowpre[r] + wsum[wave][r] + inc[r] - v[r];
     }
 }
 
@@ -727,18 +857,43 @@ BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
     p.capacity = capacity;
     int B = 0;
     while ((1ll << B) < (long long)p.ntiles) ++B;          // key bits: ids in [0, ntiles)
-    p.passes = B == 0 ? 1 : (B + 7) / 8;                    // a single tile still takes one (copying) pass
-    for (int i = 0; i < 4; ++i) p.bits[i] = 0;
-    {
-        const int w = (B + p.passes - 1) / p.passes;
-        int left = B;
-        for (int i = 0; i < p.passes; ++i) { p.bits[i] = left < w ? left : w; left -= p.bits[i]; }
-    }
     p.nb_g = (n + 255) / 256;
     p.redundant_groups = p.nb_g > 0 && p.nb_g <= kMaxRedundantGroups;
     p.seg_groups = p.nb_g <= kMaxRedundantGroups ? 1 : 4;
     p.nseg = (p.nb_g + p.seg_groups - 1) / p.seg_groups;
-    // later passes: smaller blocks when the pair buffer is small, so the launch still fills the chip
+    auto redundant_ok = [&](int bits, int cols) {
+        const size_t entries = ((size_t)1 << bits) * (size_t)(cols > 0 ? cols : 1);
+        return bits >= 2 && entries <= (size_t)kMaxRedundantTable && (int64_t)entries * cols <= kMaxRedundantReads;
+    };
+    for (int i = 0; i < 4; ++i) p.bits[i] = 0;
+    p.shift0 = 0;
+    p.lo_bits = 0;
+    if (B <= 8) {                            // one pass sorts the whole key
+        p.order_kind = 0;
+        p.passes = 1;
+        p.bits[0] = B;
+    } else if (B <= 16 && capacity <= kMaxBucketCapacity) {   // high digit first, then a workgroup per bucket
+        p.order_kind = 1;
+        p.passes = 1;
+        const int lo_min = B - 8 > 1 ? B - 8 : 1;          // high digit <= 8 bits, low digit >= 1 bit
+        int hi = B - 3 < 8 ? B - 3 : 8;
+        if (hi < lo_min) hi = lo_min;
+        // fewer buckets if that lets the first pass skip its scan kernels
+        for (int h = hi; h >= lo_min && !redundant_ok(hi, p.nseg); --h)
+            if (redundant_ok(h, p.nseg)) hi = h;
+        p.bits[0] = hi;
+        p.lo_bits = B - hi;
+        p.shift0 = p.lo_bits;
+        const int64_t per_bucket = capacity / 2 / ((int64_t)1 << hi);      // capacity holds ~2x slack
+        p.bucket_lanes = per_bucket <= 1024 ? 4 : per_bucket <= 2048 ? 8 : 16;
+    } else {                                 // LSD passes of <= 8 bits
+        p.order_kind = 2;
+        p.passes = (B + 7) / 8;
+        const int w = (B + p.passes - 1) / p.passes;
+        int left = B;
+        for (int i = 0; i < p.passes; ++i) { p.bits[i] = left < w ? left : w; left -= p.bits[i]; }
+    }
+    // later LSD passes: smaller blocks when the pair buffer is small, so the launch still fills the chip
     p.pass_lanes = capacity <= (1ll << 19) ? 4 : capacity <= (1ll << 22) ? 8 : 16;
     const int64_t chunk = (int64_t)kBT * p.pass_lanes;
     p.nbs = (int)((capacity + chunk - 1) / chunk);
@@ -747,8 +902,7 @@ BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
         const int cols = i == 0 ? p.nseg : p.nbs;
         p.ncols_cap[i] = cols;
         const size_t entries = ((size_t)1 << p.bits[i]) * (size_t)(cols > 0 ? cols : 1);
-        p.table_redundant[i] = p.bits[i] >= 2 && entries <= (size_t)kMaxRedundantTable &&
-                               (int64_t)entries * cols <= kMaxRedundantReads;
+        p.table_redundant[i] = redundant_ok(p.bits[i], cols);
         if (entries > table) table = entries;
     }
     size_t off = align256(sizeof(BinHeader));
@@ -757,15 +911,20 @@ BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
     p.off_valt = off; off = align256(off + sizeof(uint32_t) * (size_t)(capacity > 0 ? capacity : 1));
     p.off_table = off; off = align256(off + sizeof(uint32_t) * table);
     p.off_tsp = off; off = align256(off + sizeof(uint32_t) * ((table + kScanChunk - 1) / kScanChunk + 1));
+    p.off_bstart = off; off = align256(off + sizeof(uint32_t) * 260);
     p.bytes = off;
     return p;
 }
 
 const void *bin_total_ptr(const void *ws) { return &static_cast<const BinHeader *>(ws)->total; }
 
+unsigned long long *bin_group_sums(const BinPlan &p, void *ws) {
+    return reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + p.off_part);
+}
+
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
-                           void *ws, hipStream_t s) {
+                           void *ws, hipStream_t s, bool groups_done) {
     char *w = static_cast<char *>(ws);
     BinHeader *hdr = reinterpret_cast<BinHeader *>(w);
     unsigned long long *part = reinterpret_cast<unsigned long long *>(w + p.off_part);
@@ -773,40 +932,64 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     uint32_t *valt = reinterpret_cast<uint32_t *>(w + p.off_valt);
     uint32_t *table = reinterpret_cast<uint32_t *>(w + p.off_table);
     uint32_t *tsp = reinterpret_cast<uint32_t *>(w + p.off_tsp);
+    uint32_t *bstart = reinterpret_cast<uint32_t *>(w + p.off_bstart);
     const uint2 *box = reinterpret_cast<const uint2 *>(pixbox);
-    // ranges, then the tile order when one is asked for (also for n == 0 or capacity == 0)
+    uint2 *rg = reinterpret_cast<uint2 *>(ranges);
+    const bool lsd = p.order_kind == 2;
+    // the tile order when one is asked for (also for n == 0 or capacity == 0)
     auto finish = [&]() -> hipError_t {
-        if (p.capacity > 0)
-            k_ranges<<<(unsigned)((p.capacity + 1023) / 1024), 256, 0, s>>>(keys, hdr, (uint32_t)p.ntiles, ranges);
         if (tile_order)
-            k_tile_order<<<1, 1024, 0, s>>>(reinterpret_cast<const uint2 *>(ranges), p.ntiles, tile_order);
+            k_tile_order<<<1, 1024, 0, s>>>(rg, p.ntiles, tile_order);
         return hipGetLastError();
     };
 
-    k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, part, p.ntiles,
-                                                         reinterpret_cast<uint2 *>(ranges), hdr, offsets, d_num);
+    if (!groups_done || p.n == 0)
+        k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, part, p.ntiles, rg, hdr, offsets, d_num);
     if (p.n == 0) return finish();
     if (!p.redundant_groups)
         k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
     k_count0<<<p.nseg, kBT, 0, s>>>(p.n, p.nb_g, p.seg_groups, p.redundant_groups, (long long)p.capacity,
-                                    p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], counts, box, part,
-                                    hdr, offsets, d_num, table);
+                                    p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0], counts,
+                                    box, part, hdr, offsets, d_num, table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.capacity == 0) return finish();
-    // pass i writes keys/vals when an even number of passes follow it
-    auto dst_k = [&](int i) { return ((p.passes - 1 - i) & 1) ? kalt : keys; };
-    auto dst_v = [&](int i) { return ((p.passes - 1 - i) & 1) ? valt : vals; };
     if (!p.table_redundant[0]) {
         e = scan_u32(table, (1 << p.bits[0]) * p.ncols_cap[0], tsp, s);
         if (e != hipSuccess) return e;
     }
+    // destination of the first pass: the final arrays unless another pass follows
+    uint32_t *k0 = keys, *v0 = vals;
+    if (p.order_kind == 1 || (lsd && (p.passes & 1) == 0)) { k0 = kalt; v0 = valt; }
+    uint2 *rg0 = p.order_kind == 0 ? rg : nullptr;
     if (p.seg_groups == 1)
-        k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box,
-                                             offsets, hdr, table, dst_k(0), dst_v(0));
+        k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
+                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
+                                             p.ntiles);
+    else if (p.seg_groups == 2)
+        k_scatter0<2><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
+                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
+                                             p.ntiles);
     else
-        k_scatter0<4><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box,
-                                             offsets, hdr, table, dst_k(0), dst_v(0));
+        k_scatter0<4><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
+                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
+                                             p.ntiles);
+    if (p.order_kind == 1) {
+        const int nbk = 1 << p.bits[0];
+        if (p.bucket_lanes == 4)
+            k_bucket_sort<4><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
+        else if (p.bucket_lanes == 8)
+            k_bucket_sort<8><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
+        else
+            k_bucket_sort<16><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return finish();
+    }
+    if (p.order_kind == 0) return finish();
+    // LSD: further passes, then the ranges
+    auto dst_k = [&](int i) { return ((p.passes - 1 - i) & 1) ? kalt : keys; };
+    auto dst_v = [&](int i) { return ((p.passes - 1 - i) & 1) ? valt : vals; };
     int shift = p.bits[0];
     for (int i = 1; i < p.passes; ++i) {
         const uint32_t *sk = dst_k(i - 1), *sv = dst_v(i - 1);
@@ -826,6 +1009,9 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
             k_scatter<16><<<p.nbs, kBT, 0, s>>>(sk, sv, dst_k(i), dst_v(i), hdr, shift, b, tr, nc, table);
         shift += p.bits[i];
     }
+    k_ranges<<<(unsigned)((p.capacity + 1023) / 1024), 256, 0, s>>>(keys, hdr, (uint32_t)p.ntiles, ranges);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     return finish();
 }
 

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
 }
 
 // Sum of the per-tile partials in a fixed order, divided by the entry count.
-__global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__restrict__ part, double inv_count,
-                                                     float *__restrict__ loss) {
+__device__ __forceinline__ void loss_reduce_block(int nparts, const float *__restrict__ part, double inv_count,
+                                                  float *__restrict__ loss) {
     __shared__ double sm[256];
     double s = 0.0;
     for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
@@ -146,6 +146,11 @@ __global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__
         __syncthreads();
     }
     if (threadIdx.x == 0) *loss = (float)(sm[0] * inv_count);
+}
+
+__global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__restrict__ part, double inv_count,
+                                                     float *__restrict__ loss) {
+    loss_reduce_block(nparts, part, inv_count, loss);
 }
 
 // Backward work item: one (list entry, 4x4 pixel block) pair per thread.  Items
@@ -167,7 +172,13 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                                                         const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
                                                         const uint32_t *__restrict__ vals, uint32_t capacity,
                                                         const float *__restrict__ dL,
-                                                        float4 *__restrict__ part) {
+                                                        float4 *__restrict__ part,
+                                                        const float *__restrict__ loss_part, int nparts,
+                                                        double inv_count, float *__restrict__ loss) {
+    if (loss && blockIdx.x == gridDim.x - 1) {          // the spare last workgroup: the forward's loss
+        loss_reduce_block(nparts, loss_part, inv_count, loss);
+        return;
+    }
     __shared__ float4 gp[16 * kGpStride];               // dL/dI of the tile's pixels, block by block
     __shared__ float4 entp[4][kWaveEnt], entq[4][kWaveEnt];   // per wave: its staged entries (p, q)
     __shared__ uint16_t items[4][kWaveEnt * 16];        // per wave: entry | block << 8, entry-major
@@ -499,13 +510,17 @@ hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, 
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
-                                 hipStream_t s) {
+                                 const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const BwdPlan p = make_bwd_plan(W, H, capacity);
-    k_render_sum_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(
+    // with d_loss, 8 more workgroups: the last one (no tile under either tile map) reduces the loss
+    const int nb = padded_tiles(ntiles) + (d_loss ? 8 : 0);
+    const double inv_count = loss_count > 0 ? 1.0 / (double)loss_count : 0.0;
+    k_render_sum_bwd<<<nb, 256, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
         offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, dL_dimage,
-        reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part));
+        reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part), loss_partials, ntiles, inv_count,
+        d_loss);
     return hipGetLastError();
 }
 

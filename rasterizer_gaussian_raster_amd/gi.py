@@ -54,9 +54,10 @@ def load():
         "gi_preprocess": ([D, i64, P, P, P, P, P, P, P], i32),
         "gi_bin_sort_workspace_bytes": ([D, i64, i64], sz),
         "gi_bin_sort": ([D, i64, P, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
+        "gi_preprocess_bin_sort": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gi_render_fwd": ([D, i64, P, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_render_bwd_workspace_bytes": ([D, i64, i64], sz),
-        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P, P, sz, P], i32),
+        "gi_render_bwd": ([D, i64, P, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P, P, i64, P, P, sz, P], i32),
         "gi_loss_workspace_bytes": ([i64], sz),
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
@@ -135,6 +136,19 @@ def gi_bin_sort(d, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_n
     return int(h.value) if sync_count else None
 
 
+def gi_preprocess_bin_sort(d, n, params, logit, records, opacity, pixbox, counts, offsets, keys, vals, ranges,
+                           capacity, d_num, workspace, sync_count=False, stream=None, tile_order=None):
+    """gi_preprocess then gi_bin_sort in one call; returns as gi_bin_sort."""
+    h = ctypes.c_int64(-1)
+    st = load().gi_preprocess_bin_sort(ctypes.byref(d), int(n), _ptr(params), _ptr(logit), _ptr(records),
+                                       _ptr(opacity), _ptr(pixbox), _ptr(counts), _ptr(offsets), _ptr(keys),
+                                       _ptr(vals), _ptr(ranges), _ptr(tile_order), int(capacity), _ptr(d_num),
+                                       ctypes.byref(h) if sync_count else None, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gi_preprocess_bin_sort")
+    return int(h.value) if sync_count else None
+
+
 def gi_render_fwd(d, n, records, opacity, pixbox, ranges, vals, background, image, t_final, last, stream=None,
                   tile_order=None):
     _check(load().gi_render_fwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(pixbox),
@@ -147,13 +161,16 @@ def gi_render_bwd_workspace_bytes(d, n, capacity) -> int:
 
 
 def gi_render_bwd(d, n, records, opacity, logit, pixbox, offsets, ranges, vals, capacity, background, t_final,
-                  last, dL_dimage, dparams, dlogit, dbackground, workspace, stream=None, tile_order=None):
+                  last, dL_dimage, dparams, dlogit, dbackground, workspace, stream=None, tile_order=None,
+                  loss_partials=None, loss_count=0, d_loss=None):
+    """Sum mode: with d_loss, also reduces the forward's loss partials into d_loss (as gi_loss_reduce)."""
     _check(load().gi_render_bwd(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(logit),
                                 _ptr(pixbox), _ptr(offsets), _ptr(ranges), _ptr(tile_order), _ptr(vals),
                                 int(capacity),
                                 _ptr(background), _ptr(t_final), _ptr(last), _ptr(dL_dimage), _ptr(dparams),
-                                _ptr(dlogit), _ptr(dbackground), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)), "gi_render_bwd")
+                                _ptr(dlogit), _ptr(dbackground), _ptr(loss_partials), int(loss_count),
+                                _ptr(d_loss), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "gi_render_bwd")
 
 
 def gi_loss_workspace_bytes(count) -> int:

@@ -3,9 +3,10 @@
 Torch provides device memory and the stream; every step below is one call of
 the C ABI (through :mod:`.gi`):
 
-  render : gi_preprocess -> gi_bin_sort -> gi_render_fwd
-  fit (sum mode)   : gi_preprocess -> gi_bin_sort -> gi_render_fwd_l2 -> gi_loss_reduce
-                     -> gi_render_bwd (pair gradients left in its workspace) -> gi_adam_step_pairs
+  render : gi_preprocess_bin_sort (gi_preprocess + gi_bin_sort in one call) -> gi_render_fwd
+  fit (sum mode)   : gi_preprocess_bin_sort -> gi_render_fwd_l2
+                     -> gi_render_bwd (pair gradients left in its workspace; loss reduced in a spare
+                        workgroup) -> gi_adam_step_pairs
   fit (alpha mode) : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
 
 Fitter.capture() records the sum-mode step as HIP graphs (torch.cuda.CUDAGraph over the same
@@ -81,9 +82,20 @@ class Raster:
         gi.gi_preprocess(self.desc, self.n, params, logit, self.records, self.opacity, self.pixbox, self.counts,
                          stream)
 
-    def bin(self, sync=False, slack=1.25, stream=None, order=None):
+    def _bin_call(self, sync, stream, tile_order, params, logit):
+        if params is None:
+            return gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
+                                  self.ranges, self.capacity, self.d_num, self.ws, sync_count=sync, stream=stream,
+                                  tile_order=tile_order)
+        return gi.gi_preprocess_bin_sort(self.desc, self.n, params, logit, self.records, self.opacity, self.pixbox,
+                                         self.counts, self.offsets, self.keys, self.vals, self.ranges,
+                                         self.capacity, self.d_num, self.ws, sync_count=sync, stream=stream,
+                                         tile_order=tile_order)
+
+    def bin(self, sync=False, slack=1.25, stream=None, order=None, params=None, logit=None):
         """Bin and sort.  sync: read M back (one host wait) and grow the buffers if needed.
-        order: also (re)write the tile order; default: only when none has been written yet."""
+        order: also (re)write the tile order; default: only when none has been written yet.
+        params (and logit in alpha mode): preprocess them first, in the same call."""
         if order is None:
             order = not self.has_order
         tile_order = self.order if order else None
@@ -93,22 +105,16 @@ class Raster:
             self.set_capacity(max(1024, 4 * self.n))
             sync = True
         if not sync:
-            gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
-                           self.ranges, self.capacity, self.d_num, self.ws, sync_count=False, stream=stream,
-                           tile_order=tile_order)
+            self._bin_call(False, stream, tile_order, params, logit)
             return None
         try:
-            M = gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
-                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream,
-                               tile_order=tile_order)
+            M = self._bin_call(True, stream, tile_order, params, logit)
         except gi.GiError as e:
             if e.status != gi.GI_ERR_CAPACITY:
                 raise
             M = int(self.d_num.cpu().view(torch.int32).item()) & 0xFFFFFFFF
             self.set_capacity(int(M * slack) + 1024)
-            M = gi.gi_bin_sort(self.desc, self.n, self.pixbox, self.counts, self.offsets, self.keys, self.vals,
-                               self.ranges, self.capacity, self.d_num, self.ws, sync_count=True, stream=stream,
-                               tile_order=tile_order)
+            M = self._bin_call(True, stream, tile_order, None, None)     # preprocess outputs are in place
         self.M = M
         return M
 
@@ -123,18 +129,20 @@ class Raster:
         return self.image
 
     def backward(self, dL_dimage, dparams, logit=None, background=None, dlogit=None, dbackground=None,
-                 stream=None):
-        """dparams=None (sum mode): leave the per-pair gradients in the workspace for adam_pairs."""
+                 stream=None, d_loss=None):
+        """dparams=None (sum mode): leave the per-pair gradients in the workspace for adam_pairs.
+        d_loss (sum mode, after forward_l2): also reduce the loss partials into it, in the same launch."""
         if self.bwd_ws is None:
             nbytes = gi.gi_render_bwd_workspace_bytes(self.desc, self.n, self.capacity)
             self.bwd_ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device(self.device))
         gi.gi_render_bwd(self.desc, self.n, self.records, self.opacity, logit, self.pixbox, self.offsets,
                          self.ranges, self.vals, self.capacity, background, self.t_final, self.last, dL_dimage,
-                         dparams, dlogit, dbackground, self.bwd_ws, stream, tile_order=self._order())
+                         dparams, dlogit, dbackground, self.bwd_ws, stream, tile_order=self._order(),
+                         loss_partials=self.loss_partials if d_loss is not None else None,
+                         loss_count=3 * self.W * self.H, d_loss=d_loss)
 
     def render(self, params, logit=None, background=None, sync=True):
-        self.preprocess(params, logit)
-        self.bin(sync=sync)
+        self.bin(sync=sync, params=params, logit=logit)
         return self.forward(background)
 
 
@@ -192,14 +200,12 @@ class Fitter:
     def _sum_step(self, order, ev=(None,) * 4, d_step=None):
         """The sum-mode step's calls.  d_step: device step counter, advanced here (graph mode)."""
         r = self.raster
-        r.preprocess(self.params)
-        r.bin(sync=False, order=order)
+        r.bin(sync=False, order=order, params=self.params)
         ev[0] is not None and ev[0].record()
         r.forward_l2(self.target, self.dL)
         ev[1] is not None and ev[1].record()
-        gi.gi_loss_reduce(r.T, r.loss_partials, self.target.numel(), self.loss)
         ev[2] is not None and ev[2].record()
-        r.backward(self.dL, None)
+        r.backward(self.dL, None, d_loss=self.loss)            # the loss is reduced in the same launch
         ev[3] is not None and ev[3].record()
         if d_step is not None:
             d_step.add_(1)
@@ -244,8 +250,7 @@ class Fitter:
             self.step_count += 1
             return
         bg = self.bg4
-        r.preprocess(self.params, self.logit)
-        r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0)
+        r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.params, logit=self.logit)
         r.forward(bg)
         gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
         r.backward(self.dL, self.grad, logit=self.logit, background=bg, dlogit=self.g_logit,

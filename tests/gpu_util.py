@@ -36,14 +36,19 @@ def u16(t):
     return t.detach().cpu().numpy().view(np.uint16)
 
 
-def gpu_bin(W, H, params, logit=None, capacity=None):
+def gpu_bin(W, H, params, logit=None, capacity=None, fused=False):
+    """Preprocess and bin on the GPU: two calls, or gi_preprocess_bin_sort when fused."""
     from rasterizer_gaussian_raster_amd import gi
     from rasterizer_gaussian_raster_amd.pipeline import Raster
     n = params.shape[0]
     mode = gi.MODE_ALPHA if logit is not None else gi.MODE_SUM
     r = Raster(W, H, n, mode, capacity=capacity)
-    r.preprocess(dev(params), None if logit is None else dev(logit))
-    M = r.bin(sync=True)
+    P, L = dev(params), None if logit is None else dev(logit)
+    if fused:
+        M = r.bin(sync=True, params=P, logit=L)
+    else:
+        r.preprocess(P, L)
+        M = r.bin(sync=True)
     torch.cuda.synchronize()
     return r, {
         "M": M,

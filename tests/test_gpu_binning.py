@@ -10,12 +10,12 @@ from rasterizer_gaussian_raster_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def _check_bin(W, H, params, logit=None):
+def _check_bin(W, H, params, logit=None, fused=False):
     import oracle
     ref = oracle.bin(W, H, params.astype(np.float64), None if logit is None else logit.astype(np.float64))
     box, _ = oracle.footprint(W, H, params.astype(np.float64),
                               None if logit is None else logit.astype(np.float64))
-    _, got = gpu_bin(W, H, params, logit)
+    _, got = gpu_bin(W, H, params, logit, fused=fused)
     assert got["M"] == ref["M"]
     np.testing.assert_array_equal(got["counts"], ref["counts"])
     nz = ref["counts"] > 0
@@ -35,10 +35,11 @@ def _check_bin(W, H, params, logit=None):
     (105, 1, 1, 10, (0.3, 2.0), 2),
     (106, 257, 129, 2000, (0.3, 40.0), 50),
 ])
-def test_bin_random_cases(seed, W, H, n, sig, margin):
+@pytest.mark.parametrize("fused", [False, True])
+def test_bin_random_cases(seed, W, H, n, sig, margin, fused):
     require_gpu()
     p = synth.random_case(seed, W, H, n, sigma=sig, margin=margin)
-    _check_bin(W, H, p)
+    _check_bin(W, H, p, fused=fused)
 
 
 @pytest.mark.parametrize("name", ["tiny_fit_64x64", "kodak_768x512_50k", "div2k_1020x678_70k"])
@@ -94,16 +95,16 @@ def test_bin_large_workloads(name):
     _check_bin(W, H, p[sub], None if lg is None else lg[sub])
 
 
-def test_bin_edge_cases():
+@pytest.mark.parametrize("fused", [False, True])
+def test_bin_edge_cases(fused):
     require_gpu()
-    rng = np.random.default_rng(0)
     W, H = 70, 45
     # empty set
-    _check_bin(W, H, np.zeros((0, 8), np.float32))
+    _check_bin(W, H, np.zeros((0, 8), np.float32), fused=fused)
     # all off-image
     p = synth.random_case(1, W, H, 50)
     p[:, 0] += 1000
-    got = _check_bin(W, H, p)
+    got = _check_bin(W, H, p, fused=fused)
     assert got["M"] == 0 and np.all(got["ranges"] == 0)
     # tiny Gaussians between pixel centres, huge Gaussians covering every tile, culled parameters
     p = synth.random_case(2, W, H, 40)
@@ -117,7 +118,7 @@ def test_bin_edge_cases():
     p[17, 4] = 0.0
     p[18, 6] = np.inf
     p[19, 4] = 1e-39
-    got = _check_bin(W, H, p)
+    got = _check_bin(W, H, p, fused=fused)
     assert np.all(got["counts"][15:20] == 0)
     assert np.all(got["counts"][10:15] == (-(-W // 16)) * (-(-H // 16)))
 

@@ -1,0 +1,143 @@
+"""The fused entry points must give exactly what the separate calls give:
+gi_preprocess_bin_sort == gi_preprocess then gi_bin_sort (every output, bit for bit), and the loss
+reduced in the backward launch (d_loss) == gi_loss_reduce, with unchanged gradients."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, require_gpu, u32
+from rasterizer_gaussian_raster_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _outputs(r, M):
+    out = {"records": u32(r.records)[: r.n], "pixbox": r.pixbox.cpu().numpy()[: r.n],
+           "counts": u32(r.counts)[: r.n], "offsets": u32(r.offsets), "keys": u32(r.keys)[:M],
+           "vals": u32(r.vals)[:M], "ranges": u32(r.ranges)[: r.T], "d_num": u32(r.d_num)}
+    if r.opacity is not None:
+        out["opacity"] = u32(r.opacity)[: r.n]
+    if r.order is not None:
+        out["order_len"] = np.minimum(np.diff(out["ranges"].astype(np.int64), axis=1)[:, 0], 1023)[
+            u32(r.order)[: r.T].astype(np.int64)]
+    return out
+
+
+def _case(name):
+    if name == "kodak_768x512_50k" or name == "render_3840x2160_2m":
+        w = synth.make_workload(name)
+        return w["workload"].width, w["workload"].height, w["params"], w["logit"]
+    if name == "alpha_300x200":
+        p, lg, _ = synth.random_case(51, 300, 200, 4000, sigma=(0.5, 16.0), alpha=True)
+        return 300, 200, p, lg
+    if name == "empty":
+        return 70, 45, np.zeros((0, 8), np.float32), None
+    if name == "off_image":
+        p = synth.random_case(52, 70, 45, 50)
+        p[:, 0] += 1000
+        return 70, 45, p, None
+    if name == "large_boxes":
+        return 640, 600, synth.random_case(11, 640, 600, 700, sigma=(20.0, 150.0), margin=100), None
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["kodak_768x512_50k", "alpha_300x200", "empty", "off_image", "large_boxes",
+                                  "render_3840x2160_2m"])
+def test_preprocess_bin_sort_equals_two_calls(name):
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    W, H, p, lg = _case(name)
+    n = p.shape[0]
+    mode = gi.MODE_ALPHA if lg is not None else gi.MODE_SUM
+    P, L = dev(p), None if lg is None else dev(lg)
+    outs = []
+    for fused in (False, True):
+        r = Raster(W, H, n, mode)
+        if fused:
+            M = r.bin(sync=True, params=P, logit=L)
+        else:
+            r.preprocess(P, L)
+            M = r.bin(sync=True)
+        # a second, asynchronous pass over the same buffers (stale contents in ranges and workspace)
+        if fused:
+            r.bin(sync=False, order=True, params=P, logit=L)
+        else:
+            r.preprocess(P, L)
+            r.bin(sync=False, order=True)
+        torch.cuda.synchronize()
+        outs.append(_outputs(r, M))
+    a, b = outs
+    assert a.keys() == b.keys()
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_fused_capacity_overflow_reports_like_bin_sort():
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    W, H = 128, 96
+    p = dev(synth.random_case(5, W, H, 400, sigma=(1, 10)))
+    r = Raster(W, H, 400)
+    M = r.bin(sync=True, params=p)
+    r2 = Raster(W, H, 400, capacity=M - 1)
+    with pytest.raises(gi.GiError) as ei:
+        gi.gi_preprocess_bin_sort(r2.desc, r2.n, p, None, r2.records, None, r2.pixbox, r2.counts, r2.offsets,
+                                  r2.keys, r2.vals, r2.ranges, r2.capacity, r2.d_num, r2.ws, sync_count=True)
+    assert ei.value.status == gi.GI_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert int(u32(r2.d_num)[0]) == M and np.all(u32(r2.ranges) == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny_fit_64x64", "kodak_768x512_50k", "div2k_1020x678_70k"])
+def test_backward_loss_equals_loss_reduce(name):
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    w = synth.make_workload(name)
+    wl = w["workload"]
+    W, H, n = wl.width, wl.height, wl.n
+    r = Raster(W, H, n)
+    P, T = dev(w["params"]), dev(w["target"])
+    r.render(P)
+    dL = torch.empty_like(T)
+    r.forward_l2(T, dL)
+    ref = torch.full((1,), -1.0, device="cuda")
+    gi.gi_loss_reduce(r.T, r.loss_partials, T.numel(), ref)
+    d0 = torch.zeros_like(P)
+    r.backward(dL, d0)
+    g0 = r.bwd_ws.clone()
+    d1 = torch.zeros_like(P)
+    got = torch.full((1,), -2.0, device="cuda")
+    r.backward(dL, d1, d_loss=got)
+    g1 = r.bwd_ws.clone()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u32(got), u32(ref))
+    np.testing.assert_array_equal(u32(d1), u32(d0))
+    np.testing.assert_array_equal(g1.cpu().numpy(), g0.cpu().numpy())
+    # pair-gradient form (dparams NULL), as the fit step calls it
+    got2 = torch.full((1,), -3.0, device="cuda")
+    r.backward(dL, None, d_loss=got2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u32(got2), u32(ref))
+
+
+def test_backward_loss_argument_checks():
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    W, H = 64, 48
+    p = dev(synth.random_case(7, W, H, 100))
+    r = Raster(W, H, 100)
+    r.render(p)
+    G = torch.zeros((3, H, W), device="cuda")
+    loss = torch.zeros(1, device="cuda")
+    r.backward(G, None)                 # sizes the workspace
+    with pytest.raises(gi.GiError):     # d_loss without the partials
+        gi.gi_render_bwd(r.desc, r.n, r.records, None, None, r.pixbox, r.offsets, r.ranges, r.vals, r.capacity,
+                         None, None, None, G, None, None, None, r.bwd_ws, d_loss=loss)
+    with pytest.raises(gi.GiError):     # count < 1
+        gi.gi_render_bwd(r.desc, r.n, r.records, None, None, r.pixbox, r.offsets, r.ranges, r.vals, r.capacity,
+                         None, None, None, G, None, None, None, r.bwd_ws, loss_partials=r.loss_partials,
+                         loss_count=0, d_loss=loss)
