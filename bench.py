@@ -1,12 +1,13 @@
 """Benchmark: 768x512 synthetic target, 50,000 2D Gaussians, accumulated-sum rendering.
 
-One "step" is the whole hot path on the GPU: gi_preprocess -> gi_bin_sort -> gi_render_fwd_l2
-(forward raster + L2 loss gradient) -> gi_loss_reduce -> gi_render_bwd -> gi_adam_step_pairs (gather
-of the per-pair gradients + Adam).  `value` is fwd+bwd training
-steps per second on one MI355X with every input resident in HBM.  Also reported: render FPS
-(preprocess + bin/sort + raster) and cached-raster FPS (raster only, binning reused); per-kernel
-times from HIP events on the launch stream over a separate pass of the same step; the roofline
-of the dominant kernel; and the CPU oracle timed on a bounded pixel sample of the same workload.
+One "step" is the whole hot path on the GPU: gi_preprocess_bin_sort (preprocess + tile binning)
+-> gi_render_fwd_bwd_l2 (per tile: forward raster, L2 loss gradient, backward raster) ->
+gi_adam_step_pairs (gather of the per-pair gradients + Adam, loss reduction).  `value` is fwd+bwd
+training steps per second on one MI355X with every input resident in HBM.  Also reported: render
+FPS (preprocess + bin/sort + raster) and cached-raster FPS (raster only, binning reused); kernel
+times from HIP events on the launch stream over a separate pass of the same step (and of the
+separate forward / backward kernels on the same binning); the roofline of the dominant kernel;
+and the CPU oracle timed on a bounded pixel sample of the same workload.
 
 usage: python bench.py [--gpus 1] [--steps 2800] [--warmup 50] [--workload NAME] [--no-cpu-baseline]
 """
@@ -159,15 +160,14 @@ def main():
     for _ in range(args.warmup):
         fit.step()
     torch.cuda.synchronize()
-    # kernel timing pass (eager steps): HIP events on the launch stream bracket the raster kernels
+    # kernel timing pass (eager steps): HIP events on the launch stream bracket the fused raster kernel
     nk = max(20, min(args.steps, 500))
     E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[E() for _ in range(4)] for _ in range(nk)]
+    ev = [[E() for _ in range(2)] for _ in range(nk)]
     for k in range(nk):
         fit.step(ev[k])
     torch.cuda.synchronize()
-    fwd_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])
-    bwd_ms = np.array([ev[k][2].elapsed_time(ev[k][3]) for k in range(nk)])
+    fused_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])
     # the timed region: K eager steps
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -178,8 +178,20 @@ def main():
     assert M_now <= r.capacity, "tile-pair capacity exceeded during the timed run"
     ms_step = 1e3 * t_train / args.steps
     final_loss = float(fit.loss.item())
-    log(f"[bench] train: {ms_step:.4f} ms/step, fwd {np.median(fwd_ms)*1e3:.1f} us, "
-        f"bwd {np.median(bwd_ms)*1e3:.1f} us, loss {final_loss:.4e}")
+    # the separate forward (with L2) and backward kernels on the same binning, for reference
+    ev2 = [[E() for _ in range(3)] for _ in range(nk)]
+    for k in range(nk):
+        ev2[k][0].record()
+        r.forward_l2(fit.target, fit.dL)
+        ev2[k][1].record()
+        r.backward(fit.dL, None)
+        ev2[k][2].record()
+    torch.cuda.synchronize()
+    fwd_ms = np.array([ev2[k][0].elapsed_time(ev2[k][1]) for k in range(nk)])
+    bwd_ms = np.array([ev2[k][1].elapsed_time(ev2[k][2]) for k in range(nk)])
+    log(f"[bench] train: {ms_step:.4f} ms/step, fused fwd+bwd {np.median(fused_ms)*1e3:.1f} us "
+        f"(separate: fwd {np.median(fwd_ms)*1e3:.1f} us, bwd {np.median(bwd_ms)*1e3:.1f} us), "
+        f"loss {final_loss:.4e}")
 
     # ---------------- render-only: preprocess + bin/sort + raster, and raster alone ----------------
     rend = Raster(W, H, wl.n)
@@ -215,8 +227,10 @@ def main():
     evald = evaluated_pairs(W, H, keys, vals, pixbox)
     fwd_s = float(np.mean(fwd_ms)) * 1e-3
     bwd_s = float(np.mean(bwd_ms)) * 1e-3
+    fused_s = float(np.mean(fused_ms)) * 1e-3
     fwd_tf = FLOP_FWD * pairs / fwd_s / 1e12
     bwd_tf = FLOP_BWD * pairs / bwd_s / 1e12
+    fused_tf = (FLOP_FWD + FLOP_BWD) * pairs / fused_s / 1e12
 
     def roof(name, kfile, kname, tf, secs):
         traffic = load_traffic(kfile, kname)
@@ -226,7 +240,7 @@ def main():
 
     roof_fwd = roof("fwd", "k_raster_sum.hip", "k_render_sum_fwd<true>", fwd_tf, fwd_s)
     roof_bwd = roof("bwd", "k_raster_sum.hip", "k_render_sum_bwd", bwd_tf, bwd_s)
-    dominant = roof_bwd if bwd_s >= fwd_s else roof_fwd
+    roof_fused = roof("fused", "k_raster_sum.hip", "k_render_sum_fused", fused_tf, fused_s)
 
     out = {
         "metric": METRIC,
@@ -249,11 +263,12 @@ def main():
         "cached_raster_fps": round(1.0 / t_cached, 1),
         "fit_seconds_2800_steps": round(2800 * ms_step / 1e3, 3),
         "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
-                  "kernels_us / roofline: HIP events on the launch stream around each raster kernel over "
-                  "a separate pass of the same step",
+                  "kernels_us / roofline: HIP events on the launch stream around the raster kernel(s) over "
+                  "a separate pass of the same step (fused) and of the separate kernels on the same binning",
         "final_loss": final_loss,
-        "kernels_us": {"render_fwd": round(fwd_s * 1e6, 2), "render_bwd": round(bwd_s * 1e6, 2)},
-        "roofline": dominant,
+        "kernels_us": {"render_fwd_bwd_fused": round(fused_s * 1e6, 2), "render_fwd_l2": round(fwd_s * 1e6, 2),
+                       "render_bwd": round(bwd_s * 1e6, 2)},
+        "roofline": roof_fused,
         "roofline_fwd": roof_fwd,
         "roofline_bwd": roof_bwd,
     }

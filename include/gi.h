@@ -269,6 +269,23 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gi_render_fwd_bwd_l2 -- gi_render_fwd_l2 and then gi_render_bwd (sum mode,
+ *   dparams NULL, dL_dimage = the L2 gradient just formed) in one launch: each
+ *   tile's workgroup renders the tile, forms its dL/dimage and immediately
+ *   back-propagates it, so dL/dimage never goes through device memory and the
+ *   tile list is staged once.  Outputs are bit-identical to the two calls:
+ *   image, loss_partials (and dL_dimage when not NULL) as gi_render_fwd_l2, the
+ *   per-pair gradients in the workspace as gi_render_bwd, ready for
+ *   gi_adam_step_pairs (or a gather).  Arguments as in those two calls; the
+ *   workspace is gi_render_bwd's.  Sum mode only.
+ */
+gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
+                               const uint32_t *offsets, const uint32_t *ranges, const uint32_t *tile_order,
+                               const uint32_t *vals, int64_t capacity, const float *target, float *image,
+                               float *dL_dimage, float *loss_partials, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * gi_loss_l2 -- L = mean over the 3HW entries of (image - target)^2 and
  *   dL/dimage = 2 (image - target) / (3HW)  ("FlashImgs", --loss l2).
  *   count      number of entries (3*H*W), >= 1.
@@ -313,11 +330,17 @@ gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float 
  *             when the caller advances *d_step in the same graph.  The bias
  *             corrections 1/(1-b1^t), 1/sqrt(1-b2^t) are formed on the device in
  *             fp64 either way (the same bits for the same t).
+ *   loss_partials, loss_count, d_loss (optional): when d_loss is not NULL, one
+ *             more workgroup of the launch does what gi_loss_reduce(T,
+ *             loss_partials, loss_count, d_loss) does (T = gi_num_tiles), for the
+ *             partials of gi_render_fwd_bwd_l2: the training step's loss
+ *             without a launch of its own.
  */
 gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
                              const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
                              const float *lr, double beta1, double beta2, double eps, int32_t step,
-                             const int32_t *d_step, void *stream);
+                             const int32_t *d_step, const float *loss_partials, int64_t loss_count,
+                             float *d_loss, void *stream);
 
 #ifdef __cplusplus
 }

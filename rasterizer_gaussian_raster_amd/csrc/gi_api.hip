@@ -205,6 +205,24 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     return hip_status(e);
 }
 
+gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
+                               const uint32_t *offsets, const uint32_t *ranges, const uint32_t *tile_order,
+                               const uint32_t *vals, int64_t capacity, const float *target, float *image,
+                               float *dL_dimage, float *loss_partials, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+        capacity >= (1ll << 31))
+        return GI_ERR_INVALID_ARG;
+    if (!offsets || !ranges || !vals || !target || !image || !loss_partials || !aligned16(image) || !workspace ||
+        !aligned256(workspace))
+        return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_render_sum_fused(desc->width, desc->height, records, pixbox, offsets, ranges,
+                                                  tile_order, vals, capacity, image, target, dL_dimage,
+                                                  loss_partials, workspace, as_stream(stream)));
+}
+
 size_t gi_loss_workspace_bytes(int64_t count) { return count < 1 ? 0 : gi::loss_workspace_bytes(count); }
 
 gi_status gi_loss_l2(int64_t count, const float *image, const float *target, float *dL_dimage, float *d_loss,
@@ -218,16 +236,19 @@ gi_status gi_loss_l2(int64_t count, const float *image, const float *target, flo
 gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
                              const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
                              const float *lr, double beta1, double beta2, double eps, int32_t step,
-                             const int32_t *d_step, void *stream) {
+                             const int32_t *d_step, const float *loss_partials, int64_t loss_count, float *d_loss,
+                             void *stream) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
         capacity >= (1ll << 31) || (!d_step && step < 1) || !lr)
         return GI_ERR_INVALID_ARG;
+    if (d_loss && (!loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;
     if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0)) return GI_ERR_INVALID_ARG;
     if (!offsets || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
     if (n > 0 && (!p || !m || !v || !aligned16(p) || !aligned16(m) || !aligned16(v))) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_adam_pairs((int)n, desc->width, desc->height, offsets, capacity, workspace, p, m, v,
-                                            lr, beta1, beta2, eps, step, d_step, as_stream(stream)));
+                                            lr, beta1, beta2, eps, step, d_step, loss_partials, loss_count,
+                                            d_loss, as_stream(stream)));
 }
 
 gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float *m, float *v, const float *lr,

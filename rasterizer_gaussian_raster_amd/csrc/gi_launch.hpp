@@ -47,9 +47,11 @@ hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint1
                                  const uint32_t *ranges, const uint32_t *order, const uint32_t *vals, float *image,
                                  const float *target, float *dL_dimage, float *loss_partials, hipStream_t s);
 hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, float *d_loss, hipStream_t s);
+// d_loss (or NULL): also reduce the raster pass's per-tile loss partials into it (one more workgroup).
 hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
                              float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
-                             const int32_t *d_step, hipStream_t s);
+                             const int32_t *d_step, const float *loss_partials, int64_t loss_count, float *d_loss,
+                             hipStream_t s);
 
 // Backward workspace: per (Gaussian, tile) gradient at its emission slot.
 struct BwdPlan {
@@ -63,6 +65,11 @@ hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint1
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
                                  const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s);
+// Forward with the L2 loss and backward of each tile in one launch (dL_dimage may be NULL).
+hipError_t launch_render_sum_fused(int W, int H, const float *records, const uint16_t *pixbox,
+                                   const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
+                                   const uint32_t *vals, int64_t capacity, float *image, const float *target,
+                                   float *dL_dimage, float *loss_partials, void *ws, hipStream_t s);
 // Adds each Gaussian's slots (offsets[g] .. offsets[g+1]) in order to dparams / dlogit, and the
 // per-tile background partials to dbackground.
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,

@@ -35,31 +35,41 @@ struct SumRec { float4 p, q; };   // p = (mux, muy, a, b), q = (c, cr, cg, cb)
 
 constexpr int kFwdBatch = 128;    // list entries staged per round (16 KB of LDS: 8+ workgroups per CU)
 
-// L2 = true also forms the L2 loss gradient 2 (I - T) / (3 W H) from the target
-// and each tile's sum of squared residuals (reduced over the tile in a fixed order).
-template <bool L2>
-__global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_x, int ntiles,
-                                                        const float4 *__restrict__ records,
-                                                        const uint2 *__restrict__ pixbox,
-                                                        const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
-                                                        const uint32_t *__restrict__ vals,
-                                                        float *__restrict__ image,
-                                                        const float *__restrict__ target,
-                                                        float *__restrict__ dL, float gscale,
-                                                        float *__restrict__ loss_part) {
-    __shared__ SumRec lst[4][kFwdBatch];
-    __shared__ int wq[4][4];                      // [wave][quadrant]: staged count this batch
-    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
-    if (t >= ntiles) return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
-    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
-    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
-    const uint2 rg = ranges[t];
-    const uint64_t below = lanes_below();
-    float ar = 0.0f, ag = 0.0f, ab = 0.0f;
+// Backward work item: one (list entry, 4x4 pixel block) pair per lane.  Each
+// wave takes a quarter of every batch of list entries and packs their items
+// entry by entry, 64 per round; each item writes its 8 values to an LDS slot,
+// then every entry adds its own items in block order -- no atomics, and the
+// result does not depend on timing.
+constexpr int kBwdBatch = 128;                    // list entries per block round, split over the 4 waves
+constexpr int kWaveEnt = kBwdBatch / 4;           // entries a wave takes per round (at most)
+constexpr int kGpStride = 17;                     // padded LDS run of one 4x4 block's dL/dI (float4):
+                                                  // the 16 blocks' pixels at one offset span all
+                                                  // 8 bank groups (at most 2-way conflicts)
 
+// LDS of the two phases; the fused kernel overlays them (the forward's lists
+// are dead once the tile's image is formed).
+struct FwdLds {
+    SumRec lst[4][kFwdBatch];                     // per quadrant: the batch's entries that touch it
+    int wq[4][4];                                 // [wave][quadrant]: staged count this batch
+};
+struct BwdLds {
+    float4 entp[4][kWaveEnt], entq[4][kWaveEnt];  // per wave: its staged entries (p, q)
+    uint16_t items[4][kWaveEnt * 16];             // per wave: entry | block << 8, entry-major
+    float4 ipart[4][2][64];                       // per wave: this round's item results
+};
+constexpr size_t kPhaseLds = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : sizeof(BwdLds);
+
+// Forward of one tile for this thread's pixel (px, py) = pixel centre: the
+// three channel sums over the tile's list in list order.  The list is staged
+// 128 entries at a time; each entry's pixel box is tested against the four
+// 8x8 quadrants and the records are compacted, in list order, into one LDS
+// list per quadrant; wave w walks quadrant w's list.  On return other waves
+// may still read S: barrier before reusing it.
+__device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg, const float4 *__restrict__ records,
+                                             const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
+                                             float px, float py, float &ar, float &ag, float &ab) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t below = lanes_below();
     for (uint32_t base = rg.x; base < rg.y; base += kFwdBatch) {
         const uint32_t idx = base + tid;
         uint32_t qm = 0;
@@ -82,20 +92,20 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
         for (int q = 0; q < 4; ++q) {
             const uint64_t m = __ballot((qm >> q) & 1u);
             rank[q] = (uint32_t)__popcll(m & below);
-            if (lane == 0) wq[wave][q] = __popcll(m);
+            if (lane == 0) S.wq[wave][q] = __popcll(m);
         }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if ((qm >> q) & 1u) {
                 int off = rank[q];
-                for (int w = 0; w < wave; ++w) off += wq[w][q];
-                lst[q][off] = r;
+                for (int w = 0; w < wave; ++w) off += S.wq[w][q];
+                S.lst[q][off] = r;
             }
         }
-        const int cnt = __builtin_amdgcn_readfirstlane(wq[0][wave] + wq[1][wave] + wq[2][wave] + wq[3][wave]);
+        const int cnt = __builtin_amdgcn_readfirstlane(S.wq[0][wave] + S.wq[1][wave] + S.wq[2][wave] + S.wq[3][wave]);
         __syncthreads();
-        const SumRec *L = lst[wave];
+        const SumRec *L = S.lst[wave];
         for (int k = 0; k < cnt; ++k) {
             const float4 A = L[k].p, B = L[k].q;
             const float dx = px - A.x, dy = py - A.y;
@@ -110,33 +120,12 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
         }
         if (base + kFwdBatch < rg.y) __syncthreads();   // the next batch reuses lst / wq
     }
-    float sq = 0.0f;
-    if (pxi < W && pyi < H) {
-        const size_t o = (size_t)pyi * W + pxi, plane = (size_t)W * H;
-        image[o] = ar;
-        image[o + plane] = ag;
-        image[o + 2 * plane] = ab;
-        if (L2) {
-            const float rr = ar - target[o], rgr = ag - target[o + plane], rbr = ab - target[o + 2 * plane];
-            dL[o] = gscale * rr;
-            dL[o + plane] = gscale * rgr;
-            dL[o + 2 * plane] = gscale * rbr;
-            sq = fmaf(rbr, rbr, fmaf(rgr, rgr, rr * rr));
-        }
-    }
-    if (L2) {
-        __shared__ float wsq[4];
-        const float ws = wave_total(sq);
-        if (lane == 0) wsq[wave] = ws;
-        __syncthreads();
-        if (tid == 0) loss_part[t] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
-    }
 }
 
 // Sum of the per-tile partials in a fixed order, divided by the entry count.
+// sm: 256 doubles of LDS.
 __device__ __forceinline__ void loss_reduce_block(int nparts, const float *__restrict__ part, double inv_count,
-                                                  float *__restrict__ loss) {
-    __shared__ double sm[256];
+                                                  float *__restrict__ loss, double *sm) {
     double s = 0.0;
     for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
     sm[threadIdx.x] = s;
@@ -148,102 +137,153 @@ __device__ __forceinline__ void loss_reduce_block(int nparts, const float *__res
     if (threadIdx.x == 0) *loss = (float)(sm[0] * inv_count);
 }
 
-__global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__restrict__ part, double inv_count,
-                                                     float *__restrict__ loss) {
-    loss_reduce_block(nparts, part, inv_count, loss);
+// Writes the image (and the L2 terms) of this thread's pixel and, with a
+// target, the tile's sum of squared residuals (in a fixed order).  Returns the
+// pixel's dL/dI (zero off the image).  Contains a workgroup barrier when L2.
+template <bool L2>
+__device__ __forceinline__ float4 sum_fwd_store(int W, int H, int pxi, int pyi, int t, float ar, float ag, float ab,
+                                                float *__restrict__ image, const float *__restrict__ target,
+                                                float *__restrict__ dL, float gscale, float *__restrict__ loss_part,
+                                                float *wsq /* LDS [4] */) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float sq = 0.0f;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pxi < W && pyi < H) {
+        const size_t o = (size_t)pyi * W + pxi, plane = (size_t)W * H;
+        image[o] = ar;
+        image[o + plane] = ag;
+        image[o + 2 * plane] = ab;
+        if (L2) {
+            const float rr = ar - target[o], rgr = ag - target[o + plane], rbr = ab - target[o + 2 * plane];
+            g = make_float4(gscale * rr, gscale * rgr, gscale * rbr, 0.f);
+            if (dL) {
+                dL[o] = g.x;
+                dL[o + plane] = g.y;
+                dL[o + 2 * plane] = g.z;
+            }
+            sq = fmaf(rbr, rbr, fmaf(rgr, rgr, rr * rr));
+        }
+    }
+    if (L2) {
+        const float ws = wave_total(sq);
+        if (lane == 0) wsq[wave] = ws;
+        __syncthreads();
+        if (threadIdx.x == 0) loss_part[t] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
+    }
+    return g;
 }
 
-// Backward work item: one (list entry, 4x4 pixel block) pair per thread.  Items
-// are laid out block-major (all entries overlapping block 0 in list order, then
-// block 1, ...), so the lanes of a wave mostly share one block and their dL/dI
-// reads from LDS are broadcasts.  Items run in rounds of 256 (one per thread);
-// each writes its 8 values to an LDS slot, then every entry adds its own items
-// in block order -- no atomics, and the result does not depend on timing.
-constexpr int kBwdBatch = 128;                    // list entries per block round, split over the 4 waves
-constexpr int kWaveEnt = kBwdBatch / 4;           // entries a wave takes per round (at most)
-constexpr int kGpStride = 17;                     // padded LDS run of one 4x4 block's dL/dI (float4):
-                                                  // the 16 blocks' pixels at one offset span all
-                                                  // 8 bank groups (at most 2-way conflicts)
-
-__global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
+// L2 = true also forms the L2 loss gradient 2 (I - T) / (3 W H) from the target
+// and each tile's sum of squared residuals (reduced over the tile in a fixed order).
+template <bool L2>
+__global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
-                                                        const uint32_t *__restrict__ offsets,
                                                         const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
-                                                        const uint32_t *__restrict__ vals, uint32_t capacity,
-                                                        const float *__restrict__ dL,
-                                                        float4 *__restrict__ part,
-                                                        const float *__restrict__ loss_part, int nparts,
-                                                        double inv_count, float *__restrict__ loss) {
-    if (loss && blockIdx.x == gridDim.x - 1) {          // the spare last workgroup: the forward's loss
-        loss_reduce_block(nparts, loss_part, inv_count, loss);
-        return;
-    }
-    __shared__ float4 gp[16 * kGpStride];               // dL/dI of the tile's pixels, block by block
-    __shared__ float4 entp[4][kWaveEnt], entq[4][kWaveEnt];   // per wave: its staged entries (p, q)
-    __shared__ uint16_t items[4][kWaveEnt * 16];        // per wave: entry | block << 8, entry-major
-    __shared__ float4 ipart[4][2][64];                  // per wave: this round's item results
+                                                        const uint32_t *__restrict__ vals,
+                                                        float *__restrict__ image,
+                                                        const float *__restrict__ target,
+                                                        float *__restrict__ dL, float gscale,
+                                                        float *__restrict__ loss_part) {
+    __shared__ FwdLds S;
+    __shared__ float wsq[4];
     const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
-    const uint2 rg = ranges[t];
-    if (rg.x == rg.y) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tx = t % tiles_x, ty = t / tiles_x;
+    const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
+    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
+    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
+    float ar = 0.0f, ag = 0.0f, ab = 0.0f;
+    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
+    sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
+}
+
+__global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__restrict__ part, double inv_count,
+                                                     float *__restrict__ loss) {
+    __shared__ double sm[256];
+    loss_reduce_block(nparts, part, inv_count, loss, sm);
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+// One lane's entry of a wave's share, loaded into registers.
+struct BwdEntry {
+    float4 p, q;
+    uint2 box;
+    uint32_t off;          // offsets[g]
+};
+
+// This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
+__device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0, uint32_t &ne) {
+    const uint32_t nb = min((uint32_t)kBwdBatch, rg.y - base);
+    const uint32_t q = (nb + 3) >> 2;
+    e0 = base + (uint32_t)(threadIdx.x >> 6) * q;
+    const uint32_t end = base + nb;
+    ne = e0 < end ? min(q, end - e0) : 0u;
+}
+
+__device__ __forceinline__ void bwd_load(uint32_t e0, uint32_t ne, const float4 *__restrict__ records,
+                                         const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ offsets,
+                                         const uint32_t *__restrict__ vals, BwdEntry &E) {
+    const uint32_t lane = threadIdx.x & 63;
+    E.p = E.q = make_float4(0.f, 0.f, 0.f, 0.f);
+    E.box = make_uint2(1u, 0u);
+    E.off = 0u;
+    if (lane < ne) {
+        const uint32_t g = vals[e0 + lane];
+        E.p = records[2 * g];
+        E.q = records[2 * g + 1];
+        E.box = pixbox[g];
+        E.off = offsets[g];
+    }
+}
+
+// Stages lane `lane`'s entry: its record in LDS, its emission slot and the
+// rectangle of 4x4 blocks its pixel box overlaps (empty when none).
+__device__ __forceinline__ void bwd_stage(BwdLds &S, uint32_t ne, const BwdEntry &E, int tx, int ty, int x0, int y0,
+                                          int &bx0, int &bx1, int &by0, int &by1, uint32_t &slot) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    bx0 = 4; bx1 = -1; by0 = 4; by1 = -1;
+    slot = 0xffffffffu;
+    if ((uint32_t)lane < ne) {
+        S.entp[wave][lane] = E.p;
+        S.entq[wave][lane] = E.q;
+        const uint2 bx = E.box;
+        slot = emit_slot(E.off, bx, tx, ty);
+        bx0 = max((int)(bx.x & 0xffff) - x0, 0) >> 2;
+        bx1 = min((int)(bx.y & 0xffff) - x0, 15) >> 2;
+        by0 = max((int)(bx.x >> 16) - y0, 0) >> 2;
+        by1 = min((int)(bx.y >> 16) - y0, 15) >> 2;
+    }
+}
+
+// LDS index of pixel (x, y) of the tile in gp: block (y/4)*4 + x/4, offset (y%4)*4 + x%4.
+__device__ __forceinline__ int gp_index(int x, int y) {
+    return (((y >> 2) << 2) | (x >> 2)) * kGpStride + ((y & 3) << 2) + (x & 3);
+}
+
+// Backward of one tile with its dL/dI published in gp and the first share's
+// entries (E0) already loaded; each entry's 8 values go to its emission slot.
+// Wave-local from here on (no workgroup barrier).
+__device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx, int ty, uint2 rg, BwdEntry E0,
+                                             const float4 *__restrict__ records, const uint2 *__restrict__ pixbox,
+                                             const uint32_t *__restrict__ offsets,
+                                             const uint32_t *__restrict__ vals, uint32_t capacity,
+                                             float4 *__restrict__ part) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int x0 = tx * kTile, y0 = ty * kTile;
     const float k2 = 2.0f * kLn2;
     const float is = 1.0f / kScale;
-
-    // This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
-    auto share = [&](uint32_t base, uint32_t &e0, uint32_t &ne) {
-        const uint32_t nb = min((uint32_t)kBwdBatch, rg.y - base);
-        const uint32_t q = (nb + 3) >> 2;
-        e0 = base + (uint32_t)wave * q;
-        const uint32_t end = base + nb;
-        ne = e0 < end ? min(q, end - e0) : 0u;
-    };
-    // Stages lane `lane`'s entry of the share: its record in LDS, its emission slot
-    // and the rectangle of 4x4 blocks its pixel box overlaps (empty when none).
-    int bx0, bx1, by0, by1;
-    uint32_t slot;
-    auto stage = [&](uint32_t e0, uint32_t ne) {
-        bx0 = 4; bx1 = -1; by0 = 4; by1 = -1;
-        slot = 0xffffffffu;
-        if ((uint32_t)lane < ne) {
-            const uint32_t g = vals[e0 + lane];
-            entp[wave][lane] = records[2 * g];
-            entq[wave][lane] = records[2 * g + 1];
-            const uint2 bx = pixbox[g];
-            slot = emit_slot(offsets[g], bx, tx, ty);
-            bx0 = max((int)(bx.x & 0xffff) - x0, 0) >> 2;
-            bx1 = min((int)(bx.y & 0xffff) - x0, 15) >> 2;
-            by0 = max((int)(bx.x >> 16) - y0, 0) >> 2;
-            by1 = min((int)(bx.y >> 16) - y0, 15) >> 2;
-        }
-    };
-
-    // dL/dI loads and the first share's staging go out together; one workgroup
-    // barrier publishes the tile's dL/dI, everything after it is wave-local.
-    uint32_t e0, ne;
-    share(rg.x, e0, ne);
-    float4 gv0 = make_float4(0.f, 0.f, 0.f, 0.f);
-    {
-        const int xi = x0 + (tid & 15), yi = y0 + (tid >> 4);
-        if (xi < W && yi < H) {
-            const size_t o = (size_t)yi * W + xi, plane = (size_t)W * H;
-            gv0 = make_float4(dL[o], dL[o + plane], dL[o + 2 * plane], 0.f);
-        }
-    }
-    stage(e0, ne);
-    // pixel (x, y) of the tile: block (y/4)*4 + x/4, offset (y%4)*4 + x%4
-    gp[(((tid >> 6) << 2) | ((tid & 15) >> 2)) * kGpStride + (((tid >> 4) & 3) << 2) + (tid & 3)] = gv0;
-    __syncthreads();
-
     for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
-        if (base != rg.x) {
-            share(base, e0, ne);
-            stage(e0, ne);
-        }
+        uint32_t e0, ne;
+        bwd_share(rg, base, e0, ne);
         if (ne == 0) continue;                              // wave-uniform; no workgroup barrier below
+        BwdEntry E = E0;
+        if (base != rg.x) bwd_load(e0, ne, records, pixbox, offsets, vals, E);
+        int bx0, bx1, by0, by1;
+        uint32_t slot;
+        bwd_stage(S, ne, E, tx, ty, x0, y0, bx0, bx1, by0, by1, slot);
         // entry-major item positions: lane e's items are [s_e, s_e + n_e), blocks in
         // ascending order (row-major over its rectangle)
         const uint32_t n_e = (uint32_t)(lane) < ne ? (uint32_t)((bx1 - bx0 + 1) * (by1 - by0 + 1)) : 0u;
@@ -253,17 +293,17 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
         {
             uint32_t o = s_e;
             for (int by = by0; by <= by1; ++by)
-                for (int bx = bx0; bx <= bx1; ++bx) items[wave][o++] = (uint16_t)(lane | ((by * 4 + bx) << 8));
+                for (int bx = bx0; bx <= bx1; ++bx) S.items[wave][o++] = (uint16_t)(lane | ((by * 4 + bx) << 8));
         }
         wave_sync();
         float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // this lane's entry
         for (uint32_t rb = 0; rb < nitems; rb += 64) {
             const uint32_t it = rb + lane;
             if (it < nitems) {
-                const uint32_t code = items[wave][it];
+                const uint32_t code = S.items[wave][it];
                 const uint32_t e = code & 0xffu, blk = code >> 8;
                 const int lx = (int)(blk & 3u) * 4, ly = (int)(blk >> 2) * 4;
-                const float4 A = entp[wave][e], B = entq[wave][e];
+                const float4 A = S.entp[wave][e], B = S.entq[wave][e];
                 float dy[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
@@ -299,16 +339,16 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
                 // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22).
                 const float a = A.z, b = A.w, c = B.x;
                 const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                ipart[wave][0][lane] = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv,
-                                                   -is * fmaf(a * a, da, a * b * db), -is * (a * c * db));
-                ipart[wave][1][lane] = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
+                S.ipart[wave][0][lane] = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv,
+                                                     -is * fmaf(a * a, da, a * b * db), -is * (a * c * db));
+                S.ipart[wave][1][lane] = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
             }
             wave_sync();
             // each entry adds its items of this round in order: blocks ascending
             // whatever the rounds are, so the sum is reproducible
             const uint32_t lo = max(s_e, rb), hi = min(s_e + n_e, rb + 64u);
             for (uint32_t p = lo; p < hi; ++p) {
-                const float4 u0 = ipart[wave][0][p - rb], u1 = ipart[wave][1][p - rb];
+                const float4 u0 = S.ipart[wave][0][p - rb], u1 = S.ipart[wave][1][p - rb];
                 acc0.x += u0.x; acc0.y += u0.y; acc0.z += u0.z; acc0.w += u0.w;
                 acc1.x += u1.x; acc1.y += u1.y; acc1.z += u1.z; acc1.w += u1.w;
             }
@@ -320,6 +360,89 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
         }
         wave_sync();                                        // ent / items are rewritten next batch
     }
+}
+
+__global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
+                                                        const float4 *__restrict__ records,
+                                                        const uint2 *__restrict__ pixbox,
+                                                        const uint32_t *__restrict__ offsets,
+                                                        const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
+                                                        const uint32_t *__restrict__ vals, uint32_t capacity,
+                                                        const float *__restrict__ dL,
+                                                        float4 *__restrict__ part,
+                                                        const float *__restrict__ loss_part, int nparts,
+                                                        double inv_count, float *__restrict__ loss) {
+    __shared__ float4 gp[16 * kGpStride];               // dL/dI of the tile's pixels, block by block
+    __shared__ __align__(16) unsigned char lds[sizeof(BwdLds)];
+    if (loss && blockIdx.x == gridDim.x - 1) {          // the spare last workgroup: the forward's loss
+        loss_reduce_block(nparts, loss_part, inv_count, loss, reinterpret_cast<double *>(lds));
+        return;
+    }
+    BwdLds &S = *reinterpret_cast<BwdLds *>(lds);
+    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
+    if (t >= ntiles) return;
+    const uint2 rg = ranges[t];
+    if (rg.x == rg.y) return;
+    const int tid = threadIdx.x;
+    const int tx = t % tiles_x, ty = t / tiles_x;
+    const int x0 = tx * kTile, y0 = ty * kTile;
+    // dL/dI loads and the first share's loads go out together; one workgroup
+    // barrier publishes the tile's dL/dI, everything after it is wave-local.
+    uint32_t e0, ne;
+    bwd_share(rg, rg.x, e0, ne);
+    float4 gv0 = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+        const int xi = x0 + (tid & 15), yi = y0 + (tid >> 4);
+        if (xi < W && yi < H) {
+            const size_t o = (size_t)yi * W + xi, plane = (size_t)W * H;
+            gv0 = make_float4(dL[o], dL[o + plane], dL[o + 2 * plane], 0.f);
+        }
+    }
+    BwdEntry E0;
+    bwd_load(e0, ne, records, pixbox, offsets, vals, E0);
+    gp[gp_index(tid & 15, tid >> 4)] = gv0;
+    __syncthreads();
+    sum_bwd_tile(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, capacity, part);
+}
+
+// Forward with the L2 loss, then the backward of the same tile, in one
+// workgroup: the tile's dL/dI never leaves LDS, and the backward's first share
+// of entries is loaded while the forward runs.  Same results, bit for bit, as
+// k_render_sum_fwd<true> followed by k_render_sum_bwd.
+__global__ __launch_bounds__(256) void k_render_sum_fused(int W, int H, int tiles_x, int ntiles,
+                                                          const float4 *__restrict__ records,
+                                                          const uint2 *__restrict__ pixbox,
+                                                          const uint32_t *__restrict__ offsets,
+                                                          const uint2 *__restrict__ ranges,
+                                                          const uint32_t *__restrict__ order,
+                                                          const uint32_t *__restrict__ vals, uint32_t capacity,
+                                                          float *__restrict__ image, const float *__restrict__ target,
+                                                          float *__restrict__ dL, float gscale,
+                                                          float *__restrict__ loss_part, float4 *__restrict__ part) {
+    __shared__ float4 gp[16 * kGpStride];
+    __shared__ __align__(16) unsigned char lds[kPhaseLds];
+    __shared__ float wsq[4];
+    const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
+    if (t >= ntiles) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tx = t % tiles_x, ty = t / tiles_x;
+    const int x0 = tx * kTile, y0 = ty * kTile;
+    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
+    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
+    const uint2 rg = ranges[t];
+    uint32_t e0, ne;
+    bwd_share(rg, rg.x, e0, ne);
+    BwdEntry E0;
+    bwd_load(e0, ne, records, pixbox, offsets, vals, E0);
+    float ar = 0.0f, ag = 0.0f, ab = 0.0f;
+    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, (float)pxi + 0.5f,
+                 (float)pyi + 0.5f, ar, ag, ab);
+    const float4 g = sum_fwd_store<true>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
+    if (rg.x == rg.y) return;                             // uniform
+    gp[gp_index(pxi - x0, pyi - y0)] = g;
+    __syncthreads();                                      // gp published; the forward's lists are dead
+    sum_bwd_tile(*reinterpret_cast<BwdLds *>(lds), gp, tx, ty, rg, E0, records, pixbox, offsets, vals, capacity,
+                 part);
 }
 
 // Adds the pair slots q in [o0, o1) (part[2q], part[2q + 1]) into (a, b) in
@@ -407,9 +530,18 @@ __device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, flo
     p -= lr * (m * inv_bc1) / (sqrtf(v) * inv_sqrt_bc2 + a.eps);
 }
 
+// With `loss`, one more workgroup (the last) reduces the loss partials of the
+// raster pass into it.
 __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
                                                     const float4 *__restrict__ part, float4 *__restrict__ p,
-                                                    float4 *__restrict__ m, float4 *__restrict__ v, AdamPairArgs a) {
+                                                    float4 *__restrict__ m, float4 *__restrict__ v, AdamPairArgs a,
+                                                    const float *__restrict__ loss_part, int nparts, double inv_count,
+                                                    float *__restrict__ loss) {
+    if (loss && blockIdx.x == gridDim.x - 1) {
+        __shared__ double sm[256];
+        loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
+        return;
+    }
     const int g = blockIdx.x * 256 + threadIdx.x;
     if (g >= n) return;
     float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
@@ -449,8 +581,10 @@ BwdPlan make_bwd_plan(int W, int H, int64_t capacity) {
 
 hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
                              float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
-                             const int32_t *d_step, hipStream_t s) {
-    if (n == 0) return hipSuccess;
+                             const int32_t *d_step, const float *loss_partials, int64_t loss_count, float *d_loss,
+                             hipStream_t s) {
+    const int nb = (n + 255) / 256 + (d_loss ? 1 : 0);
+    if (nb == 0) return hipSuccess;
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
     AdamPairArgs a{};
     for (int i = 0; i < 8; ++i) a.lr[i] = lr[i];
@@ -463,9 +597,11 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
     a.b2d = beta2;
     a.step = step;
     a.d_step = d_step;
-    k_adam_pairs<<<(n + 255) / 256, 256, 0, s>>>(
+    const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+    k_adam_pairs<<<nb, 256, 0, s>>>(
         n, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(static_cast<const char *>(ws) + pl.off_part),
-        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a);
+        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a,
+        loss_partials, ntiles, loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss);
     return hipGetLastError();
 }
 
@@ -521,6 +657,20 @@ hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint1
         offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, dL_dimage,
         reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part), loss_partials, ntiles, inv_count,
         d_loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_render_sum_fused(int W, int H, const float *records, const uint16_t *pixbox,
+                                   const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
+                                   const uint32_t *vals, int64_t capacity, float *image, const float *target,
+                                   float *dL_dimage, float *loss_partials, void *ws, hipStream_t s) {
+    const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
+    const BwdPlan p = make_bwd_plan(W, H, capacity);
+    const float gscale = (float)(2.0 / (3.0 * (double)W * (double)H));
+    k_render_sum_fused<<<padded_tiles(ntiles), 256, 0, s>>>(
+        W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
+        offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, image, target, dL_dimage,
+        gscale, loss_partials, reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part));
     return hipGetLastError();
 }
 

@@ -63,7 +63,8 @@ def load():
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
-        "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P], i32),
+        "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P, i64, P, P], i32),
+        "gi_render_fwd_bwd_l2": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -204,11 +205,22 @@ def gi_loss_reduce(nparts, loss_partials, count, d_loss, stream=None):
 
 
 def gi_adam_step_pairs(d, n, offsets, capacity, workspace, p, m, v, lr, beta1, beta2, eps, step, stream=None,
-                       d_step=None):
-    """d_step: optional device int32 [1] holding the step (read on the device; `step` is then ignored)."""
+                       d_step=None, loss_partials=None, loss_count=0, d_loss=None):
+    """d_step: optional device int32 [1] holding the step (read on the device; `step` is then ignored).
+    d_loss: also reduce loss_partials into it (as gi_loss_reduce) in the same launch."""
     lr_arr = (ctypes.c_float * 8)(*[float(x) for x in lr])
     _check(load().gi_adam_step_pairs(ctypes.byref(d), int(n), _ptr(offsets), int(capacity), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _ptr(p), _ptr(m), _ptr(v),
                                      lr_arr, float(beta1), float(beta2), float(eps), int(step), _ptr(d_step),
-                                     _stream(stream)),
+                                     _ptr(loss_partials), int(loss_count), _ptr(d_loss), _stream(stream)),
            "gi_adam_step_pairs")
+
+
+def gi_render_fwd_bwd_l2(d, n, records, pixbox, offsets, ranges, vals, capacity, target, image, dL_dimage,
+                         loss_partials, workspace, stream=None, tile_order=None):
+    """Forward with the L2 loss and backward (pair gradients into workspace) in one launch."""
+    _check(load().gi_render_fwd_bwd_l2(ctypes.byref(d), int(n), _ptr(records), _ptr(pixbox), _ptr(offsets),
+                                       _ptr(ranges), _ptr(tile_order), _ptr(vals), int(capacity), _ptr(target),
+                                       _ptr(image), _ptr(dL_dimage), _ptr(loss_partials), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gi_render_fwd_bwd_l2")

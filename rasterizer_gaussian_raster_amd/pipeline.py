@@ -4,9 +4,9 @@ Torch provides device memory and the stream; every step below is one call of
 the C ABI (through :mod:`.gi`):
 
   render : gi_preprocess_bin_sort (gi_preprocess + gi_bin_sort in one call) -> gi_render_fwd
-  fit (sum mode)   : gi_preprocess_bin_sort -> gi_render_fwd_l2
-                     -> gi_render_bwd (pair gradients left in its workspace; loss reduced in a spare
-                        workgroup) -> gi_adam_step_pairs
+  fit (sum mode)   : gi_preprocess_bin_sort -> gi_render_fwd_bwd_l2 (per tile: forward, L2 gradient,
+                     backward; pair gradients left in the workspace) -> gi_adam_step_pairs (gather +
+                     Adam; the loss reduced in a spare workgroup)
   fit (alpha mode) : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
 
 Fitter.capture() records the sum-mode step as HIP graphs (torch.cuda.CUDAGraph over the same
@@ -141,6 +141,16 @@ class Raster:
                          loss_partials=self.loss_partials if d_loss is not None else None,
                          loss_count=3 * self.W * self.H, d_loss=d_loss)
 
+    def forward_backward_l2(self, target, dL_dimage=None, stream=None):
+        """Sum mode: forward_l2 then backward(dL, None) in one launch (pair gradients in bwd_ws)."""
+        if self.bwd_ws is None:
+            nbytes = gi.gi_render_bwd_workspace_bytes(self.desc, self.n, self.capacity)
+            self.bwd_ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device(self.device))
+        gi.gi_render_fwd_bwd_l2(self.desc, self.n, self.records, self.pixbox, self.offsets, self.ranges, self.vals,
+                                self.capacity, target, self.image, dL_dimage, self.loss_partials, self.bwd_ws,
+                                stream, tile_order=self._order())
+        return self.image
+
     def render(self, params, logit=None, background=None, sync=True):
         self.bin(sync=sync, params=params, logit=logit)
         return self.forward(background)
@@ -197,21 +207,19 @@ class Fitter:
             return True
         return False
 
-    def _sum_step(self, order, ev=(None,) * 4, d_step=None):
+    def _sum_step(self, order, ev=(None,) * 2, d_step=None):
         """The sum-mode step's calls.  d_step: device step counter, advanced here (graph mode)."""
         r = self.raster
         r.bin(sync=False, order=order, params=self.params)
         ev[0] is not None and ev[0].record()
-        r.forward_l2(self.target, self.dL)
+        r.forward_backward_l2(self.target)                     # image, loss partials, pair gradients
         ev[1] is not None and ev[1].record()
-        ev[2] is not None and ev[2].record()
-        r.backward(self.dL, None, d_loss=self.loss)            # the loss is reduced in the same launch
-        ev[3] is not None and ev[3].record()
         if d_step is not None:
             d_step.add_(1)
         b1, b2 = self.betas
         gi.gi_adam_step_pairs(r.desc, self.n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v,
-                              self.lr, b1, b2, self.eps, self.step_count + 1, d_step=d_step)
+                              self.lr, b1, b2, self.eps, self.step_count + 1, d_step=d_step,
+                              loss_partials=r.loss_partials, loss_count=3 * r.W * r.H, d_loss=self.loss)
 
     def capture(self, warmup=2):
         """Record the sum-mode step as two HIP graphs (with and without the tile-order refresh).  The
@@ -238,15 +246,15 @@ class Fitter:
         self.graphs = graphs
 
     def step(self, events=None):
-        """One training step.  events: optional 4 torch events recorded around the raster kernels
-        (before/after forward, before/after backward) on the current stream (eager steps only)."""
+        """One training step.  events: optional 2 torch events recorded before / after the fused raster
+        kernel on the current stream (eager steps only)."""
         if self.graphs is not None:
             self.graphs[self.step_count % ORDER_EVERY == 0].replay()
             self.step_count += 1
             return
         r = self.raster
         if self.logit is None:
-            self._sum_step(self.step_count % ORDER_EVERY == 0, events if events is not None else (None,) * 4)
+            self._sum_step(self.step_count % ORDER_EVERY == 0, events if events is not None else (None,) * 2)
             self.step_count += 1
             return
         bg = self.bg4

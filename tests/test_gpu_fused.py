@@ -141,3 +141,100 @@ def test_backward_loss_argument_checks():
         gi.gi_render_bwd(r.desc, r.n, r.records, None, None, r.pixbox, r.offsets, r.ranges, r.vals, r.capacity,
                          None, None, None, G, None, None, None, r.bwd_ws, loss_partials=r.loss_partials,
                          loss_count=0, d_loss=loss)
+
+
+def _fused_case(name):
+    if name in ("tiny_fit_64x64", "kodak_768x512_50k", "div2k_1020x678_70k"):
+        w = synth.make_workload(name)
+        return w["workload"].width, w["workload"].height, w["params"], w["target"]
+    rng = np.random.default_rng(61)
+    if name == "ragged_300x200":
+        W, H, p = 300, 200, synth.random_case(62, 300, 200, 4000, sigma=(0.3, 20.0), margin=20)
+    elif name == "long_lists":                      # every tile list longer than one staging batch
+        W, H = 64, 48
+        n = 3000
+        p = np.zeros((n, 8), np.float32)
+        p[:, 0] = rng.uniform(0, W, n)
+        p[:, 1] = rng.uniform(0, H, n)
+        p[:, 2] = rng.uniform(2.0, 12.0, n)
+        p[:, 3] = rng.uniform(-3.0, 3.0, n)
+        p[:, 4] = rng.uniform(2.0, 12.0, n)
+        p[:, 5:] = rng.uniform(-0.1, 0.1, (n, 3))
+    elif name == "empty":
+        W, H, p = 70, 45, np.zeros((0, 8), np.float32)
+    else:
+        raise KeyError(name)
+    return W, H, p, rng.uniform(0, 1, (3, H, W)).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", ["tiny_fit_64x64", "kodak_768x512_50k", "div2k_1020x678_70k", "ragged_300x200",
+                                  "long_lists", "empty"])
+@pytest.mark.parametrize("use_order", [False, True])
+def test_fwd_bwd_fused_equals_separate_calls(name, use_order):
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    W, H, p, tgt = _fused_case(name)
+    n = p.shape[0]
+    r = Raster(W, H, n)
+    P, T = dev(p), dev(tgt)
+    M = r.bin(sync=True, params=P, order=True)
+    if not use_order:
+        r.has_order = False
+    ws_bytes = gi.gi_render_bwd_workspace_bytes(r.desc, n, r.capacity)
+    # separate: forward with L2, then backward (pair gradients left in the workspace)
+    img1, dl1, lp1 = torch.empty_like(T), torch.empty_like(T), torch.empty_like(r.loss_partials)
+    ws1 = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    gi.gi_render_fwd_l2(r.desc, n, r.records, r.pixbox, r.ranges, r.vals, T, img1, dl1, lp1, tile_order=r._order())
+    gi.gi_render_bwd(r.desc, n, r.records, None, None, r.pixbox, r.offsets, r.ranges, r.vals, r.capacity, None, None,
+                     None, dl1, None, None, None, ws1, tile_order=r._order())
+    # fused
+    img2, dl2, lp2 = torch.full_like(T, 7.0), torch.full_like(T, 7.0), torch.full_like(r.loss_partials, 7.0)
+    ws2 = torch.full((ws_bytes,), 0x5a, dtype=torch.uint8, device="cuda")
+    gi.gi_render_fwd_bwd_l2(r.desc, n, r.records, r.pixbox, r.offsets, r.ranges, r.vals, r.capacity, T, img2, dl2,
+                            lp2, ws2, tile_order=r._order())
+    # and without the optional dL/dI output
+    img3 = torch.empty_like(T)
+    ws3 = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    lp3 = torch.empty_like(r.loss_partials)
+    gi.gi_render_fwd_bwd_l2(r.desc, n, r.records, r.pixbox, r.offsets, r.ranges, r.vals, r.capacity, T, img3, None,
+                            lp3, ws3, tile_order=r._order())
+    torch.cuda.synchronize()
+    for a, b in [(img1, img2), (dl1, dl2), (lp1[: r.T], lp2[: r.T]), (img1, img3), (lp1[: r.T], lp3[: r.T])]:
+        np.testing.assert_array_equal(u32(a), u32(b))
+    g1 = ws1[: 32 * M].cpu().numpy()
+    np.testing.assert_array_equal(g1, ws2[: 32 * M].cpu().numpy())
+    np.testing.assert_array_equal(g1, ws3[: 32 * M].cpu().numpy())
+
+
+def test_adam_pairs_loss_equals_loss_reduce():
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    w = synth.make_workload("kodak_768x512_50k")
+    W, H, n = 768, 512, 50_000
+    r = Raster(W, H, n)
+    P, T = dev(w["params"]), dev(w["target"])
+    r.bin(sync=True, params=P)
+    r.forward_backward_l2(T)
+    ref = torch.full((1,), -1.0, device="cuda")
+    gi.gi_loss_reduce(r.T, r.loss_partials, T.numel(), ref)
+    lr = [0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005]
+    outs = []
+    for with_loss in (False, True):
+        p2, m2, v2 = P.clone(), torch.full_like(P, 0.01), torch.full_like(P, 0.02)
+        got = torch.full((1,), -2.0, device="cuda")
+        kw = dict(loss_partials=r.loss_partials, loss_count=T.numel(), d_loss=got) if with_loss else {}
+        gi.gi_adam_step_pairs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, p2, m2, v2, lr, 0.9, 0.999, 1e-8, 3, **kw)
+        torch.cuda.synchronize()
+        outs.append([u32(p2), u32(m2), u32(v2)])
+        if with_loss:
+            np.testing.assert_array_equal(u32(got), u32(ref))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    # n = 0: only the loss workgroup runs
+    got0 = torch.full((1,), -3.0, device="cuda")
+    gi.gi_adam_step_pairs(r.desc, 0, r.offsets, r.capacity, r.bwd_ws, None, None, None, lr, 0.9, 0.999, 1e-8, 1,
+                          loss_partials=r.loss_partials, loss_count=T.numel(), d_loss=got0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u32(got0), u32(ref))
