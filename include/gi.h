@@ -129,12 +129,17 @@ gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, con
  *   vals      device uint32 [capacity] out: Gaussian index of pair m.
  *   ranges    device uint32 [T][2] out: [start, end) of tile t in keys/vals;
  *             (0, 0) for a tile with no pair.
- *   tile_order device uint32 [T] out, or NULL: the tiles by decreasing list
- *             length (lengths of 1023 or more count as equal; ties in no
- *             particular order).  Passed to the raster calls it makes them take
- *             long lists first, which balances the CUs when the whole grid of
- *             tiles is resident at once (a few thousand tiles); it never changes
- *             a result.  Costs one single-workgroup launch; an order from an
+ *   tile_order device uint32 [T] out, or NULL: a permutation of the tiles for
+ *             the raster calls.  The tiles are ranked by decreasing list length
+ *             (lengths of 1023 or more count as equal; ties in no particular
+ *             order) and rank p goes to launch position serp(p): positions come
+ *             in layers of P = the device's CU count, layer k holding ranks
+ *             kP .. kP+P-1, in reverse order in odd layers (a last, partial layer
+ *             of width r reversed within its r positions).  The hardware deals
+ *             consecutive workgroups round-robin over the CUs, so each CU then
+ *             gets a mix of long and short lists, which balances the CUs when the
+ *             whole grid of tiles is resident at once (a few thousand tiles); it
+ *             never changes a result.  Costs one single-workgroup launch; an order from an
  *             earlier binning is as valid (any permutation of the tiles is),
  *             so a caller may refresh it only now and then.
  *   capacity  length of keys/vals, 0 <= capacity < 2^31.

@@ -35,12 +35,24 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// b^t (t >= 0) by binary powering in fp64: a short chain of multiplications
+// (a few ulps of fp64 from the exact power, far below the fp32 rounding that
+// follows) instead of a general pow.
+__device__ __forceinline__ double powi_f64(double b, int t) {
+    double r = 1.0, x = b;
+    for (unsigned e = (unsigned)t; e != 0u; e >>= 1) {
+        if (e & 1u) r *= x;
+        x *= x;
+    }
+    return r;
+}
+
 // Adam's bias corrections for step t (t < 1 is taken as 1), formed in fp64 and
 // rounded once: 1/(1 - b1^t) and 1/sqrt(1 - b2^t).
 __device__ __forceinline__ void adam_bias(double b1, double b2, int t, float &inv_bc1, float &inv_sqrt_bc2) {
-    const double td = (double)(t < 1 ? 1 : t);
-    inv_bc1 = (float)(1.0 / (1.0 - pow(b1, td)));
-    inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(b2, td)));
+    const int tt = t < 1 ? 1 : t;
+    inv_bc1 = (float)(1.0 / (1.0 - powi_f64(b1, tt)));
+    inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - powi_f64(b2, tt)));
 }
 
 // 2^x with the hardware transcendental (v_exp_f32).

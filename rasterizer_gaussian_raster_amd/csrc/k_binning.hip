@@ -27,10 +27,10 @@
 //     otherwise      : LSD -- the first pass took the low digit, k_count /
 //                      k_scatter take the next ones over blocks of 1024-4096
 //                      keys, and k_ranges marks where each run starts and ends.
-//   5. k_tile_order : (optional) the tiles by decreasing list length, the order
-//                     in which the raster kernels should take them: long lists
-//                     first spread the work evenly over the CUs when the whole
-//                     grid is resident at once.
+//   5. k_tile_order : (optional) the order in which the raster kernels should
+//                     take the tiles: sorted by decreasing list length and dealt
+//                     to the CUs in serpentine layers, which balances the CUs
+//                     when the whole grid is resident at once.
 //
 // Each scatter ranks up to 4096 keys at a time: every wave takes a contiguous
 // span of the chunk and finds the rank of each key among the equal digits of
@@ -818,7 +818,17 @@ __global__ __launch_bounds__(256) void k_ranges(const uint32_t *__restrict__ key
 // of 1023 or more share the first bucket, and tiles of equal bucket land in no
 // particular order (the order only schedules work: every tile's results are
 // its own, whatever the order).
-__global__ __launch_bounds__(1024) void k_tile_order(const uint2 *__restrict__ ranges, int ntiles,
+// Launch position of the tile of sorted rank p: ranks are dealt in layers of
+// `period` positions (the CU count: the hardware deals consecutive workgroups
+// round-robin over the CUs), reversed in every odd layer, so that each CU's
+// workgroups mix long and short lists when the whole grid is resident.
+__device__ __forceinline__ uint32_t serpentine(uint32_t p, uint32_t period, uint32_t n) {
+    const uint32_t layer = p / period, c = p - layer * period;
+    const uint32_t base = layer * period, width = min(period, n - base);
+    return base + ((layer & 1u) ? width - 1u - c : c);
+}
+
+__global__ __launch_bounds__(1024) void k_tile_order(const uint2 *__restrict__ ranges, int ntiles, int period,
                                                      uint32_t *__restrict__ order) {
     __shared__ uint32_t hist[1024];
     __shared__ uint32_t sm[16];
@@ -839,7 +849,8 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint2 *__restrict__ r
     for (int t = tid; t < ntiles; t += 1024) {
         const uint2 r = ranges[t];
         const uint32_t len = r.y > r.x ? r.y - r.x : 0u;
-        order[atomicAdd(&hist[1023u - min(len, 1023u)], 1u)] = (uint32_t)t;
+        const uint32_t rank = atomicAdd(&hist[1023u - min(len, 1023u)], 1u);
+        order[serpentine(rank, (uint32_t)period, (uint32_t)ntiles)] = (uint32_t)t;
     }
 }
 
@@ -847,6 +858,20 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint2 *__restrict__ r
 // host side
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// CUs of the current device (cached per device; 256 if the query fails).
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
 
 BinPlan make_bin_plan(int n, int W, int H, int64_t capacity) {
     BinPlan p{};
@@ -939,7 +964,7 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     // the tile order when one is asked for (also for n == 0 or capacity == 0)
     auto finish = [&]() -> hipError_t {
         if (tile_order)
-            k_tile_order<<<1, 1024, 0, s>>>(rg, p.ntiles, tile_order);
+            k_tile_order<<<1, 1024, 0, s>>>(rg, p.ntiles, device_cus(), tile_order);
         return hipGetLastError();
     };
 

@@ -514,7 +514,11 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
 
 // Adam on each Gaussian's 8 parameters with the gradient gathered from its
 // pairs' slots (offsets[g] .. offsets[g+1], emission order): the gather and
-// the optimizer in one pass, no gradient array.
+// the optimizer in one pass, no gradient array.  Eight lanes per Gaussian, lane
+// j on parameter j: a Gaussian's parameters, moments and each slot are 32
+// contiguous bytes read by its 8 lanes together, and up to 8 slots are loaded
+// at once.  Each parameter's slots are added in ascending order, as in
+// gather_slots (same bits as a gather followed by the Adam step).
 struct AdamPairArgs {
     float lr[8];
     float b1, omb1, b2, omb2, eps;
@@ -523,18 +527,11 @@ struct AdamPairArgs {
     const int32_t *d_step;           // device step count (graph replays), or NULL
 };
 
-__device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, float lr, const AdamPairArgs &a,
-                                      float inv_bc1, float inv_sqrt_bc2) {
-    m = fmaf(a.b1, m, a.omb1 * g);
-    v = fmaf(a.b2, v, a.omb2 * g * g);
-    p -= lr * (m * inv_bc1) / (sqrtf(v) * inv_sqrt_bc2 + a.eps);
-}
-
 // With `loss`, one more workgroup (the last) reduces the loss partials of the
 // raster pass into it.
 __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
-                                                    const float4 *__restrict__ part, float4 *__restrict__ p,
-                                                    float4 *__restrict__ m, float4 *__restrict__ v, AdamPairArgs a,
+                                                    const float *__restrict__ part, float *__restrict__ p,
+                                                    float *__restrict__ m, float *__restrict__ v, AdamPairArgs a,
                                                     const float *__restrict__ loss_part, int nparts, double inv_count,
                                                     float *__restrict__ loss) {
     if (loss && blockIdx.x == gridDim.x - 1) {
@@ -542,25 +539,33 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
         loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
         return;
     }
-    const int g = blockIdx.x * 256 + threadIdx.x;
+    const int i = blockIdx.x * 256 + threadIdx.x;     // parameter i % 8 of Gaussian i / 8
+    const int g = i >> 3, j = i & 7;
     if (g >= n) return;
-    float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
-    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    float P = p[i], Mo = m[i], V = v[i];
     const int t = a.d_step ? *a.d_step : a.step;
-    if (offsets[n] <= capacity) gather_slots(part, offsets[g], offsets[g + 1], g0, g1);   // else: zero gradient
+    const bool ok = offsets[n] <= capacity;           // else the binning overflowed: zero gradient
+    const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
+    float G = 0.0f;
+    for (uint32_t q = o0; q < o1; q += 8) {
+        float u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) u[k] = part[8 * (size_t)min(q + (uint32_t)k, o1 - 1u) + j];   // repeats not added
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (q + (uint32_t)k < o1) G += u[k];
+    }
     float c1, c2;
     adam_bias(a.b1d, a.b2d, t, c1, c2);
-    adam1(P0.x, g0.x, M0.x, V0.x, a.lr[0], a, c1, c2);
-    adam1(P0.y, g0.y, M0.y, V0.y, a.lr[1], a, c1, c2);
-    adam1(P0.z, g0.z, M0.z, V0.z, a.lr[2], a, c1, c2);
-    adam1(P0.w, g0.w, M0.w, V0.w, a.lr[3], a, c1, c2);
-    adam1(P1.x, g1.x, M1.x, V1.x, a.lr[4], a, c1, c2);
-    adam1(P1.y, g1.y, M1.y, V1.y, a.lr[5], a, c1, c2);
-    adam1(P1.z, g1.z, M1.z, V1.z, a.lr[6], a, c1, c2);
-    adam1(P1.w, g1.w, M1.w, V1.w, a.lr[7], a, c1, c2);
-    p[2 * g] = P0; p[2 * g + 1] = P1;
-    m[2 * g] = M0; m[2 * g + 1] = M1;
-    v[2 * g] = V0; v[2 * g + 1] = V1;
+    float lr = a.lr[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) lr = j == k ? a.lr[k] : lr;
+    Mo = fmaf(a.b1, Mo, a.omb1 * G);
+    V = fmaf(a.b2, V, a.omb2 * G * G);
+    P -= lr * (Mo * c1) / (sqrtf(V) * c2 + a.eps);
+    p[i] = P;
+    m[i] = Mo;
+    v[i] = V;
 }
 
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
@@ -583,7 +588,7 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
                              float *m, float *v, const float *lr, double beta1, double beta2, double eps, int step,
                              const int32_t *d_step, const float *loss_partials, int64_t loss_count, float *d_loss,
                              hipStream_t s) {
-    const int nb = (n + 255) / 256 + (d_loss ? 1 : 0);
+    const int nb = (int)(((int64_t)n * 8 + 255) / 256) + (d_loss ? 1 : 0);
     if (nb == 0) return hipSuccess;
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
     AdamPairArgs a{};
@@ -599,8 +604,8 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
     a.d_step = d_step;
     const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
     k_adam_pairs<<<nb, 256, 0, s>>>(
-        n, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(static_cast<const char *>(ws) + pl.off_part),
-        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a,
+        n, offsets, (uint32_t)capacity, reinterpret_cast<const float *>(static_cast<const char *>(ws) + pl.off_part),
+        p, m, v, a,
         loss_partials, ntiles, loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss);
     return hipGetLastError();
 }

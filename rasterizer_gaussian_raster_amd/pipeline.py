@@ -25,11 +25,12 @@ from . import gi
 # colour units for the colours).
 DEFAULT_LR = (0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005)
 
-# Up to this many tiles the raster kernels take the tiles longest list first
-# (gi_bin_sort's tile_order): the whole grid is then resident on the chip at once
-# and the order is what balances the CUs.  Larger grids balance themselves.  The
-# order is a schedule, not data: one from an earlier binning is as valid, so a fit
-# refreshes it every ORDER_EVERY steps only.
+# Up to this many tiles the raster kernels take the tiles in gi_bin_sort's
+# tile_order (ranked by list length, dealt to the CUs in serpentine layers): the
+# whole grid is then resident on the chip at once and the order is what balances
+# the CUs.  Larger grids balance themselves.  The order is a schedule, not data:
+# one from an earlier binning is as valid, so a fit refreshes it every
+# ORDER_EVERY steps only.
 ORDER_MAX_TILES = 8192
 ORDER_EVERY = 16
 

@@ -1,6 +1,6 @@
-"""The tile order of gi_bin_sort (longest list first) only schedules work: it must be a permutation
-of the tiles sorted by list length, and every raster output must be bit-identical with and without
-it."""
+"""The tile order of gi_bin_sort only schedules work: it must be a permutation of the tiles ranked by
+list length and dealt in serpentine layers of the CU count, and every raster output must be
+bit-identical with and without it."""
 import numpy as np
 import pytest
 import torch
@@ -11,23 +11,35 @@ from rasterizer_gaussian_raster_amd import synth
 pytestmark = pytest.mark.gpu
 
 
+def _serpentine(p, period, n):
+    layer, c = divmod(p, period)
+    base = layer * period
+    width = min(period, n - base)
+    return base + (width - 1 - c if layer % 2 else c)
+
+
 def _check_order(r):
+    """A permutation of the tiles; read in rank order (launch position serp(rank)), the list
+    lengths are non-increasing."""
     order = u32(r.order)[: r.T].astype(np.int64)
     rg = u32(r.ranges)[: r.T].astype(np.int64)
     np.testing.assert_array_equal(np.sort(order), np.arange(r.T))
-    ln = np.minimum(rg[:, 1] - rg[:, 0], 1023)[order]
+    period = torch.cuda.get_device_properties(0).multi_processor_count
+    pos = np.array([_serpentine(p, period, r.T) for p in range(r.T)])
+    np.testing.assert_array_equal(np.sort(pos), np.arange(r.T))
+    ln = np.minimum(rg[:, 1] - rg[:, 0], 1023)[order[pos]]
     assert np.all(np.diff(ln) <= 0)
 
 
-@pytest.mark.parametrize("case", ["kodak_768x512_50k", "random_300x200", "single_tile"])
-def test_tile_order_is_longest_first(case):
+@pytest.mark.parametrize("case", ["kodak_768x512_50k", "div2k_1020x678_70k", "random_300x200", "single_tile"])
+def test_tile_order_is_serpentine_by_length(case):
     require_gpu()
     from rasterizer_gaussian_raster_amd.pipeline import Raster
     if case == "random_300x200":
         W, H, p = 300, 200, synth.random_case(31, 300, 200, 3000, sigma=(0.3, 20.0))
     elif case == "single_tile":
         W, H, p = 13, 9, synth.random_case(32, 13, 9, 50)
-    else:
+    else:           # 1536 tiles (6 full layers of 256) and 2752 (a partial last layer)
         w = synth.make_workload(case)
         W, H, p = w["workload"].width, w["workload"].height, w["params"]
     r = Raster(W, H, p.shape[0])
