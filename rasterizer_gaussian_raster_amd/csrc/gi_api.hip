@@ -84,7 +84,7 @@ gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, con
                         float *opacity, uint16_t *pixbox, uint32_t *counts, void *stream) {
     if (!preprocess_args_ok(desc, n, params, logit, records, opacity, pixbox, counts)) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_preprocess((int)n, desc->width, desc->height, params, logit, records, opacity,
-                                            pixbox, counts, nullptr, nullptr, as_stream(stream)));
+                                            pixbox, counts, nullptr, nullptr, gi::BinHist{}, as_stream(stream)));
 }
 
 size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
@@ -119,7 +119,8 @@ gi_status gi_preprocess_bin_sort(const gi_desc *desc, int64_t n, const float *pa
     const gi::BinPlan plan = gi::make_bin_plan((int)n, desc->width, desc->height, capacity);
     hipStream_t s = as_stream(stream);
     hipError_t e = gi::launch_preprocess((int)n, desc->width, desc->height, params, logit, records, opacity,
-                                         pixbox, counts, gi::bin_group_sums(plan, workspace), ranges, s);
+                                         pixbox, counts, gi::bin_group_sums(plan, workspace), ranges,
+                                         gi::bin_hist(plan, workspace), s);
     if (e == hipSuccess)
         e = gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges, tile_order, d_num, workspace, s,
                                 true);

@@ -118,4 +118,24 @@ __device__ __forceinline__ uint32_t emit_slot(uint32_t off_g, uint2 box, int tx,
     return off_g + (uint32_t)((ty - ty0) * (tx1 - tx0 + 1) + (tx - tx0));
 }
 
+// Adds the tile pairs of one Gaussian (count c, packed pixel box bx) to an LDS
+// histogram of the digit (tile id >> shift) & dmask.  Each row of its tile
+// rectangle is a run of consecutive tile ids, added run by run where the digit
+// changes (one atomic per run instead of one per pair).
+__device__ __forceinline__ void hist_add_pairs(uint32_t *hist, uint32_t c, uint2 bx, int tiles_x, int shift,
+                                               uint32_t dmask) {
+    if (c == 0u) return;
+    const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
+    const uint32_t wt = ((bx.y & 0xffffu) >> 4) - tx0 + 1u;
+    const uint32_t rows = c / wt;
+    for (uint32_t r = 0; r < rows; ++r) {
+        const uint32_t lo = (ty0 + r) * (uint32_t)tiles_x + tx0, hi = lo + wt - 1u;
+        for (uint32_t a = lo; a <= hi;) {
+            const uint32_t e = min(hi, (((a >> shift) + 1u) << shift) - 1u);
+            atomicAdd(&hist[(a >> shift) & dmask], e - a + 1u);
+            a = e + 1u;
+        }
+    }
+}
+
 }  // namespace gi

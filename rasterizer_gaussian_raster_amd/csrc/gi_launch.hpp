@@ -7,11 +7,22 @@
 
 namespace gi {
 
+// The binning's first-pass digit histogram, one table column per 256-Gaussian
+// segment, written by the kernel that forms the tile counts (table NULL: not
+// written; the binning then counts in a kernel of its own).
+struct BinHist {
+    uint32_t *table;
+    int tiles_x, shift, bits;
+    int redundant;         // layout [column][digit] (read raw), else [digit][ncols_cap] (scanned)
+    int ncols_cap;
+};
+
 // k_preprocess.hip
-// group_sums / ranges (or NULL): the binning's group sums and cleared ranges (gi_preprocess_bin_sort).
+// group_sums / ranges (or NULL): the binning's group sums and cleared ranges (gi_preprocess_bin_sort),
+// and the digit histogram when hist.table is set.
 hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
                              float *opacity, uint16_t *pixbox, uint32_t *counts, unsigned long long *group_sums,
-                             uint32_t *ranges, hipStream_t s);
+                             uint32_t *ranges, BinHist hist, hipStream_t s);
 
 // k_binning.hip
 struct BinPlan {
@@ -39,6 +50,9 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
                            void *ws, hipStream_t s, bool groups_done = false);
 // device address of the group sums inside the bin workspace
 unsigned long long *bin_group_sums(const BinPlan &p, void *ws);
+// what gi_preprocess_bin_sort's preprocess kernel histograms for the plan (table NULL when the
+// plan counts in a kernel of its own)
+BinHist bin_hist(const BinPlan &p, void *ws);
 // device address of the 64-bit instance total inside the workspace
 const void *bin_total_ptr(const void *ws);
 

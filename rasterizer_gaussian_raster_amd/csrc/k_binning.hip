@@ -309,15 +309,20 @@ __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span,
 // 1-2: group sums
 // ---------------------------------------------------------------------------
 // Also clears the tile ranges (tiles that receive no pair keep (0, 0)); with
-// n == 0 it publishes M = 0 itself.
+// n == 0 it publishes M = 0 itself.  With hist.table set it also writes the
+// group's first-pass digit histogram (no count kernel runs then).
 __global__ __launch_bounds__(kBT) void k_group_sums(int n, const uint32_t *__restrict__ counts,
+                                                    const uint2 *__restrict__ pixbox,
                                                     unsigned long long *__restrict__ part, int ntiles,
                                                     uint2 *__restrict__ ranges, BinHeader *__restrict__ hdr,
-                                                    uint32_t *__restrict__ offsets, uint32_t *__restrict__ d_num) {
+                                                    uint32_t *__restrict__ offsets, uint32_t *__restrict__ d_num,
+                                                    BinHist hist) {
     __shared__ unsigned long long sm[4];
-    for (int t = blockIdx.x * kBT + threadIdx.x; t < ntiles; t += gridDim.x * kBT) ranges[t] = make_uint2(0u, 0u);
+    __shared__ uint32_t h[256];
+    const int tid = threadIdx.x;
+    for (int t = blockIdx.x * kBT + tid; t < ntiles; t += gridDim.x * kBT) ranges[t] = make_uint2(0u, 0u);
     if (n == 0) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (blockIdx.x == 0 && tid == 0) {
             hdr->total = 0ull;
             hdr->m_eff = 0u;
             *d_num = 0u;
@@ -325,11 +330,22 @@ __global__ __launch_bounds__(kBT) void k_group_sums(int n, const uint32_t *__res
         }
         return;
     }
-    const int g = blockIdx.x * kBT + threadIdx.x;
-    unsigned long long c = g < n ? counts[g] : 0ull;
+    const int radix = 1 << hist.bits;
+    if (hist.table && tid < radix) h[tid] = 0u;
+    const int g = blockIdx.x * kBT + tid;
+    const uint32_t c = g < n ? counts[g] : 0u;
+    const uint2 bx = (hist.table && g < n) ? pixbox[g] : make_uint2(0u, 0u);
     unsigned long long tot;
-    block_exclusive_scan<unsigned long long, kBT>(c, sm, &tot);
-    if (threadIdx.x == 0) part[blockIdx.x] = tot;
+    block_exclusive_scan<unsigned long long, kBT>((unsigned long long)c, sm, &tot);   // barriers publish h
+    if (tid == 0) part[blockIdx.x] = tot;
+    if (hist.table) {                                     // uniform
+        hist_add_pairs(h, c, bx, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
+        __syncthreads();
+        if (tid < radix) {
+            if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + tid] = h[tid];
+            else hist.table[(size_t)tid * hist.ncols_cap + blockIdx.x] = h[tid];
+        }
+    }
 }
 
 __device__ __forceinline__ void publish_total(unsigned long long tot, long long capacity, int n,
@@ -376,7 +392,6 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
                                                 const unsigned long long *__restrict__ part,
                                                 BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
                                                 uint32_t *__restrict__ d_num, uint32_t *__restrict__ table) {
-    __shared__ SegLds<kBT> G;
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sm[4];
     __shared__ unsigned long long sm64[8];
@@ -424,29 +439,7 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
         uint32_t tot;
         const uint32_t local = block_exclusive_scan<uint32_t, kBT>(c, sm, &tot);
         if (gid < n) offsets[gid] = sat32(base + local);
-        const bool big = __syncthreads_or(c > kDirectMax);
-        if (emit && tot > 0 && !big) {                            // uniform: each thread its own tiles
-            const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
-            const uint32_t wt = ((bx.y & 0xffffu) >> 4) - tx0 + 1;
-            uint32_t row = ty0 * (uint32_t)tiles_x + tx0, col = 0;
-            for (uint32_t k = 0; k < c; ++k) {
-                atomicAdd(&hist[((row + col) >> shift) & dmask], 1u);
-                if (++col == wt) { col = 0; row += (uint32_t)tiles_x; }
-            }
-        } else if (emit && tot > 0) {                             // uniform: pairs spread over the lanes
-            G.excl[tid] = local;
-            if (tid == 0) G.excl[kBT] = tot;
-            G.box[tid] = bx;
-            __syncthreads();
-            const int ns = min(kBT, n - g * kBT);
-            for (uint32_t idx = tid; idx < tot; idx += kBT) {
-                uint32_t key;
-                int lo;
-                regen_pair<kBT>(G, ns, idx, tiles_x, key, lo);
-                atomicAdd(&hist[(key >> shift) & dmask], 1u);
-            }
-            __syncthreads();
-        }
+        if (emit) hist_add_pairs(hist, c, bx, tiles_x, shift, dmask);
         base += tot;
     }
     __syncthreads();
@@ -463,34 +456,76 @@ template <int SG>
 // Workgroup 0 also publishes where each digit's run starts (bucket_start[d],
 // d <= radix, the last one M) for the bucket pass, and, when this pass sorts
 // the whole key (ranges != NULL), the tile ranges themselves.
+//
+// Two ways in.  With `counts` (segments of one group, raw group sums in part[],
+// at most kMaxRedundantGroups groups) the block forms its Gaussians' emission
+// offsets itself, writes offsets[] and, in workgroup 0, publishes M: no count
+// kernel ran.  Without, offsets[] and M come from k_count0.
 __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift, int bits, int table_redundant,
                                                   int ncols_cap, const uint2 *__restrict__ pixbox,
-                                                  const uint32_t *__restrict__ offsets,
-                                                  const BinHeader *__restrict__ hdr,
+                                                  uint32_t *__restrict__ offsets, BinHeader *__restrict__ hdr,
                                                   const uint32_t *__restrict__ table, uint32_t *__restrict__ kout,
                                                   uint32_t *__restrict__ vout, uint32_t *__restrict__ bucket_start,
-                                                  uint2 *__restrict__ ranges, int ntiles) {
+                                                  uint2 *__restrict__ ranges, int ntiles,
+                                                  const uint32_t *__restrict__ counts,
+                                                  const unsigned long long *__restrict__ part, int ngroups,
+                                                  long long capacity, uint32_t *__restrict__ d_num) {
     constexpr int S = kBT * SG;
     __shared__ SegLds<S> G;
     __shared__ ChunkLds<kPerLane> L;
     __shared__ BaseLds B;
+    __shared__ unsigned long long sm64[8];
+    __shared__ uint32_t smc[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int first = blockIdx.x * S;
     const int ns = min(S, n - first);
-    // One round of loads: the segment's offsets and boxes, M, the digit table.
+    // One round of loads: the segment's offsets (or counts and the group sums)
+    // and boxes, M, the digit table.
     uint32_t o[SG], o1[SG];
     uint2 bx[SG];
+    uint32_t o0, oend, M;
+    DigitAcc acc;
+    if (counts) {                                     // SG == 1
+        const uint32_t c = tid < ns ? counts[first + tid] : 0u;
+        bx[0] = tid < ns ? pixbox[first + tid] : make_uint2(0u, 0u);
+        unsigned long long v[kMaxRedundantGroups / kBT];
 #pragma unroll
-    for (int r = 0; r < SG; ++r) {
-        const int i = r * kBT + tid;
-        o[r] = i < ns ? offsets[first + i] : 0u;
-        o1[r] = i < ns ? offsets[first + i + 1] : 0u;
-        bx[r] = i < ns ? pixbox[first + i] : make_uint2(0u, 0u);
+        for (int k = 0; k < kMaxRedundantGroups / kBT; ++k) {
+            const int i = tid + k * kBT;
+            v[k] = i < ngroups ? part[i] : 0ull;
+        }
+        acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
+        unsigned long long before = 0, all = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxRedundantGroups / kBT; ++k) {
+            all += v[k];
+            before += tid + k * kBT < (int)blockIdx.x ? v[k] : 0ull;
+        }
+        unsigned long long tb, ta;
+        block_exclusive_scan<unsigned long long, kBT>(before, sm64, &tb);
+        block_exclusive_scan<unsigned long long, kBT>(all, sm64 + 4, &ta);
+        uint32_t tot;
+        const uint32_t local = block_exclusive_scan<uint32_t, kBT>(c, smc, &tot);
+        if (tid < ns) offsets[first + tid] = sat32(tb + local);
+        if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num);
+        M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
+        o0 = (uint32_t)tb;                           // exact whenever M > 0
+        o[0] = o0 + local;
+        o1[0] = o[0] + c;
+        oend = o0 + tot;
+    } else {
+#pragma unroll
+        for (int r = 0; r < SG; ++r) {
+            const int i = r * kBT + tid;
+            o[r] = i < ns ? offsets[first + i] : 0u;
+            o1[r] = i < ns ? offsets[first + i + 1] : 0u;
+            bx[r] = i < ns ? pixbox[first + i] : make_uint2(0u, 0u);
+        }
+        o0 = offsets[first];
+        oend = offsets[first + ns];                  // the next segment's first slot, or M
+        M = hdr->m_eff;
+        acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
     }
-    const uint32_t o0 = offsets[first];
-    const uint32_t oend = offsets[first + ns];       // the next segment's first slot, or M
-    const uint32_t M = hdr->m_eff;
-    const DigitAcc acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
     if (M == 0u) return;                              // overflow or no pair (then offsets may saturate): uniform
 #pragma unroll
     for (int r = 0; r < SG; ++r) {
@@ -947,6 +982,19 @@ unsigned long long *bin_group_sums(const BinPlan &p, void *ws) {
     return reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + p.off_part);
 }
 
+BinHist bin_hist(const BinPlan &p, void *ws) {
+    BinHist h{};
+    if (p.n > 0 && p.seg_groups == 1 && p.redundant_groups) {
+        h.table = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + p.off_table);
+        h.tiles_x = p.tiles_x;
+        h.shift = p.shift0;
+        h.bits = p.bits[0];
+        h.redundant = p.table_redundant[0];
+        h.ncols_cap = p.ncols_cap[0];
+    }
+    return h;
+}
+
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
                            void *ws, hipStream_t s, bool groups_done) {
@@ -968,17 +1016,26 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
         return hipGetLastError();
     };
 
+    // Segments of one group with the group sums read raw: the counting step is
+    // folded into the kernel that forms the group sums (this one, or the
+    // preprocess kernel) and the first scatter forms the offsets itself.
+    const BinHist hist = bin_hist(p, ws);
+    const bool folded = hist.table != nullptr;
     if (!groups_done || p.n == 0)
-        k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, part, p.ntiles, rg, hdr, offsets, d_num);
+        k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, box, part, p.ntiles, rg, hdr, offsets,
+                                                            d_num, hist);
     if (p.n == 0) return finish();
-    if (!p.redundant_groups)
-        k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
-    k_count0<<<p.nseg, kBT, 0, s>>>(p.n, p.nb_g, p.seg_groups, p.redundant_groups, (long long)p.capacity,
-                                    p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0], counts,
-                                    box, part, hdr, offsets, d_num, table);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.capacity == 0) return finish();
+    hipError_t e;
+    if (!folded) {
+        if (!p.redundant_groups)
+            k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
+        k_count0<<<p.nseg, kBT, 0, s>>>(p.n, p.nb_g, p.seg_groups, p.redundant_groups, (long long)p.capacity,
+                                        p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0],
+                                        counts, box, part, hdr, offsets, d_num, table);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (p.capacity == 0) return finish();
+    }
     if (!p.table_redundant[0]) {
         e = scan_u32(table, (1 << p.bits[0]) * p.ncols_cap[0], tsp, s);
         if (e != hipSuccess) return e;
@@ -987,18 +1044,26 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     uint32_t *k0 = keys, *v0 = vals;
     if (p.order_kind == 1 || (lsd && (p.passes & 1) == 0)) { k0 = kalt; v0 = valt; }
     uint2 *rg0 = p.order_kind == 0 ? rg : nullptr;
-    if (p.seg_groups == 1)
+    if (folded)             // also when capacity == 0: it publishes offsets and M
         k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
                                              p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles);
+                                             p.ntiles, counts, part, p.nb_g, (long long)p.capacity, d_num);
+    else if (p.seg_groups == 1)
+        k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
+                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
+                                             p.ntiles, nullptr, nullptr, 0, 0, nullptr);
     else if (p.seg_groups == 2)
         k_scatter0<2><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
                                              p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles);
+                                             p.ntiles, nullptr, nullptr, 0, 0, nullptr);
     else
         k_scatter0<4><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
                                              p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles);
+                                             p.ntiles, nullptr, nullptr, 0, 0, nullptr);
+    if (p.capacity == 0) {
+        e = hipGetLastError();
+        return e != hipSuccess ? e : finish();
+    }
     if (p.order_kind == 1) {
         const int nbk = 1 << p.bits[0];
         if (p.bucket_lanes == 4)

@@ -12,11 +12,11 @@
 
 namespace gi {
 
-// One Gaussian: record, pixel box, tile count (returned), opacity.
+// One Gaussian: record, pixel box (also returned in *box_out), tile count (returned), opacity.
 __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const float4 *__restrict__ params,
                                                    const float *__restrict__ logit, float4 *__restrict__ records,
                                                    float *__restrict__ opacity, uint2 *__restrict__ pixbox,
-                                                   uint32_t *__restrict__ counts) {
+                                                   uint32_t *__restrict__ counts, uint2 *box_out) {
     const float4 p0 = params[2 * g];       // mux, muy, l11, l21
     const float4 p1 = params[2 * g + 1];   // l22, cr, cg, cb
     const float l11 = p0.z, l21 = p0.w, l22 = p1.x;
@@ -60,6 +60,7 @@ __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const fl
     records[2 * g + 1] = ok ? make_float4(c, p1.y, p1.z, p1.w) : make_float4(0.f, 0.f, 0.f, 0.f);
     pixbox[g] = box;
     counts[g] = cnt;
+    *box_out = box;
     if (opacity) {
         const float l = fminf(lam, kLogitMax);
         opacity[g] = ok ? 1.0f / (1.0f + expf(-l)) : 0.0f;
@@ -68,41 +69,54 @@ __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const fl
 }
 
 // With group_sums (binning in the same call): also the sum of each 256-Gaussian
-// group's tile counts, and the tile ranges cleared -- the binning's first step.
+// group's tile counts, the tile ranges cleared and, when hist.table is set, the
+// group's first-pass digit histogram -- the binning's first step.
 __global__ __launch_bounds__(256) void k_preprocess(int n, int W, int H, const float4 *__restrict__ params,
                                                     const float *__restrict__ logit,
                                                     float4 *__restrict__ records, float *__restrict__ opacity,
                                                     uint2 *__restrict__ pixbox, uint32_t *__restrict__ counts,
                                                     unsigned long long *__restrict__ group_sums,
-                                                    uint2 *__restrict__ ranges, int ntiles) {
+                                                    uint2 *__restrict__ ranges, int ntiles, BinHist hist) {
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    uint2 box;
     if (group_sums) {
-        for (int t = g; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
-        const uint32_t c = g < n ? preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts) : 0u;
-        // block sum of the counts (u64), waves then the workgroup
         __shared__ unsigned long long ws[4];
+        __shared__ uint32_t h[256];
+        const int radix = 1 << hist.bits;
+        if (hist.table && (int)threadIdx.x < radix) h[threadIdx.x] = 0u;
+        for (int t = g; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
+        const uint32_t c = g < n ? preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box) : 0u;
+        // block sum of the counts (u64), waves then the workgroup
         unsigned long long x = c;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
         if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = x;
-        __syncthreads();
+        __syncthreads();                                  // also publishes the cleared histogram
         if (threadIdx.x == 0) group_sums[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+        if (hist.table) {                                 // uniform
+            hist_add_pairs(h, c, box, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
+            __syncthreads();
+            if ((int)threadIdx.x < radix) {
+                if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + threadIdx.x] = h[threadIdx.x];
+                else hist.table[(size_t)threadIdx.x * hist.ncols_cap + blockIdx.x] = h[threadIdx.x];
+            }
+        }
         return;
     }
     if (g >= n) return;
-    preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts);
+    preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box);
 }
 
 hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
                              float *opacity, uint16_t *pixbox, uint32_t *counts, unsigned long long *group_sums,
-                             uint32_t *ranges, hipStream_t s) {
+                             uint32_t *ranges, BinHist hist, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const int bs = 256;
     const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
     k_preprocess<<<(n + bs - 1) / bs, bs, 0, s>>>(n, W, H, reinterpret_cast<const float4 *>(params), logit,
                                                   reinterpret_cast<float4 *>(records), opacity,
                                                   reinterpret_cast<uint2 *>(pixbox), counts, group_sums,
-                                                  reinterpret_cast<uint2 *>(ranges), ntiles);
+                                                  reinterpret_cast<uint2 *>(ranges), ntiles, hist);
     return hipGetLastError();
 }
 
