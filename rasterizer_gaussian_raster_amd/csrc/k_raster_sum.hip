@@ -35,13 +35,20 @@ struct SumRec { float4 p, q; };   // p = (mux, muy, a, b), q = (c, cr, cg, cb)
 
 constexpr int kFwdBatch = 128;    // list entries staged per round (16 KB of LDS: 8+ workgroups per CU)
 
-// Backward work item: one (list entry, 4x4 pixel block) pair per lane.  Each
-// wave takes a quarter of every batch of list entries and packs their items
-// entry by entry, 64 per round; each item writes its 8 values to an LDS slot,
-// then every entry adds its own items in block order -- no atomics, and the
-// result does not depend on timing.
+// Backward work item: one (list entry, 4x4 pixel block) pair.  Each wave takes
+// a quarter of every batch of list entries and lists their items entry by entry
+// (blocks ascending); with R = ceil(items / 64), lane l takes the run of items
+// [l R, l R + R) and adds them up in registers, entry by entry.  A run meets at
+// most a few entries and an entry spans few runs: each (entry, run) partial
+// goes to an LDS slot -- the entry's first run to slot e, a run that continues
+// an entry from the lane before to slot kWaveEnt + l -- and each entry finally
+// adds its partials in run order.  No atomics; the result does not depend on
+// timing.
 constexpr int kBwdBatch = 128;                    // list entries per block round, split over the 4 waves
 constexpr int kWaveEnt = kBwdBatch / 4;           // entries a wave takes per round (at most)
+constexpr int kBwdWavesPerSimd = 6;              // occupancy the backward kernels are built for (<= 80
+                                                  // VGPRs): 6 tile workgroups per CU, all 1536 tiles of a
+                                                  // 768x512 image resident at once
 constexpr int kGpStride = 17;                     // padded LDS run of one 4x4 block's dL/dI (float4):
                                                   // the 16 blocks' pixels at one offset span all
                                                   // 8 bank groups (at most 2-way conflicts)
@@ -55,7 +62,7 @@ struct FwdLds {
 struct BwdLds {
     float4 entp[4][kWaveEnt], entq[4][kWaveEnt];  // per wave: its staged entries (p, q)
     uint16_t items[4][kWaveEnt * 16];             // per wave: entry | block << 8, entry-major
-    float4 ipart[4][2][64];                       // per wave: this round's item results
+    float4 part[4][kWaveEnt + 64][2];             // per wave: (entry, run) partial sums
 };
 constexpr size_t kPhaseLds = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : sizeof(BwdLds);
 
@@ -296,12 +303,26 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 for (int bx = bx0; bx <= bx1; ++bx) S.items[wave][o++] = (uint16_t)(lane | ((by * 4 + bx) << 8));
         }
         wave_sync();
-        float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // this lane's entry
-        for (uint32_t rb = 0; rb < nitems; rb += 64) {
-            const uint32_t it = rb + lane;
-            if (it < nitems) {
+        const uint32_t R = (nitems + 63u) >> 6;             // items per lane (wave-uniform)
+        const uint32_t f = (uint32_t)lane * R, fend = min(f + R, nitems);
+        float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // the current (entry, run) partial
+        uint32_t cur = 0xffffffffu, cur_slot = 0u;
+        for (uint32_t r = 0; r < R; ++r) {
+            const uint32_t it = f + r;
+            if (it < fend) {
                 const uint32_t code = S.items[wave][it];
                 const uint32_t e = code & 0xffu, blk = code >> 8;
+                if (e != cur) {                             // a new (entry, run) segment
+                    if (cur != 0xffffffffu) {
+                        S.part[wave][cur_slot][0] = acc0;
+                        S.part[wave][cur_slot][1] = acc1;
+                        acc0 = acc1 = make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
+                    // the run's first item continues the previous lane's entry, or an entry starts here
+                    const bool cont = r == 0 && it > 0 && (S.items[wave][it - 1] & 0xffu) == e;
+                    cur = e;
+                    cur_slot = cont ? (uint32_t)(kWaveEnt + lane) : e;
+                }
                 const int lx = (int)(blk & 3u) * 4, ly = (int)(blk >> 2) * 4;
                 const float4 A = S.entp[wave][e], B = S.entq[wave][e];
                 float dy[4];
@@ -339,30 +360,43 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22).
                 const float a = A.z, b = A.w, c = B.x;
                 const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                S.ipart[wave][0][lane] = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv,
-                                                     -is * fmaf(a * a, da, a * b * db), -is * (a * c * db));
-                S.ipart[wave][1][lane] = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
+                acc0.x += k2 * fmaf(a, Hu, b * Hv);
+                acc0.y += k2 * c * Hv;
+                acc0.z += -is * fmaf(a * a, da, a * b * db);
+                acc0.w += -is * (a * c * db);
+                acc1.x += -is * fmaf(b * c, db, c * c * dc);
+                acc1.y += Cr;
+                acc1.z += Cg;
+                acc1.w += Cb;
             }
-            wave_sync();
-            // each entry adds its items of this round in order: blocks ascending
-            // whatever the rounds are, so the sum is reproducible
-            const uint32_t lo = max(s_e, rb), hi = min(s_e + n_e, rb + 64u);
-            for (uint32_t p = lo; p < hi; ++p) {
-                const float4 u0 = S.ipart[wave][0][p - rb], u1 = S.ipart[wave][1][p - rb];
-                acc0.x += u0.x; acc0.y += u0.y; acc0.z += u0.z; acc0.w += u0.w;
-                acc1.x += u1.x; acc1.y += u1.y; acc1.z += u1.z; acc1.w += u1.w;
-            }
-            wave_sync();                                    // ipart is rewritten next round
         }
+        if (cur != 0xffffffffu) {
+            S.part[wave][cur_slot][0] = acc0;
+            S.part[wave][cur_slot][1] = acc1;
+        }
+        wave_sync();
+        // entry e (lane e): its first run's partial, then those of the runs of lanes
+        // L0 + 1 .. L1 that continue it, in order
         if ((uint32_t)lane < ne && slot < capacity) {
-            part[2 * (size_t)slot] = acc0;
-            part[2 * (size_t)slot + 1] = acc1;
+            float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+            if (n_e > 0u) {                                 // always, for a box that meets the tile
+                s0 = S.part[wave][lane][0];
+                s1 = S.part[wave][lane][1];
+            }
+            const uint32_t L0 = s_e / R, L1 = n_e > 0u ? (s_e + n_e - 1u) / R : L0;
+            for (uint32_t L = L0 + 1u; L <= L1; ++L) {
+                const float4 u0 = S.part[wave][kWaveEnt + L][0], u1 = S.part[wave][kWaveEnt + L][1];
+                s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
+                s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+            }
+            part[2 * (size_t)slot] = s0;
+            part[2 * (size_t)slot + 1] = s1;
         }
         wave_sync();                                        // ent / items are rewritten next batch
     }
 }
 
-__global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
+__global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
                                                         const uint32_t *__restrict__ offsets,
@@ -409,7 +443,7 @@ __global__ __launch_bounds__(256) void k_render_sum_bwd(int W, int H, int tiles_
 // workgroup: the tile's dL/dI never leaves LDS, and the backward's first share
 // of entries is loaded while the forward runs.  Same results, bit for bit, as
 // k_render_sum_fwd<true> followed by k_render_sum_bwd.
-__global__ __launch_bounds__(256) void k_render_sum_fused(int W, int H, int tiles_x, int ntiles,
+__global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int W, int H, int tiles_x, int ntiles,
                                                           const float4 *__restrict__ records,
                                                           const uint2 *__restrict__ pixbox,
                                                           const uint32_t *__restrict__ offsets,
