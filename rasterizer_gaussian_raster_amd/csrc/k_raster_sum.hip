@@ -66,33 +66,63 @@ struct BwdLds {
 };
 constexpr size_t kPhaseLds = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : sizeof(BwdLds);
 
+// One lane's entry of a wave's share, loaded into registers.
+struct BwdEntry {
+    float4 p, q;
+    uint2 box;
+    uint32_t off;          // offsets[g]
+};
+
+// This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
+__device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0, uint32_t &ne) {
+    const uint32_t nb = min((uint32_t)kBwdBatch, rg.y - base);
+    const uint32_t q = (nb + 3) >> 2;
+    e0 = base + (uint32_t)(threadIdx.x >> 6) * q;
+    const uint32_t end = base + nb;
+    ne = e0 < end ? min(q, end - e0) : 0u;
+}
+
 // Forward of one tile for this thread's pixel (px, py) = pixel centre: the
 // three channel sums over the tile's list in list order.  The list is staged
-// 128 entries at a time; each entry's pixel box is tested against the four
+// 128 entries at a time, wave w loading the w-th quarter of the batch (the
+// backward's share layout); each entry's pixel box is tested against the four
 // 8x8 quadrants and the records are compacted, in list order, into one LDS
-// list per quadrant; wave w walks quadrant w's list.  On return other waves
+// list per quadrant; wave w walks quadrant w's list.  With `first`, this lane's
+// entry of the first batch (with its offsets[] value) is also kept there: the
+// backward's first share, loaded once for both passes.  On return other waves
 // may still read S: barrier before reusing it.
 __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg, const float4 *__restrict__ records,
                                              const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
-                                             float px, float py, float &ar, float &ag, float &ab) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+                                             const uint32_t *__restrict__ offsets, BwdEntry *first, float px,
+                                             float py, float &ar, float &ag, float &ab) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint64_t below = lanes_below();
     for (uint32_t base = rg.x; base < rg.y; base += kFwdBatch) {
-        const uint32_t idx = base + tid;
+        uint32_t e0, ne;
+        bwd_share(rg, base, e0, ne);
         uint32_t qm = 0;
         SumRec r;
         r.p = r.q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tid < kFwdBatch && idx < rg.y) {
-            const uint32_t g = vals[idx];
+        uint2 bx = make_uint2(1u, 0u);
+        uint32_t off = 0u;
+        if ((uint32_t)lane < ne) {
+            const uint32_t g = vals[e0 + lane];
             r.p = records[2 * g];
             r.q = records[2 * g + 1];
-            const uint2 bx = pixbox[g];
+            bx = pixbox[g];
+            if (first && base == rg.x) off = offsets[g];
             const int j0 = bx.x & 0xffff, i0 = bx.x >> 16, j1 = bx.y & 0xffff, i1 = bx.y >> 16;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int qx0 = x0 + (q & 1) * 8, qy0 = y0 + (q >> 1) * 8;
                 qm |= (j0 <= qx0 + 7 && j1 >= qx0 && i0 <= qy0 + 7 && i1 >= qy0) ? (1u << q) : 0u;
             }
+        }
+        if (first && base == rg.x) {
+            first->p = r.p;
+            first->q = r.q;
+            first->box = bx;
+            first->off = off;
         }
         uint32_t rank[4];
 #pragma unroll
@@ -105,9 +135,9 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if ((qm >> q) & 1u) {
-                int off = rank[q];
-                for (int w = 0; w < wave; ++w) off += S.wq[w][q];
-                S.lst[q][off] = r;
+                int o = rank[q];
+                for (int w = 0; w < wave; ++w) o += S.wq[w][q];
+                S.lst[q][o] = r;
             }
         }
         const int cnt = __builtin_amdgcn_readfirstlane(S.wq[0][wave] + S.wq[1][wave] + S.wq[2][wave] + S.wq[3][wave]);
@@ -201,7 +231,8 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
+    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, nullptr, nullptr, (float)pxi + 0.5f, (float)pyi + 0.5f,
+                 ar, ag, ab);
     sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
 }
 
@@ -214,22 +245,6 @@ __global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-// One lane's entry of a wave's share, loaded into registers.
-struct BwdEntry {
-    float4 p, q;
-    uint2 box;
-    uint32_t off;          // offsets[g]
-};
-
-// This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
-__device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0, uint32_t &ne) {
-    const uint32_t nb = min((uint32_t)kBwdBatch, rg.y - base);
-    const uint32_t q = (nb + 3) >> 2;
-    e0 = base + (uint32_t)(threadIdx.x >> 6) * q;
-    const uint32_t end = base + nb;
-    ne = e0 < end ? min(q, end - e0) : 0u;
-}
-
 __device__ __forceinline__ void bwd_load(uint32_t e0, uint32_t ne, const float4 *__restrict__ records,
                                          const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ offsets,
                                          const uint32_t *__restrict__ vals, BwdEntry &E) {
@@ -441,7 +456,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W,
 
 // Forward with the L2 loss, then the backward of the same tile, in one
 // workgroup: the tile's dL/dI never leaves LDS, and the backward's first share
-// of entries is loaded while the forward runs.  Same results, bit for bit, as
+// of entries is the forward's own first batch, kept in registers.  Same results, bit for bit, as
 // k_render_sum_fwd<true> followed by k_render_sum_bwd.
 __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int W, int H, int tiles_x, int ntiles,
                                                           const float4 *__restrict__ records,
@@ -464,13 +479,13 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
     const uint2 rg = ranges[t];
-    uint32_t e0, ne;
-    bwd_share(rg, rg.x, e0, ne);
-    BwdEntry E0;
-    bwd_load(e0, ne, records, pixbox, offsets, vals, E0);
+    BwdEntry E0;                                          // the backward's first share, loaded by the forward
+    E0.p = E0.q = make_float4(0.f, 0.f, 0.f, 0.f);
+    E0.box = make_uint2(1u, 0u);
+    E0.off = 0u;
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, (float)pxi + 0.5f,
-                 (float)pyi + 0.5f, ar, ag, ab);
+    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, offsets, &E0,
+                 (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     const float4 g = sum_fwd_store<true>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
     if (rg.x == rg.y) return;                             // uniform
     gp[gp_index(pxi - x0, pyi - y0)] = g;
