@@ -100,6 +100,37 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *t
     return off + inc - x;
 }
 
+// One barrier: the workgroup sums of x and y (u64) and the exclusive scan of c
+// (with its total).  sm64 [8] and sm32 [4] must not be reused without a barrier.
+__device__ __forceinline__ void block_sums2_scan(unsigned long long x, unsigned long long y, uint32_t c,
+                                                 unsigned long long &sx, unsigned long long &sy, uint32_t &excl,
+                                                 uint32_t &ctot, unsigned long long *sm64, uint32_t *sm32) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        x += __shfl_xor(x, o, 64);
+        y += __shfl_xor(y, o, 64);
+    }
+    const uint32_t inc = wave_scan_incl(c);
+    if (lane == 63) {
+        sm64[wave] = x;
+        sm64[4 + wave] = y;
+        sm32[wave] = inc;
+    }
+    __syncthreads();
+    sx = ((sm64[0] + sm64[1]) + sm64[2]) + sm64[3];
+    sy = ((sm64[4] + sm64[5]) + sm64[6]) + sm64[7];
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kBT / 64; ++w) {
+        const uint32_t v = sm32[w];
+        off += w < wave ? v : 0u;
+        tot += v;
+    }
+    excl = off + inc - c;
+    ctot = tot;
+}
+
 __device__ __forceinline__ uint32_t sat32(unsigned long long x) { return x > 0xffffffffull ? 0xffffffffu : (uint32_t)x; }
 
 // ---------------------------------------------------------------------------
@@ -198,19 +229,31 @@ __device__ __forceinline__ void digit_finish(const DigitAcc &a, int redundant, i
     B.part_b[tid] = a.b;
     B.part_t[tid] = a.t;
     __syncthreads();
-    for (int s = kBT >> 1; s >= q; s >>= 1) {          // fold threads with equal tid mod q
-        if (tid < s) {
-            const uint4 ob = B.part_b[tid + s], ot = B.part_t[tid + s];
-            uint4 &mb = B.part_b[tid], &mt = B.part_t[tid];
-            mb.x += ob.x; mb.y += ob.y; mb.z += ob.z; mb.w += ob.w;
-            mt.x += ot.x; mt.y += ot.y; mt.z += ot.z; mt.w += ot.w;
-        }
-        __syncthreads();
-    }
     uint32_t b = 0, t = 0;
-    if (tid < radix) {
-        b = reinterpret_cast<const uint32_t *>(B.part_b)[tid];    // uint4 (d>>2), component (d&3)
-        t = reinterpret_cast<const uint32_t *>(B.part_t)[tid];
+    if (q >= 16) {                                     // digit d: add the kBT / q threads that hold it
+        if (tid < radix) {
+            const uint32_t *pb = reinterpret_cast<const uint32_t *>(B.part_b);
+            const uint32_t *pt = reinterpret_cast<const uint32_t *>(B.part_t);
+            const int g4 = tid >> 2, comp = tid & 3;
+            for (int k = 0; k < kBT / q; ++k) {
+                b += pb[(g4 + k * q) * 4 + comp];
+                t += pt[(g4 + k * q) * 4 + comp];
+            }
+        }
+    } else {
+        for (int s = kBT >> 1; s >= q; s >>= 1) {      // fold threads with equal tid mod q
+            if (tid < s) {
+                const uint4 ob = B.part_b[tid + s], ot = B.part_t[tid + s];
+                uint4 &mb = B.part_b[tid], &mt = B.part_t[tid];
+                mb.x += ob.x; mb.y += ob.y; mb.z += ob.z; mb.w += ob.w;
+                mt.x += ot.x; mt.y += ot.y; mt.z += ot.z; mt.w += ot.w;
+            }
+            __syncthreads();
+        }
+        if (tid < radix) {
+            b = reinterpret_cast<const uint32_t *>(B.part_b)[tid];    // uint4 (d>>2), component (d&3)
+            t = reinterpret_cast<const uint32_t *>(B.part_t)[tid];
+        }
     }
     uint32_t all;
     const uint32_t start = block_exclusive_scan<uint32_t, kBT>(t, B.sm, &all);
@@ -231,7 +274,11 @@ struct ChunkLds {
 };
 
 // Scatters the chunk's `cc` keys to kout/vout at gbase[digit] + (rank of the
-// key among the chunk's keys of its digit), then advances gbase past the chunk.
+// key among the chunk's keys of its digit), then, unless it is the block's last
+// chunk, advances gbase past the chunk.  L.dstart[d] keeps the chunk-local
+// first slot of digit d afterwards.  With flat_base, key j of the chunk's
+// digit order goes to flat_base + j (gbase is ignored): the chunk is a whole
+// bucket sorted in place of its input range.
 // Key i sits in lane i % 64 of wave i / span, register (i % span) / 64, for
 // the `span` (a multiple of 64, span * 4 >= cc) the caller loaded with.
 // Entered and left by all threads with LDS in a settled state.
@@ -239,7 +286,7 @@ template <int PL>
 __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span, int shift, int bits,
                                               const uint32_t (&key)[PL], const uint32_t (&val)[PL],
                                               uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
-                                              uint32_t cap) {
+                                              uint32_t cap, bool last, uint32_t flat_base = 0xffffffffu) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int radix = 1 << bits;
     const uint32_t dmask = (uint32_t)(radix - 1);
@@ -272,6 +319,7 @@ __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span,
     const uint32_t ds = block_exclusive_scan<uint32_t, kBT>(tot, L.sm, &all);
     if (tid < radix) {
         L.dstart[tid] = ds;
+        if (flat_base != 0xffffffffu) L.gbase[tid] = flat_base + ds;
         L.cnt[0][tid] = ds;
         L.cnt[1][tid] = ds + c0;
         L.cnt[2][tid] = ds + c0 + c1;
@@ -300,6 +348,7 @@ __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span,
             vout[pos] = L.sv[j];
         }
     }
+    if (last) return;                                     // uniform
     __syncthreads();
     if (tid < radix) L.gbase[tid] += tot;
     __syncthreads();
@@ -502,10 +551,8 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
             before += tid + k * kBT < (int)blockIdx.x ? v[k] : 0ull;
         }
         unsigned long long tb, ta;
-        block_exclusive_scan<unsigned long long, kBT>(before, sm64, &tb);
-        block_exclusive_scan<unsigned long long, kBT>(all, sm64 + 4, &ta);
-        uint32_t tot;
-        const uint32_t local = block_exclusive_scan<uint32_t, kBT>(c, smc, &tot);
+        uint32_t local, tot;
+        block_sums2_scan(before, all, c, tb, ta, local, tot, sm64, smc);
         if (tid < ns) offsets[first + tid] = sat32(tb + local);
         if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num);
         M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
@@ -596,7 +643,7 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
                 }
             }
         }
-        scatter_chunk(L, cc, span, shift, bits, key, val, kout, vout, M);
+        scatter_chunk(L, cc, span, shift, bits, key, val, kout, vout, M, cs + (uint32_t)kChunk >= tot);
     }
 }
 
@@ -658,7 +705,7 @@ __global__ __launch_bounds__(kBT) void k_scatter(const uint32_t *__restrict__ ki
     const DigitAcc acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
     digit_finish(acc, table_redundant, bits, L.gbase, B);
     const int cc = (int)min((uint32_t)CH, M - base);
-    scatter_chunk(L, cc, SPAN, shift, bits, key, val, kout, vout, M);
+    scatter_chunk(L, cc, SPAN, shift, bits, key, val, kout, vout, M, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -681,6 +728,29 @@ __global__ __launch_bounds__(kBT) void k_bucket_sort(const uint32_t *__restrict_
     const int radix = 1 << lo_bits;
     const uint32_t M = hdr->m_eff;
     const uint32_t s0 = M ? bucket_start[blockIdx.x] : 0u, s1 = M ? bucket_start[blockIdx.x + 1] : 0u;
+    if (s1 - s0 <= (uint32_t)CH) {                                // uniform: the bucket is one chunk
+        if (s1 == s0) return;                                     // its tiles keep the cleared (0, 0)
+        const int cc = (int)(s1 - s0);
+        const int span = ((cc + kBT - 1) / kBT) * 64;
+        const int iters = span >> 6;
+        uint32_t key[PL], val[PL];
+#pragma unroll
+        for (int it = 0; it < PL; ++it) {
+            if (it < iters) {
+                const int idx = wave * span + it * 64 + lane;
+                const uint32_t q = s0 + (uint32_t)(idx < cc ? idx : cc - 1);
+                key[it] = kin[q];
+                val[it] = vin[q];
+            }
+        }
+        scatter_chunk(L, cc, span, 0, lo_bits, key, val, kout, vout, M, true, s0);
+        if (tid < radix) {                                        // the digit starts are the tile ranges
+            const int t = (blockIdx.x << lo_bits) + tid;
+            const uint32_t a = L.dstart[tid], e = tid + 1 < radix ? L.dstart[tid + 1] : (uint32_t)cc;
+            if (t < ntiles) ranges[t] = e > a ? make_uint2(s0 + a, s0 + e) : make_uint2(0u, 0u);
+        }
+        return;
+    }
     if (tid < radix) hist[tid] = 0u;
     __syncthreads();
     for (uint32_t base = s0; base < s1; base += CH) {            // uniform
@@ -718,7 +788,7 @@ __global__ __launch_bounds__(kBT) void k_bucket_sort(const uint32_t *__restrict_
                 val[it] = vin[q];
             }
         }
-        scatter_chunk(L, cc, span, 0, lo_bits, key, val, kout, vout, M);
+        scatter_chunk(L, cc, span, 0, lo_bits, key, val, kout, vout, M, base + (uint32_t)CH >= s1);
     }
 }
 
