@@ -1,13 +1,14 @@
 """Benchmark: 768x512 synthetic target, 50,000 2D Gaussians, accumulated-sum rendering.
 
-One "step" is the whole hot path on the GPU: gi_preprocess_bin_sort (preprocess + tile binning)
--> gi_render_fwd_bwd_l2 (per tile: forward raster, L2 loss gradient, backward raster) ->
-gi_adam_step_pairs (gather of the per-pair gradients + Adam, loss reduction).  `value` is fwd+bwd
-training steps per second on one MI355X with every input resident in HBM.  Also reported: render
-FPS (preprocess + bin/sort + raster) and cached-raster FPS (raster only, binning reused); kernel
-times from HIP events on the launch stream over a separate pass of the same step (and of the
-separate forward / backward kernels on the same binning); the roofline of the dominant kernel;
-and the CPU oracle timed on a bounded pixel sample of the same workload.
+One "step" is the whole hot path on the GPU, one gi_fit_step_sum call: tile binning, the fused
+per-tile forward raster + L2 loss gradient + backward raster, and Adam with the gather of the
+per-pair gradients (which also reduces the loss and sets up the updated parameters for the next
+step's binning).  `value` is fwd+bwd training steps per second on one MI355X with every input
+resident in HBM.  Also reported: render FPS (preprocess + bin/sort + raster) and cached-raster FPS
+(raster only, binning reused); kernel times from HIP events on the launch stream over passes of the
+fused raster kernel (and of the separate forward / backward kernels) on the trained parameters'
+binning; the roofline of the dominant kernel; and the CPU oracle timed on a bounded pixel sample of
+the same workload.
 
 usage: python bench.py [--gpus 1] [--steps 2800] [--warmup 50] [--workload NAME] [--no-cpu-baseline]
 """
@@ -160,14 +161,6 @@ def main():
     for _ in range(args.warmup):
         fit.step()
     torch.cuda.synchronize()
-    # kernel timing pass (eager steps): HIP events on the launch stream bracket the fused raster kernel
-    nk = max(20, min(args.steps, 500))
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[E() for _ in range(2)] for _ in range(nk)]
-    for k in range(nk):
-        fit.step(ev[k])
-    torch.cuda.synchronize()
-    fused_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])
     # the timed region: K eager steps
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -178,20 +171,7 @@ def main():
     assert M_now <= r.capacity, "tile-pair capacity exceeded during the timed run"
     ms_step = 1e3 * t_train / args.steps
     final_loss = float(fit.loss.item())
-    # the separate forward (with L2) and backward kernels on the same binning, for reference
-    ev2 = [[E() for _ in range(3)] for _ in range(nk)]
-    for k in range(nk):
-        ev2[k][0].record()
-        r.forward_l2(fit.target, fit.dL)
-        ev2[k][1].record()
-        r.backward(fit.dL, None)
-        ev2[k][2].record()
-    torch.cuda.synchronize()
-    fwd_ms = np.array([ev2[k][0].elapsed_time(ev2[k][1]) for k in range(nk)])
-    bwd_ms = np.array([ev2[k][1].elapsed_time(ev2[k][2]) for k in range(nk)])
-    log(f"[bench] train: {ms_step:.4f} ms/step, fused fwd+bwd {np.median(fused_ms)*1e3:.1f} us "
-        f"(separate: fwd {np.median(fwd_ms)*1e3:.1f} us, bwd {np.median(bwd_ms)*1e3:.1f} us), "
-        f"loss {final_loss:.4e}")
+    log(f"[bench] train: {ms_step:.4f} ms/step, loss {final_loss:.4e}")
 
     # ---------------- render-only: preprocess + bin/sort + raster, and raster alone ----------------
     rend = Raster(W, H, wl.n)
@@ -199,6 +179,28 @@ def main():
     M = rend.bin(sync=True)
     rend.set_capacity(int(M * 1.5) + 4096)
     rend.bin(sync=True, order=True)
+    # kernel timing: HIP events on the launch stream around the fused raster kernel of the training
+    # step, and around the separate forward (with L2) and backward kernels, on this binning
+    nk = max(20, min(args.steps, 500))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    dL = torch.empty_like(target)
+    ev = [[E() for _ in range(5)] for _ in range(nk)]
+    for k in range(nk):
+        ev[k][0].record()
+        rend.forward_backward_l2(target)
+        ev[k][1].record()
+    for k in range(nk):
+        ev[k][2].record()
+        rend.forward_l2(target, dL)
+        ev[k][3].record()
+        rend.backward(dL, None)
+        ev[k][4].record()
+    torch.cuda.synchronize()
+    fused_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])
+    fwd_ms = np.array([ev[k][2].elapsed_time(ev[k][3]) for k in range(nk)])
+    bwd_ms = np.array([ev[k][3].elapsed_time(ev[k][4]) for k in range(nk)])
+    log(f"[bench] fused fwd+bwd {np.median(fused_ms)*1e3:.1f} us (separate: fwd {np.median(fwd_ms)*1e3:.1f} us, "
+        f"bwd {np.median(bwd_ms)*1e3:.1f} us)")
     reps = max(50, args.steps // 4)
 
     def loop_time(fn):
@@ -263,8 +265,8 @@ def main():
         "cached_raster_fps": round(1.0 / t_cached, 1),
         "fit_seconds_2800_steps": round(2800 * ms_step / 1e3, 3),
         "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
-                  "kernels_us / roofline: HIP events on the launch stream around the raster kernel(s) over "
-                  "a separate pass of the same step (fused) and of the separate kernels on the same binning",
+                  "kernels_us / roofline: HIP events on the launch stream around the fused raster kernel of the "
+                  "training step and the separate forward / backward kernels, on the trained parameters' binning",
         "final_loss": final_loss,
         "kernels_us": {"render_fwd_bwd_fused": round(fused_s * 1e6, 2), "render_fwd_l2": round(fwd_s * 1e6, 2),
                        "render_bwd": round(bwd_s * 1e6, 2)},

@@ -347,6 +347,72 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
                              const int32_t *d_step, const float *loss_partials, int64_t loss_count,
                              float *d_loss, void *stream);
 
+/*
+ * gi_fit_step_sum -- one training step of the accumulated-sum fit (sum mode,
+ *   L2 loss, Adam) in one call: the tile binning of the parameters, the fused
+ *   forward + L2 gradient + backward (gi_render_fwd_bwd_l2), and the Adam step
+ *   with the gathered gradient (gi_adam_step_pairs, with the loss reduced into
+ *   d_loss).  The Adam kernel then goes on to set up the updated parameters
+ *   for the next step's binning -- what gi_preprocess_bin_sort's preprocess
+ *   kernel does (records, pixbox, counts, the binning's group totals and digit
+ *   histogram in the bin workspace, ranges cleared) -- so that the next call can
+ *   start with the sort (GI_FIT_PREPARED): one launch and one pass over the
+ *   parameters fewer per step.  Every result is bit-identical to the sequence
+ *   gi_preprocess_bin_sort, gi_render_fwd_bwd_l2, gi_adam_step_pairs.
+ *   Reading: "FlashImgs" (train --loss l2, max_steps; Performance) and fvdb's
+ *   Adam (GaussianSplatOptimizer), run as one step.
+ *
+ *   b         the buffers (gi_fit_buffers), as in the calls above; after the
+ *             call params / m / v hold the updated values, image and *d_loss
+ *             the forward of this step (before the update), offsets / keys /
+ *             vals / d_num this step's binning, records / pixbox / counts the
+ *             set-up of the UPDATED parameters, and ranges are cleared (ready for
+ *             the next binning).
+ *   hp        Adam hyperparameters (host), as gi_adam_step_pairs'.
+ *   step, d_step  Adam's step t, as gi_adam_step_pairs'.
+ *   flags     GI_FIT_PREPARED: the previous gi_fit_step_sum on the same buffers,
+ *             desc, n and capacity left the set-up (skip the preprocess kernel);
+ *             without it the call preprocesses params first.  Only valid if
+ *             params were not changed in between.
+ *             GI_FIT_ORDER: also (re)write b->tile_order from this binning (as
+ *             gi_bin_sort's tile_order).  When b->tile_order is not NULL the raster
+ *             pass takes the tiles in that order, so it must hold a valid order
+ *             (from an earlier call with GI_FIT_ORDER, or gi_bin_sort).
+ *   Errors as the calls above; a binning overflow (M > capacity) shows in
+ *   *d_num and gives a zero gradient (the Adam step still runs).
+ */
+#define GI_FIT_PREPARED 1u
+#define GI_FIT_ORDER 2u
+
+typedef struct gi_fit_buffers {
+    float *params, *m, *v;          /* device float [n][8]: parameters and Adam moments, in place */
+    const float *target;            /* device float [3][H][W] */
+    float *image;                   /* device float [3][H][W] out */
+    float *loss_partials;           /* device float [T] (scratch) */
+    float *d_loss;                  /* device float [1] out, or NULL */
+    float *records;                 /* device float [n][8] */
+    uint16_t *pixbox;               /* device uint16 [n][4] */
+    uint32_t *counts;               /* device uint32 [n] */
+    uint32_t *offsets;              /* device uint32 [n+1] */
+    uint32_t *keys, *vals;          /* device uint32 [capacity] */
+    uint32_t *ranges;               /* device uint32 [T][2] */
+    uint32_t *tile_order;           /* device uint32 [T], or NULL */
+    uint32_t *d_num;                /* device uint32 [1] out: M */
+    int64_t capacity;
+    void *bin_workspace;            /* gi_bin_sort_workspace_bytes(desc, n, capacity) bytes */
+    size_t bin_workspace_bytes;
+    void *bwd_workspace;            /* gi_render_bwd_workspace_bytes(desc, n, capacity) bytes */
+    size_t bwd_workspace_bytes;
+} gi_fit_buffers;
+
+typedef struct gi_adam_hparams {
+    float lr[8];                    /* per parameter slot */
+    double beta1, beta2, eps;
+} gi_adam_hparams;
+
+gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
+                          int32_t step, const int32_t *d_step, uint32_t flags, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

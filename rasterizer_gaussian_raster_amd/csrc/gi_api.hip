@@ -224,6 +224,47 @@ gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *reco
                                                   loss_partials, workspace, as_stream(stream)));
 }
 
+gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
+                          int32_t step, const int32_t *d_step, uint32_t flags, void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || !hp || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER)) != 0u) return GI_ERR_INVALID_ARG;
+    if (!d_step && step < 1) return GI_ERR_INVALID_ARG;
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps >= 0.0))
+        return GI_ERR_INVALID_ARG;
+    if (!preprocess_args_ok(desc, n, b->params, nullptr, b->records, nullptr, b->pixbox, b->counts) ||
+        !bin_args_ok(desc, n, b->pixbox, b->counts, b->offsets, b->keys, b->vals, b->ranges, b->capacity, b->d_num,
+                     b->bin_workspace, b->bin_workspace_bytes))
+        return GI_ERR_INVALID_ARG;
+    if ((flags & GI_FIT_ORDER) && !b->tile_order) return GI_ERR_INVALID_ARG;
+    if (!b->target || !b->image || !aligned16(b->image) || !b->loss_partials || !b->bwd_workspace ||
+        !aligned256(b->bwd_workspace))
+        return GI_ERR_INVALID_ARG;
+    const int W = desc->width, H = desc->height;
+    if (b->bwd_workspace_bytes < gi::make_bwd_plan(W, H, b->capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!b->m || !b->v || !aligned16(b->m) || !aligned16(b->v))) return GI_ERR_INVALID_ARG;
+    const gi::BinPlan plan = gi::make_bin_plan((int)n, W, H, b->capacity);
+    const gi::BinHist hist = gi::bin_hist(plan, b->bin_workspace);
+    unsigned long long *groups = gi::bin_group_sums(plan, b->bin_workspace);
+    hipStream_t s = as_stream(stream);
+    hipError_t e = hipSuccess;
+    if (!(flags & GI_FIT_PREPARED))
+        e = gi::launch_preprocess((int)n, W, H, b->params, nullptr, b->records, nullptr, b->pixbox, b->counts, groups,
+                                  b->ranges, hist, s);
+    if (e == hipSuccess)
+        e = gi::launch_bin_sort(plan, b->pixbox, b->counts, b->offsets, b->keys, b->vals, b->ranges,
+                                (flags & GI_FIT_ORDER) ? b->tile_order : nullptr, b->d_num, b->bin_workspace, s, true);
+    if (e == hipSuccess)
+        e = gi::launch_render_sum_fused(W, H, b->records, b->pixbox, b->offsets, b->ranges, b->tile_order, b->vals,
+                                        b->capacity, b->image, b->target, nullptr, b->loss_partials, b->bwd_workspace,
+                                        s);
+    if (e == hipSuccess)
+        e = gi::launch_adam_preprocess((int)n, W, H, b->offsets, b->capacity, b->bwd_workspace, b->params, b->m, b->v,
+                                       gi::make_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, step, d_step),
+                                       b->records, b->pixbox, b->counts, groups, b->ranges, hist, b->loss_partials,
+                                       3ll * W * H, b->d_loss, s);
+    return hip_status(e);
+}
+
 size_t gi_loss_workspace_bytes(int64_t count) { return count < 1 ? 0 : gi::loss_workspace_bytes(count); }
 
 gi_status gi_loss_l2(int64_t count, const float *image, const float *target, float *dL_dimage, float *d_loss,

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gi_launch.hpp"
+
 namespace gi {
 
 constexpr int kTile = 16;            // tile edge, pixels (fvdb config: tile_size = 16)
@@ -53,6 +55,50 @@ __device__ __forceinline__ void adam_bias(double b1, double b2, int t, float &in
     const int tt = t < 1 ? 1 : t;
     inv_bc1 = (float)(1.0 / (1.0 - powi_f64(b1, tt)));
     inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - powi_f64(b2, tt)));
+}
+
+// One Adam update of a scalar: the same expression in every optimizer kernel.
+__device__ __forceinline__ void adam_update(float &p, float g, float &m, float &v, float lr, const AdamHP &a,
+                                            float inv_bc1, float inv_sqrt_bc2) {
+    m = fmaf(a.b1, m, a.omb1 * g);
+    v = fmaf(a.b2, v, a.omb2 * g * g);
+    p -= lr * (m * inv_bc1) / (sqrtf(v) * inv_sqrt_bc2 + a.eps);
+}
+
+// Adds the pair slots q in [o0, o1) (part[2q], part[2q + 1]) into (a, b) in
+// ascending q; four slots are loaded at a time so that their latencies overlap.
+__device__ __forceinline__ void gather_slots(const float4 *__restrict__ part, uint32_t o0, uint32_t o1, float4 &a,
+                                             float4 &b) {
+    for (uint32_t q = o0; q < o1; q += 4) {
+        float4 u[4], w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t qq = min(q + (uint32_t)k, o1 - 1u);     // in range; repeats are not added
+            u[k] = part[2 * (size_t)qq];
+            w[k] = part[2 * (size_t)qq + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (q + (uint32_t)k < o1) {
+                a.x += u[k].x; a.y += u[k].y; a.z += u[k].z; a.w += u[k].w;
+                b.x += w[k].x; b.y += w[k].y; b.z += w[k].z; b.w += w[k].w;
+            }
+    }
+}
+
+// Sum of the per-tile partials in a fixed order, divided by the entry count
+// (one workgroup of 256; sm: 256 doubles of LDS).
+__device__ __forceinline__ void loss_reduce_block(int nparts, const float *__restrict__ part, double inv_count,
+                                                  float *__restrict__ loss, double *sm) {
+    double s = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *loss = (float)(sm[0] * inv_count);
 }
 
 // 2^x with the hardware transcendental (v_exp_f32).

@@ -17,12 +17,29 @@ struct BinHist {
     int ncols_cap;
 };
 
+// Adam hyperparameters as the kernels take them (1 - beta formed in fp64 on the host).
+struct AdamHP {
+    float lr[8];
+    float b1, omb1, b2, omb2, eps;
+    double b1d, b2d;                 // for the bias corrections (formed on the device)
+    int step;                        // used when d_step is NULL
+    const int32_t *d_step;           // device step count (graph replays), or NULL
+};
+AdamHP make_adam_hp(const float *lr, double beta1, double beta2, double eps, int step, const int32_t *d_step);
+
 // k_preprocess.hip
 // group_sums / ranges (or NULL): the binning's group sums and cleared ranges (gi_preprocess_bin_sort),
 // and the digit histogram when hist.table is set.
 hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
                              float *opacity, uint16_t *pixbox, uint32_t *counts, unsigned long long *group_sums,
                              uint32_t *ranges, BinHist hist, hipStream_t s);
+
+// Adam from the pair slots (as launch_adam_pairs), then the set-up of the updated Gaussians
+// for the next binning (as launch_preprocess with group_sums); d_loss: also the loss reduction.
+hipError_t launch_adam_preprocess(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *bwd_ws,
+                                  float *p, float *m, float *v, const AdamHP &a, float *records, uint16_t *pixbox,
+                                  uint32_t *counts, unsigned long long *group_sums, uint32_t *ranges, BinHist hist,
+                                  const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s);
 
 // k_binning.hip
 struct BinPlan {

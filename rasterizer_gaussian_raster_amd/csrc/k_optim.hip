@@ -75,10 +75,13 @@ struct AdamBias {
 
 __device__ __forceinline__ void adam_one(float &p, float &g, float &m, float &v, float lr, const AdamArgs &a,
                                          const AdamBias &c) {
-    m = fmaf(a.b1, m, a.omb1 * g);
-    v = fmaf(a.b2, v, a.omb2 * g * g);
-    const float den = sqrtf(v) * c.inv_sqrt_bc2 + a.eps;
-    p -= lr * (m * c.inv_bc1) / den;
+    AdamHP h{};
+    h.b1 = a.b1;
+    h.omb1 = a.omb1;
+    h.b2 = a.b2;
+    h.omb2 = a.omb2;
+    h.eps = a.eps;
+    adam_update(p, g, m, v, lr, h, c.inv_bc1, c.inv_sqrt_bc2);
 }
 
 // 4 consecutive scalars per thread (row_len divisible by 4, 16-byte aligned arrays).

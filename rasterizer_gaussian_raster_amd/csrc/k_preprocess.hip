@@ -12,21 +12,20 @@
 
 namespace gi {
 
-// One Gaussian: record, pixel box (also returned in *box_out), tile count (returned), opacity.
-__device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const float4 *__restrict__ params,
-                                                   const float *__restrict__ logit, float4 *__restrict__ records,
-                                                   float *__restrict__ opacity, uint2 *__restrict__ pixbox,
-                                                   uint32_t *__restrict__ counts, uint2 *box_out) {
-    const float4 p0 = params[2 * g];       // mux, muy, l11, l21
-    const float4 p1 = params[2 * g + 1];   // l22, cr, cg, cb
+// One Gaussian's set-up from its parameters p0 = (mux, muy, l11, l21),
+// p1 = (l22, cr, cg, cb) and, when has_logit, its logit.
+struct Prep {
+    float4 rp, rq;     // record
+    uint2 box;         // packed pixel box
+    uint32_t cnt;      // tiles covered
+    float opacity;
+};
+
+__device__ __forceinline__ Prep preprocess_gaussian(float4 p0, float4 p1, bool has_logit, float lam, int W, int H) {
     const float l11 = p0.z, l21 = p0.w, l22 = p1.x;
     bool ok = isfinite(p0.x) && isfinite(p0.y) && isfinite(l11) && isfinite(l21) && isfinite(l22) &&
               isfinite(p1.y) && isfinite(p1.z) && isfinite(p1.w);
-    float lam = 0.0f;
-    if (logit) {
-        lam = logit[g];
-        ok = ok && isfinite(lam);
-    }
+    if (has_logit) ok = ok && isfinite(lam);
     ok = ok && l11 != 0.0f && l22 != 0.0f;
     float a = 0.0f, b = 0.0f, c = 0.0f;
     if (ok) {
@@ -38,8 +37,9 @@ __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const fl
         b = k * kScale;
         c = i22 * kScale;
     }
-    uint32_t cnt = 0;
-    uint2 box = make_uint2(1u | (1u << 16), 0u);   // empty: j0 = i0 = 1, j1 = i1 = 0
+    Prep o;
+    o.cnt = 0;
+    o.box = make_uint2(1u | (1u << 16), 0u);   // empty: j0 = i0 = 1, j1 = i1 = 0
     if (ok) {
         const float rx = 3.0f * fabsf(l11) + kPad;
         const float ry = 3.0f * sqrtf(fmaf(l21, l21, l22 * l22)) + kPad;
@@ -50,22 +50,56 @@ __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const fl
         const float fi1 = fminf(floorf(cy + ry), (float)(H - 1));
         if (fj0 <= fj1 && fi0 <= fi1) {
             const uint32_t j0 = (uint32_t)fj0, j1 = (uint32_t)fj1, i0 = (uint32_t)fi0, i1 = (uint32_t)fi1;
-            box = make_uint2(j0 | (i0 << 16), j1 | (i1 << 16));
-            cnt = ((j1 >> 4) - (j0 >> 4) + 1) * ((i1 >> 4) - (i0 >> 4) + 1);
+            o.box = make_uint2(j0 | (i0 << 16), j1 | (i1 << 16));
+            o.cnt = ((j1 >> 4) - (j0 >> 4) + 1) * ((i1 >> 4) - (i0 >> 4) + 1);
         }
     } else {
         a = b = c = 0.0f;
     }
-    records[2 * g] = ok ? make_float4(p0.x, p0.y, a, b) : make_float4(0.f, 0.f, 0.f, 0.f);
-    records[2 * g + 1] = ok ? make_float4(c, p1.y, p1.z, p1.w) : make_float4(0.f, 0.f, 0.f, 0.f);
-    pixbox[g] = box;
-    counts[g] = cnt;
-    *box_out = box;
-    if (opacity) {
-        const float l = fminf(lam, kLogitMax);
-        opacity[g] = ok ? 1.0f / (1.0f + expf(-l)) : 0.0f;
+    o.rp = ok ? make_float4(p0.x, p0.y, a, b) : make_float4(0.f, 0.f, 0.f, 0.f);
+    o.rq = ok ? make_float4(c, p1.y, p1.z, p1.w) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float l = fminf(lam, kLogitMax);
+    o.opacity = ok ? 1.0f / (1.0f + expf(-l)) : 0.0f;
+    return o;
+}
+
+// One Gaussian: record, pixel box (also returned in *box_out), tile count (returned), opacity.
+__device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const float4 *__restrict__ params,
+                                                   const float *__restrict__ logit, float4 *__restrict__ records,
+                                                   float *__restrict__ opacity, uint2 *__restrict__ pixbox,
+                                                   uint32_t *__restrict__ counts, uint2 *box_out) {
+    const Prep o = preprocess_gaussian(params[2 * g], params[2 * g + 1], logit != nullptr, logit ? logit[g] : 0.0f,
+                                       W, H);
+    records[2 * g] = o.rp;
+    records[2 * g + 1] = o.rq;
+    pixbox[g] = o.box;
+    counts[g] = o.cnt;
+    if (opacity) opacity[g] = o.opacity;
+    *box_out = o.box;
+    return o.cnt;
+}
+
+// The binning's first step for one 256-Gaussian group, given each thread's
+// tile count c and box: the group's pair total, its first-pass digit histogram
+// (when hist.table is set).  h: 256 u32 of LDS, cleared by the caller before
+// the barrier this function starts with; ws: 4 u64 of LDS.
+__device__ __forceinline__ void group_totals(uint32_t c, uint2 box, unsigned long long *__restrict__ group_sums,
+                                             BinHist hist, uint32_t *h, unsigned long long *ws) {
+    const int radix = 1 << hist.bits;
+    unsigned long long x = c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = x;
+    __syncthreads();                                      // also publishes the cleared histogram
+    if (threadIdx.x == 0) group_sums[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    if (hist.table) {                                     // uniform
+        hist_add_pairs(h, c, box, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
+        __syncthreads();
+        if ((int)threadIdx.x < radix) {
+            if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + threadIdx.x] = h[threadIdx.x];
+            else hist.table[(size_t)threadIdx.x * hist.ncols_cap + blockIdx.x] = h[threadIdx.x];
+        }
     }
-    return cnt;
 }
 
 // With group_sums (binning in the same call): also the sum of each 256-Gaussian
@@ -78,29 +112,14 @@ __global__ __launch_bounds__(256) void k_preprocess(int n, int W, int H, const f
                                                     unsigned long long *__restrict__ group_sums,
                                                     uint2 *__restrict__ ranges, int ntiles, BinHist hist) {
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
-    uint2 box;
+    uint2 box = make_uint2(1u, 0u);
     if (group_sums) {
         __shared__ unsigned long long ws[4];
         __shared__ uint32_t h[256];
-        const int radix = 1 << hist.bits;
-        if (hist.table && (int)threadIdx.x < radix) h[threadIdx.x] = 0u;
+        if (hist.table && (int)threadIdx.x < (1 << hist.bits)) h[threadIdx.x] = 0u;
         for (int t = g; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
         const uint32_t c = g < n ? preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box) : 0u;
-        // block sum of the counts (u64), waves then the workgroup
-        unsigned long long x = c;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-        if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = x;
-        __syncthreads();                                  // also publishes the cleared histogram
-        if (threadIdx.x == 0) group_sums[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
-        if (hist.table) {                                 // uniform
-            hist_add_pairs(h, c, box, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
-            __syncthreads();
-            if ((int)threadIdx.x < radix) {
-                if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + threadIdx.x] = h[threadIdx.x];
-                else hist.table[(size_t)threadIdx.x * hist.ncols_cap + blockIdx.x] = h[threadIdx.x];
-            }
-        }
+        group_totals(c, box, group_sums, hist, h, ws);
         return;
     }
     if (g >= n) return;
@@ -117,6 +136,84 @@ hipError_t launch_preprocess(int n, int W, int H, const float *params, const flo
                                                   reinterpret_cast<float4 *>(records), opacity,
                                                   reinterpret_cast<uint2 *>(pixbox), counts, group_sums,
                                                   reinterpret_cast<uint2 *>(ranges), ntiles, hist);
+    return hipGetLastError();
+}
+
+// Adam on each Gaussian's 8 parameters with the gradient gathered from its
+// pair slots (the arithmetic of k_adam_pairs, so the same bits), then the
+// set-up of the updated Gaussian for the next binning, as k_preprocess with
+// group_sums: record, pixel box, tile count, the group's pair total and digit
+// histogram, and the tile ranges cleared.  With `loss`, the last workgroup
+// reduces the loss partials of the raster pass instead.
+__global__ __launch_bounds__(256) void k_adam_preprocess(int n, int W, int H, int ngroups,
+                                                         const uint32_t *__restrict__ offsets, uint32_t capacity,
+                                                         const float4 *__restrict__ part, float4 *__restrict__ p,
+                                                         float4 *__restrict__ m, float4 *__restrict__ v, AdamHP a,
+                                                         float4 *__restrict__ records, uint2 *__restrict__ pixbox,
+                                                         uint32_t *__restrict__ counts,
+                                                         unsigned long long *__restrict__ group_sums,
+                                                         uint2 *__restrict__ ranges, int ntiles, BinHist hist,
+                                                         const float *__restrict__ loss_part, int nparts,
+                                                         double inv_count, float *__restrict__ loss) {
+    if (loss && (int)blockIdx.x == ngroups) {
+        __shared__ double sm[256];
+        loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
+        return;
+    }
+    __shared__ unsigned long long ws[4];
+    __shared__ uint32_t h[256];
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (hist.table && (int)threadIdx.x < (1 << hist.bits)) h[threadIdx.x] = 0u;
+    for (int t = g; t < ntiles; t += ngroups * 256) ranges[t] = make_uint2(0u, 0u);
+    uint32_t c = 0u;
+    uint2 box = make_uint2(1u, 0u);
+    if (g < n) {
+        float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
+        const int t = a.d_step ? *a.d_step : a.step;
+        const bool ok = offsets[n] <= capacity;           // else the binning overflowed: zero gradient
+        const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
+        float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+        gather_slots(part, o0, o1, g0, g1);
+        float c1, c2;
+        adam_bias(a.b1d, a.b2d, t, c1, c2);
+        adam_update(P0.x, g0.x, M0.x, V0.x, a.lr[0], a, c1, c2);
+        adam_update(P0.y, g0.y, M0.y, V0.y, a.lr[1], a, c1, c2);
+        adam_update(P0.z, g0.z, M0.z, V0.z, a.lr[2], a, c1, c2);
+        adam_update(P0.w, g0.w, M0.w, V0.w, a.lr[3], a, c1, c2);
+        adam_update(P1.x, g1.x, M1.x, V1.x, a.lr[4], a, c1, c2);
+        adam_update(P1.y, g1.y, M1.y, V1.y, a.lr[5], a, c1, c2);
+        adam_update(P1.z, g1.z, M1.z, V1.z, a.lr[6], a, c1, c2);
+        adam_update(P1.w, g1.w, M1.w, V1.w, a.lr[7], a, c1, c2);
+        p[2 * g] = P0; p[2 * g + 1] = P1;
+        m[2 * g] = M0; m[2 * g + 1] = M1;
+        v[2 * g] = V0; v[2 * g + 1] = V1;
+        const Prep o = preprocess_gaussian(P0, P1, false, 0.0f, W, H);
+        records[2 * g] = o.rp;
+        records[2 * g + 1] = o.rq;
+        pixbox[g] = o.box;
+        counts[g] = o.cnt;
+        c = o.cnt;
+        box = o.box;
+    }
+    group_totals(c, box, group_sums, hist, h, ws);
+}
+
+hipError_t launch_adam_preprocess(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *bwd_ws,
+                                  float *p, float *m, float *v, const AdamHP &a, float *records, uint16_t *pixbox,
+                                  uint32_t *counts, unsigned long long *group_sums, uint32_t *ranges, BinHist hist,
+                                  const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s) {
+    const int ngroups = (n + 255) / 256;
+    const int nb = ngroups + (d_loss ? 1 : 0);
+    if (nb == 0) return hipSuccess;
+    const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+    const BwdPlan pl = make_bwd_plan(W, H, capacity);
+    k_adam_preprocess<<<nb, 256, 0, s>>>(
+        n, W, H, ngroups, offsets, (uint32_t)capacity,
+        reinterpret_cast<const float4 *>(static_cast<const char *>(bwd_ws) + pl.off_part),
+        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a,
+        reinterpret_cast<float4 *>(records), reinterpret_cast<uint2 *>(pixbox), counts, group_sums,
+        reinterpret_cast<uint2 *>(ranges), ntiles, hist, loss_partials, ntiles,
+        loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss);
     return hipGetLastError();
 }
 

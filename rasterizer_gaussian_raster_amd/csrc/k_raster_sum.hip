@@ -159,21 +159,6 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
     }
 }
 
-// Sum of the per-tile partials in a fixed order, divided by the entry count.
-// sm: 256 doubles of LDS.
-__device__ __forceinline__ void loss_reduce_block(int nparts, const float *__restrict__ part, double inv_count,
-                                                  float *__restrict__ loss, double *sm) {
-    double s = 0.0;
-    for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
-    sm[threadIdx.x] = s;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *loss = (float)(sm[0] * inv_count);
-}
-
 // Writes the image (and the L2 terms) of this thread's pixel and, with a
 // target, the tile's sum of squared residuals (in a fixed order).  Returns the
 // pixel's dL/dI (zero off the image).  Contains a workgroup barrier when L2.
@@ -494,27 +479,6 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
                  part);
 }
 
-// Adds the pair slots q in [o0, o1) (part[2q], part[2q + 1]) into (a, b) in
-// ascending q; four slots are loaded at a time so that their latencies overlap.
-__device__ __forceinline__ void gather_slots(const float4 *__restrict__ part, uint32_t o0, uint32_t o1, float4 &a,
-                                             float4 &b) {
-    for (uint32_t q = o0; q < o1; q += 4) {
-        float4 u[4], w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t qq = min(q + (uint32_t)k, o1 - 1u);     // in range; repeats are not added
-            u[k] = part[2 * (size_t)qq];
-            w[k] = part[2 * (size_t)qq + 1];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (q + (uint32_t)k < o1) {
-                a.x += u[k].x; a.y += u[k].y; a.z += u[k].z; a.w += u[k].w;
-                b.x += w[k].x; b.y += w[k].y; b.z += w[k].z; b.w += w[k].w;
-            }
-    }
-}
-
 // One thread per Gaussian: its pairs' partial gradients sit at offsets[g] ..
 // offsets[g+1] in emission order; add them in that order (reproducible).
 __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const uint32_t *__restrict__ offsets,
@@ -568,19 +532,11 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
 // contiguous bytes read by its 8 lanes together, and up to 8 slots are loaded
 // at once.  Each parameter's slots are added in ascending order, as in
 // gather_slots (same bits as a gather followed by the Adam step).
-struct AdamPairArgs {
-    float lr[8];
-    float b1, omb1, b2, omb2, eps;
-    double b1d, b2d;                 // for the bias corrections
-    int step;                        // used when d_step is NULL
-    const int32_t *d_step;           // device step count (graph replays), or NULL
-};
-
 // With `loss`, one more workgroup (the last) reduces the loss partials of the
 // raster pass into it.
 __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
                                                     const float *__restrict__ part, float *__restrict__ p,
-                                                    float *__restrict__ m, float *__restrict__ v, AdamPairArgs a,
+                                                    float *__restrict__ m, float *__restrict__ v, AdamHP a,
                                                     const float *__restrict__ loss_part, int nparts, double inv_count,
                                                     float *__restrict__ loss) {
     if (loss && blockIdx.x == gridDim.x - 1) {
@@ -609,12 +565,25 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
     float lr = a.lr[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) lr = j == k ? a.lr[k] : lr;
-    Mo = fmaf(a.b1, Mo, a.omb1 * G);
-    V = fmaf(a.b2, V, a.omb2 * G * G);
-    P -= lr * (Mo * c1) / (sqrtf(V) * c2 + a.eps);
+    adam_update(P, G, Mo, V, lr, a, c1, c2);
     p[i] = P;
     m[i] = Mo;
     v[i] = V;
+}
+
+AdamHP make_adam_hp(const float *lr, double beta1, double beta2, double eps, int step, const int32_t *d_step) {
+    AdamHP a{};
+    for (int i = 0; i < 8; ++i) a.lr[i] = lr[i];
+    a.b1 = (float)beta1;
+    a.omb1 = (float)(1.0 - beta1);
+    a.b2 = (float)beta2;
+    a.omb2 = (float)(1.0 - beta2);
+    a.eps = (float)eps;
+    a.b1d = beta1;
+    a.b2d = beta2;
+    a.step = step;
+    a.d_step = d_step;
+    return a;
 }
 
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
@@ -640,17 +609,7 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
     const int nb = (int)(((int64_t)n * 8 + 255) / 256) + (d_loss ? 1 : 0);
     if (nb == 0) return hipSuccess;
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
-    AdamPairArgs a{};
-    for (int i = 0; i < 8; ++i) a.lr[i] = lr[i];
-    a.b1 = (float)beta1;
-    a.omb1 = (float)(1.0 - beta1);
-    a.b2 = (float)beta2;
-    a.omb2 = (float)(1.0 - beta2);
-    a.eps = (float)eps;
-    a.b1d = beta1;
-    a.b2d = beta2;
-    a.step = step;
-    a.d_step = d_step;
+    const AdamHP a = make_adam_hp(lr, beta1, beta2, eps, step, d_step);
     const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
     k_adam_pairs<<<nb, 256, 0, s>>>(
         n, offsets, (uint32_t)capacity, reinterpret_cast<const float *>(static_cast<const char *>(ws) + pl.off_part),

@@ -37,6 +37,22 @@ def desc(width: int, height: int, mode: int = MODE_SUM) -> gi_desc:
     return gi_desc(int(width), int(height), int(mode), 0)
 
 
+FIT_PREPARED, FIT_ORDER = 1, 2
+
+
+class gi_fit_buffers(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("params", "m", "v", "target", "image", "loss_partials", "d_loss", "records", "pixbox", "counts",
+                 "offsets", "keys", "vals", "ranges", "tile_order", "d_num")] + [
+        ("capacity", ctypes.c_int64), ("bin_workspace", ctypes.c_void_p), ("bin_workspace_bytes", ctypes.c_size_t),
+        ("bwd_workspace", ctypes.c_void_p), ("bwd_workspace_bytes", ctypes.c_size_t)]
+
+
+class gi_adam_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float * 8), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double)]
+
+
 def load():
     """Open libgi.so (built by rasterizer_gaussian_raster_amd.build); raise if it is absent."""
     global _lib
@@ -65,6 +81,8 @@ def load():
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
         "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P, i64, P, P], i32),
         "gi_render_fwd_bwd_l2": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P], i32),
+        "gi_fit_step_sum": ([D, i64, ctypes.POINTER(gi_fit_buffers), ctypes.POINTER(gi_adam_hparams), i32, P,
+                             ctypes.c_uint32, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -224,3 +242,40 @@ def gi_render_fwd_bwd_l2(d, n, records, pixbox, offsets, ranges, vals, capacity,
                                        _ptr(image), _ptr(dL_dimage), _ptr(loss_partials), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "gi_render_fwd_bwd_l2")
+
+
+def _addr(t):
+    p = _ptr(t)
+    return None if p is None else p.value
+
+
+def fit_buffers(params, m, v, target, image, loss_partials, d_loss, records, pixbox, counts, offsets, keys, vals,
+                ranges, tile_order, d_num, capacity, bin_workspace, bwd_workspace) -> gi_fit_buffers:
+    """The gi_fit_buffers struct of gi_fit_step_sum from device tensors (tile_order / d_loss may be None)."""
+    b = gi_fit_buffers()
+    for name, t in (("params", params), ("m", m), ("v", v), ("target", target), ("image", image),
+                    ("loss_partials", loss_partials), ("d_loss", d_loss), ("records", records), ("pixbox", pixbox),
+                    ("counts", counts), ("offsets", offsets), ("keys", keys), ("vals", vals), ("ranges", ranges),
+                    ("tile_order", tile_order), ("d_num", d_num)):
+        setattr(b, name, _addr(t))
+    b.capacity = int(capacity)
+    b.bin_workspace = _addr(bin_workspace)
+    b.bin_workspace_bytes = bin_workspace.numel() * bin_workspace.element_size()
+    b.bwd_workspace = _addr(bwd_workspace)
+    b.bwd_workspace_bytes = bwd_workspace.numel() * bwd_workspace.element_size()
+    return b
+
+
+def adam_hparams(lr, beta1, beta2, eps) -> gi_adam_hparams:
+    h = gi_adam_hparams()
+    for i, x in enumerate(lr):
+        h.lr[i] = float(x)
+    h.beta1, h.beta2, h.eps = float(beta1), float(beta2), float(eps)
+    return h
+
+
+def gi_fit_step_sum(d, n, buffers: gi_fit_buffers, hparams: gi_adam_hparams, step, d_step=None, flags=0,
+                    stream=None):
+    """One sum-mode training step (binning, fused raster, Adam + set-up of the next binning)."""
+    _check(load().gi_fit_step_sum(ctypes.byref(d), int(n), ctypes.byref(buffers), ctypes.byref(hparams), int(step),
+                                  _ptr(d_step), int(flags), _stream(stream)), "gi_fit_step_sum")

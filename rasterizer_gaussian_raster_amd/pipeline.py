@@ -4,9 +4,9 @@ Torch provides device memory and the stream; every step below is one call of
 the C ABI (through :mod:`.gi`):
 
   render : gi_preprocess_bin_sort (gi_preprocess + gi_bin_sort in one call) -> gi_render_fwd
-  fit (sum mode)   : gi_preprocess_bin_sort -> gi_render_fwd_bwd_l2 (per tile: forward, L2 gradient,
-                     backward; pair gradients left in the workspace) -> gi_adam_step_pairs (gather +
-                     Adam; the loss reduced in a spare workgroup)
+  fit (sum mode)   : gi_fit_step_sum, one call per step: binning -> the fused per-tile forward, L2
+                     gradient and backward -> Adam with the gathered gradient, which also sets up the
+                     updated parameters for the next step's binning (and reduces the loss)
   fit (alpha mode) : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
 
 Fitter.capture() records the sum-mode step as HIP graphs (torch.cuda.CUDAGraph over the same
@@ -188,6 +188,9 @@ class Fitter:
         self.graphs = None
         self.d_step = None
         self.slack = capacity_slack
+        self.prepared = False           # the last fit step left the set-up of the current params
+        self._fb = None                 # gi_fit_buffers over the current buffers
+        self._hp = gi.adam_hparams(self.lr, betas[0], betas[1], eps)
         # size the tile-pair buffers once, with room for the Gaussians to spread
         self.raster.preprocess(self.params, self.logit)
         M = self.raster.bin(sync=True)
@@ -201,6 +204,8 @@ class Fitter:
         M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
         if M > 0.8 * self.raster.capacity:
             self.graphs = None              # the captured graphs hold the old buffers: capture() again
+            self.prepared = False           # the new bin workspace holds no set-up
+            self._fb = None
             self.raster.set_capacity(int(M * self.slack) + 4096)
             self.raster.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(self.raster.desc, self.n,
                                                                               self.raster.capacity),
@@ -208,19 +213,22 @@ class Fitter:
             return True
         return False
 
-    def _sum_step(self, order, ev=(None,) * 2, d_step=None):
-        """The sum-mode step's calls.  d_step: device step counter, advanced here (graph mode)."""
+    def _sum_step(self, order, d_step=None):
+        """The sum-mode step: one gi_fit_step_sum call (binning, fused raster, Adam + the set-up of the
+        updated parameters for the next call).  d_step: device step counter, advanced here (graph mode)."""
         r = self.raster
-        r.bin(sync=False, order=order, params=self.params)
-        ev[0] is not None and ev[0].record()
-        r.forward_backward_l2(self.target)                     # image, loss partials, pair gradients
-        ev[1] is not None and ev[1].record()
+        if self._fb is None:
+            self._fb = gi.fit_buffers(self.params, self.m, self.v, self.target, r.image, r.loss_partials, self.loss,
+                                      r.records, r.pixbox, r.counts, r.offsets, r.keys, r.vals, r.ranges, r.order,
+                                      r.d_num, r.capacity, r.ws, r.bwd_ws)
+        flags = gi.FIT_PREPARED if self.prepared else 0
+        if r.order is not None and (order or not r.has_order):
+            flags |= gi.FIT_ORDER
+            r.has_order = True
         if d_step is not None:
             d_step.add_(1)
-        b1, b2 = self.betas
-        gi.gi_adam_step_pairs(r.desc, self.n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v,
-                              self.lr, b1, b2, self.eps, self.step_count + 1, d_step=d_step,
-                              loss_partials=r.loss_partials, loss_count=3 * r.W * r.H, d_loss=self.loss)
+        gi.gi_fit_step_sum(r.desc, self.n, self._fb, self._hp, self.step_count + 1, d_step=d_step, flags=flags)
+        self.prepared = True
 
     def capture(self, warmup=2):
         """Record the sum-mode step as two HIP graphs (with and without the tile-order refresh).  The
@@ -246,16 +254,16 @@ class Fitter:
         torch.cuda.synchronize(dev)
         self.graphs = graphs
 
-    def step(self, events=None):
-        """One training step.  events: optional 2 torch events recorded before / after the fused raster
-        kernel on the current stream (eager steps only)."""
+    def step(self):
+        """One training step.  In sum mode the raster's records / boxes describe the updated parameters
+        afterwards and its tile ranges are cleared (the next step's binning starts from them)."""
         if self.graphs is not None:
             self.graphs[self.step_count % ORDER_EVERY == 0].replay()
             self.step_count += 1
             return
         r = self.raster
         if self.logit is None:
-            self._sum_step(self.step_count % ORDER_EVERY == 0, events if events is not None else (None,) * 2)
+            self._sum_step(self.step_count % ORDER_EVERY == 0)
             self.step_count += 1
             return
         bg = self.bg4

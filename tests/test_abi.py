@@ -58,6 +58,24 @@ def test_host_only_calls(lib):
     assert st == gi.GI_ERR_INVALID_ARG
     st = gi.load().gi_adam_step(1, 17, None, None, None, None, None, 0.9, 0.999, 1e-8, 1, 0, None)
     assert st == gi.GI_ERR_INVALID_ARG
+    # the one-call training step: missing buffers, alpha mode, unknown flags, bad Adam settings
+    d = gi.desc(64, 48)
+    hp = gi.adam_hparams([0.01] * 8, 0.9, 0.999, 1e-8)
+    fb = gi.gi_fit_buffers()
+    L = gi.load()
+    assert L.gi_fit_step_sum(ctypes.byref(d), 10, None, ctypes.byref(hp), 1, None, 0, None) == gi.GI_ERR_INVALID_ARG
+    assert L.gi_fit_step_sum(ctypes.byref(d), 10, ctypes.byref(fb), ctypes.byref(hp), 1, None, 0,
+                             None) == gi.GI_ERR_INVALID_ARG
+    da = gi.desc(64, 48, gi.MODE_ALPHA)
+    assert L.gi_fit_step_sum(ctypes.byref(da), 0, ctypes.byref(fb), ctypes.byref(hp), 1, None, 0,
+                             None) == gi.GI_ERR_INVALID_ARG
+    assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp), 1, None, 4,
+                             None) == gi.GI_ERR_INVALID_ARG
+    hp_bad = gi.adam_hparams([0.01] * 8, 1.0, 0.999, 1e-8)
+    assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp_bad), 1, None, 0,
+                             None) == gi.GI_ERR_INVALID_ARG
+    assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp), 0, None, 0,
+                             None) == gi.GI_ERR_INVALID_ARG
     assert gi.status_string(gi.GI_ERR_CAPACITY) == "GI_ERR_CAPACITY"
 
 

@@ -238,3 +238,49 @@ def test_adam_pairs_loss_equals_loss_reduce():
                           loss_partials=r.loss_partials, loss_count=T.numel(), d_loss=got0)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(u32(got0), u32(ref))
+
+
+@pytest.mark.parametrize("name", ["tiny_fit_64x64", "kodak_768x512_50k", "ragged_300x200", "long_lists"])
+def test_fit_step_equals_the_three_calls(name):
+    """gi_fit_step_sum (binning, fused raster, Adam + set-up of the next binning in one call, the
+    next call skipping its preprocess) gives, step after step, the same bits as
+    gi_preprocess_bin_sort -> gi_render_fwd_bwd_l2 -> gi_adam_step_pairs."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    W, H, p, tgt = _fused_case(name)
+    n = p.shape[0]
+    T = dev(tgt)
+    lr = [0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005]
+    b1, b2, eps = 0.9, 0.999, 1e-8
+    states = []
+    for one_call in (False, True):
+        P = dev(p)
+        Mo, V = torch.zeros_like(P), torch.zeros_like(P)
+        r = Raster(W, H, n)
+        M = r.bin(sync=True, params=P)
+        r.set_capacity(int(M * 2) + 4096)
+        r.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(r.desc, n, r.capacity), dtype=torch.uint8,
+                               device="cuda")
+        loss = torch.zeros(1, device="cuda")
+        fb = gi.fit_buffers(P, Mo, V, T, r.image, r.loss_partials, loss, r.records, r.pixbox, r.counts, r.offsets,
+                            r.keys, r.vals, r.ranges, r.order, r.d_num, r.capacity, r.ws, r.bwd_ws)
+        hp = gi.adam_hparams(lr, b1, b2, eps)
+        hist = []
+        for step in range(1, 8):
+            order = step in (1, 5)
+            if one_call:
+                flags = (gi.FIT_PREPARED if step not in (1, 4) else 0) | (gi.FIT_ORDER if order else 0)
+                gi.gi_fit_step_sum(r.desc, n, fb, hp, step, flags=flags)
+            else:
+                r.bin(sync=False, params=P, order=order)
+                r.forward_backward_l2(T)
+                gi.gi_adam_step_pairs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, P, Mo, V, lr, b1, b2, eps, step,
+                                      loss_partials=r.loss_partials, loss_count=3 * W * H, d_loss=loss)
+            torch.cuda.synchronize()
+            hist.append([u32(P).copy(), u32(Mo).copy(), u32(V).copy(), u32(loss).copy(), u32(r.image).copy(),
+                         u32(r.offsets).copy()])
+        states.append(hist)
+    for step, (a, b) in enumerate(zip(*states)):
+        for k, (x, y) in enumerate(zip(a, b)):
+            np.testing.assert_array_equal(x, y, err_msg=f"step {step + 1} output {k}")
