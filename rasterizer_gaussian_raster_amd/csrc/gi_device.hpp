@@ -66,19 +66,20 @@ __device__ __forceinline__ void adam_update(float &p, float g, float &m, float &
 }
 
 // Adds the pair slots q in [o0, o1) (part[2q], part[2q + 1]) into (a, b) in
-// ascending q; four slots are loaded at a time so that their latencies overlap.
+// ascending q; K slots are loaded at a time so that their latencies overlap.
+template <int K = 4>
 __device__ __forceinline__ void gather_slots(const float4 *__restrict__ part, uint32_t o0, uint32_t o1, float4 &a,
                                              float4 &b) {
-    for (uint32_t q = o0; q < o1; q += 4) {
-        float4 u[4], w[4];
+    for (uint32_t q = o0; q < o1; q += K) {
+        float4 u[K], w[K];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < K; ++k) {
             const uint32_t qq = min(q + (uint32_t)k, o1 - 1u);     // in range; repeats are not added
             u[k] = part[2 * (size_t)qq];
             w[k] = part[2 * (size_t)qq + 1];
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < K; ++k)
             if (q + (uint32_t)k < o1) {
                 a.x += u[k].x; a.y += u[k].y; a.z += u[k].z; a.w += u[k].w;
                 b.x += w[k].x; b.y += w[k].y; b.z += w[k].z; b.w += w[k].w;

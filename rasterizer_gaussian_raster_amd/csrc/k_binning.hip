@@ -58,6 +58,8 @@ constexpr int kScanItems = 16;
 constexpr int kScanChunk = 256 * kScanItems;   // table entries per scan block
 constexpr uint32_t kDirectMax = 64;            // a thread emits its Gaussian's pairs itself up to this many tiles
 constexpr int64_t kMaxBucketCapacity = 1 << 21; // bucket pass for pair buffers up to this (larger: LSD passes)
+constexpr bool kDirectScatter = true;          // one-group first-pass segments and one-chunk buckets: store keys
+                                               // without an LDS reorder (large segments keep the reorder)
 
 struct BinHeader {
     unsigned long long total;   // M, 64-bit
@@ -282,7 +284,10 @@ struct ChunkLds {
 // Key i sits in lane i % 64 of wave i / span, register (i % span) / 64, for
 // the `span` (a multiple of 64, span * 4 >= cc) the caller loaded with.
 // Entered and left by all threads with LDS in a settled state.
-template <int PL>
+// With DIRECT, each key is stored straight from its register to its final
+// position (no LDS reorder; stores of a wave scatter over the digits' runs):
+// fewer barriers for the small chunks of the first pass and of the buckets.
+template <int PL, bool DIRECT = false>
 __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span, int shift, int bits,
                                               const uint32_t (&key)[PL], const uint32_t (&val)[PL],
                                               uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
@@ -326,6 +331,26 @@ __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span,
         L.cnt[3][tid] = ds + c0 + c1 + c2;
     }
     __syncthreads();
+    if (DIRECT) {
+#pragma unroll
+        for (int it = 0; it < PL; ++it) {
+            if (it >= iters) continue;
+            const int idx = wave * span + it * 64 + lane;
+            if (idx < cc) {
+                const uint32_t d = (key[it] >> shift) & dmask;
+                const uint32_t pos = L.gbase[d] + (L.cnt[wave][d] + rk[it]) - L.dstart[d];
+                if (pos < cap) {                          // holds by construction; keeps a bad table in bounds
+                    kout[pos] = key[it];
+                    vout[pos] = val[it];
+                }
+            }
+        }
+        if (last) return;                                 // uniform
+        __syncthreads();
+        if (tid < radix) L.gbase[tid] += tot;
+        __syncthreads();
+        return;
+    }
 #pragma unroll
     for (int it = 0; it < PL; ++it) {
         if (it >= iters) continue;
@@ -643,7 +668,8 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
                 }
             }
         }
-        scatter_chunk(L, cc, span, shift, bits, key, val, kout, vout, M, cs + (uint32_t)kChunk >= tot);
+        scatter_chunk<kPerLane, kDirectScatter && SG == 1>(L, cc, span, shift, bits, key, val, kout, vout, M,
+                                                            cs + (uint32_t)kChunk >= tot);
     }
 }
 
@@ -743,7 +769,7 @@ __global__ __launch_bounds__(kBT) void k_bucket_sort(const uint32_t *__restrict_
                 val[it] = vin[q];
             }
         }
-        scatter_chunk(L, cc, span, 0, lo_bits, key, val, kout, vout, M, true, s0);
+        scatter_chunk<PL, kDirectScatter>(L, cc, span, 0, lo_bits, key, val, kout, vout, M, true, s0);
         if (tid < radix) {                                        // the digit starts are the tile ranges
             const int t = (blockIdx.x << lo_bits) + tid;
             const uint32_t a = L.dstart[tid], e = tid + 1 < radix ? L.dstart[tid + 1] : (uint32_t)cc;
