@@ -70,7 +70,7 @@ constexpr size_t kPhaseLds = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : 
 struct BwdEntry {
     float4 p, q;
     uint2 box;
-    uint32_t off;          // offsets[g]
+    uint32_t g;            // the Gaussian (its emission offset is loaded by the backward itself)
 };
 
 // This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
@@ -88,12 +88,12 @@ __device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0,
 // backward's share layout); each entry's pixel box is tested against the four
 // 8x8 quadrants and the records are compacted, in list order, into one LDS
 // list per quadrant; wave w walks quadrant w's list.  With `first`, this lane's
-// entry of the first batch (with its offsets[] value) is also kept there: the
-// backward's first share, loaded once for both passes.  On return other waves
+// entry of the first batch is also kept there: the backward's first share,
+// loaded once for both passes.  On return other waves
 // may still read S: barrier before reusing it.
 __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg, const float4 *__restrict__ records,
                                              const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
-                                             const uint32_t *__restrict__ offsets, BwdEntry *first, float px,
+                                             BwdEntry *first, float px,
                                              float py, float &ar, float &ag, float &ab) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint64_t below = lanes_below();
@@ -104,13 +104,12 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
         SumRec r;
         r.p = r.q = make_float4(0.f, 0.f, 0.f, 0.f);
         uint2 bx = make_uint2(1u, 0u);
-        uint32_t off = 0u;
+        uint32_t g = 0u;
         if ((uint32_t)lane < ne) {
-            const uint32_t g = vals[e0 + lane];
+            g = vals[e0 + lane];
             r.p = records[2 * g];
             r.q = records[2 * g + 1];
             bx = pixbox[g];
-            if (first && base == rg.x) off = offsets[g];
             const int j0 = bx.x & 0xffff, i0 = bx.x >> 16, j1 = bx.y & 0xffff, i1 = bx.y >> 16;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -122,7 +121,7 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
             first->p = r.p;
             first->q = r.q;
             first->box = bx;
-            first->off = off;
+            first->g = g;
         }
         uint32_t rank[4];
 #pragma unroll
@@ -216,8 +215,8 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, nullptr, nullptr, (float)pxi + 0.5f, (float)pyi + 0.5f,
-                 ar, ag, ab);
+    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, nullptr, (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag,
+                 ab);
     sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
 }
 
@@ -231,33 +230,31 @@ __global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__
 // backward
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void bwd_load(uint32_t e0, uint32_t ne, const float4 *__restrict__ records,
-                                         const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ offsets,
-                                         const uint32_t *__restrict__ vals, BwdEntry &E) {
+                                         const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
+                                         BwdEntry &E) {
     const uint32_t lane = threadIdx.x & 63;
     E.p = E.q = make_float4(0.f, 0.f, 0.f, 0.f);
     E.box = make_uint2(1u, 0u);
-    E.off = 0u;
+    E.g = 0u;
     if (lane < ne) {
         const uint32_t g = vals[e0 + lane];
         E.p = records[2 * g];
         E.q = records[2 * g + 1];
         E.box = pixbox[g];
-        E.off = offsets[g];
+        E.g = g;
     }
 }
 
-// Stages lane `lane`'s entry: its record in LDS, its emission slot and the
-// rectangle of 4x4 blocks its pixel box overlaps (empty when none).
-__device__ __forceinline__ void bwd_stage(BwdLds &S, uint32_t ne, const BwdEntry &E, int tx, int ty, int x0, int y0,
-                                          int &bx0, int &bx1, int &by0, int &by1, uint32_t &slot) {
+// Stages lane `lane`'s entry: its record in LDS and the rectangle of 4x4
+// blocks its pixel box overlaps (empty when none).
+__device__ __forceinline__ void bwd_stage(BwdLds &S, uint32_t ne, const BwdEntry &E, int x0, int y0, int &bx0,
+                                          int &bx1, int &by0, int &by1) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     bx0 = 4; bx1 = -1; by0 = 4; by1 = -1;
-    slot = 0xffffffffu;
     if ((uint32_t)lane < ne) {
         S.entp[wave][lane] = E.p;
         S.entq[wave][lane] = E.q;
         const uint2 bx = E.box;
-        slot = emit_slot(E.off, bx, tx, ty);
         bx0 = max((int)(bx.x & 0xffff) - x0, 0) >> 2;
         bx1 = min((int)(bx.y & 0xffff) - x0, 15) >> 2;
         by0 = max((int)(bx.x >> 16) - y0, 0) >> 2;
@@ -287,10 +284,12 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
         bwd_share(rg, base, e0, ne);
         if (ne == 0) continue;                              // wave-uniform; no workgroup barrier below
         BwdEntry E = E0;
-        if (base != rg.x) bwd_load(e0, ne, records, pixbox, offsets, vals, E);
+        if (base != rg.x) bwd_load(e0, ne, records, pixbox, vals, E);
         int bx0, bx1, by0, by1;
-        uint32_t slot;
-        bwd_stage(S, ne, E, tx, ty, x0, y0, bx0, bx1, by0, by1, slot);
+        bwd_stage(S, ne, E, x0, y0, bx0, bx1, by0, by1);
+        // the entry's emission offset is only needed for the final store: its load goes out now and
+        // its latency hides behind the items (and stays out of the staging loads)
+        const uint32_t goff = (uint32_t)lane < ne ? offsets[E.g] : 0u;
         // entry-major item positions: lane e's items are [s_e, s_e + n_e), blocks in
         // ascending order (row-major over its rectangle)
         const uint32_t n_e = (uint32_t)(lane) < ne ? (uint32_t)((bx1 - bx0 + 1) * (by1 - by0 + 1)) : 0u;
@@ -377,6 +376,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
         wave_sync();
         // entry e (lane e): its first run's partial, then those of the runs of lanes
         // L0 + 1 .. L1 that continue it, in order
+        const uint32_t slot = (uint32_t)lane < ne ? emit_slot(goff, E.box, tx, ty) : 0xffffffffu;
         if ((uint32_t)lane < ne && slot < capacity) {
             float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
             if (n_e > 0u) {                                 // always, for a box that meets the tile
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W,
         }
     }
     BwdEntry E0;
-    bwd_load(e0, ne, records, pixbox, offsets, vals, E0);
+    bwd_load(e0, ne, records, pixbox, vals, E0);
     gp[gp_index(tid & 15, tid >> 4)] = gv0;
     __syncthreads();
     sum_bwd_tile(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, capacity, part);
@@ -467,9 +467,9 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     BwdEntry E0;                                          // the backward's first share, loaded by the forward
     E0.p = E0.q = make_float4(0.f, 0.f, 0.f, 0.f);
     E0.box = make_uint2(1u, 0u);
-    E0.off = 0u;
+    E0.g = 0u;
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, offsets, &E0,
+    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, &E0,
                  (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     const float4 g = sum_fwd_store<true>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
     if (rg.x == rg.y) return;                             // uniform
