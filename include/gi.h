@@ -375,14 +375,22 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
  *             without it the call preprocesses params first.  Only valid if
  *             params were not changed in between.
  *             GI_FIT_ORDER: also (re)write b->tile_order from this binning (as
- *             gi_bin_sort's tile_order).  When b->tile_order is not NULL the raster
- *             pass takes the tiles in that order, so it must hold a valid order
- *             (from an earlier call with GI_FIT_ORDER, or gi_bin_sort).
+ *             gi_bin_sort's tile_order; it may be written after this call's
+ *             raster pass, i.e. take effect from the next call).
+ *             GI_FIT_USE_ORDER: the raster pass takes the tiles in b->tile_order,
+ *             which must hold a valid order (an earlier call's GI_FIT_ORDER, or
+ *             gi_bin_sort); any permutation gives the same results.
+ *   When each first-pass bucket holds at most 16 tiles (up to 2^21 pairs of
+ *   capacity and a low digit of <= 4 bits, e.g. 768x512), the raster's
+ *   workgroups finish the sort themselves -- each reads its tile's bucket and
+ *   picks its entries out in bucket order, writing keys, vals and the range
+ *   exactly where the bucket pass would -- and that pass is not launched.
  *   Errors as the calls above; a binning overflow (M > capacity) shows in
  *   *d_num and gives a zero gradient (the Adam step still runs).
  */
 #define GI_FIT_PREPARED 1u
 #define GI_FIT_ORDER 2u
+#define GI_FIT_USE_ORDER 4u
 
 typedef struct gi_fit_buffers {
     float *params, *m, *v;          /* device float [n][8]: parameters and Adam moments, in place */

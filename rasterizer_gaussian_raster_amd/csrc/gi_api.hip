@@ -227,7 +227,7 @@ gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *reco
 gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
                           int32_t step, const int32_t *d_step, uint32_t flags, void *stream) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || !hp || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
-    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER)) != 0u) return GI_ERR_INVALID_ARG;
+    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER)) != 0u) return GI_ERR_INVALID_ARG;
     if (!d_step && step < 1) return GI_ERR_INVALID_ARG;
     if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps >= 0.0))
         return GI_ERR_INVALID_ARG;
@@ -235,7 +235,7 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
         !bin_args_ok(desc, n, b->pixbox, b->counts, b->offsets, b->keys, b->vals, b->ranges, b->capacity, b->d_num,
                      b->bin_workspace, b->bin_workspace_bytes))
         return GI_ERR_INVALID_ARG;
-    if ((flags & GI_FIT_ORDER) && !b->tile_order) return GI_ERR_INVALID_ARG;
+    if ((flags & (GI_FIT_ORDER | GI_FIT_USE_ORDER)) && !b->tile_order) return GI_ERR_INVALID_ARG;
     if (!b->target || !b->image || !aligned16(b->image) || !b->loss_partials || !b->bwd_workspace ||
         !aligned256(b->bwd_workspace))
         return GI_ERR_INVALID_ARG;
@@ -250,13 +250,22 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
     if (!(flags & GI_FIT_PREPARED))
         e = gi::launch_preprocess((int)n, W, H, b->params, nullptr, b->records, nullptr, b->pixbox, b->counts, groups,
                                   b->ranges, hist, s);
+    // Buckets of at most 16 tiles: the raster's workgroups finish the sort themselves (each picks its
+    // tile's entries out of its bucket), so the bucket pass is not launched; the tile order, when
+    // asked for, is then formed after the raster from the ranges it wrote.
+    const bool bucket = gi::bucket_list_mode(plan);
+    const uint32_t *order = (flags & GI_FIT_USE_ORDER) ? b->tile_order : nullptr;
     if (e == hipSuccess)
         e = gi::launch_bin_sort(plan, b->pixbox, b->counts, b->offsets, b->keys, b->vals, b->ranges,
-                                (flags & GI_FIT_ORDER) ? b->tile_order : nullptr, b->d_num, b->bin_workspace, s, true);
-    if (e == hipSuccess)
-        e = gi::launch_render_sum_fused(W, H, b->records, b->pixbox, b->offsets, b->ranges, b->tile_order, b->vals,
+                                (!bucket && (flags & GI_FIT_ORDER)) ? b->tile_order : nullptr, b->d_num,
+                                b->bin_workspace, s, true, bucket);
+    if (e == hipSuccess) {
+        const gi::BucketList bl = gi::bin_bucket_list(plan, b->bin_workspace, b->keys, b->vals, b->ranges);
+        e = gi::launch_render_sum_fused(W, H, b->records, b->pixbox, b->offsets, b->ranges, order, b->vals,
                                         b->capacity, b->image, b->target, nullptr, b->loss_partials, b->bwd_workspace,
-                                        s);
+                                        s, bucket ? &bl : nullptr);
+    }
+    if (e == hipSuccess && bucket && (flags & GI_FIT_ORDER)) e = gi::launch_tile_order(plan, b->ranges, b->tile_order, s);
     if (e == hipSuccess)
         e = gi::launch_adam_preprocess((int)n, W, H, b->offsets, b->capacity, b->bwd_workspace, b->params, b->m, b->v,
                                        gi::make_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, step, d_step),

@@ -62,9 +62,27 @@ struct BinPlan {
 };
 BinPlan make_bin_plan(int n, int W, int H, int64_t capacity);
 // groups_done: the preprocess kernel already wrote the group sums and cleared the ranges.
+// first_pass_only: stop after the first sort pass (bucket_list_mode plans; the raster finishes the sort).
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
-                           void *ws, hipStream_t s, bool groups_done = false);
+                           void *ws, hipStream_t s, bool groups_done = false, bool first_pass_only = false);
+// The tile order from the ranges (as gi_bin_sort's tile_order).
+hipError_t launch_tile_order(const BinPlan &p, const uint32_t *ranges, uint32_t *tile_order, hipStream_t s);
+
+// The second sort pass done by the raster's own workgroups: the first pass left each bucket
+// (tiles sharing the high digit) in emission order; tile t's workgroup picks its entries out of
+// its bucket and writes them, and its range, where the bucket pass would have.
+struct BucketList {
+    const uint32_t *kin, *vin;     // first-pass output
+    const uint32_t *bstart;        // bucket starts [2^hi + 1]
+    const uint32_t *m_eff;         // M, or 0 when nothing was binned
+    int lo_bits;
+    uint32_t *kout, *vout;         // final keys / vals
+    uint32_t *ranges;              // final ranges [T][2]
+};
+// Plans whose buckets hold at most 16 tiles (MSD order, low digit <= 4 bits).
+bool bucket_list_mode(const BinPlan &p);
+BucketList bin_bucket_list(const BinPlan &p, void *ws, uint32_t *keys, uint32_t *vals, uint32_t *ranges);
 // device address of the group sums inside the bin workspace
 unsigned long long *bin_group_sums(const BinPlan &p, void *ws);
 // what gi_preprocess_bin_sort's preprocess kernel histograms for the plan (table NULL when the
@@ -96,11 +114,13 @@ hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint1
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
                                  const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s);
-// Forward with the L2 loss and backward of each tile in one launch (dL_dimage may be NULL).
+// Forward with the L2 loss and backward of each tile in one launch (dL_dimage may be NULL).  With
+// bl, each tile's list is taken from its bucket (and written out) instead of ranges / vals.
 hipError_t launch_render_sum_fused(int W, int H, const float *records, const uint16_t *pixbox,
                                    const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                    const uint32_t *vals, int64_t capacity, float *image, const float *target,
-                                   float *dL_dimage, float *loss_partials, void *ws, hipStream_t s);
+                                   float *dL_dimage, float *loss_partials, void *ws, hipStream_t s,
+                                   const BucketList *bl = nullptr);
 // Adds each Gaussian's slots (offsets[g] .. offsets[g+1]) in order to dparams / dlogit, and the
 // per-tile background partials to dbackground.
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,

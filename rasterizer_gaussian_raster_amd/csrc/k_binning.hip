@@ -1091,9 +1091,30 @@ BinHist bin_hist(const BinPlan &p, void *ws) {
     return h;
 }
 
+bool bucket_list_mode(const BinPlan &p) { return p.n > 0 && p.order_kind == 1 && p.lo_bits <= 4; }
+
+BucketList bin_bucket_list(const BinPlan &p, void *ws, uint32_t *keys, uint32_t *vals, uint32_t *ranges) {
+    char *w = static_cast<char *>(ws);
+    BucketList b{};
+    b.kin = reinterpret_cast<const uint32_t *>(w + p.off_kalt);
+    b.vin = reinterpret_cast<const uint32_t *>(w + p.off_valt);
+    b.bstart = reinterpret_cast<const uint32_t *>(w + p.off_bstart);
+    b.m_eff = &reinterpret_cast<const BinHeader *>(w)->m_eff;
+    b.lo_bits = p.lo_bits;
+    b.kout = keys;
+    b.vout = vals;
+    b.ranges = ranges;
+    return b;
+}
+
+hipError_t launch_tile_order(const BinPlan &p, const uint32_t *ranges, uint32_t *tile_order, hipStream_t s) {
+    k_tile_order<<<1, 1024, 0, s>>>(reinterpret_cast<const uint2 *>(ranges), p.ntiles, device_cus(), tile_order);
+    return hipGetLastError();
+}
+
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
-                           void *ws, hipStream_t s, bool groups_done) {
+                           void *ws, hipStream_t s, bool groups_done, bool first_pass_only) {
     char *w = static_cast<char *>(ws);
     BinHeader *hdr = reinterpret_cast<BinHeader *>(w);
     unsigned long long *part = reinterpret_cast<unsigned long long *>(w + p.off_part);
@@ -1160,6 +1181,7 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
         e = hipGetLastError();
         return e != hipSuccess ? e : finish();
     }
+    if (p.order_kind == 1 && first_pass_only) return hipGetLastError();
     if (p.order_kind == 1) {
         const int nbk = 1 << p.bits[0];
         if (p.bucket_lanes == 4)

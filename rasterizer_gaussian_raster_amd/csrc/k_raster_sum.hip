@@ -73,6 +73,12 @@ struct BwdEntry {
     uint32_t g;            // the Gaussian (its emission offset is loaded by the backward itself)
 };
 
+// List entry i.  fresh: the list was written by this workgroup during this
+// launch, so the load bypasses the CU's L1 (agent-scope atomic load).
+__device__ __forceinline__ uint32_t load_list(const uint32_t *vals, uint32_t i, bool fresh) {
+    return fresh ? __hip_atomic_load(vals + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : vals[i];
+}
+
 // This wave's share of the batch at `base`: entries [e0, e0 + ne) (wave-uniform).
 __device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0, uint32_t &ne) {
     const uint32_t nb = min((uint32_t)kBwdBatch, rg.y - base);
@@ -89,11 +95,12 @@ __device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0,
 // 8x8 quadrants and the records are compacted, in list order, into one LDS
 // list per quadrant; wave w walks quadrant w's list.  With `first`, this lane's
 // entry of the first batch is also kept there: the backward's first share,
-// loaded once for both passes.  On return other waves
+// loaded once for both passes.  With tl0, the first batch's Gaussians come from
+// that LDS copy of the list instead of vals.  On return other waves
 // may still read S: barrier before reusing it.
 __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg, const float4 *__restrict__ records,
                                              const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
-                                             BwdEntry *first, float px,
+                                             const uint32_t *tl0, BwdEntry *first, float px,
                                              float py, float &ar, float &ag, float &ab) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint64_t below = lanes_below();
@@ -106,7 +113,7 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
         uint2 bx = make_uint2(1u, 0u);
         uint32_t g = 0u;
         if ((uint32_t)lane < ne) {
-            g = vals[e0 + lane];
+            g = (tl0 && base == rg.x) ? tl0[e0 - rg.x + lane] : load_list(vals, e0 + lane, tl0 != nullptr);
             r.p = records[2 * g];
             r.q = records[2 * g + 1];
             bx = pixbox[g];
@@ -215,8 +222,8 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, nullptr, (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag,
-                 ab);
+    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, nullptr, nullptr, (float)pxi + 0.5f, (float)pyi + 0.5f,
+                 ar, ag, ab);
     sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
 }
 
@@ -230,14 +237,14 @@ __global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__
 // backward
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void bwd_load(uint32_t e0, uint32_t ne, const float4 *__restrict__ records,
-                                         const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
+                                         const uint2 *__restrict__ pixbox, const uint32_t *vals, bool fresh,
                                          BwdEntry &E) {
     const uint32_t lane = threadIdx.x & 63;
     E.p = E.q = make_float4(0.f, 0.f, 0.f, 0.f);
     E.box = make_uint2(1u, 0u);
     E.g = 0u;
     if (lane < ne) {
-        const uint32_t g = vals[e0 + lane];
+        const uint32_t g = load_list(vals, e0 + lane, fresh);
         E.p = records[2 * g];
         E.q = records[2 * g + 1];
         E.box = pixbox[g];
@@ -272,9 +279,8 @@ __device__ __forceinline__ int gp_index(int x, int y) {
 // Wave-local from here on (no workgroup barrier).
 __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx, int ty, uint2 rg, BwdEntry E0,
                                              const float4 *__restrict__ records, const uint2 *__restrict__ pixbox,
-                                             const uint32_t *__restrict__ offsets,
-                                             const uint32_t *__restrict__ vals, uint32_t capacity,
-                                             float4 *__restrict__ part) {
+                                             const uint32_t *__restrict__ offsets, const uint32_t *vals,
+                                             bool fresh_vals, uint32_t capacity, float4 *__restrict__ part) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int x0 = tx * kTile, y0 = ty * kTile;
     const float k2 = 2.0f * kLn2;
@@ -284,7 +290,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
         bwd_share(rg, base, e0, ne);
         if (ne == 0) continue;                              // wave-uniform; no workgroup barrier below
         BwdEntry E = E0;
-        if (base != rg.x) bwd_load(e0, ne, records, pixbox, vals, E);
+        if (base != rg.x) bwd_load(e0, ne, records, pixbox, vals, fresh_vals, E);
         int bx0, bx1, by0, by1;
         bwd_stage(S, ne, E, x0, y0, bx0, bx1, by0, by1);
         // the entry's emission offset is only needed for the final store: its load goes out now and
@@ -433,10 +439,135 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W,
         }
     }
     BwdEntry E0;
-    bwd_load(e0, ne, records, pixbox, vals, E0);
+    bwd_load(e0, ne, records, pixbox, vals, false, E0);
     gp[gp_index(tid & 15, tid >> 4)] = gv0;
     __syncthreads();
-    sum_bwd_tile(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, capacity, part);
+    sum_bwd_tile(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, false, capacity, part);
+}
+
+// Tile t's list from its first-pass bucket (entries of the tiles sharing t's
+// high digit, in emission order): the entries with key t, in bucket order, are
+// the tile's list (the stable sort), placed after the bucket's entries with
+// smaller keys.  Writes them to kout / vout and the range to ranges -- what the
+// bucket pass writes -- and the first kFwdBatch Gaussians to tl.  Buckets are
+// read 2048 entries at a time (one round for the usual sizes).  sc: LDS
+// scratch of 2 + 8 rows of 4.  Ends with a barrier.
+constexpr int kBucketPL = 8;
+__device__ __forceinline__ uint2 bucket_tile_list(const BucketList &B, int t, uint32_t *tl, uint32_t (*sc)[4]) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t below = lanes_below();
+    uint2 *ranges = reinterpret_cast<uint2 *>(B.ranges);
+    if (*B.m_eff == 0u) {                                 // nothing binned (or overflow): uniform
+        if (tid == 0) ranges[t] = make_uint2(0u, 0u);
+        return make_uint2(0u, 0u);
+    }
+    const uint32_t b = (uint32_t)t >> B.lo_bits, tt = (uint32_t)t;
+    const uint32_t s0 = B.bstart[b], s1 = B.bstart[b + 1];
+    constexpr uint32_t CH = 256u * kBucketPL;
+    const bool one = s1 - s0 <= CH;                       // uniform: keep the chunk in registers
+    uint32_t k[kBucketPL], v[kBucketPL];
+    if (one) {                                            // one round of loads, one barrier for counts and ranks
+        uint64_t m[kBucketPL];
+        uint32_t wl = 0;
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            const uint32_t idx = s0 + (uint32_t)(i * 256 + tid);
+            k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
+            v[i] = idx < s1 ? B.vin[idx] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            m[i] = __ballot(k[i] == tt);
+            wl += (uint32_t)__popcll(__ballot(k[i] < tt));
+            if (lane == 0) sc[2 + i][wave] = (uint32_t)__popcll(m[i]);
+        }
+        if (lane == 0) sc[0][wave] = wl;
+        __syncthreads();
+        const uint32_t lt = ((sc[0][0] + sc[0][1]) + sc[0][2]) + sc[0][3];
+        uint32_t base = 0;
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t c = sc[2 + i][w];
+                before += w < wave ? c : 0u;
+                all += c;
+            }
+            if (k[i] == tt) {
+                const uint32_t r = base + before + (uint32_t)__popcll(m[i] & below);
+                B.kout[s0 + lt + r] = tt;
+                B.vout[s0 + lt + r] = v[i];
+                if (r < (uint32_t)kFwdBatch) tl[r] = v[i];
+            }
+            base += all;
+        }
+        const uint2 rg = base ? make_uint2(s0 + lt, s0 + lt + base) : make_uint2(0u, 0u);
+        if (tid == 0) ranges[t] = rg;
+        __syncthreads();                                  // publishes tl / vout
+        return rg;
+    }
+    // pass 1: entries below t and equal to t, per wave
+    uint32_t wl = 0, we = 0;
+    for (uint32_t c0 = s0; c0 < s1; c0 += CH) {
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            const uint32_t idx = c0 + (uint32_t)(i * 256 + tid);
+            k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
+            if (one) v[i] = idx < s1 ? B.vin[idx] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            wl += (uint32_t)__popcll(__ballot(k[i] < tt));
+            we += (uint32_t)__popcll(__ballot(k[i] == tt));
+        }
+    }
+    if (lane == 0) { sc[0][wave] = wl; sc[1][wave] = we; }
+    __syncthreads();
+    const uint32_t lt = ((sc[0][0] + sc[0][1]) + sc[0][2]) + sc[0][3];
+    const uint32_t eq = ((sc[1][0] + sc[1][1]) + sc[1][2]) + sc[1][3];
+    const uint2 rg = eq ? make_uint2(s0 + lt, s0 + lt + eq) : make_uint2(0u, 0u);
+    if (tid == 0) ranges[t] = rg;
+    // pass 2: ranks of the tile's entries in bucket order (chunk, register, wave, lane)
+    uint32_t r0 = 0;
+    for (uint32_t c0 = s0; c0 < s1 && r0 < eq; c0 += CH) {   // uniform
+        if (!one) {
+#pragma unroll
+            for (int i = 0; i < kBucketPL; ++i) {
+                const uint32_t idx = c0 + (uint32_t)(i * 256 + tid);
+                k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
+                v[i] = idx < s1 ? B.vin[idx] : 0u;
+            }
+        }
+        uint64_t m[kBucketPL];
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            m[i] = __ballot(k[i] == tt);
+            if (lane == 0) sc[2 + i][wave] = (uint32_t)__popcll(m[i]);
+        }
+        __syncthreads();
+        uint32_t base = r0;
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t c = sc[2 + i][w];
+                before += w < wave ? c : 0u;
+                all += c;
+            }
+            if (k[i] == tt) {
+                const uint32_t r = base + before + (uint32_t)__popcll(m[i] & below);
+                B.kout[rg.x + r] = tt;
+                B.vout[rg.x + r] = v[i];
+                if (r < (uint32_t)kFwdBatch) tl[r] = v[i];
+            }
+            base += all;
+        }
+        r0 = base;
+        __syncthreads();                                  // sc is rewritten next chunk; publishes tl / vout
+    }
+    return rg;
 }
 
 // Forward with the L2 loss, then the backward of the same tile, in one
@@ -449,13 +580,16 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
                                                           const uint32_t *__restrict__ offsets,
                                                           const uint2 *__restrict__ ranges,
                                                           const uint32_t *__restrict__ order,
-                                                          const uint32_t *__restrict__ vals, uint32_t capacity,
+                                                          const uint32_t *vals, uint32_t capacity,
                                                           float *__restrict__ image, const float *__restrict__ target,
                                                           float *__restrict__ dL, float gscale,
-                                                          float *__restrict__ loss_part, float4 *__restrict__ part) {
+                                                          float *__restrict__ loss_part, float4 *__restrict__ part,
+                                                          BucketList bl) {
     __shared__ float4 gp[16 * kGpStride];
     __shared__ __align__(16) unsigned char lds[kPhaseLds];
     __shared__ float wsq[4];
+    __shared__ uint32_t tl[kFwdBatch];                    // bucket mode: the list's first batch
+    __shared__ uint32_t sc[2 + kBucketPL][4];
     const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -463,19 +597,21 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     const int x0 = tx * kTile, y0 = ty * kTile;
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
-    const uint2 rg = ranges[t];
+    const bool bucket = bl.kin != nullptr;                // uniform
+    const uint2 rg = bucket ? bucket_tile_list(bl, t, tl, sc) : ranges[t];
+    if (bucket) vals = bl.vout;                           // later batches read the list just written
     BwdEntry E0;                                          // the backward's first share, loaded by the forward
     E0.p = E0.q = make_float4(0.f, 0.f, 0.f, 0.f);
     E0.box = make_uint2(1u, 0u);
     E0.g = 0u;
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, &E0,
+    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, bucket ? tl : nullptr, &E0,
                  (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     const float4 g = sum_fwd_store<true>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
     if (rg.x == rg.y) return;                             // uniform
     gp[gp_index(pxi - x0, pyi - y0)] = g;
     __syncthreads();                                      // gp published; the forward's lists are dead
-    sum_bwd_tile(*reinterpret_cast<BwdLds *>(lds), gp, tx, ty, rg, E0, records, pixbox, offsets, vals, capacity,
+    sum_bwd_tile(*reinterpret_cast<BwdLds *>(lds), gp, tx, ty, rg, E0, records, pixbox, offsets, vals, bucket, capacity,
                  part);
 }
 
@@ -676,14 +812,16 @@ hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint1
 hipError_t launch_render_sum_fused(int W, int H, const float *records, const uint16_t *pixbox,
                                    const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                    const uint32_t *vals, int64_t capacity, float *image, const float *target,
-                                   float *dL_dimage, float *loss_partials, void *ws, hipStream_t s) {
+                                   float *dL_dimage, float *loss_partials, void *ws, hipStream_t s,
+                                   const BucketList *bl) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     const float gscale = (float)(2.0 / (3.0 * (double)W * (double)H));
+    const BucketList b = bl ? *bl : BucketList{};
     k_render_sum_fused<<<padded_tiles(ntiles), 256, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
         offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, image, target, dL_dimage,
-        gscale, loss_partials, reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part));
+        gscale, loss_partials, reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part), b);
     return hipGetLastError();
 }
 

@@ -222,9 +222,12 @@ class Fitter:
                                       r.records, r.pixbox, r.counts, r.offsets, r.keys, r.vals, r.ranges, r.order,
                                       r.d_num, r.capacity, r.ws, r.bwd_ws)
         flags = gi.FIT_PREPARED if self.prepared else 0
-        if r.order is not None and (order or not r.has_order):
-            flags |= gi.FIT_ORDER
-            r.has_order = True
+        if r.order is not None:
+            if r.has_order:                 # written by an earlier call (any permutation is valid)
+                flags |= gi.FIT_USE_ORDER
+            if order or not r.has_order:
+                flags |= gi.FIT_ORDER
+                r.has_order = True
         if d_step is not None:
             d_step.add_(1)
         gi.gi_fit_step_sum(r.desc, self.n, self._fb, self._hp, self.step_count + 1, d_step=d_step, flags=flags)

@@ -69,7 +69,7 @@ def test_host_only_calls(lib):
     da = gi.desc(64, 48, gi.MODE_ALPHA)
     assert L.gi_fit_step_sum(ctypes.byref(da), 0, ctypes.byref(fb), ctypes.byref(hp), 1, None, 0,
                              None) == gi.GI_ERR_INVALID_ARG
-    assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp), 1, None, 4,
+    assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp), 1, None, 8,
                              None) == gi.GI_ERR_INVALID_ARG
     hp_bad = gi.adam_hparams([0.01] * 8, 1.0, 0.999, 1e-8)
     assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp_bad), 1, None, 0,

@@ -162,6 +162,16 @@ def _fused_case(name):
         p[:, 5:] = rng.uniform(-0.1, 0.1, (n, 3))
     elif name == "empty":
         W, H, p = 70, 45, np.zeros((0, 8), np.float32)
+    elif name == "dense_400x300":                   # 475 tiles: buckets of 8 tiles, > 2048 pairs, lists > 128
+        W, H = 400, 300
+        n = 20000
+        p = np.zeros((n, 8), np.float32)
+        p[:, 0] = rng.uniform(0, W, n)
+        p[:, 1] = rng.uniform(0, H, n)
+        p[:, 2] = rng.uniform(3.0, 14.0, n)
+        p[:, 3] = rng.uniform(-2.0, 2.0, n)
+        p[:, 4] = rng.uniform(3.0, 14.0, n)
+        p[:, 5:] = rng.uniform(-0.05, 0.1, (n, 3))
     else:
         raise KeyError(name)
     return W, H, p, rng.uniform(0, 1, (3, H, W)).astype(np.float32)
@@ -240,7 +250,8 @@ def test_adam_pairs_loss_equals_loss_reduce():
     np.testing.assert_array_equal(u32(got0), u32(ref))
 
 
-@pytest.mark.parametrize("name", ["tiny_fit_64x64", "kodak_768x512_50k", "ragged_300x200", "long_lists"])
+@pytest.mark.parametrize("name", ["tiny_fit_64x64", "kodak_768x512_50k", "ragged_300x200", "long_lists",
+                                  "dense_400x300"])
 def test_fit_step_equals_the_three_calls(name):
     """gi_fit_step_sum (binning, fused raster, Adam + set-up of the next binning in one call, the
     next call skipping its preprocess) gives, step after step, the same bits as
@@ -270,7 +281,8 @@ def test_fit_step_equals_the_three_calls(name):
         for step in range(1, 8):
             order = step in (1, 5)
             if one_call:
-                flags = (gi.FIT_PREPARED if step not in (1, 4) else 0) | (gi.FIT_ORDER if order else 0)
+                flags = ((gi.FIT_PREPARED if step not in (1, 4) else 0) | (gi.FIT_ORDER if order else 0) |
+                         (gi.FIT_USE_ORDER if step > 1 else 0))
                 gi.gi_fit_step_sum(r.desc, n, fb, hp, step, flags=flags)
             else:
                 r.bin(sync=False, params=P, order=order)
@@ -278,8 +290,9 @@ def test_fit_step_equals_the_three_calls(name):
                 gi.gi_adam_step_pairs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, P, Mo, V, lr, b1, b2, eps, step,
                                       loss_partials=r.loss_partials, loss_count=3 * W * H, d_loss=loss)
             torch.cuda.synchronize()
+            Mb = int(u32(r.d_num)[0])
             hist.append([u32(P).copy(), u32(Mo).copy(), u32(V).copy(), u32(loss).copy(), u32(r.image).copy(),
-                         u32(r.offsets).copy()])
+                         u32(r.offsets).copy(), u32(r.keys)[:Mb].copy(), u32(r.vals)[:Mb].copy()])
         states.append(hist)
     for step, (a, b) in enumerate(zip(*states)):
         for k, (x, y) in enumerate(zip(a, b)):
