@@ -203,6 +203,32 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
                         const float *background, float *image, float *t_final, uint32_t *last,
                         void *stream);
 
+/* Flags of gi_render_image and gi_fit_step_sum (see there). */
+#define GI_FIT_PREPARED 1u
+#define GI_FIT_ORDER 2u
+#define GI_FIT_USE_ORDER 4u
+
+/*
+ * gi_render_image -- gi_preprocess_bin_sort followed by gi_render_fwd in one
+ *   call: params (and logit) in, image (and t_final, last) out, with every
+ *   intermediate written as those calls write it.  In sum mode, when each
+ *   first-pass bucket holds at most 16 tiles (see gi_fit_step_sum), the
+ *   raster's workgroups finish the sort themselves and the bucket pass is not
+ *   launched; keys, vals, ranges and every output are still bit-identical to
+ *   the two calls.
+ *   flags     GI_FIT_ORDER: (re)write tile_order from this binning (possibly
+ *             after this call's raster pass); GI_FIT_USE_ORDER: the raster pass
+ *             takes the tiles in tile_order, which must hold a valid order.
+ *   h_num     as in gi_bin_sort (waits; GI_ERR_CAPACITY when M > capacity, the
+ *             image then being empty).
+ *   Other arguments as in gi_preprocess_bin_sort and gi_render_fwd.
+ */
+gi_status gi_render_image(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                          const float *background, float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
+                          uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
+                          uint32_t flags, int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace,
+                          size_t workspace_bytes, float *image, float *t_final, uint32_t *last, void *stream);
+
 /*
  * gi_render_fwd_l2 -- gi_render_fwd (sum mode) fused with the L2 loss of
  *   "FlashImgs" (train --loss l2): besides the image it writes
@@ -388,9 +414,6 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
  *   Errors as the calls above; a binning overflow (M > capacity) shows in
  *   *d_num and gives a zero gradient (the Adam step still runs).
  */
-#define GI_FIT_PREPARED 1u
-#define GI_FIT_ORDER 2u
-#define GI_FIT_USE_ORDER 4u
 
 typedef struct gi_fit_buffers {
     float *params, *m, *v;          /* device float [n][8]: parameters and Adam moments, in place */

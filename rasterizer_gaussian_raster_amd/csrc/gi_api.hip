@@ -128,6 +128,49 @@ gi_status gi_preprocess_bin_sort(const gi_desc *desc, int64_t n, const float *pa
     return h_num ? read_total(workspace, capacity, h_num, s) : GI_OK;
 }
 
+gi_status gi_render_image(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                          const float *background, float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
+                          uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
+                          uint32_t flags, int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace,
+                          size_t workspace_bytes, float *image, float *t_final, uint32_t *last, void *stream) {
+    if (!preprocess_args_ok(desc, n, params, logit, records, opacity, pixbox, counts) ||
+        !bin_args_ok(desc, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
+                     workspace_bytes))
+        return GI_ERR_INVALID_ARG;
+    if ((flags & ~(uint32_t)(GI_FIT_ORDER | GI_FIT_USE_ORDER)) != 0u) return GI_ERR_INVALID_ARG;
+    if ((flags & (GI_FIT_ORDER | GI_FIT_USE_ORDER)) && !tile_order) return GI_ERR_INVALID_ARG;
+    if (!image || !aligned16(image)) return GI_ERR_INVALID_ARG;
+    const bool alpha = desc->mode == GI_MODE_ALPHA;
+    if (alpha && (!background || !t_final || !last)) return GI_ERR_INVALID_ARG;
+    if (!alpha && (background || t_final || last)) return GI_ERR_INVALID_ARG;
+    const int W = desc->width, H = desc->height;
+    const gi::BinPlan plan = gi::make_bin_plan((int)n, W, H, capacity);
+    hipStream_t s = as_stream(stream);
+    const uint32_t *order = (flags & GI_FIT_USE_ORDER) ? tile_order : nullptr;
+    // sum mode with buckets of at most 16 tiles: the raster finishes the sort (no bucket pass)
+    const bool bucket = !alpha && gi::bucket_list_mode(plan);
+    hipError_t e = gi::launch_preprocess((int)n, W, H, params, logit, records, opacity, pixbox, counts,
+                                         gi::bin_group_sums(plan, workspace), ranges,
+                                         gi::bin_hist(plan, workspace), s);
+    if (e == hipSuccess)
+        e = gi::launch_bin_sort(plan, pixbox, counts, offsets, keys, vals, ranges,
+                                (!bucket && (flags & GI_FIT_ORDER)) ? tile_order : nullptr, d_num, workspace, s,
+                                true, bucket);
+    if (e == hipSuccess) {
+        if (alpha) {
+            e = gi::launch_render_alpha_fwd(W, H, records, opacity, pixbox, ranges, order, vals, background, image,
+                                            t_final, last, s);
+        } else {
+            const gi::BucketList bl = gi::bin_bucket_list(plan, workspace, keys, vals, ranges);
+            e = gi::launch_render_sum_fwd(W, H, records, pixbox, ranges, order, vals, image, nullptr, nullptr,
+                                          nullptr, s, bucket ? &bl : nullptr);
+        }
+    }
+    if (e == hipSuccess && bucket && (flags & GI_FIT_ORDER)) e = gi::launch_tile_order(plan, ranges, tile_order, s);
+    if (e != hipSuccess) return GI_ERR_HIP;
+    return h_num ? read_total(workspace, capacity, h_num, s) : GI_OK;
+}
+
 gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
                         const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *tile_order,
                         const uint32_t *vals, const float *background, float *image, float *t_final, uint32_t *last,

@@ -92,9 +92,7 @@ BinHist bin_hist(const BinPlan &p, void *ws);
 const void *bin_total_ptr(const void *ws);
 
 // k_raster_sum.hip
-hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
-                                 const uint32_t *ranges, const uint32_t *order, const uint32_t *vals, float *image,
-                                 const float *target, float *dL_dimage, float *loss_partials, hipStream_t s);
+
 hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, float *d_loss, hipStream_t s);
 // d_loss (or NULL): also reduce the raster pass's per-tile loss partials into it (one more workgroup).
 hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws, float *p,
@@ -114,6 +112,12 @@ hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint1
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
                                  const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s);
+// Forward (target: also the L2 gradient and loss partials).  With bl, each tile's list is taken
+// from its bucket (and written out) instead of ranges / vals.
+hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
+                                 const uint32_t *ranges, const uint32_t *order, const uint32_t *vals, float *image,
+                                 const float *target, float *dL_dimage, float *loss_partials, hipStream_t s,
+                                 const BucketList *bl = nullptr);
 // Forward with the L2 loss and backward of each tile in one launch (dL_dimage may be NULL).  With
 // bl, each tile's list is taken from its bucket (and written out) instead of ranges / vals.
 hipError_t launch_render_sum_fused(int W, int H, const float *records, const uint16_t *pixbox,

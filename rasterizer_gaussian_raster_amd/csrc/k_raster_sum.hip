@@ -201,29 +201,160 @@ __device__ __forceinline__ float4 sum_fwd_store(int W, int H, int pxi, int pyi, 
     return g;
 }
 
+// Tile t's list from its first-pass bucket (entries of the tiles sharing t's
+// high digit, in emission order): the entries with key t, in bucket order, are
+// the tile's list (the stable sort), placed after the bucket's entries with
+// smaller keys.  Writes them to kout / vout and the range to ranges -- what the
+// bucket pass writes -- and the first kFwdBatch Gaussians to tl.  Buckets are
+// read 2048 entries at a time (one round for the usual sizes).  sc: LDS
+// scratch of 2 + 8 rows of 4.  Ends with a barrier.
+constexpr int kBucketPL = 8;
+__device__ __forceinline__ uint2 bucket_tile_list(const BucketList &B, int t, uint32_t *tl, uint32_t (*sc)[4]) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t below = lanes_below();
+    uint2 *ranges = reinterpret_cast<uint2 *>(B.ranges);
+    if (*B.m_eff == 0u) {                                 // nothing binned (or overflow): uniform
+        if (tid == 0) ranges[t] = make_uint2(0u, 0u);
+        return make_uint2(0u, 0u);
+    }
+    const uint32_t b = (uint32_t)t >> B.lo_bits, tt = (uint32_t)t;
+    const uint32_t s0 = B.bstart[b], s1 = B.bstart[b + 1];
+    constexpr uint32_t CH = 256u * kBucketPL;
+    const bool one = s1 - s0 <= CH;                       // uniform: keep the chunk in registers
+    uint32_t k[kBucketPL], v[kBucketPL];
+    if (one) {                                            // one round of loads, one barrier for counts and ranks
+        uint64_t m[kBucketPL];
+        uint32_t wl = 0;
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            const uint32_t idx = s0 + (uint32_t)(i * 256 + tid);
+            k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
+            v[i] = idx < s1 ? B.vin[idx] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            m[i] = __ballot(k[i] == tt);
+            wl += (uint32_t)__popcll(__ballot(k[i] < tt));
+            if (lane == 0) sc[2 + i][wave] = (uint32_t)__popcll(m[i]);
+        }
+        if (lane == 0) sc[0][wave] = wl;
+        __syncthreads();
+        const uint32_t lt = ((sc[0][0] + sc[0][1]) + sc[0][2]) + sc[0][3];
+        uint32_t base = 0;
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t c = sc[2 + i][w];
+                before += w < wave ? c : 0u;
+                all += c;
+            }
+            if (k[i] == tt) {
+                const uint32_t r = base + before + (uint32_t)__popcll(m[i] & below);
+                B.kout[s0 + lt + r] = tt;
+                B.vout[s0 + lt + r] = v[i];
+                if (r < (uint32_t)kFwdBatch) tl[r] = v[i];
+            }
+            base += all;
+        }
+        const uint2 rg = base ? make_uint2(s0 + lt, s0 + lt + base) : make_uint2(0u, 0u);
+        if (tid == 0) ranges[t] = rg;
+        __syncthreads();                                  // publishes tl / vout
+        return rg;
+    }
+    // pass 1: entries below t and equal to t, per wave
+    uint32_t wl = 0, we = 0;
+    for (uint32_t c0 = s0; c0 < s1; c0 += CH) {
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            const uint32_t idx = c0 + (uint32_t)(i * 256 + tid);
+            k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
+            if (one) v[i] = idx < s1 ? B.vin[idx] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            wl += (uint32_t)__popcll(__ballot(k[i] < tt));
+            we += (uint32_t)__popcll(__ballot(k[i] == tt));
+        }
+    }
+    if (lane == 0) { sc[0][wave] = wl; sc[1][wave] = we; }
+    __syncthreads();
+    const uint32_t lt = ((sc[0][0] + sc[0][1]) + sc[0][2]) + sc[0][3];
+    const uint32_t eq = ((sc[1][0] + sc[1][1]) + sc[1][2]) + sc[1][3];
+    const uint2 rg = eq ? make_uint2(s0 + lt, s0 + lt + eq) : make_uint2(0u, 0u);
+    if (tid == 0) ranges[t] = rg;
+    // pass 2: ranks of the tile's entries in bucket order (chunk, register, wave, lane)
+    uint32_t r0 = 0;
+    for (uint32_t c0 = s0; c0 < s1 && r0 < eq; c0 += CH) {   // uniform
+        if (!one) {
+#pragma unroll
+            for (int i = 0; i < kBucketPL; ++i) {
+                const uint32_t idx = c0 + (uint32_t)(i * 256 + tid);
+                k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
+                v[i] = idx < s1 ? B.vin[idx] : 0u;
+            }
+        }
+        uint64_t m[kBucketPL];
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            m[i] = __ballot(k[i] == tt);
+            if (lane == 0) sc[2 + i][wave] = (uint32_t)__popcll(m[i]);
+        }
+        __syncthreads();
+        uint32_t base = r0;
+#pragma unroll
+        for (int i = 0; i < kBucketPL; ++i) {
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t c = sc[2 + i][w];
+                before += w < wave ? c : 0u;
+                all += c;
+            }
+            if (k[i] == tt) {
+                const uint32_t r = base + before + (uint32_t)__popcll(m[i] & below);
+                B.kout[rg.x + r] = tt;
+                B.vout[rg.x + r] = v[i];
+                if (r < (uint32_t)kFwdBatch) tl[r] = v[i];
+            }
+            base += all;
+        }
+        r0 = base;
+        __syncthreads();                                  // sc is rewritten next chunk; publishes tl / vout
+    }
+    return rg;
+}
+
 // L2 = true also forms the L2 loss gradient 2 (I - T) / (3 W H) from the target
 // and each tile's sum of squared residuals (reduced over the tile in a fixed order).
+// With bl, each tile's list is taken from its first-pass bucket (and written
+// out) instead of ranges / vals.
 template <bool L2>
 __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
                                                         const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
-                                                        const uint32_t *__restrict__ vals,
+                                                        const uint32_t *vals,
                                                         float *__restrict__ image,
                                                         const float *__restrict__ target,
                                                         float *__restrict__ dL, float gscale,
-                                                        float *__restrict__ loss_part) {
+                                                        float *__restrict__ loss_part, BucketList bl) {
     __shared__ FwdLds S;
     __shared__ float wsq[4];
+    __shared__ uint32_t tl[kFwdBatch];
+    __shared__ uint32_t sc[2 + kBucketPL][4];
     const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
+    const bool bucket = bl.kin != nullptr;                // uniform
+    const uint2 rg = bucket ? bucket_tile_list(bl, t, tl, sc) : ranges[t];
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(S, x0, y0, ranges[t], records, pixbox, vals, nullptr, nullptr, (float)pxi + 0.5f, (float)pyi + 0.5f,
-                 ar, ag, ab);
+    sum_fwd_tile(S, x0, y0, rg, records, pixbox, bucket ? bl.vout : vals, bucket ? tl : nullptr, nullptr,
+                 (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
 }
 
@@ -445,131 +576,6 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W,
     sum_bwd_tile(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, false, capacity, part);
 }
 
-// Tile t's list from its first-pass bucket (entries of the tiles sharing t's
-// high digit, in emission order): the entries with key t, in bucket order, are
-// the tile's list (the stable sort), placed after the bucket's entries with
-// smaller keys.  Writes them to kout / vout and the range to ranges -- what the
-// bucket pass writes -- and the first kFwdBatch Gaussians to tl.  Buckets are
-// read 2048 entries at a time (one round for the usual sizes).  sc: LDS
-// scratch of 2 + 8 rows of 4.  Ends with a barrier.
-constexpr int kBucketPL = 8;
-__device__ __forceinline__ uint2 bucket_tile_list(const BucketList &B, int t, uint32_t *tl, uint32_t (*sc)[4]) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const uint64_t below = lanes_below();
-    uint2 *ranges = reinterpret_cast<uint2 *>(B.ranges);
-    if (*B.m_eff == 0u) {                                 // nothing binned (or overflow): uniform
-        if (tid == 0) ranges[t] = make_uint2(0u, 0u);
-        return make_uint2(0u, 0u);
-    }
-    const uint32_t b = (uint32_t)t >> B.lo_bits, tt = (uint32_t)t;
-    const uint32_t s0 = B.bstart[b], s1 = B.bstart[b + 1];
-    constexpr uint32_t CH = 256u * kBucketPL;
-    const bool one = s1 - s0 <= CH;                       // uniform: keep the chunk in registers
-    uint32_t k[kBucketPL], v[kBucketPL];
-    if (one) {                                            // one round of loads, one barrier for counts and ranks
-        uint64_t m[kBucketPL];
-        uint32_t wl = 0;
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            const uint32_t idx = s0 + (uint32_t)(i * 256 + tid);
-            k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
-            v[i] = idx < s1 ? B.vin[idx] : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            m[i] = __ballot(k[i] == tt);
-            wl += (uint32_t)__popcll(__ballot(k[i] < tt));
-            if (lane == 0) sc[2 + i][wave] = (uint32_t)__popcll(m[i]);
-        }
-        if (lane == 0) sc[0][wave] = wl;
-        __syncthreads();
-        const uint32_t lt = ((sc[0][0] + sc[0][1]) + sc[0][2]) + sc[0][3];
-        uint32_t base = 0;
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            uint32_t before = 0, all = 0;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t c = sc[2 + i][w];
-                before += w < wave ? c : 0u;
-                all += c;
-            }
-            if (k[i] == tt) {
-                const uint32_t r = base + before + (uint32_t)__popcll(m[i] & below);
-                B.kout[s0 + lt + r] = tt;
-                B.vout[s0 + lt + r] = v[i];
-                if (r < (uint32_t)kFwdBatch) tl[r] = v[i];
-            }
-            base += all;
-        }
-        const uint2 rg = base ? make_uint2(s0 + lt, s0 + lt + base) : make_uint2(0u, 0u);
-        if (tid == 0) ranges[t] = rg;
-        __syncthreads();                                  // publishes tl / vout
-        return rg;
-    }
-    // pass 1: entries below t and equal to t, per wave
-    uint32_t wl = 0, we = 0;
-    for (uint32_t c0 = s0; c0 < s1; c0 += CH) {
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            const uint32_t idx = c0 + (uint32_t)(i * 256 + tid);
-            k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
-            if (one) v[i] = idx < s1 ? B.vin[idx] : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            wl += (uint32_t)__popcll(__ballot(k[i] < tt));
-            we += (uint32_t)__popcll(__ballot(k[i] == tt));
-        }
-    }
-    if (lane == 0) { sc[0][wave] = wl; sc[1][wave] = we; }
-    __syncthreads();
-    const uint32_t lt = ((sc[0][0] + sc[0][1]) + sc[0][2]) + sc[0][3];
-    const uint32_t eq = ((sc[1][0] + sc[1][1]) + sc[1][2]) + sc[1][3];
-    const uint2 rg = eq ? make_uint2(s0 + lt, s0 + lt + eq) : make_uint2(0u, 0u);
-    if (tid == 0) ranges[t] = rg;
-    // pass 2: ranks of the tile's entries in bucket order (chunk, register, wave, lane)
-    uint32_t r0 = 0;
-    for (uint32_t c0 = s0; c0 < s1 && r0 < eq; c0 += CH) {   // uniform
-        if (!one) {
-#pragma unroll
-            for (int i = 0; i < kBucketPL; ++i) {
-                const uint32_t idx = c0 + (uint32_t)(i * 256 + tid);
-                k[i] = idx < s1 ? B.kin[idx] : 0xffffffffu;
-                v[i] = idx < s1 ? B.vin[idx] : 0u;
-            }
-        }
-        uint64_t m[kBucketPL];
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            m[i] = __ballot(k[i] == tt);
-            if (lane == 0) sc[2 + i][wave] = (uint32_t)__popcll(m[i]);
-        }
-        __syncthreads();
-        uint32_t base = r0;
-#pragma unroll
-        for (int i = 0; i < kBucketPL; ++i) {
-            uint32_t before = 0, all = 0;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t c = sc[2 + i][w];
-                before += w < wave ? c : 0u;
-                all += c;
-            }
-            if (k[i] == tt) {
-                const uint32_t r = base + before + (uint32_t)__popcll(m[i] & below);
-                B.kout[rg.x + r] = tt;
-                B.vout[rg.x + r] = v[i];
-                if (r < (uint32_t)kFwdBatch) tl[r] = v[i];
-            }
-            base += all;
-        }
-        r0 = base;
-        __syncthreads();                                  // sc is rewritten next chunk; publishes tl / vout
-    }
-    return rg;
-}
-
 // Forward with the L2 loss, then the backward of the same tile, in one
 // workgroup: the tile's dL/dI never leaves LDS, and the backward's first share
 // of entries is the forward's own first batch, kept in registers.  Same results, bit for bit, as
@@ -771,18 +777,20 @@ hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *o
 
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *ranges, const uint32_t *order, const uint32_t *vals, float *image,
-                                 const float *target, float *dL_dimage, float *loss_partials, hipStream_t s) {
+                                 const float *target, float *dL_dimage, float *loss_partials, hipStream_t s,
+                                 const BucketList *bl) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
+    const BucketList b = bl ? *bl : BucketList{};
     const float4 *rec = reinterpret_cast<const float4 *>(records);
     const uint2 *bx = reinterpret_cast<const uint2 *>(pixbox);
     const uint2 *rg = reinterpret_cast<const uint2 *>(ranges);
     if (target) {
         const float gscale = (float)(2.0 / (3.0 * (double)W * (double)H));
         k_render_sum_fwd<true><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, order, vals,
-                                                                     image, target, dL_dimage, gscale, loss_partials);
+                                                                     image, target, dL_dimage, gscale, loss_partials, b);
     } else {
         k_render_sum_fwd<false><<<padded_tiles(ntiles), 256, 0, s>>>(W, H, tiles_x, ntiles, rec, bx, rg, order, vals,
-                                                                      image, nullptr, nullptr, 0.0f, nullptr);
+                                                                      image, nullptr, nullptr, 0.0f, nullptr, b);
     }
     return hipGetLastError();
 }

@@ -81,6 +81,8 @@ def load():
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
         "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P, i64, P, P], i32),
         "gi_render_fwd_bwd_l2": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P], i32),
+        "gi_render_image": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, i64, P, P, P, sz, P, P, P,
+                             P], i32),
         "gi_fit_step_sum": ([D, i64, ctypes.POINTER(gi_fit_buffers), ctypes.POINTER(gi_adam_hparams), i32, P,
                              ctypes.c_uint32, P], i32),
     }
@@ -165,6 +167,22 @@ def gi_preprocess_bin_sort(d, n, params, logit, records, opacity, pixbox, counts
                                        ctypes.byref(h) if sync_count else None, _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gi_preprocess_bin_sort")
+    return int(h.value) if sync_count else None
+
+
+def gi_render_image(d, n, params, logit, background, records, opacity, pixbox, counts, offsets, keys, vals, ranges,
+                    tile_order, flags, capacity, d_num, workspace, image, t_final=None, last=None, sync_count=False,
+                    stream=None):
+    """Preprocess, bin and render in one call.  Returns M when sync_count (raising GiError(GI_ERR_CAPACITY)
+    on overflow), else None."""
+    h = ctypes.c_int64(-1)
+    st = load().gi_render_image(ctypes.byref(d), int(n), _ptr(params), _ptr(logit), _ptr(background), _ptr(records),
+                                _ptr(opacity), _ptr(pixbox), _ptr(counts), _ptr(offsets), _ptr(keys), _ptr(vals),
+                                _ptr(ranges), _ptr(tile_order), int(flags), int(capacity), _ptr(d_num),
+                                ctypes.byref(h) if sync_count else None, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(image), _ptr(t_final), _ptr(last),
+                                _stream(stream))
+    _check(st, "gi_render_image")
     return int(h.value) if sync_count else None
 
 

@@ -3,7 +3,8 @@
 Torch provides device memory and the stream; every step below is one call of
 the C ABI (through :mod:`.gi`):
 
-  render : gi_preprocess_bin_sort (gi_preprocess + gi_bin_sort in one call) -> gi_render_fwd
+  render : gi_render_image (preprocess, binning and the forward in one call; same results as
+           gi_preprocess_bin_sort -> gi_render_fwd)
   fit (sum mode)   : gi_fit_step_sum, one call per step: binning -> the fused per-tile forward, L2
                      gradient and backward -> Adam with the gathered gradient, which also sets up the
                      updated parameters for the next step's binning (and reduces the loss)
@@ -152,9 +153,34 @@ class Raster:
                                 stream, tile_order=self._order())
         return self.image
 
-    def render(self, params, logit=None, background=None, sync=True):
-        self.bin(sync=sync, params=params, logit=logit)
-        return self.forward(background)
+    def render(self, params, logit=None, background=None, sync=True, stream=None):
+        """Preprocess, bin and render in one gi_render_image call.  sync: read M back (one host wait)
+        and grow the buffers (and render again) if needed."""
+        if self.keys is None:
+            self.set_capacity(max(1024, 4 * self.n))
+            sync = True
+        flags = 0
+        if self.order is not None:
+            flags |= gi.FIT_USE_ORDER if self.has_order else gi.FIT_ORDER
+        call = lambda sc, fl: gi.gi_render_image(self.desc, self.n, params, logit, background, self.records,
+                                                 self.opacity, self.pixbox, self.counts, self.offsets, self.keys,
+                                                 self.vals, self.ranges, self.order, fl, self.capacity, self.d_num,
+                                                 self.ws, self.image, self.t_final, self.last, sync_count=sc,
+                                                 stream=stream)
+        if not sync:
+            call(False, flags)
+        else:
+            try:
+                self.M = call(True, flags)
+            except gi.GiError as e:
+                if e.status != gi.GI_ERR_CAPACITY:
+                    raise
+                M = int(self.d_num.cpu().view(torch.int32).item()) & 0xFFFFFFFF
+                self.set_capacity(int(M * 1.25) + 1024)
+                self.M = call(True, flags)
+        if flags & gi.FIT_ORDER:
+            self.has_order = True
+        return self.image
 
 
 class Fitter:

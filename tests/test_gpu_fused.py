@@ -297,3 +297,42 @@ def test_fit_step_equals_the_three_calls(name):
     for step, (a, b) in enumerate(zip(*states)):
         for k, (x, y) in enumerate(zip(a, b)):
             np.testing.assert_array_equal(x, y, err_msg=f"step {step + 1} output {k}")
+
+
+@pytest.mark.parametrize("name", ["kodak_768x512_50k", "ragged_300x200", "dense_400x300", "empty", "alpha_300x200"])
+def test_render_image_equals_the_two_calls(name):
+    """gi_render_image (the raster finishing the sort in sum mode where it can) gives the same image,
+    offsets, sorted keys / vals and ranges as gi_preprocess_bin_sort -> gi_render_fwd."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    if name == "alpha_300x200":
+        W, H, p, lg = _case(name)
+        bg = dev(np.array([0.2, 0.5, 0.7, 0.0], np.float32))
+    else:
+        W, H, p, _ = _fused_case(name)
+        lg, bg = None, None
+    n = p.shape[0]
+    mode = gi.MODE_ALPHA if lg is not None else gi.MODE_SUM
+    P, L = dev(p), None if lg is None else dev(lg)
+    outs = []
+    for one_call in (False, True):
+        r = Raster(W, H, n, mode)
+        M = r.bin(sync=True, params=P, logit=L)
+        r.set_capacity(int(M * 2) + 1024)
+        if one_call:
+            M2 = gi.gi_render_image(r.desc, n, P, L, bg, r.records, r.opacity, r.pixbox, r.counts, r.offsets, r.keys,
+                                    r.vals, r.ranges, r.order, 0, r.capacity, r.d_num, r.ws, r.image, r.t_final,
+                                    r.last, sync_count=True)
+        else:
+            M2 = r.bin(sync=True, params=P, logit=L, order=False)
+            r.forward(bg)
+        torch.cuda.synchronize()
+        o = [u32(r.image), u32(r.offsets), u32(r.keys)[:M2], u32(r.vals)[:M2], u32(r.ranges)[: r.T],
+             u32(r.records)[:n], u32(r.counts)[:n]]
+        if r.t_final is not None:
+            o += [u32(r.t_final), u32(r.last)]
+        outs.append((M2, o))
+    assert outs[0][0] == outs[1][0]
+    for k, (a, b) in enumerate(zip(outs[0][1], outs[1][1])):
+        np.testing.assert_array_equal(a, b, err_msg=f"output {k}")
