@@ -6,18 +6,22 @@
 // each tile's list in ascending Gaussian index.
 //
 //   1. k_group_sums : per 256-Gaussian group, the sum of tile counts (u64);
-//                     clears the tile ranges.
-//   2. k_group_scan : one workgroup scans the group sums (only for more than
-//                     2048 groups; below that every block of step 3 adds up the
-//                     sums before it itself).
-//   3. k_count0     : per segment of 1 or 4 groups: offsets[], M, and the
-//                     histogram of the first digit over the segment's pairs.
+//                     clears the tile ranges.  Up to 2048 groups it also
+//                     writes the group's first-digit histogram (as the
+//                     preprocess kernels do when they form the counts), and
+//                     steps 2-3 do not run.
+//   2. k_group_scan : one workgroup scans the group sums (more than 2048 groups).
+//   3. k_count0     : per segment of 4 groups: offsets[], M, and the histogram
+//                     of the first digit over the segment's pairs.
+//   4. k_scatter0w  : (up to 2048 groups) first sort pass, one group per block:
+//                     each block adds up the group sums and the histograms
+//                     before it itself, writes its offsets[] and scatters.
+//      k_scatter0   : (more groups) first sort pass over segments of 4 groups.
 //                     The pairs are never written in emission order: they are
 //                     regenerated from the pixel boxes wherever they are needed
 //                     (each thread walks its own Gaussian's tiles; when some
 //                     Gaussian of the segment covers more than 64 tiles, a
 //                     binary search in LDS spreads the pairs over the lanes).
-//   4. k_scatter0   : first sort pass, straight from the regenerated pairs.
 //   Then, by the number B of key bits and the size of the pair buffer:
 //     B <= 8         : that pass sorted the whole key; its workgroup 0 writes
 //                      the tile ranges from the digit starts.
@@ -58,8 +62,8 @@ constexpr int kScanItems = 16;
 constexpr int kScanChunk = 256 * kScanItems;   // table entries per scan block
 constexpr uint32_t kDirectMax = 64;            // a thread emits its Gaussian's pairs itself up to this many tiles
 constexpr int64_t kMaxBucketCapacity = 1 << 21; // bucket pass for pair buffers up to this (larger: LSD passes)
-constexpr bool kDirectScatter = true;          // one-group first-pass segments and one-chunk buckets: store keys
-                                               // without an LDS reorder (large segments keep the reorder)
+constexpr bool kDirectScatter = true;          // one-chunk buckets store keys without an LDS reorder (the
+                                               // segmented first pass keeps the reorder)
 
 struct BinHeader {
     unsigned long long total;   // M, 64-bit
@@ -103,10 +107,13 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T *smem /*[NT/64]*/, T *t
 }
 
 // One barrier: the workgroup sums of x and y (u64) and the exclusive scan of c
-// (with its total).  sm64 [8] and sm32 [4] must not be reused without a barrier.
+// (with its total), over NT threads.  sm64 [2 NT/64] and sm32 [NT/64] must not
+// be reused without a barrier.
+template <int NT>
 __device__ __forceinline__ void block_sums2_scan(unsigned long long x, unsigned long long y, uint32_t c,
                                                  unsigned long long &sx, unsigned long long &sy, uint32_t &excl,
                                                  uint32_t &ctot, unsigned long long *sm64, uint32_t *sm32) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -116,19 +123,22 @@ __device__ __forceinline__ void block_sums2_scan(unsigned long long x, unsigned 
     const uint32_t inc = wave_scan_incl(c);
     if (lane == 63) {
         sm64[wave] = x;
-        sm64[4 + wave] = y;
+        sm64[NW + wave] = y;
         sm32[wave] = inc;
     }
     __syncthreads();
-    sx = ((sm64[0] + sm64[1]) + sm64[2]) + sm64[3];
-    sy = ((sm64[4] + sm64[5]) + sm64[6]) + sm64[7];
+    unsigned long long ax = 0, ay = 0;
     uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kBT / 64; ++w) {
+    for (int w = 0; w < NW; ++w) {
+        ax += sm64[w];
+        ay += sm64[NW + w];
         const uint32_t v = sm32[w];
         off += w < wave ? v : 0u;
         tot += v;
     }
+    sx = ax;
+    sy = ay;
     excl = off + inc - c;
     ctot = tot;
 }
@@ -182,6 +192,7 @@ struct DigitAcc {
     uint32_t x;      // scanned: the block's base of digit tid
 };
 
+template <int NB = 16, int NT = kBT>
 __device__ __forceinline__ DigitAcc digit_load(const uint32_t *__restrict__ table, int redundant, int ncols_cap,
                                                int me, int bits) {
     const int tid = threadIdx.x;
@@ -194,23 +205,25 @@ __device__ __forceinline__ DigitAcc digit_load(const uint32_t *__restrict__ tabl
         return a;
     }
     // uint4 q of column c holds digits 4*(q mod Q) .. +3, Q = radix/4 (divides 256):
-    // thread t always reads the same 4 digits, from columns t/Q, t/Q + 256/Q, ...
+    // thread t always reads the same 4 digits, from columns t/Q, t/Q + NT/Q, ...
     const int lq = bits - 2;
     const int g4 = tid & ((1 << lq) - 1);
-    const int cstep = kBT >> lq;
+    const int cstep = NT >> lq;
     const uint4 *t4 = reinterpret_cast<const uint4 *>(table);
-    // batches of 16 loads, all in flight together (at most 2 batches: the table
-    // holds <= kMaxRedundantTable entries, 1024 per column step)
-    for (int c0 = tid >> lq; c0 < ncols_cap; c0 += 16 * cstep) {
-        uint4 v[16];
+    // batches of NB loads, all in flight together (one batch when NB * NT * 4
+    // >= kMaxRedundantTable, the most a redundant table holds)
+    // (unconditional loads with 32-bit offsets: columns past the end read entry 0 and are dropped)
+    for (int c0 = tid >> lq; c0 < ncols_cap; c0 += NB * cstep) {
+        uint4 v[NB];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const int c = c0 + k * cstep;
-            v[k] = c < ncols_cap ? t4[((size_t)c << lq) + g4] : make_uint4(0u, 0u, 0u, 0u);
+            v[k] = t4[c < ncols_cap ? ((uint32_t)c << lq) + (uint32_t)g4 : 0u];
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const int c = c0 + k * cstep;
+            if (c >= ncols_cap) v[k] = make_uint4(0u, 0u, 0u, 0u);
             a.t.x += v[k].x; a.t.y += v[k].y; a.t.z += v[k].z; a.t.w += v[k].w;
             if (c < me) { a.b.x += v[k].x; a.b.y += v[k].y; a.b.z += v[k].z; a.b.w += v[k].w; }
         }
@@ -526,78 +539,40 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
 // ---------------------------------------------------------------------------
 // 4: first sort pass from the regenerated pairs (segments of 256 * SG Gaussians)
 // ---------------------------------------------------------------------------
+// Segments of SG groups, offsets[] and M from k_count0 (more than
+// kMaxRedundantGroups groups; fewer take k_scatter0w below).  Workgroup 0 also
+// publishes where each digit's run starts (bucket_start[d], d <= radix, the
+// last one M) for the bucket pass, and, when this pass sorts the whole key
+// (ranges != NULL), the tile ranges themselves.
 template <int SG>
-// Workgroup 0 also publishes where each digit's run starts (bucket_start[d],
-// d <= radix, the last one M) for the bucket pass, and, when this pass sorts
-// the whole key (ranges != NULL), the tile ranges themselves.
-//
-// Two ways in.  With `counts` (segments of one group, raw group sums in part[],
-// at most kMaxRedundantGroups groups) the block forms its Gaussians' emission
-// offsets itself, writes offsets[] and, in workgroup 0, publishes M: no count
-// kernel ran.  Without, offsets[] and M come from k_count0.
 __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift, int bits, int table_redundant,
                                                   int ncols_cap, const uint2 *__restrict__ pixbox,
-                                                  uint32_t *__restrict__ offsets, BinHeader *__restrict__ hdr,
+                                                  const uint32_t *__restrict__ offsets,
+                                                  const BinHeader *__restrict__ hdr,
                                                   const uint32_t *__restrict__ table, uint32_t *__restrict__ kout,
                                                   uint32_t *__restrict__ vout, uint32_t *__restrict__ bucket_start,
-                                                  uint2 *__restrict__ ranges, int ntiles,
-                                                  const uint32_t *__restrict__ counts,
-                                                  const unsigned long long *__restrict__ part, int ngroups,
-                                                  long long capacity, uint32_t *__restrict__ d_num) {
+                                                  uint2 *__restrict__ ranges, int ntiles) {
     constexpr int S = kBT * SG;
     __shared__ SegLds<S> G;
     __shared__ ChunkLds<kPerLane> L;
     __shared__ BaseLds B;
-    __shared__ unsigned long long sm64[8];
-    __shared__ uint32_t smc[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int first = blockIdx.x * S;
     const int ns = min(S, n - first);
-    // One round of loads: the segment's offsets (or counts and the group sums)
-    // and boxes, M, the digit table.
+    // One round of loads: the segment's offsets and boxes, M, the digit table.
     uint32_t o[SG], o1[SG];
     uint2 bx[SG];
-    uint32_t o0, oend, M;
-    DigitAcc acc;
-    if (counts) {                                     // SG == 1
-        const uint32_t c = tid < ns ? counts[first + tid] : 0u;
-        bx[0] = tid < ns ? pixbox[first + tid] : make_uint2(0u, 0u);
-        unsigned long long v[kMaxRedundantGroups / kBT];
 #pragma unroll
-        for (int k = 0; k < kMaxRedundantGroups / kBT; ++k) {
-            const int i = tid + k * kBT;
-            v[k] = i < ngroups ? part[i] : 0ull;
-        }
-        acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
-        unsigned long long before = 0, all = 0;
-#pragma unroll
-        for (int k = 0; k < kMaxRedundantGroups / kBT; ++k) {
-            all += v[k];
-            before += tid + k * kBT < (int)blockIdx.x ? v[k] : 0ull;
-        }
-        unsigned long long tb, ta;
-        uint32_t local, tot;
-        block_sums2_scan(before, all, c, tb, ta, local, tot, sm64, smc);
-        if (tid < ns) offsets[first + tid] = sat32(tb + local);
-        if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num);
-        M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
-        o0 = (uint32_t)tb;                           // exact whenever M > 0
-        o[0] = o0 + local;
-        o1[0] = o[0] + c;
-        oend = o0 + tot;
-    } else {
-#pragma unroll
-        for (int r = 0; r < SG; ++r) {
-            const int i = r * kBT + tid;
-            o[r] = i < ns ? offsets[first + i] : 0u;
-            o1[r] = i < ns ? offsets[first + i + 1] : 0u;
-            bx[r] = i < ns ? pixbox[first + i] : make_uint2(0u, 0u);
-        }
-        o0 = offsets[first];
-        oend = offsets[first + ns];                  // the next segment's first slot, or M
-        M = hdr->m_eff;
-        acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
+    for (int r = 0; r < SG; ++r) {
+        const int i = r * kBT + tid;
+        o[r] = i < ns ? offsets[first + i] : 0u;
+        o1[r] = i < ns ? offsets[first + i + 1] : 0u;
+        bx[r] = i < ns ? pixbox[first + i] : make_uint2(0u, 0u);
     }
+    const uint32_t o0 = offsets[first];
+    const uint32_t oend = offsets[first + ns];        // the next segment's first slot, or M
+    const uint32_t M = hdr->m_eff;
+    const DigitAcc acc = digit_load(table, table_redundant, ncols_cap, blockIdx.x, bits);
     if (M == 0u) return;                              // overflow or no pair (then offsets may saturate): uniform
 #pragma unroll
     for (int r = 0; r < SG; ++r) {
@@ -668,8 +643,232 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
                 }
             }
         }
-        scatter_chunk<kPerLane, kDirectScatter && SG == 1>(L, cc, span, shift, bits, key, val, kout, vout, M,
-                                                            cs + (uint32_t)kChunk >= tot);
+        scatter_chunk<kPerLane>(L, cc, span, shift, bits, key, val, kout, vout, M, cs + (uint32_t)kChunk >= tot);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4w: the first pass for one-group segments, 512 threads per group
+// ---------------------------------------------------------------------------
+// With one group (256 Gaussians) per block the first pass runs about one block
+// per CU and is bound by the latency of each wave's instruction stream, not by
+// memory: here 8 waves share the digit table loads, the ranking and the
+// stores, so each issues about half of what a 4-wave block would (1024 threads
+// measured slower: one such block per CU leaves a tail once the groups
+// outnumber the CUs).  Threads 0..255 own the group's Gaussians.  The group sums and the digit table are read raw (no
+// count kernel ran): each block forms its Gaussians' emission offsets, writes
+// offsets[], and workgroup 0 publishes M and the bucket starts.  Keys go
+// straight from registers to their final positions: position = the block's
+// first slot of the digit + the keys of that digit in the chunk's earlier waves
+// + the key's rank among its wave's keys of the digit (ballots, in key order),
+// so the pass is stable.
+constexpr int kWPL = 4;                        // keys per lane per chunk (at most)
+constexpr int kWideThreads = 512;             // threads per group: 8 waves (two blocks fit a CU)
+
+template <int NT>
+struct WideLds {
+    static constexpr int NW = NT / 64;
+    SegLds<kBT> G;                             // the group's emission scan and boxes
+    uint32_t cnt[NW][256];                     // per wave and digit: keys so far, then the wave's first slot
+    uint32_t gbase[256];                       // output position of the block's next key of each digit
+    union {
+        struct { uint32_t sk[NT * kWPL], sv[NT * kWPL]; } st;   // a chunk's pairs, emitted by their owners
+        struct { uint4 b[NW][64], t[NW][64]; } fold;             // per wave: digit-quad sums of the table
+    } u;
+    unsigned long long sm64[2 * NW];
+    uint32_t sm32[NW];
+};
+
+// gbase[d] = first output position of this block's keys of digit d, from the
+// table sums of digit_load<_, NT>.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void wide_digit_finish(const DigitAcc &a, int redundant, int bits, WideLds<NT> &L) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, radix = 1 << bits;
+    if (!redundant) {
+        if (tid < radix) L.gbase[tid] = a.x;
+        __syncthreads();
+        return;
+    }
+    // lanes of a wave with equal lane mod Q hold the same 4 digits: add them up
+    const int Q = radix >> 2;
+    uint4 b = a.b, t = a.t;
+    for (int o = Q; o < 64; o <<= 1) {               // uniform
+        b.x += __shfl_xor(b.x, o, 64); b.y += __shfl_xor(b.y, o, 64);
+        b.z += __shfl_xor(b.z, o, 64); b.w += __shfl_xor(b.w, o, 64);
+        t.x += __shfl_xor(t.x, o, 64); t.y += __shfl_xor(t.y, o, 64);
+        t.z += __shfl_xor(t.z, o, 64); t.w += __shfl_xor(t.w, o, 64);
+    }
+    if (lane < Q) {
+        L.u.fold.b[wave][lane] = b;
+        L.u.fold.t[wave][lane] = t;
+    }
+    __syncthreads();
+    uint32_t sb = 0, st = 0;
+    if (tid < radix) {
+        const uint32_t *pb = reinterpret_cast<const uint32_t *>(&L.u.fold.b[0][0]);
+        const uint32_t *pt = reinterpret_cast<const uint32_t *>(&L.u.fold.t[0][0]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            sb += pb[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
+            st += pt[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
+        }
+    }
+    uint32_t all;
+    const uint32_t start = block_exclusive_scan<uint32_t, NT>(st, L.sm32, &all);
+    if (tid < radix) L.gbase[tid] = start + sb;
+    __syncthreads();
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x, int shift, int bits, int table_redundant,
+                                                   int ncols_cap, const uint2 *__restrict__ pixbox,
+                                                   uint32_t *__restrict__ offsets, BinHeader *__restrict__ hdr,
+                                                   const uint32_t *__restrict__ table, uint32_t *__restrict__ kout,
+                                                   uint32_t *__restrict__ vout, uint32_t *__restrict__ bucket_start,
+                                                   uint2 *__restrict__ ranges, int ntiles,
+                                                   const uint32_t *__restrict__ counts,
+                                                   const unsigned long long *__restrict__ part, int ngroups,
+                                                   long long capacity, uint32_t *__restrict__ d_num) {
+    constexpr int NW = NT / 64, CH = NT * kWPL;
+    __shared__ WideLds<NT> L;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << bits;
+    const uint32_t dmask = (uint32_t)(radix - 1);
+    const int first = blockIdx.x * kBT;
+    const int ns = min(kBT, n - first);
+    const bool own = tid < ns;
+    // one round of loads: the group's counts and boxes, the group sums, the digit table
+    const uint32_t c = own ? counts[first + tid] : 0u;
+    const uint2 bx = own ? pixbox[first + tid] : make_uint2(0u, 0u);
+    unsigned long long v[kMaxRedundantGroups / NT];
+#pragma unroll
+    for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
+        const int i = tid + k * NT;
+        v[k] = i < ngroups ? part[i] : 0ull;
+    }
+    const DigitAcc acc = digit_load<kMaxRedundantTable / (4 * NT), NT>(table, table_redundant, ncols_cap,
+                                                                     blockIdx.x, bits);
+    unsigned long long before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
+        all += v[k];
+        before += tid + k * NT < (int)blockIdx.x ? v[k] : 0ull;
+    }
+    unsigned long long tb, ta;
+    uint32_t local, tot;
+    block_sums2_scan<NT>(before, all, c, tb, ta, local, tot, L.sm64, L.sm32);
+    if (own) offsets[first + tid] = sat32(tb + local);
+    if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num);
+    const uint32_t M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
+    if (M == 0u) return;                              // overflow or no pair: uniform
+    if (own) {
+        L.G.excl[tid] = local;
+        L.G.box[tid] = bx;
+    }
+    if (tid == 0) L.G.excl[ns] = tot;
+    const bool big = __syncthreads_or(own && c > kDirectMax);   // else each owner emits its own pairs
+    wide_digit_finish<NT>(acc, table_redundant, bits, L);        // its barriers also publish G
+    if (blockIdx.x == 0) {
+        if (tid < radix) bucket_start[tid] = L.gbase[tid];
+        if (tid == 0) bucket_start[radix] = M;
+        if (ranges && tid < radix && tid < ntiles) {
+            const uint32_t a = L.gbase[tid], e = tid + 1 < radix ? L.gbase[tid + 1] : M;
+            ranges[tid] = e > a ? make_uint2(a, e) : make_uint2(0u, 0u);
+        }
+    }
+    const uint64_t below = lanes_below();
+    for (uint32_t cs = 0; cs < tot; cs += CH) {
+        const int cc = (int)min((uint32_t)CH, tot - cs);
+        const int span = ((cc + NT - 1) / NT) * 64;     // keys per wave: a multiple of 64, NW * span >= cc
+        const int iters = span >> 6;
+        uint32_t key[kWPL], val[kWPL];
+        if (!big) {                                       // uniform
+            if (own) {                                    // the owner writes its pairs of this chunk
+                const uint32_t lo = max(local, cs), hi = min(local + c, cs + (uint32_t)cc);
+                if (lo < hi) {
+                    const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
+                    const uint32_t wt = ((bx.y & 0xffffu) >> 4) - tx0 + 1;
+                    const uint32_t q = (lo - local) / wt;
+                    uint32_t col = (lo - local) - q * wt, row = (ty0 + q) * (uint32_t)tiles_x + tx0;
+                    for (uint32_t x = lo; x < hi; ++x) {
+                        L.u.st.sk[x - cs] = row + col;
+                        L.u.st.sv[x - cs] = (uint32_t)(first + tid);
+                        if (++col == wt) { col = 0; row += (uint32_t)tiles_x; }
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kWPL; ++it) {
+                if (it < iters) {                         // uniform
+                    const int idx = wave * span + it * 64 + lane;
+                    const int q = idx < cc ? idx : cc - 1;
+                    key[it] = L.u.st.sk[q];
+                    val[it] = L.u.st.sv[q];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < kWPL; ++it) {
+                if (it < iters) {                         // uniform
+                    const int idx = wave * span + it * 64 + lane;
+                    int lo;
+                    regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
+                    val[it] = (uint32_t)(first + lo);
+                }
+            }
+        }
+        // rank of each key among its wave's keys of the same digit (wave-local counts)
+        for (int d = lane; d < radix; d += 64) L.cnt[wave][d] = 0u;
+        uint32_t rk[kWPL];
+#pragma unroll
+        for (int it = 0; it < kWPL; ++it) {
+            if (it >= iters) continue;                    // uniform
+            const int idx = wave * span + it * 64 + lane;
+            const bool valid = idx < cc;
+            const uint32_t d = (key[it] >> shift) & dmask;
+            uint64_t peers = __ballot(valid);
+            for (int b = 0; b < bits; ++b) {
+                const bool on = (d >> b) & 1u;
+                const uint64_t m = __ballot(on);
+                peers &= on ? m : ~m;
+            }
+            const uint32_t before_w = valid ? L.cnt[wave][d] : 0u;
+            rk[it] = before_w + (uint32_t)__popcll(peers & below);
+            if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before_w + (uint32_t)__popcll(peers);
+        }
+        __syncthreads();
+        // per digit: each wave's first slot among the chunk's keys of the digit
+        uint32_t dtot = 0;
+        if (tid < radix) {
+            uint32_t cw[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) cw[w] = L.cnt[w][tid];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                L.cnt[w][tid] = dtot;
+                dtot += cw[w];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kWPL; ++it) {
+            if (it >= iters) continue;                    // uniform
+            const int idx = wave * span + it * 64 + lane;
+            if (idx < cc) {
+                const uint32_t d = (key[it] >> shift) & dmask;
+                const uint32_t pos = L.gbase[d] + L.cnt[wave][d] + rk[it];
+                if (pos < M) {                            // holds by construction; keeps a bad table in bounds
+                    kout[pos] = key[it];
+                    vout[pos] = val[it];
+                }
+            }
+        }
+        if (cs + (uint32_t)CH >= tot) break;              // uniform: the last chunk
+        __syncthreads();                                  // every wave has its positions and its keys
+        if (tid < radix) L.gbase[tid] += dtot;
+        __syncthreads();
     }
 }
 
@@ -1162,21 +1361,13 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     if (p.order_kind == 1 || (lsd && (p.passes & 1) == 0)) { k0 = kalt; v0 = valt; }
     uint2 *rg0 = p.order_kind == 0 ? rg : nullptr;
     if (folded)             // also when capacity == 0: it publishes offsets and M
-        k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
-                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles, counts, part, p.nb_g, (long long)p.capacity, d_num);
-    else if (p.seg_groups == 1)
-        k_scatter0<1><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
-                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles, nullptr, nullptr, 0, 0, nullptr);
-    else if (p.seg_groups == 2)
-        k_scatter0<2><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
-                                             p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles, nullptr, nullptr, 0, 0, nullptr);
-    else
+        k_scatter0w<kWideThreads><<<p.nseg, kWideThreads, 0, s>>>(
+            p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box, offsets, hdr, table, k0,
+            v0, bstart, rg0, p.ntiles, counts, part, p.nb_g, (long long)p.capacity, d_num);
+    else                    // not folded: more than kMaxRedundantGroups groups, segments of 4
         k_scatter0<4><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
                                              p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,
-                                             p.ntiles, nullptr, nullptr, 0, 0, nullptr);
+                                             p.ntiles);
     if (p.capacity == 0) {
         e = hipGetLastError();
         return e != hipSuccess ? e : finish();
