@@ -40,7 +40,7 @@ __device__ __forceinline__ void wave_sync() {
 // b^t (t >= 0) by binary powering in fp64: a short chain of multiplications
 // (a few ulps of fp64 from the exact power, far below the fp32 rounding that
 // follows) instead of a general pow.
-__device__ __forceinline__ double powi_f64(double b, int t) {
+__host__ __device__ __forceinline__ double powi_f64(double b, int t) {
     double r = 1.0, x = b;
     for (unsigned e = (unsigned)t; e != 0u; e >>= 1) {
         if (e & 1u) r *= x;
@@ -50,11 +50,25 @@ __device__ __forceinline__ double powi_f64(double b, int t) {
 }
 
 // Adam's bias corrections for step t (t < 1 is taken as 1), formed in fp64 and
-// rounded once: 1/(1 - b1^t) and 1/sqrt(1 - b2^t).
-__device__ __forceinline__ void adam_bias(double b1, double b2, int t, float &inv_bc1, float &inv_sqrt_bc2) {
+// rounded once: 1/(1 - b1^t) and 1/sqrt(1 - b2^t).  The host forms them the
+// same way (IEEE fp64 products, quotient and square root: the same bits).
+__host__ __device__ __forceinline__ void adam_bias(double b1, double b2, int t, float &inv_bc1,
+                                                   float &inv_sqrt_bc2) {
     const int tt = t < 1 ? 1 : t;
     inv_bc1 = (float)(1.0 / (1.0 - powi_f64(b1, tt)));
     inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - powi_f64(b2, tt)));
+}
+
+// This step's corrections: the host's, or formed here from the device step
+// count (graph replays).  Called before any load is issued (the fp64 loop of
+// the device path then costs no wait on outstanding loads).
+__device__ __forceinline__ void adam_step_bias(const AdamHP &a, float &inv_bc1, float &inv_sqrt_bc2) {
+    if (a.d_step) {                                        // uniform
+        adam_bias(a.b1d, a.b2d, *a.d_step, inv_bc1, inv_sqrt_bc2);
+    } else {
+        inv_bc1 = a.bc1;
+        inv_sqrt_bc2 = a.bc2;
+    }
 }
 
 // One Adam update of a scalar: the same expression in every optimizer kernel.
@@ -87,13 +101,50 @@ __device__ __forceinline__ void gather_slots(const float4 *__restrict__ part, ui
     }
 }
 
+// Half h of the same sum (part[2q + h] for q in [o0, o1), ascending q): the
+// value gather_slots forms for that half, bit for bit.
+// The first K slots are loaded outside the loop, so that they go out as soon as
+// the offsets are in (a loop would wait for every load in flight first).
+template <int K = 4>
+__device__ __forceinline__ void gather_half(const float4 *__restrict__ part, uint32_t o0, uint32_t o1, int h,
+                                            float4 &a) {
+    {
+        float4 u[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t qq = o1 > o0 ? min(o0 + (uint32_t)k, o1 - 1u) : 0u;   // in range; extras not added
+            u[k] = part[2 * (size_t)qq + h];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (o0 + (uint32_t)k < o1) {
+                a.x += u[k].x; a.y += u[k].y; a.z += u[k].z; a.w += u[k].w;
+            }
+    }
+    for (uint32_t q = o0 + K; q < o1; q += K) {
+        float4 u[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t qq = min(q + (uint32_t)k, o1 - 1u);     // in range; repeats are not added
+            u[k] = part[2 * (size_t)qq + h];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (q + (uint32_t)k < o1) {
+                a.x += u[k].x; a.y += u[k].y; a.z += u[k].z; a.w += u[k].w;
+            }
+    }
+}
+
 // Sum of the per-tile partials in a fixed order, divided by the entry count
-// (one workgroup of 256; sm: 256 doubles of LDS).
+// (the first 256 threads of a workgroup of 256 or more; sm: 256 doubles of LDS).
 __device__ __forceinline__ void loss_reduce_block(int nparts, const float *__restrict__ part, double inv_count,
                                                   float *__restrict__ loss, double *sm) {
     double s = 0.0;
-    for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
-    sm[threadIdx.x] = s;
+    if (threadIdx.x < 256) {                               // a larger block's other threads only take the barriers
+        for (int i = threadIdx.x; i < nparts; i += 256) s += (double)part[i];
+        sm[threadIdx.x] = s;
+    }
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
         if (threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];

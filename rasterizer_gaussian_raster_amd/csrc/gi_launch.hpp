@@ -21,7 +21,8 @@ struct BinHist {
 struct AdamHP {
     float lr[8];
     float b1, omb1, b2, omb2, eps;
-    double b1d, b2d;                 // for the bias corrections (formed on the device)
+    double b1d, b2d;                 // for the bias corrections formed on the device (d_step set)
+    float bc1, bc2;                  // the corrections for `step`, formed on the host (d_step NULL)
     int step;                        // used when d_step is NULL
     const int32_t *d_step;           // device step count (graph replays), or NULL
 };

@@ -81,8 +81,10 @@ __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const fl
 
 // The binning's first step for one 256-Gaussian group, given each thread's
 // tile count c and box: the group's pair total, its first-pass digit histogram
-// (when hist.table is set).  h: 256 u32 of LDS, cleared by the caller before
-// the barrier this function starts with; ws: 4 u64 of LDS.
+// (when hist.table is set), over a block of NT threads.  h: 256 u32 of LDS,
+// cleared by the caller before the barrier this function starts with; ws:
+// NT/64 u64 of LDS.
+template <int NT = 256>
 __device__ __forceinline__ void group_totals(uint32_t c, uint2 box, unsigned long long *__restrict__ group_sums,
                                              BinHist hist, uint32_t *h, unsigned long long *ws) {
     const int radix = 1 << hist.bits;
@@ -91,7 +93,12 @@ __device__ __forceinline__ void group_totals(uint32_t c, uint2 box, unsigned lon
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
     if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = x;
     __syncthreads();                                      // also publishes the cleared histogram
-    if (threadIdx.x == 0) group_sums[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    if (threadIdx.x == 0) {
+        unsigned long long t = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) t += ws[w];
+        group_sums[blockIdx.x] = t;
+    }
     if (hist.table) {                                     // uniform
         hist_add_pairs(h, c, box, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
         __syncthreads();
@@ -145,57 +152,64 @@ hipError_t launch_preprocess(int n, int W, int H, const float *params, const flo
 // group_sums: record, pixel box, tile count, the group's pair total and digit
 // histogram, and the tile ranges cleared.  With `loss`, the last workgroup
 // reduces the loss partials of the raster pass instead.
-__global__ __launch_bounds__(256) void k_adam_preprocess(int n, int W, int H, int ngroups,
-                                                         const uint32_t *__restrict__ offsets, uint32_t capacity,
-                                                         const float4 *__restrict__ part, float4 *__restrict__ p,
-                                                         float4 *__restrict__ m, float4 *__restrict__ v, AdamHP a,
-                                                         float4 *__restrict__ records, uint2 *__restrict__ pixbox,
-                                                         uint32_t *__restrict__ counts,
-                                                         unsigned long long *__restrict__ group_sums,
-                                                         uint2 *__restrict__ ranges, int ntiles, BinHist hist,
-                                                         const float *__restrict__ loss_part, int nparts,
-                                                         double inv_count, float *__restrict__ loss) {
+//
+// Two lanes per Gaussian (512 threads per 256-Gaussian group): lane h of the
+// pair gathers and updates the parameter half h (float4), so each lane's chain
+// of dependent loads and Adam steps is half as long; the pair then swaps
+// halves and both form the set-up (the even lane keeps the count).
+constexpr int kAdamPrepThreads = 512;
+__global__ __launch_bounds__(kAdamPrepThreads) void k_adam_preprocess(
+    int n, int W, int H, int ngroups, const uint32_t *__restrict__ offsets, uint32_t capacity,
+    const float4 *__restrict__ part, float4 *__restrict__ p, float4 *__restrict__ m, float4 *__restrict__ v, AdamHP a,
+    float4 *__restrict__ records, uint2 *__restrict__ pixbox, uint32_t *__restrict__ counts,
+    unsigned long long *__restrict__ group_sums, uint2 *__restrict__ ranges, int ntiles, BinHist hist,
+    const float *__restrict__ loss_part, int nparts, double inv_count, float *__restrict__ loss) {
+    constexpr int NT = kAdamPrepThreads;
     if (loss && (int)blockIdx.x == ngroups) {
         __shared__ double sm[256];
         loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
         return;
     }
-    __shared__ unsigned long long ws[4];
-    __shared__ uint32_t h[256];
-    const int g = blockIdx.x * 256 + threadIdx.x;
-    if (hist.table && (int)threadIdx.x < (1 << hist.bits)) h[threadIdx.x] = 0u;
-    for (int t = g; t < ntiles; t += ngroups * 256) ranges[t] = make_uint2(0u, 0u);
+    __shared__ unsigned long long ws[NT / 64];
+    __shared__ uint32_t hl[256];
+    const int tid = threadIdx.x, half = tid & 1;
+    const int g = blockIdx.x * 256 + (tid >> 1);
+    if (hist.table && tid < (1 << hist.bits)) hl[tid] = 0u;
+    for (int t = blockIdx.x * NT + tid; t < ntiles; t += ngroups * NT) ranges[t] = make_uint2(0u, 0u);
+    float c1, c2;
+    adam_step_bias(a, c1, c2);
     uint32_t c = 0u;
     uint2 box = make_uint2(1u, 0u);
-    if (g < n) {
-        float4 P0 = p[2 * g], P1 = p[2 * g + 1], M0 = m[2 * g], M1 = m[2 * g + 1], V0 = v[2 * g], V1 = v[2 * g + 1];
-        const int t = a.d_step ? *a.d_step : a.step;
-        const bool ok = offsets[n] <= capacity;           // else the binning overflowed: zero gradient
-        const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
-        float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
-        gather_slots(part, o0, o1, g0, g1);
-        float c1, c2;
-        adam_bias(a.b1d, a.b2d, t, c1, c2);
-        adam_update(P0.x, g0.x, M0.x, V0.x, a.lr[0], a, c1, c2);
-        adam_update(P0.y, g0.y, M0.y, V0.y, a.lr[1], a, c1, c2);
-        adam_update(P0.z, g0.z, M0.z, V0.z, a.lr[2], a, c1, c2);
-        adam_update(P0.w, g0.w, M0.w, V0.w, a.lr[3], a, c1, c2);
-        adam_update(P1.x, g1.x, M1.x, V1.x, a.lr[4], a, c1, c2);
-        adam_update(P1.y, g1.y, M1.y, V1.y, a.lr[5], a, c1, c2);
-        adam_update(P1.z, g1.z, M1.z, V1.z, a.lr[6], a, c1, c2);
-        adam_update(P1.w, g1.w, M1.w, V1.w, a.lr[7], a, c1, c2);
-        p[2 * g] = P0; p[2 * g + 1] = P1;
-        m[2 * g] = M0; m[2 * g + 1] = M1;
-        v[2 * g] = V0; v[2 * g + 1] = V1;
+    if (g < n) {                                          // both lanes of the pair
+        const size_t q = 2 * (size_t)g + half;
+        float4 P = p[q], Mm = m[q], V = v[q];
+        const uint32_t o0 = offsets[g], o1r = offsets[g + 1];   // both loads out with the parameter loads
+        const uint32_t o1 = offsets[n] <= capacity ? o1r : o0;  // else the binning overflowed: zero gradient
+        float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
+        gather_half(part, o0, o1, half, gr);
+        const int l0 = 4 * half;
+        adam_update(P.x, gr.x, Mm.x, V.x, a.lr[l0], a, c1, c2);
+        adam_update(P.y, gr.y, Mm.y, V.y, a.lr[l0 + 1], a, c1, c2);
+        adam_update(P.z, gr.z, Mm.z, V.z, a.lr[l0 + 2], a, c1, c2);
+        adam_update(P.w, gr.w, Mm.w, V.w, a.lr[l0 + 3], a, c1, c2);
+        p[q] = P;
+        m[q] = Mm;
+        v[q] = V;
+        const float4 Q = make_float4(__shfl_xor(P.x, 1, 64), __shfl_xor(P.y, 1, 64), __shfl_xor(P.z, 1, 64),
+                                     __shfl_xor(P.w, 1, 64));
+        const float4 P0 = half ? Q : P, P1 = half ? P : Q;
         const Prep o = preprocess_gaussian(P0, P1, false, 0.0f, W, H);
-        records[2 * g] = o.rp;
-        records[2 * g + 1] = o.rq;
-        pixbox[g] = o.box;
-        counts[g] = o.cnt;
-        c = o.cnt;
-        box = o.box;
+        if (half) {
+            records[q] = o.rq;
+        } else {
+            records[q] = o.rp;
+            pixbox[g] = o.box;
+            counts[g] = o.cnt;
+            c = o.cnt;
+            box = o.box;
+        }
     }
-    group_totals(c, box, group_sums, hist, h, ws);
+    group_totals<NT>(c, box, group_sums, hist, hl, ws);
 }
 
 hipError_t launch_adam_preprocess(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *bwd_ws,
@@ -207,7 +221,7 @@ hipError_t launch_adam_preprocess(int n, int W, int H, const uint32_t *offsets, 
     if (nb == 0) return hipSuccess;
     const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
-    k_adam_preprocess<<<nb, 256, 0, s>>>(
+    k_adam_preprocess<<<nb, kAdamPrepThreads, 0, s>>>(
         n, W, H, ngroups, offsets, (uint32_t)capacity,
         reinterpret_cast<const float4 *>(static_cast<const char *>(bwd_ws) + pl.off_part),
         reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a,

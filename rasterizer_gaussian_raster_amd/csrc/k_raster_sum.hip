@@ -689,10 +689,11 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
     const int i = blockIdx.x * 256 + threadIdx.x;     // parameter i % 8 of Gaussian i / 8
     const int g = i >> 3, j = i & 7;
     if (g >= n) return;
+    float c1, c2;
+    adam_step_bias(a, c1, c2);
     float P = p[i], Mo = m[i], V = v[i];
-    const int t = a.d_step ? *a.d_step : a.step;
-    const bool ok = offsets[n] <= capacity;           // else the binning overflowed: zero gradient
-    const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
+    const uint32_t o0 = offsets[g], o1r = offsets[g + 1];
+    const uint32_t o1 = offsets[n] <= capacity ? o1r : o0;   // else the binning overflowed: zero gradient
     float G = 0.0f;
     for (uint32_t q = o0; q < o1; q += 8) {
         float u[8];
@@ -702,8 +703,6 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
         for (int k = 0; k < 8; ++k)
             if (q + (uint32_t)k < o1) G += u[k];
     }
-    float c1, c2;
-    adam_bias(a.b1d, a.b2d, t, c1, c2);
     float lr = a.lr[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) lr = j == k ? a.lr[k] : lr;
@@ -725,6 +724,7 @@ AdamHP make_adam_hp(const float *lr, double beta1, double beta2, double eps, int
     a.b2d = beta2;
     a.step = step;
     a.d_step = d_step;
+    if (!d_step) adam_bias(beta1, beta2, step, a.bc1, a.bc2);
     return a;
 }
 
