@@ -420,6 +420,9 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
         uint32_t e0, ne;
         bwd_share(rg, base, e0, ne);
         if (ne == 0) continue;                              // wave-uniform; no workgroup barrier below
+        // wave priority: the staging (loads, then a short LDS pass) before other waves' item loops, so
+        // that its loads go out early; the item loop at the default priority
+        __builtin_amdgcn_s_setprio(2);
         BwdEntry E = E0;
         if (base != rg.x) bwd_load(e0, ne, records, pixbox, vals, fresh_vals, E);
         int bx0, bx1, by0, by1;
@@ -439,6 +442,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 for (int bx = bx0; bx <= bx1; ++bx) S.items[wave][o++] = (uint16_t)(lane | ((by * 4 + bx) << 8));
         }
         wave_sync();
+        __builtin_amdgcn_s_setprio(0);
         const uint32_t R = (nitems + 63u) >> 6;             // items per lane (wave-uniform)
         const uint32_t f = (uint32_t)lane * R, fend = min(f + R, nitems);
         float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // the current (entry, run) partial
@@ -603,6 +607,10 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     const int x0 = tx * kTile, y0 = ty * kTile;
     const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
     const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
+    // Wave priority: the list, its staging and the forward ahead of the backward item loops of
+    // the CU's other workgroups (every tile's workgroup is resident from the start; the oldest
+    // ones would otherwise hold the issue slots while the others' loads wait to go out).
+    __builtin_amdgcn_s_setprio(2);
     const bool bucket = bl.kin != nullptr;                // uniform
     const uint2 rg = bucket ? bucket_tile_list(bl, t, tl, sc) : ranges[t];
     if (bucket) vals = bl.vout;                           // later batches read the list just written
@@ -617,6 +625,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     if (rg.x == rg.y) return;                             // uniform
     gp[gp_index(pxi - x0, pyi - y0)] = g;
     __syncthreads();                                      // gp published; the forward's lists are dead
+    __builtin_amdgcn_s_setprio(0);
     sum_bwd_tile(*reinterpret_cast<BwdLds *>(lds), gp, tx, ty, rg, E0, records, pixbox, offsets, vals, bucket, capacity,
                  part);
 }
