@@ -225,7 +225,7 @@ __device__ __forceinline__ void hist_add_pairs(uint32_t *hist, uint32_t c, uint2
     if (c == 0u) return;
     const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
     const uint32_t wt = ((bx.y & 0xffffu) >> 4) - tx0 + 1u;
-    const uint32_t rows = c / wt;
+    const uint32_t rows = ((bx.y >> 16) >> 4) - ty0 + 1u;   // c = rows * wt
     for (uint32_t r = 0; r < rows; ++r) {
         const uint32_t lo = (ty0 + r) * (uint32_t)tiles_x + tx0, hi = lo + wt - 1u;
         for (uint32_t a = lo; a <= hi;) {

@@ -133,6 +133,39 @@ __global__ __launch_bounds__(256) void k_preprocess(int n, int W, int H, const f
     preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box);
 }
 
+// group_totals for a block of NT threads with one histogram per wave (hw: NT/64 rows of 256 u32 of
+// LDS, nothing to clear beforehand): each wave clears and fills its own row, so a single barrier
+// publishes the rows and the wave sums (ws: NT/64 u64); the row sums go to the table.
+template <int NT>
+__device__ __forceinline__ void group_totals_waves(uint32_t c, uint2 box, unsigned long long *__restrict__ group_sums,
+                                                   BinHist hist, uint32_t *hw, unsigned long long *ws) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << hist.bits;
+    uint32_t *row = hw + wave * 256;
+    if (hist.table) {                                     // uniform; LDS ops of a wave stay in order
+        for (int d = lane; d < radix; d += 64) row[d] = 0u;
+        hist_add_pairs(row, c, box, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
+    }
+    unsigned long long x = c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    if (lane == 0) ws[wave] = x;
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long t = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) t += ws[w];
+        group_sums[blockIdx.x] = t;
+    }
+    if (hist.table && tid < radix) {
+        uint32_t h = 0u;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) h += hw[w * 256 + tid];
+        if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + tid] = h;
+        else hist.table[(size_t)tid * hist.ncols_cap + blockIdx.x] = h;
+    }
+}
+
 hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
                              float *opacity, uint16_t *pixbox, uint32_t *counts, unsigned long long *group_sums,
                              uint32_t *ranges, BinHist hist, hipStream_t s) {
@@ -171,10 +204,9 @@ __global__ __launch_bounds__(kAdamPrepThreads) void k_adam_preprocess(
         return;
     }
     __shared__ unsigned long long ws[NT / 64];
-    __shared__ uint32_t hl[256];
+    __shared__ uint32_t hw[NT / 64 * 256];
     const int tid = threadIdx.x, half = tid & 1;
     const int g = blockIdx.x * 256 + (tid >> 1);
-    if (hist.table && tid < (1 << hist.bits)) hl[tid] = 0u;
     for (int t = blockIdx.x * NT + tid; t < ntiles; t += ngroups * NT) ranges[t] = make_uint2(0u, 0u);
     float c1, c2;
     adam_step_bias(a, c1, c2);
@@ -209,7 +241,7 @@ __global__ __launch_bounds__(kAdamPrepThreads) void k_adam_preprocess(
             box = o.box;
         }
     }
-    group_totals<NT>(c, box, group_sums, hist, hl, ws);
+    group_totals_waves<NT>(c, box, group_sums, hist, hw, ws);
 }
 
 hipError_t launch_adam_preprocess(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *bwd_ws,
