@@ -79,62 +79,10 @@ __device__ __forceinline__ uint32_t preprocess_one(int g, int W, int H, const fl
     return o.cnt;
 }
 
-// The binning's first step for one 256-Gaussian group, given each thread's
-// tile count c and box: the group's pair total, its first-pass digit histogram
-// (when hist.table is set), over a block of NT threads.  h: 256 u32 of LDS,
-// cleared by the caller before the barrier this function starts with; ws:
-// NT/64 u64 of LDS.
-template <int NT = 256>
-__device__ __forceinline__ void group_totals(uint32_t c, uint2 box, unsigned long long *__restrict__ group_sums,
-                                             BinHist hist, uint32_t *h, unsigned long long *ws) {
-    const int radix = 1 << hist.bits;
-    unsigned long long x = c;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = x;
-    __syncthreads();                                      // also publishes the cleared histogram
-    if (threadIdx.x == 0) {
-        unsigned long long t = 0;
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) t += ws[w];
-        group_sums[blockIdx.x] = t;
-    }
-    if (hist.table) {                                     // uniform
-        hist_add_pairs(h, c, box, hist.tiles_x, hist.shift, (uint32_t)(radix - 1));
-        __syncthreads();
-        if ((int)threadIdx.x < radix) {
-            if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + threadIdx.x] = h[threadIdx.x];
-            else hist.table[(size_t)threadIdx.x * hist.ncols_cap + blockIdx.x] = h[threadIdx.x];
-        }
-    }
-}
-
-// With group_sums (binning in the same call): also the sum of each 256-Gaussian
-// group's tile counts, the tile ranges cleared and, when hist.table is set, the
-// group's first-pass digit histogram -- the binning's first step.
-__global__ __launch_bounds__(256) void k_preprocess(int n, int W, int H, const float4 *__restrict__ params,
-                                                    const float *__restrict__ logit,
-                                                    float4 *__restrict__ records, float *__restrict__ opacity,
-                                                    uint2 *__restrict__ pixbox, uint32_t *__restrict__ counts,
-                                                    unsigned long long *__restrict__ group_sums,
-                                                    uint2 *__restrict__ ranges, int ntiles, BinHist hist) {
-    const int g = blockIdx.x * blockDim.x + threadIdx.x;
-    uint2 box = make_uint2(1u, 0u);
-    if (group_sums) {
-        __shared__ unsigned long long ws[4];
-        __shared__ uint32_t h[256];
-        if (hist.table && (int)threadIdx.x < (1 << hist.bits)) h[threadIdx.x] = 0u;
-        for (int t = g; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
-        const uint32_t c = g < n ? preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box) : 0u;
-        group_totals(c, box, group_sums, hist, h, ws);
-        return;
-    }
-    if (g >= n) return;
-    preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box);
-}
-
-// group_totals for a block of NT threads with one histogram per wave (hw: NT/64 rows of 256 u32 of
-// LDS, nothing to clear beforehand): each wave clears and fills its own row, so a single barrier
+// The binning's first step for one 256-Gaussian group of a block of NT threads, given each
+// thread's tile count c and box: the group's pair total and, when hist.table is set, its
+// first-pass digit histogram.  One histogram row per wave (hw: NT/64 rows of 256 u32 of LDS,
+// nothing to clear beforehand): each wave clears and fills its own row, so a single barrier
 // publishes the rows and the wave sums (ws: NT/64 u64); the row sums go to the table.
 template <int NT>
 __device__ __forceinline__ void group_totals_waves(uint32_t c, uint2 box, unsigned long long *__restrict__ group_sums,
@@ -164,6 +112,29 @@ __device__ __forceinline__ void group_totals_waves(uint32_t c, uint2 box, unsign
         if (hist.redundant) hist.table[(size_t)blockIdx.x * radix + tid] = h;
         else hist.table[(size_t)tid * hist.ncols_cap + blockIdx.x] = h;
     }
+}
+
+// With group_sums (binning in the same call): also the sum of each 256-Gaussian
+// group's tile counts, the tile ranges cleared and, when hist.table is set, the
+// group's first-pass digit histogram -- the binning's first step.
+__global__ __launch_bounds__(256) void k_preprocess(int n, int W, int H, const float4 *__restrict__ params,
+                                                    const float *__restrict__ logit,
+                                                    float4 *__restrict__ records, float *__restrict__ opacity,
+                                                    uint2 *__restrict__ pixbox, uint32_t *__restrict__ counts,
+                                                    unsigned long long *__restrict__ group_sums,
+                                                    uint2 *__restrict__ ranges, int ntiles, BinHist hist) {
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    uint2 box = make_uint2(1u, 0u);
+    if (group_sums) {
+        __shared__ unsigned long long ws[4];
+        __shared__ uint32_t hw[4 * 256];
+        for (int t = g; t < ntiles; t += gridDim.x * 256) ranges[t] = make_uint2(0u, 0u);
+        const uint32_t c = g < n ? preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box) : 0u;
+        group_totals_waves<256>(c, box, group_sums, hist, hw, ws);
+        return;
+    }
+    if (g >= n) return;
+    preprocess_one(g, W, H, params, logit, records, opacity, pixbox, counts, &box);
 }
 
 hipError_t launch_preprocess(int n, int W, int H, const float *params, const float *logit, float *records,
