@@ -213,6 +213,23 @@ __device__ __forceinline__ DigitAcc digit_load(const uint32_t *__restrict__ tabl
     // batches of NB loads, all in flight together (one batch when NB * NT * 4
     // >= kMaxRedundantTable, the most a redundant table holds)
     // (unconditional loads with 32-bit offsets: columns past the end read entry 0 and are dropped)
+    if (NB * NT * 4 >= kMaxRedundantTable) {            // one batch covers every redundant table: no loop
+        const int c0 = tid >> lq;                       // (a loop would first wait for every load in flight)
+        uint4 v[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int c = c0 + k * cstep;
+            v[k] = t4[c < ncols_cap ? ((uint32_t)c << lq) + (uint32_t)g4 : 0u];
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int c = c0 + k * cstep;
+            if (c >= ncols_cap) v[k] = make_uint4(0u, 0u, 0u, 0u);
+            a.t.x += v[k].x; a.t.y += v[k].y; a.t.z += v[k].z; a.t.w += v[k].w;
+            if (c < me) { a.b.x += v[k].x; a.b.y += v[k].y; a.b.z += v[k].z; a.b.w += v[k].w; }
+        }
+        return a;
+    }
     for (int c0 = tid >> lq; c0 < ncols_cap; c0 += NB * cstep) {
         uint4 v[NB];
 #pragma unroll
@@ -738,22 +755,28 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
     const int first = blockIdx.x * kBT;
     const int ns = min(kBT, n - first);
     const bool own = tid < ns;
-    // one round of loads: the group's counts and boxes, the group sums, the digit table
-    const uint32_t c = own ? counts[first + tid] : 0u;
-    const uint2 bx = own ? pixbox[first + tid] : make_uint2(0u, 0u);
+    // one round of loads: the group's counts and boxes, the group sums, the digit table (all
+    // unconditional, in range, unused values dropped: no branch holds a load back)
+    const int gi = first + (own ? tid : 0);
+    const uint32_t c0 = counts[gi];
+    const uint2 bx0 = pixbox[gi];
     unsigned long long v[kMaxRedundantGroups / NT];
 #pragma unroll
     for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
         const int i = tid + k * NT;
-        v[k] = i < ngroups ? part[i] : 0ull;
+        v[k] = part[i < ngroups ? i : 0];
     }
     const DigitAcc acc = digit_load<kMaxRedundantTable / (4 * NT), NT>(table, table_redundant, ncols_cap,
                                                                      blockIdx.x, bits);
+    const uint32_t c = own ? c0 : 0u;
+    const uint2 bx = own ? bx0 : make_uint2(0u, 0u);
     unsigned long long before = 0, all = 0;
 #pragma unroll
     for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
-        all += v[k];
-        before += tid + k * NT < (int)blockIdx.x ? v[k] : 0ull;
+        const int i = tid + k * NT;
+        const unsigned long long x = i < ngroups ? v[k] : 0ull;
+        all += x;
+        before += i < (int)blockIdx.x ? x : 0ull;
     }
     unsigned long long tb, ta;
     uint32_t local, tot;
