@@ -668,17 +668,18 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
 // 4w: the first pass for one-group segments, 512 threads per group
 // ---------------------------------------------------------------------------
 // With one group (256 Gaussians) per block the first pass runs about one block
-// per CU and is bound by the latency of each wave's instruction stream, not by
-// memory: here 8 waves share the digit table loads, the ranking and the
-// stores, so each issues about half of what a 4-wave block would (1024 threads
-// measured slower: one such block per CU leaves a tail once the groups
-// outnumber the CUs).  Threads 0..255 own the group's Gaussians.  The group sums and the digit table are read raw (no
-// count kernel ran): each block forms its Gaussians' emission offsets, writes
-// offsets[], and workgroup 0 publishes M and the bucket starts.  Keys go
-// straight from registers to their final positions: position = the block's
-// first slot of the digit + the keys of that digit in the chunk's earlier waves
-// + the key's rank among its wave's keys of the digit (ballots, in key order),
-// so the pass is stable.
+// per CU and is bound by the latency of each wave's instruction stream and of
+// its barriers, not by memory: 8 waves share the digit table loads, the
+// ranking and the stores (1024 threads measured slower: one such block per CU
+// leaves a tail once the groups outnumber the CUs), and the block takes four
+// barriers for a one-chunk group.  Threads 0..255 own the group's Gaussians.
+// The group sums and the digit table are read raw (no count kernel ran): each
+// block forms its Gaussians' emission offsets, writes offsets[], and workgroup
+// 0 publishes M and the bucket starts.  Each key is regenerated from the
+// group's emission scan (binary search in LDS) and stored straight from its
+// register: position = the block's next slot of the digit + the chunk's keys of
+// the digit in earlier waves + its rank among its wave's keys of the digit
+// (ballots, in key order), so the pass is stable.
 constexpr int kWPL = 4;                        // keys per lane per chunk (at most)
 constexpr int kWideThreads = 512;             // threads per group: 8 waves (two blocks fit a CU)
 
@@ -686,56 +687,13 @@ template <int NT>
 struct WideLds {
     static constexpr int NW = NT / 64;
     SegLds<kBT> G;                             // the group's emission scan and boxes
-    uint32_t cnt[NW][256];                     // per wave and digit: keys so far, then the wave's first slot
+    uint32_t cnt[NW][256];                     // per wave and digit: the chunk's keys of the digit in the wave
     uint32_t gbase[256];                       // output position of the block's next key of each digit
-    union {
-        struct { uint32_t sk[NT * kWPL], sv[NT * kWPL]; } st;   // a chunk's pairs, emitted by their owners
-        struct { uint4 b[NW][64], t[NW][64]; } fold;             // per wave: digit-quad sums of the table
-    } u;
-    unsigned long long sm64[2 * NW];
-    uint32_t sm32[NW];
+    uint4 fb[NW][64], ft[NW][64];              // per wave: digit-quad sums of the table (before, all)
+    unsigned long long sm64[2 * NW];           // per wave: group sums before this group, all
+    uint32_t sm32[NW];                         // per wave: its Gaussians' tile counts
+    uint32_t dsum[4];                          // per wave of digits: their total keys
 };
-
-// gbase[d] = first output position of this block's keys of digit d, from the
-// table sums of digit_load<_, NT>.  Ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void wide_digit_finish(const DigitAcc &a, int redundant, int bits, WideLds<NT> &L) {
-    constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, radix = 1 << bits;
-    if (!redundant) {
-        if (tid < radix) L.gbase[tid] = a.x;
-        __syncthreads();
-        return;
-    }
-    // lanes of a wave with equal lane mod Q hold the same 4 digits: add them up
-    const int Q = radix >> 2;
-    uint4 b = a.b, t = a.t;
-    for (int o = Q; o < 64; o <<= 1) {               // uniform
-        b.x += __shfl_xor(b.x, o, 64); b.y += __shfl_xor(b.y, o, 64);
-        b.z += __shfl_xor(b.z, o, 64); b.w += __shfl_xor(b.w, o, 64);
-        t.x += __shfl_xor(t.x, o, 64); t.y += __shfl_xor(t.y, o, 64);
-        t.z += __shfl_xor(t.z, o, 64); t.w += __shfl_xor(t.w, o, 64);
-    }
-    if (lane < Q) {
-        L.u.fold.b[wave][lane] = b;
-        L.u.fold.t[wave][lane] = t;
-    }
-    __syncthreads();
-    uint32_t sb = 0, st = 0;
-    if (tid < radix) {
-        const uint32_t *pb = reinterpret_cast<const uint32_t *>(&L.u.fold.b[0][0]);
-        const uint32_t *pt = reinterpret_cast<const uint32_t *>(&L.u.fold.t[0][0]);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            sb += pb[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
-            st += pt[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
-        }
-    }
-    uint32_t all;
-    const uint32_t start = block_exclusive_scan<uint32_t, NT>(st, L.sm32, &all);
-    if (tid < radix) L.gbase[tid] = start + sb;
-    __syncthreads();
-}
 
 template <int NT>
 __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x, int shift, int bits, int table_redundant,
@@ -770,6 +728,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
                                                                      blockIdx.x, bits);
     const uint32_t c = own ? c0 : 0u;
     const uint2 bx = own ? bx0 : make_uint2(0u, 0u);
+    // Wave-level partials of everything that needs the whole block: one barrier publishes them.
     unsigned long long before = 0, all = 0;
 #pragma unroll
     for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
@@ -778,9 +737,43 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
         all += x;
         before += i < (int)blockIdx.x ? x : 0ull;
     }
-    unsigned long long tb, ta;
-    uint32_t local, tot;
-    block_sums2_scan<NT>(before, all, c, tb, ta, local, tot, L.sm64, L.sm32);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        before += __shfl_xor(before, o, 64);
+        all += __shfl_xor(all, o, 64);
+    }
+    const uint32_t cinc = wave_scan_incl(c);
+    if (lane == 63) {
+        L.sm64[wave] = before;
+        L.sm64[NW + wave] = all;
+        L.sm32[wave] = cinc;
+    }
+    const int Q = radix >> 2;                         // digit quads (redundant tables: radix >= 4)
+    if (table_redundant) {                            // uniform: lanes with equal lane mod Q hold the same digits
+        uint4 fb = acc.b, ft = acc.t;
+        for (int o = Q; o < 64; o <<= 1) {
+            fb.x += __shfl_xor(fb.x, o, 64); fb.y += __shfl_xor(fb.y, o, 64);
+            fb.z += __shfl_xor(fb.z, o, 64); fb.w += __shfl_xor(fb.w, o, 64);
+            ft.x += __shfl_xor(ft.x, o, 64); ft.y += __shfl_xor(ft.y, o, 64);
+            ft.z += __shfl_xor(ft.z, o, 64); ft.w += __shfl_xor(ft.w, o, 64);
+        }
+        if (lane < Q) {
+            L.fb[wave][lane] = fb;
+            L.ft[wave][lane] = ft;
+        }
+    }
+    __syncthreads();                                  // 1: wave partials
+    unsigned long long tb = 0, ta = 0;
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        tb += L.sm64[w];
+        ta += L.sm64[NW + w];
+        const uint32_t x = L.sm32[w];
+        off += w < wave ? x : 0u;
+        tot += x;
+    }
+    const uint32_t local = off + cinc - c;
     if (own) offsets[first + tid] = sat32(tb + local);
     if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num);
     const uint32_t M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
@@ -790,8 +783,31 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
         L.G.box[tid] = bx;
     }
     if (tid == 0) L.G.excl[ns] = tot;
-    const bool big = __syncthreads_or(own && c > kDirectMax);   // else each owner emits its own pairs
-    wide_digit_finish<NT>(acc, table_redundant, bits, L);        // its barriers also publish G
+    // digit bases: gbase[d] = (keys of smaller digits, all groups) + (keys of d in earlier groups)
+    if (table_redundant) {                            // uniform
+        uint32_t sb = 0, st = 0;
+        if (tid < radix) {
+            const uint32_t *pb = reinterpret_cast<const uint32_t *>(&L.fb[0][0]);
+            const uint32_t *pt = reinterpret_cast<const uint32_t *>(&L.ft[0][0]);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                sb += pb[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
+                st += pt[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
+            }
+        }
+        const uint32_t dinc = wave_scan_incl(st);     // digits tid (< 256) sit in waves 0..3
+        if (wave < 4 && lane == 63) L.dsum[wave] = dinc;
+        __syncthreads();                              // 2: digit totals per wave; G
+        if (tid < radix) {
+            uint32_t dbase = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) dbase += w < wave ? L.dsum[w] : 0u;
+            L.gbase[tid] = dbase + dinc - st + sb;
+        }
+    } else {
+        if (tid < radix) L.gbase[tid] = acc.x;        // the scanned table holds the bases
+    }
+    __syncthreads();                                  // 3: gbase
     if (blockIdx.x == 0) {
         if (tid < radix) bucket_start[tid] = L.gbase[tid];
         if (tid == 0) bucket_start[radix] = M;
@@ -806,40 +822,14 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
         const int span = ((cc + NT - 1) / NT) * 64;     // keys per wave: a multiple of 64, NW * span >= cc
         const int iters = span >> 6;
         uint32_t key[kWPL], val[kWPL];
-        if (!big) {                                       // uniform
-            if (own) {                                    // the owner writes its pairs of this chunk
-                const uint32_t lo = max(local, cs), hi = min(local + c, cs + (uint32_t)cc);
-                if (lo < hi) {
-                    const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
-                    const uint32_t wt = ((bx.y & 0xffffu) >> 4) - tx0 + 1;
-                    const uint32_t q = (lo - local) / wt;
-                    uint32_t col = (lo - local) - q * wt, row = (ty0 + q) * (uint32_t)tiles_x + tx0;
-                    for (uint32_t x = lo; x < hi; ++x) {
-                        L.u.st.sk[x - cs] = row + col;
-                        L.u.st.sv[x - cs] = (uint32_t)(first + tid);
-                        if (++col == wt) { col = 0; row += (uint32_t)tiles_x; }
-                    }
-                }
-            }
-            __syncthreads();
+        // each key regenerated from the group's emission scan (binary search in LDS)
 #pragma unroll
-            for (int it = 0; it < kWPL; ++it) {
-                if (it < iters) {                         // uniform
-                    const int idx = wave * span + it * 64 + lane;
-                    const int q = idx < cc ? idx : cc - 1;
-                    key[it] = L.u.st.sk[q];
-                    val[it] = L.u.st.sv[q];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < kWPL; ++it) {
-                if (it < iters) {                         // uniform
-                    const int idx = wave * span + it * 64 + lane;
-                    int lo;
-                    regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
-                    val[it] = (uint32_t)(first + lo);
-                }
+        for (int it = 0; it < kWPL; ++it) {
+            if (it < iters) {                             // uniform
+                const int idx = wave * span + it * 64 + lane;
+                int lo;
+                regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
+                val[it] = (uint32_t)(first + lo);
             }
         }
         // rank of each key among its wave's keys of the same digit (wave-local counts)
@@ -861,27 +851,16 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             rk[it] = before_w + (uint32_t)__popcll(peers & below);
             if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before_w + (uint32_t)__popcll(peers);
         }
-        __syncthreads();
-        // per digit: each wave's first slot among the chunk's keys of the digit
-        uint32_t dtot = 0;
-        if (tid < radix) {
-            uint32_t cw[NW];
-#pragma unroll
-            for (int w = 0; w < NW; ++w) cw[w] = L.cnt[w][tid];
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                L.cnt[w][tid] = dtot;
-                dtot += cw[w];
-            }
-        }
-        __syncthreads();
+        __syncthreads();                              // the waves' counts
+        // position = the block's next slot of the digit + its keys in earlier waves + the rank
 #pragma unroll
         for (int it = 0; it < kWPL; ++it) {
             if (it >= iters) continue;                    // uniform
             const int idx = wave * span + it * 64 + lane;
             if (idx < cc) {
                 const uint32_t d = (key[it] >> shift) & dmask;
-                const uint32_t pos = L.gbase[d] + L.cnt[wave][d] + rk[it];
+                uint32_t pos = L.gbase[d] + rk[it];
+                for (int w = 0; w < wave; ++w) pos += L.cnt[w][d];
                 if (pos < M) {                            // holds by construction; keeps a bad table in bounds
                     kout[pos] = key[it];
                     vout[pos] = val[it];
@@ -889,8 +868,13 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             }
         }
         if (cs + (uint32_t)CH >= tot) break;              // uniform: the last chunk
-        __syncthreads();                                  // every wave has its positions and its keys
-        if (tid < radix) L.gbase[tid] += dtot;
+        __syncthreads();                                  // every wave has its positions
+        if (tid < radix) {
+            uint32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += L.cnt[w][tid];
+            L.gbase[tid] += t;
+        }
         __syncthreads();
     }
 }
