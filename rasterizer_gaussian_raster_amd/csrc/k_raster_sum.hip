@@ -166,8 +166,9 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
 }
 
 // Writes the image (and the L2 terms) of this thread's pixel and, with a
-// target, the tile's sum of squared residuals (in a fixed order).  Returns the
-// pixel's dL/dI (zero off the image).  Contains a workgroup barrier when L2.
+// target, each wave's sum of squared residuals to wsq.  Returns the pixel's
+// dL/dI (zero off the image).  The caller's next barrier publishes wsq; then
+// loss_part_store writes the tile's sum.
 template <bool L2>
 __device__ __forceinline__ float4 sum_fwd_store(int W, int H, int pxi, int pyi, int t, float ar, float ag, float ab,
                                                 float *__restrict__ image, const float *__restrict__ target,
@@ -195,10 +196,13 @@ __device__ __forceinline__ float4 sum_fwd_store(int W, int H, int pxi, int pyi, 
     if (L2) {
         const float ws = wave_total(sq);
         if (lane == 0) wsq[wave] = ws;
-        __syncthreads();
-        if (threadIdx.x == 0) loss_part[t] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
     }
     return g;
+}
+
+// The tile's sum of squared residuals, in a fixed order (after the barrier that publishes wsq).
+__device__ __forceinline__ void loss_part_store(int t, const float *wsq, float *__restrict__ loss_part) {
+    if (threadIdx.x == 0) loss_part[t] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
 }
 
 // Tile t's list from its first-pass bucket (entries of the tiles sharing t's
@@ -356,6 +360,10 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
     sum_fwd_tile(S, x0, y0, rg, records, pixbox, bucket ? bl.vout : vals, bucket ? tl : nullptr, nullptr,
                  (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
+    if (L2) {
+        __syncthreads();
+        loss_part_store(t, wsq, loss_part);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_loss_reduce(int nparts, const float *__restrict__ part, double inv_count,
@@ -622,9 +630,10 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, bucket ? tl : nullptr, &E0,
                  (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     const float4 g = sum_fwd_store<true>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
-    if (rg.x == rg.y) return;                             // uniform
     gp[gp_index(pxi - x0, pyi - y0)] = g;
-    __syncthreads();                                      // gp published; the forward's lists are dead
+    __syncthreads();                                      // gp and wsq published; the forward's lists are dead
+    loss_part_store(t, wsq, loss_part);
+    if (rg.x == rg.y) return;                             // uniform
     __builtin_amdgcn_s_setprio(0);
     sum_bwd_tile(*reinterpret_cast<BwdLds *>(lds), gp, tx, ty, rg, E0, records, pixbox, offsets, vals, bucket, capacity,
                  part);
