@@ -880,6 +880,150 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
 }
 
 // ---------------------------------------------------------------------------
+// 5b: the bucket pass with 16 waves per bucket
+// ---------------------------------------------------------------------------
+// One block of 1024 threads per high digit: buckets are few (64 at 1020x678)
+// and each holds thousands of keys, so a 4-wave block per bucket leaves most
+// CUs idle and walks its keys in several rounds.  Keys sit 8 per lane (8192 per
+// chunk); each wave ranks its span of the chunk by the low digit with ballots
+// (in key order), and key position = the digit's next slot in the bucket + the
+// chunk's keys of the digit in earlier waves + the rank: stable, stored straight
+// from the registers.  The digit totals of the bucket are its tiles' ranges.
+constexpr int kBWT = 1024, kBWW = kBWT / 64, kBWPL = 8;
+struct BucketWLds {
+    uint32_t cnt[kBWW][256];      // per wave and digit: the chunk's keys of the digit in the wave
+    uint32_t gbase[256];          // next output slot of each digit
+    uint32_t hist[256];           // the bucket's keys per digit (buckets of several chunks)
+    uint32_t dsum[4];             // per wave of digits: their total
+};
+
+// Ranks of a chunk's keys (wave-local counts into L.cnt); ends with the barrier that publishes them.
+__device__ __forceinline__ void bucketw_rank(BucketWLds &L, int cc, int span, int iters, int lo_bits,
+                                             const uint32_t (&key)[kBWPL], uint32_t (&rk)[kBWPL]) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << lo_bits;
+    const uint32_t dmask = (uint32_t)(radix - 1);
+    const uint64_t below = lanes_below();
+    for (int d = lane; d < radix; d += 64) L.cnt[wave][d] = 0u;
+#pragma unroll
+    for (int it = 0; it < kBWPL; ++it) {
+        if (it >= iters) continue;                        // uniform
+        const int idx = wave * span + it * 64 + lane;
+        const bool valid = idx < cc;
+        const uint32_t d = key[it] & dmask;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < lo_bits; ++b) {
+            const bool on = (d >> b) & 1u;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        const uint32_t before = valid ? L.cnt[wave][d] : 0u;
+        rk[it] = before + (uint32_t)__popcll(peers & below);
+        if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+}
+
+// gbase[d] = s0 + exclusive scan of tot over the digits (threads < radix hold tot), and the tiles'
+// ranges.  Two barriers; gbase is published on return.
+__device__ __forceinline__ void bucketw_bases(BucketWLds &L, uint32_t tot, uint32_t s0, int lo_bits, int ntiles,
+                                              uint2 *__restrict__ ranges) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << lo_bits;
+    const uint32_t inc = wave_scan_incl(tot);             // digits (< 256) sit in waves 0..3
+    if (wave < 4 && lane == 63) L.dsum[wave] = inc;
+    __syncthreads();
+    if (tid < radix) {
+        uint32_t ex = inc - tot;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ex += w < wave ? L.dsum[w] : 0u;
+        L.gbase[tid] = s0 + ex;
+        const int t = (blockIdx.x << lo_bits) + tid;
+        if (t < ntiles) ranges[t] = tot ? make_uint2(s0 + ex, s0 + ex + tot) : make_uint2(0u, 0u);
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kBWT) void k_bucket_sortw(const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin,
+                                                       uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                                       const BinHeader *__restrict__ hdr,
+                                                       const uint32_t *__restrict__ bucket_start, int lo_bits,
+                                                       int ntiles, uint2 *__restrict__ ranges) {
+    constexpr uint32_t CH = (uint32_t)kBWT * kBWPL;
+    __shared__ BucketWLds L;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int radix = 1 << lo_bits;
+    const uint32_t dmask = (uint32_t)(radix - 1);
+    const uint32_t M = hdr->m_eff;
+    const uint32_t s0 = M ? bucket_start[blockIdx.x] : 0u, s1 = M ? bucket_start[blockIdx.x + 1] : 0u;
+    if (s1 == s0) return;                                 // uniform: its tiles keep the cleared (0, 0)
+    const bool one = s1 - s0 <= CH;                       // uniform
+    if (!one) {                                           // the bucket's digit totals first
+        if (tid < radix) L.hist[tid] = 0u;
+        __syncthreads();
+        for (uint32_t base = s0; base < s1; base += CH) {
+            uint32_t k[kBWPL];
+#pragma unroll
+            for (int it = 0; it < kBWPL; ++it) {
+                const uint32_t idx = base + it * kBWT + tid;
+                k[it] = kin[idx < s1 ? idx : s1 - 1];
+            }
+#pragma unroll
+            for (int it = 0; it < kBWPL; ++it)
+                if (base + it * kBWT + tid < s1) atomicAdd(&L.hist[k[it] & dmask], 1u);
+        }
+        __syncthreads();
+        bucketw_bases(L, tid < radix ? L.hist[tid] : 0u, s0, lo_bits, ntiles, ranges);
+    }
+    for (uint32_t base = s0; base < s1; base += CH) {    // uniform
+        const int cc = (int)min(CH, s1 - base);
+        const int span = ((cc + kBWT - 1) / kBWT) * 64;   // keys per wave: a multiple of 64, 16 * span >= cc
+        const int iters = span >> 6;
+        uint32_t key[kBWPL], val[kBWPL], rk[kBWPL];
+#pragma unroll
+        for (int it = 0; it < kBWPL; ++it) {
+            if (it < iters) {                             // uniform
+                const int idx = wave * span + it * 64 + lane;
+                const uint32_t q = base + (uint32_t)(idx < cc ? idx : cc - 1);
+                key[it] = kin[q];
+                val[it] = vin[q];
+            }
+        }
+        bucketw_rank(L, cc, span, iters, lo_bits, key, rk);
+        if (one) {                                        // the chunk is the bucket: its counts give the bases
+            uint32_t tot = 0;
+            if (tid < radix)
+#pragma unroll
+                for (int w = 0; w < kBWW; ++w) tot += L.cnt[w][tid];
+            bucketw_bases(L, tot, s0, lo_bits, ntiles, ranges);
+        }
+#pragma unroll
+        for (int it = 0; it < kBWPL; ++it) {
+            if (it >= iters) continue;                    // uniform
+            const int idx = wave * span + it * 64 + lane;
+            if (idx < cc) {
+                const uint32_t d = key[it] & dmask;
+                uint32_t pos = L.gbase[d] + rk[it];
+                for (int w = 0; w < wave; ++w) pos += L.cnt[w][d];
+                if (pos < s1) {                           // holds by construction; keeps a bad table in bounds
+                    kout[pos] = key[it];
+                    vout[pos] = val[it];
+                }
+            }
+        }
+        if (base + CH >= s1) break;                       // uniform: the last chunk
+        __syncthreads();                                  // every wave has its positions
+        if (tid < radix) {
+            uint32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < kBWW; ++w) t += L.cnt[w][tid];
+            L.gbase[tid] += t;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 5: further passes over blocks of 256 * PL keys
 // ---------------------------------------------------------------------------
 template <int PL>
@@ -1382,12 +1526,12 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     if (p.order_kind == 1 && first_pass_only) return hipGetLastError();
     if (p.order_kind == 1) {
         const int nbk = 1 << p.bits[0];
-        if (p.bucket_lanes == 4)
+        if (p.bucket_lanes == 16)        // big buckets: 16 waves each
+            k_bucket_sortw<<<nbk, kBWT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
+        else if (p.bucket_lanes == 4)
             k_bucket_sort<4><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
-        else if (p.bucket_lanes == 8)
-            k_bucket_sort<8><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
         else
-            k_bucket_sort<16><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
+            k_bucket_sort<8><<<nbk, kBT, 0, s>>>(kalt, valt, keys, vals, hdr, bstart, p.lo_bits, p.ntiles, rg);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         return finish();
