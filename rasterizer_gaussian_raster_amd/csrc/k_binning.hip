@@ -61,7 +61,7 @@ constexpr int64_t kMaxRedundantReads = 8 << 20;// ... when all blocks together r
 constexpr int kScanItems = 16;
 constexpr int kScanChunk = 256 * kScanItems;   // table entries per scan block
 constexpr uint32_t kDirectMax = 64;            // a thread emits its Gaussian's pairs itself up to this many tiles
-constexpr int64_t kMaxBucketCapacity = 1 << 21; // bucket pass for pair buffers up to this (larger: LSD passes)
+constexpr int64_t kMaxBucketCapacity = 1ll << 26; // bucket pass for pair buffers up to this (larger: LSD passes)
 constexpr bool kDirectScatter = true;          // one-chunk buckets store keys without an LDS reorder (the
                                                // segmented first pass keeps the reorder)
 
