@@ -8,7 +8,9 @@ resident in HBM.  Also reported: render FPS (preprocess + bin/sort + raster) and
 (raster only, binning reused); kernel times from HIP events on the launch stream over passes of the
 fused raster kernel (and of the separate forward / backward kernels) on the trained parameters'
 binning; the roofline of the dominant kernel; and the CPU oracle timed on a bounded pixel sample of
-the same workload.
+the same workload.  With an alpha-compositing workload (--workload alpha_2048x2048_500k) a step is
+binning + alpha forward + L2 loss + alpha backward + Adam, and the roofline is that of the slower
+of the alpha forward / backward kernels.
 
 usage: python bench.py [--gpus 1] [--steps 2800] [--warmup 50] [--workload NAME] [--no-cpu-baseline]
 """
@@ -31,6 +33,8 @@ PEAK_FP32 = 157.3          # TFLOP/s, MI355X FP32 vector (AMD published)
 PEAK_HBM = 8000.0          # GB/s
 FLOP_FWD = 17              # per binned pair: dx, dy 2; cutoff exponent 7; scale + exp2 2; 3 colour FMA 6
 FLOP_BWD = 32              # per binned pair (recompute 11, colour/h 9, mean/conic partials 11, reduce 1)
+FLOP_FWD_ALPHA = 21        # per binned pair: the sum forward's 17 + alpha, alpha T, T update and the stop test
+FLOP_BWD_ALPHA = 55        # per binned pair: recompute, T_j and the suffix colour, mean/conic/opacity partials
 
 
 def log(msg):
@@ -115,6 +119,162 @@ def cpu_baseline(wl, params, target_seconds=15.0):
             "seconds": round(t, 3)}
 
 
+def cpu_baseline_alpha(wl, params, logit, bg, target_seconds=15.0):
+    """The oracle's alpha compositing (brute force over all N Gaussians per pixel, fp64) on a bounded
+    pixel sample: render + analytic gradient of the same pixels, extrapolated to one full-frame step."""
+    import oracle
+    W, H = wl.width, wl.height
+    p64, l64, b64 = params.astype(np.float64), logit.astype(np.float64), bg.astype(np.float64)
+    rng = np.random.default_rng(12345)
+    G = np.zeros((3, H, W))
+
+    def run(npix):
+        idx = rng.choice(W * H, size=npix, replace=False)
+        pix = np.stack([idx // W, idx % W], 1).astype(np.int32)
+        G[:] = 0.0
+        G[:, pix[:, 0], pix[:, 1]] = rng.normal(size=(3, npix))
+        t0 = time.perf_counter()
+        oracle.render_alpha(W, H, p64, l64, b64, pixels=pix)
+        oracle.grad_alpha(W, H, p64, l64, b64, G)
+        return time.perf_counter() - t0
+
+    run(16)
+    npix = 64
+    t = run(npix)
+    while t < 0.6 * target_seconds and npix < W * H:
+        npix = int(min(W * H, npix * min(16.0, max(2.0, target_seconds / max(t, 1e-3)))))
+        t = run(npix)
+    per_frame = t * (W * H) / npix
+    return {"value": 1.0 / per_frame, "unit": "fwd+bwd steps/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{npix} random pixels of the {W}x{H} frame, all {params.shape[0]} Gaussians per pixel "
+                      f"(alpha render + gradient), {t:.1f} s, extrapolated linearly to the full frame",
+            "seconds": round(t, 3)}
+
+
+def bench_alpha(args, w, target, params, dev):
+    """The alpha-compositing workload: one step = bin (with preprocess) + alpha forward + L2 loss +
+    alpha backward + Adam on the parameters, logits and background (separate launches)."""
+    import torch
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter, Raster
+
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    logit = torch.from_numpy(w["logit"]).to(dev)
+    bg = torch.from_numpy(w["background"]).to(dev)
+    fit = Fitter(target, params, logit=logit, background=bg, capacity_slack=2.0)
+    for _ in range(args.warmup):
+        fit.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fit.step()
+    torch.cuda.synchronize()
+    t_train = time.perf_counter() - t0
+    r = fit.raster
+    M_now = int(r.d_num.cpu().item()) & 0xFFFFFFFF
+    assert M_now <= r.capacity, "tile-pair capacity exceeded during the timed run"
+    ms_step = 1e3 * t_train / args.steps
+    final_loss = float(fit.loss.item())
+    log(f"[bench] train: {ms_step:.4f} ms/step, loss {final_loss:.4e}")
+
+    # kernel timing: HIP events on the launch stream around the alpha forward and backward kernels
+    rend = Raster(W, H, wl.n, gi.MODE_ALPHA)
+    rend.preprocess(fit.params, fit.logit)
+    M = rend.bin(sync=True)
+    rend.set_capacity(int(M * 1.5) + 4096)
+    rend.bin(sync=True, order=True, params=fit.params, logit=fit.logit)
+    bg4 = fit.bg4
+    dL = torch.empty_like(target)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    loss_ws = torch.empty(gi.gi_loss_workspace_bytes(target.numel()), dtype=torch.uint8, device=dev)
+    rend.forward(bg4)
+    gi.gi_loss_l2(target.numel(), rend.image, target, dL, loss, loss_ws)
+    grad = torch.zeros_like(fit.params)
+    dlogit = torch.zeros_like(fit.logit)
+    dbg = torch.zeros(4, dtype=torch.float32, device=dev)
+    nk = max(20, min(args.steps, 200))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E() for _ in range(3)] for _ in range(nk)]
+    for k in range(nk):
+        ev[k][0].record()
+        rend.forward(bg4)
+        ev[k][1].record()
+        rend.backward(dL, grad, logit=fit.logit, background=bg4, dlogit=dlogit, dbackground=dbg)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    fwd_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])
+    bwd_ms = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(nk)])
+    log(f"[bench] alpha fwd {np.median(fwd_ms)*1e3:.1f} us, bwd {np.median(bwd_ms)*1e3:.1f} us")
+    reps = max(20, args.steps // 4)
+
+    def loop_time(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    t_render = loop_time(lambda: rend.render(fit.params, logit=fit.logit, background=bg4, sync=False))
+    t_cached = loop_time(lambda: rend.forward(bg4))
+    log(f"[bench] render {t_render*1e6:.1f} us ({1/t_render:.0f} FPS), cached raster {t_cached*1e6:.1f} us")
+
+    rend.preprocess(fit.params, fit.logit)
+    M = rend.bin(sync=True)
+    torch.cuda.synchronize()
+    ranges = rend.ranges.cpu().numpy().view(np.uint32)
+    pairs = binned_pairs(W, H, ranges)
+    t_fin = rend.t_final.cpu().numpy()
+    fwd_s = float(np.mean(fwd_ms)) * 1e-3
+    bwd_s = float(np.mean(bwd_ms)) * 1e-3
+
+    def roof(kname, flop, secs):
+        tf = flop * pairs / secs / 1e12
+        return {"bound": "alu", "kernel": kname, "achieved": round(tf, 3), "peak": PEAK_FP32, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_FP32, 4), "traffic": load_traffic("k_raster_alpha.hip", kname),
+                "avg_launch_us": round(secs * 1e6, 2)}
+
+    roof_fwd = roof("k_render_alpha_fwd", FLOP_FWD_ALPHA, fwd_s)
+    roof_bwd = roof("k_render_alpha_bwd", FLOP_BWD_ALPHA, bwd_s)
+    dominant, other = (roof_bwd, roof_fwd) if bwd_s >= fwd_s else (roof_fwd, roof_bwd)
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "fwd+bwd steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "width": W, "height": H, "gaussians": wl.n, "mode": "alpha",
+                   "tiles": int(rend.T), "tile_pairs": int(M), "binned_pixel_pairs": pairs,
+                   "pixels_stopped_early": int((t_fin < 1e-4).sum())},
+        "render_fps": round(1.0 / t_render, 1),
+        "mpix_per_s": round(W * H / t_render / 1e6, 1),
+        "cached_raster_fps": round(1.0 / t_cached, 1),
+        "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
+                  "roofline: HIP events on the launch stream around the alpha forward and backward kernels, "
+                  "on the trained parameters' binning",
+        "final_loss": final_loss,
+        "kernels_us": {"render_alpha_fwd": round(fwd_s * 1e6, 2), "render_alpha_bwd": round(bwd_s * 1e6, 2)},
+        "roofline": dominant,
+        "roofline_other": other,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a pixel sample ...")
+        out["cpu_baseline"] = cpu_baseline_alpha(wl, w["params"], w["logit"], w["background"])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,9 +302,9 @@ def main():
     dev = torch.device("cuda:0")
     target = torch.from_numpy(w["target"]).to(dev)
     params = torch.from_numpy(w["params"]).to(dev)
-    if wl.mode != "sum":
-        raise SystemExit("bench.py times the accumulated-sum workloads")
     log(f"[bench] {wlname}: {W}x{H}, N={wl.n}, steps={args.steps}, warmup={args.warmup}")
+    if wl.mode != "sum":
+        return bench_alpha(args, w, target, params, dev)
 
     if args.copy_calibration:
         a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
