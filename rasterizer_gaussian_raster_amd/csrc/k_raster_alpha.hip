@@ -17,11 +17,12 @@
 // Gaussian, and one scalar suffix accumulator gS = sum_k g_k S_k carries the
 // colour behind it (S_k = later contributions + T_final bg_k), so
 //   dL/dalpha_j = T_j (g . c_j) - gS / (1 - alpha_j),  gS += (g . c_j) alpha_j T_j.
-// The 9 per-pixel contributions of a Gaussian are summed over the wave with
-// DPP row ops and broadcasts (skipped when no pixel of the wave is covered) and
-// written over the entry's slot in the wave's own quadrant list; each list
-// entry then adds its four quadrant results in quadrant order and stores the
-// gradient at its emission slot for the per-Gaussian gather.  No atomics: the
+// The 9 per-pixel contributions of a Gaussian are summed over the wave for 8
+// entries at a time, by one butterfly transpose-reduce (skipped when no pixel of
+// the wave is covered), and written over the entries' slots in the wave's own
+// quadrant list; each list entry then adds its four quadrant sums in quadrant
+// order, turns them into the gradients of its record (linear in the sums) and
+// stores them at its emission slot for the per-Gaussian gather.  No atomics: the
 // gradients are bitwise reproducible.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
@@ -51,7 +52,8 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4]
                                            const float *__restrict__ opacity, const float *__restrict__ logit,
                                            const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
                                            uint64_t below, const uint32_t *__restrict__ offsets = nullptr,
-                                           uint32_t *eslot = nullptr, uint8_t (*qpos)[4] = nullptr) {
+                                           uint32_t *eslot = nullptr, uint8_t (*qpos)[4] = nullptr,
+                                           float4 *own = nullptr) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t idx = lo + tid;
     uint32_t qm = 0;
@@ -68,6 +70,7 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4]
         qm = quadrant_mask(bx, x0, y0);
         if (offsets) eslot[tid] = emit_slot(offsets[g], bx, x0 / kTile, y0 / kTile);
     }
+    if (own) *own = make_float4(rp.z, rp.w, rq.x, rr.z);     // a, b, c, so
     uint32_t rank[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -92,6 +95,36 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4]
     const int cnt = __builtin_amdgcn_readfirstlane(wq[0][wave] + wq[1][wave] + wq[2][wave] + wq[3][wave]);
     __syncthreads();
     return cnt;
+}
+
+// Butterfly transpose-reduce over the wave: lane l holds 64 values x[i]; on return lane l holds
+// the sum over all 64 lanes of x[l].  Each step sums pairs of values across a lane pair and keeps
+// one of them, by the lane's side: upper half / lower half (permlane32 swap), odd / even row
+// (permlane16 swap), then row mirror, half-row mirror and two quad permutations (DPP).  63 + 63
+// swaps / moves and adds per 64 sums, against 64 x 6 for 64 separate reductions.
+template <int N>
+__device__ __forceinline__ void bfly_swap32(float (&x)[2 * N], float (&y)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N]), false, false);
+        y[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+template <int N>
+__device__ __forceinline__ void bfly_swap16(float (&x)[2 * N], float (&y)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N]), false, false);
+        y[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+template <int CTRL, int N>
+__device__ __forceinline__ void bfly_dpp(float (&x)[2 * N], float (&y)[N], bool low) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float keep = low ? x[i] : x[i + N], send = low ? x[i + N] : x[i];
+        y[i] = keep + dpp_f<CTRL>(send);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tiles_x, int ntiles,
@@ -230,64 +263,87 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
     for (uint32_t hi = bend0; hi > rg.x;) {
         const uint32_t lo = hi - rg.x > (uint32_t)kBatch ? hi - kBatch : rg.x;
         __syncthreads();                                   // previous batch fully consumed
+        float4 own;
         const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, records, opacity, logit, pixbox, vals, below,
-                                    offsets, eslot, qpos);
+                                    offsets, eslot, qpos, &own);
         const AlphaRec *L = lst[wave];
-        for (int k = cnt - 1; k >= 0; --k) {
-            const float4 A = L[k].p, B = L[k].q, R = L[k].r;
-            const uint32_t pos = __float_as_uint(R.y);
-            const float dx = px - A.x, dy = py - A.y;
-            const float u = A.z * dx;
-            const float tb = A.w * dx;
-            const float v = fmaf(B.x, dy, tb);
-            const float e = fmaf(v, v, u * u);
-            const bool act = pos < lp && e <= kE9;
-            float *res = reinterpret_cast<float *>(&lst[wave][k]);   // this wave is done reading entry k
-            if (__ballot(act) == 0) {                                  // uniform
-                if (lane == 0) {
-                    lst[wave][k].p = make_float4(0.f, 0.f, 0.f, 0.f);
-                    lst[wave][k].q = make_float4(0.f, 0.f, 0.f, 0.f);
-                    res[8] = 0.0f;
+        float *res = reinterpret_cast<float *>(&lst[wave][0]);   // entry k's results: res[12 k + 0..8]
+        // groups of 8 entries, back to front; per pixel and entry 9 values (the pixel's parts of
+        // sum h u, h v, h u dx, h v dx, h v dy, g aT (3), dL/dalpha w), reduced over the wave together
+        for (int k0 = cnt - 1; k0 >= 0; k0 -= 8) {
+            float x[64], xo[8];
+            bool any = false;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[8 * j + c] = 0.0f;
+                xo[j] = 0.0f;
+                const int k = k0 - j;
+                if (k < 0) continue;                                  // uniform
+                const float4 A = L[k].p, B = L[k].q, R = L[k].r;
+                const uint32_t pos = __float_as_uint(R.y);
+                const float dx = px - A.x, dy = py - A.y;
+                const float u = A.z * dx;
+                const float tb = A.w * dx;
+                const float v = fmaf(B.x, dy, tb);
+                const float e = fmaf(v, v, u * u);
+                const bool act = pos < lp && e <= kE9;
+                if (__ballot(act) == 0) continue;                     // uniform
+                any = true;
+                if (act) {
+                    const float w = exp2_hw(-e);
+                    const float al = R.x * w;
+                    const float rinv = __builtin_amdgcn_rcpf(1.0f - al);
+                    const float Tj = T * rinv;
+                    const float aTj = al * Tj;
+                    const float gc = fmaf(gb, B.w, fmaf(gg, B.z, gr * B.y));
+                    const float dal = fmaf(Tj, gc, -(rinv * gS));
+                    gS = fmaf(gc, aTj, gS);
+                    T = Tj;
+                    const float h = dal * al;                         // dL/dw * w, with dL/dw = dal * o
+                    const float hu = h * u, hv = h * v;
+                    x[8 * j + 0] = hu;
+                    x[8 * j + 1] = hv;
+                    x[8 * j + 2] = hu * dx;
+                    x[8 * j + 3] = hv * dx;
+                    x[8 * j + 4] = hv * dy;
+                    x[8 * j + 5] = gr * aTj;
+                    x[8 * j + 6] = gg * aTj;
+                    x[8 * j + 7] = gb * aTj;
+                    xo[j] = dal * w;
+                }
+            }
+            const int kk = k0 - (lane >> 3);                          // this lane's entry after the reduce
+            if (!any) {                                               // uniform: no pixel met these entries
+                if (kk >= 0) {
+                    res[12 * kk + (lane & 7)] = 0.0f;
+                    if ((lane & 7) == 0) res[12 * kk + 8] = 0.0f;
                 }
                 continue;
             }
-            float dcr = 0.f, dcg = 0.f, dcb = 0.f, hu = 0.f, hv = 0.f, hudx = 0.f, hvdx = 0.f, hvdy = 0.f, dlg = 0.f;
-            if (act) {
-                const float w = exp2_hw(-e);
-                const float al = R.x * w;
-                const float rinv = __builtin_amdgcn_rcpf(1.0f - al);
-                const float Tj = T * rinv;
-                const float aTj = al * Tj;
-                dcr = gr * aTj;
-                dcg = gg * aTj;
-                dcb = gb * aTj;
-                const float gc = fmaf(gb, B.w, fmaf(gg, B.z, gr * B.y));
-                const float dal = fmaf(Tj, gc, -(rinv * gS));
-                gS = fmaf(gc, aTj, gS);
-                T = Tj;
-                const float h = dal * al;                  // dL/dw * w, with dL/dw = dal * o
-                hu = h * u;
-                hv = h * v;
-                hudx = hu * dx;
-                hvdx = hv * dx;
-                hvdy = hv * dy;
-                dlg = dal * w * R.z;
-            }
-            const float Hu = wave_total(hu), Hv = wave_total(hv), Hudx = wave_total(hudx);
-            const float Hvdx = wave_total(hvdx), Hvdy = wave_total(hvdy);
-            const float Cr = wave_total(dcr), Cg = wave_total(dcg), Cb = wave_total(dcb);
-            const float Dl = wave_total(dlg);
-            if (lane == 0) {
-                const float a = A.z, b = A.w, c = B.x;
-                const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                lst[wave][k].p = make_float4(k2 * fmaf(a, Hu, b * Hv), k2 * c * Hv, -is * fmaf(a * a, da, a * b * db),
-                                             -is * (a * c * db));
-                lst[wave][k].q = make_float4(-is * fmaf(b * c, db, c * c * dc), Cr, Cg, Cb);
-                res[8] = Dl;
+            float y32[32], y16[16], y8[8], y4[4], y2[2], y1[1];
+            bfly_swap32<32>(x, y32);
+            bfly_swap16<16>(y32, y16);
+            bfly_dpp<0x140, 8>(y16, y8, (lane & 8) == 0);             // row mirror
+            bfly_dpp<0x141, 4>(y8, y4, (lane & 4) == 0);              // half-row mirror
+            bfly_dpp<0x4e, 2>(y4, y2, (lane & 2) == 0);               // quad: lanes ^ 2
+            bfly_dpp<0xb1, 1>(y2, y1, (lane & 1) == 0);               // quad: lanes ^ 1
+            // the entries' dL/dalpha w: 8 values, summed within each 8-lane group after three steps
+            float o4[4], o2[2], o1[1];
+            bfly_swap32<4>(xo, o4);
+            bfly_swap16<2>(o4, o2);
+            bfly_dpp<0x140, 1>(o2, o1, (lane & 8) == 0);
+            float ot = o1[0];
+            ot += dpp_f<0x141>(ot);
+            ot += dpp_f<0x4e>(ot);
+            ot += dpp_f<0xb1>(ot);
+            if (kk >= 0) {                                            // lane l: entry k0 - l/8, value l%8
+                res[12 * kk + (lane & 7)] = y1[0];
+                if ((lane & 7) == 0) res[12 * kk + 8] = ot;
             }
         }
         __syncthreads();
-        if (tid < kBatch && lo + tid < hi) {      // quadrant results of this entry, added in quadrant order
+        if (tid < kBatch && lo + tid < hi) {      // quadrant sums of this entry, added in quadrant order
             float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
             float sl = 0.f;
 #pragma unroll
@@ -300,11 +356,18 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                     sl += lst[q][k].r.x;
                 }
             }
+            // e = u^2 + v^2, w = 2^-e: dL/de = -ln2 h, summed through (Hu, Hv, ...); then
+            // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22); dL/dlogit = so sum dL/dalpha w
+            const float a = own.x, b = own.y, c = own.z;
+            const float da = -k2 * s0.z, db = -k2 * s0.w, dc = -k2 * s1.x;
+            const float4 d0 = make_float4(k2 * fmaf(a, s0.x, b * s0.y), k2 * c * s0.y,
+                                          -is * fmaf(a * a, da, a * b * db), -is * (a * c * db));
+            const float4 d1 = make_float4(-is * fmaf(b * c, db, c * c * dc), s1.y, s1.z, s1.w);
             const uint32_t slot = eslot[tid];
             if (slot < capacity) {
-                part[2 * (size_t)slot] = s0;
-                part[2 * (size_t)slot + 1] = s1;
-                part_l[slot] = sl;
+                part[2 * (size_t)slot] = d0;
+                part[2 * (size_t)slot + 1] = d1;
+                part_l[slot] = own.w * sl;
             }
         }
         hi = lo;
