@@ -164,16 +164,17 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
             const float tb = A.w * dx;
             const float v = fmaf(B.x, dy, tb);
             const float e = fmaf(v, v, u * u);
-            if (!done && e <= kE9) {
-                const float al = R.x * exp2_hw(-e);
-                const float aT = al * T;
-                cr = fmaf(B.y, aT, cr);
-                cg = fmaf(B.z, aT, cg);
-                cb = fmaf(B.w, aT, cb);
-                T -= aT;
-                lst_end = __float_as_uint(R.y) + 1u;
-                done = T < kTmin;
-            }
+            // without a branch: alpha = 0 leaves T and the colour unchanged (a running sum from +0
+            // never becomes -0, so adding c * 0 keeps its bits)
+            const bool act = !done && e <= kE9;
+            const float al = act ? R.x * exp2_hw(-e) : 0.0f;
+            const float aT = al * T;
+            cr = fmaf(B.y, aT, cr);
+            cg = fmaf(B.z, aT, cg);
+            cb = fmaf(B.w, aT, cb);
+            T -= aT;
+            lst_end = act ? __float_as_uint(R.y) + 1u : lst_end;
+            done = T < kTmin;
         }
         const bool wave_done = __ballot(!done) == 0;        // all lanes vote (outside any branch)
         if (lane == 0) wdone[wave] = wave_done;
@@ -275,11 +276,13 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
             bool any = false;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-#pragma unroll
-                for (int c = 0; c < 8; ++c) x[8 * j + c] = 0.0f;
-                xo[j] = 0.0f;
                 const int k = k0 - j;
-                if (k < 0) continue;                                  // uniform
+                if (k < 0) {                                          // uniform
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) x[8 * j + c] = 0.0f;
+                    xo[j] = 0.0f;
+                    continue;
+                }
                 const float4 A = L[k].p, B = L[k].q, R = L[k].r;
                 const uint32_t pos = __float_as_uint(R.y);
                 const float dx = px - A.x, dy = py - A.y;
@@ -288,10 +291,15 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                 const float v = fmaf(B.x, dy, tb);
                 const float e = fmaf(v, v, u * u);
                 const bool act = pos < lp && e <= kE9;
-                if (__ballot(act) == 0) continue;                     // uniform
+                if (__ballot(act) == 0) {                             // uniform
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) x[8 * j + c] = 0.0f;
+                    xo[j] = 0.0f;
+                    continue;
+                }
                 any = true;
-                if (act) {
-                    const float w = exp2_hw(-e);
+                {   // without a branch: w = 0 gives rinv = 1, T and gS unchanged and zero contributions
+                    const float w = act ? exp2_hw(-e) : 0.0f;
                     const float al = R.x * w;
                     const float rinv = __builtin_amdgcn_rcpf(1.0f - al);
                     const float Tj = T * rinv;
