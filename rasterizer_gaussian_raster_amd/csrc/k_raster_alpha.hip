@@ -2,11 +2,12 @@
 // ("Drawing with Gaussians", Overview: anisotropic 2D Gaussians alpha-composited
 // over a trainable background; fused kernels with custom VJPs) and its backward.
 //
-// Layout as the sum forward: one workgroup per 16x16 tile, wave w owns the 8x8
-// quadrant (w & 1, w >> 1), one pixel per lane, the tile list staged 128 at a
-// time and compacted per quadrant in list order.  A Gaussian dropped for a
-// quadrant has alpha = 0 at every pixel there, so T and C are unchanged by it:
-// compaction keeps the results bit for bit.
+// Layout: one workgroup of two waves per 16x16 tile; wave w owns the 8x16 half
+// of columns 8w .. 8w + 7, two pixels per lane (rows r and r + 8 of one column,
+// which share the Gaussian's x terms); the tile list is staged 128 entries at a
+// time, one per thread, and compacted per half in list order.  A Gaussian
+// dropped for a half has alpha = 0 at every pixel there, so T and C are
+// unchanged by it: compaction keeps the results bit for bit.
 //
 // Forward per admitted pair: alpha = o 2^-e, C += c alpha T, T -= alpha T; a
 // pixel stops after the Gaussian that leaves T < 1e-4 (recorded as `last`, one
@@ -31,34 +32,37 @@ namespace gi {
 
 struct AlphaRec { float4 p, q, r; };   // p = (mux, muy, a, b), q = (c, cr, cg, cb), r = (o, pos, so, g)
 
-constexpr int kBatch = 128;           // list entries staged per round (24 KB of LDS per workgroup)
+constexpr int kAlphaThreads = 128;    // two waves per tile
+constexpr int kBatch = kAlphaThreads; // list entries staged per round, one per thread (12 KB of LDS)
 
-__device__ __forceinline__ uint32_t quadrant_mask(uint2 bx, int x0, int y0) {
+// Halves of the tile at (x0, y0) that the pixel box meets: bit h for columns x0 + 8h .. x0 + 8h + 7.
+__device__ __forceinline__ uint32_t half_mask(uint2 bx, int x0, int y0) {
     const int j0 = bx.x & 0xffff, i0 = bx.x >> 16, j1 = bx.y & 0xffff, i1 = bx.y >> 16;
-    uint32_t qm = 0;
+    if (i0 > y0 + 15 || i1 < y0) return 0u;
+    uint32_t m = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int qx0 = x0 + (q & 1) * 8, qy0 = y0 + (q >> 1) * 8;
-        qm |= (j0 <= qx0 + 7 && j1 >= qx0 && i0 <= qy0 + 7 && i1 >= qy0) ? (1u << q) : 0u;
+    for (int h = 0; h < 2; ++h) {
+        const int hx0 = x0 + 8 * h;
+        m |= (j0 <= hx0 + 7 && j1 >= hx0) ? (1u << h) : 0u;
     }
-    return qm;
+    return m;
 }
 
-// Stage list entries [lo, hi) (hi - lo <= kBatch) into the per-quadrant lists; returns this wave's count.
-// Backward only (offsets != nullptr): also the entry's emission slot -> eslot[tid]
-// and its position in each quadrant list -> qpos[tid][q] (0xff: not in that list).
-__device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4], uint32_t lo, uint32_t hi, int x0,
+// Stage list entries [lo, hi) (hi - lo <= kBatch) into the per-half lists; returns this wave's count.
+// Backward only (offsets != nullptr): also the entry's emission slot -> eslot[tid], its position
+// in each half's list -> qpos[tid][h] (0xff: not in that list) and its (a, b, c, so) -> *own.
+__device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[2], uint32_t lo, uint32_t hi, int x0,
                                            int y0, const float4 *__restrict__ records,
                                            const float *__restrict__ opacity, const float *__restrict__ logit,
                                            const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
                                            uint64_t below, const uint32_t *__restrict__ offsets = nullptr,
-                                           uint32_t *eslot = nullptr, uint8_t (*qpos)[4] = nullptr,
+                                           uint32_t *eslot = nullptr, uint8_t (*qpos)[2] = nullptr,
                                            float4 *own = nullptr) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t idx = lo + tid;
-    uint32_t qm = 0;
+    uint32_t hm = 0;
     float4 rp = make_float4(0.f, 0.f, 0.f, 0.f), rq = rp, rr = rp;
-    if (tid < kBatch && idx < hi) {
+    if (idx < hi) {
         const uint32_t g = vals[idx];
         rp = records[2 * g];
         rq = records[2 * g + 1];
@@ -67,32 +71,31 @@ __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[4]
         if (logit) so = logit[g] < kLogitMax ? o * (1.0f - o) : 0.0f;
         rr = make_float4(o, __uint_as_float(idx), so, __uint_as_float(g));
         const uint2 bx = pixbox[g];
-        qm = quadrant_mask(bx, x0, y0);
+        hm = half_mask(bx, x0, y0);
         if (offsets) eslot[tid] = emit_slot(offsets[g], bx, x0 / kTile, y0 / kTile);
     }
     if (own) *own = make_float4(rp.z, rp.w, rq.x, rr.z);     // a, b, c, so
-    uint32_t rank[4];
+    uint32_t rank[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint64_t m = __ballot((qm >> q) & 1u);
-        rank[q] = (uint32_t)__popcll(m & below);
-        if (lane == 0) wq[wave][q] = __popcll(m);
+    for (int h = 0; h < 2; ++h) {
+        const uint64_t m = __ballot((hm >> h) & 1u);
+        rank[h] = (uint32_t)__popcll(m & below);
+        if (lane == 0) wq[wave][h] = __popcll(m);
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if ((qm >> q) & 1u) {
-            int off = rank[q];
-            for (int w = 0; w < wave; ++w) off += wq[w][q];
-            lst[q][off].p = rp;
-            lst[q][off].q = rq;
-            lst[q][off].r = rr;
-            if (qpos) qpos[tid][q] = (uint8_t)off;
-        } else if (qpos && tid < kBatch) {
-            qpos[tid][q] = 0xff;
+    for (int h = 0; h < 2; ++h) {
+        if ((hm >> h) & 1u) {
+            const int off = (int)rank[h] + (wave ? wq[0][h] : 0);
+            lst[h][off].p = rp;
+            lst[h][off].q = rq;
+            lst[h][off].r = rr;
+            if (qpos) qpos[tid][h] = (uint8_t)off;
+        } else if (qpos) {
+            qpos[tid][h] = 0xff;
         }
     }
-    const int cnt = __builtin_amdgcn_readfirstlane(wq[0][wave] + wq[1][wave] + wq[2][wave] + wq[3][wave]);
+    const int cnt = __builtin_amdgcn_readfirstlane(wq[0][wave] + wq[1][wave]);
     __syncthreads();
     return cnt;
 }
@@ -127,7 +130,7 @@ __device__ __forceinline__ void bfly_dpp(float (&x)[2 * N], float (&y)[N], bool 
     }
 }
 
-__global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tiles_x, int ntiles,
+__global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_fwd(int W, int H, int tiles_x, int ntiles,
                                                           const float4 *__restrict__ records,
                                                           const float *__restrict__ opacity,
                                                           const uint2 *__restrict__ pixbox,
@@ -136,63 +139,98 @@ __global__ __launch_bounds__(256) void k_render_alpha_fwd(int W, int H, int tile
                                                           const float *__restrict__ bg,
                                                           float *__restrict__ image, float *__restrict__ t_final,
                                                           uint32_t *__restrict__ last) {
-    __shared__ AlphaRec lst[4][kBatch];
-    __shared__ int wq[4][4];
-    __shared__ int wdone[4];
+    __shared__ AlphaRec lst[2][kBatch];
+    __shared__ int wq[2][2];
+    __shared__ int wdone[2];
     const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
-    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
-    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    const int pxi = x0 + wave * 8 + (lane & 7);
+    const int pyi = y0 + (lane >> 3);                     // the lane's upper pixel; the lower one is 8 rows down
+    const float px = (float)pxi + 0.5f, py0 = (float)pyi + 0.5f, py1 = (float)(pyi + 8) + 0.5f;
     const uint2 rg = ranges[t];
     const uint64_t below = lanes_below();
-    float T = 1.0f, cr = 0.f, cg = 0.f, cb = 0.f;
-    uint32_t lst_end = rg.x;
-    bool done = false;
+    float T0 = 1.0f, r0 = 0.f, g0 = 0.f, b0 = 0.f, T1 = 1.0f, r1 = 0.f, g1 = 0.f, b1 = 0.f;
+    uint32_t end0 = rg.x, end1 = rg.x;
+    bool done0 = false, done1 = false;
 
     for (uint32_t base = rg.x; base < rg.y; base += kBatch) {
         const uint32_t hi = rg.y - base > (uint32_t)kBatch ? base + kBatch : rg.y;
         const int cnt = stage_alpha(lst, wq, base, hi, x0, y0, records, opacity, nullptr, pixbox, vals, below);
         const AlphaRec *L = lst[wave];
         for (int k = 0; k < cnt; ++k) {
-            if (__ballot(!done) == 0) break;
+            if (__ballot(!(done0 && done1)) == 0) break;
             const float4 A = L[k].p, B = L[k].q, R = L[k].r;
-            const float dx = px - A.x, dy = py - A.y;
+            const float dx = px - A.x;
             const float u = A.z * dx;
             const float tb = A.w * dx;
-            const float v = fmaf(B.x, dy, tb);
-            const float e = fmaf(v, v, u * u);
+            const float uu = u * u;
+            const float v0 = fmaf(B.x, py0 - A.y, tb), v1 = fmaf(B.x, py1 - A.y, tb);
+            const float e0 = fmaf(v0, v0, uu), e1 = fmaf(v1, v1, uu);
             // without a branch: alpha = 0 leaves T and the colour unchanged (a running sum from +0
             // never becomes -0, so adding c * 0 keeps its bits)
-            const bool act = !done && e <= kE9;
-            const float al = act ? R.x * exp2_hw(-e) : 0.0f;
-            const float aT = al * T;
-            cr = fmaf(B.y, aT, cr);
-            cg = fmaf(B.z, aT, cg);
-            cb = fmaf(B.w, aT, cb);
-            T -= aT;
-            lst_end = act ? __float_as_uint(R.y) + 1u : lst_end;
-            done = T < kTmin;
+            const bool a0 = !done0 && e0 <= kE9, a1 = !done1 && e1 <= kE9;
+            const float al0 = a0 ? R.x * exp2_hw(-e0) : 0.0f, al1 = a1 ? R.x * exp2_hw(-e1) : 0.0f;
+            const float aT0 = al0 * T0, aT1 = al1 * T1;
+            r0 = fmaf(B.y, aT0, r0);
+            g0 = fmaf(B.z, aT0, g0);
+            b0 = fmaf(B.w, aT0, b0);
+            r1 = fmaf(B.y, aT1, r1);
+            g1 = fmaf(B.z, aT1, g1);
+            b1 = fmaf(B.w, aT1, b1);
+            T0 -= aT0;
+            T1 -= aT1;
+            const uint32_t pe = __float_as_uint(R.y) + 1u;
+            end0 = a0 ? pe : end0;
+            end1 = a1 ? pe : end1;
+            done0 = T0 < kTmin;
+            done1 = T1 < kTmin;
         }
-        const bool wave_done = __ballot(!done) == 0;        // all lanes vote (outside any branch)
+        const bool wave_done = __ballot(!(done0 && done1)) == 0;   // all lanes vote (outside any branch)
         if (lane == 0) wdone[wave] = wave_done;
         if (hi >= rg.y) break;
         __syncthreads();
-        if (wdone[0] && wdone[1] && wdone[2] && wdone[3]) break;   // uniform
+        if (wdone[0] && wdone[1]) break;                   // uniform
     }
+    const size_t plane = (size_t)W * H;
     if (pxi < W && pyi < H) {
-        const size_t o = (size_t)pyi * W + pxi, plane = (size_t)W * H;
-        image[o] = fmaf(T, bg[0], cr);
-        image[o + plane] = fmaf(T, bg[1], cg);
-        image[o + 2 * plane] = fmaf(T, bg[2], cb);
-        t_final[o] = T;
-        last[o] = lst_end;
+        const size_t o = (size_t)pyi * W + pxi;
+        image[o] = fmaf(T0, bg[0], r0);
+        image[o + plane] = fmaf(T0, bg[1], g0);
+        image[o + 2 * plane] = fmaf(T0, bg[2], b0);
+        t_final[o] = T0;
+        last[o] = end0;
+    }
+    if (pxi < W && pyi + 8 < H) {
+        const size_t o = (size_t)(pyi + 8) * W + pxi;
+        image[o] = fmaf(T1, bg[0], r1);
+        image[o + plane] = fmaf(T1, bg[1], g1);
+        image[o + 2 * plane] = fmaf(T1, bg[2], b1);
+        t_final[o] = T1;
+        last[o] = end1;
     }
 }
 
-__global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tiles_x, int ntiles,
+// One pixel's step back over entry (A, B, R): w = 0 (not touched, or behind the pixel's stop) gives
+// rinv = 1, T and gS unchanged and zero contributions.  Returns h = dL/dw w (dL/dw = dL/dalpha o)
+// and the pixel's dL/dalpha w, alpha T (through refs).
+__device__ __forceinline__ float alpha_back_pixel(bool act, float e, float o, float gr, float gg, float gb,
+                                                  float4 B, float &T, float &gS, float &dalw, float &aT) {
+    const float w = act ? exp2_hw(-e) : 0.0f;
+    const float al = o * w;
+    const float rinv = __builtin_amdgcn_rcpf(1.0f - al);
+    const float Tj = T * rinv;
+    aT = al * Tj;
+    const float gc = fmaf(gb, B.w, fmaf(gg, B.z, gr * B.y));
+    const float dal = fmaf(Tj, gc, -(rinv * gS));
+    gS = fmaf(gc, aT, gS);
+    T = Tj;
+    dalw = dal * w;
+    return dal * al;
+}
+
+__global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H, int tiles_x, int ntiles,
                                                           const float4 *__restrict__ records,
                                                           const float *__restrict__ opacity,
                                                           const float *__restrict__ logit,
@@ -206,49 +244,56 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                                                           const float *__restrict__ dL,
                                                           float4 *__restrict__ part, float *__restrict__ part_l,
                                                           float4 *__restrict__ part_bg) {
-    __shared__ AlphaRec lst[4][kBatch];
-    __shared__ int wq[4][4];
-    __shared__ uint32_t wmax[4];
-    __shared__ float wbg[4][3];
+    __shared__ AlphaRec lst[2][kBatch];
+    __shared__ int wq[2][2];
+    __shared__ uint32_t wmax[2];
+    __shared__ float wbg[2][3];
     __shared__ uint32_t eslot[kBatch];
-    __shared__ uint8_t qpos[kBatch][4];
+    __shared__ uint8_t qpos[kBatch][2];
     const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
-    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
-    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    const int pxi = x0 + wave * 8 + (lane & 7);
+    const int pyi = y0 + (lane >> 3);                     // the lane's upper pixel; the lower one is 8 rows down
+    const float px = (float)pxi + 0.5f, py0 = (float)pyi + 0.5f, py1 = (float)(pyi + 8) + 0.5f;
     const uint2 rg = ranges[t];
     const uint64_t below = lanes_below();
-    const bool inside = pxi < W && pyi < H;
-    float T = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
-    uint32_t lp = rg.x;
-    if (inside) {
-        const size_t o = (size_t)pyi * W + pxi, plane = (size_t)W * H;
-        T = t_final[o];
-        lp = min(max(last[o], rg.x), rg.y);     // stays inside the tile's list whatever `last` holds
-        gr = dL[o];
-        gg = dL[o + plane];
-        gb = dL[o + 2 * plane];
+    const size_t plane = (size_t)W * H;
+    float T0 = 0.f, gr0 = 0.f, gg0 = 0.f, gb0 = 0.f, T1 = 0.f, gr1 = 0.f, gg1 = 0.f, gb1 = 0.f;
+    uint32_t lp0 = rg.x, lp1 = rg.x;
+    if (pxi < W && pyi < H) {
+        const size_t o = (size_t)pyi * W + pxi;
+        T0 = t_final[o];
+        lp0 = min(max(last[o], rg.x), rg.y);     // stays inside the tile's list whatever `last` holds
+        gr0 = dL[o];
+        gg0 = dL[o + plane];
+        gb0 = dL[o + 2 * plane];
+    }
+    if (pxi < W && pyi + 8 < H) {
+        const size_t o = (size_t)(pyi + 8) * W + pxi;
+        T1 = t_final[o];
+        lp1 = min(max(last[o], rg.x), rg.y);
+        gr1 = dL[o];
+        gg1 = dL[o + plane];
+        gb1 = dL[o + 2 * plane];
     }
     // dL/dbg_k = sum_p g_k T_final: one partial per tile
     {
-        const float sr = wave_total(gr * T), sg = wave_total(gg * T), sb = wave_total(gb * T);
+        const float sr = wave_total(fmaf(gr1, T1, gr0 * T0)), sg = wave_total(fmaf(gg1, T1, gg0 * T0));
+        const float sb = wave_total(fmaf(gb1, T1, gb0 * T0));
         if (lane == 0) { wbg[wave][0] = sr; wbg[wave][1] = sg; wbg[wave][2] = sb; }
-        uint32_t m = lp;
+        uint32_t m = max(lp0, lp1);
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
         if (lane == 0) wmax[wave] = m;
     }
     __syncthreads();
     if (tid == 0)
-        part_bg[t] = make_float4(((wbg[0][0] + wbg[1][0]) + wbg[2][0]) + wbg[3][0],
-                                 ((wbg[0][1] + wbg[1][1]) + wbg[2][1]) + wbg[3][1],
-                                 ((wbg[0][2] + wbg[1][2]) + wbg[2][2]) + wbg[3][2], 0.f);
-    const uint32_t bend0 = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+        part_bg[t] = make_float4(wbg[0][0] + wbg[1][0], wbg[0][1] + wbg[1][1], wbg[0][2] + wbg[1][2], 0.f);
+    const uint32_t bend0 = max(wmax[0], wmax[1]);
     // entries behind every pixel's stop contribute nothing: their slots get zeros
-    for (uint32_t idx = bend0 + tid; idx < rg.y; idx += 256) {
+    for (uint32_t idx = bend0 + tid; idx < rg.y; idx += kAlphaThreads) {
         const uint32_t g = vals[idx];
         const uint32_t slot = emit_slot(offsets[g], pixbox[g], x0 / kTile, y0 / kTile);
         if (slot < capacity) {
@@ -257,7 +302,8 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
             part_l[slot] = 0.f;
         }
     }
-    float gS = T * fmaf(gb, bg[2], fmaf(gg, bg[1], gr * bg[0]));
+    float gS0 = T0 * fmaf(gb0, bg[2], fmaf(gg0, bg[1], gr0 * bg[0]));
+    float gS1 = T1 * fmaf(gb1, bg[2], fmaf(gg1, bg[1], gr1 * bg[0]));
     const float k2 = 2.0f * kLn2;
     const float is = 1.0f / kScale;
 
@@ -269,8 +315,9 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                                     offsets, eslot, qpos, &own);
         const AlphaRec *L = lst[wave];
         float *res = reinterpret_cast<float *>(&lst[wave][0]);   // entry k's results: res[12 k + 0..8]
-        // groups of 8 entries, back to front; per pixel and entry 9 values (the pixel's parts of
-        // sum h u, h v, h u dx, h v dx, h v dy, g aT (3), dL/dalpha w), reduced over the wave together
+        // groups of 8 entries, back to front; per lane (two pixels) and entry 9 values (the pixels'
+        // parts of sum h u, h v, h u dx, h v dx, h v dy, g aT (3), dL/dalpha w), reduced over the
+        // wave together
         for (int k0 = cnt - 1; k0 >= 0; k0 -= 8) {
             float x[64], xo[8];
             bool any = false;
@@ -285,41 +332,36 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
                 }
                 const float4 A = L[k].p, B = L[k].q, R = L[k].r;
                 const uint32_t pos = __float_as_uint(R.y);
-                const float dx = px - A.x, dy = py - A.y;
+                const float dx = px - A.x;
+                const float dy0 = py0 - A.y, dy1 = py1 - A.y;
                 const float u = A.z * dx;
                 const float tb = A.w * dx;
-                const float v = fmaf(B.x, dy, tb);
-                const float e = fmaf(v, v, u * u);
-                const bool act = pos < lp && e <= kE9;
-                if (__ballot(act) == 0) {                             // uniform
+                const float uu = u * u;
+                const float v0 = fmaf(B.x, dy0, tb), v1 = fmaf(B.x, dy1, tb);
+                const float e0 = fmaf(v0, v0, uu), e1 = fmaf(v1, v1, uu);
+                const bool act0 = pos < lp0 && e0 <= kE9, act1 = pos < lp1 && e1 <= kE9;
+                if (__ballot(act0 || act1) == 0) {                    // uniform
 #pragma unroll
                     for (int c = 0; c < 8; ++c) x[8 * j + c] = 0.0f;
                     xo[j] = 0.0f;
                     continue;
                 }
                 any = true;
-                {   // without a branch: w = 0 gives rinv = 1, T and gS unchanged and zero contributions
-                    const float w = act ? exp2_hw(-e) : 0.0f;
-                    const float al = R.x * w;
-                    const float rinv = __builtin_amdgcn_rcpf(1.0f - al);
-                    const float Tj = T * rinv;
-                    const float aTj = al * Tj;
-                    const float gc = fmaf(gb, B.w, fmaf(gg, B.z, gr * B.y));
-                    const float dal = fmaf(Tj, gc, -(rinv * gS));
-                    gS = fmaf(gc, aTj, gS);
-                    T = Tj;
-                    const float h = dal * al;                         // dL/dw * w, with dL/dw = dal * o
-                    const float hu = h * u, hv = h * v;
-                    x[8 * j + 0] = hu;
-                    x[8 * j + 1] = hv;
-                    x[8 * j + 2] = hu * dx;
-                    x[8 * j + 3] = hv * dx;
-                    x[8 * j + 4] = hv * dy;
-                    x[8 * j + 5] = gr * aTj;
-                    x[8 * j + 6] = gg * aTj;
-                    x[8 * j + 7] = gb * aTj;
-                    xo[j] = dal * w;
-                }
+                float dw0, dw1, aT0, aT1;
+                const float h0 = alpha_back_pixel(act0, e0, R.x, gr0, gg0, gb0, B, T0, gS0, dw0, aT0);
+                const float h1 = alpha_back_pixel(act1, e1, R.x, gr1, gg1, gb1, B, T1, gS1, dw1, aT1);
+                const float hu = u * (h0 + h1);                       // u and dx are the two pixels'
+                const float hv0 = h0 * v0, hv1 = h1 * v1;
+                const float hv = hv0 + hv1;
+                x[8 * j + 0] = hu;
+                x[8 * j + 1] = hv;
+                x[8 * j + 2] = hu * dx;
+                x[8 * j + 3] = hv * dx;
+                x[8 * j + 4] = fmaf(hv1, dy1, hv0 * dy0);
+                x[8 * j + 5] = fmaf(gr1, aT1, gr0 * aT0);
+                x[8 * j + 6] = fmaf(gg1, aT1, gg0 * aT0);
+                x[8 * j + 7] = fmaf(gb1, aT1, gb0 * aT0);
+                xo[j] = dw0 + dw1;
             }
             const int kk = k0 - (lane >> 3);                          // this lane's entry after the reduce
             if (!any) {                                               // uniform: no pixel met these entries
@@ -351,17 +393,17 @@ __global__ __launch_bounds__(256) void k_render_alpha_bwd(int W, int H, int tile
             }
         }
         __syncthreads();
-        if (tid < kBatch && lo + tid < hi) {      // quadrant sums of this entry, added in quadrant order
+        if (lo + tid < hi) {                      // the two halves' sums of this entry, added in order
             float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
             float sl = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k = qpos[tid][q];
+            for (int h = 0; h < 2; ++h) {
+                const int k = qpos[tid][h];
                 if (k != 0xff) {
-                    const float4 u0 = lst[q][k].p, u1 = lst[q][k].q;
+                    const float4 u0 = lst[h][k].p, u1 = lst[h][k].q;
                     s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
                     s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
-                    sl += lst[q][k].r.x;
+                    sl += lst[h][k].r.x;
                 }
             }
             // e = u^2 + v^2, w = 2^-e: dL/de = -ln2 h, summed through (Hu, Hv, ...); then
@@ -389,7 +431,7 @@ hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const flo
                                    const uint32_t *vals, const float *background, float *image, float *t_final,
                                    uint32_t *last, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
-    k_render_alpha_fwd<<<padded_tiles(ntiles), 256, 0, s>>>(
+    k_render_alpha_fwd<<<padded_tiles(ntiles), kAlphaThreads, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity,
         reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), order, vals, background,
         image, t_final, last);
@@ -405,7 +447,7 @@ hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const flo
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     char *w = static_cast<char *>(ws);
-    k_render_alpha_bwd<<<padded_tiles(ntiles), 256, 0, s>>>(
+    k_render_alpha_bwd<<<padded_tiles(ntiles), kAlphaThreads, 0, s>>>(
         W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity, logit,
         reinterpret_cast<const uint2 *>(pixbox), offsets, reinterpret_cast<const uint2 *>(ranges), order, vals,
         (uint32_t)capacity, background, t_final, last, dL_dimage, reinterpret_cast<float4 *>(w + p.off_part),
