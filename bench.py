@@ -303,8 +303,6 @@ def main():
     target = torch.from_numpy(w["target"]).to(dev)
     params = torch.from_numpy(w["params"]).to(dev)
     log(f"[bench] {wlname}: {W}x{H}, N={wl.n}, steps={args.steps}, warmup={args.warmup}")
-    if wl.mode != "sum":
-        return bench_alpha(args, w, target, params, dev)
 
     if args.copy_calibration:
         a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
@@ -314,6 +312,8 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 256 MiB device-to-device copies")
+    if wl.mode != "sum":
+        return bench_alpha(args, w, target, params, dev)
 
     # ---------------- training step (the whole hot path) ----------------
     fit = Fitter(target, params, capacity_slack=2.0)
