@@ -13,7 +13,10 @@ header states the definitions and the pages they come from.
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, a library normal density, exact rational arithmetic for the
 fp32 cutoff, numpy's stable sort for the bin order, central finite
-differences, torch's Adam).  No function is "parity unpinned".
+differences, torch's Adam; for the rotation-scale form and rendering at another
+scale: numpy's Cholesky factor fed to the Cholesky-form oracle, rotation
+symmetries, numpy's matrix inverse for the cutoff set).  No function is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -75,6 +78,11 @@ def _load():
     lib.oracle_adam.argtypes = [i64, i32, P, P, P, P, P, ctypes.c_double, ctypes.c_double,
                                 ctypes.c_double, i32]
     lib.oracle_adam.restype = None
+    f64 = ctypes.c_double
+    lib.oracle_render_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i64, i32, P, P, P]
+    lib.oracle_render_sum_rs.restype = None
+    lib.oracle_grad_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i32, P, P, P]
+    lib.oracle_grad_sum_rs.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = i32
     _lib = lib
@@ -219,6 +227,33 @@ def grad_alpha(W, H, params, logit, bg, dL_dI, force_last=None, with_cond=False)
     _load().oracle_grad_alpha(W, H, n, _p(par), _p(lg), _p(b), _p(G), _p(fl), _p(d), _p(dl), _p(dbg),
                               _p(a), _p(c))
     return (d, dl, dbg, a, c) if with_cond else (d, dl, dbg, a)
+
+
+def render_sum_rs(W, H, params_rs, fx=1.0, fy=1.0, pixels=None, cutoff=True):
+    """Sum image of rotation-scale Gaussians (mux, muy, sx, sy, theta, cr, cg, cb) rendered at scale
+    (fx, fy) into a W x H image.  Returns (image, sabs, amb): [3,H,W] for all pixels or [3,P] for a
+    pixel list; amb = sum |c| w over the pairs whose cutoff decision is ambiguous in fp32."""
+    par = _f64(params_rs).reshape(-1, 8)
+    pix = _pix(pixels)
+    npix = W * H if pix is None else pix.shape[0]
+    out, sabs, amb = np.zeros((3, npix)), np.zeros((3, npix)), np.zeros((3, npix))
+    _load().oracle_render_sum_rs(W, H, par.shape[0], _p(par), float(fx), float(fy), _p(pix), npix,
+                                 1 if cutoff else 0, _p(out), _p(sabs), _p(amb))
+    if pix is None:
+        return out.reshape(3, H, W), sabs.reshape(3, H, W), amb.reshape(3, H, W)
+    return out, sabs, amb
+
+
+def grad_sum_rs(W, H, params_rs, dL_dI, fx=1.0, fy=1.0, cutoff=True):
+    """(dparams [N,8], running-error scale [N,8], ambiguous-pair magnitude [N,8]) of
+    L = <dL_dI, I> for the rotation-scale sum image rendered at scale (fx, fy)."""
+    par = _f64(params_rs).reshape(-1, 8)
+    G = _f64(dL_dI).reshape(3, H, W)
+    n = par.shape[0]
+    d, c, a = np.zeros((n, 8)), np.zeros((n, 8)), np.zeros((n, 8))
+    _load().oracle_grad_sum_rs(W, H, n, _p(par), float(fx), float(fy), _p(G), 1 if cutoff else 0, _p(d), _p(c),
+                               _p(a))
+    return d, c, a
 
 
 def loss_l2(image, target):

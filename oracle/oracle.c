@@ -589,3 +589,163 @@ void oracle_adam(int64_t rows, int row_len, double *p, const double *g, double *
 }
 
 int oracle_threads(void) { return omp_get_max_threads(); }
+
+/* ------------------------------------------------------------------------ */
+/* Rotation-scale Gaussians and rendering at another resolution             */
+/* ------------------------------------------------------------------------ */
+/* "GaussianImage" (Overview and its training scripts): besides the Cholesky
+ * factor, a Gaussian's covariance may be given by a rotation angle and two
+ * scales ("gaussianimage_rs").  "FlashImgs" (Library API) keeps the tensors
+ * xy, scale, rot, feat and renders a trained set at any output size.
+ * Here prs[n] = (mux, muy, sx, sy, theta, cr, cg, cb), theta in radians:
+ *   Sigma = R diag(sx^2, sy^2) R^T,  R = [[cos, -sin], [sin, cos]],
+ * so with r = R^T d (d = p - mu, coordinates along the Gaussian's axes)
+ *   q = (r1/sx)^2 + (r2/sy)^2,  r1 = cos dx + sin dy,  r2 = -sin dx + cos dy.
+ * Rendering at scale (fx, fy) maps the image plane by D = diag(fx, fy): mean
+ * D mu and covariance D Sigma D, i.e. the new image's pixel centre p is the
+ * point D^-1 p of the original frame.  The cutoff is q <= 9 in fp64; a pair
+ * whose q lies within 1e-4 (relative) of 9 is "ambiguous": an fp32 pipeline
+ * that forms the covariance by other (rounded) steps may decide it either
+ * way, so the magnitude of its contribution is reported separately. */
+
+typedef struct { int ok; double mx, my, sx, sy, cs, sn, c[3]; } rsg;
+
+static rsg rs_setup(const double *p)
+{
+    rsg g;
+    memset(&g, 0, sizeof g);
+    for (int k = 0; k < 8; ++k)
+        if (!isfinite(p[k])) return g;
+    if (p[2] == 0.0 || p[3] == 0.0) return g;
+    g.mx = p[0]; g.my = p[1]; g.sx = p[2]; g.sy = p[3];
+    g.cs = cos(p[4]); g.sn = sin(p[4]);
+    g.c[0] = p[5]; g.c[1] = p[6]; g.c[2] = p[7];
+    g.ok = 1;
+    return g;
+}
+
+#define RS_AMBIG 1e-4
+
+/* 0: outside the cutoff, 1: inside, 2: inside or outside within the ambiguity band */
+static int rs_class(double q, int cutoff)
+{
+    if (!cutoff) return 1;
+    if (fabs(q - 9.0) <= 9.0 * RS_AMBIG) return 2;
+    return q <= 9.0 ? 1 : 0;
+}
+
+/* Sum image of rotation-scale Gaussians rendered at scale (fx, fy), at npix
+ * pixels (pix = NULL: every pixel of the W x H output, row-major).
+ * out[3,npix]; sabs[3,npix] = sum |c| w; amb[3,npix] = sum |c| w over the
+ * ambiguous pairs (those are included in out when q <= 9). */
+void oracle_render_sum_rs(int W, int H, int64_t n, const double *prs, double fx, double fy, const int32_t *pix,
+                          int64_t npix, int cutoff, double *out, double *sabs, double *amb)
+{
+    rsg *gs = (rsg *)malloc(sizeof(rsg) * (n > 0 ? n : 1));
+    for (int64_t g = 0; g < n; ++g) gs[g] = rs_setup(prs + 8 * g);
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npix; ++p) {
+        int i, j; pixel_of(pix, p, W, &i, &j);
+        const double x = (j + 0.5) / fx, y = (i + 0.5) / fy;
+        double acc[3] = {0, 0, 0}, aab[3] = {0, 0, 0}, am[3] = {0, 0, 0};
+        for (int64_t g = 0; g < n; ++g) {
+            if (!gs[g].ok) continue;
+            const double dx = x - gs[g].mx, dy = y - gs[g].my;
+            const double r1 = gs[g].cs * dx + gs[g].sn * dy, r2 = -gs[g].sn * dx + gs[g].cs * dy;
+            const double q = (r1 / gs[g].sx) * (r1 / gs[g].sx) + (r2 / gs[g].sy) * (r2 / gs[g].sy);
+            const int cl = rs_class(q, cutoff);
+            if (cl == 0) continue;
+            const double w = exp(-0.5 * q);
+            for (int k = 0; k < 3; ++k) {
+                if (cl == 2) am[k] += fabs(gs[g].c[k]) * w;
+                if (cl == 2 && q > 9.0) continue;
+                acc[k] += gs[g].c[k] * w;
+                aab[k] += fabs(gs[g].c[k]) * w;
+            }
+        }
+        for (int k = 0; k < 3; ++k) {
+            out[k*npix + p] = acc[k];
+            if (sabs) sabs[k*npix + p] = aab[k];
+            if (amb) amb[k*npix + p] = am[k];
+        }
+    }
+    free(gs);
+}
+
+/* Gradient of L = sum_{k,p} G_k(p) I_k(p) (G [3,H,W] over the output image)
+ * with respect to the rotation-scale parameters prs[n,8] of the image
+ * rendered at scale (fx, fy).  With h = dL/dq = -w/2 (g . c):
+ *   dq/dmu    = -2 (r1/sx^2 R[:,0] + r2/sy^2 R[:,1]),  R[:,0] = (cos, sin), R[:,1] = (-sin, cos)
+ *   dq/dsx    = -2 r1^2 / sx^3,   dq/dsy = -2 r2^2 / sy^3,
+ *   dq/dtheta = 2 r1 r2 (1/sx^2 - 1/sy^2)   (dr1/dtheta = r2, dr2/dtheta = -r1),
+ *   dL/dc_k   = sum_p G_k w.
+ * acond[n,8]: running-error scale (every inner sum over absolute values);
+ * amb[n,8]: sum of |contribution| over the ambiguous pairs. */
+void oracle_grad_sum_rs(int W, int H, int64_t n, const double *prs, double fx, double fy, const double *G,
+                        int cutoff, double *dparams, double *acond, double *amb)
+{
+    const int nt = omp_get_max_threads();
+    const size_t nn = (size_t)(n > 0 ? n : 1);
+    rsg *gs = (rsg *)malloc(sizeof(rsg) * nn);
+    for (int64_t g = 0; g < n; ++g) gs[g] = rs_setup(prs + 8 * g);
+    double *part = (double *)calloc((size_t)nt * 24 * nn, sizeof(double));
+    const int64_t HW = (int64_t)H * W;
+    #pragma omp parallel
+    {
+        double *mine = part + (size_t)omp_get_thread_num() * 24 * nn;
+        #pragma omp for schedule(dynamic, 4)
+        for (int i = 0; i < H; ++i)
+            for (int j = 0; j < W; ++j) {
+                const double gk[3] = {G[(int64_t)i*W + j], G[HW + (int64_t)i*W + j], G[2*HW + (int64_t)i*W + j]};
+                if (gk[0] == 0.0 && gk[1] == 0.0 && gk[2] == 0.0) continue;   /* contributes exactly 0 */
+                const double x = (j + 0.5) / fx, y = (i + 0.5) / fy;
+                for (int64_t g = 0; g < n; ++g) {
+                    const rsg *s = &gs[g];
+                    if (!s->ok) continue;
+                    const double dx = x - s->mx, dy = y - s->my;
+                    const double r1 = s->cs * dx + s->sn * dy, r2 = -s->sn * dx + s->cs * dy;
+                    const double ix2 = 1.0 / (s->sx * s->sx), iy2 = 1.0 / (s->sy * s->sy);
+                    const double q = r1 * r1 * ix2 + r2 * r2 * iy2;
+                    const int cl = rs_class(q, cutoff);
+                    if (cl == 0 || (cl == 2 && q > 9.0 && !amb)) continue;
+                    const double w = exp(-0.5 * q);
+                    const double gc = gk[0]*s->c[0] + gk[1]*s->c[1] + gk[2]*s->c[2];
+                    const double gca = fabs(gk[0]*s->c[0]) + fabs(gk[1]*s->c[1]) + fabs(gk[2]*s->c[2]);
+                    const double h = -0.5 * w * gc, ha = 0.5 * w * gca;
+                    const double a1 = fabs(s->cs * dx) + fabs(s->sn * dy), a2 = fabs(s->sn * dx) + fabs(s->cs * dy);
+                    double dq[5], dqa[5];
+                    dq[0] = -2.0 * (r1 * ix2 * s->cs - r2 * iy2 * s->sn);
+                    dq[1] = -2.0 * (r1 * ix2 * s->sn + r2 * iy2 * s->cs);
+                    dq[2] = -2.0 * r1 * r1 * ix2 / s->sx;
+                    dq[3] = -2.0 * r2 * r2 * iy2 / s->sy;
+                    dq[4] = 2.0 * r1 * r2 * (ix2 - iy2);
+                    dqa[0] = 2.0 * (a1 * ix2 * fabs(s->cs) + a2 * iy2 * fabs(s->sn));
+                    dqa[1] = 2.0 * (a1 * ix2 * fabs(s->sn) + a2 * iy2 * fabs(s->cs));
+                    dqa[2] = 2.0 * a1 * a1 * ix2 / fabs(s->sx);
+                    dqa[3] = 2.0 * a2 * a2 * iy2 / fabs(s->sy);
+                    dqa[4] = 2.0 * a1 * a2 * (ix2 + iy2);
+                    double contrib[8], cond[8];
+                    for (int t = 0; t < 5; ++t) { contrib[t] = h * dq[t]; cond[t] = ha * dqa[t]; }
+                    for (int k = 0; k < 3; ++k) { contrib[5+k] = gk[k] * w; cond[5+k] = fabs(contrib[5+k]); }
+                    const int inside = !(cl == 2 && q > 9.0);
+                    for (int t = 0; t < 8; ++t) {
+                        if (inside) { mine[24*g + t] += contrib[t]; mine[24*g + 8 + t] += cond[t]; }
+                        if (cl == 2) mine[24*g + 16 + t] += fabs(contrib[t]);
+                    }
+                }
+            }
+    }
+    for (int64_t g = 0; g < n; ++g)
+        for (int t = 0; t < 8; ++t) {
+            double s = 0, c = 0, a = 0;
+            for (int th = 0; th < nt; ++th) {
+                s += part[(size_t)th*24*nn + 24*g + t];
+                c += part[(size_t)th*24*nn + 24*g + 8 + t];
+                a += part[(size_t)th*24*nn + 24*g + 16 + t];
+            }
+            dparams[8*g + t] = s;
+            if (acond) acond[8*g + t] = c;
+            if (amb) amb[8*g + t] = a;
+        }
+    free(part); free(gs);
+}

@@ -9,7 +9,10 @@
 - alpha compositing: one- and two-Gaussian closed forms, o -> 0, order dependence,
   a hand-worked early-termination example;
 - gradients: central finite differences (sum and alpha, with and without cutoff);
-- loss: numpy; Adam: the first-step closed form and torch.optim.Adam in float64.
+- loss: numpy; Adam: the first-step closed form and torch.optim.Adam in float64;
+- rotation-scale Gaussians and rendering at another scale: the Cholesky-form oracle on numpy's
+  Cholesky factor of R diag(s^2) R^T (and of D Sigma D), the rotation symmetries, numpy's matrix
+  inverse for the cutoff set, a hand-worked value at scale 2, central finite differences.
 """
 import math
 from fractions import Fraction
@@ -509,3 +512,105 @@ def test_running_error_scale(orc):
     _, _, _, a3, c3 = orc.grad_alpha(W, H, p.astype(np.float64), lg.astype(np.float64), bg.astype(np.float64), G,
                                      with_cond=True)
     assert np.all(c3 >= a3 * (1 - 1e-12))
+
+
+# --------------------------------------------------------------------------------------------
+# rotation-scale Gaussians, rendering at another scale
+# --------------------------------------------------------------------------------------------
+
+def _rs_case(seed, n, W, H):
+    rng = np.random.default_rng(seed)
+    p = np.zeros((n, 8))
+    p[:, 0] = rng.uniform(0, W, n)
+    p[:, 1] = rng.uniform(0, H, n)
+    p[:, 2] = np.exp(rng.uniform(np.log(0.7), np.log(6.0), n))
+    p[:, 3] = np.exp(rng.uniform(np.log(0.7), np.log(6.0), n))
+    p[:, 4] = rng.uniform(-np.pi, np.pi, n)
+    p[:, 5:] = rng.uniform(-1, 1, (n, 3))
+    return p
+
+
+def _rs_to_cholesky_numpy(p, fx=1.0, fy=1.0):
+    """Cholesky-form params of D Sigma D (Sigma = R diag(sx^2, sy^2) R^T) by numpy's linalg."""
+    out = np.zeros_like(p)
+    D = np.diag([fx, fy])
+    for g in range(p.shape[0]):
+        c, s = np.cos(p[g, 4]), np.sin(p[g, 4])
+        R = np.array([[c, -s], [s, c]])
+        S = D @ R @ np.diag([p[g, 2] ** 2, p[g, 3] ** 2]) @ R.T @ D
+        L = np.linalg.cholesky(S)
+        out[g] = [fx * p[g, 0], fy * p[g, 1], L[0, 0], L[1, 0], L[1, 1], p[g, 5], p[g, 6], p[g, 7]]
+    return out
+
+
+@pytest.mark.parametrize("fx,fy", [(1.0, 1.0), (1.5, 0.75), (2.0, 2.0)])
+def test_rs_render_matches_cholesky_form(fx, fy):
+    import oracle
+    W0, H0 = 30, 22
+    p = _rs_case(701, 12, W0, H0)
+    W, H = int(W0 * fx), int(H0 * fy)
+    rs, _, _ = oracle.render_sum_rs(W, H, p, fx, fy, cutoff=False)
+    ch, _ = oracle.render_sum(W, H, _rs_to_cholesky_numpy(p, fx, fy), cutoff=False)
+    np.testing.assert_allclose(rs, ch, rtol=1e-10, atol=1e-13)
+
+
+def test_rs_rotation_symmetries():
+    import oracle
+    p = _rs_case(702, 10, 28, 20)
+    base, _, _ = oracle.render_sum_rs(28, 20, p, cutoff=False)
+    q = p.copy()
+    q[:, 4] += np.pi                                   # R(theta + pi) = -R(theta)
+    np.testing.assert_allclose(oracle.render_sum_rs(28, 20, q, cutoff=False)[0], base, rtol=1e-10, atol=1e-13)
+    q = p.copy()
+    q[:, 2], q[:, 3], q[:, 4] = p[:, 3], p[:, 2], p[:, 4] + np.pi / 2   # axes swapped
+    np.testing.assert_allclose(oracle.render_sum_rs(28, 20, q, cutoff=False)[0], base, rtol=1e-10, atol=1e-13)
+
+
+def test_rs_cutoff_set_and_ambiguity():
+    import oracle
+    p = _rs_case(703, 1, 40, 40)
+    p[0, :2] = (20.2, 19.7)
+    img, _, amb = oracle.render_sum_rs(40, 40, p, cutoff=True)
+    c, s = np.cos(p[0, 4]), np.sin(p[0, 4])
+    R = np.array([[c, -s], [s, c]])
+    Pinv = np.linalg.inv(R @ np.diag([p[0, 2] ** 2, p[0, 3] ** 2]) @ R.T)
+    yy, xx = np.mgrid[0:40, 0:40]
+    d = np.stack([xx + 0.5 - p[0, 0], yy + 0.5 - p[0, 1]], -1)
+    q = np.einsum("...i,ij,...j->...", d, Pinv, d)
+    w = np.exp(-0.5 * q)
+    want = np.where(q <= 9.0, w, 0.0)
+    np.testing.assert_allclose(img, p[0, 5:, None, None] * want[None], rtol=1e-10, atol=1e-15)
+    band = np.abs(q - 9.0) <= 9e-4
+    np.testing.assert_allclose(amb, np.abs(p[0, 5:, None, None]) * np.where(band, w, 0.0)[None], rtol=1e-10,
+                               atol=1e-15)
+
+
+def test_rs_render_at_scale_hand_value():
+    import oracle
+    # isotropic s = 2 at (5, 5), rendered at scale 2: output pixel (9, 9) samples (4.75, 4.75)
+    p = np.array([[5.0, 5.0, 2.0, 2.0, 0.3, 1.0, 0.5, -2.0]])
+    img, _, _ = oracle.render_sum_rs(12, 12, p, 2.0, 2.0, cutoff=True)
+    w = math.exp(-0.5 * (0.25 ** 2 + 0.25 ** 2) / 4.0)
+    np.testing.assert_allclose(img[:, 9, 9], [w, 0.5 * w, -2.0 * w], rtol=1e-14)
+
+
+@pytest.mark.parametrize("fx,fy", [(1.0, 1.0), (1.3, 0.8)])
+def test_rs_grad_finite_differences(fx, fy):
+    import oracle
+    W, H = 14, 11
+    p = _rs_case(704, 3, W / fx, H / fy)
+    G = np.random.default_rng(705).normal(size=(3, H, W))
+    d, _, _ = oracle.grad_sum_rs(W, H, p, G, fx, fy, cutoff=False)
+
+    def L(q):
+        return float(np.sum(G * oracle.render_sum_rs(W, H, q, fx, fy, cutoff=False)[0]))
+
+    num = np.zeros_like(p)
+    for g in range(p.shape[0]):
+        for t in range(8):
+            h = 1e-6 * max(1.0, abs(p[g, t]))
+            a, b = p.copy(), p.copy()
+            a[g, t] += h
+            b[g, t] -= h
+            num[g, t] = (L(a) - L(b)) / (2 * h)
+    np.testing.assert_allclose(d, num, rtol=1e-6, atol=1e-7)
