@@ -275,6 +275,93 @@ def bench_alpha(args, w, target, params, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_rs(args, wlname, target, dev):
+    """Rotation-scale Gaussians on a sum workload: one step = gi_params_to_cholesky + preprocess and
+    binning + gi_render_fwd_l2 + gi_render_bwd (gather, loss) + gi_params_to_cholesky_grad + Adam."""
+    import torch
+    from rasterizer_gaussian_raster_amd import gi, synth
+    from rasterizer_gaussian_raster_amd.pipeline import FitterRS
+
+    w = synth.make_workload_rs(wlname)
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    fit = FitterRS(target, torch.from_numpy(w["params_rs"]).to(dev), capacity_slack=2.0)
+    for _ in range(args.warmup):
+        fit.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fit.step()
+    torch.cuda.synchronize()
+    t_train = time.perf_counter() - t0
+    r = fit.raster
+    M_now = int(r.d_num.cpu().item()) & 0xFFFFFFFF
+    assert M_now <= r.capacity, "tile-pair capacity exceeded during the timed run"
+    ms_step = 1e3 * t_train / args.steps
+    final_loss = float(fit.loss.item())
+    log(f"[bench] rotation-scale train: {ms_step:.4f} ms/step, loss {final_loss:.4e}")
+
+    # HIP events on the launch stream: the conversion, its chain rule, and the separate forward / backward
+    n = fit.n
+    nk = max(20, min(args.steps, 500))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E() for _ in range(5)] for _ in range(nk)]
+    for k in range(nk):
+        ev[k][0].record()
+        gi.gi_params_to_cholesky(gi.PARAMS_RS, n, fit.params, 1.0, 1.0, fit.chol)
+        ev[k][1].record()
+        r.forward_l2(fit.target, fit.dL)
+        ev[k][2].record()
+        r.backward(fit.dL, fit.gchol)
+        ev[k][3].record()
+        gi.gi_params_to_cholesky_grad(gi.PARAMS_RS, n, fit.params, 1.0, 1.0, fit.gchol, fit.grad)
+        ev[k][4].record()
+    torch.cuda.synchronize()
+    ms = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(4)] for k in range(nk)])
+    conv_s, fwd_s, bwd_s, chain_s = (float(x) * 1e-3 for x in ms.mean(0))
+    log(f"[bench] convert {conv_s*1e6:.1f} us, fwd {fwd_s*1e6:.1f} us, bwd+gather {bwd_s*1e6:.1f} us, "
+        f"chain {chain_s*1e6:.1f} us")
+    ranges = r.ranges.cpu().numpy().view(np.uint32)
+    pairs = binned_pairs(W, H, ranges)
+
+    def roof_alu(kname, flop, secs):
+        tf = flop * pairs / secs / 1e12
+        return {"bound": "alu", "kernel": kname, "achieved": round(tf, 3), "peak": PEAK_FP32, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_FP32, 4), "traffic": None, "avg_launch_us": round(secs * 1e6, 2)}
+
+    def roof_hbm(kname, nbytes, secs):
+        gbs = nbytes / secs / 1e9
+        return {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM, 4), "traffic": None, "avg_launch_us": round(secs * 1e6, 2)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "fwd+bwd steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wlname, "width": W, "height": H, "gaussians": wl.n, "mode": "sum",
+                   "params": "rotation-scale", "binned_pixel_pairs": pairs},
+        "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
+                  "kernels_us: HIP events on the launch stream around each launch, on the trained parameters",
+        "final_loss": final_loss,
+        "kernels_us": {"params_to_cholesky": round(conv_s * 1e6, 2), "render_fwd_l2": round(fwd_s * 1e6, 2),
+                       "render_bwd_gather": round(bwd_s * 1e6, 2), "params_to_cholesky_grad": round(chain_s * 1e6, 2)},
+        "roofline": roof_alu("k_render_sum_bwd (+ gather)", FLOP_BWD, bwd_s),
+        "roofline_convert": roof_hbm("k_params_to_cholesky", 64 * n, conv_s),
+        "roofline_chain": roof_hbm("k_params_to_cholesky_grad", 96 * n, chain_s),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +369,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="kodak_768x512_50k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--params", choices=["cholesky", "rs"], default="cholesky",
+                    help="parameter form of the Gaussians (rs: rotation-scale, converted on the GPU each step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -314,6 +403,8 @@ def main():
         log("[bench] copy calibration: 3 x 256 MiB device-to-device copies")
     if wl.mode != "sum":
         return bench_alpha(args, w, target, params, dev)
+    if args.params == "rs":
+        return bench_rs(args, wlname, target, dev)
 
     # ---------------- training step (the whole hot path) ----------------
     fit = Fitter(target, params, capacity_slack=2.0)

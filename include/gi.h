@@ -444,6 +444,49 @@ typedef struct gi_adam_hparams {
 gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
                           int32_t step, const int32_t *d_step, uint32_t flags, void *stream);
 
+/*
+ * Parameter forms ("GaussianImage", Overview and its training scripts: the
+ * covariance as a Cholesky factor or as a rotation and two scales;
+ * "FlashImgs", Library API: xy / scale / rot tensors, and rendering a trained
+ * set at any output size).
+ *   GI_PARAMS_CHOLESKY  the params above.
+ *   GI_PARAMS_RS        mux, muy, sx, sy, theta, cr, cg, cb (theta in radians):
+ *                       Sigma = R diag(sx^2, sy^2) R^T,
+ *                       R = [[cos theta, -sin theta], [sin theta, cos theta]].
+ */
+typedef enum { GI_PARAMS_CHOLESKY = 0, GI_PARAMS_RS = 1 } gi_param_kind;
+
+/*
+ * gi_params_to_cholesky -- the Cholesky-form params (the form every other call
+ *   takes) of n Gaussians given in form `kind`, with the image plane scaled by
+ *   D = diag(fx, fy): mean D mu, covariance D Sigma D, i.e. L -> D L.  To render
+ *   a set at another size W' x H', pass fx = W'/W, fy = H'/H; fx = fy = 1 only
+ *   converts.  RS, in fp32 with (cs, sn) = sincosf(theta), ax = |sx|, ay = |sy|:
+ *     l11 = sqrt(fma(cs ax, cs ax, (sn ay)^2)),
+ *     l21 = (cs sn) ((ax - ay)(ax + ay)) / l11,   l22 = (ax ay) / l11
+ *   (the Cholesky factor of Sigma; l22 from det Sigma = (ax ay)^2 without
+ *   cancellation), then (fx l11, fy l21, fy l22).  A zero scale gives l22 = 0,
+ *   which the raster culls.  The cutoff rule above then applies to these
+ *   Cholesky params.
+ *   params  device float [n][8] in form `kind`.
+ *   out     device float [n][8]; may alias params only for GI_PARAMS_CHOLESKY.
+ *   fx, fy  > 0 and finite.
+ */
+gi_status gi_params_to_cholesky(int32_t kind, int64_t n, const float *params, float fx, float fy, float *out,
+                                void *stream);
+
+/*
+ * gi_params_to_cholesky_grad -- the chain rule of gi_params_to_cholesky:
+ *   dparams = J^T dout, J its Jacobian at params (same kind, fx, fy).
+ *   dout       device float [n][8]: gradient w.r.t. the Cholesky-form params
+ *              (e.g. gi_render_bwd's dparams).
+ *   dparams    device float [n][8], must not alias params; overwritten, or added
+ *              to when accumulate != 0.  A Gaussian whose Cholesky form has
+ *              l11 == 0 or a non-finite entry gets a zero gradient.
+ */
+gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *params, float fx, float fy,
+                                     const float *dout, float *dparams, int32_t accumulate, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

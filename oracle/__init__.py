@@ -81,7 +81,7 @@ def _load():
     f64 = ctypes.c_double
     lib.oracle_render_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i64, i32, P, P, P]
     lib.oracle_render_sum_rs.restype = None
-    lib.oracle_grad_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i32, P, P, P]
+    lib.oracle_grad_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i32, P, P, P, P]
     lib.oracle_grad_sum_rs.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = i32
@@ -244,16 +244,18 @@ def render_sum_rs(W, H, params_rs, fx=1.0, fy=1.0, pixels=None, cutoff=True):
     return out, sabs, amb
 
 
-def grad_sum_rs(W, H, params_rs, dL_dI, fx=1.0, fy=1.0, cutoff=True):
+def grad_sum_rs(W, H, params_rs, dL_dI, fx=1.0, fy=1.0, cutoff=True, with_chain=False):
     """(dparams [N,8], running-error scale [N,8], ambiguous-pair magnitude [N,8]) of
-    L = <dL_dI, I> for the rotation-scale sum image rendered at scale (fx, fy)."""
+    L = <dL_dI, I> for the rotation-scale sum image rendered at scale (fx, fy); with_chain also
+    returns the running-error scale of evaluating through the Cholesky factor and the chain rule."""
     par = _f64(params_rs).reshape(-1, 8)
     G = _f64(dL_dI).reshape(3, H, W)
     n = par.shape[0]
     d, c, a = np.zeros((n, 8)), np.zeros((n, 8)), np.zeros((n, 8))
+    ch = np.zeros((n, 8)) if with_chain else None
     _load().oracle_grad_sum_rs(W, H, n, _p(par), float(fx), float(fy), _p(G), 1 if cutoff else 0, _p(d), _p(c),
-                               _p(a))
-    return d, c, a
+                               _p(a), _p(ch))
+    return (d, c, a, ch) if with_chain else (d, c, a)
 
 
 def loss_l2(image, target):

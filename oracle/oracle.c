@@ -680,25 +680,55 @@ void oracle_render_sum_rs(int W, int H, int64_t n, const double *prs, double fx,
  *   dq/dtheta = 2 r1 r2 (1/sx^2 - 1/sy^2)   (dr1/dtheta = r2, dr2/dtheta = -r1),
  *   dL/dc_k   = sum_p G_k w.
  * acond[n,8]: running-error scale (every inner sum over absolute values);
- * amb[n,8]: sum of |contribution| over the ambiguous pairs. */
+ * amb[n,8]: sum of |contribution| over the ambiguous pairs.
+ * acond_chain[n,8] (may be NULL): the running-error scale of the other order
+ * of evaluation -- the gradient w.r.t. the Cholesky factor L' = D L of
+ * D Sigma D first (its running-error scale C' as for the Cholesky form), then
+ * the chain rule: |J|^T C', J = d(D mu, L')/d(mu, sx, sy, theta), from
+ *   L = chol(Sigma): l11 = sqrt(A), l21 = B/l11, l22 = P/l11,
+ *   A = (cos ax)^2 + (sin ay)^2, B = cos sin (ax^2 - ay^2), P = ax ay,
+ *   ax = |sx|, ay = |sy|.  A rotated, strongly anisotropic Gaussian has a
+ * skewed factor (|l21| >> l11), and the chain amplifies the rounding of the
+ * factor's gradient accordingly. */
 void oracle_grad_sum_rs(int W, int H, int64_t n, const double *prs, double fx, double fy, const double *G,
-                        int cutoff, double *dparams, double *acond, double *amb)
+                        int cutoff, double *dparams, double *acond, double *amb, double *acond_chain)
 {
     const int nt = omp_get_max_threads();
     const size_t nn = (size_t)(n > 0 ? n : 1);
     rsg *gs = (rsg *)malloc(sizeof(rsg) * nn);
-    for (int64_t g = 0; g < n; ++g) gs[g] = rs_setup(prs + 8 * g);
-    double *part = (double *)calloc((size_t)nt * 24 * nn, sizeof(double));
+    gauss64 *gc64 = (gauss64 *)malloc(sizeof(gauss64) * nn);   /* the scaled Cholesky form */
+    double *jac = (double *)calloc(nn * 9, sizeof(double));    /* d(l11', l21', l22')/d(sx, sy, theta) */
+    for (int64_t g = 0; g < n; ++g) {
+        gs[g] = rs_setup(prs + 8 * g);
+        if (!gs[g].ok) continue;
+        const double cs = gs[g].cs, sn = gs[g].sn, ax = fabs(gs[g].sx), ay = fabs(gs[g].sy);
+        const double A = cs * cs * ax * ax + sn * sn * ay * ay, B = cs * sn * (ax * ax - ay * ay), P = ax * ay;
+        const double l11 = sqrt(A), l21 = B / l11, l22 = P / l11;
+        const double p8[8] = {fx * gs[g].mx, fy * gs[g].my, fx * l11, fy * l21, fy * l22, 0, 0, 0};
+        gc64[g] = gauss_setup(p8, NULL);
+        const double dA[3] = {2 * cs * cs * ax, 2 * sn * sn * ay, -2 * B};
+        const double dB[3] = {2 * cs * sn * ax, -2 * cs * sn * ay, (cs * cs - sn * sn) * (ax * ax - ay * ay)};
+        const double dP[3] = {ay, ax, 0.0};
+        const double sg[3] = {gs[g].sx < 0 ? -1.0 : 1.0, gs[g].sy < 0 ? -1.0 : 1.0, 1.0};
+        for (int k = 0; k < 3; ++k) {
+            const double d11 = dA[k] / (2 * l11);
+            jac[9*g + 0*3 + k] = fx * sg[k] * d11;
+            jac[9*g + 1*3 + k] = fy * sg[k] * (dB[k] - l21 * d11) / l11;
+            jac[9*g + 2*3 + k] = fy * sg[k] * (dP[k] - l22 * d11) / l11;
+        }
+    }
+    double *part = (double *)calloc((size_t)nt * 32 * nn, sizeof(double));
     const int64_t HW = (int64_t)H * W;
     #pragma omp parallel
     {
-        double *mine = part + (size_t)omp_get_thread_num() * 24 * nn;
+        double *mine = part + (size_t)omp_get_thread_num() * 32 * nn;
         #pragma omp for schedule(dynamic, 4)
         for (int i = 0; i < H; ++i)
             for (int j = 0; j < W; ++j) {
                 const double gk[3] = {G[(int64_t)i*W + j], G[HW + (int64_t)i*W + j], G[2*HW + (int64_t)i*W + j]};
                 if (gk[0] == 0.0 && gk[1] == 0.0 && gk[2] == 0.0) continue;   /* contributes exactly 0 */
                 const double x = (j + 0.5) / fx, y = (i + 0.5) / fy;
+                const double xo = j + 0.5, yo = i + 0.5;
                 for (int64_t g = 0; g < n; ++g) {
                     const rsg *s = &gs[g];
                     if (!s->ok) continue;
@@ -729,23 +759,39 @@ void oracle_grad_sum_rs(int W, int H, int64_t n, const double *prs, double fx, d
                     for (int k = 0; k < 3; ++k) { contrib[5+k] = gk[k] * w; cond[5+k] = fabs(contrib[5+k]); }
                     const int inside = !(cl == 2 && q > 9.0);
                     for (int t = 0; t < 8; ++t) {
-                        if (inside) { mine[24*g + t] += contrib[t]; mine[24*g + 8 + t] += cond[t]; }
-                        if (cl == 2) mine[24*g + 16 + t] += fabs(contrib[t]);
+                        if (inside) { mine[32*g + t] += contrib[t]; mine[32*g + 8 + t] += cond[t]; }
+                        if (cl == 2) mine[32*g + 16 + t] += fabs(contrib[t]);
+                    }
+                    if (inside && acond_chain) {     /* the Cholesky-form scale, in the output frame */
+                        double dqc[5];
+                        gauss_dq_abs(&gc64[g], xo - gc64[g].mx, yo - gc64[g].my, dqc);
+                        for (int t = 0; t < 5; ++t) mine[32*g + 24 + t] += ha * dqc[t];
                     }
                 }
             }
     }
-    for (int64_t g = 0; g < n; ++g)
+    for (int64_t g = 0; g < n; ++g) {
+        double cc[5] = {0, 0, 0, 0, 0};
         for (int t = 0; t < 8; ++t) {
             double s = 0, c = 0, a = 0;
             for (int th = 0; th < nt; ++th) {
-                s += part[(size_t)th*24*nn + 24*g + t];
-                c += part[(size_t)th*24*nn + 24*g + 8 + t];
-                a += part[(size_t)th*24*nn + 24*g + 16 + t];
+                s += part[(size_t)th*32*nn + 32*g + t];
+                c += part[(size_t)th*32*nn + 32*g + 8 + t];
+                a += part[(size_t)th*32*nn + 32*g + 16 + t];
+                if (t < 5) cc[t] += part[(size_t)th*32*nn + 32*g + 24 + t];
             }
             dparams[8*g + t] = s;
             if (acond) acond[8*g + t] = c;
             if (amb) amb[8*g + t] = a;
         }
-    free(part); free(gs);
+        if (acond_chain) {
+            acond_chain[8*g + 0] = fx * cc[0];
+            acond_chain[8*g + 1] = fy * cc[1];
+            for (int k = 0; k < 3; ++k)
+                acond_chain[8*g + 2 + k] = fabs(jac[9*g + k]) * cc[2] + fabs(jac[9*g + 3 + k]) * cc[3] +
+                                           fabs(jac[9*g + 6 + k]) * cc[4];
+            for (int t = 5; t < 8; ++t) acond_chain[8*g + t] = acond ? acond[8*g + t] : 0.0;
+        }
+    }
+    free(part); free(gs); free(gc64); free(jac);
 }

@@ -2,6 +2,8 @@
 // checks, launch of the gfx950 kernels on the caller's stream, status codes.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "../../include/gi.h"
 #include "gi_launch.hpp"
 
@@ -357,6 +359,30 @@ gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float 
     }
     return hip_status(gi::launch_adam(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_grad,
                                       as_stream(stream)));
+}
+
+gi_status gi_params_to_cholesky(int32_t kind, int64_t n, const float *params, float fx, float fy, float *out,
+                                void *stream) {
+    if ((kind != GI_PARAMS_CHOLESKY && kind != GI_PARAMS_RS) || n < 0) return GI_ERR_INVALID_ARG;
+    if (!(fx > 0.0f) || !(fy > 0.0f) || !std::isfinite(fx) || !std::isfinite(fy)) return GI_ERR_INVALID_ARG;
+    if (n > 0) {
+        if (!params || !out || !aligned16(params) || !aligned16(out)) return GI_ERR_INVALID_ARG;
+        if (kind == GI_PARAMS_RS && params == out) return GI_ERR_INVALID_ARG;
+    }
+    return hip_status(gi::launch_params_to_cholesky(kind, n, params, fx, fy, out, as_stream(stream)));
+}
+
+gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *params, float fx, float fy,
+                                     const float *dout, float *dparams, int32_t accumulate, void *stream) {
+    if ((kind != GI_PARAMS_CHOLESKY && kind != GI_PARAMS_RS) || n < 0) return GI_ERR_INVALID_ARG;
+    if (!(fx > 0.0f) || !(fy > 0.0f) || !std::isfinite(fx) || !std::isfinite(fy)) return GI_ERR_INVALID_ARG;
+    if (n > 0) {
+        if (!params || !dout || !dparams || !aligned16(params) || !aligned16(dout) || !aligned16(dparams))
+            return GI_ERR_INVALID_ARG;
+        if (dparams == params) return GI_ERR_INVALID_ARG;
+    }
+    return hip_status(gi::launch_params_to_cholesky_grad(kind, n, params, fx, fy, dout, dparams, accumulate != 0,
+                                                         as_stream(stream)));
 }
 
 }  // extern "C"

@@ -151,4 +151,10 @@ hipError_t launch_loss_l2(int64_t count, const float *image, const float *target
 hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, float *v, const float *lr,
                        double beta1, double beta2, double eps, int step, int zero_grad, hipStream_t s);
 
+// k_params.hip
+hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
+                                     hipStream_t s);
+hipError_t launch_params_to_cholesky_grad(int kind, int64_t n, const float *in, float fx, float fy,
+                                          const float *dout, float *din, int accumulate, hipStream_t s);
+
 }  // namespace gi

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgi.so")
 
 GI_OK, GI_ERR_INVALID_ARG, GI_ERR_HIP, GI_ERR_CAPACITY = 0, 1, 2, 3
 MODE_SUM, MODE_ALPHA = 0, 1
+PARAMS_CHOLESKY, PARAMS_RS = 0, 1
 TILE = 16
 
 _lib = None
@@ -77,6 +78,8 @@ def load():
         "gi_loss_workspace_bytes": ([i64], sz),
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
+        "gi_params_to_cholesky": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P], i32),
+        "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
         "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P, i64, P, P], i32),
@@ -225,6 +228,17 @@ def gi_adam_step(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_gr
     _check(load().gi_adam_step(int(rows), int(row_len), _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr_arr,
                                float(beta1), float(beta2), float(eps), int(step), int(zero_grad),
                                _stream(stream)), "gi_adam_step")
+
+
+def gi_params_to_cholesky(kind, n, params, fx, fy, out, stream=None):
+    _check(load().gi_params_to_cholesky(int(kind), int(n), _ptr(params), float(fx), float(fy), _ptr(out),
+                                        _stream(stream)), "gi_params_to_cholesky")
+
+
+def gi_params_to_cholesky_grad(kind, n, params, fx, fy, dout, dparams, accumulate=False, stream=None):
+    _check(load().gi_params_to_cholesky_grad(int(kind), int(n), _ptr(params), float(fx), float(fy), _ptr(dout),
+                                             _ptr(dparams), 1 if accumulate else 0, _stream(stream)),
+           "gi_params_to_cholesky_grad")
 
 
 def gi_render_fwd_l2(d, n, records, pixbox, ranges, vals, target, image, dL_dimage, loss_partials, stream=None,

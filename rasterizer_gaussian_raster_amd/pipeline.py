@@ -183,6 +183,65 @@ class Raster:
         return self.image
 
 
+DEFAULT_LR_RS = (0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005)   # mu, mu, sx, sy, theta, colour
+
+
+def cholesky_params(params, kind=gi.PARAMS_RS, fx=1.0, fy=1.0, out=None, stream=None):
+    """Cholesky-form params of Gaussians given in form `kind`, with the image plane scaled by
+    (fx, fy) (to render at another size: fx = W'/W, fy = H'/H)."""
+    if out is None:
+        out = torch.empty_like(params)
+    gi.gi_params_to_cholesky(kind, params.shape[0], params, fx, fy, out, stream)
+    return out
+
+
+class FitterRS:
+    """Fits rotation-scale Gaussians (mux, muy, sx, sy, theta, cr, cg, cb) with L2 loss and Adam
+    (sum mode).  A step: gi_params_to_cholesky, preprocess + binning, gi_render_fwd_l2,
+    gi_render_bwd (with the per-Gaussian gather and the loss), gi_params_to_cholesky_grad, and Adam
+    on the rotation-scale parameters."""
+
+    def __init__(self, target, params_rs, lr=DEFAULT_LR_RS, betas=(0.9, 0.999), eps=1e-8, capacity_slack=1.5):
+        self.target = target.contiguous()
+        _, H, W = self.target.shape
+        self.params = params_rs.contiguous().clone()
+        self.n = self.params.shape[0]
+        self.raster = Raster(W, H, self.n, device=self.params.device)
+        self.chol = torch.empty_like(self.params)
+        self.gchol = torch.zeros_like(self.params)
+        self.grad = torch.zeros_like(self.params)
+        self.m = torch.zeros_like(self.params)
+        self.v = torch.zeros_like(self.params)
+        self.dL = torch.empty_like(self.target)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=self.params.device)
+        self.lr, self.betas, self.eps = tuple(lr), betas, eps
+        self.step_count = 0
+        self.slack = capacity_slack
+        cholesky_params(self.params, out=self.chol)
+        self.raster.preprocess(self.chol)
+        M = self.raster.bin(sync=True)
+        self.raster.set_capacity(int(M * capacity_slack) + 4096)
+
+    def check_capacity(self):
+        M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
+        if M > 0.8 * self.raster.capacity:
+            self.raster.set_capacity(int(M * self.slack) + 4096)
+            return True
+        return False
+
+    def step(self):
+        r, n = self.raster, self.n
+        cholesky_params(self.params, out=self.chol)
+        r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.chol)
+        r.forward_l2(self.target, self.dL)
+        self.gchol.zero_()
+        r.backward(self.dL, self.gchol, d_loss=self.loss)
+        gi.gi_params_to_cholesky_grad(gi.PARAMS_RS, n, self.params, 1.0, 1.0, self.gchol, self.grad)
+        self.step_count += 1
+        b1, b2 = self.betas
+        gi.gi_adam_step(n, 8, self.params, self.grad, self.m, self.v, self.lr, b1, b2, self.eps, self.step_count, 0)
+
+
 class Fitter:
     """Fits Gaussians to a target image with L2 loss and Adam (all steps in libgi)."""
 

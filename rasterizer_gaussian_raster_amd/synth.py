@@ -167,6 +167,54 @@ def make_workload(name: str, n: int | None = None):
     return {"workload": wl, "target": tgt, "params": params, "logit": logit, "background": bg}
 
 
+def make_gaussians_rs(n, W, H, sigma, seed, means="uniform", target=None):
+    """[n,8] float32 rotation-scale params (mux, muy, sx, sy, theta, cr, cg, cb): means as
+    make_gaussians, scales log-uniform over sigma, theta uniform over (-pi, pi]."""
+    rng = np.random.default_rng([seed, 17])
+    p = np.zeros((n, 8), np.float64)
+    if means == "gradient" and target is not None:
+        gy, gx = np.gradient(target.astype(np.float64), axis=(1, 2))
+        wgt = np.sqrt(gx * gx + gy * gy).sum(axis=0).reshape(-1) + 1e-6
+        idx = rng.choice(wgt.size, size=n, p=wgt / wgt.sum())
+        p[:, 0] = (idx % W) + rng.uniform(0, 1, n)
+        p[:, 1] = (idx // W) + rng.uniform(0, 1, n)
+    else:
+        p[:, 0] = rng.uniform(0, W, n)
+        p[:, 1] = rng.uniform(0, H, n)
+    lo, hi = np.log(sigma[0]), np.log(sigma[1])
+    p[:, 2] = np.exp(rng.uniform(lo, hi, n))
+    p[:, 3] = np.exp(rng.uniform(lo, hi, n))
+    p[:, 4] = rng.uniform(-np.pi, np.pi, n)
+    p[:, 5:8] = rng.uniform(0.0, 1.0, (n, 3))
+    return np.ascontiguousarray(p, dtype=np.float32)
+
+
+def make_workload_rs(name: str, n: int | None = None):
+    """A sum-mode workload with rotation-scale Gaussians of the same sizes and distributions:
+    dict(workload, target [3,H,W], params_rs [N,8])."""
+    wl = WORKLOADS[name]
+    if wl.mode != "sum":
+        raise ValueError("rotation-scale workloads are sum-mode")
+    N = wl.n if n is None else n
+    tgt = make_target(wl.target, wl.width, wl.height, wl.seed)
+    prs = make_gaussians_rs(N, wl.width, wl.height, wl.sigma, wl.seed, wl.means, tgt)
+    return {"workload": wl, "target": tgt, "params_rs": prs}
+
+
+def random_case_rs(seed, W, H, n, sigma=(0.5, 6.0), margin=0.0):
+    """Small seeded rotation-scale parity case (signed scales, any angle)."""
+    rng = np.random.default_rng([seed, 19])
+    p = np.zeros((n, 8), np.float64)
+    p[:, 0] = rng.uniform(-margin, W + margin, n)
+    p[:, 1] = rng.uniform(-margin, H + margin, n)
+    lo, hi = np.log(sigma[0]), np.log(sigma[1])
+    p[:, 2] = np.exp(rng.uniform(lo, hi, n)) * rng.choice([-1.0, 1.0], n)
+    p[:, 3] = np.exp(rng.uniform(lo, hi, n)) * rng.choice([-1.0, 1.0], n)
+    p[:, 4] = rng.uniform(-4.0, 4.0, n)
+    p[:, 5:8] = rng.uniform(-0.2, 1.0, (n, 3))
+    return np.ascontiguousarray(p, dtype=np.float32)
+
+
 def random_case(seed, W, H, n, sigma=(0.5, 6.0), offdiag_std=0.3, alpha=False, margin=0.0):
     """Small seeded parity case; margin extends the mean range beyond the image (px)."""
     rng = np.random.default_rng([seed, 13])

@@ -58,6 +58,13 @@ def test_host_only_calls(lib):
     assert st == gi.GI_ERR_INVALID_ARG
     st = gi.load().gi_adam_step(1, 17, None, None, None, None, None, 0.9, 0.999, 1e-8, 1, 0, None)
     assert st == gi.GI_ERR_INVALID_ARG
+    st = gi.load().gi_params_to_cholesky(7, 0, None, 1.0, 1.0, None, None)
+    assert st == gi.GI_ERR_INVALID_ARG
+    st = gi.load().gi_params_to_cholesky(gi.PARAMS_RS, 0, None, 0.0, 1.0, None, None)
+    assert st == gi.GI_ERR_INVALID_ARG
+    st = gi.load().gi_params_to_cholesky_grad(gi.PARAMS_RS, 4, None, 1.0, 1.0, None, None, 0, None)
+    assert st == gi.GI_ERR_INVALID_ARG
+    assert gi.load().gi_params_to_cholesky(gi.PARAMS_RS, 0, None, 2.0, 2.0, None, None) == gi.GI_OK
     # the one-call training step: missing buffers, alpha mode, unknown flags, bad Adam settings
     d = gi.desc(64, 48)
     hp = gi.adam_hparams([0.01] * 8, 0.9, 0.999, 1e-8)

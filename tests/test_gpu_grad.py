@@ -129,6 +129,20 @@ def test_alpha_grad_random(seed, W, H, n):
     _alpha_case_grad(W, H, p, lg, bg, G)
 
 
+def test_alpha_grad_workload():
+    """Every Gaussian's gradient (and the background's) on the 2048x2048 / 500K alpha workload, in
+    the launch configuration the benchmark times; dL/dI is nonzero on sampled pixels only."""
+    require_gpu()
+    w = synth.make_workload("alpha_2048x2048_500k")
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    rng = np.random.default_rng(wl.seed + 50)
+    G = np.zeros((3, H, W), np.float32)
+    pix = sample_pixels(W, H, 2048, 4, seed=wl.seed + 60)
+    G[:, pix[:, 0], pix[:, 1]] = rng.normal(size=(3, len(pix)))
+    _alpha_case_grad(W, H, w["params"], w["logit"], w["background"], G)
+
+
 def test_alpha_grad_termination_stress():
     require_gpu()
     rng = np.random.default_rng(181)

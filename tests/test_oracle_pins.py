@@ -614,3 +614,27 @@ def test_rs_grad_finite_differences(fx, fy):
             b[g, t] -= h
             num[g, t] = (L(a) - L(b)) / (2 * h)
     np.testing.assert_allclose(d, num, rtol=1e-6, atol=1e-7)
+
+
+def test_rs_chain_scale_is_the_propagated_cholesky_scale():
+    """acond_chain = |J|^T C': C' the Cholesky-form oracle's running-error scale of the factor of
+    D Sigma D, J the Jacobian of that factor (numpy's Cholesky, central differences)."""
+    import oracle
+    W, H, fx, fy = 24, 20, 1.25, 0.8
+    p = np.array([[9.3, 13.1, 4.5, 0.9, 1.2, 0.7, -0.3, 0.4]])
+    G = np.zeros((3, H, W))
+    G[:, 11, 12] = (0.5, -1.0, 2.0)
+    G[:, 9, 10] = (1.5, 0.2, -0.7)
+    _, _, _, chain = oracle.grad_sum_rs(W, H, p, G, fx, fy, with_chain=True)
+    chol = _rs_to_cholesky_numpy(p, fx, fy)
+    _, _, Cc = oracle.grad_sum(W, H, chol, G, with_cond=True)
+    J = np.zeros((3, 3))
+    for k in range(3):
+        h = 1e-6
+        a, b = p.copy(), p.copy()
+        a[0, 2 + k] += h
+        b[0, 2 + k] -= h
+        J[:, k] = (_rs_to_cholesky_numpy(a, fx, fy)[0, 2:5] - _rs_to_cholesky_numpy(b, fx, fy)[0, 2:5]) / (2 * h)
+    want = np.abs(J).T @ Cc[0, 2:5]
+    np.testing.assert_allclose(chain[0, 2:5], want, rtol=1e-6)
+    np.testing.assert_allclose(chain[0, :2], [fx * Cc[0, 0], fy * Cc[0, 1]], rtol=1e-12)
