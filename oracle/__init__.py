@@ -15,8 +15,10 @@ Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 fp32 cutoff, numpy's stable sort for the bin order, central finite
 differences, torch's Adam; for the rotation-scale form and rendering at another
 scale: numpy's Cholesky factor fed to the Cholesky-form oracle, rotation
-symmetries, numpy's matrix inverse for the cutoff set).  No function is
-"parity unpinned".
+symmetries, numpy's matrix inverse for the cutoff set; for the SSIM loss:
+scipy's Gaussian window and zero-padded correlation, closed forms for shifted
+and scaled images, central finite differences).  No function is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -83,6 +85,8 @@ def _load():
     lib.oracle_render_sum_rs.restype = None
     lib.oracle_grad_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i32, P, P, P, P]
     lib.oracle_grad_sum_rs.restype = None
+    lib.oracle_loss_ssim.argtypes = [i32, i32, P, P, f64, f64, f64, P, P, P, P]
+    lib.oracle_loss_ssim.restype = f64
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = i32
     _lib = lib
@@ -256,6 +260,21 @@ def grad_sum_rs(W, H, params_rs, dL_dI, fx=1.0, fy=1.0, cutoff=True, with_chain=
     _load().oracle_grad_sum_rs(W, H, n, _p(par), float(fx), float(fy), _p(G), 1 if cutoff else 0, _p(d), _p(c),
                                _p(a), _p(ch))
     return (d, c, a, ch) if with_chain else (d, c, a)
+
+
+def loss_ssim(image, target, w1=0.8, w2=0.0, ws=0.2, with_grad=True):
+    """L = w1 mean|x - y| + w2 mean (x - y)^2 + ws (1 - SSIM) of [3,H,W] images.  Returns dict(loss,
+    ssim (mean), map [3,H,W], grad [3,H,W], scale [3,H,W]: running-error scale of the gradient)."""
+    x = _f64(image)
+    y = _f64(target)
+    _, H, W = x.shape
+    smap = np.zeros_like(x)
+    g = np.zeros_like(x) if with_grad else None
+    sc = np.zeros_like(x) if with_grad else None
+    ss = ctypes.c_double(0.0)
+    L = _load().oracle_loss_ssim(W, H, _p(x), _p(y), float(w1), float(w2), float(ws), _p(g), _p(smap), _p(sc),
+                                 ctypes.byref(ss))
+    return {"loss": float(L), "ssim": float(ss.value), "map": smap, "grad": g, "scale": sc}
 
 
 def loss_l2(image, target):

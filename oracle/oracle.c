@@ -795,3 +795,122 @@ void oracle_grad_sum_rs(int W, int H, int64_t n, const double *prs, double fx, d
     }
     free(part); free(gs); free(gc64); free(jac);
 }
+
+/* ------------------------------------------------------------------------ */
+/* SSIM pixel loss                                                          */
+/* ------------------------------------------------------------------------ */
+/* "Drawing with Gaussians" (2D fitting): the pixel loss (1 - w) L1 +
+ * w (1 - SSIM), w = 0.2; "FlashImgs" (Commands, --loss l2 / l1 / l2+ssim /
+ * l1+ssim; parse_loss gives the (l1, l2, ssim) ratios); fvdb (ssim_lambda).
+ * The pages print no SSIM formula; the reading is the usual structural
+ * similarity index: per channel, local statistics under an 11x11 Gaussian
+ * window (sigma 1.5, weights normalised to sum 1), pixels outside the image
+ * count as 0 (the map has the image's size), and
+ *   SSIM(p) = (2 mx my + C1)(2 sxy + C2) / ((mx^2 + my^2 + C1)(sxx + syy + C2)),
+ *   mx = sum_q G(q-p) x(q), sxx = sum_q G(q-p) x(q)^2 - mx^2,
+ *   sxy = sum_q G(q-p) x(q) y(q) - mx my,  C1 = 0.01^2, C2 = 0.03^2,
+ * x = the rendered image, y = the target; SSIM = the mean of the map over
+ * the 3HW entries.  The loss:
+ *   L = w1 mean|x - y| + w2 mean (x - y)^2 + ws (1 - SSIM).
+ * Its gradient with respect to x, with f = SSIM(p) a function of the window
+ * moments (mx, my, Exx, Eyy, Exy) at p:
+ *   dSSIM/dx(q) = (1/3HW) sum_p G(q-p) [df/dmx(p) + 2 x(q) df/dExx(p)
+ *                                     + y(q) df/dExy(p)],
+ *   df/dmx  = f (2my/n1 - 2my/n2 - 2mx/d1 + 2mx/d2),
+ *   df/dExx = -f / d2,   df/dExy = 2 f / n2,
+ * n1 = 2 mx my + C1, n2 = 2 sxy + C2, d1 = mx^2 + my^2 + C1, d2 = sxx + syy + C2.
+ * d|x - y|/dx = sign(x - y) (0 at 0). */
+
+static void ssim_window(double g[11])
+{
+    double s = 0.0;
+    for (int k = 0; k < 11; ++k) { g[k] = exp(-((k - 5) * (k - 5)) / (2.0 * 1.5 * 1.5)); s += g[k]; }
+    for (int k = 0; k < 11; ++k) g[k] /= s;
+}
+
+/* The five window moments at every pixel of one channel (zero outside). */
+static void ssim_moments(int W, int H, const double *x, const double *y, double *m /*[5][H*W]*/)
+{
+    double g[11];
+    ssim_window(g);
+    const int64_t HW = (int64_t)H * W;
+    #pragma omp parallel for schedule(static)
+    for (int i = 0; i < H; ++i)
+        for (int j = 0; j < W; ++j) {
+            double s[5] = {0, 0, 0, 0, 0};
+            for (int a = -5; a <= 5; ++a)
+                for (int b = -5; b <= 5; ++b) {
+                    int ii = i + a, jj = j + b;
+                    if (ii < 0 || ii >= H || jj < 0 || jj >= W) continue;
+                    double wgt = g[a + 5] * g[b + 5];
+                    double xv = x[(int64_t)ii * W + jj], yv = y[(int64_t)ii * W + jj];
+                    s[0] += wgt * xv; s[1] += wgt * yv;
+                    s[2] += wgt * xv * xv; s[3] += wgt * yv * yv; s[4] += wgt * xv * yv;
+                }
+            for (int k = 0; k < 5; ++k) m[k * HW + (int64_t)i * W + j] = s[k];
+        }
+}
+
+/* Loss value and (if dx != NULL) dL/dx [3,H,W]; ssim_map (may be NULL) [3,H,W];
+ * dscale (may be NULL) [3,H,W]: a running-error scale of dL/dx (every sum
+ * and every inner sum taken over absolute values).  Returns L; *ssim_out =
+ * the mean SSIM. */
+double oracle_loss_ssim(int W, int H, const double *x, const double *y, double w1, double w2, double ws,
+                        double *dx, double *ssim_map, double *dscale, double *ssim_out)
+{
+    const double C1 = 0.0001, C2 = 0.0009;
+    const int64_t HW = (int64_t)H * W, N = 3 * HW;
+    double g[11];
+    ssim_window(g);
+    double *m = (double *)malloc(sizeof(double) * 5 * HW);
+    double *D = (double *)malloc(sizeof(double) * 6 * HW);     /* df/dmx, df/dExx, df/dExy and their abs scales */
+    double l1 = 0.0, l2 = 0.0, ss = 0.0;
+    for (int k = 0; k < 3; ++k) {
+        const double *xk = x + k * HW, *yk = y + k * HW;
+        ssim_moments(W, H, xk, yk, m);
+        for (int64_t p = 0; p < HW; ++p) {
+            const double mx = m[p], my = m[HW + p];
+            const double sxx = m[2*HW + p] - mx * mx, syy = m[3*HW + p] - my * my, sxy = m[4*HW + p] - mx * my;
+            const double n1 = 2 * mx * my + C1, n2 = 2 * sxy + C2, d1 = mx * mx + my * my + C1, d2 = sxx + syy + C2;
+            const double f = (n1 * n2) / (d1 * d2);
+            ss += f;
+            if (ssim_map) ssim_map[k * HW + p] = f;
+            D[p] = f * (2 * my / n1 - 2 * my / n2 - 2 * mx / d1 + 2 * mx / d2);
+            D[HW + p] = -f / d2;
+            D[2*HW + p] = 2 * f / n2;
+            D[3*HW + p] = fabs(f) * (2 * fabs(my) / fabs(n1) + 2 * fabs(my) / fabs(n2) + 2 * fabs(mx) / fabs(d1) +
+                                     2 * fabs(mx) / fabs(d2));
+            D[4*HW + p] = fabs(D[HW + p]);
+            D[5*HW + p] = fabs(D[2*HW + p]);
+            const double e = xk[p] - yk[p];
+            l1 += fabs(e);
+            l2 += e * e;
+        }
+        if (!dx) continue;
+        #pragma omp parallel for schedule(static)
+        for (int i = 0; i < H; ++i)
+            for (int j = 0; j < W; ++j) {
+                double s0 = 0, s1 = 0, s2 = 0, a0 = 0, a1 = 0, a2 = 0;
+                for (int a = -5; a <= 5; ++a)
+                    for (int b = -5; b <= 5; ++b) {
+                        int ii = i + a, jj = j + b;
+                        if (ii < 0 || ii >= H || jj < 0 || jj >= W) continue;
+                        double wgt = g[a + 5] * g[b + 5];
+                        int64_t pp = (int64_t)ii * W + jj;
+                        s0 += wgt * D[pp]; s1 += wgt * D[HW + pp]; s2 += wgt * D[2*HW + pp];
+                        a0 += wgt * D[3*HW + pp]; a1 += wgt * D[4*HW + pp]; a2 += wgt * D[5*HW + pp];
+                    }
+                const int64_t q = (int64_t)i * W + j;
+                const double xv = xk[q], yv = yk[q], e = xv - yv;
+                const double dssim = (s0 + 2 * xv * s1 + yv * s2) / (double)N;
+                const double sg = e > 0 ? 1.0 : (e < 0 ? -1.0 : 0.0);
+                dx[k * HW + q] = w1 * sg / (double)N + w2 * 2 * e / (double)N - ws * dssim;
+                if (dscale)
+                    dscale[k * HW + q] = fabs(w1) / (double)N + fabs(w2) * 2 * (fabs(xv) + fabs(yv)) / (double)N +
+                                         fabs(ws) * (a0 + 2 * fabs(xv) * a1 + fabs(yv) * a2) / (double)N;
+            }
+    }
+    free(m); free(D);
+    if (ssim_out) *ssim_out = ss / (double)N;
+    return w1 * l1 / (double)N + w2 * l2 / (double)N + ws * (1.0 - ss / (double)N);
+}

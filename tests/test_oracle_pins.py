@@ -12,7 +12,9 @@
 - loss: numpy; Adam: the first-step closed form and torch.optim.Adam in float64;
 - rotation-scale Gaussians and rendering at another scale: the Cholesky-form oracle on numpy's
   Cholesky factor of R diag(s^2) R^T (and of D Sigma D), the rotation symmetries, numpy's matrix
-  inverse for the cutoff set, a hand-worked value at scale 2, central finite differences.
+  inverse for the cutoff set, a hand-worked value at scale 2, central finite differences;
+- the SSIM loss: scipy's Gaussian window with a zero-padded correlation for the local moments,
+  closed forms for x = y + d and x = a y, identical images, central finite differences.
 """
 import math
 from fractions import Fraction
@@ -638,3 +640,86 @@ def test_rs_chain_scale_is_the_propagated_cholesky_scale():
     want = np.abs(J).T @ Cc[0, 2:5]
     np.testing.assert_allclose(chain[0, 2:5], want, rtol=1e-6)
     np.testing.assert_allclose(chain[0, :2], [fx * Cc[0, 0], fy * Cc[0, 1]], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------------------------
+# SSIM pixel loss
+# --------------------------------------------------------------------------------------------
+
+def _lib_moments(x, y):
+    """Window moments by scipy: a library Gaussian window (11 taps, std 1.5, normalised) and a
+    zero-padded correlation."""
+    from scipy.ndimage import correlate
+    from scipy.signal.windows import gaussian
+    g = gaussian(11, 1.5)
+    w = np.outer(g, g) / g.sum() ** 2
+    c = lambda a: correlate(a, w, mode="constant", cval=0.0)
+    return c(x), c(y), c(x * x), c(y * y), c(x * y)
+
+
+def test_ssim_identical_images():
+    import oracle
+    x = np.random.default_rng(801).uniform(0, 1, (3, 20, 24))
+    r = oracle.loss_ssim(x, x, 0.8, 0.3, 0.2)
+    assert abs(r["ssim"] - 1.0) < 1e-14 and abs(r["loss"]) < 1e-14
+    assert np.abs(r["grad"]).max() < 1e-15
+
+
+@pytest.mark.parametrize("kind", ["offset", "scale"])
+def test_ssim_closed_forms(kind):
+    """x = y + d (luminance term only) and x = a y (both terms), against moments from scipy."""
+    import oracle
+    rng = np.random.default_rng(802)
+    y = rng.uniform(0.1, 0.9, (3, 23, 27))
+    x = y + 0.07 if kind == "offset" else 1.3 * y
+    r = oracle.loss_ssim(x, y, 0.0, 0.0, 1.0, with_grad=False)
+    C1, C2 = 0.01 ** 2, 0.03 ** 2
+    for k in range(3):
+        _, my, _, eyy, _ = _lib_moments(x[k], y[k])
+        vy = eyy - my * my
+        if kind == "offset":
+            mx = my + 0.07 * _lib_moments(np.ones_like(y[k]), y[k])[0]     # the in-image window weight
+            want = (2 * mx * my + C1) / (mx * mx + my * my + C1)
+            sl = np.s_[5:-5, 5:-5]                                          # full windows: sigma_x = sigma_y
+        else:
+            a = 1.3
+            want = (2 * a * my * my + C1) / ((1 + a * a) * my * my + C1) * (2 * a * vy + C2) / ((1 + a * a) * vy + C2)
+            sl = np.s_[:, :]
+        np.testing.assert_allclose(r["map"][k][sl], want[sl], rtol=1e-10, atol=1e-13)
+
+
+def test_ssim_map_against_library_moments():
+    import oracle
+    rng = np.random.default_rng(803)
+    x, y = rng.uniform(0, 1, (3, 17, 29)), rng.uniform(0, 1, (3, 17, 29))
+    r = oracle.loss_ssim(x, y, 0.0, 0.0, 1.0, with_grad=False)
+    C1, C2 = 0.01 ** 2, 0.03 ** 2
+    tot = 0.0
+    for k in range(3):
+        mx, my, exx, eyy, exy = _lib_moments(x[k], y[k])
+        vx, vy, cxy = exx - mx * mx, eyy - my * my, exy - mx * my
+        m = (2 * mx * my + C1) * (2 * cxy + C2) / ((mx * mx + my * my + C1) * (vx + vy + C2))
+        np.testing.assert_allclose(r["map"][k], m, rtol=1e-9, atol=1e-12)
+        tot += m.sum()
+    assert abs(r["ssim"] - tot / x.size) < 1e-12
+    assert abs(r["loss"] - (1 - tot / x.size)) < 1e-12
+
+
+def test_ssim_loss_grad_finite_differences():
+    import oracle
+    rng = np.random.default_rng(804)
+    x, y = rng.uniform(0, 1, (3, 12, 10)), rng.uniform(0, 1, (3, 12, 10))
+    w = (0.7, 0.25, 0.3)
+    r = oracle.loss_ssim(x, y, *w)
+    num = np.zeros_like(x)
+    h = 1e-6
+    for idx in np.ndindex(x.shape):
+        a, b = x.copy(), x.copy()
+        a[idx] += h
+        b[idx] -= h
+        num[idx] = (oracle.loss_ssim(a, y, *w, with_grad=False)["loss"] -
+                    oracle.loss_ssim(b, y, *w, with_grad=False)["loss"]) / (2 * h)
+    np.testing.assert_allclose(r["grad"], num, rtol=1e-5, atol=1e-9)
+    l1 = np.abs(x - y).mean()
+    l2 = ((x - y) ** 2).mean()
+    assert abs(r["loss"] - (w[0] * l1 + w[1] * l2 + w[2] * (1 - r["ssim"]))) < 1e-14
