@@ -275,6 +275,72 @@ def bench_alpha(args, w, target, params, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_ssim(args, w, target, params, dev):
+    """Sum mode with the SSIM pixel loss: one step = preprocess and binning + forward + gi_loss_ssim
+    (two stencil kernels) + backward with the gather + Adam."""
+    import torch
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter
+
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    lw = tuple(float(v) for v in args.loss.split(","))
+    if len(lw) != 3:
+        raise SystemExit("--loss takes l2 or three weights w1,w2,ws")
+    fit = Fitter(target, params, capacity_slack=2.0, loss=lw)
+    for _ in range(args.warmup):
+        fit.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fit.step()
+    torch.cuda.synchronize()
+    t_train = time.perf_counter() - t0
+    r = fit.raster
+    M_now = int(r.d_num.cpu().item()) & 0xFFFFFFFF
+    assert M_now <= r.capacity, "tile-pair capacity exceeded during the timed run"
+    ms_step = 1e3 * t_train / args.steps
+    final_loss = float(fit.loss.item())
+    log(f"[bench] ssim-loss train: {ms_step:.4f} ms/step, loss {final_loss:.4e}")
+    nk = max(20, min(args.steps, 500))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E() for _ in range(2)] for _ in range(nk)]
+    for k in range(nk):
+        ev[k][0].record()
+        gi.gi_loss_ssim(W, H, r.image, fit.target, *lw, fit.dL, fit.loss, fit.ssim_ws)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ssim_s = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])) * 1e-3
+    nbytes = 44 * 3 * W * H           # per entry: 8 B read + 12 B written, then 20 B read + 4 B written
+    gbs = nbytes / ssim_s / 1e9
+    log(f"[bench] gi_loss_ssim {ssim_s*1e6:.1f} us ({gbs:.0f} GB/s algorithmic)")
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "fwd+bwd steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "width": W, "height": H, "gaussians": wl.n, "mode": "sum",
+                   "loss": {"w1": lw[0], "w2": lw[1], "ws": lw[2]}},
+        "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
+                  "roofline: HIP events on the launch stream around gi_loss_ssim (two kernels)",
+        "final_loss": final_loss,
+        "kernels_us": {"loss_ssim": round(ssim_s * 1e6, 2)},
+        "roofline": {"bound": "hbm", "kernel": "k_ssim_fwd + k_ssim_bwd", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM, "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4), "traffic": None,
+                     "avg_launch_us": round(ssim_s * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_rs(args, wlname, target, dev):
     """Rotation-scale Gaussians on a sum workload: one step = gi_params_to_cholesky + preprocess and
     binning + gi_render_fwd_l2 + gi_render_bwd (gather, loss) + gi_params_to_cholesky_grad + Adam."""
@@ -371,6 +437,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--params", choices=["cholesky", "rs"], default="cholesky",
                     help="parameter form of the Gaussians (rs: rotation-scale, converted on the GPU each step)")
+    ap.add_argument("--loss", default="l2", help="l2, or weights w1,w2,ws of w1 L1 + w2 L2 + ws (1 - SSIM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -405,6 +472,8 @@ def main():
         return bench_alpha(args, w, target, params, dev)
     if args.params == "rs":
         return bench_rs(args, wlname, target, dev)
+    if args.loss != "l2":
+        return bench_ssim(args, w, target, params, dev)
 
     # ---------------- training step (the whole hot path) ----------------
     fit = Fitter(target, params, capacity_slack=2.0)

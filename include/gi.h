@@ -487,6 +487,30 @@ gi_status gi_params_to_cholesky(int32_t kind, int64_t n, const float *params, fl
 gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *params, float fx, float fy,
                                      const float *dout, float *dparams, int32_t accumulate, void *stream);
 
+/*
+ * gi_loss_ssim -- the pixel loss
+ *     L = w1 mean|I - T| + w2 mean (I - T)^2 + ws (1 - SSIM)
+ *   over the 3HW entries, and dL/dI ("Drawing with Gaussians", 2D fitting:
+ *   (1 - w) L1 + w (1 - SSIM) with w = 0.2; "FlashImgs", Commands: --loss l2,
+ *   l1, l2+ssim, l1+ssim, and parse_loss's (l1, l2, ssim) ratios; fvdb:
+ *   ssim_lambda).  SSIM (a reading: the pages give no formula) is the mean
+ *   over the 3HW entries of the structural similarity map: per channel, the
+ *   local statistics under an 11x11 Gaussian window (sigma 1.5, weights
+ *   normalised to 1; pixels outside the image count as 0, the map has the
+ *   image's size),
+ *     SSIM(p) = (2 mx my + C1)(2 sxy + C2) / ((mx^2 + my^2 + C1)(sxx + syy + C2)),
+ *   C1 = 0.01^2, C2 = 0.03^2 (x = I, y = T).  d|e|/de = sign(e), 0 at 0.
+ *   Two stencil kernels (fp32); the loss is added up in fp64 in a fixed order.
+ *   image, target  device float [3][H][W].
+ *   dL_dimage      device float [3][H][W], written; must not alias the inputs.
+ *   d_loss         device float [1] (written: L) or NULL.
+ *   workspace      device, >= gi_loss_ssim_workspace_bytes(W, H), 256-byte aligned.
+ */
+size_t gi_loss_ssim_workspace_bytes(int32_t width, int32_t height);
+gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const float *target, float w1, float w2,
+                       float ws, float *dL_dimage, float *d_loss, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

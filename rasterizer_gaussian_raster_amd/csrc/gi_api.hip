@@ -385,4 +385,21 @@ gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *param
                                                          as_stream(stream)));
 }
 
+size_t gi_loss_ssim_workspace_bytes(int32_t width, int32_t height) {
+    if (width < 1 || height < 1 || width > kMaxDim || height > kMaxDim) return 0;
+    return gi::ssim_workspace_bytes(width, height);
+}
+
+gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const float *target, float w1, float w2,
+                       float ws, float *dL_dimage, float *d_loss, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    if (width < 1 || height < 1 || width > kMaxDim || height > kMaxDim) return GI_ERR_INVALID_ARG;
+    if (!std::isfinite(w1) || !std::isfinite(w2) || !std::isfinite(ws)) return GI_ERR_INVALID_ARG;
+    if (!image || !target || !dL_dimage || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::ssim_workspace_bytes(width, height)) return GI_ERR_INVALID_ARG;
+    if (dL_dimage == image || dL_dimage == target) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_loss_ssim(width, height, image, target, w1, w2, ws, dL_dimage, d_loss, workspace,
+                                           as_stream(stream)));
+}
+
 }  // extern "C"

@@ -151,6 +151,11 @@ hipError_t launch_loss_l2(int64_t count, const float *image, const float *target
 hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, float *v, const float *lr,
                        double beta1, double beta2, double eps, int step, int zero_grad, hipStream_t s);
 
+// k_ssim.hip
+size_t ssim_workspace_bytes(int W, int H);
+hipError_t launch_loss_ssim(int W, int H, const float *x, const float *y, float w1, float w2, float ws, float *dL,
+                            float *loss, void *ws_ptr, hipStream_t s);
+
 // k_params.hip
 hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
                                      hipStream_t s);

@@ -79,6 +79,8 @@ def load():
         "gi_loss_l2": ([i64, P, P, P, P, P, sz, P], i32),
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
         "gi_params_to_cholesky": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P], i32),
+        "gi_loss_ssim_workspace_bytes": ([i32, i32], sz),
+        "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, P], i32),
         "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
@@ -239,6 +241,16 @@ def gi_params_to_cholesky_grad(kind, n, params, fx, fy, dout, dparams, accumulat
     _check(load().gi_params_to_cholesky_grad(int(kind), int(n), _ptr(params), float(fx), float(fy), _ptr(dout),
                                              _ptr(dparams), 1 if accumulate else 0, _stream(stream)),
            "gi_params_to_cholesky_grad")
+
+
+def gi_loss_ssim_workspace_bytes(W, H):
+    return int(load().gi_loss_ssim_workspace_bytes(int(W), int(H)))
+
+
+def gi_loss_ssim(W, H, image, target, w1, w2, ws, dL_dimage, d_loss, workspace, stream=None):
+    _check(load().gi_loss_ssim(int(W), int(H), _ptr(image), _ptr(target), float(w1), float(w2), float(ws),
+                               _ptr(dL_dimage), _ptr(d_loss), _ptr(workspace), int(workspace.numel()),
+                               _stream(stream)), "gi_loss_ssim")
 
 
 def gi_render_fwd_l2(d, n, records, pixbox, ranges, vals, target, image, dL_dimage, loss_partials, stream=None,

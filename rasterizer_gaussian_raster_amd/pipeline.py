@@ -246,7 +246,9 @@ class Fitter:
     """Fits Gaussians to a target image with L2 loss and Adam (all steps in libgi)."""
 
     def __init__(self, target, params, logit=None, background=None, lr=DEFAULT_LR, lr_logit=0.05, lr_bg=0.01,
-                 betas=(0.9, 0.999), eps=1e-8, capacity_slack=1.5):
+                 betas=(0.9, 0.999), eps=1e-8, capacity_slack=1.5, loss=None):
+        """loss: None for the L2 loss, or weights (w1, w2, ws) of w1 L1 + w2 L2 + ws (1 - SSIM)
+        (gi_loss_ssim; the sum mode then takes the separate forward / loss / backward / Adam launches)."""
         self.target = target.contiguous()
         _, H, W = self.target.shape
         self.params = params.contiguous().clone()
@@ -269,6 +271,9 @@ class Fitter:
         self.dL = torch.empty_like(self.target)
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self.loss_ws = torch.empty(gi.gi_loss_workspace_bytes(self.target.numel()), dtype=torch.uint8, device=dev)
+        self.loss_w = None if loss is None else tuple(float(v) for v in loss)
+        if self.loss_w is not None:
+            self.ssim_ws = torch.empty(gi.gi_loss_ssim_workspace_bytes(W, H), dtype=torch.uint8, device=dev)
         self.step_count = 0
         self.graphs = None
         self.d_step = None
@@ -321,8 +326,8 @@ class Fitter:
     def capture(self, warmup=2):
         """Record the sum-mode step as two HIP graphs (with and without the tile-order refresh).  The
         `warmup` steps run first (real steps) on a side stream, as graph capture asks."""
-        if self.logit is not None:
-            raise ValueError("graph capture is for the sum mode")
+        if self.logit is not None or self.loss_w is not None:
+            raise ValueError("graph capture is for the sum mode with the L2 loss")
         dev = self.params.device
         self.d_step = torch.full((1,), self.step_count, dtype=torch.int32, device=dev)
         side = torch.cuda.Stream(device=dev)
@@ -350,14 +355,25 @@ class Fitter:
             self.step_count += 1
             return
         r = self.raster
-        if self.logit is None:
+        if self.logit is None and self.loss_w is None:
             self._sum_step(self.step_count % ORDER_EVERY == 0)
             self.step_count += 1
             return
-        bg = self.bg4
+        bg = self.bg4 if self.logit is not None else None
         r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.params, logit=self.logit)
         r.forward(bg)
-        gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
+        if self.loss_w is None:
+            gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
+        else:
+            _, H, W = self.target.shape
+            gi.gi_loss_ssim(W, H, r.image, self.target, *self.loss_w, self.dL, self.loss, self.ssim_ws)
+        if self.logit is None:
+            r.backward(self.dL, self.grad)
+            self.step_count += 1
+            b1, b2 = self.betas
+            gi.gi_adam_step(self.n, 8, self.params, self.grad, self.m, self.v, self.lr, b1, b2, self.eps,
+                            self.step_count, 1)
+            return
         r.backward(self.dL, self.grad, logit=self.logit, background=bg, dlogit=self.g_logit,
                    dbackground=self.g_bg)
         self.step_count += 1
