@@ -32,32 +32,57 @@ __device__ __forceinline__ float ssim_at(const float *a, int W, int H, int i, in
 __global__ __launch_bounds__(256) void k_ssim_fwd(int W, int H, const float *__restrict__ x,
                                                   const float *__restrict__ y, SsimWin win,
                                                   float *__restrict__ D, float *__restrict__ part) {
-    __shared__ float sx[kSsimS][kSsimS + 1], sy[kSsimS][kSsimS + 1];
+    __shared__ float sv[2][kSsimS][kSsimS + 1];           // x, y of the staged pixels
     __shared__ float hs[5][kSsimS][kSsimT + 1];
     __shared__ float red[3][4];
     const int tid = threadIdx.x, ch = blockIdx.z;
     const int x0 = blockIdx.x * kSsimT, y0 = blockIdx.y * kSsimT;
     const size_t plane = (size_t)W * H;
     const float *xc = x + ch * plane, *yc = y + ch * plane;
-    for (int e = tid; e < kSsimS * kSsimS; e += 256) {
-        const int r = e / kSsimS, c = e % kSsimS;
-        sx[r][c] = ssim_at(xc, W, H, y0 - kSsimR + r, x0 - kSsimR + c);
-        sy[r][c] = ssim_at(yc, W, H, y0 - kSsimR + r, x0 - kSsimR + c);
+    // every load of the staging goes out before the first LDS store (one round of memory latency)
+    constexpr int kRounds = (kSsimS * kSsimS + 255) / 256;
+    float vx[kRounds], vy[kRounds];
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+        const int e = tid + 256 * q, r = e / kSsimS, c = e % kSsimS;
+        const bool ok = e < kSsimS * kSsimS;
+        vx[q] = ok ? ssim_at(xc, W, H, y0 - kSsimR + r, x0 - kSsimR + c) : 0.0f;
+        vy[q] = ok ? ssim_at(yc, W, H, y0 - kSsimR + r, x0 - kSsimR + c) : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+        const int e = tid + 256 * q, r = e / kSsimS, c = e % kSsimS;
+        if (e < kSsimS * kSsimS) {
+            sv[0][r][c] = vx[q];
+            sv[1][r][c] = vy[q];
+        }
     }
     __syncthreads();
-    for (int e = tid; e < kSsimS * kSsimT; e += 256) {      // rows: every staged row, the tile's columns
-        const int r = e / kSsimT, c = e % kSsimT;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
+    // rows: every staged row, the tile's columns, two adjacent columns per thread (their 12 inputs
+    // read once from LDS; the pass is bound by LDS reads)
+    if (tid < kSsimS * kSsimT / 2) {
+        const int r = tid >> 3, c = (tid & 7) * 2;
+        float xv[12], yv[12];
 #pragma unroll
-        for (int b = 0; b < 11; ++b) {
-            const float xv = sx[r][c + b], yv = sy[r][c + b], g = win.g[b];
-            a0 = fmaf(g, xv, a0);
-            a1 = fmaf(g, yv, a1);
-            a2 = fmaf(g, xv * xv, a2);
-            a3 = fmaf(g, yv * yv, a3);
-            a4 = fmaf(g, xv * yv, a4);
+        for (int b = 0; b < 12; ++b) {
+            xv[b] = sv[0][r][c + b];
+            yv[b] = sv[1][r][c + b];
         }
-        hs[0][r][c] = a0; hs[1][r][c] = a1; hs[2][r][c] = a2; hs[3][r][c] = a3; hs[4][r][c] = a4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
+#pragma unroll
+            for (int b = 0; b < 11; ++b) {
+                const float g = win.g[b], u = xv[b + h], w = yv[b + h];
+                a0 = fmaf(g, u, a0);
+                a1 = fmaf(g, w, a1);
+                a2 = fmaf(g, u * u, a2);
+                a3 = fmaf(g, w * w, a3);
+                a4 = fmaf(g, u * w, a4);
+            }
+            hs[0][r][c + h] = a0; hs[1][r][c + h] = a1; hs[2][r][c + h] = a2; hs[3][r][c + h] = a3;
+            hs[4][r][c + h] = a4;
+        }
     }
     __syncthreads();
     const int tx = tid & 15, ty = tid >> 4;
@@ -75,13 +100,16 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(int W, int H, const float *__r
         const float sxx = m[2] - mx * mx, syy = m[3] - my * my, sxy = m[4] - mx * my;
         const float n1 = fmaf(2.0f * mx, my, kC1), n2 = fmaf(2.0f, sxy, kC2);
         const float d1 = mx * mx + my * my + kC1, d2 = sxx + syy + kC2;
-        f = (n1 * n2) / (d1 * d2);
-        const float D0 = f * (2.0f * my / n1 - 2.0f * my / n2 - 2.0f * mx / d1 + 2.0f * mx / d2);
+        // hardware reciprocals (1 ulp): the divisions' rounding is far below the loss's tolerance
+        const float rn1 = __builtin_amdgcn_rcpf(n1), rn2 = __builtin_amdgcn_rcpf(n2);
+        const float rd1 = __builtin_amdgcn_rcpf(d1), rd2 = __builtin_amdgcn_rcpf(d2);
+        f = (n1 * n2) * (rd1 * rd2);
+        const float D0 = f * (2.0f * my * (rn1 - rn2) + 2.0f * mx * (rd2 - rd1));
         const size_t o = ch * plane + (size_t)i * W + j;
         D[o] = D0;
-        D[3 * plane + o] = -f / d2;
-        D[6 * plane + o] = 2.0f * f / n2;
-        const float e = sx[ty + kSsimR][tx + kSsimR] - sy[ty + kSsimR][tx + kSsimR];
+        D[3 * plane + o] = -f * rd2;
+        D[6 * plane + o] = 2.0f * f * rn2;
+        const float e = sv[0][ty + kSsimR][tx + kSsimR] - sv[1][ty + kSsimR][tx + kSsimR];
         l1 = fabsf(e);
         l2 = e * e;
     }
@@ -111,48 +139,70 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(int W, int H, const float *__r
     const double inv_n = 1.0 / (3.0 * (double)plane);
     if (blockIdx.z == 3) {                                // the spare workgroup: the loss
         if (blockIdx.x != 0 || blockIdx.y != 0) return;
-        __shared__ double sred[3][256];
+        __shared__ double sred[3][4];
         double a[3] = {0.0, 0.0, 0.0};
         for (int t = threadIdx.x; t < nparts; t += 256)
+#pragma unroll
             for (int k = 0; k < 3; ++k) a[k] += (double)part[3 * t + k];
-        for (int k = 0; k < 3; ++k) sred[k][threadIdx.x] = a[k];
-        __syncthreads();
-        for (int s = 128; s >= 1; s >>= 1) {
-            if (threadIdx.x < s)
-                for (int k = 0; k < 3; ++k) sred[k][threadIdx.x] += sred[k][threadIdx.x + s];
-            __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) a[k] += __shfl_xor(a[k], d, 64);
+            if ((threadIdx.x & 63) == 0) sred[k][threadIdx.x >> 6] = a[k];
         }
-        if (threadIdx.x == 0 && loss)
-            loss[0] = (float)(w1d * sred[1][0] * inv_n + w2d * sred[2][0] * inv_n + wsd * (1.0 - sred[0][0] * inv_n));
+        __syncthreads();
+        if (threadIdx.x == 0 && loss) {
+            double t[3];
+            for (int k = 0; k < 3; ++k) t[k] = ((sred[k][0] + sred[k][1]) + sred[k][2]) + sred[k][3];
+            loss[0] = (float)(w1d * t[1] * inv_n + w2d * t[2] * inv_n + wsd * (1.0 - t[0] * inv_n));
+        }
         return;
     }
     __shared__ float sd[3][kSsimS][kSsimS + 1];
     __shared__ float hs[3][kSsimS][kSsimT + 1];
     const int tid = threadIdx.x, ch = blockIdx.z;
     const int x0 = blockIdx.x * kSsimT, y0 = blockIdx.y * kSsimT;
-    for (int e = tid; e < kSsimS * kSsimS; e += 256) {
-        const int r = e / kSsimS, c = e % kSsimS;
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            sd[k][r][c] = ssim_at(D + (3 * k + ch) * plane, W, H, y0 - kSsimR + r, x0 - kSsimR + c);
-    }
-    __syncthreads();
-    for (int e = tid; e < kSsimS * kSsimT; e += 256) {
-        const int r = e / kSsimT, c = e % kSsimT;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-#pragma unroll
-        for (int b = 0; b < 11; ++b) {
-            const float g = win.g[b];
-            a0 = fmaf(g, sd[0][r][c + b], a0);
-            a1 = fmaf(g, sd[1][r][c + b], a1);
-            a2 = fmaf(g, sd[2][r][c + b], a2);
-        }
-        hs[0][r][c] = a0; hs[1][r][c] = a1; hs[2][r][c] = a2;
-    }
-    __syncthreads();
     const int tx = tid & 15, ty = tid >> 4;
     const int i = y0 + ty, j = x0 + tx;
-    if (i >= H || j >= W) return;
+    const bool inside = i < H && j < W;
+    const size_t o = ch * plane + (size_t)(inside ? i : 0) * W + (inside ? j : 0);
+    const float xv = x[o], yv = y[o];                     // the own pixel's inputs, with the staging loads
+    constexpr int kRounds = (kSsimS * kSsimS + 255) / 256;
+    float v[3][kRounds];
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+        const int e = tid + 256 * q, r = e / kSsimS, c = e % kSsimS;
+        const bool ok = e < kSsimS * kSsimS;
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            v[k][q] = ok ? ssim_at(D + (3 * k + ch) * plane, W, H, y0 - kSsimR + r, x0 - kSsimR + c) : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+        const int e = tid + 256 * q, r = e / kSsimS, c = e % kSsimS;
+        if (e < kSsimS * kSsimS)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) sd[k][r][c] = v[k][q];
+    }
+    __syncthreads();
+    if (tid < kSsimS * kSsimT / 2) {                      // rows, two adjacent columns per thread
+        const int r = tid >> 3, c = (tid & 7) * 2;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            float dv[12];
+#pragma unroll
+            for (int b = 0; b < 12; ++b) dv[b] = sd[k][r][c + b];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float a = 0.f;
+#pragma unroll
+                for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], dv[b + h], a);
+                hs[k][r][c + h] = a;
+            }
+        }
+    }
+    __syncthreads();
+    if (!inside) return;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int a = 0; a < 11; ++a) {
@@ -161,8 +211,7 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(int W, int H, const float *__r
         s1 = fmaf(g, hs[1][ty + a][tx], s1);
         s2 = fmaf(g, hs[2][ty + a][tx], s2);
     }
-    const size_t o = ch * plane + (size_t)i * W + j;
-    const float xv = x[o], yv = y[o], e = xv - yv;
+    const float e = xv - yv;
     const float n = (float)(3.0 * (double)plane);
     const float dssim = fmaf(yv, s2, fmaf(2.0f * xv, s1, s0)) / n;
     const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
