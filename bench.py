@@ -343,7 +343,8 @@ def bench_ssim(args, w, target, params, dev):
 
 def bench_rs(args, wlname, target, dev):
     """Rotation-scale Gaussians on a sum workload: one step = gi_params_to_cholesky + preprocess and
-    binning + gi_render_fwd_l2 + gi_render_bwd (gather, loss) + gi_params_to_cholesky_grad + Adam."""
+    binning + the fused forward / L2 / backward raster + gi_adam_step_pairs_rs (gather, chain rule,
+    Adam, loss)."""
     import torch
     from rasterizer_gaussian_raster_amd import gi, synth
     from rasterizer_gaussian_raster_amd.pipeline import FitterRS
@@ -367,26 +368,27 @@ def bench_rs(args, wlname, target, dev):
     final_loss = float(fit.loss.item())
     log(f"[bench] rotation-scale train: {ms_step:.4f} ms/step, loss {final_loss:.4e}")
 
-    # HIP events on the launch stream: the conversion, its chain rule, and the separate forward / backward
+    # HIP events on the launch stream: the conversion, the fused raster, and gather + chain rule + Adam
+    # (on copies of the optimiser state, so the trained parameters stay as they are)
     n = fit.n
     nk = max(20, min(args.steps, 500))
+    p2, m2, v2 = fit.params.clone(), fit.m.clone(), fit.v.clone()
     E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[E() for _ in range(5)] for _ in range(nk)]
+    ev = [[E() for _ in range(4)] for _ in range(nk)]
     for k in range(nk):
         ev[k][0].record()
         gi.gi_params_to_cholesky(gi.PARAMS_RS, n, fit.params, 1.0, 1.0, fit.chol)
         ev[k][1].record()
-        r.forward_l2(fit.target, fit.dL)
+        r.forward_backward_l2(fit.target)
         ev[k][2].record()
-        r.backward(fit.dL, fit.gchol)
+        gi.gi_adam_step_pairs_rs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, p2, m2, v2, fit.lr, 0.9, 0.999, 1e-8,
+                                 fit.step_count + 1)
         ev[k][3].record()
-        gi.gi_params_to_cholesky_grad(gi.PARAMS_RS, n, fit.params, 1.0, 1.0, fit.gchol, fit.grad)
-        ev[k][4].record()
     torch.cuda.synchronize()
-    ms = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(4)] for k in range(nk)])
-    conv_s, fwd_s, bwd_s, chain_s = (float(x) * 1e-3 for x in ms.mean(0))
-    log(f"[bench] convert {conv_s*1e6:.1f} us, fwd {fwd_s*1e6:.1f} us, bwd+gather {bwd_s*1e6:.1f} us, "
-        f"chain {chain_s*1e6:.1f} us")
+    ms = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(3)] for k in range(nk)])
+    conv_s, fused_s, chain_s = (float(x) * 1e-3 for x in ms.mean(0))
+    log(f"[bench] convert {conv_s*1e6:.1f} us, fused raster {fused_s*1e6:.1f} us, gather+chain+adam "
+        f"{chain_s*1e6:.1f} us")
     ranges = r.ranges.cpu().numpy().view(np.uint32)
     pairs = binned_pairs(W, H, ranges)
 
@@ -418,11 +420,10 @@ def bench_rs(args, wlname, target, dev):
         "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
                   "kernels_us: HIP events on the launch stream around each launch, on the trained parameters",
         "final_loss": final_loss,
-        "kernels_us": {"params_to_cholesky": round(conv_s * 1e6, 2), "render_fwd_l2": round(fwd_s * 1e6, 2),
-                       "render_bwd_gather": round(bwd_s * 1e6, 2), "params_to_cholesky_grad": round(chain_s * 1e6, 2)},
-        "roofline": roof_alu("k_render_sum_bwd (+ gather)", FLOP_BWD, bwd_s),
+        "kernels_us": {"params_to_cholesky": round(conv_s * 1e6, 2), "render_fwd_bwd_fused": round(fused_s * 1e6, 2),
+                       "adam_pairs_rs": round(chain_s * 1e6, 2)},
+        "roofline": roof_alu("k_render_sum_fused", FLOP_FWD + FLOP_BWD, fused_s),
         "roofline_convert": roof_hbm("k_params_to_cholesky", 64 * n, conv_s),
-        "roofline_chain": roof_hbm("k_params_to_cholesky_grad", 96 * n, chain_s),
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

@@ -511,6 +511,21 @@ gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const 
                        float ws, float *dL_dimage, float *d_loss, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/*
+ * gi_adam_step_pairs_rs -- gi_adam_step_pairs for rotation-scale params (the
+ *   "gaussianimage_rs" form of "GaussianImage"): each Gaussian's per-pair
+ *   gradient slots (left by gi_render_fwd_bwd_l2, or gi_render_bwd with
+ *   dparams = NULL, for the Cholesky params gi_params_to_cholesky made with
+ *   fx = fy = 1) are added in emission order, carried through
+ *   gi_params_to_cholesky_grad's chain rule and applied to p by the Adam step,
+ *   in one pass.  Arguments as gi_adam_step_pairs (no device step counter);
+ *   p, m, v device float [n][8] in the rotation-scale form.
+ */
+gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
+                                const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
+                                const float *lr, double beta1, double beta2, double eps, int32_t step,
+                                const float *loss_partials, int64_t loss_count, float *d_loss, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@
 // One thread per Gaussian, two 16-byte loads and stores: HBM-bound.
 #include <hip/hip_runtime.h>
 
+#include "gi_device.hpp"
 #include "gi_launch.hpp"
 
 namespace gi {
@@ -50,16 +51,12 @@ __global__ __launch_bounds__(256) void k_params_to_cholesky(int kind, int64_t n,
     out[2 * g + 1] = ob;
 }
 
-__global__ __launch_bounds__(256) void k_params_to_cholesky_grad(int kind, int64_t n, const float4 *__restrict__ in,
-                                                                float fx, float fy, const float4 *__restrict__ dout,
-                                                                float4 *__restrict__ din, int accumulate) {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (g >= n) return;
-    const float4 a = in[2 * g], b = in[2 * g + 1];
-    const float4 d0 = dout[2 * g], d1 = dout[2 * g + 1];
+// d(loss)/d(params in form `kind`) from the gradient (d0, d1) w.r.t. the Cholesky form of the
+// Gaussian (a, b) scaled by (fx, fy).
+__device__ __forceinline__ void chol_chain(int kind, float4 a, float4 b, float fx, float fy, float4 d0, float4 d1,
+                                           float4 &r0, float4 &r1) {
     // gradients w.r.t. the unscaled Cholesky form
     const float gmx = fx * d0.x, gmy = fy * d0.y, g11 = fx * d0.z, g21 = fy * d0.w, g22 = fy * d1.x;
-    float4 r0, r1;
     if (kind == 1) {
         const CholRS c = rs_cholesky(a.z, a.w, b.x);
         if (!(c.l11 > 0.0f) || !isfinite(c.l11) || !isfinite(c.l21) || !isfinite(c.l22)) {
@@ -82,6 +79,17 @@ __global__ __launch_bounds__(256) void k_params_to_cholesky_grad(int kind, int64
         r0 = make_float4(gmx, gmy, g11, g21);
         r1 = make_float4(g22, d1.y, d1.z, d1.w);
     }
+}
+
+__global__ __launch_bounds__(256) void k_params_to_cholesky_grad(int kind, int64_t n, const float4 *__restrict__ in,
+                                                                float fx, float fy, const float4 *__restrict__ dout,
+                                                                float4 *__restrict__ din, int accumulate) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= n) return;
+    const float4 a = in[2 * g], b = in[2 * g + 1];
+    const float4 d0 = dout[2 * g], d1 = dout[2 * g + 1];
+    float4 r0, r1;
+    chol_chain(kind, a, b, fx, fy, d0, d1, r0, r1);
     if (accumulate) {
         const float4 o0 = din[2 * g], o1 = din[2 * g + 1];
         r0 = make_float4(o0.x + r0.x, o0.y + r0.y, o0.z + r0.z, o0.w + r0.w);
@@ -91,11 +99,66 @@ __global__ __launch_bounds__(256) void k_params_to_cholesky_grad(int kind, int64
     din[2 * g + 1] = r1;
 }
 
+// Rotation-scale training: each Gaussian's per-pair gradient slots added in emission order (the
+// Cholesky-form gradient, as k_grad_gather forms it), the chain rule, and the Adam update of the
+// rotation-scale params; one thread per Gaussian.  The spare last workgroup reduces the loss.
+__global__ __launch_bounds__(256) void k_adam_pairs_rs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
+                                                       const float4 *__restrict__ part, float4 *__restrict__ p,
+                                                       float4 *__restrict__ m, float4 *__restrict__ v, AdamHP ah,
+                                                       const float *__restrict__ loss_part, int nparts,
+                                                       double inv_count, float *__restrict__ loss) {
+    if (loss && blockIdx.x == gridDim.x - 1) {
+        __shared__ double sm[256];
+        loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
+        return;
+    }
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= n) return;
+    float c1, c2;
+    adam_step_bias(ah, c1, c2);
+    const uint32_t o0 = offsets[g], o1r = offsets[g + 1];
+    const uint32_t o1 = offsets[n] <= capacity ? o1r : o0;   // else the binning overflowed: zero gradient
+    float4 d0 = make_float4(0.f, 0.f, 0.f, 0.f), d1 = d0;
+    gather_slots(part, o0, o1, d0, d1);
+    const float4 a = p[2 * g], b = p[2 * g + 1];
+    float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0;
+    if (o1 > o0) chol_chain(1, a, b, 1.0f, 1.0f, d0, d1, r0, r1);
+    float P[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const float G[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    const float4 m0 = m[2 * g], m1 = m[2 * g + 1], v0 = v[2 * g], v1 = v[2 * g + 1];
+    float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adam_update(P[k], G[k], M[k], V[k], ah.lr[k], ah, c1, c2);
+    p[2 * g] = make_float4(P[0], P[1], P[2], P[3]);
+    p[2 * g + 1] = make_float4(P[4], P[5], P[6], P[7]);
+    m[2 * g] = make_float4(M[0], M[1], M[2], M[3]);
+    m[2 * g + 1] = make_float4(M[4], M[5], M[6], M[7]);
+    v[2 * g] = make_float4(V[0], V[1], V[2], V[3]);
+    v[2 * g + 1] = make_float4(V[4], V[5], V[6], V[7]);
+}
+
 hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
                                      hipStream_t s) {
     if (n == 0) return hipSuccess;
     k_params_to_cholesky<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
         kind, n, reinterpret_cast<const float4 *>(in), fx, fy, reinterpret_cast<float4 *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_pairs_rs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws,
+                                float *p, float *m, float *v, const float *lr, double beta1, double beta2, double eps,
+                                int step, const float *loss_partials, int64_t loss_count, float *d_loss,
+                                hipStream_t s) {
+    const int nb = (n + 255) / 256 + (d_loss ? 1 : 0);
+    if (nb == 0) return hipSuccess;
+    const BwdPlan pl = make_bwd_plan(W, H, capacity);
+    const AdamHP a = make_adam_hp(lr, beta1, beta2, eps, step, nullptr);
+    const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+    k_adam_pairs_rs<<<nb, 256, 0, s>>>(
+        n, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(static_cast<const char *>(ws) + pl.off_part),
+        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a,
+        loss_partials, ntiles, loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss);
     return hipGetLastError();
 }
 

@@ -197,9 +197,9 @@ def cholesky_params(params, kind=gi.PARAMS_RS, fx=1.0, fy=1.0, out=None, stream=
 
 class FitterRS:
     """Fits rotation-scale Gaussians (mux, muy, sx, sy, theta, cr, cg, cb) with L2 loss and Adam
-    (sum mode).  A step: gi_params_to_cholesky, preprocess + binning, gi_render_fwd_l2,
-    gi_render_bwd (with the per-Gaussian gather and the loss), gi_params_to_cholesky_grad, and Adam
-    on the rotation-scale parameters."""
+    (sum mode).  A step: gi_params_to_cholesky, preprocess + binning, the fused forward / L2 /
+    backward raster (gi_render_fwd_bwd_l2), and gi_adam_step_pairs_rs (gather of the per-pair
+    gradients, chain rule, Adam on the rotation-scale parameters, and the loss)."""
 
     def __init__(self, target, params_rs, lr=DEFAULT_LR_RS, betas=(0.9, 0.999), eps=1e-8, capacity_slack=1.5):
         self.target = target.contiguous()
@@ -230,6 +230,19 @@ class FitterRS:
         return False
 
     def step(self):
+        r, n = self.raster, self.n
+        cholesky_params(self.params, out=self.chol)
+        r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.chol)
+        r.forward_backward_l2(self.target)
+        self.step_count += 1
+        b1, b2 = self.betas
+        gi.gi_adam_step_pairs_rs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v, self.lr,
+                                 b1, b2, self.eps, self.step_count, loss_partials=r.loss_partials,
+                                 loss_count=3 * r.W * r.H, d_loss=self.loss)
+
+    def step_separate(self):
+        """The same step from the separate calls (forward + L2, backward with the gather, the chain
+        rule, Adam): a cross-check of the fused one."""
         r, n = self.raster, self.n
         cholesky_params(self.params, out=self.chol)
         r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.chol)

@@ -188,3 +188,21 @@ def test_rs_fit_reduces_loss():
     last = float(fit.loss.item())
     print(f"rs fit: loss {first:.4e} -> {last:.4e}")
     assert np.isfinite(last) and last < 0.7 * first
+
+
+def test_rs_fused_step_matches_separate_calls():
+    """gi_adam_step_pairs_rs (gather + chain rule + Adam in one pass) against the separate calls."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd.pipeline import FitterRS
+    w = synth.make_workload_rs("tiny_fit_64x64")
+    a = FitterRS(dev(w["target"]), dev(w["params_rs"]))
+    b = FitterRS(dev(w["target"]), dev(w["params_rs"]))
+    for _ in range(3):
+        a.step()
+        b.step_separate()
+    torch.cuda.synchronize()
+    pa, pb = a.params.cpu().numpy(), b.params.cpu().numpy()
+    err = np.abs(pa - pb).max()
+    print(f"fused vs separate rotation-scale steps: max |dp| {err:.3e}, loss {a.loss.item():.6e} / {b.loss.item():.6e}")
+    np.testing.assert_allclose(pa, pb, rtol=1e-5, atol=1e-6)
+    assert abs(a.loss.item() - b.loss.item()) <= 1e-6 * abs(b.loss.item())
