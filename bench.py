@@ -342,9 +342,9 @@ def bench_ssim(args, w, target, params, dev):
 
 
 def bench_rs(args, wlname, target, dev):
-    """Rotation-scale Gaussians on a sum workload: one step = gi_params_to_cholesky + preprocess and
-    binning + the fused forward / L2 / backward raster + gi_adam_step_pairs_rs (gather, chain rule,
-    Adam, loss)."""
+    """Rotation-scale Gaussians on a sum workload: one step = preprocess and binning of the Cholesky
+    form + the fused forward / L2 / backward raster + gi_adam_step_pairs_rs (gather, chain rule,
+    Adam, loss, and the updated Gaussians' Cholesky form for the next step)."""
     import torch
     from rasterizer_gaussian_raster_amd import gi, synth
     from rasterizer_gaussian_raster_amd.pipeline import FitterRS
@@ -372,7 +372,7 @@ def bench_rs(args, wlname, target, dev):
     # (on copies of the optimiser state, so the trained parameters stay as they are)
     n = fit.n
     nk = max(20, min(args.steps, 500))
-    p2, m2, v2 = fit.params.clone(), fit.m.clone(), fit.v.clone()
+    p2, m2, v2, c2 = fit.params.clone(), fit.m.clone(), fit.v.clone(), torch.empty_like(fit.chol)
     E = lambda: torch.cuda.Event(enable_timing=True)
     ev = [[E() for _ in range(4)] for _ in range(nk)]
     for k in range(nk):
@@ -382,7 +382,7 @@ def bench_rs(args, wlname, target, dev):
         r.forward_backward_l2(fit.target)
         ev[k][2].record()
         gi.gi_adam_step_pairs_rs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, p2, m2, v2, fit.lr, 0.9, 0.999, 1e-8,
-                                 fit.step_count + 1)
+                                 fit.step_count + 1, chol_out=c2)
         ev[k][3].record()
     torch.cuda.synchronize()
     ms = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(3)] for k in range(nk)])

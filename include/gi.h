@@ -520,11 +520,15 @@ gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const 
  *   gi_params_to_cholesky_grad's chain rule and applied to p by the Adam step,
  *   in one pass.  Arguments as gi_adam_step_pairs (no device step counter);
  *   p, m, v device float [n][8] in the rotation-scale form.
+ *   chol_out  device float [n][8] or NULL: also the updated Gaussians'
+ *             Cholesky form (what gi_params_to_cholesky with fx = fy = 1
+ *             writes, bit for bit), ready for the next step's binning.
  */
 gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
                                 const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
                                 const float *lr, double beta1, double beta2, double eps, int32_t step,
-                                const float *loss_partials, int64_t loss_count, float *d_loss, void *stream);
+                                const float *loss_partials, int64_t loss_count, float *d_loss, float *chol_out,
+                                void *stream);
 
 #ifdef __cplusplus
 }

@@ -405,7 +405,8 @@ gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const 
 gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
                                 const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
                                 const float *lr, double beta1, double beta2, double eps, int32_t step,
-                                const float *loss_partials, int64_t loss_count, float *d_loss, void *stream) {
+                                const float *loss_partials, int64_t loss_count, float *d_loss, float *chol_out,
+                                void *stream) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
         capacity >= (1ll << 31) || step < 1 || !lr)
         return GI_ERR_INVALID_ARG;
@@ -414,9 +415,10 @@ gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *
     if (!offsets || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
     if (n > 0 && (!p || !m || !v || !aligned16(p) || !aligned16(m) || !aligned16(v))) return GI_ERR_INVALID_ARG;
+    if (n > 0 && chol_out && (!aligned16(chol_out) || chol_out == p)) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_adam_pairs_rs((int)n, desc->width, desc->height, offsets, capacity, workspace, p, m,
                                                v, lr, beta1, beta2, eps, step, loss_partials, loss_count, d_loss,
-                                               as_stream(stream)));
+                                               chol_out, as_stream(stream)));
 }
 
 }  // extern "C"

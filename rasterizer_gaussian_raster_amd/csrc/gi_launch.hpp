@@ -163,7 +163,7 @@ hipError_t launch_params_to_cholesky_grad(int kind, int64_t n, const float *in, 
                                           const float *dout, float *din, int accumulate, hipStream_t s);
 hipError_t launch_adam_pairs_rs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws,
                                 float *p, float *m, float *v, const float *lr, double beta1, double beta2, double eps,
-                                int step, const float *loss_partials, int64_t loss_count, float *d_loss,
+                                int step, const float *loss_partials, int64_t loss_count, float *d_loss, float *chol,
                                 hipStream_t s);
 
 }  // namespace gi

@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256) void k_adam_pairs_rs(int n, const uint32_t *__
                                                        const float4 *__restrict__ part, float4 *__restrict__ p,
                                                        float4 *__restrict__ m, float4 *__restrict__ v, AdamHP ah,
                                                        const float *__restrict__ loss_part, int nparts,
-                                                       double inv_count, float *__restrict__ loss) {
+                                                       double inv_count, float *__restrict__ loss,
+                                                       float4 *__restrict__ chol) {
     if (loss && blockIdx.x == gridDim.x - 1) {
         __shared__ double sm[256];
         loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
@@ -136,6 +137,11 @@ __global__ __launch_bounds__(256) void k_adam_pairs_rs(int n, const uint32_t *__
     m[2 * g + 1] = make_float4(M[4], M[5], M[6], M[7]);
     v[2 * g] = make_float4(V[0], V[1], V[2], V[3]);
     v[2 * g + 1] = make_float4(V[4], V[5], V[6], V[7]);
+    if (chol) {                                           // the next step's Cholesky form
+        const CholRS c = rs_cholesky(P[2], P[3], P[4]);
+        chol[2 * g] = make_float4(P[0], P[1], c.l11, c.l21);
+        chol[2 * g + 1] = make_float4(c.l22, P[5], P[6], P[7]);
+    }
 }
 
 hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
@@ -148,7 +154,7 @@ hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float
 
 hipError_t launch_adam_pairs_rs(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws,
                                 float *p, float *m, float *v, const float *lr, double beta1, double beta2, double eps,
-                                int step, const float *loss_partials, int64_t loss_count, float *d_loss,
+                                int step, const float *loss_partials, int64_t loss_count, float *d_loss, float *chol,
                                 hipStream_t s) {
     const int nb = (n + 255) / 256 + (d_loss ? 1 : 0);
     if (nb == 0) return hipSuccess;
@@ -158,7 +164,8 @@ hipError_t launch_adam_pairs_rs(int n, int W, int H, const uint32_t *offsets, in
     k_adam_pairs_rs<<<nb, 256, 0, s>>>(
         n, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(static_cast<const char *>(ws) + pl.off_part),
         reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a,
-        loss_partials, ntiles, loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss);
+        loss_partials, ntiles, loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss,
+        reinterpret_cast<float4 *>(chol));
     return hipGetLastError();
 }
 

@@ -85,7 +85,7 @@ def load():
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
         "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P, i64, P, P], i32),
-        "gi_adam_step_pairs_rs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, i64, P, P], i32),
+        "gi_adam_step_pairs_rs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, i64, P, P, P], i32),
         "gi_render_fwd_bwd_l2": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P], i32),
         "gi_render_image": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, i64, P, P, P, sz, P, P, P,
                              P], i32),
@@ -234,12 +234,13 @@ def gi_adam_step(rows, row_len, p, g, m, v, lr, beta1, beta2, eps, step, zero_gr
 
 
 def gi_adam_step_pairs_rs(d, n, offsets, capacity, workspace, p, m, v, lr, beta1, beta2, eps, step, stream=None,
-                          loss_partials=None, loss_count=0, d_loss=None):
+                          loss_partials=None, loss_count=0, d_loss=None, chol_out=None):
     lr_arr = (ctypes.c_float * 8)(*[float(x) for x in lr])
     _check(load().gi_adam_step_pairs_rs(ctypes.byref(d), int(n), _ptr(offsets), int(capacity), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(p), _ptr(m), _ptr(v),
                                         lr_arr, float(beta1), float(beta2), float(eps), int(step),
-                                        _ptr(loss_partials), int(loss_count), _ptr(d_loss), _stream(stream)),
+                                        _ptr(loss_partials), int(loss_count), _ptr(d_loss), _ptr(chol_out),
+                                        _stream(stream)),
            "gi_adam_step_pairs_rs")
 
 

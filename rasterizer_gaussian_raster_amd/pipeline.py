@@ -230,15 +230,16 @@ class FitterRS:
         return False
 
     def step(self):
+        """The Cholesky form of the current params is in self.chol: written by the previous step's
+        gi_adam_step_pairs_rs (or by __init__ / step_separate)."""
         r, n = self.raster, self.n
-        cholesky_params(self.params, out=self.chol)
         r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.chol)
         r.forward_backward_l2(self.target)
         self.step_count += 1
         b1, b2 = self.betas
         gi.gi_adam_step_pairs_rs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v, self.lr,
                                  b1, b2, self.eps, self.step_count, loss_partials=r.loss_partials,
-                                 loss_count=3 * r.W * r.H, d_loss=self.loss)
+                                 loss_count=3 * r.W * r.H, d_loss=self.loss, chol_out=self.chol)
 
     def step_separate(self):
         """The same step from the separate calls (forward + L2, backward with the gather, the chain
@@ -253,6 +254,7 @@ class FitterRS:
         self.step_count += 1
         b1, b2 = self.betas
         gi.gi_adam_step(n, 8, self.params, self.grad, self.m, self.v, self.lr, b1, b2, self.eps, self.step_count, 0)
+        cholesky_params(self.params, out=self.chol)
 
 
 class Fitter:

@@ -206,3 +206,7 @@ def test_rs_fused_step_matches_separate_calls():
     print(f"fused vs separate rotation-scale steps: max |dp| {err:.3e}, loss {a.loss.item():.6e} / {b.loss.item():.6e}")
     np.testing.assert_allclose(pa, pb, rtol=1e-5, atol=1e-6)
     assert abs(a.loss.item() - b.loss.item()) <= 1e-6 * abs(b.loss.item())
+    # the fused step's Cholesky form for the next step = gi_params_to_cholesky of the updated params
+    from rasterizer_gaussian_raster_amd.pipeline import cholesky_params
+    want = cholesky_params(a.params).cpu().numpy()
+    np.testing.assert_array_equal(a.chol.cpu().numpy().view(np.uint32), want.view(np.uint32))
