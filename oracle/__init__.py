@@ -17,8 +17,9 @@ differences, torch's Adam; for the rotation-scale form and rendering at another
 scale: numpy's Cholesky factor fed to the Cholesky-form oracle, rotation
 symmetries, numpy's matrix inverse for the cutoff set; for the SSIM loss:
 scipy's Gaussian window and zero-padded correlation, closed forms for shifted
-and scaled images, central finite differences).  No function is "parity
-unpinned".
+and scaled images, central finite differences; for the merge: moments and
+channel integrals by numerical quadrature of the two summed Gaussians, and
+identical pairs).  No function is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -87,6 +88,8 @@ def _load():
     lib.oracle_grad_sum_rs.restype = None
     lib.oracle_loss_ssim.argtypes = [i32, i32, P, P, f64, f64, f64, P, P, P, P]
     lib.oracle_loss_ssim.restype = f64
+    lib.oracle_merge_pairs.argtypes = [i64, P, P, P]
+    lib.oracle_merge_pairs.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = i32
     _lib = lib
@@ -275,6 +278,15 @@ def loss_ssim(image, target, w1=0.8, w2=0.0, ws=0.2, with_grad=True):
     L = _load().oracle_loss_ssim(W, H, _p(x), _p(y), float(w1), float(w2), float(ws), _p(g), _p(smap), _p(sc),
                                  ctypes.byref(ss))
     return {"loss": float(L), "ssim": float(ss.value), "map": smap, "grad": g, "scale": sc}
+
+
+def merge_pairs(params, pairs):
+    """Moment-matching merge of the Gaussian pairs [P,2] (indices into params [N,8]) -> [P,8]."""
+    par = _f64(params).reshape(-1, 8)
+    pr = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    out = np.zeros((pr.shape[0], 8))
+    _load().oracle_merge_pairs(pr.shape[0], _p(par), _p(pr), _p(out))
+    return out
 
 
 def loss_l2(image, target):

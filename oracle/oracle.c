@@ -914,3 +914,50 @@ double oracle_loss_ssim(int W, int H, const double *x, const double *y, double w
     if (ssim_out) *ssim_out = ss / (double)N;
     return w1 * l1 / (double)N + w2 * l2 / (double)N + ws * (1.0 - ss / (double)N);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Moment-matching merge                                                    */
+/* ------------------------------------------------------------------------ */
+/* "FlashImgs" (Commands, merge: an overcomplete set merged down, 80K -> 50K,
+ * by moment matching; Library API: merge_gaussians).  The pages give no
+ * formula; the reading: a Gaussian n of the sum image is the function
+ * c_n exp(-q_n/2), whose integral per channel is 2 pi |det L_n| c_{n,k}.  Two
+ * Gaussians (i, j) merge into the one whose mean and covariance are those of
+ * the mixture weighted by the masses w = |det L| sum_k |c_k|:
+ *   W = w_i + w_j,  mu = (w_i mu_i + w_j mu_j) / W,
+ *   Sigma = sum_{n=i,j} (w_n / W) (Sigma_n + (mu_n - mu)(mu_n - mu)^T),
+ * L = chol(Sigma) (positive diagonal), and whose colour keeps each channel's
+ * integral:  c_k = (|det L_i| c_{i,k} + |det L_j| c_{j,k}) / |det L|.
+ * W = 0 (no mass) takes equal weights.  Sigma_n = L_n L_n^T as elsewhere. */
+void oracle_merge_pairs(int64_t np, const double *params, const int64_t *pairs, double *out)
+{
+    for (int64_t t = 0; t < np; ++t) {
+        const double *a = params + 8 * pairs[2*t], *b = params + 8 * pairs[2*t + 1];
+        const double *pp[2] = {a, b};
+        double det[2], w[2], S[2][3];
+        for (int s = 0; s < 2; ++s) {
+            const double *p = pp[s];
+            det[s] = fabs(p[2] * p[4]);
+            w[s] = det[s] * (fabs(p[5]) + fabs(p[6]) + fabs(p[7]));
+            S[s][0] = p[2] * p[2];                 /* Sigma11 */
+            S[s][1] = p[2] * p[3];                 /* Sigma21 */
+            S[s][2] = p[3] * p[3] + p[4] * p[4];   /* Sigma22 */
+        }
+        double W = w[0] + w[1];
+        double f0 = W > 0 ? w[0] / W : 0.5, f1 = W > 0 ? w[1] / W : 0.5;
+        const double mx = f0 * a[0] + f1 * b[0], my = f0 * a[1] + f1 * b[1];
+        double s11 = 0, s21 = 0, s22 = 0;
+        for (int s = 0; s < 2; ++s) {
+            const double f = s ? f1 : f0;
+            const double dx = pp[s][0] - mx, dy = pp[s][1] - my;
+            s11 += f * (S[s][0] + dx * dx);
+            s21 += f * (S[s][1] + dx * dy);
+            s22 += f * (S[s][2] + dy * dy);
+        }
+        const double l11 = sqrt(s11), l21 = s21 / l11, l22 = sqrt(s22 - l21 * l21);
+        const double dn = l11 * l22;
+        double *o = out + 8 * t;
+        o[0] = mx; o[1] = my; o[2] = l11; o[3] = l21; o[4] = l22;
+        for (int k = 0; k < 3; ++k) o[5 + k] = (det[0] * a[5 + k] + det[1] * b[5 + k]) / dn;
+    }
+}

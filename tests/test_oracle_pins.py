@@ -723,3 +723,57 @@ def test_ssim_loss_grad_finite_differences():
     l1 = np.abs(x - y).mean()
     l2 = ((x - y) ** 2).mean()
     assert abs(r["loss"] - (w[0] * l1 + w[1] * l2 + w[2] * (1 - r["ssim"]))) < 1e-14
+
+
+# --------------------------------------------------------------------------------------------
+# moment-matching merge
+# --------------------------------------------------------------------------------------------
+
+def _quad_moments(p, lo, hi, n=1201):
+    """Mass, mean and covariance of sum_n w_n N(mu_n, Sigma_n)-shaped functions by quadrature on a
+    fine grid (rectangle rule), using each Gaussian's own normalised density (scipy) times its mass
+    weight |det L| sum|c|, and each channel's integral of c exp(-q/2)."""
+    from scipy.stats import multivariate_normal
+    xs = np.linspace(lo, hi, n)
+    X, Y = np.meshgrid(xs, xs)
+    pts = np.stack([X, Y], -1)
+    h = (hi - lo) / (n - 1)
+    dens = np.zeros_like(X)
+    chan = np.zeros(3)
+    for g in p:
+        L = np.array([[g[2], 0.0], [g[3], g[4]]])
+        S = L @ L.T
+        w = abs(g[2] * g[4]) * np.abs(g[5:]).sum()
+        dens += w * multivariate_normal(g[:2], S).pdf(pts)
+        chan += g[5:] * 2 * np.pi * abs(g[2] * g[4])
+    m = dens.sum() * h * h
+    mu = np.array([(dens * X).sum(), (dens * Y).sum()]) * h * h / m
+    dx, dy = X - mu[0], Y - mu[1]
+    C = np.array([[(dens * dx * dx).sum(), (dens * dx * dy).sum()],
+                  [(dens * dx * dy).sum(), (dens * dy * dy).sum()]]) * h * h / m
+    return mu, C, chan
+
+
+def test_merge_matches_the_mixture_moments():
+    import oracle
+    p = np.array([[10.0, 12.0, 1.5, 0.4, 1.1, 0.6, 0.2, 0.9],
+                  [13.0, 11.0, -0.9, -0.3, 1.8, 0.3, -0.5, 0.4]])
+    o = oracle.merge_pairs(p, [[0, 1]])[0]
+    mu, C, chan = _quad_moments(p, -10.0, 35.0)
+    np.testing.assert_allclose(o[:2], mu, rtol=1e-6, atol=1e-6)
+    L = np.array([[o[2], 0.0], [o[3], o[4]]])
+    np.testing.assert_allclose(L @ L.T, C, rtol=1e-5, atol=1e-6)
+    assert o[2] > 0 and o[4] > 0
+    np.testing.assert_allclose(o[5:] * 2 * np.pi * abs(o[2] * o[4]), chan, rtol=1e-12)
+
+
+def test_merge_of_identical_gaussians():
+    import oracle
+    g = np.array([4.0, -2.0, -1.3, 0.7, 2.2, 0.5, -0.1, 0.8])
+    o = oracle.merge_pairs(np.stack([g, g]), [[0, 1]])[0]
+    want = g.copy()
+    want[2] = abs(g[2])
+    want[3] = g[3] * np.sign(g[2])
+    want[4] = abs(g[4])
+    want[5:] = 2 * g[5:]
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-14)
