@@ -341,6 +341,42 @@ def bench_ssim(args, w, target, params, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_merge(args, dev):
+    """gi_merge_pairs on the merge phase's shape: 30K disjoint pairs of 80K Gaussians (80K -> 50K)."""
+    import torch
+    from rasterizer_gaussian_raster_amd import gi, synth
+
+    n, npairs = 80000, 30000
+    p = torch.from_numpy(synth.random_case(301, 768, 512, n, sigma=(0.5, 8.0))).to(dev)
+    perm = np.random.default_rng(302).permutation(n)
+    pairs = torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).astype(np.int32)).to(dev)
+    out = torch.empty((npairs, 8), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        gi.gi_merge_pairs(npairs, pairs, n, p, out)
+    nk = max(20, min(args.steps, 1000))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E(), E()] for _ in range(nk)]
+    for k in range(nk):
+        ev[k][0].record()
+        gi.gi_merge_pairs(npairs, pairs, n, p, out)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    secs = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    nbytes = 104 * npairs             # two 32 B records + 8 B of indices read, 32 B written per pair
+    gbs = nbytes / secs / 1e9
+    log(f"[bench] gi_merge_pairs: {secs*1e6:.2f} us for {npairs} pairs ({gbs:.0f} GB/s algorithmic)")
+    print(json.dumps({
+        "metric": "moment-matching merge, pairs/s", "value": round(npairs / secs, 1), "unit": "pairs/s",
+        "n_gpus": 1, "steps": nk, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "merge_80k_to_50k", "gaussians": n, "pairs": npairs},
+        "timing": "HIP events on the launch stream around each launch",
+        "roofline": {"bound": "hbm", "kernel": "k_merge_pairs", "achieved": round(gbs, 1), "peak": PEAK_HBM,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4), "traffic": None,
+                     "avg_launch_us": round(secs * 1e6, 2)},
+        "cpu_baseline": None}), flush=True)
+
+
 def bench_rs(args, wlname, target, dev):
     """Rotation-scale Gaussians on a sum workload: one step = preprocess and binning of the Cholesky
     form + the fused forward / L2 / backward raster + gi_adam_step_pairs_rs (gather, chain rule,
@@ -439,6 +475,8 @@ def main():
     ap.add_argument("--params", choices=["cholesky", "rs"], default="cholesky",
                     help="parameter form of the Gaussians (rs: rotation-scale, converted on the GPU each step)")
     ap.add_argument("--loss", default="l2", help="l2, or weights w1,w2,ws of w1 L1 + w2 L2 + ws (1 - SSIM)")
+    ap.add_argument("--op", choices=["fit", "merge"], default="fit",
+                    help="merge: time the moment-matching merge of 30K pairs of 80K Gaussians (80K -> 50K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -471,6 +509,8 @@ def main():
         log("[bench] copy calibration: 3 x 256 MiB device-to-device copies")
     if wl.mode != "sum":
         return bench_alpha(args, w, target, params, dev)
+    if args.op == "merge":
+        return bench_merge(args, dev)
     if args.params == "rs":
         return bench_rs(args, wlname, target, dev)
     if args.loss != "l2":

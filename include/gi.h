@@ -530,6 +530,27 @@ gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *
                                 const float *loss_partials, int64_t loss_count, float *d_loss, float *chol_out,
                                 void *stream);
 
+/*
+ * gi_merge_pairs -- moment-matching merge of Gaussian pairs ("FlashImgs",
+ *   Commands: merge, an overcomplete set merged down (80K -> 50K) by moment
+ *   matching; Library API: merge_gaussians).  A reading, as the pages give no
+ *   formula: Gaussian n is the function c_n exp(-q_n/2) with per-channel
+ *   integral 2 pi |det L_n| c_{n,k} and mass w_n = |det L_n| sum_k |c_{n,k}|;
+ *   pair (i, j) becomes the Gaussian with the mean and covariance of the
+ *   mass-weighted mixture,
+ *     mu = (w_i mu_i + w_j mu_j)/W,  Sigma = sum (w/W)(Sigma_n + d_n d_n^T),
+ *     d_n = mu_n - mu, W = w_i + w_j (equal weights when W = 0),
+ *   L = chol(Sigma) with a positive diagonal, and the colour that keeps each
+ *   channel's integral: c_k = (|det L_i| c_{i,k} + |det L_j| c_{j,k}) / |det L|.
+ *   Computed in fp64, rounded to fp32.  Which pairs to merge is the caller's.
+ *   pairs   device int32 [n_pairs][2], 8-byte aligned: indices into params; a
+ *           pair with an index outside [0, n) gives an all-NaN row.
+ *   params  device float [n][8] (Cholesky form); out device float [n_pairs][8],
+ *           not aliasing params.
+ */
+gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const float *params, float *out,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -421,4 +421,13 @@ gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *
                                                chol_out, as_stream(stream)));
 }
 
+gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const float *params, float *out,
+                         void *stream) {
+    if (n_pairs < 0 || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (n_pairs > 0 && (!pairs || !params || !out || !aligned16(params) || !aligned16(out) ||
+                        (reinterpret_cast<uintptr_t>(pairs) & 7u) != 0 || out == params))
+        return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_merge_pairs(n_pairs, n, params, pairs, out, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -157,6 +157,8 @@ hipError_t launch_loss_ssim(int W, int H, const float *x, const float *y, float 
                             float *loss, void *ws_ptr, hipStream_t s);
 
 // k_params.hip
+hipError_t launch_merge_pairs(int64_t np, int64_t n, const float *params, const int32_t *pairs, float *out,
+                              hipStream_t s);
 hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
                                      hipStream_t s);
 hipError_t launch_params_to_cholesky_grad(int kind, int64_t n, const float *in, float fx, float fy,

@@ -80,6 +80,7 @@ def load():
         "gi_adam_step": ([i64, i32, P, P, P, P, P, f64, f64, f64, i32, i32, P], i32),
         "gi_params_to_cholesky": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P], i32),
         "gi_loss_ssim_workspace_bytes": ([i32, i32], sz),
+        "gi_merge_pairs": ([i64, P, i64, P, P, P], i32),
         "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, P], i32),
         "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
@@ -253,6 +254,11 @@ def gi_params_to_cholesky_grad(kind, n, params, fx, fy, dout, dparams, accumulat
     _check(load().gi_params_to_cholesky_grad(int(kind), int(n), _ptr(params), float(fx), float(fy), _ptr(dout),
                                              _ptr(dparams), 1 if accumulate else 0, _stream(stream)),
            "gi_params_to_cholesky_grad")
+
+
+def gi_merge_pairs(n_pairs, pairs, n, params, out, stream=None):
+    _check(load().gi_merge_pairs(int(n_pairs), _ptr(pairs), int(n), _ptr(params), _ptr(out), _stream(stream)),
+           "gi_merge_pairs")
 
 
 def gi_loss_ssim_workspace_bytes(W, H):
