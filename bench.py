@@ -341,6 +341,52 @@ def bench_ssim(args, w, target, params, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_absgrad(args, wlname, target, params, dev):
+    """The sum backward with the per-Gaussian gather, with and without the absgrad output, on the
+    workload's parameters (HIP events on the launch stream)."""
+    import torch
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+
+    W, H = target.shape[2], target.shape[1]
+    n = params.shape[0]
+    r = Raster(W, H, n)
+    r.render(params)
+    dL = torch.empty_like(target)
+    r.forward_l2(target, dL)
+    dp = torch.zeros((n, 8), dtype=torch.float32, device=dev)
+    da = torch.zeros((n, 2), dtype=torch.float32, device=dev)
+    nk = max(20, min(args.steps, 500))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E() for _ in range(3)] for _ in range(nk)]
+    for _ in range(args.warmup):
+        r.backward(dL, dp)
+        r.backward_absgrad(dL, dp, da)
+    for k in range(nk):
+        ev[k][0].record()
+        r.backward(dL, dp)
+        ev[k][1].record()
+        r.backward_absgrad(dL, dp, da)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    ms = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(2)] for k in range(nk)]).mean(0)
+    plain_s, abs_s = float(ms[0]) * 1e-3, float(ms[1]) * 1e-3
+    pairs = binned_pairs(W, H, r.ranges.cpu().numpy().view(np.uint32))
+    tf = FLOP_BWD * pairs / abs_s / 1e12
+    log(f"[bench] backward + gather {plain_s*1e6:.1f} us, with absgrad {abs_s*1e6:.1f} us")
+    print(json.dumps({
+        "metric": METRIC, "value": round(1.0 / abs_s, 1), "unit": "backward passes/s (with absgrad)",
+        "n_gpus": 1, "steps": nk, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wlname, "width": W, "height": H, "gaussians": n, "op": "absgrad"},
+        "timing": "HIP events on the launch stream around gi_render_bwd and gi_render_bwd_absgrad (each with "
+                  "its gather)",
+        "kernels_us": {"bwd_gather": round(plain_s * 1e6, 2), "bwd_gather_absgrad": round(abs_s * 1e6, 2)},
+        "roofline": {"bound": "alu", "kernel": "k_render_sum_bwd<true> (+ gather)", "achieved": round(tf, 3),
+                     "peak": PEAK_FP32, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32, 4), "traffic": None,
+                     "avg_launch_us": round(abs_s * 1e6, 2)},
+        "cpu_baseline": None}), flush=True)
+
+
 def bench_merge(args, dev):
     """gi_merge_pairs on the merge phase's shape: 30K disjoint pairs of 80K Gaussians (80K -> 50K)."""
     import torch
@@ -475,8 +521,9 @@ def main():
     ap.add_argument("--params", choices=["cholesky", "rs"], default="cholesky",
                     help="parameter form of the Gaussians (rs: rotation-scale, converted on the GPU each step)")
     ap.add_argument("--loss", default="l2", help="l2, or weights w1,w2,ws of w1 L1 + w2 L2 + ws (1 - SSIM)")
-    ap.add_argument("--op", choices=["fit", "merge"], default="fit",
-                    help="merge: time the moment-matching merge of 30K pairs of 80K Gaussians (80K -> 50K)")
+    ap.add_argument("--op", choices=["fit", "merge", "absgrad"], default="fit",
+                    help="merge: time the moment-matching merge of 30K pairs of 80K Gaussians (80K -> 50K); "
+                         "absgrad: the sum backward with and without the absgrad output")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -511,6 +558,8 @@ def main():
         return bench_alpha(args, w, target, params, dev)
     if args.op == "merge":
         return bench_merge(args, dev)
+    if args.op == "absgrad":
+        return bench_absgrad(args, wlname, target, params, dev)
     if args.params == "rs":
         return bench_rs(args, wlname, target, dev)
     if args.loss != "l2":

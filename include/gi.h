@@ -551,6 +551,23 @@ gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *
 gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const float *params, float *out,
                          void *stream);
 
+/*
+ * gi_render_bwd_absgrad -- gi_render_bwd in the sum mode (dparams accumulated,
+ *   no loss) that also accumulates each Gaussian's "absgrad" ("Drawing with
+ *   Gaussians", 3D densification: the backward accumulates the per-pixel
+ *   absolute screen-space mean-gradient contributions, which do not cancel):
+ *     dabs[g] += ( sum_p |dL_p/dmux|, sum_p |dL_p/dmuy| )
+ *   over the pixels p the Gaussian is summed at, dL_p/dmu being pixel p's term
+ *   of dL/dmu (p's own 3 channels).  dparams equals gi_render_bwd's bit for bit.
+ *   dabs   device float [n][2], 8-byte aligned, accumulated (+=).
+ *   Other arguments as gi_render_bwd (workspace from
+ *   gi_render_bwd_workspace_bytes).
+ */
+gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
+                                const uint32_t *offsets, const uint32_t *ranges, const uint32_t *tile_order,
+                                const uint32_t *vals, int64_t capacity, const float *dL_dimage, float *dparams,
+                                float *dabs, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -430,4 +430,27 @@ gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const
     return hip_status(gi::launch_merge_pairs(n_pairs, n, params, pairs, out, as_stream(stream)));
 }
 
+gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
+                                const uint32_t *offsets, const uint32_t *ranges, const uint32_t *tile_order,
+                                const uint32_t *vals, int64_t capacity, const float *dL_dimage, float *dparams,
+                                float *dabs, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+        capacity >= (1ll << 31))
+        return GI_ERR_INVALID_ARG;
+    if (!offsets || !ranges || !vals || !dL_dimage || !workspace || !aligned256(workspace))
+        return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !pixbox || !dparams || !dabs || !aligned16(records) || !aligned16(dparams) ||
+                  (reinterpret_cast<uintptr_t>(dabs) & 7u) != 0))
+        return GI_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const int W = desc->width, H = desc->height;
+    hipError_t e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, tile_order, vals, capacity,
+                                             dL_dimage, workspace, nullptr, 0, nullptr, s, true);
+    if (e == hipSuccess)
+        e = gi::launch_grad_gather((int)n, W, H, (int)gi_num_tiles(desc), offsets, capacity, workspace, 0, dparams,
+                                   nullptr, nullptr, s, dabs);
+    return hip_status(e);
+}
+
 }  // extern "C"

@@ -106,13 +106,15 @@ struct BwdPlan {
     size_t off_part;    // float4 [capacity][2]: dmux, dmuy, dl11, dl21 | dl22, dcr, dcg, dcb
     size_t off_logit;   // float [capacity]: dlogit (alpha)
     size_t off_bg;      // float4 [ntiles]: dbackground per tile (alpha)
+    size_t off_abs;     // float2 [capacity]: sum |d mux|, sum |d muy| over the pair's pixels (absgrad)
     size_t bytes;
 };
 BwdPlan make_bwd_plan(int W, int H, int64_t capacity);
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
-                                 const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s);
+                                 const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s,
+                                 bool absgrad = false);
 // Forward (target: also the L2 gradient and loss partials).  With bl, each tile's list is taken
 // from its bucket (and written out) instead of ranges / vals.
 hipError_t launch_render_sum_fwd(int W, int H, const float *records, const uint16_t *pixbox,
@@ -130,7 +132,7 @@ hipError_t launch_render_sum_fused(int W, int H, const float *records, const uin
 // per-tile background partials to dbackground.
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
                               const void *ws, int alpha, float *dparams, float *dlogit, float *dbackground,
-                              hipStream_t s);
+                              hipStream_t s, float *dabs = nullptr);
 
 // k_raster_alpha.hip
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,

@@ -415,11 +415,16 @@ __device__ __forceinline__ int gp_index(int x, int y) {
 
 // Backward of one tile with its dL/dI published in gp and the first share's
 // entries (E0) already loaded; each entry's 8 values go to its emission slot.
-// Wave-local from here on (no workgroup barrier).
+// Wave-local from here on (no workgroup barrier).  ABS also forms each pair's
+// sums of |per-pixel d mux| and |per-pixel d muy| ("absgrad": run partials in
+// pabs [4][kWaveEnt + 64], the pair's total at its slot of part_abs).
+template <bool ABS = false>
 __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx, int ty, uint2 rg, BwdEntry E0,
                                              const float4 *__restrict__ records, const uint2 *__restrict__ pixbox,
                                              const uint32_t *__restrict__ offsets, const uint32_t *vals,
-                                             bool fresh_vals, uint32_t capacity, float4 *__restrict__ part) {
+                                             bool fresh_vals, uint32_t capacity, float4 *__restrict__ part,
+                                             float2 (*pabs)[kWaveEnt + 64] = nullptr,
+                                             float2 *__restrict__ part_abs = nullptr) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int x0 = tx * kTile, y0 = ty * kTile;
     const float k2 = 2.0f * kLn2;
@@ -454,6 +459,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
         const uint32_t R = (nitems + 63u) >> 6;             // items per lane (wave-uniform)
         const uint32_t f = (uint32_t)lane * R, fend = min(f + R, nitems);
         float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;   // the current (entry, run) partial
+        float2 accA = make_float2(0.f, 0.f);                         // ABS: its sums of |h (a u + b v)|, |h v|
         uint32_t cur = 0xffffffffu, cur_slot = 0u;
         for (uint32_t r = 0; r < R; ++r) {
             const uint32_t it = f + r;
@@ -465,6 +471,10 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                         S.part[wave][cur_slot][0] = acc0;
                         S.part[wave][cur_slot][1] = acc1;
                         acc0 = acc1 = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if constexpr (ABS) {
+                            pabs[wave][cur_slot] = accA;
+                            accA = make_float2(0.f, 0.f);
+                        }
                     }
                     // the run's first item continues the previous lane's entry, or an entry starts here
                     const bool cont = r == 0 && it > 0 && (S.items[wave][it - 1] & 0xffu) == e;
@@ -477,12 +487,14 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
                 float Hu = 0.f, Hv = 0.f, Hudx = 0.f, Hvdx = 0.f, Hvdy = 0.f, Cr = 0.f, Cg = 0.f, Cb = 0.f;
+                float Ax = 0.f, Ay = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const float dx = ((float)(x0 + lx + c) + 0.5f) - A.x;
                     const float u = A.z * dx;
                     const float tb = A.w * dx;
                     const float uu = u * u;
+                    const float au = A.z * u;
                     float ch = 0.f, chv = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
@@ -498,6 +510,10 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                         ch += h;
                         chv += hv;
                         Hvdy = fmaf(hv, dy[rr], Hvdy);
+                        if constexpr (ABS) {
+                            Ax += fabsf(h * fmaf(A.w, v, au));
+                            Ay += fabsf(hv);
+                        }
                     }
                     Hu = fmaf(u, ch, Hu);
                     Hudx = fmaf(u * dx, ch, Hudx);
@@ -516,11 +532,16 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 acc1.y += Cr;
                 acc1.z += Cg;
                 acc1.w += Cb;
+                if constexpr (ABS) {
+                    accA.x += k2 * Ax;
+                    accA.y += k2 * fabsf(c) * Ay;
+                }
             }
         }
         if (cur != 0xffffffffu) {
             S.part[wave][cur_slot][0] = acc0;
             S.part[wave][cur_slot][1] = acc1;
+            if constexpr (ABS) pabs[wave][cur_slot] = accA;
         }
         wave_sync();
         // entry e (lane e): its first run's partial, then those of the runs of lanes
@@ -533,18 +554,29 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 s1 = S.part[wave][lane][1];
             }
             const uint32_t L0 = s_e / R, L1 = n_e > 0u ? (s_e + n_e - 1u) / R : L0;
+            float2 sa = make_float2(0.f, 0.f);
+            if constexpr (ABS) {
+                if (n_e > 0u) sa = pabs[wave][lane];
+            }
             for (uint32_t L = L0 + 1u; L <= L1; ++L) {
                 const float4 u0 = S.part[wave][kWaveEnt + L][0], u1 = S.part[wave][kWaveEnt + L][1];
                 s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
                 s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+                if constexpr (ABS) {
+                    const float2 ua = pabs[wave][kWaveEnt + L];
+                    sa.x += ua.x;
+                    sa.y += ua.y;
+                }
             }
             part[2 * (size_t)slot] = s0;
             part[2 * (size_t)slot + 1] = s1;
+            if constexpr (ABS) part_abs[slot] = sa;
         }
         wave_sync();                                        // ent / items are rewritten next batch
     }
 }
 
+template <bool ABS>
 __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W, int H, int tiles_x, int ntiles,
                                                         const float4 *__restrict__ records,
                                                         const uint2 *__restrict__ pixbox,
@@ -554,8 +586,10 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W,
                                                         const float *__restrict__ dL,
                                                         float4 *__restrict__ part,
                                                         const float *__restrict__ loss_part, int nparts,
-                                                        double inv_count, float *__restrict__ loss) {
+                                                        double inv_count, float *__restrict__ loss,
+                                                        float2 *__restrict__ part_abs) {
     __shared__ float4 gp[16 * kGpStride];               // dL/dI of the tile's pixels, block by block
+    __shared__ float2 pabs[ABS ? 4 : 1][kWaveEnt + 64];
     __shared__ __align__(16) unsigned char lds[sizeof(BwdLds)];
     if (loss && blockIdx.x == gridDim.x - 1) {          // the spare last workgroup: the forward's loss
         loss_reduce_block(nparts, loss_part, inv_count, loss, reinterpret_cast<double *>(lds));
@@ -585,7 +619,8 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_bwd(int W,
     bwd_load(e0, ne, records, pixbox, vals, false, E0);
     gp[gp_index(tid & 15, tid >> 4)] = gv0;
     __syncthreads();
-    sum_bwd_tile(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, false, capacity, part);
+    sum_bwd_tile<ABS>(S, gp, tx, ty, rg, E0, records, pixbox, offsets, vals, false, capacity, part,
+                      ABS ? pabs : nullptr, part_abs);
 }
 
 // Forward with the L2 loss, then the backward of the same tile, in one
@@ -646,7 +681,8 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
                                                      const float *__restrict__ part_l,
                                                      const float4 *__restrict__ part_bg,
                                                      float *__restrict__ dparams, float *__restrict__ dlogit,
-                                                     float *__restrict__ dbg) {
+                                                     float *__restrict__ dbg, const float2 *__restrict__ part_abs,
+                                                     float2 *__restrict__ dabs) {
     if (offsets[n] > capacity) return;                  // binning overflowed: nothing was rendered
     if (dbg && blockIdx.x == 0) {
         __shared__ float4 sm[256];
@@ -671,6 +707,15 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
     if (g >= n) return;
     const uint32_t o0 = offsets[g], o1 = offsets[g + 1];
     if (o1 == o0) return;
+    if (dabs) {                                         // absgrad: the pairs' sums, in emission order
+        float2 s = dabs[g];
+        for (uint32_t q = o0; q < o1; ++q) {
+            const float2 u = part_abs[q];
+            s.x += u.x;
+            s.y += u.y;
+        }
+        dabs[g] = s;
+    }
     float4 *d = reinterpret_cast<float4 *>(dparams) + 2 * (size_t)g;
     float4 d0 = d[0], d1 = d[1];
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
@@ -758,6 +803,7 @@ BwdPlan make_bwd_plan(int W, int H, int64_t capacity) {
     p.off_part = off; off = align256(off + 32 * cap);
     p.off_logit = off; off = align256(off + 4 * cap);
     p.off_bg = off; off = align256(off + 16 * (size_t)ntiles);
+    p.off_abs = off; off = align256(off + 8 * cap);
     p.bytes = off;
     return p;
 }
@@ -780,7 +826,7 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
 
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
                               const void *ws, int alpha, float *dparams, float *dlogit, float *dbackground,
-                              hipStream_t s) {
+                              hipStream_t s, float *dabs) {
     if (n == 0 && !(alpha && dbackground)) return hipSuccess;
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     const char *w = static_cast<const char *>(ws);
@@ -789,7 +835,8 @@ hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *o
         n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(w + p.off_part),
         alpha ? reinterpret_cast<const float *>(w + p.off_logit) : nullptr,
         reinterpret_cast<const float4 *>(w + p.off_bg), dparams, alpha ? dlogit : nullptr,
-        alpha ? dbackground : nullptr);
+        alpha ? dbackground : nullptr, reinterpret_cast<const float2 *>(w + p.off_abs),
+        reinterpret_cast<float2 *>(dabs));
     return hipGetLastError();
 }
 
@@ -821,17 +868,25 @@ hipError_t launch_loss_reduce(int nparts, const float *partials, int64_t count, 
 hipError_t launch_render_sum_bwd(int W, int H, const float *records, const uint16_t *pixbox,
                                  const uint32_t *offsets, const uint32_t *ranges, const uint32_t *order,
                                  const uint32_t *vals, int64_t capacity, const float *dL_dimage, void *ws,
-                                 const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s) {
+                                 const float *loss_partials, int64_t loss_count, float *d_loss, hipStream_t s,
+                                 bool absgrad) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     // with d_loss, 8 more workgroups: the last one (no tile under either tile map) reduces the loss
     const int nb = padded_tiles(ntiles) + (d_loss ? 8 : 0);
     const double inv_count = loss_count > 0 ? 1.0 / (double)loss_count : 0.0;
-    k_render_sum_bwd<<<nb, 256, 0, s>>>(
-        W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
-        offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, dL_dimage,
-        reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part), loss_partials, ntiles, inv_count,
-        d_loss);
+    float4 *part = reinterpret_cast<float4 *>(static_cast<char *>(ws) + p.off_part);
+    float2 *pa = reinterpret_cast<float2 *>(static_cast<char *>(ws) + p.off_abs);
+    if (absgrad)
+        k_render_sum_bwd<true><<<nb, 256, 0, s>>>(
+            W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
+            offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, dL_dimage, part,
+            loss_partials, ntiles, inv_count, d_loss, pa);
+    else
+        k_render_sum_bwd<false><<<nb, 256, 0, s>>>(
+            W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), reinterpret_cast<const uint2 *>(pixbox),
+            offsets, reinterpret_cast<const uint2 *>(ranges), order, vals, (uint32_t)capacity, dL_dimage, part,
+            loss_partials, ntiles, inv_count, d_loss, nullptr);
     return hipGetLastError();
 }
 

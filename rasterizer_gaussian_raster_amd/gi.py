@@ -81,6 +81,7 @@ def load():
         "gi_params_to_cholesky": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P], i32),
         "gi_loss_ssim_workspace_bytes": ([i32, i32], sz),
         "gi_merge_pairs": ([i64, P, i64, P, P, P], i32),
+        "gi_render_bwd_absgrad": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, sz, P], i32),
         "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, P], i32),
         "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
@@ -254,6 +255,15 @@ def gi_params_to_cholesky_grad(kind, n, params, fx, fy, dout, dparams, accumulat
     _check(load().gi_params_to_cholesky_grad(int(kind), int(n), _ptr(params), float(fx), float(fy), _ptr(dout),
                                              _ptr(dparams), 1 if accumulate else 0, _stream(stream)),
            "gi_params_to_cholesky_grad")
+
+
+def gi_render_bwd_absgrad(d, n, records, pixbox, offsets, ranges, vals, capacity, dL_dimage, dparams, dabs,
+                          workspace, stream=None, tile_order=None):
+    _check(load().gi_render_bwd_absgrad(ctypes.byref(d), int(n), _ptr(records), _ptr(pixbox), _ptr(offsets),
+                                        _ptr(ranges), _ptr(tile_order), _ptr(vals), int(capacity), _ptr(dL_dimage),
+                                        _ptr(dparams), _ptr(dabs), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gi_render_bwd_absgrad")
 
 
 def gi_merge_pairs(n_pairs, pairs, n, params, out, stream=None):

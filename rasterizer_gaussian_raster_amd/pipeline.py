@@ -143,6 +143,16 @@ class Raster:
                          loss_partials=self.loss_partials if d_loss is not None else None,
                          loss_count=3 * self.W * self.H, d_loss=d_loss)
 
+    def backward_absgrad(self, dL_dimage, dparams, dabs, stream=None):
+        """Sum mode: backward with the gather into dparams (+=), and each Gaussian's absgrad into
+        dabs [n,2] (+=)."""
+        if self.bwd_ws is None:
+            nbytes = gi.gi_render_bwd_workspace_bytes(self.desc, self.n, self.capacity)
+            self.bwd_ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device(self.device))
+        gi.gi_render_bwd_absgrad(self.desc, self.n, self.records, self.pixbox, self.offsets, self.ranges, self.vals,
+                                 self.capacity, dL_dimage, dparams, dabs, self.bwd_ws, stream,
+                                 tile_order=self._order())
+
     def forward_backward_l2(self, target, dL_dimage=None, stream=None):
         """Sum mode: forward_l2 then backward(dL, None) in one launch (pair gradients in bwd_ws)."""
         if self.bwd_ws is None:

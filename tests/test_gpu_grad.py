@@ -191,3 +191,48 @@ def test_alpha_backward_is_bitwise_reproducible():
         torch.cuda.synchronize()
         outs.append(np.concatenate([dp.cpu().numpy().ravel(), dl.cpu().numpy(), db.cpu().numpy()]))
     np.testing.assert_array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+def _absgrad(W, H, params, G):
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    n = params.shape[0]
+    r = Raster(W, H, n)
+    r.render(dev(params))
+    dp = torch.zeros((n, 8), dtype=torch.float32, device="cuda")
+    da = torch.zeros((n, 2), dtype=torch.float32, device="cuda")
+    Gd = dev(G.astype(np.float32))
+    r.backward_absgrad(Gd, dp, da)
+    dp2 = torch.zeros((n, 8), dtype=torch.float32, device="cuda")
+    r.backward(Gd, dp2)
+    torch.cuda.synchronize()
+    return dp.cpu().numpy(), da.cpu().numpy(), dp2.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,seed,W,H,n", [("random", 251, 100, 37, 600), ("random", 252, 257, 129, 1500),
+                                             ("kodak_768x512_50k", 0, 768, 512, 50000)])
+def test_absgrad(name, seed, W, H, n):
+    """Sum of |per-pixel dL/dmu| per Gaussian (the oracle's plain-scale sums for the means) within
+    1e-5 of the running-error scale C of the means' gradient: the sum has no cancellation, but a
+    pixel's term h (a u + b v) can (a sparse dL/dI leaves some Gaussians a few such pixels); the
+    gradient equals gi_render_bwd's bit for bit."""
+    require_gpu()
+    import oracle
+    if name == "random":
+        p = synth.random_case(seed, W, H, n, sigma=(0.3, 12.0), margin=20)
+        G = np.random.default_rng(seed).normal(size=(3, H, W)).astype(np.float32)
+    else:
+        w = synth.make_workload(name)
+        p = w["params"]
+        G = np.zeros((3, H, W), np.float32)
+        pix = sample_pixels(W, H, 4096, 8, seed=90)
+        G[:, pix[:, 0], pix[:, 1]] = np.random.default_rng(91).normal(size=(3, len(pix)))
+    dp, da, dp2 = _absgrad(W, H, p, G)
+    np.testing.assert_array_equal(dp.view(np.uint32), dp2.view(np.uint32))
+    _, A, C = oracle.grad_sum(W, H, p.astype(np.float64), G.astype(np.float64), with_cond=True)
+    ref = A[:, :2]
+    scale = np.maximum(C[:, :2], ref)
+    zero = scale == 0
+    assert np.all(da[zero] == 0)
+    err = float((np.abs(da - ref) / np.where(zero, 1.0, scale)).max())
+    print(f"absgrad {W}x{H} n={n}: max rel err {err:.3e}")
+    assert err <= 1e-5

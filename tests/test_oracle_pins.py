@@ -777,3 +777,25 @@ def test_merge_of_identical_gaussians():
     want[4] = abs(g[4])
     want[5:] = 2 * g[5:]
     np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-14)
+
+
+def test_absgrad_is_the_sum_of_per_pixel_absolute_mean_gradients():
+    """The gradient's plain scale for the means (absgrad) = sum over pixels of |d(G_p . I_p)/dmu|,
+    each pixel's derivative by central differences of the render at that pixel."""
+    import oracle
+    W, H = 10, 8
+    p = synth.random_case(811, W, H, 3, sigma=(0.8, 3.0)).astype(np.float64)
+    G = np.random.default_rng(812).normal(size=(3, H, W))
+    _, A = oracle.grad_sum(W, H, p, G, cutoff=False)
+    want = np.zeros((3, 2))
+    h = 1e-6
+    for g in range(3):
+        for t in range(2):
+            a, b = p.copy(), p.copy()
+            a[g, t] += h
+            b[g, t] -= h
+            Ia, _ = oracle.render_sum(W, H, a, cutoff=False)
+            Ib, _ = oracle.render_sum(W, H, b, cutoff=False)
+            per_px = (G * (Ia - Ib)).sum(axis=0) / (2 * h)      # pixel p's term of dL/dmu
+            want[g, t] = np.abs(per_px).sum()
+    np.testing.assert_allclose(A[:, :2], want, rtol=1e-6)
