@@ -651,7 +651,7 @@ def main():
                 "traffic": traffic, "avg_launch_us": round(secs * 1e6, 2)}
 
     roof_fwd = roof("fwd", "k_raster_sum.hip", "k_render_sum_fwd<true>", fwd_tf, fwd_s)
-    roof_bwd = roof("bwd", "k_raster_sum.hip", "k_render_sum_bwd", bwd_tf, bwd_s)
+    roof_bwd = roof("bwd", "k_raster_sum.hip", "k_render_sum_bwd<false>", bwd_tf, bwd_s)
     roof_fused = roof("fused", "k_raster_sum.hip", "k_render_sum_fused", fused_tf, fused_s)
 
     out = {
