@@ -568,6 +568,42 @@ gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *rec
                                 const uint32_t *vals, int64_t capacity, const float *dL_dimage, float *dparams,
                                 float *dabs, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * gi_render_fwd_alpha_l2 -- gi_render_fwd in the alpha mode that also writes
+ *   the L2 loss gradient dL/dI = 2 (I - T) / (3HW) (what gi_loss_l2 writes,
+ *   bit for bit) and each tile's sum of squared residuals to loss_partials
+ *   ("Drawing with Gaussians", Overview: fused kernels for the alpha
+ *   compositing fit; "FlashImgs", --loss l2).
+ *   target, dL_dimage  device float [3][H][W] (dL_dimage written; no aliasing).
+ *   loss_partials      device float [gi_num_tiles] (written).
+ *   Other arguments as gi_render_fwd (alpha mode).
+ */
+gi_status gi_render_fwd_alpha_l2(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
+                                 const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *tile_order,
+                                 const uint32_t *vals, const float *background, const float *target, float *image,
+                                 float *t_final, uint32_t *last, float *dL_dimage, float *loss_partials,
+                                 void *stream);
+
+/*
+ * gi_adam_step_pairs_alpha -- the alpha mode's update in one pass: the
+ *   per-pair slots that gi_render_bwd (alpha, dparams = NULL) left in its
+ *   workspace are added per Gaussian in emission order (as its gather does)
+ *   and the Adam step (as gi_adam_step) applied to the 8 params and the logit
+ *   of every Gaussian, and to the background's 3 channels from the tiles'
+ *   background partials; d_loss (optional) also gets the loss of
+ *   gi_render_fwd_alpha_l2's partials (as gi_loss_reduce).
+ *   p, m, v              device float [n][8];  lr host float [8].
+ *   logit, m_logit, v_logit  device float [n];  lr_logit.
+ *   background, m_bg, v_bg   device float [3] (at least);  lr_bg.
+ *   Other arguments as gi_adam_step_pairs.  A binning overflow gives zero gradients.
+ */
+gi_status gi_adam_step_pairs_alpha(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
+                                   const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
+                                   const float *lr, float *logit, float *m_logit, float *v_logit, float lr_logit,
+                                   float *background, float *m_bg, float *v_bg, float lr_bg, double beta1,
+                                   double beta2, double eps, int32_t step, const float *loss_partials,
+                                   int64_t loss_count, float *d_loss, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

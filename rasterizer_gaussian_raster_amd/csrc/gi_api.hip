@@ -241,11 +241,10 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
                                        nullptr, s);
         return hip_status(e);
     }
-    if (n > 0 && !dparams) return GI_ERR_INVALID_ARG;
     if (!background || !t_final || !last || (n > 0 && (!opacity || !logit))) return GI_ERR_INVALID_ARG;
     e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, tile_order, vals, capacity,
                                     background, t_final, last, dL_dimage, workspace, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && dparams)               // dparams = NULL: the slots stay for gi_adam_step_pairs_alpha
         e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 1, dparams, dlogit,
                                    dbackground, s);
     return hip_status(e);
@@ -451,6 +450,43 @@ gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *rec
         e = gi::launch_grad_gather((int)n, W, H, (int)gi_num_tiles(desc), offsets, capacity, workspace, 0, dparams,
                                    nullptr, nullptr, s, dabs);
     return hip_status(e);
+}
+
+gi_status gi_render_fwd_alpha_l2(const gi_desc *desc, int64_t n, const float *records, const float *opacity,
+                                 const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *tile_order,
+                                 const uint32_t *vals, const float *background, const float *target, float *image,
+                                 float *t_final, uint32_t *last, float *dL_dimage, float *loss_partials,
+                                 void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_ALPHA || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!ranges || !vals || !background || !target || !image || !t_final || !last || !dL_dimage || !loss_partials)
+        return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!records || !opacity || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
+    if (dL_dimage == target || dL_dimage == image) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_render_alpha_fwd(desc->width, desc->height, records, opacity, pixbox, ranges,
+                                                  tile_order, vals, background, image, t_final, last,
+                                                  as_stream(stream), target, dL_dimage, loss_partials));
+}
+
+gi_status gi_adam_step_pairs_alpha(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,
+                                   const void *workspace, size_t workspace_bytes, float *p, float *m, float *v,
+                                   const float *lr, float *logit, float *m_logit, float *v_logit, float lr_logit,
+                                   float *background, float *m_bg, float *v_bg, float lr_bg, double beta1,
+                                   double beta2, double eps, int32_t step, const float *loss_partials,
+                                   int64_t loss_count, float *d_loss, void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_ALPHA || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+        capacity >= (1ll << 31) || step < 1 || !lr)
+        return GI_ERR_INVALID_ARG;
+    if (d_loss && (!loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0)) return GI_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !aligned256(workspace) || !background || !m_bg || !v_bg) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!p || !m || !v || !logit || !m_logit || !v_logit || !aligned16(p) || !aligned16(m) ||
+                  !aligned16(v)))
+        return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_adam_pairs_alpha((int)n, desc->width, desc->height, offsets, capacity, workspace, p,
+                                                  m, v, lr, logit, m_logit, v_logit, lr_logit, background, m_bg,
+                                                  v_bg, lr_bg, beta1, beta2, eps, step, loss_partials, loss_count,
+                                                  d_loss, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -138,7 +138,13 @@ hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *o
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
                                    const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *order,
                                    const uint32_t *vals, const float *background, float *image, float *t_final,
-                                   uint32_t *last, hipStream_t s);
+                                   uint32_t *last, hipStream_t s, const float *target = nullptr,
+                                   float *dL = nullptr, float *loss_part = nullptr);
+hipError_t launch_adam_pairs_alpha(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws,
+                                   float *p, float *m, float *v, const float *lr, float *logit, float *ml, float *vl,
+                                   float lr_logit, float *bg, float *mbg, float *vbg, float lr_bg, double beta1,
+                                   double beta2, double eps, int step, const float *loss_partials, int64_t loss_count,
+                                   float *d_loss, hipStream_t s);
 hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
                                    const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
                                    const uint32_t *order, const uint32_t *vals, int64_t capacity,

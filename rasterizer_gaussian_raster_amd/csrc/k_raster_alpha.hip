@@ -130,6 +130,9 @@ __device__ __forceinline__ void bfly_dpp(float (&x)[2 * N], float (&y)[N], bool 
     }
 }
 
+// L2: also dL/dI = gscale (I - T) (what gi_loss_l2 writes, bit for bit) and the tile's sum of
+// squared residuals in loss_part[t] (lanes, then the two waves, in a fixed order).
+template <bool L2>
 __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_fwd(int W, int H, int tiles_x, int ntiles,
                                                           const float4 *__restrict__ records,
                                                           const float *__restrict__ opacity,
@@ -138,10 +141,13 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_fwd(int W, int H
                                                           const uint32_t *__restrict__ vals,
                                                           const float *__restrict__ bg,
                                                           float *__restrict__ image, float *__restrict__ t_final,
-                                                          uint32_t *__restrict__ last) {
+                                                          uint32_t *__restrict__ last, const float *__restrict__ target,
+                                                          float *__restrict__ dL, float gscale,
+                                                          float *__restrict__ loss_part) {
     __shared__ AlphaRec lst[2][kBatch];
     __shared__ int wq[2][2];
     __shared__ int wdone[2];
+    __shared__ float wsq[2];
     const int t = tile_of(blockIdx.x, gridDim.x, ntiles, order);
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -194,21 +200,34 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_fwd(int W, int H
         if (wdone[0] && wdone[1]) break;                   // uniform
     }
     const size_t plane = (size_t)W * H;
-    if (pxi < W && pyi < H) {
-        const size_t o = (size_t)pyi * W + pxi;
-        image[o] = fmaf(T0, bg[0], r0);
-        image[o + plane] = fmaf(T0, bg[1], g0);
-        image[o + 2 * plane] = fmaf(T0, bg[2], b0);
-        t_final[o] = T0;
-        last[o] = end0;
+    float sq = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int yi = pyi + 8 * h;
+        if (pxi < W && yi < H) {
+            const size_t o = (size_t)yi * W + pxi;
+            const float T = h ? T1 : T0;
+            const float ir = fmaf(T, bg[0], h ? r1 : r0), ig = fmaf(T, bg[1], h ? g1 : g0);
+            const float ib = fmaf(T, bg[2], h ? b1 : b0);
+            image[o] = ir;
+            image[o + plane] = ig;
+            image[o + 2 * plane] = ib;
+            t_final[o] = T;
+            last[o] = h ? end1 : end0;
+            if (L2) {
+                const float rr = ir - target[o], rg = ig - target[o + plane], rb = ib - target[o + 2 * plane];
+                dL[o] = gscale * rr;
+                dL[o + plane] = gscale * rg;
+                dL[o + 2 * plane] = gscale * rb;
+                sq += fmaf(rb, rb, fmaf(rg, rg, rr * rr));
+            }
+        }
     }
-    if (pxi < W && pyi + 8 < H) {
-        const size_t o = (size_t)(pyi + 8) * W + pxi;
-        image[o] = fmaf(T1, bg[0], r1);
-        image[o + plane] = fmaf(T1, bg[1], g1);
-        image[o + 2 * plane] = fmaf(T1, bg[2], b1);
-        t_final[o] = T1;
-        last[o] = end1;
+    if (L2) {
+        const float s = wave_total(sq);
+        if (lane == 0) wsq[wave] = s;
+        __syncthreads();
+        if (tid == 0) loss_part[t] = wsq[0] + wsq[1];
     }
 }
 
@@ -426,15 +445,122 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
 
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
 
+// The alpha training step's update in one pass: each Gaussian's per-pair slots (8 values and the
+// logit's) added in emission order (as k_grad_gather), and the Adam step of its 8 params and its
+// logit; the second-to-last workgroup adds up the tiles' background partials (as k_grad_gather)
+// and steps the background's 3 channels; the last one reduces the loss partials.
+__global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, const uint32_t *__restrict__ offsets,
+                                                          uint32_t capacity, const float4 *__restrict__ part,
+                                                          const float *__restrict__ part_l,
+                                                          const float4 *__restrict__ part_bg, float4 *__restrict__ p,
+                                                          float4 *__restrict__ m, float4 *__restrict__ v, AdamHP a,
+                                                          float *__restrict__ logit, float *__restrict__ ml,
+                                                          float *__restrict__ vl, float lr_logit,
+                                                          float *__restrict__ bg, float *__restrict__ mbg,
+                                                          float *__restrict__ vbg, float lr_bg,
+                                                          const float *__restrict__ loss_part, double inv_count,
+                                                          float *__restrict__ loss) {
+    const int nb = (n + 255) / 256;
+    float c1, c2;
+    adam_step_bias(a, c1, c2);
+    const bool ok = offsets[n] <= capacity;               // else the binning overflowed: zero gradients
+    if ((int)blockIdx.x == nb) {                          // the background
+        __shared__ float4 sm[256];
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ok)
+            for (int t = threadIdx.x; t < ntiles; t += 256) {
+                const float4 u = part_bg[t];
+                s.x += u.x; s.y += u.y; s.z += u.z;
+            }
+        sm[threadIdx.x] = s;
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if (threadIdx.x < o) {
+                sm[threadIdx.x].x += sm[threadIdx.x + o].x;
+                sm[threadIdx.x].y += sm[threadIdx.x + o].y;
+                sm[threadIdx.x].z += sm[threadIdx.x + o].z;
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x < 3) {
+            const float G = threadIdx.x == 0 ? sm[0].x : threadIdx.x == 1 ? sm[0].y : sm[0].z;
+            float P = bg[threadIdx.x], Mo = mbg[threadIdx.x], V = vbg[threadIdx.x];
+            adam_update(P, G, Mo, V, lr_bg, a, c1, c2);
+            bg[threadIdx.x] = P;
+            mbg[threadIdx.x] = Mo;
+            vbg[threadIdx.x] = V;
+        }
+        return;
+    }
+    if ((int)blockIdx.x == nb + 1) {                      // the loss
+        if (loss) {
+            __shared__ double sd[256];
+            loss_reduce_block(ntiles, loss_part, inv_count, loss, sd);
+        }
+        return;
+    }
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= n) return;
+    const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
+    float4 d0 = make_float4(0.f, 0.f, 0.f, 0.f), d1 = d0;
+    gather_slots(part, o0, o1, d0, d1);
+    float dl = 0.f;
+    for (uint32_t q = o0; q < o1; ++q) dl += part_l[q];
+    const float4 a0 = p[2 * g], a1 = p[2 * g + 1], m0 = m[2 * g], m1 = m[2 * g + 1], v0 = v[2 * g], v1 = v[2 * g + 1];
+    float P[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float G[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adam_update(P[k], G[k], M[k], V[k], a.lr[k], a, c1, c2);
+    p[2 * g] = make_float4(P[0], P[1], P[2], P[3]);
+    p[2 * g + 1] = make_float4(P[4], P[5], P[6], P[7]);
+    m[2 * g] = make_float4(M[0], M[1], M[2], M[3]);
+    m[2 * g + 1] = make_float4(M[4], M[5], M[6], M[7]);
+    v[2 * g] = make_float4(V[0], V[1], V[2], V[3]);
+    v[2 * g + 1] = make_float4(V[4], V[5], V[6], V[7]);
+    float L = logit[g], Ml = ml[g], Vl = vl[g];
+    adam_update(L, dl, Ml, Vl, lr_logit, a, c1, c2);
+    logit[g] = L;
+    ml[g] = Ml;
+    vl[g] = Vl;
+}
+
+hipError_t launch_adam_pairs_alpha(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws,
+                                   float *p, float *m, float *v, const float *lr, float *logit, float *ml, float *vl,
+                                   float lr_logit, float *bg, float *mbg, float *vbg, float lr_bg, double beta1,
+                                   double beta2, double eps, int step, const float *loss_partials, int64_t loss_count,
+                                   float *d_loss, hipStream_t s) {
+    const int ntiles = ((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+    const BwdPlan pl = make_bwd_plan(W, H, capacity);
+    const AdamHP a = make_adam_hp(lr, beta1, beta2, eps, step, nullptr);
+    const char *w = static_cast<const char *>(ws);
+    k_adam_pairs_alpha<<<(n + 255) / 256 + 2, 256, 0, s>>>(
+        n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(w + pl.off_part),
+        reinterpret_cast<const float *>(w + pl.off_logit), reinterpret_cast<const float4 *>(w + pl.off_bg),
+        reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a, logit, ml, vl,
+        lr_logit, bg, mbg, vbg, lr_bg, loss_partials, loss_count > 0 ? 1.0 / (double)loss_count : 0.0, d_loss);
+    return hipGetLastError();
+}
+
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
                                    const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *order,
                                    const uint32_t *vals, const float *background, float *image, float *t_final,
-                                   uint32_t *last, hipStream_t s) {
+                                   uint32_t *last, hipStream_t s, const float *target, float *dL,
+                                   float *loss_part) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
-    k_render_alpha_fwd<<<padded_tiles(ntiles), kAlphaThreads, 0, s>>>(
-        W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity,
-        reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), order, vals, background,
-        image, t_final, last);
+    if (target) {
+        const float gscale = (float)(2.0 / (3.0 * (double)W * (double)H));
+        k_render_alpha_fwd<true><<<padded_tiles(ntiles), kAlphaThreads, 0, s>>>(
+            W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity,
+            reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), order, vals, background,
+            image, t_final, last, target, dL, gscale, loss_part);
+    } else {
+        k_render_alpha_fwd<false><<<padded_tiles(ntiles), kAlphaThreads, 0, s>>>(
+            W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity,
+            reinterpret_cast<const uint2 *>(pixbox), reinterpret_cast<const uint2 *>(ranges), order, vals, background,
+            image, t_final, last, nullptr, nullptr, 0.0f, nullptr);
+    }
     return hipGetLastError();
 }
 

@@ -81,6 +81,9 @@ def load():
         "gi_params_to_cholesky": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P], i32),
         "gi_loss_ssim_workspace_bytes": ([i32, i32], sz),
         "gi_merge_pairs": ([i64, P, i64, P, P, P], i32),
+        "gi_render_fwd_alpha_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P], i32),
+        "gi_adam_step_pairs_alpha": ([D, i64, P, i64, P, sz, P, P, P, P, P, P, P, ctypes.c_float, P, P, P,
+                                      ctypes.c_float, f64, f64, f64, i32, P, i64, P, P], i32),
         "gi_render_bwd_absgrad": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, sz, P], i32),
         "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, P], i32),
         "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
@@ -264,6 +267,27 @@ def gi_render_bwd_absgrad(d, n, records, pixbox, offsets, ranges, vals, capacity
                                         _ptr(dparams), _ptr(dabs), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)),
            "gi_render_bwd_absgrad")
+
+
+def gi_render_fwd_alpha_l2(d, n, records, opacity, pixbox, ranges, vals, background, target, image, t_final, last,
+                           dL_dimage, loss_partials, stream=None, tile_order=None):
+    _check(load().gi_render_fwd_alpha_l2(ctypes.byref(d), int(n), _ptr(records), _ptr(opacity), _ptr(pixbox),
+                                         _ptr(ranges), _ptr(tile_order), _ptr(vals), _ptr(background), _ptr(target),
+                                         _ptr(image), _ptr(t_final), _ptr(last), _ptr(dL_dimage),
+                                         _ptr(loss_partials), _stream(stream)), "gi_render_fwd_alpha_l2")
+
+
+def gi_adam_step_pairs_alpha(d, n, offsets, capacity, workspace, p, m, v, lr, logit, m_logit, v_logit, lr_logit,
+                             bg, m_bg, v_bg, lr_bg, beta1, beta2, eps, step, loss_partials=None, loss_count=0,
+                             d_loss=None, stream=None):
+    lr_arr = (ctypes.c_float * 8)(*[float(x) for x in lr])
+    _check(load().gi_adam_step_pairs_alpha(ctypes.byref(d), int(n), _ptr(offsets), int(capacity), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _ptr(p), _ptr(m), _ptr(v),
+                                           lr_arr, _ptr(logit), _ptr(m_logit), _ptr(v_logit), float(lr_logit),
+                                           _ptr(bg), _ptr(m_bg), _ptr(v_bg), float(lr_bg), float(beta1),
+                                           float(beta2), float(eps), int(step), _ptr(loss_partials),
+                                           int(loss_count), _ptr(d_loss), _stream(stream)),
+           "gi_adam_step_pairs_alpha")
 
 
 def gi_merge_pairs(n_pairs, pairs, n, params, out, stream=None):

@@ -384,6 +384,27 @@ class Fitter:
             self._sum_step(self.step_count % ORDER_EVERY == 0)
             self.step_count += 1
             return
+        if self.loss_w is None:             # alpha mode, L2: forward with the loss gradient, one update pass
+            bg = self.bg4
+            r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.params, logit=self.logit)
+            gi.gi_render_fwd_alpha_l2(r.desc, self.n, r.records, r.opacity, r.pixbox, r.ranges, r.vals, bg,
+                                      self.target, r.image, r.t_final, r.last, self.dL, r.loss_partials,
+                                      tile_order=r._order())
+            r.backward(self.dL, None, logit=self.logit, background=bg)
+            self.step_count += 1
+            b1, b2 = self.betas
+            gi.gi_adam_step_pairs_alpha(r.desc, self.n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m,
+                                        self.v, self.lr, self.logit, self.m_logit, self.v_logit, self.lr_logit,
+                                        self.bg4, self.m_bg, self.v_bg, self.lr_bg, b1, b2, self.eps,
+                                        self.step_count, loss_partials=r.loss_partials,
+                                        loss_count=self.target.numel(), d_loss=self.loss)
+            return
+        self.step_separate()
+
+    def step_separate(self):
+        """The step from separate calls: forward, the loss (L2 or SSIM), backward with the gather, and
+        Adam (in the alpha mode with L2 a cross-check of the fused step)."""
+        r = self.raster
         bg = self.bg4 if self.logit is not None else None
         r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.params, logit=self.logit)
         r.forward(bg)

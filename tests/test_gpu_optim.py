@@ -149,3 +149,28 @@ def test_adam_pairs_equals_gather_then_adam():
     torch.cuda.synchronize()
     for a, b in [(P1, P2), (M1, M2), (V1, V2)]:
         np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_alpha_fused_step_matches_separate_calls():
+    """Alpha fit: forward with the L2 gradient + one update pass (gi_render_fwd_alpha_l2,
+    gi_adam_step_pairs_alpha) against the separate calls (forward, gi_loss_l2, backward with the
+    gather, three gi_adam_step calls)."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter
+    p, lg, bg = synth.random_case(311, 96, 80, 600, sigma=(0.5, 8.0), alpha=True)
+    tgt = np.random.default_rng(312).uniform(0, 1, (3, 80, 96)).astype(np.float32)
+    a = Fitter(dev(tgt), dev(p), logit=dev(lg), background=dev(bg))
+    b = Fitter(dev(tgt), dev(p), logit=dev(lg), background=dev(bg))
+    a.step()
+    b.step_separate()
+    torch.cuda.synchronize()     # same params so far: the L2 gradient is the same, bit for bit
+    np.testing.assert_array_equal(a.dL.cpu().numpy().view(np.uint32), b.dL.cpu().numpy().view(np.uint32))
+    for _ in range(2):
+        a.step()
+        b.step_separate()
+    torch.cuda.synchronize()
+    for x, y in [(a.params, b.params), (a.logit, b.logit), (a.bg4, b.bg4)]:
+        np.testing.assert_allclose(x.cpu().numpy(), y.cpu().numpy(), rtol=1e-5, atol=1e-6)
+    la, lb = a.loss.item(), b.loss.item()
+    print(f"alpha fused vs separate: loss {la:.7e} / {lb:.7e}")
+    assert abs(la - lb) <= 1e-5 * abs(lb)
