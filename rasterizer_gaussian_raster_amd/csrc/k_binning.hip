@@ -891,7 +891,8 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
 // from the registers.  The digit totals of the bucket are its tiles' ranges.
 constexpr int kBWT = 1024, kBWW = kBWT / 64, kBWPL = 8;
 struct BucketWLds {
-    uint32_t cnt[kBWW][256];      // per wave and digit: the chunk's keys of the digit in the wave
+    uint32_t cnt[kBWW][256];      // per wave and digit: the chunk's keys of the digit in the wave, then
+                                  // in earlier waves (exclusive prefix over the waves)
     uint32_t gbase[256];          // next output slot of each digit
     uint32_t hist[256];           // the bucket's keys per digit (buckets of several chunks)
     uint32_t dsum[4];             // per wave of digits: their total
@@ -990,21 +991,26 @@ __global__ __launch_bounds__(kBWT) void k_bucket_sortw(const uint32_t *__restric
             }
         }
         bucketw_rank(L, cc, span, iters, lo_bits, key, rk);
-        if (one) {                                        // the chunk is the bucket: its counts give the bases
-            uint32_t tot = 0;
-            if (tid < radix)
+        // per digit, the chunk's keys in earlier waves: an exclusive prefix over the waves, in place
+        uint32_t tot = 0;
+        if (tid < radix)
 #pragma unroll
-                for (int w = 0; w < kBWW; ++w) tot += L.cnt[w][tid];
-            bucketw_bases(L, tot, s0, lo_bits, ntiles, ranges);
-        }
+            for (int w = 0; w < kBWW; ++w) {
+                const uint32_t c = L.cnt[w][tid];
+                L.cnt[w][tid] = tot;
+                tot += c;
+            }
+        if (one)                                          // the chunk is the bucket: its counts give the bases
+            bucketw_bases(L, tot, s0, lo_bits, ntiles, ranges);   // (its barriers publish the prefix)
+        else
+            __syncthreads();
 #pragma unroll
         for (int it = 0; it < kBWPL; ++it) {
             if (it >= iters) continue;                    // uniform
             const int idx = wave * span + it * 64 + lane;
             if (idx < cc) {
                 const uint32_t d = key[it] & dmask;
-                uint32_t pos = L.gbase[d] + rk[it];
-                for (int w = 0; w < wave; ++w) pos += L.cnt[w][d];
+                const uint32_t pos = L.gbase[d] + L.cnt[wave][d] + rk[it];
                 if (pos < s1) {                           // holds by construction; keeps a bad table in bounds
                     kout[pos] = key[it];
                     vout[pos] = val[it];
@@ -1013,12 +1019,7 @@ __global__ __launch_bounds__(kBWT) void k_bucket_sortw(const uint32_t *__restric
         }
         if (base + CH >= s1) break;                       // uniform: the last chunk
         __syncthreads();                                  // every wave has its positions
-        if (tid < radix) {
-            uint32_t t = 0;
-#pragma unroll
-            for (int w = 0; w < kBWW; ++w) t += L.cnt[w][tid];
-            L.gbase[tid] += t;
-        }
+        if (tid < radix) L.gbase[tid] += tot;
         __syncthreads();
     }
 }
