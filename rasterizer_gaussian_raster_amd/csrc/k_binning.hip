@@ -896,6 +896,8 @@ struct BucketWLds {
     uint32_t gbase[256];          // next output slot of each digit
     uint32_t hist[256];           // the bucket's keys per digit (buckets of several chunks)
     uint32_t dsum[4];             // per wave of digits: their total
+    uint32_t ldo[256];            // buckets of several chunks: each digit's first slot in the chunk's reorder
+    uint32_t sk[kBWT * kBWPL], sv[kBWT * kBWPL];   // ... and the reordered chunk (digit-major, stable)
 };
 
 // Ranks of a chunk's keys (wave-local counts into L.cnt); ends with the barrier that publishes them.
@@ -1000,20 +1002,52 @@ __global__ __launch_bounds__(kBWT) void k_bucket_sortw(const uint32_t *__restric
                 L.cnt[w][tid] = tot;
                 tot += c;
             }
-        if (one)                                          // the chunk is the bucket: its counts give the bases
+        if (one) {                                        // the chunk is the bucket: its counts give the bases
             bucketw_bases(L, tot, s0, lo_bits, ntiles, ranges);   // (its barriers publish the prefix)
-        else
+#pragma unroll
+            for (int it = 0; it < kBWPL; ++it) {
+                if (it >= iters) continue;                // uniform
+                const int idx = wave * span + it * 64 + lane;
+                if (idx < cc) {
+                    const uint32_t d = key[it] & dmask;
+                    const uint32_t pos = L.gbase[d] + L.cnt[wave][d] + rk[it];
+                    if (pos < s1) {                       // holds by construction; keeps a bad table in bounds
+                        kout[pos] = key[it];
+                        vout[pos] = val[it];
+                    }
+                }
+            }
+        } else {
+            // a chunk of a big bucket is reordered in LDS (digit-major, stable) and written out as
+            // runs: consecutive threads store consecutive slots
+            const uint32_t inc = wave_scan_incl(tot);     // digits (< 256) sit in waves 0..3
+            if (wave < 4 && lane == 63) L.dsum[wave] = inc;
+            __syncthreads();
+            if (tid < radix) {
+                uint32_t ex = inc - tot;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) ex += w < wave ? L.dsum[w] : 0u;
+                L.ldo[tid] = ex;
+            }
             __syncthreads();
 #pragma unroll
-        for (int it = 0; it < kBWPL; ++it) {
-            if (it >= iters) continue;                    // uniform
-            const int idx = wave * span + it * 64 + lane;
-            if (idx < cc) {
-                const uint32_t d = key[it] & dmask;
-                const uint32_t pos = L.gbase[d] + L.cnt[wave][d] + rk[it];
-                if (pos < s1) {                           // holds by construction; keeps a bad table in bounds
-                    kout[pos] = key[it];
-                    vout[pos] = val[it];
+            for (int it = 0; it < kBWPL; ++it) {
+                if (it >= iters) continue;                // uniform
+                const int idx = wave * span + it * 64 + lane;
+                if (idx < cc) {
+                    const uint32_t d = key[it] & dmask;
+                    const uint32_t loc = L.ldo[d] + L.cnt[wave][d] + rk[it];   // < cc by construction
+                    L.sk[loc] = key[it];
+                    L.sv[loc] = val[it];
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < cc; i += kBWT) {
+                const uint32_t k = L.sk[i], d = k & dmask;
+                const uint32_t pos = L.gbase[d] + ((uint32_t)i - L.ldo[d]);
+                if (pos < s1) {
+                    kout[pos] = k;
+                    vout[pos] = L.sv[i];
                 }
             }
         }
