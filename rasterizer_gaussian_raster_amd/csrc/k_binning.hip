@@ -1004,18 +1004,22 @@ __global__ __launch_bounds__(kBWT) void k_bucket_sortw(const uint32_t *__restric
             }
         if (one) {                                        // the chunk is the bucket: its counts give the bases
             bucketw_bases(L, tot, s0, lo_bits, ntiles, ranges);   // (its barriers publish the prefix)
+            // reordered in LDS (digit-major, stable), then the bucket goes out as one run
 #pragma unroll
             for (int it = 0; it < kBWPL; ++it) {
                 if (it >= iters) continue;                // uniform
                 const int idx = wave * span + it * 64 + lane;
                 if (idx < cc) {
                     const uint32_t d = key[it] & dmask;
-                    const uint32_t pos = L.gbase[d] + L.cnt[wave][d] + rk[it];
-                    if (pos < s1) {                       // holds by construction; keeps a bad table in bounds
-                        kout[pos] = key[it];
-                        vout[pos] = val[it];
-                    }
+                    const uint32_t loc = L.gbase[d] - s0 + L.cnt[wave][d] + rk[it];   // < cc by construction
+                    L.sk[loc] = key[it];
+                    L.sv[loc] = val[it];
                 }
+            }
+            __syncthreads();
+            for (int i = tid; i < cc; i += kBWT) {
+                kout[s0 + (uint32_t)i] = L.sk[i];
+                vout[s0 + (uint32_t)i] = L.sv[i];
             }
         } else {
             // a chunk of a big bucket is reordered in LDS (digit-major, stable) and written out as
