@@ -237,7 +237,7 @@ def bench_alpha(args, w, target, params, dev):
                 "frac": round(tf / PEAK_FP32, 4), "traffic": load_traffic("k_raster_alpha.hip", kname),
                 "avg_launch_us": round(secs * 1e6, 2)}
 
-    roof_fwd = roof("k_render_alpha_fwd", FLOP_FWD_ALPHA, fwd_s)
+    roof_fwd = roof("k_render_alpha_fwd<false>", FLOP_FWD_ALPHA, fwd_s)
     roof_bwd = roof("k_render_alpha_bwd", FLOP_BWD_ALPHA, bwd_s)
     dominant, other = (roof_bwd, roof_fwd) if bwd_s >= fwd_s else (roof_fwd, roof_bwd)
     out = {
