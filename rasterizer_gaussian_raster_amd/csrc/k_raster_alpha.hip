@@ -446,9 +446,10 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
 static int padded_tiles(int ntiles) { return (ntiles + 7) & ~7; }
 
 // The alpha training step's update in one pass: each Gaussian's per-pair slots (8 values and the
-// logit's) added in emission order (as k_grad_gather), and the Adam step of its 8 params and its
-// logit; the second-to-last workgroup adds up the tiles' background partials (as k_grad_gather)
-// and steps the background's 3 channels; the last one reduces the loss partials.
+// logit's) added in emission order (as k_grad_gather; two lanes per Gaussian, four values each),
+// and the Adam step of its 8 params and its logit; the second-to-last workgroup adds up the tiles'
+// background partials (as k_grad_gather) and steps the background's 3 channels; the last one
+// reduces the loss partials.
 __global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, const uint32_t *__restrict__ offsets,
                                                           uint32_t capacity, const float4 *__restrict__ part,
                                                           const float *__restrict__ part_l,
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, con
                                                           float *__restrict__ vbg, float lr_bg,
                                                           const float *__restrict__ loss_part, double inv_count,
                                                           float *__restrict__ loss) {
-    const int nb = (n + 255) / 256;
+    const int nb = (2 * n + 255) / 256;
     float c1, c2;
     adam_step_bias(a, c1, c2);
     const bool ok = offsets[n] <= capacity;               // else the binning overflowed: zero gradients
@@ -499,31 +500,31 @@ __global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, con
         }
         return;
     }
-    const int g = blockIdx.x * 256 + threadIdx.x;
+    const int i = blockIdx.x * 256 + threadIdx.x;          // lane h = i & 1 of Gaussian i >> 1: params 4h .. 4h + 3
+    const int g = i >> 1, h = i & 1;
     if (g >= n) return;
     const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
-    float4 d0 = make_float4(0.f, 0.f, 0.f, 0.f), d1 = d0;
-    gather_slots(part, o0, o1, d0, d1);
-    float dl = 0.f;
-    for (uint32_t q = o0; q < o1; ++q) dl += part_l[q];
-    const float4 a0 = p[2 * g], a1 = p[2 * g + 1], m0 = m[2 * g], m1 = m[2 * g + 1], v0 = v[2 * g], v1 = v[2 * g + 1];
-    float P[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float G[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-    float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
+    gather_half(reinterpret_cast<const float4 *>(part), o0, o1, h, gr);
+    const float4 a4 = p[2 * g + h], m4 = m[2 * g + h], v4 = v[2 * g + h];
+    float P[4] = {a4.x, a4.y, a4.z, a4.w};
+    const float G[4] = {gr.x, gr.y, gr.z, gr.w};
+    float M[4] = {m4.x, m4.y, m4.z, m4.w};
+    float V[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) adam_update(P[k], G[k], M[k], V[k], a.lr[k], a, c1, c2);
-    p[2 * g] = make_float4(P[0], P[1], P[2], P[3]);
-    p[2 * g + 1] = make_float4(P[4], P[5], P[6], P[7]);
-    m[2 * g] = make_float4(M[0], M[1], M[2], M[3]);
-    m[2 * g + 1] = make_float4(M[4], M[5], M[6], M[7]);
-    v[2 * g] = make_float4(V[0], V[1], V[2], V[3]);
-    v[2 * g + 1] = make_float4(V[4], V[5], V[6], V[7]);
-    float L = logit[g], Ml = ml[g], Vl = vl[g];
-    adam_update(L, dl, Ml, Vl, lr_logit, a, c1, c2);
-    logit[g] = L;
-    ml[g] = Ml;
-    vl[g] = Vl;
+    for (int k = 0; k < 4; ++k) adam_update(P[k], G[k], M[k], V[k], a.lr[4 * h + k], a, c1, c2);
+    p[2 * g + h] = make_float4(P[0], P[1], P[2], P[3]);
+    m[2 * g + h] = make_float4(M[0], M[1], M[2], M[3]);
+    v[2 * g + h] = make_float4(V[0], V[1], V[2], V[3]);
+    if (h == 1) {
+        float dl = 0.f;
+        for (uint32_t q = o0; q < o1; ++q) dl += part_l[q];
+        float L = logit[g], Ml = ml[g], Vl = vl[g];
+        adam_update(L, dl, Ml, Vl, lr_logit, a, c1, c2);
+        logit[g] = L;
+        ml[g] = Ml;
+        vl[g] = Vl;
+    }
 }
 
 hipError_t launch_adam_pairs_alpha(int n, int W, int H, const uint32_t *offsets, int64_t capacity, const void *ws,
@@ -535,7 +536,7 @@ hipError_t launch_adam_pairs_alpha(int n, int W, int H, const uint32_t *offsets,
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
     const AdamHP a = make_adam_hp(lr, beta1, beta2, eps, step, nullptr);
     const char *w = static_cast<const char *>(ws);
-    k_adam_pairs_alpha<<<(n + 255) / 256 + 2, 256, 0, s>>>(
+    k_adam_pairs_alpha<<<(2 * n + 255) / 256 + 2, 256, 0, s>>>(
         n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(w + pl.off_part),
         reinterpret_cast<const float *>(w + pl.off_logit), reinterpret_cast<const float4 *>(w + pl.off_bg),
         reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a, logit, ml, vl,
