@@ -85,16 +85,28 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(int W, int H, const float *__r
         }
     }
     __syncthreads();
-    const int tx = tid & 15, ty = tid >> 4;
-    float m[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int a = 0; a < 11; ++a) {
-        const float g = win.g[a];
-#pragma unroll
-        for (int k = 0; k < 5; ++k) m[k] = fmaf(g, hs[k][ty + a][tx], m[k]);
-    }
-    const int i = y0 + ty, j = x0 + tx;
+    // columns: two vertically adjacent outputs per thread (threads < 128), the 12 rows they need
+    // read once from LDS
     float f = 0.f, l1 = 0.f, l2 = 0.f;
+    if (tid < kSsimT * kSsimT / 2) {
+    const int tx = tid & 15, ty0 = (tid >> 4) * 2;
+    float mm[2][5] = {{0.f, 0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        float hv[12];
+#pragma unroll
+        for (int a = 0; a < 12; ++a) hv[a] = hs[k][ty0 + a][tx];
+#pragma unroll
+        for (int a = 0; a < 11; ++a) {
+            mm[0][k] = fmaf(win.g[a], hv[a], mm[0][k]);
+            mm[1][k] = fmaf(win.g[a], hv[a + 1], mm[1][k]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+    const float *m = mm[r];
+    const int ty = ty0 + r;
+    const int i = y0 + ty, j = x0 + tx;
     if (i < H && j < W) {
         const float mx = m[0], my = m[1];
         const float sxx = m[2] - mx * mx, syy = m[3] - my * my, sxy = m[4] - mx * my;
@@ -103,15 +115,18 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(int W, int H, const float *__r
         // hardware reciprocals (1 ulp): the divisions' rounding is far below the loss's tolerance
         const float rn1 = __builtin_amdgcn_rcpf(n1), rn2 = __builtin_amdgcn_rcpf(n2);
         const float rd1 = __builtin_amdgcn_rcpf(d1), rd2 = __builtin_amdgcn_rcpf(d2);
-        f = (n1 * n2) * (rd1 * rd2);
-        const float D0 = f * (2.0f * my * (rn1 - rn2) + 2.0f * mx * (rd2 - rd1));
+        const float fr = (n1 * n2) * (rd1 * rd2);
+        f += fr;
+        const float D0 = fr * (2.0f * my * (rn1 - rn2) + 2.0f * mx * (rd2 - rd1));
         const size_t o = ch * plane + (size_t)i * W + j;
         D[o] = D0;
-        D[3 * plane + o] = -f * rd2;
-        D[6 * plane + o] = 2.0f * f * rn2;
+        D[3 * plane + o] = -fr * rd2;
+        D[6 * plane + o] = 2.0f * fr * rn2;
         const float e = sv[0][ty + kSsimR][tx + kSsimR] - sv[1][ty + kSsimR][tx + kSsimR];
-        l1 = fabsf(e);
-        l2 = e * e;
+        l1 += fabsf(e);
+        l2 += e * e;
+    }
+    }
     }
     // tile partials, reduced in a fixed order
     float v[3] = {f, l1, l2};
@@ -162,11 +177,20 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(int W, int H, const float *__r
     __shared__ float hs[3][kSsimS][kSsimT + 1];
     const int tid = threadIdx.x, ch = blockIdx.z;
     const int x0 = blockIdx.x * kSsimT, y0 = blockIdx.y * kSsimT;
-    const int tx = tid & 15, ty = tid >> 4;
-    const int i = y0 + ty, j = x0 + tx;
-    const bool inside = i < H && j < W;
-    const size_t o = ch * plane + (size_t)(inside ? i : 0) * W + (inside ? j : 0);
-    const float xv = x[o], yv = y[o];                     // the own pixel's inputs, with the staging loads
+    // two vertically adjacent outputs per thread (threads < 128); their inputs load with the staging
+    const bool act = tid < kSsimT * kSsimT / 2;
+    const int tx = tid & 15, ty0 = ((tid >> 4) & 7) * 2;
+    float xv[2], yv[2];
+    size_t oo[2];
+    bool ins[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int i = y0 + ty0 + r, j = x0 + tx;
+        ins[r] = act && i < H && j < W;
+        oo[r] = ch * plane + (size_t)(ins[r] ? i : 0) * W + (ins[r] ? j : 0);
+        xv[r] = x[oo[r]];
+        yv[r] = y[oo[r]];
+    }
     constexpr int kRounds = (kSsimS * kSsimS + 255) / 256;
     float v[3][kRounds];
 #pragma unroll
@@ -202,20 +226,28 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(int W, int H, const float *__r
         }
     }
     __syncthreads();
-    if (!inside) return;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+    if (!act) return;
+    float ss[2][3] = {{0.f, 0.f, 0.f}, {0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int a = 0; a < 11; ++a) {
-        const float g = win.g[a];
-        s0 = fmaf(g, hs[0][ty + a][tx], s0);
-        s1 = fmaf(g, hs[1][ty + a][tx], s1);
-        s2 = fmaf(g, hs[2][ty + a][tx], s2);
+    for (int k = 0; k < 3; ++k) {
+        float hv[12];
+#pragma unroll
+        for (int a = 0; a < 12; ++a) hv[a] = hs[k][ty0 + a][tx];
+#pragma unroll
+        for (int a = 0; a < 11; ++a) {
+            ss[0][k] = fmaf(win.g[a], hv[a], ss[0][k]);
+            ss[1][k] = fmaf(win.g[a], hv[a + 1], ss[1][k]);
+        }
     }
-    const float e = xv - yv;
     const float n = (float)(3.0 * (double)plane);
-    const float dssim = fmaf(yv, s2, fmaf(2.0f * xv, s1, s0)) / n;
-    const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
-    dL[o] = fmaf(w1, sg / n, fmaf(w2, 2.0f * e / n, -(ws * dssim)));
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (!ins[r]) continue;
+        const float e = xv[r] - yv[r];
+        const float dssim = fmaf(yv[r], ss[r][2], fmaf(2.0f * xv[r], ss[r][1], ss[r][0])) / n;
+        const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
+        dL[oo[r]] = fmaf(w1, sg / n, fmaf(w2, 2.0f * e / n, -(ws * dssim)));
+    }
 }
 
 static SsimWin ssim_window() {
