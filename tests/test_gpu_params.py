@@ -210,3 +210,33 @@ def test_rs_fused_step_matches_separate_calls():
     from rasterizer_gaussian_raster_amd.pipeline import cholesky_params
     want = cholesky_params(a.params).cpu().numpy()
     np.testing.assert_array_equal(a.chol.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_new_entry_points_on_empty_sets():
+    """Conversion, chain rule, merge, absgrad, the rotation-scale and alpha update passes and the
+    SSIM loss with no Gaussians / no pairs: they run, write nothing out of range, and give zeros."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter, FitterRS, Raster, cholesky_params
+    W, H = 70, 45
+    e8 = torch.zeros((0, 8), dtype=torch.float32, device="cuda")
+    assert cholesky_params(e8, gi.PARAMS_RS, 2.0, 2.0).shape == (0, 8)
+    gi.gi_params_to_cholesky_grad(gi.PARAMS_RS, 0, e8, 1.0, 1.0, e8, torch.zeros_like(e8))
+    gi.gi_merge_pairs(0, torch.zeros((0, 2), dtype=torch.int32, device="cuda"), 0, e8, torch.zeros_like(e8))
+    r = Raster(W, H, 0)
+    img = r.render(e8).clone()
+    r.backward_absgrad(torch.ones((3, H, W), dtype=torch.float32, device="cuda"), e8.clone(),
+                       torch.zeros((0, 2), dtype=torch.float32, device="cuda"))
+    tgt = torch.full((3, H, W), 0.25, dtype=torch.float32, device="cuda")
+    frs = FitterRS(tgt, e8)
+    frs.step()
+    fa = Fitter(tgt, e8, logit=torch.zeros(0, dtype=torch.float32, device="cuda"),
+                background=torch.full((3,), 0.5, dtype=torch.float32, device="cuda"))
+    fa.step()
+    fs = Fitter(tgt, e8, loss=(0.8, 0.0, 0.2))
+    fs.step()
+    torch.cuda.synchronize()
+    assert float(img.abs().max()) == 0.0
+    assert abs(frs.loss.item() - 0.25 ** 2) < 1e-7                 # image 0 against 0.25
+    assert abs(fa.loss.item() - 0.25 ** 2) < 1e-7                  # background 0.5 against 0.25
+    assert np.isfinite(fs.loss.item())
