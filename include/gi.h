@@ -207,6 +207,7 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
 #define GI_FIT_PREPARED 1u
 #define GI_FIT_ORDER 2u
 #define GI_FIT_USE_ORDER 4u
+#define GI_FIT_NO_UPDATE 8u
 
 /*
  * gi_render_image -- gi_preprocess_bin_sort followed by gi_render_fwd in one
@@ -406,6 +407,12 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
  *             GI_FIT_USE_ORDER: the raster pass takes the tiles in b->tile_order,
  *             which must hold a valid order (an earlier call's GI_FIT_ORDER, or
  *             gi_bin_sort); any permutation gives the same results.
+ *             GI_FIT_NO_UPDATE: binning and the fused raster only -- the
+ *             per-pair gradient slots stay in b->bwd_workspace and the loss
+ *             partials in b->loss_partials for the caller's own update pass
+ *             (e.g. gi_adam_step_pairs_rs of another parameter form whose
+ *             Cholesky form is b->params); hp, step, d_step, m, v and d_loss
+ *             are unused, and the next call must not pass GI_FIT_PREPARED.
  *   When each first-pass bucket holds at most 16 tiles (up to 2^21 pairs of
  *   capacity and a low digit of <= 4 bits, e.g. 768x512), the raster's
  *   workgroups finish the sort themselves -- each reads its tile's bucket and

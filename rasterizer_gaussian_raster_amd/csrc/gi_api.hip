@@ -271,8 +271,10 @@ gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *reco
 gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
                           int32_t step, const int32_t *d_step, uint32_t flags, void *stream) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || !hp || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
-    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER)) != 0u) return GI_ERR_INVALID_ARG;
-    if (!d_step && step < 1) return GI_ERR_INVALID_ARG;
+    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER | GI_FIT_NO_UPDATE)) != 0u)
+        return GI_ERR_INVALID_ARG;
+    const bool update = !(flags & GI_FIT_NO_UPDATE);
+    if (update && !d_step && step < 1) return GI_ERR_INVALID_ARG;
     if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps >= 0.0))
         return GI_ERR_INVALID_ARG;
     if (!preprocess_args_ok(desc, n, b->params, nullptr, b->records, nullptr, b->pixbox, b->counts) ||
@@ -285,7 +287,7 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
         return GI_ERR_INVALID_ARG;
     const int W = desc->width, H = desc->height;
     if (b->bwd_workspace_bytes < gi::make_bwd_plan(W, H, b->capacity).bytes) return GI_ERR_INVALID_ARG;
-    if (n > 0 && (!b->m || !b->v || !aligned16(b->m) || !aligned16(b->v))) return GI_ERR_INVALID_ARG;
+    if (update && n > 0 && (!b->m || !b->v || !aligned16(b->m) || !aligned16(b->v))) return GI_ERR_INVALID_ARG;
     const gi::BinPlan plan = gi::make_bin_plan((int)n, W, H, b->capacity);
     const gi::BinHist hist = gi::bin_hist(plan, b->bin_workspace);
     unsigned long long *groups = gi::bin_group_sums(plan, b->bin_workspace);
@@ -310,7 +312,7 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
                                         s, bucket ? &bl : nullptr);
     }
     if (e == hipSuccess && bucket && (flags & GI_FIT_ORDER)) e = gi::launch_tile_order(plan, b->ranges, b->tile_order, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && update)
         e = gi::launch_adam_preprocess((int)n, W, H, b->offsets, b->capacity, b->bwd_workspace, b->params, b->m, b->v,
                                        gi::make_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, step, d_step),
                                        b->records, b->pixbox, b->counts, groups, b->ranges, hist, b->loss_partials,

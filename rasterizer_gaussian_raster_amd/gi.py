@@ -38,7 +38,7 @@ def desc(width: int, height: int, mode: int = MODE_SUM) -> gi_desc:
     return gi_desc(int(width), int(height), int(mode), 0)
 
 
-FIT_PREPARED, FIT_ORDER, FIT_USE_ORDER = 1, 2, 4
+FIT_PREPARED, FIT_ORDER, FIT_USE_ORDER, FIT_NO_UPDATE = 1, 2, 4, 8
 
 
 class gi_fit_buffers(ctypes.Structure):

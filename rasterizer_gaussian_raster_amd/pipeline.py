@@ -225,6 +225,7 @@ class FitterRS:
         self.dL = torch.empty_like(self.target)
         self.loss = torch.zeros(1, dtype=torch.float32, device=self.params.device)
         self.lr, self.betas, self.eps = tuple(lr), betas, eps
+        self._hp = gi.adam_hparams(self.lr, betas[0], betas[1], eps)
         self.step_count = 0
         self.slack = capacity_slack
         cholesky_params(self.params, out=self.chol)
@@ -241,10 +242,24 @@ class FitterRS:
 
     def step(self):
         """The Cholesky form of the current params is in self.chol: written by the previous step's
-        gi_adam_step_pairs_rs (or by __init__ / step_separate)."""
+        gi_adam_step_pairs_rs (or by __init__ / step_separate).  Binning and the fused raster run as
+        gi_fit_step_sum with GI_FIT_NO_UPDATE (so the raster's workgroups finish the sort where the
+        buckets are small), then gi_adam_step_pairs_rs updates the rotation-scale params."""
         r, n = self.raster, self.n
-        r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.chol)
-        r.forward_backward_l2(self.target)
+        if r.bwd_ws is None:
+            r.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(r.desc, n, r.capacity), dtype=torch.uint8,
+                                   device=self.params.device)
+        fb = gi.fit_buffers(self.chol, None, None, self.target, r.image, r.loss_partials, None, r.records, r.pixbox,
+                            r.counts, r.offsets, r.keys, r.vals, r.ranges, r.order, r.d_num, r.capacity, r.ws,
+                            r.bwd_ws)
+        flags = gi.FIT_NO_UPDATE
+        if r.order is not None:
+            if r.has_order:
+                flags |= gi.FIT_USE_ORDER
+            if self.step_count % ORDER_EVERY == 0 or not r.has_order:
+                flags |= gi.FIT_ORDER
+                r.has_order = True
+        gi.gi_fit_step_sum(r.desc, n, fb, self._hp, 1, flags=flags)
         self.step_count += 1
         b1, b2 = self.betas
         gi.gi_adam_step_pairs_rs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, self.params, self.m, self.v, self.lr,
