@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void k_params_to_cholesky_grad(int kind, int64
 
 // Rotation-scale training: each Gaussian's per-pair gradient slots added in emission order (the
 // Cholesky-form gradient, as k_grad_gather forms it), the chain rule, and the Adam update of the
-// rotation-scale params; one thread per Gaussian.  The spare last workgroup reduces the loss.
+// rotation-scale params; two lanes per Gaussian (four values each, swapped for the chain rule and
+// the conversion).  The spare last workgroup reduces the loss.
 __global__ __launch_bounds__(256) void k_adam_pairs_rs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
                                                        const float4 *__restrict__ part, float4 *__restrict__ p,
                                                        float4 *__restrict__ m, float4 *__restrict__ v, AdamHP ah,
@@ -113,34 +114,44 @@ __global__ __launch_bounds__(256) void k_adam_pairs_rs(int n, const uint32_t *__
         loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
         return;
     }
-    const int g = blockIdx.x * 256 + threadIdx.x;
+    const int i = blockIdx.x * 256 + threadIdx.x;         // lane h = i & 1 of Gaussian i >> 1: params 4h .. 4h + 3
+    const int g = i >> 1, h = i & 1;
     if (g >= n) return;
     float c1, c2;
     adam_step_bias(ah, c1, c2);
     const uint32_t o0 = offsets[g], o1r = offsets[g + 1];
     const uint32_t o1 = offsets[n] <= capacity ? o1r : o0;   // else the binning overflowed: zero gradient
-    float4 d0 = make_float4(0.f, 0.f, 0.f, 0.f), d1 = d0;
-    gather_slots(part, o0, o1, d0, d1);
-    const float4 a = p[2 * g], b = p[2 * g + 1];
+    float4 gh = make_float4(0.f, 0.f, 0.f, 0.f);
+    gather_half(part, o0, o1, h, gh);                     // this lane's 4 of the Cholesky-form gradient
+    const float4 mine = p[2 * g + h];
+    // the partner lane's halves: the whole gradient and params for the chain rule
+    const float4 oth = make_float4(__shfl_xor(gh.x, 1, 64), __shfl_xor(gh.y, 1, 64), __shfl_xor(gh.z, 1, 64),
+                                   __shfl_xor(gh.w, 1, 64));
+    const float4 op = make_float4(__shfl_xor(mine.x, 1, 64), __shfl_xor(mine.y, 1, 64), __shfl_xor(mine.z, 1, 64),
+                                  __shfl_xor(mine.w, 1, 64));
+    const float4 d0 = h ? oth : gh, d1 = h ? gh : oth;
+    const float4 a = h ? op : mine, b = h ? mine : op;
     float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0;
     if (o1 > o0) chol_chain(1, a, b, 1.0f, 1.0f, d0, d1, r0, r1);
-    float P[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    const float G[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    const float4 m0 = m[2 * g], m1 = m[2 * g + 1], v0 = v[2 * g], v1 = v[2 * g + 1];
-    float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float4 rg = h ? r1 : r0;
+    float P[4] = {mine.x, mine.y, mine.z, mine.w};
+    const float G[4] = {rg.x, rg.y, rg.z, rg.w};
+    const float4 m4 = m[2 * g + h], v4 = v[2 * g + h];
+    float M[4] = {m4.x, m4.y, m4.z, m4.w};
+    float V[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) adam_update(P[k], G[k], M[k], V[k], ah.lr[k], ah, c1, c2);
-    p[2 * g] = make_float4(P[0], P[1], P[2], P[3]);
-    p[2 * g + 1] = make_float4(P[4], P[5], P[6], P[7]);
-    m[2 * g] = make_float4(M[0], M[1], M[2], M[3]);
-    m[2 * g + 1] = make_float4(M[4], M[5], M[6], M[7]);
-    v[2 * g] = make_float4(V[0], V[1], V[2], V[3]);
-    v[2 * g + 1] = make_float4(V[4], V[5], V[6], V[7]);
+    for (int k = 0; k < 4; ++k) adam_update(P[k], G[k], M[k], V[k], ah.lr[4 * h + k], ah, c1, c2);
+    p[2 * g + h] = make_float4(P[0], P[1], P[2], P[3]);
+    m[2 * g + h] = make_float4(M[0], M[1], M[2], M[3]);
+    v[2 * g + h] = make_float4(V[0], V[1], V[2], V[3]);
     if (chol) {                                           // the next step's Cholesky form
-        const CholRS c = rs_cholesky(P[2], P[3], P[4]);
-        chol[2 * g] = make_float4(P[0], P[1], c.l11, c.l21);
-        chol[2 * g + 1] = make_float4(c.l22, P[5], P[6], P[7]);
+        const float4 np = make_float4(P[0], P[1], P[2], P[3]);
+        const float4 qp = make_float4(__shfl_xor(np.x, 1, 64), __shfl_xor(np.y, 1, 64), __shfl_xor(np.z, 1, 64),
+                                      __shfl_xor(np.w, 1, 64));
+        const float4 A = h ? qp : np, B = h ? np : qp;
+        const CholRS c = rs_cholesky(A.z, A.w, B.x);
+        if (h == 0) chol[2 * g] = make_float4(A.x, A.y, c.l11, c.l21);
+        else chol[2 * g + 1] = make_float4(c.l22, B.y, B.z, B.w);
     }
 }
 
@@ -200,7 +211,7 @@ hipError_t launch_adam_pairs_rs(int n, int W, int H, const uint32_t *offsets, in
                                 float *p, float *m, float *v, const float *lr, double beta1, double beta2, double eps,
                                 int step, const float *loss_partials, int64_t loss_count, float *d_loss, float *chol,
                                 hipStream_t s) {
-    const int nb = (n + 255) / 256 + (d_loss ? 1 : 0);
+    const int nb = (2 * n + 255) / 256 + (d_loss ? 1 : 0);
     if (nb == 0) return hipSuccess;
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
     const AdamHP a = make_adam_hp(lr, beta1, beta2, eps, step, nullptr);
