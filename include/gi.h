@@ -208,6 +208,7 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
 #define GI_FIT_ORDER 2u
 #define GI_FIT_USE_ORDER 4u
 #define GI_FIT_NO_UPDATE 8u
+#define GI_FIT_TRACK_MAX 16u
 
 /*
  * gi_render_image -- gi_preprocess_bin_sort followed by gi_render_fwd in one
@@ -271,9 +272,9 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
  *   background, t_final, last: as given to / produced by gi_render_fwd (alpha
  *             mode; NULL in sum mode).
  *   dL_dimage device float [3][H][W].
- *   dparams   device float [n][8], ACCUMULATED (+=) in the params layout; in sum
- *             mode it may be NULL, which leaves the per-pair gradients in the
- *             workspace for gi_adam_step_pairs (no gather pass).
+ *   dparams   device float [n][8], ACCUMULATED (+=) in the params layout; it may
+ *             be NULL, which leaves the pair slots in the workspace for
+ *             gi_adam_step_pairs[_rs|_alpha] or gi_grad_gather (no gather pass).
  *   dlogit    device float [n], accumulated (alpha mode) or NULL.
  *   dbackground device float [3], accumulated (alpha mode) or NULL.
  *   loss_partials, loss_count, d_loss (sum mode, optional): when d_loss is not
@@ -283,11 +284,13 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
  *             NULL in alpha mode.
  *   workspace device scratch of gi_render_bwd_workspace_bytes() bytes, 256-byte
  *             aligned, no initialisation needed.
- *   Each (Gaussian, tile) pair's gradient is formed in the tile's workgroup,
- *   its per-pixel terms added in a fixed order, and stored at the pair's
- *   emission slot offsets[g] + (position of the tile in g's tile rectangle); a
- *   second pass adds each Gaussian's slots in that order.  No atomics: the
- *   gradients are bitwise reproducible.  If gi_bin_sort overflowed
+ *   Each (Gaussian, tile) pair's sums (its pixels' terms in the Gaussian's
+ *   whitened frame, as gi_grad_gather describes) are formed in the tile's
+ *   workgroup, its per-pixel terms added in a fixed order, and stored at the
+ *   pair's emission slot offsets[g] + (position of the tile in g's tile
+ *   rectangle); a second pass adds each Gaussian's slots in that order and
+ *   maps the total to the gradient w.r.t. (mean, L, colour) with the record's
+ *   rows (a, b, c).  No atomics: the gradients are bitwise reproducible.  If gi_bin_sort overflowed
  *   (M > capacity) nothing is accumulated.
  */
 size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity);
@@ -307,8 +310,8 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
  *   back-propagates it, so dL/dimage never goes through device memory and the
  *   tile list is staged once.  Outputs are bit-identical to the two calls:
  *   image, loss_partials (and dL_dimage when not NULL) as gi_render_fwd_l2, the
- *   per-pair gradients in the workspace as gi_render_bwd, ready for
- *   gi_adam_step_pairs (or a gather).  Arguments as in those two calls; the
+ *   pair slots in the workspace as gi_render_bwd, ready for
+ *   gi_adam_step_pairs (or gi_grad_gather).  Arguments as in those two calls; the
  *   workspace is gi_render_bwd's.  Sum mode only.
  */
 gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
@@ -351,7 +354,9 @@ gi_status gi_adam_step(int64_t rows, int32_t row_len, float *p, float *g, float 
  * gi_adam_step_pairs -- gi_adam_step (rows of 8, sum mode) whose gradient is
  *   read straight from the per-pair slots that gi_render_bwd(dparams = NULL)
  *   left in its workspace: each Gaussian's slots offsets[g] .. offsets[g+1]
- *   are added in emission order (the gather) and the Adam update applied in
+ *   are added in emission order (the gather), mapped to the Cholesky-form
+ *   gradient as gi_render_bwd does (with (a, b, c) formed from p, which must
+ *   be the params the records were made from), and the Adam update applied in
  *   the same pass.  Same arguments as gi_render_bwd for the slots (desc, n,
  *   offsets, capacity, workspace) and as gi_adam_step for the update (p, m, v
  *   device float [n][8]; lr host float [8]).  A binning overflow gives a zero
@@ -408,11 +413,16 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
  *             which must hold a valid order (an earlier call's GI_FIT_ORDER, or
  *             gi_bin_sort); any permutation gives the same results.
  *             GI_FIT_NO_UPDATE: binning and the fused raster only -- the
- *             per-pair gradient slots stay in b->bwd_workspace and the loss
+ *             pair slots stay in b->bwd_workspace and the loss
  *             partials in b->loss_partials for the caller's own update pass
  *             (e.g. gi_adam_step_pairs_rs of another parameter form whose
- *             Cholesky form is b->params); hp, step, d_step, m, v and d_loss
- *             are unused, and the next call must not pass GI_FIT_PREPARED.
+ *             Cholesky form is b->params); hp (may be NULL), step, d_step, m, v
+ *             and d_loss are unused, and the next call must not pass GI_FIT_PREPARED.
+ *             GI_FIT_TRACK_MAX: b->d_num points to 2 uint32; besides M in
+ *             d_num[0], d_num[1] = max(d_num[1], M) (the caller clears it): one
+ *             read after many asynchronous steps tells whether any of their
+ *             binnings overflowed (M > capacity renders nothing and gives a
+ *             zero gradient for that step).
  *   When each first-pass bucket holds at most 16 tiles (up to 2^21 pairs of
  *   capacity and a low digit of <= 4 bits, e.g. 768x512), the raster's
  *   workgroups finish the sort themselves -- each reads its tile's bucket and
@@ -495,6 +505,38 @@ gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *param
                                      const float *dout, float *dparams, int32_t accumulate, void *stream);
 
 /*
+ * gi_grad_gather -- the gradient w.r.t. params of form `kind` straight from
+ *   the backward's pair slots: what gi_render_bwd's dparams gives followed by
+ *   gi_params_to_cholesky_grad, without going through the Cholesky-form
+ *   gradient ("GaussianImage", Overview and its "gaussianimage_rs" scripts;
+ *   "FlashImgs", Library API: scale / rot tensors, rendering at any size).
+ *   The slots hold each pair's sums in the Gaussian's whitened frame
+ *   (u, v) = (a dx, b dx + c dy) of its record: with h = (dL/dw) w, the sums
+ *   of h u, h v, h u^2, h u v, h v^2 and of g_k w.  Any parameterisation's
+ *   gradient is a linear map of a Gaussian's total; for the rotation-scale
+ *   form that map (to the Gaussian's own axes) is orthogonal up to the scales,
+ *   computed in fp64, so the result keeps the accuracy of the per-pixel terms
+ *   -- unlike the chain rule applied to the Cholesky-form gradient, which for
+ *   a rotated, elongated Gaussian is a difference of much larger terms.
+ *   desc       the rendered image (sum or alpha mode; only the 8 parameters are
+ *              gathered here).
+ *   kind       gi_param_kind of params.
+ *   params     device float [n][8] in form `kind`, whose Cholesky form at scale
+ *              (fx, fy) (gi_params_to_cholesky) made `records`.
+ *   records    device float [n][8]: gi_preprocess's records of that form, as
+ *              given to the backward.
+ *   offsets, capacity: as given to gi_render_bwd.
+ *   workspace  gi_render_bwd's workspace after gi_render_bwd with dparams NULL,
+ *              or gi_render_fwd_bwd_l2 (the slots are read, not changed).
+ *   dparams    device float [n][8], ACCUMULATED (+=), not aliasing params.
+ *   Gaussians without pairs (culled, off-image) and every Gaussian after an
+ *   overflowed binning get nothing added.
+ */
+gi_status gi_grad_gather(const gi_desc *desc, int32_t kind, int64_t n, const float *params, float fx, float fy,
+                         const float *records, const uint32_t *offsets, int64_t capacity, const void *workspace,
+                         size_t workspace_bytes, float *dparams, void *stream);
+
+/*
  * gi_loss_ssim -- the pixel loss
  *     L = w1 mean|I - T| + w2 mean (I - T)^2 + ws (1 - SSIM)
  *   over the 3HW entries, and dL/dI ("Drawing with Gaussians", 2D fitting:
@@ -523,9 +565,10 @@ gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const 
  *   "gaussianimage_rs" form of "GaussianImage"): each Gaussian's per-pair
  *   gradient slots (left by gi_render_fwd_bwd_l2, or gi_render_bwd with
  *   dparams = NULL, for the Cholesky params gi_params_to_cholesky made with
- *   fx = fy = 1) are added in emission order, carried through
- *   gi_params_to_cholesky_grad's chain rule and applied to p by the Adam step,
- *   in one pass.  Arguments as gi_adam_step_pairs (no device step counter);
+ *   fx = fy = 1) are added in emission order, mapped to the
+ *   rotation-scale gradient as gi_grad_gather does (kind GI_PARAMS_RS,
+ *   fx = fy = 1, the records' rows formed from p) and applied to p by the Adam
+ *   step, in one pass.  Arguments as gi_adam_step_pairs (no device step counter);
  *   p, m, v device float [n][8] in the rotation-scale form.
  *   chol_out  device float [n][8] or NULL: also the updated Gaussians'
  *             Cholesky form (what gi_params_to_cholesky with fx = fy = 1
@@ -594,8 +637,9 @@ gi_status gi_render_fwd_alpha_l2(const gi_desc *desc, int64_t n, const float *re
 /*
  * gi_adam_step_pairs_alpha -- the alpha mode's update in one pass: the
  *   per-pair slots that gi_render_bwd (alpha, dparams = NULL) left in its
- *   workspace are added per Gaussian in emission order (as its gather does)
- *   and the Adam step (as gi_adam_step) applied to the 8 params and the logit
+ *   workspace are added per Gaussian in emission order and mapped to the
+ *   gradient (as its gather does, with the records' rows formed from p) and
+ *   the Adam step (as gi_adam_step) applied to the 8 params and the logit
  *   of every Gaussian, and to the background's 3 channels from the tiles'
  *   background partials; d_loss (optional) also gets the loss of
  *   gi_render_fwd_alpha_l2's partials (as gi_loss_reduce).

@@ -84,8 +84,10 @@ def _load():
     f64 = ctypes.c_double
     lib.oracle_render_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i64, i32, P, P, P]
     lib.oracle_render_sum_rs.restype = None
-    lib.oracle_grad_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i32, P, P, P, P]
+    lib.oracle_grad_sum_rs.argtypes = [i32, i32, i64, P, f64, f64, P, i32, P, P, P]
     lib.oracle_grad_sum_rs.restype = None
+    lib.oracle_rs_cholesky_grad.argtypes = [i64, P, f64, f64, P, P, P]
+    lib.oracle_rs_cholesky_grad.restype = None
     lib.oracle_loss_ssim.argtypes = [i32, i32, P, P, f64, f64, f64, P, P, P, P]
     lib.oracle_loss_ssim.restype = f64
     lib.oracle_merge_pairs.argtypes = [i64, P, P, P]
@@ -251,18 +253,27 @@ def render_sum_rs(W, H, params_rs, fx=1.0, fy=1.0, pixels=None, cutoff=True):
     return out, sabs, amb
 
 
-def grad_sum_rs(W, H, params_rs, dL_dI, fx=1.0, fy=1.0, cutoff=True, with_chain=False):
+def grad_sum_rs(W, H, params_rs, dL_dI, fx=1.0, fy=1.0, cutoff=True):
     """(dparams [N,8], running-error scale [N,8], ambiguous-pair magnitude [N,8]) of
-    L = <dL_dI, I> for the rotation-scale sum image rendered at scale (fx, fy); with_chain also
-    returns the running-error scale of evaluating through the Cholesky factor and the chain rule."""
+    L = <dL_dI, I> for the rotation-scale sum image rendered at scale (fx, fy)."""
     par = _f64(params_rs).reshape(-1, 8)
     G = _f64(dL_dI).reshape(3, H, W)
     n = par.shape[0]
     d, c, a = np.zeros((n, 8)), np.zeros((n, 8)), np.zeros((n, 8))
-    ch = np.zeros((n, 8)) if with_chain else None
     _load().oracle_grad_sum_rs(W, H, n, _p(par), float(fx), float(fy), _p(G), 1 if cutoff else 0, _p(d), _p(c),
-                               _p(a), _p(ch))
-    return (d, c, a, ch) if with_chain else (d, c, a)
+                               _p(a))
+    return d, c, a
+
+
+def rs_cholesky_grad(params_rs, dout, fx=1.0, fy=1.0):
+    """(J^T dout, |J|^T |dout|) [N,8]: the chain rule of the conversion of rotation-scale params to
+    the Cholesky form at scale (fx, fy), applied to a gradient dout w.r.t. that form."""
+    par = _f64(params_rs).reshape(-1, 8)
+    d = _f64(dout).reshape(-1, 8)
+    n = par.shape[0]
+    out, sc = np.zeros((n, 8)), np.zeros((n, 8))
+    _load().oracle_rs_cholesky_grad(n, _p(par), float(fx), float(fy), _p(d), _p(out), _p(sc))
+    return out, sc
 
 
 def loss_ssim(image, target, w1=0.8, w2=0.0, ws=0.2, with_grad=True):

@@ -680,55 +680,25 @@ void oracle_render_sum_rs(int W, int H, int64_t n, const double *prs, double fx,
  *   dq/dtheta = 2 r1 r2 (1/sx^2 - 1/sy^2)   (dr1/dtheta = r2, dr2/dtheta = -r1),
  *   dL/dc_k   = sum_p G_k w.
  * acond[n,8]: running-error scale (every inner sum over absolute values);
- * amb[n,8]: sum of |contribution| over the ambiguous pairs.
- * acond_chain[n,8] (may be NULL): the running-error scale of the other order
- * of evaluation -- the gradient w.r.t. the Cholesky factor L' = D L of
- * D Sigma D first (its running-error scale C' as for the Cholesky form), then
- * the chain rule: |J|^T C', J = d(D mu, L')/d(mu, sx, sy, theta), from
- *   L = chol(Sigma): l11 = sqrt(A), l21 = B/l11, l22 = P/l11,
- *   A = (cos ax)^2 + (sin ay)^2, B = cos sin (ax^2 - ay^2), P = ax ay,
- *   ax = |sx|, ay = |sy|.  A rotated, strongly anisotropic Gaussian has a
- * skewed factor (|l21| >> l11), and the chain amplifies the rounding of the
- * factor's gradient accordingly. */
+ * amb[n,8]: sum of |contribution| over the ambiguous pairs. */
 void oracle_grad_sum_rs(int W, int H, int64_t n, const double *prs, double fx, double fy, const double *G,
-                        int cutoff, double *dparams, double *acond, double *amb, double *acond_chain)
+                        int cutoff, double *dparams, double *acond, double *amb)
 {
     const int nt = omp_get_max_threads();
     const size_t nn = (size_t)(n > 0 ? n : 1);
     rsg *gs = (rsg *)malloc(sizeof(rsg) * nn);
-    gauss64 *gc64 = (gauss64 *)malloc(sizeof(gauss64) * nn);   /* the scaled Cholesky form */
-    double *jac = (double *)calloc(nn * 9, sizeof(double));    /* d(l11', l21', l22')/d(sx, sy, theta) */
-    for (int64_t g = 0; g < n; ++g) {
-        gs[g] = rs_setup(prs + 8 * g);
-        if (!gs[g].ok) continue;
-        const double cs = gs[g].cs, sn = gs[g].sn, ax = fabs(gs[g].sx), ay = fabs(gs[g].sy);
-        const double A = cs * cs * ax * ax + sn * sn * ay * ay, B = cs * sn * (ax * ax - ay * ay), P = ax * ay;
-        const double l11 = sqrt(A), l21 = B / l11, l22 = P / l11;
-        const double p8[8] = {fx * gs[g].mx, fy * gs[g].my, fx * l11, fy * l21, fy * l22, 0, 0, 0};
-        gc64[g] = gauss_setup(p8, NULL);
-        const double dA[3] = {2 * cs * cs * ax, 2 * sn * sn * ay, -2 * B};
-        const double dB[3] = {2 * cs * sn * ax, -2 * cs * sn * ay, (cs * cs - sn * sn) * (ax * ax - ay * ay)};
-        const double dP[3] = {ay, ax, 0.0};
-        const double sg[3] = {gs[g].sx < 0 ? -1.0 : 1.0, gs[g].sy < 0 ? -1.0 : 1.0, 1.0};
-        for (int k = 0; k < 3; ++k) {
-            const double d11 = dA[k] / (2 * l11);
-            jac[9*g + 0*3 + k] = fx * sg[k] * d11;
-            jac[9*g + 1*3 + k] = fy * sg[k] * (dB[k] - l21 * d11) / l11;
-            jac[9*g + 2*3 + k] = fy * sg[k] * (dP[k] - l22 * d11) / l11;
-        }
-    }
-    double *part = (double *)calloc((size_t)nt * 32 * nn, sizeof(double));
+    for (int64_t g = 0; g < n; ++g) gs[g] = rs_setup(prs + 8 * g);
+    double *part = (double *)calloc((size_t)nt * 24 * nn, sizeof(double));
     const int64_t HW = (int64_t)H * W;
     #pragma omp parallel
     {
-        double *mine = part + (size_t)omp_get_thread_num() * 32 * nn;
+        double *mine = part + (size_t)omp_get_thread_num() * 24 * nn;
         #pragma omp for schedule(dynamic, 4)
         for (int i = 0; i < H; ++i)
             for (int j = 0; j < W; ++j) {
                 const double gk[3] = {G[(int64_t)i*W + j], G[HW + (int64_t)i*W + j], G[2*HW + (int64_t)i*W + j]};
                 if (gk[0] == 0.0 && gk[1] == 0.0 && gk[2] == 0.0) continue;   /* contributes exactly 0 */
                 const double x = (j + 0.5) / fx, y = (i + 0.5) / fy;
-                const double xo = j + 0.5, yo = i + 0.5;
                 for (int64_t g = 0; g < n; ++g) {
                     const rsg *s = &gs[g];
                     if (!s->ok) continue;
@@ -759,41 +729,62 @@ void oracle_grad_sum_rs(int W, int H, int64_t n, const double *prs, double fx, d
                     for (int k = 0; k < 3; ++k) { contrib[5+k] = gk[k] * w; cond[5+k] = fabs(contrib[5+k]); }
                     const int inside = !(cl == 2 && q > 9.0);
                     for (int t = 0; t < 8; ++t) {
-                        if (inside) { mine[32*g + t] += contrib[t]; mine[32*g + 8 + t] += cond[t]; }
-                        if (cl == 2) mine[32*g + 16 + t] += fabs(contrib[t]);
-                    }
-                    if (inside && acond_chain) {     /* the Cholesky-form scale, in the output frame */
-                        double dqc[5];
-                        gauss_dq_abs(&gc64[g], xo - gc64[g].mx, yo - gc64[g].my, dqc);
-                        for (int t = 0; t < 5; ++t) mine[32*g + 24 + t] += ha * dqc[t];
+                        if (inside) { mine[24*g + t] += contrib[t]; mine[24*g + 8 + t] += cond[t]; }
+                        if (cl == 2) mine[24*g + 16 + t] += fabs(contrib[t]);
                     }
                 }
             }
     }
     for (int64_t g = 0; g < n; ++g) {
-        double cc[5] = {0, 0, 0, 0, 0};
         for (int t = 0; t < 8; ++t) {
             double s = 0, c = 0, a = 0;
             for (int th = 0; th < nt; ++th) {
-                s += part[(size_t)th*32*nn + 32*g + t];
-                c += part[(size_t)th*32*nn + 32*g + 8 + t];
-                a += part[(size_t)th*32*nn + 32*g + 16 + t];
-                if (t < 5) cc[t] += part[(size_t)th*32*nn + 32*g + 24 + t];
+                s += part[(size_t)th*24*nn + 24*g + t];
+                c += part[(size_t)th*24*nn + 24*g + 8 + t];
+                a += part[(size_t)th*24*nn + 24*g + 16 + t];
             }
             dparams[8*g + t] = s;
             if (acond) acond[8*g + t] = c;
             if (amb) amb[8*g + t] = a;
         }
-        if (acond_chain) {
-            acond_chain[8*g + 0] = fx * cc[0];
-            acond_chain[8*g + 1] = fy * cc[1];
-            for (int k = 0; k < 3; ++k)
-                acond_chain[8*g + 2 + k] = fabs(jac[9*g + k]) * cc[2] + fabs(jac[9*g + 3 + k]) * cc[3] +
-                                           fabs(jac[9*g + 6 + k]) * cc[4];
-            for (int t = 5; t < 8; ++t) acond_chain[8*g + t] = acond ? acond[8*g + t] : 0.0;
-        }
     }
-    free(part); free(gs); free(gc64); free(jac);
+    free(part); free(gs);
+}
+
+/* The chain rule of the conversion to the Cholesky form at scale (fx, fy): given the gradient
+ * dout[n,8] w.r.t. (D mu, L', c) with L' = D chol(Sigma), out[n,8] = J^T dout w.r.t. the
+ * rotation-scale params, J = d(D mu, L', c)/d(mu, sx, sy, theta, c), and scale[n,8] = |J|^T |dout|
+ * (the size of the terms the sum adds).  The factor of Sigma = R diag(sx^2, sy^2) R^T:
+ *   l11 = sqrt(A), l21 = B/l11, l22 = P/l11,
+ *   A = (cos ax)^2 + (sin ay)^2, B = cos sin (ax^2 - ay^2), P = ax ay, ax = |sx|, ay = |sy|,
+ * differentiated by hand (then l' = (fx l11, fy l21, fy l22)).  A zero scale gives zeros. */
+void oracle_rs_cholesky_grad(int64_t n, const double *prs, double fx, double fy, const double *dout, double *out,
+                             double *scale)
+{
+    for (int64_t g = 0; g < n; ++g) {
+        const double *p = prs + 8 * g, *d = dout + 8 * g;
+        double *o = out + 8 * g, *sc = scale + 8 * g;
+        for (int t = 0; t < 8; ++t) { o[t] = 0.0; sc[t] = 0.0; }
+        const rsg r = rs_setup(p);
+        if (!r.ok) continue;
+        const double cs = r.cs, sn = r.sn, ax = fabs(r.sx), ay = fabs(r.sy);
+        const double A = cs * cs * ax * ax + sn * sn * ay * ay, B = cs * sn * (ax * ax - ay * ay), P = ax * ay;
+        const double l11 = sqrt(A), l21 = B / l11, l22 = P / l11;
+        const double dA[3] = {2 * cs * cs * ax, 2 * sn * sn * ay, -2 * B};
+        const double dB[3] = {2 * cs * sn * ax, -2 * cs * sn * ay, (cs * cs - sn * sn) * (ax * ax - ay * ay)};
+        const double dP[3] = {ay, ax, 0.0};
+        const double sg[3] = {r.sx < 0 ? -1.0 : 1.0, r.sy < 0 ? -1.0 : 1.0, 1.0};
+        o[0] = fx * d[0]; sc[0] = fabs(o[0]);
+        o[1] = fy * d[1]; sc[1] = fabs(o[1]);
+        for (int k = 0; k < 3; ++k) {
+            const double d11 = dA[k] / (2 * l11);
+            const double j[3] = {fx * sg[k] * d11, fy * sg[k] * (dB[k] - l21 * d11) / l11,
+                                 fy * sg[k] * (dP[k] - l22 * d11) / l11};
+            o[2 + k] = j[0] * d[2] + j[1] * d[3] + j[2] * d[4];
+            sc[2 + k] = fabs(j[0] * d[2]) + fabs(j[1] * d[3]) + fabs(j[2] * d[4]);
+        }
+        for (int t = 5; t < 8; ++t) { o[t] = d[t]; sc[t] = fabs(d[t]); }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -237,7 +237,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
         e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, tile_order, vals, capacity, dL_dimage,
                                       workspace, loss_partials, loss_count, d_loss, s);
         if (e == hipSuccess && dparams)
-            e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 0, dparams, nullptr,
+            e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, records, 0, dparams, nullptr,
                                        nullptr, s);
         return hip_status(e);
     }
@@ -245,7 +245,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
     e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, tile_order, vals, capacity,
                                     background, t_final, last, dL_dimage, workspace, s);
     if (e == hipSuccess && dparams)               // dparams = NULL: the slots stay for gi_adam_step_pairs_alpha
-        e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, 1, dparams, dlogit,
+        e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, records, 1, dparams, dlogit,
                                    dbackground, s);
     return hip_status(e);
 }
@@ -270,13 +270,16 @@ gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *reco
 
 gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
                           int32_t step, const int32_t *d_step, uint32_t flags, void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || !hp || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
-    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER | GI_FIT_NO_UPDATE)) != 0u)
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER | GI_FIT_NO_UPDATE |
+                             GI_FIT_TRACK_MAX)) != 0u)
         return GI_ERR_INVALID_ARG;
     const bool update = !(flags & GI_FIT_NO_UPDATE);
-    if (update && !d_step && step < 1) return GI_ERR_INVALID_ARG;
-    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps >= 0.0))
-        return GI_ERR_INVALID_ARG;
+    if (update) {                                         // hp is only read by the update pass
+        if (!hp || (!d_step && step < 1)) return GI_ERR_INVALID_ARG;
+        if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps >= 0.0))
+            return GI_ERR_INVALID_ARG;
+    }
     if (!preprocess_args_ok(desc, n, b->params, nullptr, b->records, nullptr, b->pixbox, b->counts) ||
         !bin_args_ok(desc, n, b->pixbox, b->counts, b->offsets, b->keys, b->vals, b->ranges, b->capacity, b->d_num,
                      b->bin_workspace, b->bin_workspace_bytes))
@@ -304,7 +307,7 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
     if (e == hipSuccess)
         e = gi::launch_bin_sort(plan, b->pixbox, b->counts, b->offsets, b->keys, b->vals, b->ranges,
                                 (!bucket && (flags & GI_FIT_ORDER)) ? b->tile_order : nullptr, b->d_num,
-                                b->bin_workspace, s, true, bucket);
+                                b->bin_workspace, s, true, bucket, (flags & GI_FIT_TRACK_MAX) ? b->d_num + 1 : nullptr);
     if (e == hipSuccess) {
         const gi::BucketList bl = gi::bin_bucket_list(plan, b->bin_workspace, b->keys, b->vals, b->ranges);
         e = gi::launch_render_sum_fused(W, H, b->records, b->pixbox, b->offsets, b->ranges, order, b->vals,
@@ -386,6 +389,22 @@ gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *param
                                                          as_stream(stream)));
 }
 
+gi_status gi_grad_gather(const gi_desc *desc, int32_t kind, int64_t n, const float *params, float fx, float fy,
+                         const float *records, const uint32_t *offsets, int64_t capacity, const void *workspace,
+                         size_t workspace_bytes, float *dparams, void *stream) {
+    if (!desc_ok(desc) || (kind != GI_PARAMS_CHOLESKY && kind != GI_PARAMS_RS) || n < 0 || n >= (1ll << 31) ||
+        capacity < 0 || capacity >= (1ll << 31))
+        return GI_ERR_INVALID_ARG;
+    if (!(fx > 0.0f) || !(fy > 0.0f) || !std::isfinite(fx) || !std::isfinite(fy)) return GI_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::make_bwd_plan(desc->width, desc->height, capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!params || !records || !dparams || !aligned16(params) || !aligned16(records) ||
+                  !aligned16(dparams) || dparams == params))
+        return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_grad_gather_params(kind, (int)n, desc->width, desc->height, params, fx, fy, records,
+                                                    offsets, capacity, workspace, dparams, as_stream(stream)));
+}
+
 size_t gi_loss_ssim_workspace_bytes(int32_t width, int32_t height) {
     if (width < 1 || height < 1 || width > kMaxDim || height > kMaxDim) return 0;
     return gi::ssim_workspace_bytes(width, height);
@@ -449,7 +468,8 @@ gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *rec
     hipError_t e = gi::launch_render_sum_bwd(W, H, records, pixbox, offsets, ranges, tile_order, vals, capacity,
                                              dL_dimage, workspace, nullptr, 0, nullptr, s, true);
     if (e == hipSuccess)
-        e = gi::launch_grad_gather((int)n, W, H, (int)gi_num_tiles(desc), offsets, capacity, workspace, 0, dparams,
+        e = gi::launch_grad_gather((int)n, W, H, (int)gi_num_tiles(desc), offsets, capacity, workspace, records, 0,
+                                   dparams,
                                    nullptr, nullptr, s, dabs);
     return hip_status(e);
 }

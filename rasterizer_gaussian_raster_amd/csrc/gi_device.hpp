@@ -136,6 +136,51 @@ __device__ __forceinline__ void gather_half(const float4 *__restrict__ part, uin
     }
 }
 
+// The pair slots of the backward hold, per (Gaussian, tile) pair and summed over the pair's
+// pixels, the Gaussian's sums in its scaled whitened frame: with h = (dL/dw) w and
+// (u, v) = (a dx, b dx + c dy) (the record's rows, e = u^2 + v^2, w = 2^-e, so dL/de = -ln2 h),
+//   s0 = (sum h u, sum h v, sum h u^2, sum h u v),  s1 = (sum h v^2, sum g_r w, sum g_g w, sum g_b w).
+// The gradient of any parameterisation is a linear map of a Gaussian's total, applied after the
+// gather.  Cholesky form (a = S/l11, b = -S l21/(l11 l22), c = S/l22, W = [[a, 0], [b, c]]):
+//   dL/dmu = 2 ln2 W^T (sum h u, sum h v),
+//   dL/d(l11, l21, l22) = (2 ln2 / S) (a sum h u^2 + b sum h u v, c sum h u v, c sum h v^2)
+// (the lower triangle of dL/dL = (2 ln2 / S) W^T M, M = [[sum h u^2, sum h u v], [sum h u v,
+// sum h v^2]]); the colours' gradients are the last three sums.
+// The record's rows (a, b, c) = S (1/l11, -(l21/l11)/l22, 1/l22) of a Cholesky factor, in the op
+// order of the cutoff rule (the preprocess forms every record with it; a kernel that has the
+// params rather than the record gets the same bits).
+__device__ __forceinline__ float3 conic_rows(float l11, float l21, float l22) {
+    const float i11 = 1.0f / l11;          // correctly rounded (no fast-math)
+    const float i22 = 1.0f / l22;
+    const float k = -((l21 * i11) * i22);
+    return make_float3(i11 * kScale, k * kScale, i22 * kScale);
+}
+
+constexpr float kGradMu = 2.0f * kLn2;
+constexpr float kGradL = kGradMu / kScale;
+
+// Half h of a Gaussian's Cholesky-form gradient from half h of its gathered sums (h = 0: mux,
+// muy, l11, l21; h = 1: l22 and the colours); (a, b, c) its record's rows.  Every kernel that
+// turns slots into a gradient uses these expressions, so their results agree bit for bit.
+__device__ __forceinline__ float4 slot_grad_half(int h, float a, float b, float c, float4 s) {
+    if (h == 0)
+        return make_float4(kGradMu * fmaf(a, s.x, b * s.y), kGradMu * (c * s.y), kGradL * fmaf(a, s.z, b * s.w),
+                           kGradL * (c * s.w));
+    return make_float4(kGradL * (c * s.x), s.y, s.z, s.w);
+}
+
+// Entry j of the same gradient from the sums sj (entry j of the total) and sn (entry j + 1).
+__device__ __forceinline__ float slot_grad_entry(int j, float a, float b, float c, float sj, float sn) {
+    switch (j) {
+    case 0: return kGradMu * fmaf(a, sj, b * sn);
+    case 1: return kGradMu * (c * sj);
+    case 2: return kGradL * fmaf(a, sj, b * sn);
+    case 3: return kGradL * (c * sj);
+    case 4: return kGradL * (c * sj);
+    default: return sj;
+    }
+}
+
 // Sum of the per-tile partials in a fixed order, divided by the entry count
 // (the first 256 threads of a workgroup of 256 or more; sm: 256 doubles of LDS).
 __device__ __forceinline__ void loss_reduce_block(int nparts, const float *__restrict__ part, double inv_count,

@@ -64,9 +64,11 @@ struct BinPlan {
 BinPlan make_bin_plan(int n, int W, int H, int64_t capacity);
 // groups_done: the preprocess kernel already wrote the group sums and cleared the ranges.
 // first_pass_only: stop after the first sort pass (bucket_list_mode plans; the raster finishes the sort).
+// d_max (or NULL): device running maximum of M, raised to this binning's M.
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
-                           void *ws, hipStream_t s, bool groups_done = false, bool first_pass_only = false);
+                           void *ws, hipStream_t s, bool groups_done = false, bool first_pass_only = false,
+                           uint32_t *d_max = nullptr);
 // The tile order from the ranges (as gi_bin_sort's tile_order).
 hipError_t launch_tile_order(const BinPlan &p, const uint32_t *ranges, uint32_t *tile_order, hipStream_t s);
 
@@ -103,7 +105,7 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
 
 // Backward workspace: per (Gaussian, tile) gradient at its emission slot.
 struct BwdPlan {
-    size_t off_part;    // float4 [capacity][2]: dmux, dmuy, dl11, dl21 | dl22, dcr, dcg, dcb
+    size_t off_part;    // float4 [capacity][2]: the pair's sums (slot layout: gi_device.hpp)
     size_t off_logit;   // float [capacity]: dlogit (alpha)
     size_t off_bg;      // float4 [ntiles]: dbackground per tile (alpha)
     size_t off_abs;     // float2 [capacity]: sum |d mux|, sum |d muy| over the pair's pixels (absgrad)
@@ -131,8 +133,8 @@ hipError_t launch_render_sum_fused(int W, int H, const float *records, const uin
 // Adds each Gaussian's slots (offsets[g] .. offsets[g+1]) in order to dparams / dlogit, and the
 // per-tile background partials to dbackground.
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
-                              const void *ws, int alpha, float *dparams, float *dlogit, float *dbackground,
-                              hipStream_t s, float *dabs = nullptr);
+                              const void *ws, const float *records, int alpha, float *dparams, float *dlogit,
+                              float *dbackground, hipStream_t s, float *dabs = nullptr);
 
 // k_raster_alpha.hip
 hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const float *opacity,
@@ -175,5 +177,10 @@ hipError_t launch_adam_pairs_rs(int n, int W, int H, const uint32_t *offsets, in
                                 float *p, float *m, float *v, const float *lr, double beta1, double beta2, double eps,
                                 int step, const float *loss_partials, int64_t loss_count, float *d_loss, float *chol,
                                 hipStream_t s);
+// dparams (+)= the gradient w.r.t. params of form `kind` whose Cholesky form at scale (fx, fy) made
+// `records`, from the pair slots the backward left in ws.
+hipError_t launch_grad_gather_params(int kind, int n, int W, int H, const float *params, float fx, float fy,
+                                     const float *records, const uint32_t *offsets, int64_t capacity, const void *ws,
+                                     float *dparams, hipStream_t s);
 
 }  // namespace gi

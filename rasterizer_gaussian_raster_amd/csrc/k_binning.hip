@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kBT) void k_group_sums(int n, const uint32_t *__res
                                                     unsigned long long *__restrict__ part, int ntiles,
                                                     uint2 *__restrict__ ranges, BinHeader *__restrict__ hdr,
                                                     uint32_t *__restrict__ offsets, uint32_t *__restrict__ d_num,
-                                                    BinHist hist) {
+                                                    BinHist hist, uint32_t *__restrict__ d_max) {
     __shared__ unsigned long long sm[4];
     __shared__ uint32_t h[256];
     const int tid = threadIdx.x;
@@ -452,11 +452,14 @@ __global__ __launch_bounds__(kBT) void k_group_sums(int n, const uint32_t *__res
     }
 }
 
+// d_max (or NULL): the caller's running maximum of M, raised to this M.
 __device__ __forceinline__ void publish_total(unsigned long long tot, long long capacity, int n,
-                                              BinHeader *hdr, uint32_t *offsets, uint32_t *d_num) {
+                                              BinHeader *hdr, uint32_t *offsets, uint32_t *d_num,
+                                              uint32_t *d_max) {
     hdr->total = tot;
     hdr->m_eff = (tot <= (unsigned long long)capacity) ? (uint32_t)tot : 0u;
     *d_num = sat32(tot);
+    if (d_max) *d_max = max(*d_max, sat32(tot));
     offsets[n] = sat32(tot);
 }
 
@@ -464,7 +467,7 @@ __device__ __forceinline__ void publish_total(unsigned long long tot, long long 
 __global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long long capacity,
                                                      unsigned long long *__restrict__ part,
                                                      BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
-                                                     uint32_t *__restrict__ d_num) {
+                                                     uint32_t *__restrict__ d_num, uint32_t *__restrict__ d_max) {
     __shared__ unsigned long long sm[16];
     const int per = (ngroups + 1023) / 1024;
     const int beg = threadIdx.x * per;
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long lo
             part[beg + i] = run;
             run += v;
         }
-    if (threadIdx.x == 0) publish_total(tot, capacity, n, hdr, offsets, d_num);
+    if (threadIdx.x == 0) publish_total(tot, capacity, n, hdr, offsets, d_num, d_max);
 }
 
 // ---------------------------------------------------------------------------
@@ -495,7 +498,8 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
                                                 const uint2 *__restrict__ pixbox,
                                                 const unsigned long long *__restrict__ part,
                                                 BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
-                                                uint32_t *__restrict__ d_num, uint32_t *__restrict__ table) {
+                                                uint32_t *__restrict__ d_num, uint32_t *__restrict__ table,
+                                                uint32_t *__restrict__ d_max) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sm[4];
     __shared__ unsigned long long sm64[8];
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(kBT) void k_count0(int n, int ngroups, int seg_grou
         block_exclusive_scan<unsigned long long, kBT>(all, sm64 + 4, &ta);
         base = tb;
         total = ta;
-        if (blockIdx.x == 0 && tid == 0) publish_total(total, capacity, n, hdr, offsets, d_num);
+        if (blockIdx.x == 0 && tid == 0) publish_total(total, capacity, n, hdr, offsets, d_num, d_max);
     } else {
         base = part[g0];
         total = hdr->total;
@@ -704,7 +708,8 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
                                                    uint2 *__restrict__ ranges, int ntiles,
                                                    const uint32_t *__restrict__ counts,
                                                    const unsigned long long *__restrict__ part, int ngroups,
-                                                   long long capacity, uint32_t *__restrict__ d_num) {
+                                                   long long capacity, uint32_t *__restrict__ d_num,
+                                                   uint32_t *__restrict__ d_max) {
     constexpr int NW = NT / 64, CH = NT * kWPL;
     __shared__ WideLds<NT> L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -775,7 +780,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
     }
     const uint32_t local = off + cinc - c;
     if (own) offsets[first + tid] = sat32(tb + local);
-    if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num);
+    if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num, d_max);
     const uint32_t M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
     if (M == 0u) return;                              // overflow or no pair: uniform
     if (own) {
@@ -1503,7 +1508,7 @@ hipError_t launch_tile_order(const BinPlan &p, const uint32_t *ranges, uint32_t 
 
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
-                           void *ws, hipStream_t s, bool groups_done, bool first_pass_only) {
+                           void *ws, hipStream_t s, bool groups_done, bool first_pass_only, uint32_t *d_max) {
     char *w = static_cast<char *>(ws);
     BinHeader *hdr = reinterpret_cast<BinHeader *>(w);
     unsigned long long *part = reinterpret_cast<unsigned long long *>(w + p.off_part);
@@ -1529,15 +1534,15 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     const bool folded = hist.table != nullptr;
     if (!groups_done || p.n == 0)
         k_group_sums<<<p.nb_g > 0 ? p.nb_g : 1, kBT, 0, s>>>(p.n, counts, box, part, p.ntiles, rg, hdr, offsets,
-                                                            d_num, hist);
+                                                            d_num, hist, d_max);
     if (p.n == 0) return finish();
     hipError_t e;
     if (!folded) {
         if (!p.redundant_groups)
-            k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num);
+            k_group_scan<<<1, 1024, 0, s>>>(p.nb_g, p.n, (long long)p.capacity, part, hdr, offsets, d_num, d_max);
         k_count0<<<p.nseg, kBT, 0, s>>>(p.n, p.nb_g, p.seg_groups, p.redundant_groups, (long long)p.capacity,
                                         p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0],
-                                        counts, box, part, hdr, offsets, d_num, table);
+                                        counts, box, part, hdr, offsets, d_num, table, d_max);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.capacity == 0) return finish();
@@ -1553,7 +1558,7 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     if (folded)             // also when capacity == 0: it publishes offsets and M
         k_scatter0w<kWideThreads><<<p.nseg, kWideThreads, 0, s>>>(
             p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box, offsets, hdr, table, k0,
-            v0, bstart, rg0, p.ntiles, counts, part, p.nb_g, (long long)p.capacity, d_num);
+            v0, bstart, rg0, p.ntiles, counts, part, p.nb_g, (long long)p.capacity, d_num, d_max);
     else                    // not folded: more than kMaxRedundantGroups groups, segments of 4
         k_scatter0<4><<<p.nseg, kBT, 0, s>>>(p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0],
                                              p.ncols_cap[0], box, offsets, hdr, table, k0, v0, bstart, rg0,

@@ -29,13 +29,11 @@ __device__ __forceinline__ Prep preprocess_gaussian(float4 p0, float4 p1, bool h
     ok = ok && l11 != 0.0f && l22 != 0.0f;
     float a = 0.0f, b = 0.0f, c = 0.0f;
     if (ok) {
-        const float i11 = 1.0f / l11;          // correctly rounded (no fast-math)
-        const float i22 = 1.0f / l22;
-        const float k = -((l21 * i11) * i22);
-        ok = isfinite(i11) && isfinite(i22) && isfinite(k);
-        a = i11 * kScale;
-        b = k * kScale;
-        c = i22 * kScale;
+        const float3 r = conic_rows(l11, l21, l22);
+        ok = isfinite(r.x) && isfinite(r.y) && isfinite(r.z);
+        a = r.x;
+        b = r.y;
+        c = r.z;
     }
     Prep o;
     o.cnt = 0;
@@ -190,6 +188,13 @@ __global__ __launch_bounds__(kAdamPrepThreads) void k_adam_preprocess(
         const uint32_t o1 = offsets[n] <= capacity ? o1r : o0;  // else the binning overflowed: zero gradient
         float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
         gather_half(part, o0, o1, half, gr);
+        {                                                 // sums -> gradient, with the rows of the old record
+            const float4 O = make_float4(__shfl_xor(P.x, 1, 64), __shfl_xor(P.y, 1, 64), __shfl_xor(P.z, 1, 64),
+                                         __shfl_xor(P.w, 1, 64));
+            const float4 A0 = half ? O : P, A1 = half ? P : O;
+            const float3 r = conic_rows(A0.z, A0.w, A1.x);
+            gr = o1 > o0 ? slot_grad_half(half, r.x, r.y, r.z, gr) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         const int l0 = 4 * half;
         adam_update(P.x, gr.x, Mm.x, V.x, a.lr[l0], a, c1, c2);
         adam_update(P.y, gr.y, Mm.y, V.y, a.lr[l0 + 1], a, c1, c2);

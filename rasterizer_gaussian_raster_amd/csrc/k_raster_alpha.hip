@@ -18,13 +18,14 @@
 // Gaussian, and one scalar suffix accumulator gS = sum_k g_k S_k carries the
 // colour behind it (S_k = later contributions + T_final bg_k), so
 //   dL/dalpha_j = T_j (g . c_j) - gS / (1 - alpha_j),  gS += (g . c_j) alpha_j T_j.
-// The 9 per-pixel contributions of a Gaussian are summed over the wave for 8
-// entries at a time, by one butterfly transpose-reduce (skipped when no pixel of
-// the wave is covered), and written over the entries' slots in the wave's own
-// quadrant list; each list entry then adds its four quadrant sums in quadrant
-// order, turns them into the gradients of its record (linear in the sums) and
-// stores them at its emission slot for the per-Gaussian gather.  No atomics: the
-// gradients are bitwise reproducible.
+// The 9 per-pixel contributions of a Gaussian (the slot sums of gi_device.hpp
+// with h = (dL/dalpha) alpha, and dL/dalpha w for the logit) are summed over the
+// wave for 8 entries at a time, by one butterfly transpose-reduce (skipped when
+// no pixel of the wave is covered), and written over the entries' slots in the
+// wave's own half list; each list entry then adds its two halves' sums in order
+// and stores them at its emission slot for the per-Gaussian gather, which turns
+// a Gaussian's total into its gradient.  No atomics: the gradients are bitwise
+// reproducible.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
 
@@ -323,8 +324,6 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
     }
     float gS0 = T0 * fmaf(gb0, bg[2], fmaf(gg0, bg[1], gr0 * bg[0]));
     float gS1 = T1 * fmaf(gb1, bg[2], fmaf(gg1, bg[1], gr1 * bg[0]));
-    const float k2 = 2.0f * kLn2;
-    const float is = 1.0f / kScale;
 
     for (uint32_t hi = bend0; hi > rg.x;) {
         const uint32_t lo = hi - rg.x > (uint32_t)kBatch ? hi - kBatch : rg.x;
@@ -369,14 +368,14 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
                 float dw0, dw1, aT0, aT1;
                 const float h0 = alpha_back_pixel(act0, e0, R.x, gr0, gg0, gb0, B, T0, gS0, dw0, aT0);
                 const float h1 = alpha_back_pixel(act1, e1, R.x, gr1, gg1, gb1, B, T1, gS1, dw1, aT1);
-                const float hu = u * (h0 + h1);                       // u and dx are the two pixels'
+                const float hu = u * (h0 + h1);                       // u is the two pixels'
                 const float hv0 = h0 * v0, hv1 = h1 * v1;
                 const float hv = hv0 + hv1;
                 x[8 * j + 0] = hu;
                 x[8 * j + 1] = hv;
-                x[8 * j + 2] = hu * dx;
-                x[8 * j + 3] = hv * dx;
-                x[8 * j + 4] = fmaf(hv1, dy1, hv0 * dy0);
+                x[8 * j + 2] = hu * u;
+                x[8 * j + 3] = hv * u;
+                x[8 * j + 4] = fmaf(hv1, v1, hv0 * v0);
                 x[8 * j + 5] = fmaf(gr1, aT1, gr0 * aT0);
                 x[8 * j + 6] = fmaf(gg1, aT1, gg0 * aT0);
                 x[8 * j + 7] = fmaf(gb1, aT1, gb0 * aT0);
@@ -425,17 +424,12 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
                     sl += lst[h][k].r.x;
                 }
             }
-            // e = u^2 + v^2, w = 2^-e: dL/de = -ln2 h, summed through (Hu, Hv, ...); then
-            // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22); dL/dlogit = so sum dL/dalpha w
-            const float a = own.x, b = own.y, c = own.z;
-            const float da = -k2 * s0.z, db = -k2 * s0.w, dc = -k2 * s1.x;
-            const float4 d0 = make_float4(k2 * fmaf(a, s0.x, b * s0.y), k2 * c * s0.y,
-                                          -is * fmaf(a * a, da, a * b * db), -is * (a * c * db));
-            const float4 d1 = make_float4(-is * fmaf(b * c, db, c * c * dc), s1.y, s1.z, s1.w);
+            // the pair's sums as they are (slot layout in gi_device.hpp; the gather turns a Gaussian's
+            // total into its gradient); dL/dlogit = so sum dL/dalpha w
             const uint32_t slot = eslot[tid];
             if (slot < capacity) {
-                part[2 * (size_t)slot] = d0;
-                part[2 * (size_t)slot + 1] = d1;
+                part[2 * (size_t)slot] = s0;
+                part[2 * (size_t)slot + 1] = s1;
                 part_l[slot] = own.w * sl;
             }
         }
@@ -507,6 +501,13 @@ __global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, con
     float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
     gather_half(reinterpret_cast<const float4 *>(part), o0, o1, h, gr);
     const float4 a4 = p[2 * g + h], m4 = m[2 * g + h], v4 = v[2 * g + h];
+    {                                                     // sums -> gradient, with the record's rows
+        const float4 o4 = make_float4(__shfl_xor(a4.x, 1, 64), __shfl_xor(a4.y, 1, 64), __shfl_xor(a4.z, 1, 64),
+                                      __shfl_xor(a4.w, 1, 64));
+        const float4 A0 = h ? o4 : a4, A1 = h ? a4 : o4;
+        const float3 r = conic_rows(A0.z, A0.w, A1.x);
+        gr = o1 > o0 ? slot_grad_half(h, r.x, r.y, r.z, gr) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float P[4] = {a4.x, a4.y, a4.z, a4.w};
     const float G[4] = {gr.x, gr.y, gr.z, gr.w};
     float M[4] = {m4.x, m4.y, m4.z, m4.w};

@@ -19,13 +19,17 @@
 // the tile's entries and packs their items 64 per round, one per lane, entry
 // by entry (no lane idles on a short list and no pair outside the box is
 // evaluated); after the tile's dL/dI is in LDS the waves never wait for one
-// another.  A lane walks its block's 16 pixels (dL/dI staged in
-// LDS), keeping the Gaussian's partial gradient in registers with the
-// column-invariant factors (dx, u, b dx, u^2) hoisted; the chain rule from the
-// scaled rows of L^-1 (a, b, c) to (l11, l21, l22) is applied per item, each
-// entry adds up its items in a fixed order and stores its 8 values at its
-// emission slot for the per-Gaussian gather: no atomics anywhere, so the
-// gradients are bitwise reproducible.
+// another.  A lane walks its block's 16 pixels (dL/dI staged in LDS), keeping
+// the pair's sums in registers with the column-invariant factors (dx, u, b dx,
+// u^2) hoisted.  The sums are taken in the Gaussian's whitened frame (u, v):
+// with h = (dL/dw) w, the slot holds (sum h u, sum h v, sum h u^2, sum h u v,
+// sum h v^2) and the three colour sums sum g_k w -- the gradient of any
+// parameterisation of the covariance is a linear map of these, applied once per
+// Gaussian after the gather (slot_grad_cholesky; the rotation-scale form's map
+// is orthogonal up to scale factors, so it adds no cancellation).  Each entry
+// adds up its items in a fixed order and stores its 8 values at its emission
+// slot for the per-Gaussian gather: no atomics anywhere, so the gradients are
+// bitwise reproducible.
 #include "gi_device.hpp"
 #include "gi_launch.hpp"
 
@@ -428,7 +432,6 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int x0 = tx * kTile, y0 = ty * kTile;
     const float k2 = 2.0f * kLn2;
-    const float is = 1.0f / kScale;
     for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
         uint32_t e0, ne;
         bwd_share(rg, base, e0, ne);
@@ -486,7 +489,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 float dy[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
-                float Hu = 0.f, Hv = 0.f, Hudx = 0.f, Hvdx = 0.f, Hvdy = 0.f, Cr = 0.f, Cg = 0.f, Cb = 0.f;
+                float Hu = 0.f, Hv = 0.f, Muu = 0.f, Muv = 0.f, Mvv = 0.f, Cr = 0.f, Cg = 0.f, Cb = 0.f;
                 float Ax = 0.f, Ay = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -495,7 +498,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                     const float tb = A.w * dx;
                     const float uu = u * u;
                     const float au = A.z * u;
-                    float ch = 0.f, chv = 0.f;
+                    float ch = 0.f, chv = 0.f, chvv = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         const float4 gv = gp[blk * kGpStride + rr * 4 + c];
@@ -509,32 +512,31 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                         const float hv = h * v;
                         ch += h;
                         chv += hv;
-                        Hvdy = fmaf(hv, dy[rr], Hvdy);
+                        chvv = fmaf(hv, v, chvv);
                         if constexpr (ABS) {
                             Ax += fabsf(h * fmaf(A.w, v, au));
                             Ay += fabsf(hv);
                         }
                     }
                     Hu = fmaf(u, ch, Hu);
-                    Hudx = fmaf(u * dx, ch, Hudx);
+                    Muu = fmaf(uu, ch, Muu);
+                    Muv = fmaf(u, chv, Muv);
                     Hv += chv;
-                    Hvdx = fmaf(dx, chv, Hvdx);
+                    Mvv += chvv;
                 }
-                // e = u^2 + v^2, w = 2^-e: dL/de = -ln2 h, summed through (Hu, Hv, ...); then
-                // a = S/l11, b = -S l21/(l11 l22), c = S/l22 -> (l11, l21, l22).
-                const float a = A.z, b = A.w, c = B.x;
-                const float da = -k2 * Hudx, db = -k2 * Hvdx, dc = -k2 * Hvdy;
-                acc0.x += k2 * fmaf(a, Hu, b * Hv);
-                acc0.y += k2 * c * Hv;
-                acc0.z += -is * fmaf(a * a, da, a * b * db);
-                acc0.w += -is * (a * c * db);
-                acc1.x += -is * fmaf(b * c, db, c * c * dc);
+                // the item's share of the pair's sums (slot_grad_cholesky turns a Gaussian's total
+                // into its gradient)
+                acc0.x += Hu;
+                acc0.y += Hv;
+                acc0.z += Muu;
+                acc0.w += Muv;
+                acc1.x += Mvv;
                 acc1.y += Cr;
                 acc1.z += Cg;
                 acc1.w += Cb;
                 if constexpr (ABS) {
                     accA.x += k2 * Ax;
-                    accA.y += k2 * fabsf(c) * Ay;
+                    accA.y += k2 * fabsf(B.x) * Ay;
                 }
             }
         }
@@ -677,7 +679,8 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
 // One thread per Gaussian: its pairs' partial gradients sit at offsets[g] ..
 // offsets[g+1] in emission order; add them in that order (reproducible).
 __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const uint32_t *__restrict__ offsets,
-                                                     uint32_t capacity, const float4 *__restrict__ part,
+                                                     uint32_t capacity, const float4 *__restrict__ records,
+                                                     const float4 *__restrict__ part,
                                                      const float *__restrict__ part_l,
                                                      const float4 *__restrict__ part_bg,
                                                      float *__restrict__ dparams, float *__restrict__ dlogit,
@@ -718,11 +721,14 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
     }
     float4 *d = reinterpret_cast<float4 *>(dparams) + 2 * (size_t)g;
     float4 d0 = d[0], d1 = d[1];
+    const float4 rp = records[2 * (size_t)g], rq = records[2 * (size_t)g + 1];
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
     gather_slots(part, o0, o1, a, b);
     float l = 0.f;
     if (part_l)
         for (uint32_t q = o0; q < o1; ++q) l += part_l[q];
+    a = slot_grad_half(0, rp.z, rp.w, rq.x, a);
+    b = slot_grad_half(1, rp.z, rp.w, rq.x, b);
     d0.x += a.x; d0.y += a.y; d0.z += a.z; d0.w += a.w;
     d1.x += b.x; d1.y += b.y; d1.z += b.z; d1.w += b.w;
     d[0] = d0;
@@ -735,8 +741,10 @@ __global__ __launch_bounds__(256) void k_grad_gather(int n, int ntiles, const ui
 // the optimizer in one pass, no gradient array.  Eight lanes per Gaussian, lane
 // j on parameter j: a Gaussian's parameters, moments and each slot are 32
 // contiguous bytes read by its 8 lanes together, and up to 8 slots are loaded
-// at once.  Each parameter's slots are added in ascending order, as in
-// gather_slots (same bits as a gather followed by the Adam step).
+// at once.  Each slot entry is added in ascending order, as in gather_slots,
+// and the sums are turned into the gradient by slot_grad_entry with the
+// record's rows formed from the parameters (same bits as a gather followed by
+// the Adam step).
 // With `loss`, one more workgroup (the last) reduces the loss partials of the
 // raster pass into it.
 __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__restrict__ offsets, uint32_t capacity,
@@ -749,23 +757,28 @@ __global__ __launch_bounds__(256) void k_adam_pairs(int n, const uint32_t *__res
         loss_reduce_block(nparts, loss_part, inv_count, loss, sm);
         return;
     }
-    const int i = blockIdx.x * 256 + threadIdx.x;     // parameter i % 8 of Gaussian i / 8
-    const int g = i >> 3, j = i & 7;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // parameter i % 8 of Gaussian i / 8
+    const int g = (int)(i >> 3), j = (int)(i & 7);
+    // the whole group of 8 lanes takes the same branch (the exchange below stays within it)
     if (g >= n) return;
     float c1, c2;
     adam_step_bias(a, c1, c2);
     float P = p[i], Mo = m[i], V = v[i];
     const uint32_t o0 = offsets[g], o1r = offsets[g + 1];
     const uint32_t o1 = offsets[n] <= capacity ? o1r : o0;   // else the binning overflowed: zero gradient
-    float G = 0.0f;
+    float S = 0.0f;
     for (uint32_t q = o0; q < o1; q += 8) {
         float u[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) u[k] = part[8 * (size_t)min(q + (uint32_t)k, o1 - 1u) + j];   // repeats not added
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (q + (uint32_t)k < o1) G += u[k];
+            if (q + (uint32_t)k < o1) S += u[k];
     }
+    const int lane = threadIdx.x & 63, grp = lane & ~7;
+    const float3 r = conic_rows(__shfl(P, grp + 2, 64), __shfl(P, grp + 3, 64), __shfl(P, grp + 4, 64));
+    const float Sn = __shfl(S, min(lane + 1, grp + 7), 64);
+    const float G = o1 > o0 ? slot_grad_entry(j, r.x, r.y, r.z, S, Sn) : 0.0f;   // no pairs: culled, or none
     float lr = a.lr[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) lr = j == k ? a.lr[k] : lr;
@@ -825,15 +838,15 @@ hipError_t launch_adam_pairs(int n, int W, int H, const uint32_t *offsets, int64
 }
 
 hipError_t launch_grad_gather(int n, int W, int H, int ntiles, const uint32_t *offsets, int64_t capacity,
-                              const void *ws, int alpha, float *dparams, float *dlogit, float *dbackground,
-                              hipStream_t s, float *dabs) {
+                              const void *ws, const float *records, int alpha, float *dparams, float *dlogit,
+                              float *dbackground, hipStream_t s, float *dabs) {
     if (n == 0 && !(alpha && dbackground)) return hipSuccess;
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     const char *w = static_cast<const char *>(ws);
     const int nb = (n + 255) / 256;
     k_grad_gather<<<nb > 0 ? nb : 1, 256, 0, s>>>(
-        n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(w + p.off_part),
-        alpha ? reinterpret_cast<const float *>(w + p.off_logit) : nullptr,
+        n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(records),
+        reinterpret_cast<const float4 *>(w + p.off_part), alpha ? reinterpret_cast<const float *>(w + p.off_logit) : nullptr,
         reinterpret_cast<const float4 *>(w + p.off_bg), dparams, alpha ? dlogit : nullptr,
         alpha ? dbackground : nullptr, reinterpret_cast<const float2 *>(w + p.off_abs),
         reinterpret_cast<float2 *>(dabs));

@@ -38,7 +38,7 @@ def desc(width: int, height: int, mode: int = MODE_SUM) -> gi_desc:
     return gi_desc(int(width), int(height), int(mode), 0)
 
 
-FIT_PREPARED, FIT_ORDER, FIT_USE_ORDER, FIT_NO_UPDATE = 1, 2, 4, 8
+FIT_PREPARED, FIT_ORDER, FIT_USE_ORDER, FIT_NO_UPDATE, FIT_TRACK_MAX = 1, 2, 4, 8, 16
 
 
 class gi_fit_buffers(ctypes.Structure):
@@ -87,6 +87,7 @@ def load():
         "gi_render_bwd_absgrad": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, sz, P], i32),
         "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, P], i32),
         "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
+        "gi_grad_gather": ([D, i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i64, P, sz, P, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
         "gi_loss_reduce": ([i64, P, i64, P, P], i32),
         "gi_adam_step_pairs": ([D, i64, P, i64, P, sz, P, P, P, P, f64, f64, f64, i32, P, P, i64, P, P], i32),
@@ -258,6 +259,13 @@ def gi_params_to_cholesky_grad(kind, n, params, fx, fy, dout, dparams, accumulat
     _check(load().gi_params_to_cholesky_grad(int(kind), int(n), _ptr(params), float(fx), float(fy), _ptr(dout),
                                              _ptr(dparams), 1 if accumulate else 0, _stream(stream)),
            "gi_params_to_cholesky_grad")
+
+
+def gi_grad_gather(d, kind, n, params, fx, fy, records, offsets, capacity, workspace, dparams, stream=None):
+    _check(load().gi_grad_gather(ctypes.byref(d), int(kind), int(n), _ptr(params), float(fx), float(fy),
+                                 _ptr(records), _ptr(offsets), int(capacity), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _ptr(dparams), _stream(stream)),
+           "gi_grad_gather")
 
 
 def gi_render_bwd_absgrad(d, n, records, pixbox, offsets, ranges, vals, capacity, dL_dimage, dparams, dabs,

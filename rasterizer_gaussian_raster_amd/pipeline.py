@@ -35,6 +35,11 @@ DEFAULT_LR = (0.05, 0.05, 0.01, 0.01, 0.01, 0.005, 0.005, 0.005)
 ORDER_MAX_TILES = 8192
 ORDER_EVERY = 16
 
+# The fitters read the pair count back (one host wait) every CAPACITY_EVERY steps and grow the pair
+# buffers when it comes within 80 % of capacity: a binning that overflows renders nothing and
+# gives a zero gradient for that step, so growth must come before the count gets there.
+CAPACITY_EVERY = 16
+
 
 class Raster:
     """Device buffers for one (W, H, n, mode) problem."""
@@ -52,7 +57,7 @@ class Raster:
         self.counts = torch.empty(max(self.n, 1), dtype=torch.int32, device=dev)
         self.offsets = torch.empty(self.n + 1, dtype=torch.int32, device=dev)
         self.ranges = torch.empty((max(self.T, 1), 2), dtype=torch.int32, device=dev)
-        self.d_num = torch.empty(1, dtype=torch.int32, device=dev)
+        self.d_num = torch.zeros(2, dtype=torch.int32, device=dev)   # M of the last binning; running max
         self.image = torch.empty((3, self.H, self.W), dtype=torch.float32, device=dev)
         self.t_final = torch.empty((self.H, self.W), dtype=torch.float32, device=dev) if alpha else None
         self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev) if alpha else None
@@ -114,7 +119,7 @@ class Raster:
         except gi.GiError as e:
             if e.status != gi.GI_ERR_CAPACITY:
                 raise
-            M = int(self.d_num.cpu().view(torch.int32).item()) & 0xFFFFFFFF
+            M = int(self.d_num[0].item()) & 0xFFFFFFFF
             self.set_capacity(int(M * slack) + 1024)
             M = self._bin_call(True, stream, tile_order, None, None)     # preprocess outputs are in place
         self.M = M
@@ -185,7 +190,7 @@ class Raster:
             except gi.GiError as e:
                 if e.status != gi.GI_ERR_CAPACITY:
                     raise
-                M = int(self.d_num.cpu().view(torch.int32).item()) & 0xFFFFFFFF
+                M = int(self.d_num[0].item()) & 0xFFFFFFFF
                 self.set_capacity(int(M * 1.25) + 1024)
                 self.M = call(True, flags)
         if flags & gi.FIT_ORDER:
@@ -207,9 +212,11 @@ def cholesky_params(params, kind=gi.PARAMS_RS, fx=1.0, fy=1.0, out=None, stream=
 
 class FitterRS:
     """Fits rotation-scale Gaussians (mux, muy, sx, sy, theta, cr, cg, cb) with L2 loss and Adam
-    (sum mode).  A step: gi_params_to_cholesky, preprocess + binning, the fused forward / L2 /
-    backward raster (gi_render_fwd_bwd_l2), and gi_adam_step_pairs_rs (gather of the per-pair
-    gradients, chain rule, Adam on the rotation-scale parameters, and the loss)."""
+    (sum mode).  A step: gi_fit_step_sum with GI_FIT_NO_UPDATE on their Cholesky form (preprocess,
+    binning, the fused forward / L2 / backward raster, leaving the pair slots in the workspace),
+    then gi_adam_step_pairs_rs (gather of the slots, their map to the rotation-scale gradient,
+    Adam on the rotation-scale parameters, the loss, and the Cholesky form for the next step).
+    Every CAPACITY_EVERY steps the pair count is read back and the buffers grown if needed."""
 
     def __init__(self, target, params_rs, lr=DEFAULT_LR_RS, betas=(0.9, 0.999), eps=1e-8, capacity_slack=1.5):
         self.target = target.contiguous()
@@ -234,13 +241,19 @@ class FitterRS:
         self.raster.set_capacity(int(M * capacity_slack) + 4096)
 
     def check_capacity(self):
-        M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
+        """Host wait: grow the pair buffers when the last binning came near (or over) capacity."""
+        M = int(self.raster.d_num[0].item()) & 0xFFFFFFFF
         if M > 0.8 * self.raster.capacity:
             self.raster.set_capacity(int(M * self.slack) + 4096)
             return True
         return False
 
     def step(self):
+        self._step()
+        if self.step_count % CAPACITY_EVERY == 0:
+            self.check_capacity()
+
+    def _step(self):
         """The Cholesky form of the current params is in self.chol: written by the previous step's
         gi_adam_step_pairs_rs (or by __init__ / step_separate).  Binning and the fused raster run as
         gi_fit_step_sum with GI_FIT_NO_UPDATE (so the raster's workgroups finish the sort where the
@@ -267,15 +280,16 @@ class FitterRS:
                                  loss_count=3 * r.W * r.H, d_loss=self.loss, chol_out=self.chol)
 
     def step_separate(self):
-        """The same step from the separate calls (forward + L2, backward with the gather, the chain
-        rule, Adam): a cross-check of the fused one."""
+        """The same step from the separate calls (forward + L2, backward to the pair slots, the gather
+        to the rotation-scale gradient, Adam): a cross-check of the fused one."""
         r, n = self.raster, self.n
         cholesky_params(self.params, out=self.chol)
         r.bin(sync=False, order=self.step_count % ORDER_EVERY == 0, params=self.chol)
         r.forward_l2(self.target, self.dL)
-        self.gchol.zero_()
-        r.backward(self.dL, self.gchol, d_loss=self.loss)
-        gi.gi_params_to_cholesky_grad(gi.PARAMS_RS, n, self.params, 1.0, 1.0, self.gchol, self.grad)
+        r.backward(self.dL, None, d_loss=self.loss)
+        self.grad.zero_()
+        gi.gi_grad_gather(r.desc, gi.PARAMS_RS, n, self.params, 1.0, 1.0, r.records, r.offsets, r.capacity,
+                          r.bwd_ws, self.grad)
         self.step_count += 1
         b1, b2 = self.betas
         gi.gi_adam_step(n, 8, self.params, self.grad, self.m, self.v, self.lr, b1, b2, self.eps, self.step_count, 0)
@@ -319,6 +333,7 @@ class Fitter:
         self.d_step = None
         self.slack = capacity_slack
         self.prepared = False           # the last fit step left the set-up of the current params
+        self.track_max = False          # steps also raise raster.d_num[1] to their pair count
         self._fb = None                 # gi_fit_buffers over the current buffers
         self._hp = gi.adam_hparams(self.lr, betas[0], betas[1], eps)
         # size the tile-pair buffers once, with room for the Gaussians to spread
@@ -331,7 +346,7 @@ class Fitter:
 
     def check_capacity(self):
         """Host wait: grow the pair buffers when the last binning came near (or over) capacity."""
-        M = int(self.raster.d_num.cpu().item()) & 0xFFFFFFFF
+        M = int(self.raster.d_num[0].item()) & 0xFFFFFFFF
         if M > 0.8 * self.raster.capacity:
             self.graphs = None              # the captured graphs hold the old buffers: capture() again
             self.prepared = False           # the new bin workspace holds no set-up
@@ -352,6 +367,8 @@ class Fitter:
                                       r.records, r.pixbox, r.counts, r.offsets, r.keys, r.vals, r.ranges, r.order,
                                       r.d_num, r.capacity, r.ws, r.bwd_ws)
         flags = gi.FIT_PREPARED if self.prepared else 0
+        if self.track_max:
+            flags |= gi.FIT_TRACK_MAX
         if r.order is not None:
             if r.has_order:                 # written by an earlier call (any permutation is valid)
                 flags |= gi.FIT_USE_ORDER
@@ -389,7 +406,16 @@ class Fitter:
 
     def step(self):
         """One training step.  In sum mode the raster's records / boxes describe the updated parameters
-        afterwards and its tile ranges are cleared (the next step's binning starts from them)."""
+        afterwards and its tile ranges are cleared (the next step's binning starts from them).  Every
+        CAPACITY_EVERY steps the pair count is read back and the buffers grown if it nears capacity
+        (captured graphs are then recorded again)."""
+        self._step()
+        if self.step_count % CAPACITY_EVERY == 0:
+            had_graphs = self.graphs is not None
+            if self.check_capacity() and had_graphs:
+                self.capture()
+
+    def _step(self):
         if self.graphs is not None:
             self.graphs[self.step_count % ORDER_EVERY == 0].replay()
             self.step_count += 1

@@ -336,3 +336,42 @@ def test_render_image_equals_the_two_calls(name):
     assert outs[0][0] == outs[1][0]
     for k, (a, b) in enumerate(zip(outs[0][1], outs[1][1])):
         np.testing.assert_array_equal(a, b, err_msg=f"output {k}")
+
+
+def test_fit_step_tracks_the_largest_pair_count():
+    """GI_FIT_TRACK_MAX: d_num[1] ends as the largest M of the steps since it was cleared, so one read
+    after asynchronous steps shows an overflow (a capacity below M) that d_num[0] alone would hide
+    once a later binning fits again."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    W, H, p, tgt = _fused_case("kodak_768x512_50k")
+    n = p.shape[0]
+    T = dev(tgt)
+    lr = [0.5, 0.5, 0.3, 0.3, 0.3, 0.005, 0.005, 0.005]      # large steps: M moves from step to step
+    P = dev(p)
+    Mo, V = torch.zeros_like(P), torch.zeros_like(P)
+    r = Raster(W, H, n)
+    M0 = r.bin(sync=True, params=P)
+    r.set_capacity(int(M0 * 2) + 4096)
+    r.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(r.desc, n, r.capacity), dtype=torch.uint8,
+                           device="cuda")
+    loss = torch.zeros(1, device="cuda")
+    fb = gi.fit_buffers(P, Mo, V, T, r.image, r.loss_partials, loss, r.records, r.pixbox, r.counts, r.offsets,
+                        r.keys, r.vals, r.ranges, r.order, r.d_num, r.capacity, r.ws, r.bwd_ws)
+    hp = gi.adam_hparams(lr, 0.9, 0.999, 1e-8)
+    r.d_num.zero_()
+    seen = []
+    for step in range(1, 7):
+        gi.gi_fit_step_sum(r.desc, n, fb, hp, step, flags=gi.FIT_TRACK_MAX | (gi.FIT_PREPARED if step > 1 else 0))
+        torch.cuda.synchronize()
+        d = u32(r.d_num)
+        seen.append(int(d[0]))
+        assert int(d[1]) == max(seen), (seen, d)
+    print(f"pair counts per step: {seen}")
+    assert len(set(seen)) > 1
+    # without the flag d_num[1] is left alone
+    before = int(u32(r.d_num)[1])
+    gi.gi_fit_step_sum(r.desc, n, fb, hp, 7, flags=gi.FIT_PREPARED)
+    torch.cuda.synchronize()
+    assert int(u32(r.d_num)[1]) == before

@@ -618,28 +618,29 @@ def test_rs_grad_finite_differences(fx, fy):
     np.testing.assert_allclose(d, num, rtol=1e-6, atol=1e-7)
 
 
-def test_rs_chain_scale_is_the_propagated_cholesky_scale():
-    """acond_chain = |J|^T C': C' the Cholesky-form oracle's running-error scale of the factor of
-    D Sigma D, J the Jacobian of that factor (numpy's Cholesky, central differences)."""
+def test_rs_cholesky_grad_is_the_jacobian_transpose():
+    """oracle.rs_cholesky_grad = J^T dout with J the Jacobian of numpy's Cholesky factor of
+    D Sigma D (central differences), for signed scales and several angles; the scale is
+    |J|^T |dout|; a zero scale gives zeros."""
     import oracle
-    W, H, fx, fy = 24, 20, 1.25, 0.8
-    p = np.array([[9.3, 13.1, 4.5, 0.9, 1.2, 0.7, -0.3, 0.4]])
-    G = np.zeros((3, H, W))
-    G[:, 11, 12] = (0.5, -1.0, 2.0)
-    G[:, 9, 10] = (1.5, 0.2, -0.7)
-    _, _, _, chain = oracle.grad_sum_rs(W, H, p, G, fx, fy, with_chain=True)
-    chol = _rs_to_cholesky_numpy(p, fx, fy)
-    _, _, Cc = oracle.grad_sum(W, H, chol, G, with_cond=True)
-    J = np.zeros((3, 3))
-    for k in range(3):
-        h = 1e-6
-        a, b = p.copy(), p.copy()
-        a[0, 2 + k] += h
-        b[0, 2 + k] -= h
-        J[:, k] = (_rs_to_cholesky_numpy(a, fx, fy)[0, 2:5] - _rs_to_cholesky_numpy(b, fx, fy)[0, 2:5]) / (2 * h)
-    want = np.abs(J).T @ Cc[0, 2:5]
-    np.testing.assert_allclose(chain[0, 2:5], want, rtol=1e-6)
-    np.testing.assert_allclose(chain[0, :2], [fx * Cc[0, 0], fy * Cc[0, 1]], rtol=1e-12)
+    fx, fy = 1.25, 0.8
+    p = np.array([[9.3, 13.1, 4.5, 0.9, 1.2, 0.7, -0.3, 0.4],
+                  [2.0, 3.0, -2.5, 6.0, -0.4, 0.1, 0.2, 0.3],
+                  [5.0, 1.0, 0.6, -7.5, 2.9, -1.0, 0.5, 0.0],
+                  [4.0, 4.0, 0.0, 2.0, 0.3, 1.0, 1.0, 1.0]])
+    dout = np.random.default_rng(708).normal(size=p.shape)
+    got, sc = oracle.rs_cholesky_grad(p, dout, fx, fy)
+    for g in range(3):
+        J = np.zeros((8, 8))
+        for k in range(8):
+            h = 1e-6 * max(1.0, abs(p[g, k]))
+            a, b = p[g:g + 1].copy(), p[g:g + 1].copy()
+            a[0, k] += h
+            b[0, k] -= h
+            J[:, k] = (_rs_to_cholesky_numpy(a, fx, fy)[0] - _rs_to_cholesky_numpy(b, fx, fy)[0]) / (2 * h)
+        np.testing.assert_allclose(got[g], J.T @ dout[g], rtol=1e-6, atol=1e-8)
+        np.testing.assert_allclose(sc[g], np.abs(J).T @ np.abs(dout[g]), rtol=1e-6, atol=1e-8)
+    assert np.all(got[3] == 0) and np.all(sc[3] == 0)
 
 
 # --------------------------------------------------------------------------------------------
