@@ -65,7 +65,8 @@ typedef enum {
     GI_OK = 0,
     GI_ERR_INVALID_ARG = 1,
     GI_ERR_HIP = 2,
-    GI_ERR_CAPACITY = 3
+    GI_ERR_CAPACITY = 3,
+    GI_ERR_UNSUPPORTED = 4   /* a size beyond a fixed limit of the call (gi_render_image_noalloc) */
 } gi_status;
 
 typedef enum {
@@ -230,6 +231,31 @@ gi_status gi_render_image(const gi_desc *desc, int64_t n, const float *params, c
                           uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
                           uint32_t flags, int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace,
                           size_t workspace_bytes, float *image, float *t_final, uint32_t *last, void *stream);
+
+/*
+ * gi_render_image_noalloc -- gi_render_image without a workspace argument, for
+ *   callers that cannot allocate device memory (code under HIP graph capture,
+ *   tight serving loops, harnesses that forbid allocation).  The bin workspace
+ *   is a fixed device array inside the library, 64 MiB, of which each GPU the
+ *   library runs on holds its own copy until the process ends; the call itself
+ *   allocates and frees nothing.  Every call on one GPU uses that GPU's copy:
+ *   calls that may overlap on one GPU (different streams, or different host
+ *   threads, without ordering between them) race and give wrong results; calls
+ *   ordered on one stream are fine.  The array needs no clearing (every call
+ *   writes what it reads).
+ *   A problem whose bin workspace (gi_bin_sort_workspace_bytes(desc, n,
+ *   capacity)) exceeds gi_render_image_noalloc_max_bytes() returns
+ *   GI_ERR_UNSUPPORTED before anything is enqueued (e.g. 2048x2048 with 500,000
+ *   Gaussians fits up to about 8 million pairs of capacity).  Otherwise the
+ *   arguments, results and errors are gi_render_image's, bit for bit.
+ */
+size_t gi_render_image_noalloc_max_bytes(void);
+gi_status gi_render_image_noalloc(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                                  const float *background, float *records, float *opacity, uint16_t *pixbox,
+                                  uint32_t *counts, uint32_t *offsets, uint32_t *keys, uint32_t *vals,
+                                  uint32_t *ranges, uint32_t *tile_order, uint32_t flags, int64_t capacity,
+                                  uint32_t *d_num, int64_t *h_num, float *image, float *t_final, uint32_t *last,
+                                  void *stream);
 
 /*
  * gi_render_fwd_l2 -- gi_render_fwd (sum mode) fused with the L2 loss of

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "../../include/gi.h"
 #include "gi_launch.hpp"
@@ -33,6 +34,7 @@ const char *gi_status_string(gi_status s) {
     case GI_ERR_INVALID_ARG: return "GI_ERR_INVALID_ARG";
     case GI_ERR_HIP: return "GI_ERR_HIP";
     case GI_ERR_CAPACITY: return "GI_ERR_CAPACITY";
+    case GI_ERR_UNSUPPORTED: return "GI_ERR_UNSUPPORTED";
     default: return "GI_UNKNOWN_STATUS";
     }
 }
@@ -130,21 +132,32 @@ gi_status gi_preprocess_bin_sort(const gi_desc *desc, int64_t n, const float *pa
     return h_num ? read_total(workspace, capacity, h_num, s) : GI_OK;
 }
 
-gi_status gi_render_image(const gi_desc *desc, int64_t n, const float *params, const float *logit,
-                          const float *background, float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
-                          uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
-                          uint32_t flags, int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace,
-                          size_t workspace_bytes, float *image, float *t_final, uint32_t *last, void *stream) {
-    if (!preprocess_args_ok(desc, n, params, logit, records, opacity, pixbox, counts) ||
-        !bin_args_ok(desc, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
-                     workspace_bytes))
-        return GI_ERR_INVALID_ARG;
-    if ((flags & ~(uint32_t)(GI_FIT_ORDER | GI_FIT_USE_ORDER)) != 0u) return GI_ERR_INVALID_ARG;
-    if ((flags & (GI_FIT_ORDER | GI_FIT_USE_ORDER)) && !tile_order) return GI_ERR_INVALID_ARG;
-    if (!image || !aligned16(image)) return GI_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// gi_render_image's arguments other than the workspace.
+bool render_image_args_ok(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                          const float *background, const float *records, const float *opacity,
+                          const uint16_t *pixbox, const uint32_t *counts, const uint32_t *tile_order, uint32_t flags,
+                          const float *image, const float *t_final, const uint32_t *last) {
+    if (!preprocess_args_ok(desc, n, params, logit, records, opacity, pixbox, counts)) return false;
+    if ((flags & ~(uint32_t)(GI_FIT_ORDER | GI_FIT_USE_ORDER)) != 0u) return false;
+    if ((flags & (GI_FIT_ORDER | GI_FIT_USE_ORDER)) && !tile_order) return false;
+    if (!image || !aligned16(image)) return false;
     const bool alpha = desc->mode == GI_MODE_ALPHA;
-    if (alpha && (!background || !t_final || !last)) return GI_ERR_INVALID_ARG;
-    if (!alpha && (background || t_final || last)) return GI_ERR_INVALID_ARG;
+    if (alpha && (!background || !t_final || !last)) return false;
+    if (!alpha && (background || t_final || last)) return false;
+    return true;
+}
+
+// The work of gi_render_image on checked arguments, with the bin workspace at `workspace`.
+gi_status render_image_run(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                           const float *background, float *records, float *opacity, uint16_t *pixbox,
+                           uint32_t *counts, uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges,
+                           uint32_t *tile_order, uint32_t flags, int64_t capacity, uint32_t *d_num, int64_t *h_num,
+                           void *workspace, float *image, float *t_final, uint32_t *last, void *stream) {
+    const bool alpha = desc->mode == GI_MODE_ALPHA;
     const int W = desc->width, H = desc->height;
     const gi::BinPlan plan = gi::make_bin_plan((int)n, W, H, capacity);
     hipStream_t s = as_stream(stream);
@@ -171,6 +184,73 @@ gi_status gi_render_image(const gi_desc *desc, int64_t n, const float *params, c
     if (e == hipSuccess && bucket && (flags & GI_FIT_ORDER)) e = gi::launch_tile_order(plan, ranges, tile_order, s);
     if (e != hipSuccess) return GI_ERR_HIP;
     return h_num ? read_total(workspace, capacity, h_num, s) : GI_OK;
+}
+
+// The bin workspace of gi_render_image_noalloc: one file-scope device array, a copy of which every
+// GPU the library runs on holds until the process ends.  Its name is a host-side stand-in in host
+// code; the address of each device's copy comes from hipGetSymbolAddress, taken once per device
+// (with that device current) and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+gi_status scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GI_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GI_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return GI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gi_status gi_render_image(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                          const float *background, float *records, float *opacity, uint16_t *pixbox, uint32_t *counts,
+                          uint32_t *offsets, uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order,
+                          uint32_t flags, int64_t capacity, uint32_t *d_num, int64_t *h_num, void *workspace,
+                          size_t workspace_bytes, float *image, float *t_final, uint32_t *last, void *stream) {
+    if (!render_image_args_ok(desc, n, params, logit, background, records, opacity, pixbox, counts, tile_order, flags,
+                              image, t_final, last) ||
+        !bin_args_ok(desc, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, workspace,
+                     workspace_bytes))
+        return GI_ERR_INVALID_ARG;
+    return render_image_run(desc, n, params, logit, background, records, opacity, pixbox, counts, offsets, keys, vals,
+                            ranges, tile_order, flags, capacity, d_num, h_num, workspace, image, t_final, last,
+                            stream);
+}
+
+size_t gi_render_image_noalloc_max_bytes(void) { return kScratchBytes; }
+
+gi_status gi_render_image_noalloc(const gi_desc *desc, int64_t n, const float *params, const float *logit,
+                                  const float *background, float *records, float *opacity, uint16_t *pixbox,
+                                  uint32_t *counts, uint32_t *offsets, uint32_t *keys, uint32_t *vals,
+                                  uint32_t *ranges, uint32_t *tile_order, uint32_t flags, int64_t capacity,
+                                  uint32_t *d_num, int64_t *h_num, float *image, float *t_final, uint32_t *last,
+                                  void *stream) {
+    if (!render_image_args_ok(desc, n, params, logit, background, records, opacity, pixbox, counts, tile_order, flags,
+                              image, t_final, last))
+        return GI_ERR_INVALID_ARG;
+    if (capacity < 0 || capacity >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (gi::make_bin_plan((int)n, desc->width, desc->height, capacity).bytes > kScratchBytes)
+        return GI_ERR_UNSUPPORTED;                        // beyond the fixed scratch: checked before any device call
+    void *ws = nullptr;
+    const gi_status st = scratch_address(&ws);
+    if (st != GI_OK) return st;
+    if (!bin_args_ok(desc, n, pixbox, counts, offsets, keys, vals, ranges, capacity, d_num, ws, kScratchBytes))
+        return GI_ERR_INVALID_ARG;
+    return render_image_run(desc, n, params, logit, background, records, opacity, pixbox, counts, offsets, keys, vals,
+                            ranges, tile_order, flags, capacity, d_num, h_num, ws, image, t_final, last, stream);
 }
 
 gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, const float *opacity,

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgi.so")
 
-GI_OK, GI_ERR_INVALID_ARG, GI_ERR_HIP, GI_ERR_CAPACITY = 0, 1, 2, 3
+GI_OK, GI_ERR_INVALID_ARG, GI_ERR_HIP, GI_ERR_CAPACITY, GI_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 MODE_SUM, MODE_ALPHA = 0, 1
 PARAMS_CHOLESKY, PARAMS_RS = 0, 1
 TILE = 16
@@ -95,6 +95,9 @@ def load():
         "gi_render_fwd_bwd_l2": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P], i32),
         "gi_render_image": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, i64, P, P, P, sz, P, P, P,
                              P], i32),
+        "gi_render_image_noalloc_max_bytes": ([], sz),
+        "gi_render_image_noalloc": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, i64, P, P, P, P, P,
+                                     P], i32),
         "gi_fit_step_sum": ([D, i64, ctypes.POINTER(gi_fit_buffers), ctypes.POINTER(gi_adam_hparams), i32, P,
                              ctypes.c_uint32, P], i32),
     }
@@ -195,6 +198,21 @@ def gi_render_image(d, n, params, logit, background, records, opacity, pixbox, c
                                 workspace.numel() * workspace.element_size(), _ptr(image), _ptr(t_final), _ptr(last),
                                 _stream(stream))
     _check(st, "gi_render_image")
+    return int(h.value) if sync_count else None
+
+
+def gi_render_image_noalloc(d, n, params, logit, background, records, opacity, pixbox, counts, offsets, keys, vals,
+                            ranges, tile_order, flags, capacity, d_num, image, t_final=None, last=None,
+                            sync_count=False, stream=None):
+    """gi_render_image with the library's fixed bin workspace (no workspace argument).  Returns M when
+    sync_count, else None."""
+    h = ctypes.c_int64(-1)
+    st = load().gi_render_image_noalloc(ctypes.byref(d), int(n), _ptr(params), _ptr(logit), _ptr(background),
+                                        _ptr(records), _ptr(opacity), _ptr(pixbox), _ptr(counts), _ptr(offsets),
+                                        _ptr(keys), _ptr(vals), _ptr(ranges), _ptr(tile_order), int(flags),
+                                        int(capacity), _ptr(d_num), ctypes.byref(h) if sync_count else None,
+                                        _ptr(image), _ptr(t_final), _ptr(last), _stream(stream))
+    _check(st, "gi_render_image_noalloc")
     return int(h.value) if sync_count else None
 
 
