@@ -82,6 +82,17 @@ def grad_error(gpu, ref, aabs):
     return float(rel.max()) if rel.size else 0.0
 
 
+def grad_error_plain(gpu, ref, aabs, cond, factor=10.0):
+    """The plain metric |g_gpu - g_ref| / A (A = sum of |contribution|) over the entries where the
+    running-error scale C is at most factor * A (no contribution there is much of a cancellation),
+    and the number of such entries."""
+    gpu = np.asarray(gpu, np.float64)
+    m = (aabs > 0) & (cond <= factor * aabs)
+    if not np.any(m):
+        return 0.0, 0
+    return float((np.abs(gpu[m] - ref[m]) / aabs[m]).max()), int(m.sum())
+
+
 def sample_pixels(W, H, n_random, n_tiles, seed):
     """n_random random pixels plus every pixel of n_tiles random tiles, as [P,2] (row, col)."""
     rng = np.random.default_rng(seed)

@@ -177,3 +177,43 @@ def test_bin_repeatable():
     _, b = gpu_bin(300, 200, p)
     for k in ["keys", "vals", "ranges", "offsets"]:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("capacity", [None, 1 << 20])
+def test_bin_lsd_more_than_16_key_bits(fused, capacity):
+    """A grid of more than 65,536 tiles (17 key bits): the LSD passes (k_count / k_scatter, then
+    k_ranges), with small and larger sort blocks; bit-exact against the oracle, and the image of
+    that binning against the oracle on sampled pixels."""
+    require_gpu()
+    import oracle
+    from gpu_util import image_error, sample_pixels
+    W, H, n = 4400, 4000, 3000                       # 275 x 250 = 68,750 tiles
+    p = synth.random_case(107, W, H, n, sigma=(0.3, 40.0), margin=50)
+    ref = oracle.bin(W, H, p.astype(np.float64))
+    r, got = gpu_bin(W, H, p, capacity=capacity if capacity else None, fused=fused)
+    print(f"[lsd] {W}x{H}: M = {got['M']}, capacity {r.capacity}", flush=True)
+    for k in ["counts", "offsets", "keys", "vals", "ranges"]:
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    assert got["M"] == ref["M"]
+    img = r.forward().cpu().numpy()
+    pix = sample_pixels(W, H, 2048, 4, seed=108)
+    want, S = oracle.render_sum(W, H, p.astype(np.float64), pixels=pix)
+    assert image_error(img[:, pix[:, 0], pix[:, 1]], want, S) <= 1e-5
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_bin_lsd_capacity_above_bucket_limit(fused):
+    """A pair buffer of 2^26 + 1 entries takes the LSD passes even at 11 key bits (the bucket pass
+    is limited to 2^26); bit-exact against the oracle."""
+    require_gpu()
+    import oracle
+    W, H, n = 768, 512, 3000
+    p = synth.random_case(109, W, H, n, sigma=(0.3, 30.0), margin=20)
+    ref = oracle.bin(W, H, p.astype(np.float64))
+    r, got = gpu_bin(W, H, p, capacity=(1 << 26) + 1, fused=fused)
+    print(f"[lsd] {W}x{H}: M = {got['M']}, capacity {r.capacity}", flush=True)
+    for k in ["counts", "offsets", "keys", "vals", "ranges"]:
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    del r
+    torch.cuda.empty_cache()
