@@ -19,7 +19,12 @@ symmetries, numpy's matrix inverse for the cutoff set; for the SSIM loss:
 scipy's Gaussian window and zero-padded correlation, closed forms for shifted
 and scaled images, central finite differences; for the merge: moments and
 channel integrals by numerical quadrature of the two summed Gaussians, and
-identical pairs).  No function is "parity unpinned".
+identical pairs; for the merge cost: a closed form for equal isotropic pairs,
+quadrature moments with numpy's slogdet, non-negativity; for a merge round:
+the rule re-implemented with numpy over all pairs; for merging down: channel
+integrals kept and isolated Gaussians left alone; for density control: a
+hand-worked case and numpy's eigenvalues for the bloated flag).  No function
+is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -88,6 +93,16 @@ def _load():
     lib.oracle_grad_sum_rs.restype = None
     lib.oracle_rs_cholesky_grad.argtypes = [i64, P, f64, f64, P, P, P]
     lib.oracle_rs_cholesky_grad.restype = None
+    lib.oracle_merge_cost.argtypes = [P, P]
+    lib.oracle_merge_cost.restype = f64
+    lib.oracle_merge_round.argtypes = [i32, i32, i64, P, i64, P, P]
+    lib.oracle_merge_round.restype = i64
+    lib.oracle_merge_apply.argtypes = [i64, P, i64, P, P]
+    lib.oracle_merge_apply.restype = i64
+    lib.oracle_merge_to.argtypes = [i32, i32, i64, P, i64, P, P]
+    lib.oracle_merge_to.restype = i64
+    lib.oracle_adc.argtypes = [i32, i32, i64, P, P, P, ctypes.c_float, P]
+    lib.oracle_adc.restype = i64
     lib.oracle_loss_ssim.argtypes = [i32, i32, P, P, f64, f64, f64, P, P, P, P]
     lib.oracle_loss_ssim.restype = f64
     lib.oracle_merge_pairs.argtypes = [i64, P, P, P]
@@ -319,3 +334,49 @@ def adam(p, g, m, v, lr, step, beta1=0.9, beta2=0.999, eps=1e-8):
     lr = _f64(lr).reshape(row_len)
     _load().oracle_adam(rows, row_len, _p(p), _p(g), _p(m), _p(v), _p(lr), beta1, beta2, eps, int(step))
     return p, m, v
+
+
+def merge_cost(a, b):
+    """Merge cost of two Gaussians (Cholesky-form rows; a is taken as the one of smaller index)."""
+    a, b = _f64(a).reshape(8), _f64(b).reshape(8)
+    return float(_load().oracle_merge_cost(_p(a), _p(b)))
+
+
+def merge_round(W, H, params, max_pairs):
+    """One merge round: (pairs [m,2] int64, ascending smaller index; each Gaussian's pick [n], -1 none)."""
+    par = _f64(params).reshape(-1, 8)
+    n = par.shape[0]
+    pairs = np.zeros((max(n // 2, 1), 2), np.int64)
+    best = np.zeros(max(n, 1), np.int64)
+    m = _load().oracle_merge_round(W, H, n, _p(par), int(max_pairs), _p(pairs), _p(best))
+    return pairs[:m].copy(), best[:n].copy()
+
+
+def merge_apply(params, pairs):
+    """The set after merging the given disjoint pairs (ascending smaller index): [n - m, 8]."""
+    par = _f64(params).reshape(-1, 8)
+    pr = np.ascontiguousarray(np.asarray(pairs, np.int64).reshape(-1, 2))
+    out = np.zeros((max(par.shape[0], 1), 8))
+    m = _load().oracle_merge_apply(par.shape[0], _p(par), pr.shape[0], _p(pr), _p(out))
+    return out[:m].copy()
+
+
+def merge_to(W, H, params, target):
+    """Merge rounds down to `target` Gaussians (or until no pair is found): (params [n_out, 8], rounds)."""
+    par = _f64(params).reshape(-1, 8)
+    out = np.zeros((max(par.shape[0], 1), 8))
+    rounds = np.zeros(1, np.int64)
+    m = _load().oracle_merge_to(W, H, par.shape[0], _p(par), int(target), _p(out), _p(rounds))
+    return out[:m].copy(), int(rounds[0])
+
+
+def adc(W, H, params, image, target, s0):
+    """Adaptive density control on fp32 params [n,8] with fp32 image / target [3,H,W]:
+    (new params fp32 [n,8], flags int32 [n] (1 dead, 2 out of bounds, 4 bloated), moved)."""
+    par = np.ascontiguousarray(np.asarray(params, np.float32).reshape(-1, 8)).copy()
+    img = np.ascontiguousarray(np.asarray(image, np.float32))
+    tgt = np.ascontiguousarray(np.asarray(target, np.float32))
+    n = par.shape[0]
+    flags = np.zeros(max(n, 1), np.int32)
+    moved = _load().oracle_adc(W, H, n, _p(par), _p(img), _p(tgt), float(s0), _p(flags))
+    return par, flags[:n].copy(), int(moved)

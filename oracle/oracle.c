@@ -920,35 +920,285 @@ double oracle_loss_ssim(int W, int H, const double *x, const double *y, double w
  * L = chol(Sigma) (positive diagonal), and whose colour keeps each channel's
  * integral:  c_k = (|det L_i| c_{i,k} + |det L_j| c_{j,k}) / |det L|.
  * W = 0 (no mass) takes equal weights.  Sigma_n = L_n L_n^T as elsewhere. */
+/* The merged Gaussian of a and b (Cholesky-form rows of 8) into o (moment matching, above). */
+static void merge_two(const double *a, const double *b, double *o)
+{
+    const double *pp[2] = {a, b};
+    double det[2], w[2], S[2][3];
+    for (int s = 0; s < 2; ++s) {
+        const double *p = pp[s];
+        det[s] = fabs(p[2] * p[4]);
+        w[s] = det[s] * (fabs(p[5]) + fabs(p[6]) + fabs(p[7]));
+        S[s][0] = p[2] * p[2];                 /* Sigma11 */
+        S[s][1] = p[2] * p[3];                 /* Sigma21 */
+        S[s][2] = p[3] * p[3] + p[4] * p[4];   /* Sigma22 */
+    }
+    double W = w[0] + w[1];
+    double f0 = W > 0 ? w[0] / W : 0.5, f1 = W > 0 ? w[1] / W : 0.5;
+    const double mx = f0 * a[0] + f1 * b[0], my = f0 * a[1] + f1 * b[1];
+    double s11 = 0, s21 = 0, s22 = 0;
+    for (int s = 0; s < 2; ++s) {
+        const double f = s ? f1 : f0;
+        const double dx = pp[s][0] - mx, dy = pp[s][1] - my;
+        s11 += f * (S[s][0] + dx * dx);
+        s21 += f * (S[s][1] + dx * dy);
+        s22 += f * (S[s][2] + dy * dy);
+    }
+    const double l11 = sqrt(s11), l21 = s21 / l11, l22 = sqrt(s22 - l21 * l21);
+    const double dn = l11 * l22;
+    o[0] = mx; o[1] = my; o[2] = l11; o[3] = l21; o[4] = l22;
+    for (int k = 0; k < 3; ++k) o[5 + k] = (det[0] * a[5 + k] + det[1] * b[5 + k]) / dn;
+}
+
 void oracle_merge_pairs(int64_t np, const double *params, const int64_t *pairs, double *out)
 {
-    for (int64_t t = 0; t < np; ++t) {
-        const double *a = params + 8 * pairs[2*t], *b = params + 8 * pairs[2*t + 1];
-        const double *pp[2] = {a, b};
-        double det[2], w[2], S[2][3];
-        for (int s = 0; s < 2; ++s) {
-            const double *p = pp[s];
-            det[s] = fabs(p[2] * p[4]);
-            w[s] = det[s] * (fabs(p[5]) + fabs(p[6]) + fabs(p[7]));
-            S[s][0] = p[2] * p[2];                 /* Sigma11 */
-            S[s][1] = p[2] * p[3];                 /* Sigma21 */
-            S[s][2] = p[3] * p[3] + p[4] * p[4];   /* Sigma22 */
+    for (int64_t t = 0; t < np; ++t)
+        merge_two(params + 8 * pairs[2*t], params + 8 * pairs[2*t + 1], out + 8 * t);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Merging a set down to a target count ("FlashImgs", merge: train an       */
+/* overcomplete set, merge similar Gaussians down by moment matching, 80K   */
+/* -> 50K, finetune).  The pages name neither the similarity nor the pair   */
+/* rule; the reading here:                                                  */
+/*  - cost of merging i and j: the bound on the increase of the            */
+/*    Kullback-Leibler divergence when two components of a mixture are     */
+/*    replaced by their moment-matched merge (Runnalls, "Kullback-Leibler   */
+/*    approach to Gaussian mixture reduction", IEEE Trans. AES 2007):       */
+/*      B = 1/2 [ W log det Sigma_m - w_i log det Sigma_i - w_j log det Sigma_j ], */
+/*    with the masses w and the merged covariance Sigma_m of merge_two      */
+/*    (W = w_i + w_j; B = 0 when W = 0), evaluated with the smaller index   */
+/*    first, and B = +inf when det Sigma_m is not positive;                 */
+/*  - candidates: the other mergeable Gaussians whose mean lies in the same */
+/*    or a neighbouring 16 x 16 cell (cell = floor(mu / 16) per axis,       */
+/*    clamped to the image's tiles); mergeable = all 8 params finite and    */
+/*    l11, l22 nonzero;                                                     */
+/*  - one round: every Gaussian picks its cheapest candidate (ties: the     */
+/*    smaller index); pairs that pick each other are merged, all of them,   */
+/*    or, when that is more than the count still to remove, the cheapest   */
+/*    ones by (fp32 rounding of B, smaller index);                          */
+/*  - the merged Gaussian takes the smaller index's place; the set keeps    */
+/*    index order otherwise; rounds repeat until the target is reached or   */
+/*    no pair picks each other.                                             */
+/* The cost's fp64 operations are done in the order written (no FMA).      */
+/* ------------------------------------------------------------------------ */
+
+static int mergeable(const double *p)
+{
+    for (int k = 0; k < 8; ++k)
+        if (!isfinite(p[k])) return 0;
+    return p[2] != 0.0 && p[4] != 0.0;
+}
+
+/* Merge cost of a and b (a: the smaller index). */
+static double merge_cost(const double *a, const double *b)
+{
+    const double da = fabs(a[2] * a[4]), db = fabs(b[2] * b[4]);
+    const double wa = da * ((fabs(a[5]) + fabs(a[6])) + fabs(a[7]));
+    const double wb = db * ((fabs(b[5]) + fabs(b[6])) + fabs(b[7]));
+    const double W = wa + wb;
+    const double fa = W > 0 ? wa / W : 0.5, fb = W > 0 ? wb / W : 0.5;
+    const double mx = fa * a[0] + fb * b[0], my = fa * a[1] + fb * b[1];
+    const double ax = a[0] - mx, ay = a[1] - my, bx = b[0] - mx, by = b[1] - my;
+    const double s11 = fa * (a[2] * a[2] + ax * ax) + fb * (b[2] * b[2] + bx * bx);
+    const double s21 = fa * (a[2] * a[3] + ax * ay) + fb * (b[2] * b[3] + bx * by);
+    const double s22 = fa * ((a[3] * a[3] + a[4] * a[4]) + ay * ay) + fb * ((b[3] * b[3] + b[4] * b[4]) + by * by);
+    const double dm = s11 * s22 - s21 * s21;
+    if (!(dm > 0.0)) return INFINITY;
+    if (W == 0.0) return 0.0;
+    return 0.5 * (W * log(dm) - wa * log(da * da) - wb * log(db * db));
+}
+
+double oracle_merge_cost(const double *a, const double *b) { return merge_cost(a, b); }
+
+static void merge_cell(const double *p, int tx, int ty, int *cx, int *cy)
+{
+    double x = floor(p[0] / ORACLE_TILE), y = floor(p[1] / ORACLE_TILE);
+    x = x < 0 ? 0 : (x > tx - 1 ? tx - 1 : x);
+    y = y < 0 ? 0 : (y > ty - 1 ? ty - 1 : y);
+    *cx = (int)x;
+    *cy = (int)y;
+}
+
+/* One round on params[n,8] (image W x H): the pairs merged, (i, j) with i < j, in ascending i,
+ * written to pairs[2 * count]; at most max_pairs.  best[n] (may be NULL): each Gaussian's pick
+ * (-1: none). */
+int64_t oracle_merge_round(int W, int H, int64_t n, const double *params, int64_t max_pairs, int64_t *pairs,
+                           int64_t *best)
+{
+    const int tx = (W + ORACLE_TILE - 1) / ORACLE_TILE, ty = (H + ORACLE_TILE - 1) / ORACLE_TILE;
+    int *cx = (int *)malloc(sizeof(int) * (n > 0 ? n : 1)), *cy = (int *)malloc(sizeof(int) * (n > 0 ? n : 1));
+    int64_t *pick = (int64_t *)malloc(sizeof(int64_t) * (n > 0 ? n : 1));
+    double *pc = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+    for (int64_t i = 0; i < n; ++i) merge_cell(params + 8 * i, tx, ty, &cx[i], &cy[i]);
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n; ++i) {
+        pick[i] = -1;
+        pc[i] = INFINITY;
+        if (!mergeable(params + 8 * i)) continue;
+        for (int64_t j = 0; j < n; ++j) {
+            if (j == i || !mergeable(params + 8 * j)) continue;
+            if (abs(cx[i] - cx[j]) > 1 || abs(cy[i] - cy[j]) > 1) continue;
+            const double c = i < j ? merge_cost(params + 8 * i, params + 8 * j)
+                                   : merge_cost(params + 8 * j, params + 8 * i);
+            if (pick[i] < 0 || c < pc[i] || (c == pc[i] && j < pick[i])) { pick[i] = j; pc[i] = c; }
         }
-        double W = w[0] + w[1];
-        double f0 = W > 0 ? w[0] / W : 0.5, f1 = W > 0 ? w[1] / W : 0.5;
-        const double mx = f0 * a[0] + f1 * b[0], my = f0 * a[1] + f1 * b[1];
-        double s11 = 0, s21 = 0, s22 = 0;
-        for (int s = 0; s < 2; ++s) {
-            const double f = s ? f1 : f0;
-            const double dx = pp[s][0] - mx, dy = pp[s][1] - my;
-            s11 += f * (S[s][0] + dx * dx);
-            s21 += f * (S[s][1] + dx * dy);
-            s22 += f * (S[s][2] + dy * dy);
-        }
-        const double l11 = sqrt(s11), l21 = s21 / l11, l22 = sqrt(s22 - l21 * l21);
-        const double dn = l11 * l22;
-        double *o = out + 8 * t;
-        o[0] = mx; o[1] = my; o[2] = l11; o[3] = l21; o[4] = l22;
-        for (int k = 0; k < 3; ++k) o[5 + k] = (det[0] * a[5 + k] + det[1] * b[5 + k]) / dn;
     }
+    /* mutual picks, ascending smaller index */
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t j = pick[i];
+        if (j > i && pick[j] == i && isfinite(pc[i])) { pairs[2 * m] = i; pairs[2 * m + 1] = j; ++m; }
+    }
+    if (m > max_pairs) {            /* keep the cheapest max_pairs by (fp32 cost, smaller index) */
+        float *key = (float *)malloc(sizeof(float) * m);
+        for (int64_t t = 0; t < m; ++t) key[t] = (float)pc[pairs[2 * t]];
+        char *keep = (char *)calloc(m, 1);
+        for (int64_t k = 0; k < max_pairs; ++k) {            /* selection, smallest first */
+            int64_t b = -1;
+            for (int64_t t = 0; t < m; ++t)
+                if (!keep[t] && (b < 0 || key[t] < key[b])) b = t;   /* ascending t breaks ties */
+            keep[b] = 1;
+        }
+        int64_t o = 0;
+        for (int64_t t = 0; t < m; ++t)
+            if (keep[t]) { pairs[2 * o] = pairs[2 * t]; pairs[2 * o + 1] = pairs[2 * t + 1]; ++o; }
+        m = o;
+        free(key); free(keep);
+    }
+    if (best)
+        for (int64_t i = 0; i < n; ++i) best[i] = pick[i];
+    free(cx); free(cy); free(pick); free(pc);
+    return m;
+}
+
+/* The set after merging the pairs (ascending smaller index, disjoint): out[n - npairs, 8]. */
+int64_t oracle_merge_apply(int64_t n, const double *params, int64_t npairs, const int64_t *pairs, double *out)
+{
+    int64_t *partner = (int64_t *)malloc(sizeof(int64_t) * (n > 0 ? n : 1));
+    for (int64_t i = 0; i < n; ++i) partner[i] = -1;
+    for (int64_t t = 0; t < npairs; ++t) { partner[pairs[2*t]] = pairs[2*t + 1]; partner[pairs[2*t + 1]] = pairs[2*t]; }
+    int64_t o = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (partner[i] < 0) memcpy(out + 8 * o++, params + 8 * i, 8 * sizeof(double));
+        else if (partner[i] > i) merge_two(params + 8 * i, params + 8 * partner[i], out + 8 * o++);
+    }
+    free(partner);
+    return o;
+}
+
+/* Rounds until n_out == target or no pair is found: out[n, 8] (the first n_out rows used). */
+int64_t oracle_merge_to(int W, int H, int64_t n, const double *params, int64_t target, double *out,
+                        int64_t *rounds)
+{
+    double *cur = (double *)malloc(sizeof(double) * 8 * (n > 0 ? n : 1));
+    int64_t *pairs = (int64_t *)malloc(sizeof(int64_t) * (n > 0 ? n : 2));
+    memcpy(cur, params, sizeof(double) * 8 * n);
+    int64_t m = n, r = 0;
+    while (m > target) {
+        const int64_t np = oracle_merge_round(W, H, m, cur, m - target, pairs, NULL);
+        if (np == 0) break;
+        m = oracle_merge_apply(m, cur, np, pairs, out);
+        memcpy(cur, out, sizeof(double) * 8 * m);
+        ++r;
+    }
+    memcpy(out, cur, sizeof(double) * 8 * m);
+    if (rounds) *rounds = r;
+    free(cur); free(pairs);
+    return m;
+}
+/* ------------------------------------------------------------------------ */
+/* Adaptive density control ("FlashImgs", Training features: every 300      */
+/* steps from step 150, dead, out-of-bounds and bloated Gaussians are       */
+/* relocated to high-error pixels).  The pages give no thresholds; the      */
+/* reading here:                                                            */
+/*  - dead: some parameter non-finite, l11 or l22 zero, or every colour     */
+/*    below one 8-bit level in size (max_k |c_k| < 1/255);                  */
+/*  - out of bounds: the mean outside [0, W) x [0, H);                      */
+/*  - bloated: the larger eigenvalue of Sigma above (max(W, H)/16)^2, i.e.  */
+/*    the longer axis' standard deviation above 1/16 of the image;          */
+/*  - error of pixel p: e = sum_k r_k^2 with r = target - image, in fp32 as */
+/*    fma(r_b, r_b, fma(r_g, r_g, r_r * r_r)), a NaN error counting as 0;   */
+/*  - the K = min(#flagged, W H) pixels of largest e (ties: smaller pixel   */
+/*    index) taken in ascending pixel index go, one each, to the flagged    */
+/*    Gaussians in ascending index: mean = the pixel centre, L = s0 I (s0   */
+/*    the caller's initial size), colour = r at that pixel (the Gaussian    */
+/*    then fills the residual at its centre).                               */
+/* The flag decisions are fp64 comparisons of quantities formed in the     */
+/* order written; bloated <=> not (s11 <= t and s22 <= t and                */
+/* (t - s11)(t - s22) >= s21^2), t = (max(W,H)/16)^2, Sigma from L.         */
+/* ------------------------------------------------------------------------ */
+
+/* 1: dead, 2: out of bounds, 4: bloated (0: kept). */
+static int adc_flag(const float *p, int W, int H)
+{
+    int f = 0;
+    for (int k = 0; k < 8; ++k)
+        if (!isfinite(p[k])) return 1;
+    if (p[2] == 0.0f || p[4] == 0.0f) return 1;
+    const double cm = fmax(fabs((double)p[5]), fmax(fabs((double)p[6]), fabs((double)p[7])));
+    if (cm < 1.0 / 255.0) f |= 1;
+    if (!(p[0] >= 0.0f && p[0] < (float)W && p[1] >= 0.0f && p[1] < (float)H)) f |= 2;
+    const double l11 = p[2], l21 = p[3], l22 = p[4];
+    const double s11 = l11 * l11, s21 = l11 * l21, s22 = l21 * l21 + l22 * l22;
+    const double side = (double)(W > H ? W : H) / 16.0, t = side * side;
+    if (!(s11 <= t && s22 <= t && (t - s11) * (t - s22) >= s21 * s21)) f |= 4;
+    return f;
+}
+
+/* params[n,8] fp32 (updated in place), image / target [3,H,W] fp32; flags[n] out (may be NULL).
+ * Returns the number of Gaussians relocated. */
+int64_t oracle_adc(int W, int H, int64_t n, float *params, const float *image, const float *target, float s0,
+                   int32_t *flags)
+{
+    const int64_t np = (int64_t)W * H;
+    int64_t nf = 0;
+    int *fl = (int *)malloc(sizeof(int) * (n > 0 ? n : 1));
+    for (int64_t g = 0; g < n; ++g) {
+        fl[g] = adc_flag(params + 8 * g, W, H);
+        if (flags) flags[g] = fl[g];
+        nf += fl[g] != 0;
+    }
+    const int64_t K = nf < np ? nf : np;
+    if (K == 0) { free(fl); return 0; }
+    float *e = (float *)malloc(sizeof(float) * np);
+    for (int64_t p = 0; p < np; ++p) {
+        const float r0 = target[p] - image[p], r1 = target[np + p] - image[np + p];
+        const float r2 = target[2 * np + p] - image[2 * np + p];
+        e[p] = fmaf(r2, r2, fmaf(r1, r1, r0 * r0));
+        if (!(e[p] >= 0.0f)) e[p] = 0.0f;                 /* a NaN error counts as none */
+    }
+    /* the K-th largest error (ties: smaller index first) by sorting pixel indices */
+    int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * np);
+    for (int64_t p = 0; p < np; ++p) idx[p] = p;
+    /* insertion into a max-ordered prefix would be O(np K); a full sort is plain enough */
+    for (int64_t w = 1; w < np; w *= 2) {                 /* bottom-up merge sort, stable */
+        int64_t *tmp = (int64_t *)malloc(sizeof(int64_t) * np);
+        for (int64_t lo = 0; lo < np; lo += 2 * w) {
+            int64_t a = lo, am = lo + w < np ? lo + w : np, b = am, bm = lo + 2 * w < np ? lo + 2 * w : np, o = lo;
+            while (a < am && b < bm) tmp[o++] = (e[idx[b]] > e[idx[a]]) ? idx[b++] : idx[a++];
+            while (a < am) tmp[o++] = idx[a++];
+            while (b < bm) tmp[o++] = idx[b++];
+        }
+        memcpy(idx, tmp, sizeof(int64_t) * np);
+        free(tmp);
+    }
+    char *sel = (char *)calloc(np, 1);
+    for (int64_t k = 0; k < K; ++k) sel[idx[k]] = 1;
+    int64_t g = 0, moved = 0;
+    for (int64_t p = 0; p < np && moved < K; ++p) {
+        if (!sel[p]) continue;
+        while (fl[g] == 0) ++g;                             /* the next flagged Gaussian */
+        float *q = params + 8 * g;
+        q[0] = (float)(p % W) + 0.5f;
+        q[1] = (float)(p / W) + 0.5f;
+        q[2] = s0; q[3] = 0.0f; q[4] = s0;
+        q[5] = target[p] - image[p];
+        q[6] = target[np + p] - image[np + p];
+        q[7] = target[2 * np + p] - image[2 * np + p];
+        ++g;
+        ++moved;
+    }
+    free(e); free(idx); free(sel); free(fl);
+    return moved;
 }

@@ -780,6 +780,198 @@ def test_merge_of_identical_gaussians():
     np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("sigma,d,theta", [(1.0, 0.0, 0.0), (1.0, 1.0, 0.3), (2.5, 4.0, 1.1), (0.7, 3.0, -2.0)])
+def test_merge_cost_closed_form_for_equal_isotropic_pair(sigma, d, theta):
+    """Two equal isotropic Gaussians (std sigma, same colour) a distance d apart: the merged
+    covariance is sigma^2 I + (d^2 / 4) u u^T, so the cost is w log(1 + d^2 / (4 sigma^2)),
+    w = sigma^2 sum |c| (each one's mass)."""
+    import oracle
+    u = np.array([np.cos(theta), np.sin(theta)])
+    c = np.array([0.4, -0.7, 0.2])
+    a = np.array([5.0, 6.0, sigma, 0.0, sigma, *c])
+    b = a.copy()
+    b[:2] += d * u
+    w = sigma * sigma * np.abs(c).sum()
+    want = w * np.log1p(d * d / (4 * sigma * sigma))
+    got = oracle.merge_cost(a, b)
+    assert got == pytest.approx(want, rel=1e-10, abs=1e-14)
+
+
+def test_merge_cost_against_quadrature_and_library_logdet():
+    """B = 1/2 (W log det Sigma_m - w_i log det Sigma_i - w_j log det Sigma_j) with Sigma_m the mixture's
+    covariance by quadrature and numpy's slogdet; B >= 0 over random pairs (log det is concave)."""
+    import oracle
+    p = np.array([[10.0, 12.0, 1.5, 0.4, 1.1, 0.6, 0.2, 0.9],
+                  [13.0, 11.0, -0.9, -0.3, 1.8, 0.3, -0.5, 0.4]])
+    _, C, _ = _quad_moments(p, -10.0, 35.0)
+    w = [abs(g[2] * g[4]) * np.abs(g[5:]).sum() for g in p]
+    ld = [np.linalg.slogdet(np.array([[g[2], 0], [g[3], g[4]]]) @ np.array([[g[2], 0], [g[3], g[4]]]).T)[1]
+          for g in p]
+    want = 0.5 * ((w[0] + w[1]) * np.linalg.slogdet(C)[1] - w[0] * ld[0] - w[1] * ld[1])
+    assert oracle.merge_cost(p[0], p[1]) == pytest.approx(want, rel=1e-5)
+    rng = np.random.default_rng(902)
+    for _ in range(200):
+        q = synth.random_case(int(rng.integers(1 << 30)), 40, 40, 2, sigma=(0.3, 8.0)).astype(np.float64)
+        assert oracle.merge_cost(q[0], q[1]) >= -1e-12 * (1 + abs(q[0, 5:]).sum() + abs(q[1, 5:]).sum()) * 100
+
+
+def test_merge_cost_of_massless_pairs():
+    """Zero mass on both sides: cost 0; zero mass on one side: the merge is the other Gaussian, cost ~0."""
+    import oracle
+    a = np.array([3.0, 4.0, 1.2, 0.3, 0.8, 0.0, 0.0, 0.0])
+    b = np.array([9.0, 1.0, 2.0, -0.5, 1.5, 0.0, 0.0, 0.0])
+    assert oracle.merge_cost(a, b) == 0.0
+    b[5:] = (0.5, 0.1, -0.2)
+    assert abs(oracle.merge_cost(a, b)) < 1e-12
+
+
+def _merge_round_by_numpy(W, H, p, max_pairs):
+    """The round's rule written with numpy: cells, all candidate costs, argmin with index ties,
+    mutual picks, the cheapest by (fp32 cost, smaller index)."""
+    import oracle
+    n = p.shape[0]
+    tx, ty = -(-W // 16), -(-H // 16)
+    ok = np.all(np.isfinite(p), 1) & (p[:, 2] != 0) & (p[:, 4] != 0)
+    cx = np.clip(np.floor(p[:, 0] / 16), 0, tx - 1)
+    cy = np.clip(np.floor(p[:, 1] / 16), 0, ty - 1)
+    cost = np.full((n, n), np.inf)
+    near = (np.abs(cx[:, None] - cx[None]) <= 1) & (np.abs(cy[:, None] - cy[None]) <= 1) & ok[:, None] & ok[None]
+    np.fill_diagonal(near, False)
+    for i, j in zip(*np.nonzero(near)):
+        cost[i, j] = oracle.merge_cost(p[min(i, j)], p[max(i, j)])
+    best = np.where(near.any(1), np.argmin(np.where(near, cost, np.inf), 1), -1)
+    pairs = [(i, j) for i, j in enumerate(best) if j > i and best[j] == i and np.isfinite(cost[i, j])]
+    if len(pairs) > max_pairs:
+        key = np.array([np.float32(cost[i, j]) for i, j in pairs])
+        order = np.lexsort((np.array([i for i, _ in pairs]), key))[:max_pairs]
+        pairs = sorted(pairs[k] for k in order)
+    return np.array(pairs, np.int64).reshape(-1, 2), best
+
+
+@pytest.mark.parametrize("seed,W,H,n,max_pairs", [(911, 64, 48, 300, 1000), (912, 64, 48, 300, 25),
+                                                  (913, 40, 40, 60, 1000), (914, 100, 30, 500, 10)])
+def test_merge_round_matches_the_rule(seed, W, H, n, max_pairs):
+    import oracle
+    p = synth.random_case(seed, W, H, n, sigma=(0.3, 6.0), margin=8).astype(np.float64)
+    p[:3, 5:] = 0.0                          # massless ones merge first
+    p[3, 0] = np.nan                         # never merged
+    p[4, 2] = 0.0
+    got, best = oracle.merge_round(W, H, p, max_pairs)
+    want, wbest = _merge_round_by_numpy(W, H, p, max_pairs)
+    np.testing.assert_array_equal(best, wbest)
+    np.testing.assert_array_equal(got, want)
+    assert len(set(got.ravel())) == got.size                 # disjoint
+    assert 3 not in got and 4 not in got
+
+
+def test_merge_apply_keeps_order_integrals_and_untouched_rows():
+    import oracle
+    W, H = 64, 48
+    p = synth.random_case(915, W, H, 200, sigma=(0.3, 6.0)).astype(np.float64)
+    pairs, _ = oracle.merge_round(W, H, p, 1000)
+    out = oracle.merge_apply(p, pairs)
+    assert out.shape[0] == p.shape[0] - pairs.shape[0]
+    gone = set(pairs[:, 1])
+    kept = [i for i in range(p.shape[0]) if i not in gone]
+    first = {int(i): int(j) for i, j in pairs}
+    merged = oracle.merge_pairs(p, pairs)
+    for o, i in enumerate(kept):
+        if i in first:
+            np.testing.assert_array_equal(out[o], merged[list(first).index(i)])
+        else:
+            np.testing.assert_array_equal(out[o], p[i])
+    integ = lambda q: (np.abs(q[:, 2] * q[:, 4])[:, None] * q[:, 5:]).sum(0)
+    np.testing.assert_allclose(integ(out), integ(p), rtol=1e-12)
+
+
+def test_merge_to_reaches_the_target_or_stops():
+    import oracle
+    W, H = 96, 64
+    p = synth.random_case(916, W, H, 800, sigma=(0.3, 5.0)).astype(np.float64)
+    out, rounds = oracle.merge_to(W, H, p, 500)
+    assert out.shape[0] == 500 and rounds >= 2
+    integ = lambda q: (np.abs(q[:, 2] * q[:, 4])[:, None] * q[:, 5:]).sum(0)
+    np.testing.assert_allclose(integ(out), integ(p), rtol=1e-10)
+    # isolated Gaussians (no two in neighbouring cells) are never merged
+    q = np.zeros((4, 8))
+    q[:, 0] = [8, 60, 8, 60]
+    q[:, 1] = [8, 8, 60, 60]
+    q[:, 2] = q[:, 4] = 1.0
+    q[:, 5:] = 0.5
+    out, rounds = oracle.merge_to(W, H, q, 2)
+    assert out.shape[0] == 4 and rounds == 0
+
+
+def _adc_case():
+    W, H = 64, 48
+    p = np.zeros((7, 8), np.float32)
+    p[:, 0], p[:, 1] = 20.0, 20.0
+    p[:, 2], p[:, 4] = 2.0, 2.0
+    p[:, 5:] = 0.5
+    p[1, 5:] = (0.003, -0.0039, 0.0)          # dead: every colour below 1/255
+    p[2, 0] = -3.0                             # out of bounds
+    p[3, 2] = 5.0                              # bloated: sigma_x 5 > 64/16
+    p[4, 3] = 3.9                              # sigma_y^2 = 3.9^2 + 2^2 > 16: bloated through l21
+    p[5, 4] = np.nan                           # dead
+    p[6, 0] = 63.99                            # inside, kept
+    image = np.zeros((3, H, W), np.float32)
+    target = np.zeros((3, H, W), np.float32)
+    target[:, 10, 5] = (0.3, 0.0, 0.0)         # e = 0.09
+    target[:, 2, 40] = (0.0, -0.5, 0.0)        # e = 0.25
+    target[:, 30, 1] = (0.2, 0.2, 0.2)         # e = 0.12
+    target[:, 7, 7] = (0.0, 0.0, 0.3)          # e = 0.09 (tie with (10, 5); larger index)
+    target[:, 47, 63] = (0.1, 0.0, 0.0)        # e = 0.01
+    return W, H, p, image, target
+
+
+def test_adc_hand_worked_case():
+    """Flags 1 dead, 2 out of bounds, 4 bloated; the 5 flagged Gaussians (1..5) take the 5 pixels of
+    largest error in ascending pixel order: (2, 40), (7, 7), (10, 5), (30, 1), (47, 63)."""
+    import oracle
+    W, H, p, image, target = _adc_case()
+    out, flags, moved = oracle.adc(W, H, p, image, target, 1.5)
+    np.testing.assert_array_equal(flags, [0, 1, 2, 4, 4, 1, 0])
+    assert moved == 5
+    np.testing.assert_array_equal(out[[0, 6]], p[[0, 6]])
+    want_pix = [(2, 40), (7, 7), (10, 5), (30, 1), (47, 63)]
+    for g, (i, j) in zip([1, 2, 3, 4, 5], want_pix):
+        np.testing.assert_array_equal(out[g], np.array([j + 0.5, i + 0.5, 1.5, 0.0, 1.5, *target[:, i, j]],
+                                                       np.float32))
+    # a 2 x 1 image: every Gaussian is flagged (out of bounds, bloated), two pixels go to the first two
+    out, flags, moved = oracle.adc(2, 1, p, image[:, :1, :2], target[:, :1, :2], 1.0)
+    assert moved == 2 and np.all(flags != 0)
+    assert out[0, 0] == 0.5 and out[1, 0] == 1.5 and out[0, 1] == 0.5
+    np.testing.assert_array_equal(out[2:], p[2:])
+
+
+def test_adc_bloat_flag_against_eigenvalues():
+    """The bloated flag equals (largest eigenvalue of L L^T by numpy) > (max(W, H) / 16)^2, away
+    from equality; out of bounds is the half-open image rectangle."""
+    import oracle
+    W, H = 160, 96
+    rng = np.random.default_rng(917)
+    n = 3000
+    p = np.zeros((n, 8), np.float32)
+    p[:, 0], p[:, 1] = 50.0, 40.0
+    p[:, 2] = rng.uniform(0.5, 14.0, n) * rng.choice([-1, 1], n)
+    p[:, 3] = rng.normal(0.0, 6.0, n)
+    p[:, 4] = rng.uniform(0.5, 14.0, n)
+    p[:, 5:] = 0.5
+    image = np.zeros((3, H, W), np.float32)
+    _, flags, _ = oracle.adc(W, H, p, image, image, 1.0)
+    lam = np.array([np.linalg.eigvalsh(np.array([[g[2], 0], [g[3], g[4]]], np.float64) @
+                                       np.array([[g[2], 0], [g[3], g[4]]], np.float64).T)[1] for g in p])
+    t = (max(W, H) / 16.0) ** 2
+    clear = np.abs(lam - t) > 1e-9 * t
+    np.testing.assert_array_equal((flags[clear] & 4) != 0, lam[clear] > t)
+    q = np.zeros((6, 8), np.float32)
+    q[:, 2], q[:, 4], q[:, 5:] = 1.0, 1.0, 0.5
+    q[:, 0] = [0.0, -1e-7, float(W), np.nextafter(np.float32(W), np.float32(0)), 5.0, 5.0]
+    q[:, 1] = [0.0, 0.0, 0.0, 0.0, float(H), -0.0]
+    _, f, _ = oracle.adc(W, H, q, image, image, 1.0)
+    np.testing.assert_array_equal(f & 2, [0, 2, 2, 0, 2, 0])
+
+
 def test_absgrad_is_the_sum_of_per_pixel_absolute_mean_gradients():
     """The gradient's plain scale for the means (absgrad) = sum over pixels of |d(G_p . I_p)/dmu|,
     each pixel's derivative by central differences of the render at that pixel."""
