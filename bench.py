@@ -387,17 +387,46 @@ def bench_absgrad(args, wlname, target, params, dev):
         "cpu_baseline": None}), flush=True)
 
 
-def bench_merge(args, dev):
-    """gi_merge_pairs on the merge phase's shape: 30K disjoint pairs of 80K Gaussians (80K -> 50K)."""
+def bench_merge(args, target, dev):
+    """The merge phase of an overcomplete fit at 768x512: 80,000 Gaussians fitted for a few hundred
+    steps, merged down to 50,000 (gi_merge_to), then fitted further; the merge pass is timed (host
+    clock around the call, which waits for each round's pair count), and gi_merge_pairs alone on
+    30K disjoint pairs with HIP events."""
     import torch
     from rasterizer_gaussian_raster_amd import gi, synth
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter, merge_to
 
-    n, npairs = 80000, 30000
-    p = torch.from_numpy(synth.random_case(301, 768, 512, n, sigma=(0.5, 8.0))).to(dev)
+    W, H, n, tgt_n = 768, 512, 80_000, 50_000
+    w = synth.make_workload("kodak_768x512_50k", n=n)
+    fit = Fitter(target, torch.from_numpy(w["params"]).to(dev), capacity_slack=2.0)
+    pre = max(args.warmup, 200)
+    for _ in range(pre):
+        fit.step()
+    torch.cuda.synchronize()
+    loss_pre = float(fit.loss.item())
+    merge_to(fit.params, W, H, tgt_n)                   # warm-up of the merge kernels
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    merged, rounds = merge_to(fit.params, W, H, tgt_n)
+    torch.cuda.synchronize()
+    t_merge = time.perf_counter() - t0
+    fit2 = Fitter(target, merged, capacity_slack=2.0)
+    fit2.step()
+    torch.cuda.synchronize()
+    loss_after = float(fit2.loss.item())
+    for _ in range(pre):
+        fit2.step()
+    torch.cuda.synchronize()
+    loss_post = float(fit2.loss.item())
+    log(f"[bench] 80K fit {pre} steps: loss {loss_pre:.4e}; merge to {merged.shape[0]} in {rounds} rounds, "
+        f"{t_merge*1e3:.2f} ms; loss right after {loss_after:.4e}, after {pre} more steps {loss_post:.4e}")
+    # the per-pair op alone: 30K disjoint pairs
+    npairs = 30000
     perm = np.random.default_rng(302).permutation(n)
     pairs = torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).astype(np.int32)).to(dev)
     out = torch.empty((npairs, 8), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
+    p = fit.params
+    for _ in range(10):
         gi.gi_merge_pairs(npairs, pairs, n, p, out)
     nk = max(20, min(args.steps, 1000))
     E = lambda: torch.cuda.Event(enable_timing=True)
@@ -407,19 +436,63 @@ def bench_merge(args, dev):
         gi.gi_merge_pairs(npairs, pairs, n, p, out)
         ev[k][1].record()
     torch.cuda.synchronize()
-    secs = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    secs = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
     nbytes = 104 * npairs             # two 32 B records + 8 B of indices read, 32 B written per pair
     gbs = nbytes / secs / 1e9
     log(f"[bench] gi_merge_pairs: {secs*1e6:.2f} us for {npairs} pairs ({gbs:.0f} GB/s algorithmic)")
     print(json.dumps({
-        "metric": "moment-matching merge, pairs/s", "value": round(npairs / secs, 1), "unit": "pairs/s",
-        "n_gpus": 1, "steps": nk, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
-        "config": {"workload": "merge_80k_to_50k", "gaussians": n, "pairs": npairs},
-        "timing": "HIP events on the launch stream around each launch",
+        "metric": "merge 80K -> 50K Gaussians (768x512), merges/s", "value": round((n - merged.shape[0]) / t_merge, 1),
+        "unit": "merges/s", "n_gpus": 1, "steps": 1, "warmup": 1, "ms_per_step": round(t_merge * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "merge_768x512_80k_to_50k", "gaussians": n, "target": tgt_n,
+                   "result": int(merged.shape[0]), "rounds": rounds, "fit_steps_each_phase": pre},
+        "loss": {"before_merge": loss_pre, "right_after": loss_after, "after_finetune": loss_post},
+        "timing": "value: host clock around gi_merge_to (it waits for each round's count); "
+                  "merge_pairs_us: median of HIP events around gi_merge_pairs on 30K pairs",
+        "merge_pairs_us": round(secs * 1e6, 2),
         "roofline": {"bound": "hbm", "kernel": "k_merge_pairs", "achieved": round(gbs, 1), "peak": PEAK_HBM,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4), "traffic": None,
                      "avg_launch_us": round(secs * 1e6, 2)},
+        "cpu_baseline": None}), flush=True)
+
+
+def bench_adc(args, target, params, dev):
+    """One adaptive-density-control pass at 768x512 / 50K after some fitting (gi_adc: flags, pixel
+    errors, the top-K pixel select, relocation), timed with HIP events."""
+    import torch
+    from rasterizer_gaussian_raster_amd import gi
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter
+
+    fit = Fitter(target, params, capacity_slack=2.0)
+    for _ in range(max(args.warmup, 150)):
+        fit.step()
+    torch.cuda.synchronize()
+    r = fit.raster
+    d, n = r.desc, fit.n
+    ws = torch.empty(gi.gi_adc_workspace_bytes(d, n), dtype=torch.uint8, device=dev)
+    moved = torch.zeros(1, dtype=torch.int32, device=dev)
+    P0 = fit.params.clone()
+    nk = max(20, min(args.steps, 200))
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E(), E()] for _ in range(nk)]
+    P = P0.clone()
+    for k in range(nk):
+        P.copy_(P0)
+        ev[k][0].record()
+        gi.gi_adc(d, n, P, None, None, r.image, target, 1.5, None, moved, ws)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    us = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    mv = int(moved.item())
+    log(f"[bench] gi_adc at 768x512 / {n}: median {np.median(us):.1f} us, {mv} Gaussians moved")
+    print(json.dumps({
+        "metric": "adaptive density control pass (768x512, 50K)", "value": round(1e6 / float(np.median(us)), 1),
+        "unit": "passes/s", "n_gpus": 1, "steps": nk, "warmup": 0, "ms_per_step": round(float(np.median(us)) / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "adc_768x512_50k", "gaussians": n, "moved": mv},
+        "timing_us": {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+                      "p90": round(float(np.percentile(us, 90)), 2)},
+        "timing": "HIP events on the launch stream around each gi_adc call (params restored between calls)",
         "cpu_baseline": None}), flush=True)
 
 
@@ -521,9 +594,10 @@ def main():
     ap.add_argument("--params", choices=["cholesky", "rs"], default="cholesky",
                     help="parameter form of the Gaussians (rs: rotation-scale, converted on the GPU each step)")
     ap.add_argument("--loss", default="l2", help="l2, or weights w1,w2,ws of w1 L1 + w2 L2 + ws (1 - SSIM)")
-    ap.add_argument("--op", choices=["fit", "merge", "absgrad"], default="fit",
-                    help="merge: time the moment-matching merge of 30K pairs of 80K Gaussians (80K -> 50K); "
-                         "absgrad: the sum backward with and without the absgrad output")
+    ap.add_argument("--op", choices=["fit", "merge", "absgrad", "adc"], default="fit",
+                    help="merge: fit 80K Gaussians, merge them down to 50K (gi_merge_to, timed), fit on; "
+                         "absgrad: the sum backward with and without the absgrad output; "
+                         "adc: one adaptive-density-control pass after some fitting")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -557,7 +631,9 @@ def main():
     if wl.mode != "sum":
         return bench_alpha(args, w, target, params, dev)
     if args.op == "merge":
-        return bench_merge(args, dev)
+        return bench_merge(args, target, dev)
+    if args.op == "adc":
+        return bench_adc(args, target, params, dev)
     if args.op == "absgrad":
         return bench_absgrad(args, wlname, target, params, dev)
     if args.params == "rs":

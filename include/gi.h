@@ -628,6 +628,90 @@ gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const
                          void *stream);
 
 /*
+ * gi_merge_round / gi_merge_apply / gi_merge_to -- merging a set down to a
+ *   target count ("FlashImgs", Commands: merge -- an overcomplete set, 80K ->
+ *   50K, "merges similar ones down" by moment matching; Library API:
+ *   Session.merge_to).  The pages name no similarity or pair rule; the reading:
+ *   - cost of merging Gaussians i < j: Runnalls' bound on the increase of the
+ *     Kullback-Leibler divergence when two mixture components are replaced by
+ *     their moment-matched merge ("Kullback-Leibler approach to Gaussian mixture
+ *     reduction", IEEE Trans. AES 2007), in fp64, in this order (p = i's params,
+ *     q = j's, each converted to fp64; no fused multiply-add):
+ *       da = |l11 l22|_p, wa = da ((|c0| + |c1|) + |c2|)_p, db, wb likewise,
+ *       W = wa + wb, fa = wa/W (0.5 if W = 0), fb likewise,
+ *       mx = fa px + fb qx, my likewise; ax = px - mx, ay, bx, by likewise,
+ *       s11 = fa (l11p l11p + ax ax) + fb (l11q l11q + bx bx),
+ *       s21 = fa (l11p l21p + ax ay) + fb (l11q l21q + bx by),
+ *       s22 = fa ((l21p l21p + l22p l22p) + ay ay) + fb ((...)q + by by),
+ *       dm = s11 s22 - s21 s21;  cost = +inf if not dm > 0, else 0 if W = 0,
+ *       else 0.5 (W log dm - wa log(da da) - wb log(db db));
+ *   - candidates of i: the other mergeable Gaussians (all params finite, l11
+ *     and l22 nonzero) whose cell -- the 16x16 tile of the mean's pixel, the
+ *     mean clamped to the image -- is i's or a neighbour (3x3);
+ *   - a round: each Gaussian picks its cheapest candidate (ties: the smaller
+ *     index); the pairs (i, j), i < j, that pick each other are merged, all of
+ *     them or, if more than max_pairs, the max_pairs with the smallest
+ *     (fp32 rounding of the cost, i);
+ *   - apply: the merged Gaussian (gi_merge_pairs) takes the smaller index's
+ *     place, every other Gaussian keeps its params and relative order;
+ *   - gi_merge_to: rounds (each asking for at most the count still to remove)
+ *     until target is reached or a round finds no pair.
+ *   The cost uses the platform's fp64 log on each side of a comparison, so two
+ *   costs equal to within an ulp or two could order differently elsewhere; no
+ *   other floating-point step decides an index.
+ *   n          0 <= n < 2^30 (Cholesky-form params [n][8], device).
+ *   workspace  device, >= gi_merge_workspace_bytes(desc, n), 256-byte aligned;
+ *              no initialisation needed.  All three calls take a workspace of the
+ *              size for their n (gi_merge_to: for the starting n).
+ *   gi_merge_round: pairs device int32 [n/2][2] out, 8-byte aligned;
+ *              *h_npairs (host) = their count.  Waits for the count.
+ *   gi_merge_apply: the n_pairs disjoint pairs (as gi_merge_round writes them)
+ *              merged: out device [n - n_pairs][8], not aliasing params.
+ *              Asynchronous.
+ *   gi_merge_to: out device [n][8] (the first *h_n_out rows are the result), not
+ *              aliasing params; *h_rounds (host, may be NULL) = rounds done.
+ *              Waits for each round's count.
+ */
+size_t gi_merge_workspace_bytes(const gi_desc *desc, int64_t n);
+gi_status gi_merge_round(const gi_desc *desc, int64_t n, const float *params, int64_t max_pairs, int32_t *pairs,
+                         int64_t *h_npairs, void *workspace, size_t workspace_bytes, void *stream);
+gi_status gi_merge_apply(const gi_desc *desc, int64_t n, const float *params, int64_t n_pairs, const int32_t *pairs,
+                         float *out, void *workspace, size_t workspace_bytes, void *stream);
+gi_status gi_merge_to(const gi_desc *desc, int64_t n, const float *params, int64_t target, float *out,
+                      int64_t *h_n_out, int32_t *h_rounds, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gi_adc -- adaptive density control ("FlashImgs", Training features: every
+ *   300 steps from step 150, dead, out-of-bounds and bloated Gaussians are
+ *   relocated to high-error pixels; Library API: Session.densify).  The pages
+ *   give no thresholds; the reading (sum mode):
+ *   - flags (fp64 decisions): 1 dead -- a non-finite parameter, l11 or l22
+ *     zero, or max_k |c_k| < 1/255 (cannot move a pixel by one 8-bit level);
+ *     2 out of bounds -- the mean outside [0, W) x [0, H); 4 bloated -- the
+ *     larger eigenvalue of Sigma above t = (max(W, H)/16)^2, decided as
+ *     not (s11 <= t and s22 <= t and (t - s11)(t - s22) >= s21^2) with
+ *     s11 = l11 l11, s21 = l11 l21, s22 = l21 l21 + l22 l22;
+ *   - pixel error (fp32): r = target - image, e = fma(r_b, r_b, fma(r_g, r_g,
+ *     r_r r_r)), a NaN counting as 0;
+ *   - the K = min(#flagged, W H) pixels of largest e (ties: the smaller pixel
+ *     index), in ascending pixel index, go to the flagged Gaussians in
+ *     ascending index: mean = the pixel centre, l11 = l22 = s0, l21 = 0,
+ *     colour = r at the pixel (the Gaussian fills the residual at its centre).
+ *   params     device float [n][8], updated in place (sum mode, Cholesky form).
+ *   m, v       device float [n][8] or NULL: Adam moments; a relocated
+ *              Gaussian's rows are zeroed.
+ *   image, target  device float [3][H][W] (the current render and the target).
+ *   flags      device int32 [n] out (the flags above, 0 = kept) or NULL.
+ *   d_moved    device uint32 [1] out (K) or NULL.
+ *   workspace  device, >= gi_adc_workspace_bytes(desc, n), 256-byte aligned;
+ *              no initialisation needed.  Asynchronous (no host wait).
+ */
+size_t gi_adc_workspace_bytes(const gi_desc *desc, int64_t n);
+gi_status gi_adc(const gi_desc *desc, int64_t n, float *params, float *m, float *v, const float *image,
+                 const float *target, float s0, int32_t *flags, uint32_t *d_moved, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
  * gi_render_bwd_absgrad -- gi_render_bwd in the sum mode (dparams accumulated,
  *   no loss) that also accumulates each Gaussian's "absgrad" ("Drawing with
  *   Gaussians", 3D densification: the backward accumulates the per-pixel

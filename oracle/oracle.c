@@ -1030,14 +1030,18 @@ int64_t oracle_merge_round(int W, int H, int64_t n, const double *params, int64_
     int *cx = (int *)malloc(sizeof(int) * (n > 0 ? n : 1)), *cy = (int *)malloc(sizeof(int) * (n > 0 ? n : 1));
     int64_t *pick = (int64_t *)malloc(sizeof(int64_t) * (n > 0 ? n : 1));
     double *pc = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
-    for (int64_t i = 0; i < n; ++i) merge_cell(params + 8 * i, tx, ty, &cx[i], &cy[i]);
+    char *ok = (char *)malloc(n > 0 ? n : 1);
+    for (int64_t i = 0; i < n; ++i) {
+        ok[i] = (char)mergeable(params + 8 * i);
+        if (ok[i]) merge_cell(params + 8 * i, tx, ty, &cx[i], &cy[i]);
+    }
     #pragma omp parallel for schedule(dynamic, 64)
     for (int64_t i = 0; i < n; ++i) {
         pick[i] = -1;
         pc[i] = INFINITY;
-        if (!mergeable(params + 8 * i)) continue;
+        if (!ok[i]) continue;
         for (int64_t j = 0; j < n; ++j) {
-            if (j == i || !mergeable(params + 8 * j)) continue;
+            if (j == i || !ok[j]) continue;
             if (abs(cx[i] - cx[j]) > 1 || abs(cy[i] - cy[j]) > 1) continue;
             const double c = i < j ? merge_cost(params + 8 * i, params + 8 * j)
                                    : merge_cost(params + 8 * j, params + 8 * i);
@@ -1068,7 +1072,7 @@ int64_t oracle_merge_round(int W, int H, int64_t n, const double *params, int64_
     }
     if (best)
         for (int64_t i = 0; i < n; ++i) best[i] = pick[i];
-    free(cx); free(cy); free(pick); free(pc);
+    free(cx); free(cy); free(pick); free(pc); free(ok);
     return m;
 }
 
@@ -1087,7 +1091,9 @@ int64_t oracle_merge_apply(int64_t n, const double *params, int64_t npairs, cons
     return o;
 }
 
-/* Rounds until n_out == target or no pair is found: out[n, 8] (the first n_out rows used). */
+/* Rounds until n_out == target or no pair is found: out[n, 8] (the first n_out rows used).  The
+ * set is a set of fp32 parameters (the form every other call takes them in): after each round the
+ * merged rows are rounded to fp32, and the next round starts from those values. */
 int64_t oracle_merge_to(int W, int H, int64_t n, const double *params, int64_t target, double *out,
                         int64_t *rounds)
 {
@@ -1099,7 +1105,7 @@ int64_t oracle_merge_to(int W, int H, int64_t n, const double *params, int64_t t
         const int64_t np = oracle_merge_round(W, H, m, cur, m - target, pairs, NULL);
         if (np == 0) break;
         m = oracle_merge_apply(m, cur, np, pairs, out);
-        memcpy(cur, out, sizeof(double) * 8 * m);
+        for (int64_t k = 0; k < 8 * m; ++k) cur[k] = (double)(float)out[k];
         ++r;
     }
     memcpy(out, cur, sizeof(double) * 8 * m);

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgi.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["gi_api.hip", "k_preprocess.hip", "k_binning.hip", "k_raster_sum.hip", "k_raster_alpha.hip",
-           "k_optim.hip", "k_params.hip", "k_ssim.hip"]
+           "k_optim.hip", "k_params.hip", "k_ssim.hip", "k_adapt.hip"]
 ARCH = os.environ.get("GI_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

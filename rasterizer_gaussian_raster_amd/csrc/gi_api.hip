@@ -530,6 +530,110 @@ gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const
     return hip_status(gi::launch_merge_pairs(n_pairs, n, params, pairs, out, as_stream(stream)));
 }
 
+size_t gi_merge_workspace_bytes(const gi_desc *desc, int64_t n) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 30)) return 0;
+    return gi::merge_workspace_bytes(desc->width, desc->height, n);
+}
+
+namespace {
+bool merge_args_ok(const gi_desc *desc, int64_t n, const float *params, const void *workspace,
+                   size_t workspace_bytes) {
+    if (!desc_ok(desc) || n < 0 || n >= (1ll << 30)) return false;
+    if (!workspace || !aligned256(workspace)) return false;
+    if (workspace_bytes < gi::merge_workspace_bytes(desc->width, desc->height, n)) return false;
+    return n == 0 || (params && aligned16(params));
+}
+
+// The count a merge round left in device memory, read back (one wait on the stream).
+gi_status read_count(const uint32_t *d_count, int64_t *h, hipStream_t s) {
+    uint32_t c = 0;
+    hipError_t e = hipMemcpyAsync(&c, d_count, sizeof(c), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return GI_ERR_HIP;
+    *h = (int64_t)c;
+    return GI_OK;
+}
+}  // namespace
+
+gi_status gi_merge_round(const gi_desc *desc, int64_t n, const float *params, int64_t max_pairs, int32_t *pairs,
+                         int64_t *h_npairs, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!merge_args_ok(desc, n, params, workspace, workspace_bytes) || max_pairs < 0 || !h_npairs) return GI_ERR_INVALID_ARG;
+    if (n >= 2 && (!pairs || (reinterpret_cast<uintptr_t>(pairs) & 7u))) return GI_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    uint32_t *cnt = gi::merge_count_ptr(workspace, desc->width, desc->height, n);
+    int32_t *dst = n >= 2 ? pairs : gi::merge_pairs_buffer(workspace, desc->width, desc->height, n);
+    const uint32_t mp = (uint32_t)(max_pairs < n / 2 ? max_pairs : n / 2);
+    if (gi::launch_merge_round(desc->width, desc->height, (int)n, (int)n, params, mp, dst, cnt, workspace, s) !=
+        hipSuccess)
+        return GI_ERR_HIP;
+    return read_count(cnt, h_npairs, s);
+}
+
+gi_status gi_merge_apply(const gi_desc *desc, int64_t n, const float *params, int64_t n_pairs, const int32_t *pairs,
+                         float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!merge_args_ok(desc, n, params, workspace, workspace_bytes) || n_pairs < 0 || 2 * n_pairs > n)
+        return GI_ERR_INVALID_ARG;
+    if (n_pairs > 0 && (!pairs || (reinterpret_cast<uintptr_t>(pairs) & 7u))) return GI_ERR_INVALID_ARG;
+    if (n > n_pairs && (!out || !aligned16(out) || out == params)) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_merge_apply((int)n, (int)n, params, n_pairs, pairs, out, workspace, desc->width,
+                                             desc->height, as_stream(stream)));
+}
+
+gi_status gi_merge_to(const gi_desc *desc, int64_t n, const float *params, int64_t target, float *out,
+                      int64_t *h_n_out, int32_t *h_rounds, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!merge_args_ok(desc, n, params, workspace, workspace_bytes) || target < 0 || !h_n_out) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!out || !aligned16(out) || out == params)) return GI_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const int W = desc->width, H = desc->height;
+    float *tmp = gi::merge_tmp_params(workspace, W, H, n);
+    int32_t *pairs = gi::merge_pairs_buffer(workspace, W, H, n);
+    uint32_t *cnt = gi::merge_count_ptr(workspace, W, H, n);
+    // rounds alternate between out and tmp; the workspace plan of the first n serves every round
+    const float *cur = params;
+    float *dst = out;
+    int64_t m = n;
+    int32_t rounds = 0;
+    while (m > target && m >= 2) {
+        if (gi::launch_merge_round(W, H, (int)n, (int)m, cur, (uint32_t)((m - target) < m / 2 ? (m - target) : m / 2),
+                                   pairs, cnt, workspace, s) != hipSuccess)
+            return GI_ERR_HIP;
+        int64_t np = 0;
+        const gi_status st = read_count(cnt, &np, s);
+        if (st != GI_OK) return st;
+        if (np == 0) break;
+        if (gi::launch_merge_apply((int)n, (int)m, cur, np, pairs, dst, workspace, W, H, s) != hipSuccess)
+            return GI_ERR_HIP;
+        m -= np;
+        ++rounds;
+        cur = dst;
+        dst = dst == out ? tmp : out;
+    }
+    if (cur != out && m > 0 &&
+        hipMemcpyAsync(out, cur, (size_t)m * 32, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return GI_ERR_HIP;
+    *h_n_out = m;
+    if (h_rounds) *h_rounds = rounds;
+    return GI_OK;
+}
+
+size_t gi_adc_workspace_bytes(const gi_desc *desc, int64_t n) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return 0;
+    return gi::adc_workspace_bytes(desc->width, desc->height, n);
+}
+
+gi_status gi_adc(const gi_desc *desc, int64_t n, float *params, float *m, float *v, const float *image,
+                 const float *target, float s0, int32_t *flags, uint32_t *d_moved, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if ((int64_t)desc->width * desc->height >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!std::isfinite(s0) || !image || !target || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::adc_workspace_bytes(desc->width, desc->height, n)) return GI_ERR_INVALID_ARG;
+    if (n > 0 && (!params || !aligned16(params) || (m && !aligned16(m)) || (v && !aligned16(v))))
+        return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_adc(desc->width, desc->height, (int)n, params, m, v, image, target, s0, flags, d_moved,
+                                     workspace, as_stream(stream)));
+}
+
 gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *records, const uint16_t *pixbox,
                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *tile_order,
                                 const uint32_t *vals, int64_t capacity, const float *dL_dimage, float *dparams,

@@ -166,9 +166,23 @@ size_t ssim_workspace_bytes(int W, int H);
 hipError_t launch_loss_ssim(int W, int H, const float *x, const float *y, float w1, float w2, float ws, float *dL,
                             float *loss, void *ws_ptr, hipStream_t s);
 
-// k_params.hip
+// k_adapt.hip
 hipError_t launch_merge_pairs(int64_t np, int64_t n, const float *params, const int32_t *pairs, float *out,
                               hipStream_t s);
+size_t merge_workspace_bytes(int W, int H, int64_t n);
+// One merge round: the pairs (ascending smaller index, at most max_pairs) and their count to
+// d_count (ws laid out for n_cap >= n Gaussians).
+hipError_t launch_merge_round(int W, int H, int n_cap, int n, const float *params, uint32_t max_pairs,
+                              int32_t *pairs_out, uint32_t *d_count, void *ws, hipStream_t s);
+// params with the disjoint pairs merged, index order kept: out [n - np][8].
+hipError_t launch_merge_apply(int n_cap, int n, const float *params, int64_t np, const int32_t *pairs, float *out,
+                              void *ws, int W, int H, hipStream_t s);
+float *merge_tmp_params(void *ws, int W, int H, int64_t n);       // a second [n][8] params buffer
+int32_t *merge_pairs_buffer(void *ws, int W, int H, int64_t n);   // [n/2 + 1][2]
+uint32_t *merge_count_ptr(void *ws, int W, int H, int64_t n);     // a device counter
+size_t adc_workspace_bytes(int W, int H, int64_t n);
+hipError_t launch_adc(int W, int H, int n, float *params, float *m, float *v, const float *image,
+                      const float *target, float s0, int32_t *flags_out, uint32_t *d_moved, void *ws, hipStream_t s);
 hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
                                      hipStream_t s);
 hipError_t launch_params_to_cholesky_grad(int kind, int64_t n, const float *in, float fx, float fy,

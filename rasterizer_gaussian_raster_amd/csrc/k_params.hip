@@ -234,50 +234,6 @@ __global__ __launch_bounds__(256) void k_grad_gather_params(int kind, int64_t n,
     dparams[2 * g + 1] = q;
 }
 
-// Moment-matching merge of Gaussian pairs: one thread per pair, in fp64 (the covariance sum and
-// its factor cancel; the chip's fp64 rate is no concern for a per-pair op).  Masses
-// w = |det L| sum |c|; mean and covariance of the weighted mixture; L = chol(Sigma) with a positive
-// diagonal; colours keep each channel's integral.  An index outside [0, n) gives a NaN row.
-__global__ __launch_bounds__(256) void k_merge_pairs(int64_t np, int64_t n, const float4 *__restrict__ params,
-                                                    const int2 *__restrict__ pairs, float4 *__restrict__ out) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= np) return;
-    const int2 pr = pairs[t];
-    if (pr.x < 0 || pr.y < 0 || pr.x >= n || pr.y >= n) {
-        const float q = __int_as_float(0x7fc00000);
-        out[2 * t] = make_float4(q, q, q, q);
-        out[2 * t + 1] = make_float4(q, q, q, q);
-        return;
-    }
-    const float4 a0 = params[2 * (int64_t)pr.x], a1 = params[2 * (int64_t)pr.x + 1];
-    const float4 b0 = params[2 * (int64_t)pr.y], b1 = params[2 * (int64_t)pr.y + 1];
-    const double da = fabs((double)a0.z * a1.x), db = fabs((double)b0.z * b1.x);
-    const double wa = da * (fabs((double)a1.y) + fabs((double)a1.z) + fabs((double)a1.w));
-    const double wb = db * (fabs((double)b1.y) + fabs((double)b1.z) + fabs((double)b1.w));
-    const double W = wa + wb;
-    const double fa = W > 0.0 ? wa / W : 0.5, fb = W > 0.0 ? wb / W : 0.5;
-    const double mx = fa * a0.x + fb * b0.x, my = fa * a0.y + fb * b0.y;
-    const double ax = a0.x - mx, ay = a0.y - my, bx = b0.x - mx, by = b0.y - my;
-    const double al11 = a0.z, al21 = a0.w, al22 = a1.x, bl11 = b0.z, bl21 = b0.w, bl22 = b1.x;
-    const double s11 = fa * (al11 * al11 + ax * ax) + fb * (bl11 * bl11 + bx * bx);
-    const double s21 = fa * (al11 * al21 + ax * ay) + fb * (bl11 * bl21 + bx * by);
-    const double s22 = fa * (al21 * al21 + al22 * al22 + ay * ay) + fb * (bl21 * bl21 + bl22 * bl22 + by * by);
-    const double l11 = sqrt(s11), l21 = s21 / l11, l22 = sqrt(s22 - l21 * l21);
-    const double dn = l11 * l22;
-    out[2 * t] = make_float4((float)mx, (float)my, (float)l11, (float)l21);
-    out[2 * t + 1] = make_float4((float)l22, (float)((da * a1.y + db * b1.y) / dn), (float)((da * a1.z + db * b1.z) / dn),
-                                 (float)((da * a1.w + db * b1.w) / dn));
-}
-
-hipError_t launch_merge_pairs(int64_t np, int64_t n, const float *params, const int32_t *pairs, float *out,
-                              hipStream_t s) {
-    if (np == 0) return hipSuccess;
-    k_merge_pairs<<<(unsigned)((np + 255) / 256), 256, 0, s>>>(np, n, reinterpret_cast<const float4 *>(params),
-                                                              reinterpret_cast<const int2 *>(pairs),
-                                                              reinterpret_cast<float4 *>(out));
-    return hipGetLastError();
-}
-
 hipError_t launch_params_to_cholesky(int kind, int64_t n, const float *in, float fx, float fy, float *out,
                                      hipStream_t s) {
     if (n == 0) return hipSuccess;

@@ -95,6 +95,12 @@ def load():
         "gi_render_fwd_bwd_l2": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P], i32),
         "gi_render_image": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, i64, P, P, P, sz, P, P, P,
                              P], i32),
+        "gi_merge_workspace_bytes": ([D, i64], sz),
+        "gi_merge_round": ([D, i64, P, i64, P, P, P, sz, P], i32),
+        "gi_merge_apply": ([D, i64, P, i64, P, P, P, sz, P], i32),
+        "gi_merge_to": ([D, i64, P, i64, P, P, P, P, sz, P], i32),
+        "gi_adc_workspace_bytes": ([D, i64], sz),
+        "gi_adc": ([D, i64, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P], i32),
         "gi_render_image_noalloc_max_bytes": ([], sz),
         "gi_render_image_noalloc": ([D, i64, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, i64, P, P, P, P, P,
                                      P], i32),
@@ -284,6 +290,44 @@ def gi_grad_gather(d, kind, n, params, fx, fy, records, offsets, capacity, works
                                  _ptr(records), _ptr(offsets), int(capacity), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _ptr(dparams), _stream(stream)),
            "gi_grad_gather")
+
+
+def gi_merge_workspace_bytes(d, n):
+    return int(load().gi_merge_workspace_bytes(ctypes.byref(d), int(n)))
+
+
+def gi_merge_round(d, n, params, max_pairs, pairs, workspace, stream=None):
+    """One merge round; returns the number of pairs written to pairs [n/2][2] (int32)."""
+    h = ctypes.c_int64(-1)
+    _check(load().gi_merge_round(ctypes.byref(d), int(n), _ptr(params), int(max_pairs), _ptr(pairs), ctypes.byref(h),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gi_merge_round")
+    return int(h.value)
+
+
+def gi_merge_apply(d, n, params, n_pairs, pairs, out, workspace, stream=None):
+    _check(load().gi_merge_apply(ctypes.byref(d), int(n), _ptr(params), int(n_pairs), _ptr(pairs), _ptr(out),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gi_merge_apply")
+
+
+def gi_merge_to(d, n, params, target, out, workspace, stream=None):
+    """Merge rounds down to target; returns (rows of out used, rounds)."""
+    h, r = ctypes.c_int64(-1), ctypes.c_int32(-1)
+    _check(load().gi_merge_to(ctypes.byref(d), int(n), _ptr(params), int(target), _ptr(out), ctypes.byref(h),
+                              ctypes.byref(r), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)), "gi_merge_to")
+    return int(h.value), int(r.value)
+
+
+def gi_adc_workspace_bytes(d, n):
+    return int(load().gi_adc_workspace_bytes(ctypes.byref(d), int(n)))
+
+
+def gi_adc(d, n, params, m, v, image, target, s0, flags, d_moved, workspace, stream=None):
+    _check(load().gi_adc(ctypes.byref(d), int(n), _ptr(params), _ptr(m), _ptr(v), _ptr(image), _ptr(target),
+                         float(s0), _ptr(flags), _ptr(d_moved), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream)), "gi_adc")
 
 
 def gi_render_bwd_absgrad(d, n, records, pixbox, offsets, ranges, vals, capacity, dL_dimage, dparams, dabs,

@@ -210,6 +210,18 @@ def cholesky_params(params, kind=gi.PARAMS_RS, fx=1.0, fy=1.0, out=None, stream=
     return out
 
 
+def merge_to(params, width, height, target, stream=None):
+    """Merge a Cholesky-form set [n,8] down to `target` Gaussians (gi_merge_to: rounds of mutual
+    cheapest pairs under the moment-matching cost); returns the new set [m,8] (m > target only when
+    no two Gaussians left in neighbouring cells pick each other) and the number of rounds."""
+    n = params.shape[0]
+    d = gi.desc(width, height)
+    ws = torch.empty(gi.gi_merge_workspace_bytes(d, n), dtype=torch.uint8, device=params.device)
+    out = torch.empty((max(n, 1), 8), dtype=torch.float32, device=params.device)
+    m, rounds = gi.gi_merge_to(d, n, params.contiguous(), target, out, ws, stream)
+    return out[:m].clone(), rounds
+
+
 class FitterRS:
     """Fits rotation-scale Gaussians (mux, muy, sx, sy, theta, cr, cg, cb) with L2 loss and Adam
     (sum mode).  A step: gi_fit_step_sum with GI_FIT_NO_UPDATE on their Cholesky form (preprocess,
@@ -343,6 +355,23 @@ class Fitter:
         self.raster.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(self.raster.desc, self.n,
                                                                           self.raster.capacity),
                                          dtype=torch.uint8, device=dev)
+
+    def densify(self, s0=1.5):
+        """One adaptive-density-control pass (gi_adc, sum mode): dead, out-of-bounds and bloated
+        Gaussians are moved to the pixels of largest error of the last rendered image (their Adam
+        moments cleared).  Returns a device tensor with the number moved.  The next step sets up
+        the binning afresh."""
+        if self.logit is not None:
+            raise ValueError("density control is for the sum mode")
+        r = self.raster
+        if getattr(self, "_adc_ws", None) is None:
+            self._adc_ws = torch.empty(gi.gi_adc_workspace_bytes(r.desc, self.n), dtype=torch.uint8,
+                                       device=self.params.device)
+            self._adc_moved = torch.zeros(1, dtype=torch.int32, device=self.params.device)
+        gi.gi_adc(r.desc, self.n, self.params, self.m, self.v, r.image, self.target, s0, None, self._adc_moved,
+                  self._adc_ws)
+        self.prepared = False
+        return self._adc_moved
 
     def check_capacity(self):
         """Host wait: grow the pair buffers when the last binning came near (or over) capacity."""
