@@ -41,6 +41,30 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def stats_us(x_us):
+    x = np.asarray(x_us, np.float64)
+    return {"median": round(float(np.median(x)), 2), "p10": round(float(np.percentile(x, 10)), 2),
+            "p90": round(float(np.percentile(x, 90)), 2), "mean": round(float(np.mean(x)), 2), "n": int(x.size)}
+
+
+def batch_time_us(fn, per_batch=20, batches=15, warm=5):
+    """Per-call time of fn from batches of back-to-back calls on the current stream, bracketed by HIP
+    events (the events' own overhead is spread over a batch): one value per batch, in microseconds."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(E(), E()) for _ in range(batches)]
+    for a, b in ev:
+        a.record()
+        for _ in range(per_batch):
+            fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3 / per_batch
+
+
 def binned_pairs(W, H, ranges):
     """sum over tiles of (list length) x (in-image pixels of the tile)."""
     tx = -(-W // 16)
@@ -113,10 +137,12 @@ def cpu_baseline(wl, params, target_seconds=15.0):
         npix = int(min(W * H, npix * min(16.0, max(2.0, target_seconds / max(t, 1e-3)))))
         t = run(npix)
     per_frame = t * (W * H) / npix
+    what = (f"every pixel of the {W}x{H} frame ({npix}), all {params.shape[0]} Gaussians per pixel "
+            f"(render + gradient), {t:.1f} s: one full step, not extrapolated" if npix == W * H else
+            f"{npix} random pixels of the {W}x{H} frame, all {params.shape[0]} Gaussians per pixel "
+            f"(render + gradient), {t:.1f} s, extrapolated linearly to the full frame")
     return {"value": 1.0 / per_frame, "unit": "fwd+bwd steps/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{npix} random pixels of the {W}x{H} frame, all {params.shape[0]} Gaussians per pixel "
-                      f"(render + gradient), {t:.1f} s, extrapolated linearly to the full frame",
-            "seconds": round(t, 3)}
+            "sample": what, "seconds": round(t, 3)}
 
 
 def cpu_baseline_alpha(wl, params, logit, bg, target_seconds=15.0):
@@ -497,9 +523,12 @@ def bench_adc(args, target, params, dev):
 
 
 def bench_rs(args, wlname, target, dev):
-    """Rotation-scale Gaussians on a sum workload: one step = preprocess and binning of the Cholesky
-    form + the fused forward / L2 / backward raster + gi_adam_step_pairs_rs (gather, chain rule,
-    Adam, loss, and the updated Gaussians' Cholesky form for the next step)."""
+    """Rotation-scale Gaussians on a sum workload: one step = gi_fit_step_sum without its update
+    (preprocess and binning of the Cholesky form, the fused forward / L2 / backward raster, which
+    finishes the sort per tile) + gi_adam_step_pairs_rs (gather of the pair sums, their map to the
+    rotation-scale gradient, Adam, the loss, and the updated Gaussians' Cholesky form for the next
+    step).  The breakdown times the stand-alone conversion, the fused raster on the step's binning,
+    and the update pass, between HIP events."""
     import torch
     from rasterizer_gaussian_raster_amd import gi, synth
     from rasterizer_gaussian_raster_amd.pipeline import FitterRS
@@ -542,7 +571,7 @@ def bench_rs(args, wlname, target, dev):
     torch.cuda.synchronize()
     ms = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(3)] for k in range(nk)])
     conv_s, fused_s, chain_s = (float(x) * 1e-3 for x in ms.mean(0))
-    log(f"[bench] convert {conv_s*1e6:.1f} us, fused raster {fused_s*1e6:.1f} us, gather+chain+adam "
+    log(f"[bench] convert {conv_s*1e6:.1f} us, fused raster {fused_s*1e6:.1f} us, gather+map+adam "
         f"{chain_s*1e6:.1f} us")
     ranges = r.ranges.cpu().numpy().view(np.uint32)
     pairs = binned_pairs(W, H, ranges)
@@ -591,6 +620,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="kodak_768x512_50k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the 3840x2160 HBM-rate measurements")
     ap.add_argument("--params", choices=["cholesky", "rs"], default="cholesky",
                     help="parameter form of the Gaussians (rs: rotation-scale, converted on the GPU each step)")
     ap.add_argument("--loss", default="l2", help="l2, or weights w1,w2,ws of w1 L1 + w2 L2 + ws (1 - SSIM)")
@@ -649,6 +679,7 @@ def main():
         fit._step()
     torch.cuda.synchronize()
     r.d_num[1] = 0
+    M_start = int(r.d_num[0].item()) & 0xFFFFFFFF
     # the timed region: K eager steps, no host wait in between
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -656,10 +687,20 @@ def main():
     torch.cuda.synchronize()
     t_train = time.perf_counter() - t0
     M_max = int(r.d_num[1].item()) & 0xFFFFFFFF
+    M_end = int(r.d_num[0].item()) & 0xFFFFFFFF
     assert 0 < M_max <= r.capacity, "tile-pair capacity exceeded in a timed step"
     ms_step = 1e3 * t_train / args.steps
     final_loss = float(fit.loss.item())
-    log(f"[bench] train: {ms_step:.4f} ms/step, loss {final_loss:.4e}")
+    log(f"[bench] train: {ms_step:.4f} ms/step, loss {final_loss:.4e}, pairs {M_start} -> {M_end} (max {M_max})")
+    # per-step distribution (after the timed run): steps one by one between HIP events
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    sev = [(E(), E()) for _ in range(40)]
+    for a, b in sev:
+        a.record()
+        fit._step()
+        b.record()
+    torch.cuda.synchronize()
+    step_us = np.array([a.elapsed_time(b) for a, b in sev]) * 1e3
 
     # ---------------- render-only: preprocess + bin/sort + raster, and raster alone ----------------
     rend = Raster(W, H, wl.n)
@@ -667,42 +708,21 @@ def main():
     M = rend.bin(sync=True)
     rend.set_capacity(int(M * 1.5) + 4096)
     rend.bin(sync=True, order=True)
-    # kernel timing: HIP events on the launch stream around the fused raster kernel of the training
-    # step, and around the separate forward (with L2) and backward kernels, on this binning
-    nk = max(20, min(args.steps, 500))
-    E = lambda: torch.cuda.Event(enable_timing=True)
+    # kernel timing: batches of back-to-back launches between HIP events on the launch stream, on
+    # this binning: the fused raster of the training step, the forward with the L2 terms, the
+    # plain forward, the backward to the pair slots
     dL = torch.empty_like(target)
-    ev = [[E() for _ in range(5)] for _ in range(nk)]
-    for k in range(nk):
-        ev[k][0].record()
-        rend.forward_backward_l2(target)
-        ev[k][1].record()
-    for k in range(nk):
-        ev[k][2].record()
-        rend.forward_l2(target, dL)
-        ev[k][3].record()
-        rend.backward(dL, None)
-        ev[k][4].record()
-    torch.cuda.synchronize()
-    fused_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(nk)])
-    fwd_ms = np.array([ev[k][2].elapsed_time(ev[k][3]) for k in range(nk)])
-    bwd_ms = np.array([ev[k][3].elapsed_time(ev[k][4]) for k in range(nk)])
-    log(f"[bench] fused fwd+bwd {np.median(fused_ms)*1e3:.1f} us (separate: fwd {np.median(fwd_ms)*1e3:.1f} us, "
-        f"bwd {np.median(bwd_ms)*1e3:.1f} us)")
-    reps = max(50, args.steps // 4)
-
-    def loop_time(fn):
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / reps
-
-    t_render = loop_time(lambda: rend.render(fit.params, sync=False))
-    t_cached = loop_time(lambda: rend.forward())
+    rend.forward_l2(target, dL)
+    fused_us = batch_time_us(lambda: rend.forward_backward_l2(target))
+    fwd_us = batch_time_us(lambda: rend.forward_l2(target, dL))
+    fwd0_us = batch_time_us(lambda: rend.forward())
+    rend.forward_l2(target, dL)
+    bwd_us = batch_time_us(lambda: rend.backward(dL, None))
+    log(f"[bench] fused fwd+bwd {np.median(fused_us):.1f} us (separate: fwd {np.median(fwd_us):.1f} us, "
+        f"bwd {np.median(bwd_us):.1f} us; plain forward {np.median(fwd0_us):.1f} us)")
+    render_us = batch_time_us(lambda: rend.render(fit.params, sync=False))
+    t_render = float(np.median(render_us)) * 1e-6
+    t_cached = float(np.median(fwd0_us)) * 1e-6
     log(f"[bench] render {t_render*1e6:.1f} us ({1/t_render:.0f} FPS), cached raster {t_cached*1e6:.1f} us")
 
     # ---------------- work counts of the timed problem ----------------
@@ -715,22 +735,24 @@ def main():
     pixbox = rend.pixbox.cpu().numpy().view(np.uint16)
     pairs = binned_pairs(W, H, ranges)
     evald = evaluated_pairs(W, H, keys, vals, pixbox)
-    fwd_s = float(np.mean(fwd_ms)) * 1e-3
-    bwd_s = float(np.mean(bwd_ms)) * 1e-3
-    fused_s = float(np.mean(fused_ms)) * 1e-3
-    fwd_tf = FLOP_FWD * pairs / fwd_s / 1e12
-    bwd_tf = FLOP_BWD * pairs / bwd_s / 1e12
-    fused_tf = (FLOP_FWD + FLOP_BWD) * pairs / fused_s / 1e12
+    fwd_s = float(np.median(fwd_us)) * 1e-6
+    bwd_s = float(np.median(bwd_us)) * 1e-6
+    fused_s = float(np.median(fused_us)) * 1e-6
 
-    def roof(name, kfile, kname, tf, secs):
-        traffic = load_traffic(kfile, kname)
+    def roof(kname, flop, secs, us):
+        tf = flop * pairs / secs / 1e12
         return {"bound": "alu", "kernel": kname, "achieved": round(tf, 3), "peak": PEAK_FP32,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32, 4),
-                "traffic": traffic, "avg_launch_us": round(secs * 1e6, 2)}
+                "traffic": load_traffic("k_raster_sum.hip", kname), "avg_launch_us": round(secs * 1e6, 2),
+                "launch_us": stats_us(us)}
 
-    roof_fwd = roof("fwd", "k_raster_sum.hip", "k_render_sum_fwd<true>", fwd_tf, fwd_s)
-    roof_bwd = roof("bwd", "k_raster_sum.hip", "k_render_sum_bwd<false>", bwd_tf, bwd_s)
-    roof_fused = roof("fused", "k_raster_sum.hip", "k_render_sum_fused", fused_tf, fused_s)
+    roof_fwd = roof("k_render_sum_fwd<true>", FLOP_FWD, fwd_s, fwd_us)
+    # the same launch priced on the pairs the kernel evaluates (its quadrant lists)
+    tf_e = FLOP_FWD * evald / fwd_s / 1e12
+    roof_fwd["achieved_on_evaluated_pairs"] = round(tf_e, 3)
+    roof_fwd["frac_on_evaluated_pairs"] = round(tf_e / PEAK_FP32, 4)
+    roof_bwd = roof("k_render_sum_bwd<false>", FLOP_BWD, bwd_s, bwd_us)
+    roof_fused = roof("k_render_sum_fused", FLOP_FWD + FLOP_BWD, fused_s, fused_us)
 
     out = {
         "metric": METRIC,
@@ -747,21 +769,28 @@ def main():
         "data": "synthetic",
         "config": {"workload": wlname, "width": W, "height": H, "gaussians": wl.n, "mode": "sum",
                    "tiles": int(rend.T), "tile_pairs": int(M), "binned_pixel_pairs": pairs,
-                   "evaluated_pixel_pairs_fwd": evald},
+                   "evaluated_pixel_pairs_fwd": evald,
+                   "tile_pairs_timed_steps": {"first": M_start, "last": M_end, "max": M_max}},
+        "step_us": stats_us(step_us),
         "render_fps": round(1.0 / t_render, 1),
         "mpix_per_s": round(W * H / t_render / 1e6, 1),
         "cached_raster_fps": round(1.0 / t_cached, 1),
-        "fit_seconds_2800_steps": round(2800 * ms_step / 1e3, 3),
-        "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
-                  "kernels_us / roofline: HIP events on the launch stream around the fused raster kernel of the "
-                  "training step and the separate forward / backward kernels, on the trained parameters' binning",
+        "render_us": stats_us(render_us),
+        "projected_fit_seconds_2800_steps": round(2800 * ms_step / 1e3, 3),
+        "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; step_us: "
+                  "40 later steps one by one between HIP events; kernels and render: medians over batches of 20 "
+                  "back-to-back launches between HIP events on the launch stream, on the trained parameters' "
+                  "binning (work counts of that binning)",
         "final_loss": final_loss,
         "kernels_us": {"render_fwd_bwd_fused": round(fused_s * 1e6, 2), "render_fwd_l2": round(fwd_s * 1e6, 2),
-                       "render_bwd": round(bwd_s * 1e6, 2)},
+                       "render_fwd": round(t_cached * 1e6, 2), "render_bwd": round(bwd_s * 1e6, 2)},
         "roofline": roof_fused,
         "roofline_fwd": roof_fwd,
         "roofline_bwd": roof_bwd,
     }
+    if not args.no_hbm:
+        log("[bench] HBM rates of the memory-bound kernels at 3840x2160 / 2M ...")
+        out["hbm_3840x2160_2m"] = hbm_rates_4k(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a pixel sample ...")
         out["cpu_baseline"] = cpu_baseline(wl, w["params"])
@@ -769,6 +798,52 @@ def main():
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
 
+
+def hbm_rates_4k(dev):
+    """Achieved HBM rate (algorithmic bytes / time) of the preprocess, the binning (all its kernels)
+    and the Adam pass with the per-pair gather on the 3840x2160 / 2M workload, whose buffers (64 MB of
+    params, 70+ MB of pairs) exceed the caches: medians of batches of back-to-back calls."""
+    import torch
+    from rasterizer_gaussian_raster_amd import gi, synth
+    from rasterizer_gaussian_raster_amd.pipeline import Raster
+    w = synth.make_workload("render_3840x2160_2m")
+    W, H, n = 3840, 2160, w["workload"].n
+    P = torch.from_numpy(w["params"]).to(dev)
+    r = Raster(W, H, n)
+    r.preprocess(P)
+    M = r.bin(sync=True)
+    r.set_capacity(int(M * 1.25) + 4096)
+    r.bin(sync=True)
+    T = r.T
+    pre = batch_time_us(lambda: r.preprocess(P), per_batch=10, batches=7)
+    bins = batch_time_us(lambda: r.bin(sync=False, order=False), per_batch=5, batches=7)
+    G = torch.zeros((3, H, W), dtype=torch.float32, device=dev)
+    G[:, ::7, ::5] = 1e-3
+    r.backward(G, None)
+    Mo, V = torch.zeros_like(P), torch.zeros_like(P)
+    Pc = P.clone()
+    lr = [0.0] * 8                                  # the update pass itself, params left unchanged
+    adam = batch_time_us(lambda: gi.gi_adam_step_pairs(r.desc, n, r.offsets, r.capacity, r.bwd_ws, Pc, Mo, V, lr,
+                                                       0.9, 0.999, 1e-8, 1), per_batch=10, batches=7)
+    rows = {
+        "k_preprocess": (32 + 44) * n,
+        "binning (gi_bin_sort)": 12 * n + 4 * n + (8 + 8 + 8) * M + 8 * T,
+        "k_adam_pairs": (3 * 32 * 2 + 4) * n + 32 * M,
+    }
+    out = {"gaussians": n, "tile_pairs": M, "tiles": T,
+           "bytes_per_unit": {"k_preprocess": "32 B read + 44 B written per Gaussian",
+                              "binning (gi_bin_sort)": "12 B read + 4 B written per Gaussian; 8 B written (first "
+                                                       "pass), 8 B read + 8 B written (bucket pass) per pair; "
+                                                       "8 B per tile",
+                              "k_adam_pairs": "p, m, v read and written (192 B) + offsets (4 B) per Gaussian, "
+                                              "32 B per pair slot"}}
+    for name, us in (("k_preprocess", pre), ("binning (gi_bin_sort)", bins), ("k_adam_pairs", adam)):
+        t = float(np.median(us)) * 1e-6
+        gbs = rows[name] / t / 1e9
+        out[name] = {"us": stats_us(us), "algorithmic_bytes": int(rows[name]), "achieved_gbs": round(gbs, 1),
+                     "frac_of_8tbs": round(gbs / PEAK_HBM, 4)}
+        log(f"[bench]   {name}: {t*1e6:.1f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM:.2f} of 8 TB/s)")
+    return out
 
 if __name__ == "__main__":
     main()

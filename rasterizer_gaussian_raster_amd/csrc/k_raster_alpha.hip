@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, con
                                                           float *__restrict__ vbg, float lr_bg,
                                                           const float *__restrict__ loss_part, double inv_count,
                                                           float *__restrict__ loss) {
-    const int nb = (2 * n + 255) / 256;
+    const int nb = (int)((2 * (int64_t)n + 255) / 256);
     float c1, c2;
     adam_step_bias(a, c1, c2);
     const bool ok = offsets[n] <= capacity;               // else the binning overflowed: zero gradients
@@ -494,8 +494,9 @@ __global__ __launch_bounds__(256) void k_adam_pairs_alpha(int n, int ntiles, con
         }
         return;
     }
-    const int i = blockIdx.x * 256 + threadIdx.x;          // lane h = i & 1 of Gaussian i >> 1: params 4h .. 4h + 3
-    const int g = i >> 1, h = i & 1;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // lane h = i & 1 of Gaussian i >> 1: params 4h .. 4h + 3
+    const int64_t g = i >> 1;
+    const int h = (int)(i & 1);
     if (g >= n) return;
     const uint32_t o0 = offsets[g], o1 = ok ? offsets[g + 1] : o0;
     float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -537,7 +538,7 @@ hipError_t launch_adam_pairs_alpha(int n, int W, int H, const uint32_t *offsets,
     const BwdPlan pl = make_bwd_plan(W, H, capacity);
     const AdamHP a = make_adam_hp(lr, beta1, beta2, eps, step, nullptr);
     const char *w = static_cast<const char *>(ws);
-    k_adam_pairs_alpha<<<(2 * n + 255) / 256 + 2, 256, 0, s>>>(
+    k_adam_pairs_alpha<<<(unsigned)((2 * (int64_t)n + 255) / 256) + 2, 256, 0, s>>>(
         n, ntiles, offsets, (uint32_t)capacity, reinterpret_cast<const float4 *>(w + pl.off_part),
         reinterpret_cast<const float *>(w + pl.off_logit), reinterpret_cast<const float4 *>(w + pl.off_bg),
         reinterpret_cast<float4 *>(p), reinterpret_cast<float4 *>(m), reinterpret_cast<float4 *>(v), a, logit, ml, vl,
