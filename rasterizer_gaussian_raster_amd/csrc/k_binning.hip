@@ -672,18 +672,20 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
 // 4w: the first pass for one-group segments, 512 threads per group
 // ---------------------------------------------------------------------------
 // With one group (256 Gaussians) per block the first pass runs about one block
-// per CU and is bound by the latency of each wave's instruction stream and of
-// its barriers, not by memory: 8 waves share the digit table loads, the
-// ranking and the stores (1024 threads measured slower: one such block per CU
-// leaves a tail once the groups outnumber the CUs), and the block takes four
-// barriers for a one-chunk group.  Threads 0..255 own the group's Gaussians.
-// The group sums and the digit table are read raw (no count kernel ran): each
-// block forms its Gaussians' emission offsets, writes offsets[], and workgroup
-// 0 publishes M and the bucket starts.  Each key is regenerated from the
-// group's emission scan (binary search in LDS) and stored straight from its
-// register: position = the block's next slot of the digit + the chunk's keys of
-// the digit in earlier waves + its rank among its wave's keys of the digit
-// (ballots, in key order), so the pass is stable.
+// per CU and is bound by latency -- of the loads that feed it and of each
+// wave's instruction stream -- not by memory bandwidth.  Threads 0..255 own the
+// group's Gaussians.  One round of loads goes out at the start: the group's
+// tile counts and boxes first, then the raw group sums and digit table (no
+// count kernel ran).  The keys need only the counts and boxes: the group's
+// emission scan is formed and the first chunk's keys are regenerated from it
+// (binary search in LDS) and ranked while the sums and the table are still in
+// flight; then each block forms its Gaussians' emission offsets, writes
+// offsets[], and workgroup 0 publishes M and the bucket starts.  Each key is
+// stored straight from its register: position = the block's next slot of the
+// digit + the chunk's keys of the digit in earlier waves + its rank among its
+// wave's keys of the digit (ballots, in key order), so the pass is stable.
+// (1024 threads per group measured slower: one such block per CU leaves a tail
+// once the groups outnumber the CUs.)
 constexpr int kWPL = 4;                        // keys per lane per chunk (at most)
 constexpr int kWideThreads = 512;             // threads per group: 8 waves (two blocks fit a CU)
 
@@ -699,7 +701,45 @@ struct WideLds {
     uint32_t dsum[4];                          // per wave of digits: their total keys
 };
 
+// Keys [cs, cs + cc) of the group (cc = min(CH, tot - cs)): each regenerated from the emission scan in
+// L.G and ranked among its wave's keys of the same digit (wave-local counts in L.cnt[wave]; no barrier).
 template <int NT>
+__device__ __forceinline__ void wide_chunk_keys(WideLds<NT> &L, int ns, int first, uint32_t cs, int cc, int span,
+                                                int tiles_x, int shift, int bits, uint32_t (&key)[kWPL],
+                                                uint32_t (&val)[kWPL], uint32_t (&rk)[kWPL]) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int radix = 1 << bits, iters = span >> 6;
+    const uint32_t dmask = (uint32_t)(radix - 1);
+#pragma unroll
+    for (int it = 0; it < kWPL; ++it) {
+        if (it < iters) {                                 // uniform
+            const int idx = wave * span + it * 64 + lane;
+            int lo;
+            regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
+            val[it] = (uint32_t)(first + lo);
+        }
+    }
+    for (int d = lane; d < radix; d += 64) L.cnt[wave][d] = 0u;
+    const uint64_t below = lanes_below();
+#pragma unroll
+    for (int it = 0; it < kWPL; ++it) {
+        if (it >= iters) continue;                        // uniform
+        const int idx = wave * span + it * 64 + lane;
+        const bool valid = idx < cc;
+        const uint32_t d = (key[it] >> shift) & dmask;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < bits; ++b) {
+            const bool on = (d >> b) & 1u;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        const uint32_t before_w = valid ? L.cnt[wave][d] : 0u;
+        rk[it] = before_w + (uint32_t)__popcll(peers & below);
+        if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before_w + (uint32_t)__popcll(peers);
+    }
+}
+
+template <int NT, int NB>   // NB: table loads per thread, NB * NT * 4 >= the redundant table's entries
 __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x, int shift, int bits, int table_redundant,
                                                    int ncols_cap, const uint2 *__restrict__ pixbox,
                                                    uint32_t *__restrict__ offsets, BinHeader *__restrict__ hdr,
@@ -711,6 +751,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
                                                    long long capacity, uint32_t *__restrict__ d_num,
                                                    uint32_t *__restrict__ d_max) {
     constexpr int NW = NT / 64, CH = NT * kWPL;
+    constexpr int NG = kMaxRedundantGroups / NT;          // group-sum loads per thread
     __shared__ WideLds<NT> L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int radix = 1 << bits;
@@ -718,25 +759,61 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
     const int first = blockIdx.x * kBT;
     const int ns = min(kBT, n - first);
     const bool own = tid < ns;
-    // one round of loads: the group's counts and boxes, the group sums, the digit table (all
-    // unconditional, in range, unused values dropped: no branch holds a load back)
+    // one round of loads: counts and boxes first, then the group sums and the table, consumed only
+    // after the first chunk's keys are ranked.  Every load is issued unconditionally (in-range index,
+    // unused values dropped): with no branch among them, the wait for the counts leaves the rest in
+    // flight.
     const int gi = first + (own ? tid : 0);
     const uint32_t c0 = counts[gi];
     const uint2 bx0 = pixbox[gi];
-    unsigned long long v[kMaxRedundantGroups / NT];
+    unsigned long long v[NG];
 #pragma unroll
-    for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
+    for (int k = 0; k < NG; ++k) {
         const int i = tid + k * NT;
         v[k] = part[i < ngroups ? i : 0];
     }
-    const DigitAcc acc = digit_load<kMaxRedundantTable / (4 * NT), NT>(table, table_redundant, ncols_cap,
-                                                                     blockIdx.x, bits);
+    // redundant table: uint4 q of column c holds digits 4 (q mod Q) .. +3, Q = radix / 4; thread t
+    // always reads the same 4 digits, from columns t / Q, t / Q + NT / Q, ...; scanned table: the
+    // block's base of digit tid
+    const int lq = table_redundant ? bits - 2 : 0;
+    const int g4 = tid & ((1 << lq) - 1), cstep = NT >> lq, cfirst = tid >> lq;
+    const uint4 *t4 = reinterpret_cast<const uint4 *>(table);
+    uint4 tv[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        const int col = cfirst + k * cstep;
+        tv[k] = t4[table_redundant && col < ncols_cap ? ((uint32_t)col << lq) + (uint32_t)g4 : 0u];
+    }
+    const uint32_t tx = table[!table_redundant && tid < radix ? (size_t)tid * ncols_cap + blockIdx.x : 0u];
     const uint32_t c = own ? c0 : 0u;
     const uint2 bx = own ? bx0 : make_uint2(0u, 0u);
-    // Wave-level partials of everything that needs the whole block: one barrier publishes them.
+    // the group's emission scan
+    const uint32_t cinc = wave_scan_incl(c);
+    if (lane == 63) L.sm32[wave] = cinc;
+    __syncthreads();                                      // 1: wave totals of the tile counts
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t x = L.sm32[w];
+        off += w < wave ? x : 0u;
+        tot += x;
+    }
+    const uint32_t local = off + cinc - c;
+    if (own) {
+        L.G.excl[tid] = local;
+        L.G.box[tid] = bx;
+    }
+    if (tid == 0) L.G.excl[ns] = tot;
+    __syncthreads();                                      // 2: the emission scan
+    // the first chunk's keys, regenerated and ranked (wave-local) while the loads above complete
+    uint32_t key[kWPL], val[kWPL], rk[kWPL];
+    int cc = (int)min((uint32_t)CH, tot);
+    int span = ((cc + NT - 1) / NT) * 64;                 // keys per wave: a multiple of 64, NW * span >= cc
+    if (tot > 0u) wide_chunk_keys<NT>(L, ns, first, 0u, cc, span, tiles_x, shift, bits, key, val, rk);
+    // the group sums (before this group, all) and the table's digit partials, reduced per wave
     unsigned long long before = 0, all = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxRedundantGroups / NT; ++k) {
+    for (int k = 0; k < NG; ++k) {
         const int i = tid + k * NT;
         const unsigned long long x = i < ngroups ? v[k] : 0ull;
         all += x;
@@ -747,15 +824,21 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
         before += __shfl_xor(before, o, 64);
         all += __shfl_xor(all, o, 64);
     }
-    const uint32_t cinc = wave_scan_incl(c);
     if (lane == 63) {
         L.sm64[wave] = before;
         L.sm64[NW + wave] = all;
-        L.sm32[wave] = cinc;
     }
-    const int Q = radix >> 2;                         // digit quads (redundant tables: radix >= 4)
-    if (table_redundant) {                            // uniform: lanes with equal lane mod Q hold the same digits
-        uint4 fb = acc.b, ft = acc.t;
+    const int Q = radix >> 2;                             // digit quads (redundant tables: radix >= 4)
+    if (table_redundant) {                                // uniform
+        uint4 fb = make_uint4(0u, 0u, 0u, 0u), ft = fb;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int col = cfirst + k * cstep;
+            if (col >= ncols_cap) continue;
+            ft.x += tv[k].x; ft.y += tv[k].y; ft.z += tv[k].z; ft.w += tv[k].w;
+            if (col < (int)blockIdx.x) { fb.x += tv[k].x; fb.y += tv[k].y; fb.z += tv[k].z; fb.w += tv[k].w; }
+        }
+        // lanes with equal lane mod Q hold the same digits
         for (int o = Q; o < 64; o <<= 1) {
             fb.x += __shfl_xor(fb.x, o, 64); fb.y += __shfl_xor(fb.y, o, 64);
             fb.z += __shfl_xor(fb.z, o, 64); fb.w += __shfl_xor(fb.w, o, 64);
@@ -767,29 +850,19 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             L.ft[wave][lane] = ft;
         }
     }
-    __syncthreads();                                  // 1: wave partials
+    __syncthreads();                                      // 3: sums, table partials and the waves' key counts
     unsigned long long tb = 0, ta = 0;
-    uint32_t off = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         tb += L.sm64[w];
         ta += L.sm64[NW + w];
-        const uint32_t x = L.sm32[w];
-        off += w < wave ? x : 0u;
-        tot += x;
     }
-    const uint32_t local = off + cinc - c;
     if (own) offsets[first + tid] = sat32(tb + local);
     if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num, d_max);
     const uint32_t M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
-    if (M == 0u) return;                              // overflow or no pair: uniform
-    if (own) {
-        L.G.excl[tid] = local;
-        L.G.box[tid] = bx;
-    }
-    if (tid == 0) L.G.excl[ns] = tot;
+    if (M == 0u) return;                                  // overflow or no pair: uniform
     // digit bases: gbase[d] = (keys of smaller digits, all groups) + (keys of d in earlier groups)
-    if (table_redundant) {                            // uniform
+    if (table_redundant) {                                // uniform
         uint32_t sb = 0, st = 0;
         if (tid < radix) {
             const uint32_t *pb = reinterpret_cast<const uint32_t *>(&L.fb[0][0]);
@@ -800,9 +873,9 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
                 st += pt[(w * 64 + (tid >> 2)) * 4 + (tid & 3)];
             }
         }
-        const uint32_t dinc = wave_scan_incl(st);     // digits tid (< 256) sit in waves 0..3
+        const uint32_t dinc = wave_scan_incl(st);         // digits tid (< 256) sit in waves 0..3
         if (wave < 4 && lane == 63) L.dsum[wave] = dinc;
-        __syncthreads();                              // 2: digit totals per wave; G
+        __syncthreads();                                  // 4: digit totals per wave
         if (tid < radix) {
             uint32_t dbase = 0;
 #pragma unroll
@@ -810,9 +883,9 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             L.gbase[tid] = dbase + dinc - st + sb;
         }
     } else {
-        if (tid < radix) L.gbase[tid] = acc.x;        // the scanned table holds the bases
+        if (tid < radix) L.gbase[tid] = tx;               // the scanned table holds the bases
     }
-    __syncthreads();                                  // 3: gbase
+    __syncthreads();                                      // 5: gbase
     if (blockIdx.x == 0) {
         if (tid < radix) bucket_start[tid] = L.gbase[tid];
         if (tid == 0) bucket_start[radix] = M;
@@ -821,42 +894,8 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             ranges[tid] = e > a ? make_uint2(a, e) : make_uint2(0u, 0u);
         }
     }
-    const uint64_t below = lanes_below();
-    for (uint32_t cs = 0; cs < tot; cs += CH) {
-        const int cc = (int)min((uint32_t)CH, tot - cs);
-        const int span = ((cc + NT - 1) / NT) * 64;     // keys per wave: a multiple of 64, NW * span >= cc
+    for (uint32_t cs = 0; cs < tot;) {                    // the chunk's keys are ranked and the counts published
         const int iters = span >> 6;
-        uint32_t key[kWPL], val[kWPL];
-        // each key regenerated from the group's emission scan (binary search in LDS)
-#pragma unroll
-        for (int it = 0; it < kWPL; ++it) {
-            if (it < iters) {                             // uniform
-                const int idx = wave * span + it * 64 + lane;
-                int lo;
-                regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
-                val[it] = (uint32_t)(first + lo);
-            }
-        }
-        // rank of each key among its wave's keys of the same digit (wave-local counts)
-        for (int d = lane; d < radix; d += 64) L.cnt[wave][d] = 0u;
-        uint32_t rk[kWPL];
-#pragma unroll
-        for (int it = 0; it < kWPL; ++it) {
-            if (it >= iters) continue;                    // uniform
-            const int idx = wave * span + it * 64 + lane;
-            const bool valid = idx < cc;
-            const uint32_t d = (key[it] >> shift) & dmask;
-            uint64_t peers = __ballot(valid);
-            for (int b = 0; b < bits; ++b) {
-                const bool on = (d >> b) & 1u;
-                const uint64_t m = __ballot(on);
-                peers &= on ? m : ~m;
-            }
-            const uint32_t before_w = valid ? L.cnt[wave][d] : 0u;
-            rk[it] = before_w + (uint32_t)__popcll(peers & below);
-            if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before_w + (uint32_t)__popcll(peers);
-        }
-        __syncthreads();                              // the waves' counts
         // position = the block's next slot of the digit + its keys in earlier waves + the rank
 #pragma unroll
         for (int it = 0; it < kWPL; ++it) {
@@ -872,7 +911,8 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
                 }
             }
         }
-        if (cs + (uint32_t)CH >= tot) break;              // uniform: the last chunk
+        cs += (uint32_t)CH;
+        if (cs >= tot) break;                             // uniform: the last chunk
         __syncthreads();                                  // every wave has its positions
         if (tid < radix) {
             uint32_t t = 0;
@@ -880,7 +920,11 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             for (int w = 0; w < NW; ++w) t += L.cnt[w][tid];
             L.gbase[tid] += t;
         }
-        __syncthreads();
+        __syncthreads();                                  // the counts are read: the next chunk rewrites them
+        cc = (int)min((uint32_t)CH, tot - cs);
+        span = ((cc + NT - 1) / NT) * 64;
+        wide_chunk_keys<NT>(L, ns, first, cs, cc, span, tiles_x, shift, bits, key, val, rk);
+        __syncthreads();                                  // the waves' counts
     }
 }
 
@@ -1506,6 +1550,15 @@ hipError_t launch_tile_order(const BinPlan &p, const uint32_t *ranges, uint32_t 
     return hipGetLastError();
 }
 
+// k_scatter0w with the fewest table loads per thread that cover `entries` table entries.
+template <typename... Args>
+static void launch_scatter0w(int64_t entries, int blocks, hipStream_t s, Args... args) {
+    constexpr int NT = kWideThreads;
+    if (entries <= 4 * NT * 4) k_scatter0w<NT, 4><<<blocks, NT, 0, s>>>(args...);
+    else if (entries <= 8 * NT * 4) k_scatter0w<NT, 8><<<blocks, NT, 0, s>>>(args...);
+    else k_scatter0w<NT, kMaxRedundantTable / (4 * NT)><<<blocks, NT, 0, s>>>(args...);
+}
+
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,
                            uint32_t *keys, uint32_t *vals, uint32_t *ranges, uint32_t *tile_order, uint32_t *d_num,
                            void *ws, hipStream_t s, bool groups_done, bool first_pass_only, uint32_t *d_max) {
@@ -1556,7 +1609,7 @@ hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint3
     if (p.order_kind == 1 || (lsd && (p.passes & 1) == 0)) { k0 = kalt; v0 = valt; }
     uint2 *rg0 = p.order_kind == 0 ? rg : nullptr;
     if (folded)             // also when capacity == 0: it publishes offsets and M
-        k_scatter0w<kWideThreads><<<p.nseg, kWideThreads, 0, s>>>(
+        launch_scatter0w(p.table_redundant[0] ? (int64_t)p.ncols_cap[0] << p.bits[0] : 0, p.nseg, s,
             p.n, p.tiles_x, p.shift0, p.bits[0], p.table_redundant[0], p.ncols_cap[0], box, offsets, hdr, table, k0,
             v0, bstart, rg0, p.ntiles, counts, part, p.nb_g, (long long)p.capacity, d_num, d_max);
     else                    // not folded: more than kMaxRedundantGroups groups, segments of 4

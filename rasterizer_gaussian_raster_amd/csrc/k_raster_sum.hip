@@ -431,6 +431,7 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                                              float2 *__restrict__ part_abs = nullptr) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int x0 = tx * kTile, y0 = ty * kTile;
+    const float fx0 = (float)x0 + 0.5f, fy0 = (float)y0 + 0.5f;   // the tile's first pixel centre
     const float k2 = 2.0f * kLn2;
     for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
         uint32_t e0, ne;
@@ -486,43 +487,67 @@ __device__ __forceinline__ void sum_bwd_tile(BwdLds &S, const float4 *gp, int tx
                 }
                 const int lx = (int)(blk & 3u) * 4, ly = (int)(blk >> 2) * 4;
                 const float4 A = S.entp[wave][e], B = S.entq[wave][e];
+                // pixel centres: the block's first column and row converted once, the others one
+                // more each (all exact in fp32, the same values as converting each pixel's index)
+                const float cx0 = fx0 + (float)lx, cy0 = fy0 + (float)ly;
                 float dy[4];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) dy[rr] = ((float)(y0 + ly + rr) + 0.5f) - A.y;
-                float Hu = 0.f, Hv = 0.f, Muu = 0.f, Muv = 0.f, Mvv = 0.f, Cr = 0.f, Cg = 0.f, Cb = 0.f;
+                for (int rr = 0; rr < 4; ++rr) dy[rr] = (cy0 + (float)rr) - A.y;
+                // the first column and pixel assign their sums (no addition of a zero)
+                float Hu, Hv, Muu, Muv, Mvv, Cr, Cg, Cb;
                 float Ax = 0.f, Ay = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const float dx = ((float)(x0 + lx + c) + 0.5f) - A.x;
+                    const float dx = (cx0 + (float)c) - A.x;
                     const float u = A.z * dx;
                     const float tb = A.w * dx;
                     const float uu = u * u;
                     const float au = A.z * u;
-                    float ch = 0.f, chv = 0.f, chvv = 0.f;
+                    float ch, chv, chvv;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         const float4 gv = gp[blk * kGpStride + rr * 4 + c];
                         const float v = fmaf(B.x, dy[rr], tb);
                         const float ee = fmaf(v, v, uu);
                         const float w = ee <= kE9 ? exp2_hw(-ee) : 0.0f;
-                        Cr = fmaf(gv.x, w, Cr);
-                        Cg = fmaf(gv.y, w, Cg);
-                        Cb = fmaf(gv.z, w, Cb);
+                        if (c == 0 && rr == 0) {
+                            Cr = gv.x * w;
+                            Cg = gv.y * w;
+                            Cb = gv.z * w;
+                        } else {
+                            Cr = fmaf(gv.x, w, Cr);
+                            Cg = fmaf(gv.y, w, Cg);
+                            Cb = fmaf(gv.z, w, Cb);
+                        }
                         const float h = fmaf(gv.z, B.w, fmaf(gv.y, B.z, gv.x * B.y)) * w;
                         const float hv = h * v;
-                        ch += h;
-                        chv += hv;
-                        chvv = fmaf(hv, v, chvv);
+                        if (rr == 0) {
+                            ch = h;
+                            chv = hv;
+                            chvv = hv * v;
+                        } else {
+                            ch += h;
+                            chv += hv;
+                            chvv = fmaf(hv, v, chvv);
+                        }
                         if constexpr (ABS) {
                             Ax += fabsf(h * fmaf(A.w, v, au));
                             Ay += fabsf(hv);
                         }
                     }
-                    Hu = fmaf(u, ch, Hu);
-                    Muu = fmaf(uu, ch, Muu);
-                    Muv = fmaf(u, chv, Muv);
-                    Hv += chv;
-                    Mvv += chvv;
+                    if (c == 0) {
+                        Hu = u * ch;
+                        Muu = uu * ch;
+                        Muv = u * chv;
+                        Hv = chv;
+                        Mvv = chvv;
+                    } else {
+                        Hu = fmaf(u, ch, Hu);
+                        Muu = fmaf(uu, ch, Muu);
+                        Muv = fmaf(u, chv, Muv);
+                        Hv += chv;
+                        Mvv += chvv;
+                    }
                 }
                 // the item's share of the pair's sums (slot_grad_cholesky turns a Gaussian's total
                 // into its gradient)
