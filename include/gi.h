@@ -580,11 +580,23 @@ gi_status gi_grad_gather(const gi_desc *desc, int32_t kind, int64_t n, const flo
  *   dL_dimage      device float [3][H][W], written; must not alias the inputs.
  *   d_loss         device float [1] (written: L) or NULL.
  *   workspace      device, >= gi_loss_ssim_workspace_bytes(W, H), 256-byte aligned.
+ *   flags          0, or GI_SSIM_TARGET_PREPARED: the workspace holds the window
+ *                  statistics of this target from gi_loss_ssim_target (the target
+ *                  is unchanged since); the call then filters only the image's
+ *                  maps.  Same results, bit for bit, as without the flag.
+ *
+ * gi_loss_ssim_target -- the target's window statistics (its local means of T
+ *   and T^2, the fitting loop's constant half of SSIM) into the workspace, for
+ *   later gi_loss_ssim calls with GI_SSIM_TARGET_PREPARED.  Same arguments as
+ *   above; the other workspace contents are left alone.
  */
+#define GI_SSIM_TARGET_PREPARED 1u
 size_t gi_loss_ssim_workspace_bytes(int32_t width, int32_t height);
+gi_status gi_loss_ssim_target(int32_t width, int32_t height, const float *target, void *workspace,
+                              size_t workspace_bytes, void *stream);
 gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const float *target, float w1, float w2,
                        float ws, float *dL_dimage, float *d_loss, void *workspace, size_t workspace_bytes,
-                       void *stream);
+                       uint32_t flags, void *stream);
 
 /*
  * gi_adam_step_pairs_rs -- gi_adam_step_pairs for rotation-scale params (the

@@ -490,16 +490,25 @@ size_t gi_loss_ssim_workspace_bytes(int32_t width, int32_t height) {
     return gi::ssim_workspace_bytes(width, height);
 }
 
+gi_status gi_loss_ssim_target(int32_t width, int32_t height, const float *target, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (width < 1 || height < 1 || width > kMaxDim || height > kMaxDim) return GI_ERR_INVALID_ARG;
+    if (!target || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (workspace_bytes < gi::ssim_workspace_bytes(width, height)) return GI_ERR_INVALID_ARG;
+    return hip_status(gi::launch_ssim_target(width, height, target, workspace, as_stream(stream)));
+}
+
 gi_status gi_loss_ssim(int32_t width, int32_t height, const float *image, const float *target, float w1, float w2,
                        float ws, float *dL_dimage, float *d_loss, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+                       uint32_t flags, void *stream) {
     if (width < 1 || height < 1 || width > kMaxDim || height > kMaxDim) return GI_ERR_INVALID_ARG;
     if (!std::isfinite(w1) || !std::isfinite(w2) || !std::isfinite(ws)) return GI_ERR_INVALID_ARG;
     if (!image || !target || !dL_dimage || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
+    if (flags & ~GI_SSIM_TARGET_PREPARED) return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::ssim_workspace_bytes(width, height)) return GI_ERR_INVALID_ARG;
     if (dL_dimage == image || dL_dimage == target) return GI_ERR_INVALID_ARG;
     return hip_status(gi::launch_loss_ssim(width, height, image, target, w1, w2, ws, dL_dimage, d_loss, workspace,
-                                           as_stream(stream)));
+                                           (flags & GI_SSIM_TARGET_PREPARED) != 0, as_stream(stream)));
 }
 
 gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *offsets, int64_t capacity,

@@ -163,8 +163,9 @@ hipError_t launch_adam(int64_t rows, int row_len, float *p, float *g, float *m, 
 
 // k_ssim.hip
 size_t ssim_workspace_bytes(int W, int H);
+hipError_t launch_ssim_target(int W, int H, const float *y, void *ws_ptr, hipStream_t s);
 hipError_t launch_loss_ssim(int W, int H, const float *x, const float *y, float w1, float w2, float ws, float *dL,
-                            float *loss, void *ws_ptr, hipStream_t s);
+                            float *loss, void *ws_ptr, bool target_prepared, hipStream_t s);
 
 // k_adapt.hip
 hipError_t launch_merge_pairs(int64_t np, int64_t n, const float *params, const int32_t *pairs, float *out,

@@ -1550,13 +1550,17 @@ hipError_t launch_tile_order(const BinPlan &p, const uint32_t *ranges, uint32_t 
     return hipGetLastError();
 }
 
-// k_scatter0w with the fewest table loads per thread that cover `entries` table entries.
-template <typename... Args>
-static void launch_scatter0w(int64_t entries, int blocks, hipStream_t s, Args... args) {
-    constexpr int NT = kWideThreads;
+// k_scatter0w with NT threads per group and the fewest table loads per thread that cover `entries`
+// table entries.
+template <int NT, typename... Args>
+static void launch_scatter0w_nt(int64_t entries, int blocks, hipStream_t s, Args... args) {
     if (entries <= 4 * NT * 4) k_scatter0w<NT, 4><<<blocks, NT, 0, s>>>(args...);
     else if (entries <= 8 * NT * 4) k_scatter0w<NT, 8><<<blocks, NT, 0, s>>>(args...);
-    else k_scatter0w<NT, kMaxRedundantTable / (4 * NT)><<<blocks, NT, 0, s>>>(args...);
+    else k_scatter0w<NT, (kMaxRedundantTable + 4 * NT - 1) / (4 * NT)><<<blocks, NT, 0, s>>>(args...);
+}
+template <typename... Args>
+static void launch_scatter0w(int64_t entries, int blocks, hipStream_t s, Args... args) {
+    launch_scatter0w_nt<kWideThreads>(entries, blocks, s, args...);
 }
 
 hipError_t launch_bin_sort(const BinPlan &p, const uint16_t *pixbox, const uint32_t *counts, uint32_t *offsets,

@@ -39,6 +39,7 @@ def desc(width: int, height: int, mode: int = MODE_SUM) -> gi_desc:
 
 
 FIT_PREPARED, FIT_ORDER, FIT_USE_ORDER, FIT_NO_UPDATE, FIT_TRACK_MAX = 1, 2, 4, 8, 16
+SSIM_TARGET_PREPARED = 1
 
 
 class gi_fit_buffers(ctypes.Structure):
@@ -85,7 +86,9 @@ def load():
         "gi_adam_step_pairs_alpha": ([D, i64, P, i64, P, sz, P, P, P, P, P, P, P, ctypes.c_float, P, P, P,
                                       ctypes.c_float, f64, f64, f64, i32, P, i64, P, P], i32),
         "gi_render_bwd_absgrad": ([D, i64, P, P, P, P, P, P, i64, P, P, P, P, sz, P], i32),
-        "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, P], i32),
+        "gi_loss_ssim": ([i32, i32, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P, sz, ctypes.c_uint32,
+                          P], i32),
+        "gi_loss_ssim_target": ([i32, i32, P, P, sz, P], i32),
         "gi_params_to_cholesky_grad": ([i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i32, P], i32),
         "gi_grad_gather": ([D, i32, i64, P, ctypes.c_float, ctypes.c_float, P, P, i64, P, sz, P, P], i32),
         "gi_render_fwd_l2": ([D, i64, P, P, P, P, P, P, P, P, P, P], i32),
@@ -369,9 +372,14 @@ def gi_loss_ssim_workspace_bytes(W, H):
     return int(load().gi_loss_ssim_workspace_bytes(int(W), int(H)))
 
 
-def gi_loss_ssim(W, H, image, target, w1, w2, ws, dL_dimage, d_loss, workspace, stream=None):
+def gi_loss_ssim_target(W, H, target, workspace, stream=None):
+    _check(load().gi_loss_ssim_target(int(W), int(H), _ptr(target), _ptr(workspace), int(workspace.numel()),
+                                      _stream(stream)), "gi_loss_ssim_target")
+
+
+def gi_loss_ssim(W, H, image, target, w1, w2, ws, dL_dimage, d_loss, workspace, stream=None, flags=0):
     _check(load().gi_loss_ssim(int(W), int(H), _ptr(image), _ptr(target), float(w1), float(w2), float(ws),
-                               _ptr(dL_dimage), _ptr(d_loss), _ptr(workspace), int(workspace.numel()),
+                               _ptr(dL_dimage), _ptr(d_loss), _ptr(workspace), int(workspace.numel()), int(flags),
                                _stream(stream)), "gi_loss_ssim")
 
 

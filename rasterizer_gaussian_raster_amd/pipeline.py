@@ -338,8 +338,9 @@ class Fitter:
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self.loss_ws = torch.empty(gi.gi_loss_workspace_bytes(self.target.numel()), dtype=torch.uint8, device=dev)
         self.loss_w = None if loss is None else tuple(float(v) for v in loss)
-        if self.loss_w is not None:
+        if self.loss_w is not None:             # the target's SSIM statistics, formed once for the fit
             self.ssim_ws = torch.empty(gi.gi_loss_ssim_workspace_bytes(W, H), dtype=torch.uint8, device=dev)
+            gi.gi_loss_ssim_target(W, H, self.target, self.ssim_ws)
         self.step_count = 0
         self.graphs = None
         self.d_step = None
@@ -482,7 +483,8 @@ class Fitter:
             gi.gi_loss_l2(self.target.numel(), r.image, self.target, self.dL, self.loss, self.loss_ws)
         else:
             _, H, W = self.target.shape
-            gi.gi_loss_ssim(W, H, r.image, self.target, *self.loss_w, self.dL, self.loss, self.ssim_ws)
+            gi.gi_loss_ssim(W, H, r.image, self.target, *self.loss_w, self.dL, self.loss, self.ssim_ws,
+                            flags=gi.SSIM_TARGET_PREPARED)
         if self.logit is None:
             r.backward(self.dL, self.grad)
             self.step_count += 1
