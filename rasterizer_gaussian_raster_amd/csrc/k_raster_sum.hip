@@ -2,7 +2,8 @@
 // rendering by accumulated summation of 2D Gaussians) and its backward.
 //
 // Forward (pixel-major).  One workgroup of 4 waves per 16x16 tile; wave w owns
-// the 8x8 quadrant (w & 1, w >> 1), one pixel per lane.  The tile's list is
+// the 8x8 quadrant q = (w + t) mod 4 of tile t, at (q & 1, q >> 1), one pixel per
+// lane (rotated by tile, so that a SIMD's waves hold a mix of the quadrants).  The tile's list is
 // staged 128 Gaussians at a time with coalesced loads; while staging, each
 // thread tests its Gaussian's pixel box against the four quadrants and the
 // records are compacted, in list order, into one LDS list per quadrant
@@ -97,14 +98,14 @@ __device__ __forceinline__ void bwd_share(uint2 rg, uint32_t base, uint32_t &e0,
 // 128 entries at a time, wave w loading the w-th quarter of the batch (the
 // backward's share layout); each entry's pixel box is tested against the four
 // 8x8 quadrants and the records are compacted, in list order, into one LDS
-// list per quadrant; wave w walks quadrant w's list.  With `first`, this lane's
+// list per quadrant; the wave walks quadrant quad's list.  With `first`, this lane's
 // entry of the first batch is also kept there: the backward's first share,
 // loaded once for both passes.  With tl0, the first batch's Gaussians come from
 // that LDS copy of the list instead of vals.  On return other waves
 // may still read S: barrier before reusing it.
 __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg, const float4 *__restrict__ records,
                                              const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
-                                             const uint32_t *tl0, BwdEntry *first, float px,
+                                             const uint32_t *tl0, BwdEntry *first, int quad, float px,
                                              float py, float &ar, float &ag, float &ab) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint64_t below = lanes_below();
@@ -150,9 +151,9 @@ __device__ __forceinline__ void sum_fwd_tile(FwdLds &S, int x0, int y0, uint2 rg
                 S.lst[q][o] = r;
             }
         }
-        const int cnt = __builtin_amdgcn_readfirstlane(S.wq[0][wave] + S.wq[1][wave] + S.wq[2][wave] + S.wq[3][wave]);
+        const int cnt = __builtin_amdgcn_readfirstlane(S.wq[0][quad] + S.wq[1][quad] + S.wq[2][quad] + S.wq[3][quad]);
         __syncthreads();
-        const SumRec *L = S.lst[wave];
+        const SumRec *L = S.lst[quad];
         for (int k = 0; k < cnt; ++k) {
             const float4 A = L[k].p, B = L[k].q;
             const float dx = px - A.x, dy = py - A.y;
@@ -356,12 +357,13 @@ __global__ __launch_bounds__(256) void k_render_sum_fwd(int W, int H, int tiles_
     if (t >= ntiles) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int x0 = (t % tiles_x) * kTile, y0 = (t / tiles_x) * kTile;
-    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
-    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
+    const int quad = (wave + t) & 3;                      // the wave's quadrant, rotated by tile
+    const int pxi = x0 + (quad & 1) * 8 + (lane & 7);
+    const int pyi = y0 + (quad >> 1) * 8 + (lane >> 3);
     const bool bucket = bl.kin != nullptr;                // uniform
     const uint2 rg = bucket ? bucket_tile_list(bl, t, tl, sc) : ranges[t];
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(S, x0, y0, rg, records, pixbox, bucket ? bl.vout : vals, bucket ? tl : nullptr, nullptr,
+    sum_fwd_tile(S, x0, y0, rg, records, pixbox, bucket ? bl.vout : vals, bucket ? tl : nullptr, nullptr, quad,
                  (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     sum_fwd_store<L2>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
     if (L2) {
@@ -675,8 +677,9 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tx = t % tiles_x, ty = t / tiles_x;
     const int x0 = tx * kTile, y0 = ty * kTile;
-    const int pxi = x0 + (wave & 1) * 8 + (lane & 7);
-    const int pyi = y0 + (wave >> 1) * 8 + (lane >> 3);
+    const int quad = (wave + t) & 3;                      // the wave's quadrant, rotated by tile
+    const int pxi = x0 + (quad & 1) * 8 + (lane & 7);
+    const int pyi = y0 + (quad >> 1) * 8 + (lane >> 3);
     // Wave priority: the list, its staging and the forward ahead of the backward item loops of
     // the CU's other workgroups (every tile's workgroup is resident from the start; the oldest
     // ones would otherwise hold the issue slots while the others' loads wait to go out).
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void k_render_sum_fused(int 
     E0.box = make_uint2(1u, 0u);
     E0.g = 0u;
     float ar = 0.0f, ag = 0.0f, ab = 0.0f;
-    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, bucket ? tl : nullptr, &E0,
+    sum_fwd_tile(*reinterpret_cast<FwdLds *>(lds), x0, y0, rg, records, pixbox, vals, bucket ? tl : nullptr, &E0, quad,
                  (float)pxi + 0.5f, (float)pyi + 0.5f, ar, ag, ab);
     const float4 g = sum_fwd_store<true>(W, H, pxi, pyi, t, ar, ag, ab, image, target, dL, gscale, loss_part, wsq);
     gp[gp_index(pxi - x0, pyi - y0)] = g;
