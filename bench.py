@@ -41,6 +41,64 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def provenance():
+    """Where a result comes from: a hash of the sources the library is built from (and the git
+    revision when the tree has one), the library's version string, the GPU, the host CPU, and the
+    GPU's shader-clock level at the end of the run when the driver exposes it."""
+    import glob
+    import subprocess
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rasterizer_gaussian_raster_amd", "csrc", "*"))) + [
+            os.path.join(ROOT, "include", "gi.h")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    git = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        git = r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    sclk = None
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                for line in fh:
+                    if line.strip().endswith("*"):
+                        sclk = line.split(":", 1)[1].replace("*", "").strip()
+                        break
+        except OSError:
+            continue
+        if sclk:
+            break
+    out = {"sources_sha256_16": h.hexdigest()[:16], "git_rev": git, "host_cpu": cpu, "sclk_level_at_end": sclk}
+    try:
+        import torch
+        from rasterizer_gaussian_raster_amd import gi
+        out["lib"] = gi.version()
+        out["gpu"] = torch.cuda.get_device_name(0) if torch.cuda.is_available() else None
+        out["torch"], out["hip"] = torch.__version__, torch.version.hip
+    except Exception as e:           # provenance never fails a run
+        out["error"] = repr(e)
+    return out
+
+
+def emit(out):
+    """The result line: one JSON object on stdout, with the run's provenance."""
+    out = dict(out)
+    out["provenance"] = provenance()
+    print(json.dumps(out), flush=True)
+
+
 def stats_us(x_us):
     x = np.asarray(x_us, np.float64)
     return {"median": round(float(np.median(x)), 2), "p10": round(float(np.percentile(x, 10)), 2),
@@ -298,7 +356,7 @@ def bench_alpha(args, w, target, params, dev):
         out["cpu_baseline"] = cpu_baseline_alpha(wl, w["params"], w["logit"], w["background"])
     else:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def bench_ssim(args, w, target, params, dev):
@@ -363,7 +421,7 @@ def bench_ssim(args, w, target, params, dev):
                      "avg_launch_us": round(ssim_s * 1e6, 2)},
         "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def bench_absgrad(args, wlname, target, params, dev):
@@ -398,7 +456,7 @@ def bench_absgrad(args, wlname, target, params, dev):
     pairs = binned_pairs(W, H, r.ranges.cpu().numpy().view(np.uint32))
     tf = FLOP_BWD * pairs / abs_s / 1e12
     log(f"[bench] backward + gather {plain_s*1e6:.1f} us, with absgrad {abs_s*1e6:.1f} us")
-    print(json.dumps({
+    emit({
         "metric": METRIC, "value": round(1.0 / abs_s, 1), "unit": "backward passes/s (with absgrad)",
         "n_gpus": 1, "steps": nk, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -409,7 +467,7 @@ def bench_absgrad(args, wlname, target, params, dev):
         "roofline": {"bound": "alu", "kernel": "k_render_sum_bwd<true> (+ gather)", "achieved": round(tf, 3),
                      "peak": PEAK_FP32, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32, 4), "traffic": None,
                      "avg_launch_us": round(abs_s * 1e6, 2)},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": None})
 
 
 def bench_merge(args, target, dev):
@@ -465,7 +523,7 @@ def bench_merge(args, target, dev):
     nbytes = 104 * npairs             # two 32 B records + 8 B of indices read, 32 B written per pair
     gbs = nbytes / secs / 1e9
     log(f"[bench] gi_merge_pairs: {secs*1e6:.2f} us for {npairs} pairs ({gbs:.0f} GB/s algorithmic)")
-    print(json.dumps({
+    emit({
         "metric": "merge 80K -> 50K Gaussians (768x512), merges/s", "value": round((n - merged.shape[0]) / t_merge, 1),
         "unit": "merges/s", "n_gpus": 1, "steps": 1, "warmup": 1, "ms_per_step": round(t_merge * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
@@ -478,7 +536,7 @@ def bench_merge(args, target, dev):
         "roofline": {"bound": "hbm", "kernel": "k_merge_pairs", "achieved": round(gbs, 1), "peak": PEAK_HBM,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4), "traffic": None,
                      "avg_launch_us": round(secs * 1e6, 2)},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": None})
 
 
 def bench_adc(args, target, params, dev):
@@ -510,7 +568,7 @@ def bench_adc(args, target, params, dev):
     us = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     mv = int(moved.item())
     log(f"[bench] gi_adc at 768x512 / {n}: median {np.median(us):.1f} us, {mv} Gaussians moved")
-    print(json.dumps({
+    emit({
         "metric": "adaptive density control pass (768x512, 50K)", "value": round(1e6 / float(np.median(us)), 1),
         "unit": "passes/s", "n_gpus": 1, "steps": nk, "warmup": 0, "ms_per_step": round(float(np.median(us)) / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -518,7 +576,7 @@ def bench_adc(args, target, params, dev):
         "timing_us": {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
                       "p90": round(float(np.percentile(us, 90)), 2)},
         "timing": "HIP events on the launch stream around each gi_adc call (params restored between calls)",
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": None})
 
 
 def bench_rs(args, wlname, target, dev):
@@ -609,7 +667,7 @@ def bench_rs(args, wlname, target, dev):
         "roofline_convert": roof_hbm("k_params_to_cholesky", 64 * n, conv_s),
         "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def main():
@@ -795,7 +853,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, w["params"])
     else:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def hbm_rates_4k(dev):

@@ -18,6 +18,8 @@ uint32/uint16 device arrays are held in int32/int16 tensors (same bytes).
 """
 from __future__ import annotations
 
+import math
+
 import torch
 
 from . import gi
@@ -356,6 +358,38 @@ class Fitter:
         self.raster.bwd_ws = torch.empty(gi.gi_render_bwd_workspace_bytes(self.raster.desc, self.n,
                                                                           self.raster.capacity),
                                          dtype=torch.uint8, device=dev)
+
+    def _state(self):
+        """The tensors a step updates (parameters and Adam moments, and in alpha mode the logits and
+        background with theirs)."""
+        t = [self.params, self.m, self.v]
+        if self.logit is not None:
+            t += [self.logit, self.m_logit, self.v_logit, self.bg4, self.m_bg, self.v_bg]
+        return t
+
+    def guarded_steps(self, k, spike=10.0):
+        """k training steps with divergence recovery ("FlashImgs", Training features: a loss spike is
+        rolled back).  After the k steps the loss is read (one host wait); when it is not finite or
+        above spike x the loss of the last good check, the parameters and Adam state go back to that
+        check (the k steps are dropped; step counter too) and False is returned; otherwise this state
+        becomes the good check and True is returned.  The first call checks against its own start."""
+        if getattr(self, "_good", None) is None:
+            self._good = [t.clone() for t in self._state()]
+            self._good_step, self._good_loss = self.step_count, None
+        for _ in range(k):
+            self.step()
+        loss = float(self.loss.item())
+        if not math.isfinite(loss) or (self._good_loss is not None and loss > spike * self._good_loss):
+            for t, g in zip(self._state(), self._good):
+                t.copy_(g)
+            self.step_count = self._good_step
+            self.prepared = False           # the set-up in the raster's buffers is of the dropped steps
+            self.graphs = None              # captured steps carry that set-up's flag
+            return False
+        for t, g in zip(self._state(), self._good):
+            g.copy_(t)
+        self._good_step, self._good_loss = self.step_count, loss
+        return True
 
     def densify(self, s0=1.5):
         """One adaptive-density-control pass (gi_adc, sum mode): dead, out-of-bounds and bloated
