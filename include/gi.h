@@ -309,7 +309,9 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
  *             partials of gi_render_fwd_l2; one launch fewer per training step);
  *             NULL in alpha mode.
  *   workspace device scratch of gi_render_bwd_workspace_bytes() bytes, 256-byte
- *             aligned, no initialisation needed.
+ *             aligned, no initialisation needed (alpha mode: it also holds a
+ *             64-byte copy of each Gaussian's record, opacity, box and offset,
+ *             so that the backward reads one 64-byte line per list entry).
  *   Each (Gaussian, tile) pair's sums (its pixels' terms in the Gaussian's
  *   whitened frame, as gi_grad_gather describes) are formed in the tile's
  *   workgroup, its per-pixel terms added in a fixed order, and stored at the

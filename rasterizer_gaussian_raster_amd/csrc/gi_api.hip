@@ -290,6 +290,7 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
 
 size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
     if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return 0;
+    if (desc->mode == GI_MODE_ALPHA) return gi::alpha_bwd_workspace_bytes(desc->width, desc->height, n, capacity);
     return gi::make_bwd_plan(desc->width, desc->height, capacity).bytes;
 }
 
@@ -322,8 +323,9 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
         return hip_status(e);
     }
     if (!background || !t_final || !last || (n > 0 && (!opacity || !logit))) return GI_ERR_INVALID_ARG;
-    e = gi::launch_render_alpha_bwd(W, H, records, opacity, logit, pixbox, offsets, ranges, tile_order, vals, capacity,
-                                    background, t_final, last, dL_dimage, workspace, s);
+    if (workspace_bytes < gi::alpha_bwd_workspace_bytes(W, H, n, capacity)) return GI_ERR_INVALID_ARG;
+    e = gi::launch_render_alpha_bwd(W, H, n, records, opacity, logit, pixbox, offsets, ranges, tile_order, vals,
+                                    capacity, background, t_final, last, dL_dimage, workspace, s);
     if (e == hipSuccess && dparams)               // dparams = NULL: the slots stay for gi_adam_step_pairs_alpha
         e = gi::launch_grad_gather((int)n, W, H, ntiles, offsets, capacity, workspace, records, 1, dparams, dlogit,
                                    dbackground, s);

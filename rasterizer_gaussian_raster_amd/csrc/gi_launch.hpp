@@ -147,12 +147,12 @@ hipError_t launch_adam_pairs_alpha(int n, int W, int H, const uint32_t *offsets,
                                    float lr_logit, float *bg, float *mbg, float *vbg, float lr_bg, double beta1,
                                    double beta2, double eps, int step, const float *loss_partials, int64_t loss_count,
                                    float *d_loss, hipStream_t s);
-hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
-                                   const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
-                                   const uint32_t *order, const uint32_t *vals, int64_t capacity,
-                                   const float *background,
-                                   const float *t_final, const uint32_t *last, const float *dL_dimage, void *ws,
-                                   hipStream_t s);
+size_t alpha_bwd_workspace_bytes(int W, int H, int64_t n, int64_t capacity);
+hipError_t launch_render_alpha_bwd(int W, int H, int64_t n, const float *records, const float *opacity,
+                                   const float *logit, const uint16_t *pixbox, const uint32_t *offsets,
+                                   const uint32_t *ranges, const uint32_t *order, const uint32_t *vals,
+                                   int64_t capacity, const float *background, const float *t_final,
+                                   const uint32_t *last, const float *dL_dimage, void *ws, hipStream_t s);
 
 // k_optim.hip
 size_t loss_workspace_bytes(int64_t count);

@@ -49,31 +49,42 @@ __device__ __forceinline__ uint32_t half_mask(uint2 bx, int x0, int y0) {
     return m;
 }
 
+// The backward's entry record of Gaussian g (64 bytes, so that a list entry is one aligned 64-byte
+// read instead of five scattered ones): [4 g] = (mux, muy, a, b), [4 g + 1] = (c, cr, cg, cb),
+// [4 g + 2] = (o, so, pixel box (2 x u32 bits)), [4 g + 3] = (emission offset bits, 0, 0, 0), with
+// so = o (1 - o) below the logit clamp, else 0 -- the values the separate arrays hold, bit for bit.
+struct AlphaPack { float4 p, q, r, s; };
+
 // Stage list entries [lo, hi) (hi - lo <= kBatch) into the per-half lists; returns this wave's count.
-// Backward only (offsets != nullptr): also the entry's emission slot -> eslot[tid], its position
-// in each half's list -> qpos[tid][h] (0xff: not in that list) and its (a, b, c, so) -> *own.
+// Backward only (pack != nullptr, the entries read from the packed records): also the entry's
+// emission slot -> eslot[tid], its position in each half's list -> qpos[tid][h] (0xff: not in that
+// list) and its (a, b, c, so) -> *own.
 __device__ __forceinline__ int stage_alpha(AlphaRec (*lst)[kBatch], int (*wq)[2], uint32_t lo, uint32_t hi, int x0,
                                            int y0, const float4 *__restrict__ records,
-                                           const float *__restrict__ opacity, const float *__restrict__ logit,
-                                           const uint2 *__restrict__ pixbox, const uint32_t *__restrict__ vals,
-                                           uint64_t below, const uint32_t *__restrict__ offsets = nullptr,
-                                           uint32_t *eslot = nullptr, uint8_t (*qpos)[2] = nullptr,
-                                           float4 *own = nullptr) {
+                                           const float *__restrict__ opacity, const uint2 *__restrict__ pixbox,
+                                           const uint32_t *__restrict__ vals, uint64_t below,
+                                           const AlphaPack *__restrict__ pack = nullptr, uint32_t *eslot = nullptr,
+                                           uint8_t (*qpos)[2] = nullptr, float4 *own = nullptr) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t idx = lo + tid;
     uint32_t hm = 0;
     float4 rp = make_float4(0.f, 0.f, 0.f, 0.f), rq = rp, rr = rp;
     if (idx < hi) {
         const uint32_t g = vals[idx];
-        rp = records[2 * g];
-        rq = records[2 * g + 1];
-        const float o = opacity[g];
-        float so = 0.0f;
-        if (logit) so = logit[g] < kLogitMax ? o * (1.0f - o) : 0.0f;
-        rr = make_float4(o, __uint_as_float(idx), so, __uint_as_float(g));
-        const uint2 bx = pixbox[g];
-        hm = half_mask(bx, x0, y0);
-        if (offsets) eslot[tid] = emit_slot(offsets[g], bx, x0 / kTile, y0 / kTile);
+        if (pack) {
+            const AlphaPack e = pack[g];
+            rp = e.p;
+            rq = e.q;
+            rr = make_float4(e.r.x, __uint_as_float(idx), e.r.y, __uint_as_float(g));
+            const uint2 bx = make_uint2(__float_as_uint(e.r.z), __float_as_uint(e.r.w));
+            hm = half_mask(bx, x0, y0);
+            eslot[tid] = emit_slot(__float_as_uint(e.s.x), bx, x0 / kTile, y0 / kTile);
+        } else {
+            rp = records[2 * g];
+            rq = records[2 * g + 1];
+            rr = make_float4(opacity[g], __uint_as_float(idx), 0.0f, __uint_as_float(g));
+            hm = half_mask(pixbox[g], x0, y0);
+        }
     }
     if (own) *own = make_float4(rp.z, rp.w, rq.x, rr.z);     // a, b, c, so
     uint32_t rank[2];
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_fwd(int W, int H
 
     for (uint32_t base = rg.x; base < rg.y; base += kBatch) {
         const uint32_t hi = rg.y - base > (uint32_t)kBatch ? base + kBatch : rg.y;
-        const int cnt = stage_alpha(lst, wq, base, hi, x0, y0, records, opacity, nullptr, pixbox, vals, below);
+        const int cnt = stage_alpha(lst, wq, base, hi, x0, y0, records, opacity, pixbox, vals, below);
         const AlphaRec *L = lst[wave];
         for (int k = 0; k < cnt; ++k) {
             if (__ballot(!(done0 && done1)) == 0) break;
@@ -250,12 +261,31 @@ __device__ __forceinline__ float alpha_back_pixel(bool act, float e, float o, fl
     return dal * al;
 }
 
+// The packed entry records of n Gaussians (AlphaPack above), one float4 per thread: coalesced stores.
+__global__ __launch_bounds__(256) void k_alpha_pack(int n, const float4 *__restrict__ records,
+                                                    const float *__restrict__ opacity, const float *__restrict__ logit,
+                                                    const uint2 *__restrict__ pixbox,
+                                                    const uint32_t *__restrict__ offsets, float4 *__restrict__ pack) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 i % 4 of Gaussian i / 4
+    const int64_t g = i >> 2;
+    if (g >= n) return;
+    const int k = (int)(i & 3);
+    float4 v;
+    if (k < 2) {
+        v = records[2 * g + k];
+    } else if (k == 2) {
+        const float o = opacity[g];
+        const float so = logit ? (logit[g] < kLogitMax ? o * (1.0f - o) : 0.0f) : 0.0f;
+        const uint2 bx = pixbox[g];
+        v = make_float4(o, so, __uint_as_float(bx.x), __uint_as_float(bx.y));
+    } else {
+        v = make_float4(__uint_as_float(offsets[g]), 0.0f, 0.0f, 0.0f);
+    }
+    pack[i] = v;
+}
+
 __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H, int tiles_x, int ntiles,
-                                                          const float4 *__restrict__ records,
-                                                          const float *__restrict__ opacity,
-                                                          const float *__restrict__ logit,
-                                                          const uint2 *__restrict__ pixbox,
-                                                          const uint32_t *__restrict__ offsets,
+                                                          const AlphaPack *__restrict__ pack,
                                                           const uint2 *__restrict__ ranges, const uint32_t *__restrict__ order,
                                                           const uint32_t *__restrict__ vals, uint32_t capacity,
                                                           const float *__restrict__ bg,
@@ -314,8 +344,9 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
     const uint32_t bend0 = max(wmax[0], wmax[1]);
     // entries behind every pixel's stop contribute nothing: their slots get zeros
     for (uint32_t idx = bend0 + tid; idx < rg.y; idx += kAlphaThreads) {
-        const uint32_t g = vals[idx];
-        const uint32_t slot = emit_slot(offsets[g], pixbox[g], x0 / kTile, y0 / kTile);
+        const AlphaPack &e = pack[vals[idx]];
+        const uint32_t slot = emit_slot(__float_as_uint(e.s.x), make_uint2(__float_as_uint(e.r.z), __float_as_uint(e.r.w)),
+                                        x0 / kTile, y0 / kTile);
         if (slot < capacity) {
             part[2 * (size_t)slot] = make_float4(0.f, 0.f, 0.f, 0.f);
             part[2 * (size_t)slot + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -329,8 +360,8 @@ __global__ __launch_bounds__(kAlphaThreads) void k_render_alpha_bwd(int W, int H
         const uint32_t lo = hi - rg.x > (uint32_t)kBatch ? hi - kBatch : rg.x;
         __syncthreads();                                   // previous batch fully consumed
         float4 own;
-        const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, records, opacity, logit, pixbox, vals, below,
-                                    offsets, eslot, qpos, &own);
+        const int cnt = stage_alpha(lst, wq, lo, hi, x0, y0, nullptr, nullptr, nullptr, vals, below, pack, eslot,
+                                    qpos, &own);
         const AlphaRec *L = lst[wave];
         float *res = reinterpret_cast<float *>(&lst[wave][0]);   // entry k's results: res[12 k + 0..8]
         // groups of 8 entries, back to front; per lane (two pixels) and entry 9 values (the pixels'
@@ -567,18 +598,26 @@ hipError_t launch_render_alpha_fwd(int W, int H, const float *records, const flo
     return hipGetLastError();
 }
 
-hipError_t launch_render_alpha_bwd(int W, int H, const float *records, const float *opacity, const float *logit,
-                                   const uint16_t *pixbox, const uint32_t *offsets, const uint32_t *ranges,
-                                   const uint32_t *order, const uint32_t *vals, int64_t capacity,
-                                   const float *background,
-                                   const float *t_final, const uint32_t *last, const float *dL_dimage, void *ws,
-                                   hipStream_t s) {
+// The alpha backward's workspace: the pair slots of make_bwd_plan, then the packed entry records.
+size_t alpha_bwd_workspace_bytes(int W, int H, int64_t n, int64_t capacity) {
+    return make_bwd_plan(W, H, capacity).bytes + (((size_t)(n > 0 ? n : 1) * sizeof(AlphaPack) + 255) & ~(size_t)255);
+}
+
+hipError_t launch_render_alpha_bwd(int W, int H, int64_t n, const float *records, const float *opacity,
+                                   const float *logit, const uint16_t *pixbox, const uint32_t *offsets,
+                                   const uint32_t *ranges, const uint32_t *order, const uint32_t *vals,
+                                   int64_t capacity, const float *background, const float *t_final,
+                                   const uint32_t *last, const float *dL_dimage, void *ws, hipStream_t s) {
     const int tiles_x = (W + kTile - 1) / kTile, ntiles = tiles_x * ((H + kTile - 1) / kTile);
     const BwdPlan p = make_bwd_plan(W, H, capacity);
     char *w = static_cast<char *>(ws);
+    AlphaPack *pack = reinterpret_cast<AlphaPack *>(w + p.bytes);
+    if (n > 0)
+        k_alpha_pack<<<(unsigned)((4 * n + 255) / 256), 256, 0, s>>>(
+            (int)n, reinterpret_cast<const float4 *>(records), opacity, logit, reinterpret_cast<const uint2 *>(pixbox),
+            offsets, reinterpret_cast<float4 *>(pack));
     k_render_alpha_bwd<<<padded_tiles(ntiles), kAlphaThreads, 0, s>>>(
-        W, H, tiles_x, ntiles, reinterpret_cast<const float4 *>(records), opacity, logit,
-        reinterpret_cast<const uint2 *>(pixbox), offsets, reinterpret_cast<const uint2 *>(ranges), order, vals,
+        W, H, tiles_x, ntiles, pack, reinterpret_cast<const uint2 *>(ranges), order, vals,
         (uint32_t)capacity, background, t_final, last, dL_dimage, reinterpret_cast<float4 *>(w + p.off_part),
         reinterpret_cast<float *>(w + p.off_logit), reinterpret_cast<float4 *>(w + p.off_bg));
     return hipGetLastError();
