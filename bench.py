@@ -353,7 +353,7 @@ def bench_alpha(args, w, target, params, dev):
 
 def bench_ssim(args, w, target, params, dev):
     """Sum mode with the SSIM pixel loss: one step = preprocess and binning + forward + gi_loss_ssim
-    (two stencil kernels) + backward with the gather + Adam."""
+    (one fused stencil kernel) + backward with the gather + Adam."""
     import torch
     from rasterizer_gaussian_raster_amd import gi
     from rasterizer_gaussian_raster_amd.pipeline import Fitter
@@ -384,9 +384,13 @@ def bench_ssim(args, w, target, params, dev):
     st_full = stats_us(batch_time_us(lambda: gi.gi_loss_ssim(W, H, r.image, fit.target, *lw, fit.dL, fit.loss,
                                                               fit.ssim_ws)))
     ssim_s = st["median"] * 1e-6
-    nbytes = 52 * 3 * W * H           # per entry: 16 B read + 12 B written, then 20 B read + 4 B written
+    nbytes = 20 * 3 * W * H           # per entry: image, target, the target's (mean, E[T^2]) read; dL written
     gbs = nbytes / ssim_s / 1e9
-    log(f"[bench] gi_loss_ssim {st['median']:.1f} us ({gbs:.0f} GB/s algorithmic); "
+    # per entry: two separable 11-tap filterings of three maps (x, x^2, x y, then D0..D2): 264 flop;
+    # the products, the map's derivatives and the output: 51 flop
+    nflop = 315 * 3 * W * H
+    tfs = nflop / ssim_s / 1e12
+    log(f"[bench] gi_loss_ssim {st['median']:.1f} us ({tfs:.1f} TFLOP/s, {gbs:.0f} GB/s algorithmic); "
         f"without the prepared target {st_full['median']:.1f} us")
     out = {
         "metric": METRIC,
@@ -404,13 +408,15 @@ def bench_ssim(args, w, target, params, dev):
         "config": {"workload": wl.name, "width": W, "height": H, "gaussians": wl.n, "mode": "sum",
                    "loss": {"w1": lw[0], "w2": lw[1], "ws": lw[2]}},
         "timing": "value: K steps after W warm-up steps, host clock with device syncs on both sides; "
-                  "roofline: medians over batches of back-to-back gi_loss_ssim calls (two kernels) between HIP "
+                  "roofline: medians over batches of back-to-back gi_loss_ssim calls (one kernel) between HIP "
                   "events on the launch stream",
         "final_loss": final_loss,
         "kernels_us": {"loss_ssim": st, "loss_ssim_target_unprepared": st_full},
-        "roofline": {"bound": "hbm", "kernel": "k_ssim_fwd + k_ssim_bwd", "achieved": round(gbs, 1),
-                     "peak": PEAK_HBM, "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4), "traffic": None,
-                     "avg_launch_us": round(ssim_s * 1e6, 2)},
+        "roofline": {"bound": "alu", "kernel": "k_ssim_loss", "achieved": round(tfs, 2), "peak": PEAK_FP32,
+                     "unit": "TFLOP/s", "frac": round(tfs / PEAK_FP32, 4), "traffic": None,
+                     "avg_launch_us": round(ssim_s * 1e6, 2), "flop_per_entry": 315,
+                     "hbm": {"achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM, 4), "bytes_per_entry": 20}},
         "cpu_baseline": None,
     }
     emit(out)

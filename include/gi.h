@@ -577,20 +577,26 @@ gi_status gi_grad_gather(const gi_desc *desc, int32_t kind, int64_t n, const flo
  *   image's size),
  *     SSIM(p) = (2 mx my + C1)(2 sxy + C2) / ((mx^2 + my^2 + C1)(sxx + syy + C2)),
  *   C1 = 0.01^2, C2 = 0.03^2 (x = I, y = T).  d|e|/de = sign(e), 0 at 0.
- *   Two stencil kernels (fp32); the loss is added up in fp64 in a fixed order.
+ *   One fused stencil kernel (fp32) per call; the loss is added up in fp64 in
+ *   a fixed order by the workgroup that finishes last.
  *   image, target  device float [3][H][W].
  *   dL_dimage      device float [3][H][W], written; must not alias the inputs.
  *   d_loss         device float [1] (written: L) or NULL.
- *   workspace      device, >= gi_loss_ssim_workspace_bytes(W, H), 256-byte aligned.
- *   flags          0, or GI_SSIM_TARGET_PREPARED: the workspace holds the window
- *                  statistics of this target from gi_loss_ssim_target (the target
- *                  is unchanged since); the call then filters only the image's
- *                  maps.  Same results, bit for bit, as without the flag.
+ *   workspace      device, >= gi_loss_ssim_workspace_bytes(W, H), 256-byte aligned;
+ *                  calls that share a workspace must not overlap.
+ *   flags          0: the call first forms this target's window statistics in
+ *                  the workspace (as gi_loss_ssim_target does), replacing any
+ *                  there.  GI_SSIM_TARGET_PREPARED: the workspace holds them
+ *                  from gi_loss_ssim_target (or an unflagged call) with this
+ *                  target, unchanged since, and the workspace has not been
+ *                  written by the caller since; the call then skips that step.
+ *                  Same results, bit for bit, either way.
  *
  * gi_loss_ssim_target -- the target's window statistics (its local means of T
  *   and T^2, the fitting loop's constant half of SSIM) into the workspace, for
- *   later gi_loss_ssim calls with GI_SSIM_TARGET_PREPARED.  Same arguments as
- *   above; the other workspace contents are left alone.
+ *   later gi_loss_ssim calls with GI_SSIM_TARGET_PREPARED; it also resets the
+ *   workspace's count of finished tiles that the loss reduction uses.  Same
+ *   arguments as above.
  */
 #define GI_SSIM_TARGET_PREPARED 1u
 size_t gi_loss_ssim_workspace_bytes(int32_t width, int32_t height);

@@ -6,35 +6,32 @@
 // The gradient of the mean SSIM needs the window sums of three per-pixel derivatives of the map
 // (with respect to mx, Exx = <x^2>, Exy = <x y>):
 //   dSSIM/dx(q) = (1/3HW) sum_p G(q - p) [D0(p) + 2 x(q) D1(p) + y(q) D2(p)].
-// Two stencil kernels over 32x32 output tiles, one workgroup per tile and channel, the window
-// separable (rows, then columns):
-//   k_ssim_fwd  stages x, y of the tile and a 5-pixel halo in LDS; the row pass gives each thread
-//               four adjacent outputs of a staged row (14 inputs, their products formed once, read
-//               as float4 runs), the column pass four vertically adjacent outputs of a column; it
-//               writes D0..D2 and per-tile partial sums (SSIM, |e|, e^2);
-//   k_ssim_bwd  stages D0..D2 with the halo, filters them the same way and forms dL/dx; its spare
-//               last workgroup adds up the partials (fp64, fixed order) into the loss.
-// Both are FP32-VALU bound: 5 (then 3) maps x 11 taps per pass and output, the row pass over
-// 42 staged rows per 32 output rows.  HBM: 8 B read + 12 B written per entry, then 20 B read +
-// 4 B written.
+// The window is separable: every filtering below is a row pass then a column pass.
+//   k_ssim_target  the target's half of the statistics (my, Eyy per pixel), the same for every
+//                  image of a fit: formed once into the workspace as float2 planes;
+//   k_ssim_loss    the rest in one pass per 48x32 output tile and channel: it stages x, y over the
+//                  tile and a 10-pixel border (float4 loads), filters x, x^2, x y over the tile and
+//                  a 5-pixel border, forms D0..D2 there, filters those in turn and writes dL/dx of
+//                  the tile with the tile's partial sums (SSIM, |e|, e^2); the workgroup that
+//                  finishes last adds up the partials (fp64, fixed order) into the loss.
+// No per-pixel map goes through memory between the passes: HBM sees x, y, (my, Eyy) and dL/dx once
+// (20 B per entry).  The work is FP32 VALU: per tile and map 52 x 60 row-pass outputs and 42 x 58
+// statistics, then 42 x 48 and 32 x 48 for D, 11 taps each.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 
+#include "gi_device.hpp"
 #include "gi_launch.hpp"
 
 namespace gi {
 
 constexpr int kSsimR = 5;                                   // window radius
-constexpr int kSsimTW = 32, kSsimTH = 32;                   // output tile
-constexpr int kSsimSW = kSsimTW + 2 * kSsimR;               // staged columns (42)
-constexpr int kSsimSH = kSsimTH + 2 * kSsimR;               // staged rows (42)
-constexpr int kSsimSP = (kSsimSW + 2 + 3) & ~3;             // staged row stride: 16-byte rows, room for
-                                                            // the last group's 14-wide read (44)
-constexpr int kSsimNG = kSsimTW / 4;                        // 4-column groups per row (8)
-constexpr int kSsimStageRounds = (kSsimSH + 3) / 4;         // staging: 4 rows x 64 columns per round
-static_assert(kSsimSW <= 64, "a staged row is one wave wide");
+constexpr int kSsimT = 32;                                  // output tile (32 x 32)
 constexpr float kC1 = 0.0001f, kC2 = 0.0009f;
+constexpr int kSsimGroups = 8;                              // first-level ticket counters of the loss
+constexpr int kSsimCountStride = 64;                        // unsigned: one counter per 256 bytes
 
 struct SsimWin { float g[11]; };
 
@@ -49,223 +46,381 @@ __device__ __forceinline__ void lds_run14(const float *p, float (&v)[14]) {
     v[12] = d.x; v[13] = d.y;
 }
 
-// Stages NM planes (each W x H, `plane` apart) over the tile's rows and columns plus the halo into
-// s[m][row][col] (zero outside the image).  Thread (tid / 64, tid % 64) takes column tid % 64 of
-// rows tid / 64 + 4k: every row is one contiguous read; all loads go out before the first store.
-template <int NM>
-__device__ __forceinline__ void ssim_stage(const float *__restrict__ src, size_t plane, int W, int H, int x0, int y0,
-                                           float (*s)[kSsimSH][kSsimSP]) {
-    const int tid = threadIdx.x, c = tid & 63, r0 = tid >> 6;
-    const int gx = x0 - kSsimR + c;
-    const bool colok = c < kSsimSW && gx >= 0 && gx < W;
-    float v[NM][kSsimStageRounds];
+// The window over 14 consecutive inputs: four adjacent outputs (taps in a fixed order).
+__device__ __forceinline__ float4 win4(const float (&v)[14], const SsimWin &w) {
+    float o[4];
 #pragma unroll
-    for (int k = 0; k < kSsimStageRounds; ++k) {
-        const int r = r0 + 4 * k, gy = y0 - kSsimR + r;
-        const bool ok = colok && r < kSsimSH && gy >= 0 && gy < H;
-        const size_t o = ok ? (size_t)gy * W + gx : 0;
+    for (int h = 0; h < 4; ++h) {
+        float a = 0.f;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) v[m][k] = ok ? src[m * plane + o] : 0.0f;
+        for (int b = 0; b < 11; ++b) a = fmaf(w.g[b], v[b + h], a);
+        o[h] = a;
     }
-    if (c < kSsimSW) {
-#pragma unroll
-        for (int k = 0; k < kSsimStageRounds; ++k) {
-            const int r = r0 + 4 * k;
-            if (r < kSsimSH) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m) s[m][r][c] = v[m][k];
-            }
-        }
-    }
+    return make_float4(o[0], o[1], o[2], o[3]);
 }
 
-struct SsimFwdLds {
-    alignas(16) float s[2][kSsimSH][kSsimSP];      // x, y of the staged pixels
-    alignas(16) float h[3][kSsimSH][kSsimTW];      // row pass: (x, y), then (x^2, y^2, x y)
-    float red[3][4];
+// ---------------------------------------------------------------------------------------------
+// k_ssim_target: (my, Eyy) of every pixel of channel blockIdx.z, one 32x32 tile per workgroup.
+
+constexpr int kTgSW = kSsimT + 2 * kSsimR;                  // staged columns and rows (42)
+constexpr int kTgSP = 44;                                   // staged row stride (16-byte rows)
+constexpr int kTgRounds = (kTgSW + 3) / 4;                  // staging: 4 rows x 64 columns per round
+constexpr int kTgRowTasks = kTgSW * (kSsimT / 4);           // 336
+static_assert(kTgSW <= 64 && kTgRowTasks <= 512, "one staged row per wave, two row tasks per thread");
+
+struct SsimTargetLds {
+    alignas(16) float s[kTgSW][kTgSP];                      // y of the staged pixels
+    alignas(16) float h[2][kTgSW][kSsimT];                  // row pass of y, y^2
 };
 
-// The maps a forward pass filters, by mode: kSsimFull filters x, y (first pass) and x^2, y^2, x y
-// (second); kSsimPrepared takes the target's from the workspace and filters x, then x^2, x y;
-// kSsimTarget filters the target's alone, y then y^2 (what kSsimPrepared reads).
-enum SsimMode { kSsimFull = 0, kSsimPrepared = 1, kSsimTarget = 2 };
-template <int MODE, bool SECOND>
-struct SsimMaps {
-    static constexpr int n = MODE == kSsimFull ? (SECOND ? 3 : 2) : MODE == kSsimPrepared ? (SECOND ? 2 : 1) : 1;
-};
-
-// Row pass for the task t (staged row t / NG, outputs 4 (t % NG) .. + 3) into h: the maps of
-// SsimMaps, products formed once per input.  Every map takes the same operations in the same order
-// in every mode, so a prepared target's statistics carry the bits of the full pass.
-template <int MODE, bool SECOND>
-__device__ __forceinline__ void ssim_fwd_rows(SsimFwdLds &L, int t, const SsimWin &win) {
-    const int r = t / kSsimNG, c0 = (t % kSsimNG) * 4;
-    constexpr int NM = SsimMaps<MODE, SECOND>::n;
-    float in[NM][14];
-    {
-        float xv[14], yv[14];
-        if (MODE != kSsimTarget) lds_run14(&L.s[0][r][c0], xv);
-        if (MODE != kSsimPrepared || SECOND) lds_run14(&L.s[1][r][c0], yv);
-#pragma unroll
-        for (int b = 0; b < 14; ++b) {
-            if (MODE == kSsimFull) {
-                if (SECOND) {
-                    in[0][b] = xv[b] * xv[b];
-                    in[1][b] = yv[b] * yv[b];
-                    in[2][b] = xv[b] * yv[b];
-                } else {
-                    in[0][b] = xv[b];
-                    in[1][b] = yv[b];
-                }
-            } else if (MODE == kSsimPrepared) {
-                if (SECOND) {
-                    in[0][b] = xv[b] * xv[b];
-                    in[NM - 1][b] = xv[b] * yv[b];
-                } else {
-                    in[0][b] = xv[b];
-                }
-            } else {
-                in[0][b] = SECOND ? yv[b] * yv[b] : yv[b];
-            }
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < NM; ++k) {
-        float4 o;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            float a = 0.f;
-#pragma unroll
-            for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], in[k][b + h], a);
-            reinterpret_cast<float *>(&o)[h] = a;
-        }
-        *reinterpret_cast<float4 *>(&L.h[k][r][c0]) = o;
-    }
-}
-
-// Column pass of NM maps of h: the four outputs (column tx, rows ty0 .. ty0 + 3) of each.
-template <int NM>
-__device__ __forceinline__ void ssim_cols(const float (*h)[kSsimSH][kSsimTW], int tx, int ty0, const SsimWin &win,
-                                          float (&out)[4][NM]) {
-#pragma unroll
-    for (int k = 0; k < NM; ++k) {
-        float hv[14];
-#pragma unroll
-        for (int a = 0; a < 14; ++a) hv[a] = h[k][ty0 + a][tx];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float m = 0.f;
-#pragma unroll
-            for (int a = 0; a < 11; ++a) m = fmaf(win.g[a], hv[a + q], m);
-            out[q][k] = m;
-        }
-    }
-}
-
-constexpr int kSsimRowTasks = kSsimSH * kSsimNG;           // 336: one round of 256 threads + 80
-static_assert(kSsimRowTasks <= 512, "at most two row tasks per thread");
-
-// T: the target's window statistics, planes T[c] = mean of channel c, T[3 + c] = mean of its square
-// (written by kSsimTarget, read by kSsimPrepared).
-template <int MODE>
-__global__ __launch_bounds__(256) void k_ssim_fwd(int W, int H, const float *__restrict__ x,
-                                                  const float *__restrict__ y, SsimWin win,
-                                                  float *__restrict__ D, float *__restrict__ part,
-                                                  float *__restrict__ T) {
-    __shared__ __align__(16) SsimFwdLds L;
+__global__ __launch_bounds__(256) void k_ssim_target(int W, int H, const float *__restrict__ y, SsimWin win,
+                                                     float2 *__restrict__ T, unsigned *__restrict__ done) {
+    __shared__ __align__(16) SsimTargetLds L;
     const int tid = threadIdx.x, ch = blockIdx.z;
-    const int x0 = blockIdx.x * kSsimTW, y0 = blockIdx.y * kSsimTH;
+    const int x0 = blockIdx.x * kSsimT, y0 = blockIdx.y * kSsimT;
     const size_t plane = (size_t)W * H;
-    const int tx = tid & (kSsimTW - 1), ty0 = (tid / kSsimTW) * 4;   // this thread's four outputs
-    const int j = x0 + tx;
-    float ty_m[4], ty_e[4];                               // kSsimPrepared: the target's statistics
-    if (MODE == kSsimPrepared) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = y0 + ty0 + q;
-            const size_t o = (i < H && j < W) ? (size_t)i * W + j : 0;
-            ty_m[q] = T[ch * plane + o];
-            ty_e[q] = T[(3 + ch) * plane + o];
-        }
-    }
+    const float *yc = y + ch * plane;
+    if (done && (blockIdx.x | blockIdx.y | blockIdx.z) == 0 && tid <= kSsimGroups)   // the loss's completion counts
+        done[kSsimCountStride * tid] = 0;
     {
-        // x and y (separate arrays): the staging of ssim_stage, two sources
-        const float *xc = MODE == kSsimTarget ? nullptr : x + ch * plane, *yc = y + ch * plane;
-        const int c = tid & 63, r0 = tid >> 6;
-        const int gx = x0 - kSsimR + c;
-        const bool colok = c < kSsimSW && gx >= 0 && gx < W;
-        float vx[kSsimStageRounds], vy[kSsimStageRounds];
+        // thread (tid / 64, tid % 64) stages column tid % 64 of rows tid / 64 + 4k
+        const int c = tid & 63, r0 = tid >> 6, gx = x0 - kSsimR + c;
+        const bool colok = c < kTgSW && gx >= 0 && gx < W;
+        float v[kTgRounds];
 #pragma unroll
-        for (int k = 0; k < kSsimStageRounds; ++k) {
+        for (int k = 0; k < kTgRounds; ++k) {
             const int r = r0 + 4 * k, gy = y0 - kSsimR + r;
-            const bool ok = colok && r < kSsimSH && gy >= 0 && gy < H;
-            const size_t o = ok ? (size_t)gy * W + gx : 0;
-            if (MODE != kSsimTarget) vx[k] = ok ? xc[o] : 0.0f;
-            vy[k] = ok ? yc[o] : 0.0f;
+            const bool ok = colok && r < kTgSW && gy >= 0 && gy < H;
+            v[k] = ok ? yc[(size_t)gy * W + gx] : 0.0f;
         }
-        if (c < kSsimSW) {
+        if (c < kTgSW) {
 #pragma unroll
-            for (int k = 0; k < kSsimStageRounds; ++k) {
-                const int r = r0 + 4 * k;
-                if (r < kSsimSH) {
-                    if (MODE != kSsimTarget) L.s[0][r][c] = vx[k];
-                    L.s[1][r][c] = vy[k];
-                }
-            }
+            for (int k = 0; k < kTgRounds; ++k)
+                if (r0 + 4 * k < kTgSW) L.s[r0 + 4 * k][c] = v[k];
         }
     }
     __syncthreads();
-    // the means
-    constexpr int NA = SsimMaps<MODE, false>::n, NB = SsimMaps<MODE, true>::n;
-    ssim_fwd_rows<MODE, false>(L, tid, win);
-    if (tid + 256 < kSsimRowTasks) ssim_fwd_rows<MODE, false>(L, tid + 256, win);
-    __syncthreads();
-    float mu[4][NA];
-    ssim_cols<NA>(L.h, tx, ty0, win, mu);
-    __syncthreads();                                      // h is rewritten
-    // the second moments
-    ssim_fwd_rows<MODE, true>(L, tid, win);
-    if (tid + 256 < kSsimRowTasks) ssim_fwd_rows<MODE, true>(L, tid + 256, win);
-    __syncthreads();
-    float m2[4][NB];
-    ssim_cols<NB>(L.h, tx, ty0, win, m2);
-    if (MODE == kSsimTarget) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = y0 + ty0 + q;
-            if (i < H && j < W) {
-                T[ch * plane + (size_t)i * W + j] = mu[q][0];
-                T[(3 + ch) * plane + (size_t)i * W + j] = m2[q][0];
-            }
+    for (int u = 0; u < 2; ++u) {
+        const int t = tid + 256 * u;
+        if (t < kTgRowTasks) {
+            const int r = t / (kSsimT / 4), c0 = (t % (kSsimT / 4)) * 4;
+            float v[14], v2[14];
+            lds_run14(&L.s[r][c0], v);
+#pragma unroll
+            for (int b = 0; b < 14; ++b) v2[b] = v[b] * v[b];
+            *reinterpret_cast<float4 *>(&L.h[0][r][c0]) = win4(v, win);
+            *reinterpret_cast<float4 *>(&L.h[1][r][c0]) = win4(v2, win);
         }
-        return;
     }
-    float f = 0.f, l1 = 0.f, l2 = 0.f;
+    __syncthreads();
+    const int tx = tid & (kSsimT - 1), ty0 = (tid / kSsimT) * 4, j = x0 + tx;
+    float hv[2][14];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int a = 0; a < 14; ++a) hv[k][a] = L.h[k][ty0 + a][tx];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int ty = ty0 + q, i = y0 + ty;
-        if (i < H && j < W) {
-            const float mx = mu[q][0], my = MODE == kSsimFull ? mu[q][NA - 1] : ty_m[q];
-            const float exx = m2[q][0], eyy = MODE == kSsimFull ? m2[q][1] : ty_e[q], exy = m2[q][NB - 1];
-            const float sxx = exx - mx * mx, syy = eyy - my * my, sxy = exy - mx * my;
-            const float n1 = fmaf(2.0f * mx, my, kC1), n2 = fmaf(2.0f, sxy, kC2);
-            const float d1 = mx * mx + my * my + kC1, d2 = sxx + syy + kC2;
-            // hardware reciprocals (1 ulp): the divisions' rounding is far below the loss's tolerance
-            const float rn1 = __builtin_amdgcn_rcpf(n1), rn2 = __builtin_amdgcn_rcpf(n2);
-            const float rd1 = __builtin_amdgcn_rcpf(d1), rd2 = __builtin_amdgcn_rcpf(d2);
-            const float fr = (n1 * n2) * (rd1 * rd2);
-            f += fr;
-            const float D0 = fr * (2.0f * my * (rn1 - rn2) + 2.0f * mx * (rd2 - rd1));
-            const size_t o = ch * plane + (size_t)i * W + j;
-            D[o] = D0;
-            D[3 * plane + o] = -fr * rd2;
-            D[6 * plane + o] = 2.0f * fr * rn2;
-            const float e = L.s[0][ty + kSsimR][tx + kSsimR] - L.s[1][ty + kSsimR][tx + kSsimR];
-            l1 += fabsf(e);
-            l2 += e * e;
+        const int i = y0 + ty0 + q;
+        float m[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float a = 0.f;
+#pragma unroll
+            for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], hv[k][b + q], a);
+            m[k] = a;
+        }
+        if (i < H && j < W) T[ch * plane + (size_t)i * W + j] = make_float2(m[0], m[1]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_ssim_loss: one workgroup per 48x32 output tile and channel (a 768x512 image has 768 of them,
+// three per CU of MI355X, in one round).  Regions, relative to the tile's origin (x0, y0):
+//   staged      rows y0 - 10 .. y0 + 41 (52), columns x0 - 10 .. x0 + 57 (68);
+//   statistics  rows y0 - 5 .. y0 + 36 (42), columns x0 - 5 .. x0 + 52 (58; the row pass forms 60
+//               in groups of four, the last two unused);
+//   D           the statistics region.
+// LDS holds the staged maps, ONE map's row pass at a time (x, then x^2, then x y; later D0, D1, D2
+// in turn) and one of D0..D2, about 51 KB.  Every row stride is an odd multiple of 4 floats, and the tasks that
+// read or write float4 runs give a wave's lanes consecutive rows of one column group, so each 8
+// lanes' float4 accesses cover the 32 banks once.
+constexpr int kLossNT = 512;                                // threads per workgroup (8 waves)
+constexpr int kLossWaves = kLossNT / 64;
+constexpr int kTW = 48, kTH = 32;                           // output tile
+constexpr int kSR = kTH + 4 * kSsimR;                       // 52 staged rows
+constexpr int kSC = kTW + 4 * kSsimR;                       // 68 staged columns
+constexpr int kSP = 68;                                     // staged row stride (4 mod 32)
+constexpr int kSV = (kTW + 24) / 4;                         // float4 loads per staged row (from x0 - 12)
+constexpr int kSN4 = kSR * kSV;                             // 936 per map
+constexpr int kMR = kTH + 2 * kSsimR;                       // 42 statistics rows
+constexpr int kMC = kTW + 2 * kSsimR;                       // 58 statistics columns
+constexpr int kMG = (kMC + 3) / 4;                          // 15 row-pass column groups
+constexpr int kHP = 4 * kMG;                                // 60: row-pass stride (28 mod 32)
+constexpr int kRowTasks = kSR * kMG;                        // 780
+constexpr int kColGroups = (kMR + 3) / 4;                   // 11 (the last one starts at row 38)
+constexpr int kColTasks = kMC * kColGroups;                 // 638
+constexpr int kDP = 60;                                     // D stride (28 mod 32)
+constexpr int kBG = kTW / 4;                                // 12 D row-pass column groups
+constexpr int kBRowTasks = kMR * kBG;                       // 504
+constexpr int kBP = 52;                                     // D row-pass stride (20 mod 32)
+constexpr int kOutTasks = kTW * (kTH / 4);                  // 384 tasks of four outputs
+constexpr int rounds(int n) { return (n + kLossNT - 1) / kLossNT; }
+static_assert(kSP >= kSC && kDP >= kMC && kBP >= kTW, "strides");
+static_assert(4 * (kMG - 1) + 14 <= kSP + 2 && 4 * (kBG - 1) + 14 <= kMC, "row-pass reads");
+
+struct SsimLossLds {
+    alignas(16) float s[2][kSR][kSP];                       // x, y staged (kept to the end)
+    alignas(16) float d[kMR][kDP];                          // one of D0..D2 over the statistics region
+    union {
+        alignas(16) float h[kSR][kHP];                      // row pass of one of x, x^2, x y
+        alignas(16) float hb[kMR][kBP];                     // row pass of one of D0..D2
+    };
+    float red[3][kLossWaves];
+    double dred[3][kLossWaves];
+    int last;
+};
+// the row pass's last column group reads two floats past the end of its row (for the two unused
+// outputs): the next row's, or for the last row of y the first two of d, which follows s
+static_assert(offsetof(SsimLossLds, d) == sizeof(float) * 2 * kSR * kSP, "d follows s");
+
+// Stages x and y (one channel each) over the staged region into s (zero outside the image), in two
+// halves so that other loads can be issued between them: ssim_stage_load issues this thread's loads,
+// ssim_stage_store writes them.  Loads are float4s from x0 - 12 (VEC: W a multiple of 4 and 16-byte
+// aligned planes, so each float4 of a row lies wholly inside or wholly outside the image; else
+// element by element), stored as two float2 halves two columns to the left (the halves outside the
+// staged columns are dropped).
+constexpr int kStageRounds = rounds(kSN4);                  // 2
+template <bool VEC>
+__device__ __forceinline__ void ssim_stage_load(const float *__restrict__ x, const float *__restrict__ y, int W,
+                                                int H, int x0, int y0, float4 (&vx)[kStageRounds],
+                                                float4 (&vy)[kStageRounds]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kStageRounds; ++k) {
+        const int f = tid + kLossNT * k, r = f / kSV, c = (f - r * kSV) * 4;
+        const int gy = y0 - 2 * kSsimR + r, gx = x0 - 12 + c;
+        const bool rowok = f < kSN4 && gy >= 0 && gy < H;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (VEC) {
+            if (rowok && gx >= 0 && gx < W) {
+                const size_t o = (size_t)gy * W + gx;
+                a = *reinterpret_cast<const float4 *>(x + o);
+                b = *reinterpret_cast<const float4 *>(y + o);
+            }
+        } else if (rowok) {
+            const size_t row = (size_t)gy * W;
+            float *pa = reinterpret_cast<float *>(&a), *pb = reinterpret_cast<float *>(&b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (gx + e >= 0 && gx + e < W) {
+                    pa[e] = x[row + gx + e];
+                    pb[e] = y[row + gx + e];
+                }
+        }
+        vx[k] = a;
+        vy[k] = b;
+    }
+}
+__device__ __forceinline__ void ssim_stage_store(const float4 (&vx)[kStageRounds], const float4 (&vy)[kStageRounds],
+                                                 float (*s)[kSR][kSP]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kStageRounds; ++k) {
+        const int f = tid + kLossNT * k, r = f / kSV, c = (f - r * kSV) * 4 - 2;
+        if (f < kSN4) {
+            if (c >= 0) {
+                *reinterpret_cast<float2 *>(&s[0][r][c]) = make_float2(vx[k].x, vx[k].y);
+                *reinterpret_cast<float2 *>(&s[1][r][c]) = make_float2(vy[k].x, vy[k].y);
+            }
+            if (c + 2 < kSC) {
+                *reinterpret_cast<float2 *>(&s[0][r][c + 2]) = make_float2(vx[k].z, vx[k].w);
+                *reinterpret_cast<float2 *>(&s[1][r][c + 2]) = make_float2(vy[k].z, vy[k].w);
+            }
         }
     }
-    // tile partials, reduced in a fixed order
+}
+
+// Row pass task t of map MAP (0: x, 1: x^2, 2: x y): staged row t % 52, statistics columns
+// 4 (t / 52) .. + 3.
+template <int MAP>
+__device__ __forceinline__ void ssim_loss_rows(SsimLossLds &L, int t, const SsimWin &win) {
+    const int g = t / kSR, r = t - g * kSR, c0 = 4 * g;
+    float v[14];
+    lds_run14(&L.s[0][r][c0], v);
+    if (MAP == 1) {
+#pragma unroll
+        for (int b = 0; b < 14; ++b) v[b] = v[b] * v[b];
+    } else if (MAP == 2) {
+        float w[14];
+        lds_run14(&L.s[1][r][c0], w);
+#pragma unroll
+        for (int b = 0; b < 14; ++b) v[b] = v[b] * w[b];
+    }
+    *reinterpret_cast<float4 *>(&L.h[r][c0]) = win4(v, win);
+}
+
+// Column task u: statistics column u % 58, rows i0 .. i0 + 3, i0 = 4 (u / 58) (38 for the last
+// group, which keeps rows 40, 41 only).
+__device__ __forceinline__ void ssim_col_task(int u, int &jj, int &i0) {
+    const int g = u / kMC;
+    jj = u - g * kMC;
+    i0 = g < kColGroups - 1 ? 4 * g : kMR - 4;
+}
+
+// The 11-tap window down a column of an LDS map (row stride P) from its first row: four vertically
+// adjacent outputs.
+template <int P>
+__device__ __forceinline__ void ssim_col4(const float *col, const SsimWin &win, float (&o)[4]) {
+    float hv[14];
+#pragma unroll
+    for (int a = 0; a < 14; ++a) hv[a] = col[a * P];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float a = 0.f;
+#pragma unroll
+        for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], hv[b + q], a);
+        o[q] = a;
+    }
+}
+
+constexpr int kColRounds = rounds(kColTasks);               // 2
+
+// One statistics map: its row pass into h, then the column pass of this thread's column tasks.
+template <int MAP>
+__device__ __forceinline__ void ssim_loss_map(SsimLossLds &L, const SsimWin &win, const int (&jj)[kColRounds],
+                                              const int (&i0)[kColRounds], float (&m)[kColRounds][4]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < rounds(kRowTasks); ++k)
+        if (tid + kLossNT * k < kRowTasks) ssim_loss_rows<MAP>(L, tid + kLossNT * k, win);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kColRounds; ++u)
+        if (tid + kLossNT * u < kColTasks) ssim_col4<kHP>(&L.h[i0[u]][jj[u]], win, m[u]);
+    __syncthreads();                                        // h is rewritten next
+}
+
+// three workgroups (24 waves) per CU: at most 80 VGPRs
+template <bool VEC>
+__global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) void k_ssim_loss(int W, int H, const float *__restrict__ x,
+                                                       const float *__restrict__ y, const float2 *__restrict__ T,
+                                                       SsimWin win, float w1, float w2, float ws,
+                                                       float *__restrict__ dL, float *__restrict__ part, int ntiles,
+                                                       int nblk, double w1d, double w2d, double wsd,
+                                                       float *__restrict__ loss, unsigned *__restrict__ done) {
+    __shared__ __align__(16) SsimLossLds L;
+    const int tile = xcd_remap(blockIdx.x, nblk);           // an XCD takes neighbouring tiles
+    if (tile >= ntiles) return;
+    const int gx = (W + kTW - 1) / kTW, gy = (H + kTH - 1) / kTH, per_ch = gx * gy;
+    const int ch = tile / per_ch, rem = tile - ch * per_ch;
+    const int x0 = (rem % gx) * kTW, y0 = (rem / gx) * kTH;
+    const size_t plane = (size_t)W * H;
+    const int tid = threadIdx.x;
+    // the staged maps' loads first, then the target's statistics at this thread's column tasks
+    // (needed later; pixel 0 of the plane stands in outside the image, where they are not used)
+    float4 vx[kStageRounds], vy[kStageRounds];
+    ssim_stage_load<VEC>(x + ch * plane, y + ch * plane, W, H, x0, y0, vx, vy);
+    int jj[kColRounds], i0[kColRounds];
+    float2 tq[kColRounds][4];
+#pragma unroll
+    for (int u = 0; u < kColRounds; ++u) {
+        ssim_col_task(tid + kLossNT * u, jj[u], i0[u]);
+        const int px = x0 - kSsimR + jj[u];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int py = y0 - kSsimR + i0[u] + q;
+            const bool ok = tid + kLossNT * u < kColTasks && px >= 0 && px < W && py >= 0 && py < H;
+            tq[u][q] = T[ch * plane + (ok ? (size_t)py * W + px : 0)];
+        }
+    }
+    ssim_stage_store(vx, vy, L.s);
+    __syncthreads();
+    // the statistics: mx, Exx, Exy at the column tasks' pixels
+    float mx[kColRounds][4], exx[kColRounds][4], exy[kColRounds][4];
+    ssim_loss_map<0>(L, win, jj, i0, mx);
+    ssim_loss_map<1>(L, win, jj, i0, exx);
+    ssim_loss_map<2>(L, win, jj, i0, exy);
+    // the map and D0..D2 there (zero outside the image)
+    float f = 0.f, D[3][kColRounds][4];
+#pragma unroll
+    for (int u = 0; u < kColRounds; ++u) {
+        const int px = x0 - kSsimR + jj[u];
+        const bool colin = tid + kLossNT * u < kColTasks && px >= 0 && px < W;
+        const bool colown = jj[u] >= kSsimR && jj[u] < kSsimR + kTW;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = i0[u] + q, py = y0 - kSsimR + i;
+            D[0][u][q] = D[1][u][q] = D[2][u][q] = 0.f;
+            if (colin && py >= 0 && py < H) {
+                const float a = mx[u][q], my = tq[u][q].x, eyy = tq[u][q].y;
+                const float xx = a * a, yy = my * my;
+                const float sxx = exx[u][q] - xx, syy = eyy - yy, sxy = exy[u][q] - a * my;
+                const float n1 = fmaf(2.0f * a, my, kC1), n2 = fmaf(2.0f, sxy, kC2);
+                const float d1 = (xx + yy) + kC1, d2 = (sxx + syy) + kC2;
+                // one hardware reciprocal (1 ulp) of d1 d2 (>= C1 C2) serves every quotient:
+                //   SSIM = n1 n2 r,  dSSIM/dmx = 2 r (my (n2 - n1) + mx SSIM (d1 - d2)),
+                //   dSSIM/dExx = -SSIM d1 r,  dSSIM/dExy = 2 n1 r,  r = 1 / (d1 d2)
+                const float r = __builtin_amdgcn_rcpf(d1 * d2);
+                const float fr = (n1 * n2) * r;
+                // the tile's own pixels (rows 38, 39 of the last group are the previous group's)
+                if (colown && i >= kSsimR && i < kSsimR + kTH) f += fr;
+                D[0][u][q] = (2.0f * r) * fmaf(a * fr, d1 - d2, my * (n2 - n1));
+                D[1][u][q] = -(fr * d1) * r;
+                D[2][u][q] = (2.0f * n1) * r;
+            }
+        }
+    }
+    // the window sums of D0, D1, D2 at this thread's four outputs (tasks below 384: column tx, rows
+    // ty0 .. ty0 + 3 of the tile), one map at a time
+    const bool outtask = tid < kOutTasks;
+    const int tx = tid % kTW, ty0 = 4 * (tid / kTW) % kTH;
+    float ss[3][4];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+        for (int u = 0; u < kColRounds; ++u) {
+            if (tid + kLossNT * u >= kColTasks) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (!(i0[u] == kMR - 4 && q < 2)) L.d[i0[u] + q][jj[u]] = D[k][u][q];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < rounds(kBRowTasks); ++u) {
+            const int t = tid + kLossNT * u;
+            if (t < kBRowTasks) {                           // lanes: consecutive rows of a column group
+                const int g = t / kMR, i = t - g * kMR, c0 = 4 * g;
+                float dv[14];
+                lds_run14(&L.d[i][c0], dv);
+                *reinterpret_cast<float4 *>(&L.hb[i][c0]) = win4(dv, win);
+            }
+        }
+        __syncthreads();
+        if (outtask) ssim_col4<kBP>(&L.hb[ty0][tx], win, ss[k]);
+        if (k < 2) __syncthreads();                         // d and hb are rewritten next
+    }
+    const double inv_n = 1.0 / (3.0 * (double)plane);
+    // 1 / (3 H W) rounded once (the products below round like the divisions they replace, to 1 ulp)
+    const float inv_nf = (float)inv_n;
+    const int j = x0 + tx;
+    float l1 = 0.f, l2 = 0.f;
+    if (outtask) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = y0 + ty0 + q;
+            if (i >= H || j >= W) continue;
+            const float xo = L.s[0][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR], yo = L.s[1][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR];
+            const float e = xo - yo;
+            l1 += fabsf(e);
+            l2 += e * e;
+            const float dssim = fmaf(yo, ss[2][q], fmaf(2.0f * xo, ss[1][q], ss[0][q])) * inv_nf;
+            const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
+            dL[ch * plane + (size_t)i * W + j] = fmaf(w1, sg * inv_nf, fmaf(w2, 2.0f * e * inv_nf, -(ws * dssim)));
+        }
+    }
+    // the tile's partial sums, reduced in a fixed order
     float v[3] = {f, l1, l2};
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -275,109 +430,60 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(int W, int H, const float *__r
         if ((tid & 63) == 0) L.red[k][tid >> 6] = s;
     }
     __syncthreads();
-    if (tid < 3) {
-        const size_t t = ((size_t)ch * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-        part[3 * t + tid] = ((L.red[tid][0] + L.red[tid][1]) + L.red[tid][2]) + L.red[tid][3];
-    }
-}
-
-struct SsimBwdLds {
-    union {                                         // the row pass overwrites the staged maps
-        alignas(16) float s[3][kSsimSH][kSsimSP];  // D0, D1, D2 of the staged pixels
-        alignas(16) float h[3][kSsimSH][kSsimTW];  // their row pass
-    };
-};
-
-// Row pass of the three staged maps for the task t (staged row t / NG, outputs 4 (t % NG) .. + 3).
-__device__ __forceinline__ void ssim_bwd_rows(const SsimBwdLds &L, int t, const SsimWin &win, float4 (&o)[3]) {
-    const int r = t / kSsimNG, c0 = (t % kSsimNG) * 4;
+    // The partials go out as device-scope stores (written through to the device's coherent level);
+    // once they have completed, the first wave takes a ticket.  The workgroup with the last ticket
+    // reads every partial back with device-scope loads.  Nothing else is published, so no cache
+    // write-back is needed on the way.
+    if (tid < 64) {
+        if (tid < 3) {
+            float t = 0.f;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        float dv[14];
-        lds_run14(&L.s[k][r][c0], dv);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            float a = 0.f;
-#pragma unroll
-            for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], dv[b + h], a);
-            reinterpret_cast<float *>(&o[k])[h] = a;
+            for (int w = 0; w < kLossWaves; ++w) t += L.red[tid][w];
+            __hip_atomic_store(&part[3 * tile + tid], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (!loss) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);                      // the stores have completed
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (tid == 0) {
+            // tickets in two levels (eight groups of workgroups, each counter on its own 256-byte line,
+            // then the groups), so no single counter takes every workgroup's atomic
+            const int per = nblk / kSsimGroups, g = blockIdx.x % kSsimGroups;
+            const int members = min(per, ntiles - g * per), groups = (ntiles + per - 1) / per;
+            unsigned *cg = done + kSsimCountStride * g, *ct = done + kSsimCountStride * kSsimGroups;
+            bool last = false;
+            if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(members - 1)) {
+                __hip_atomic_store(cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+                last = __hip_atomic_fetch_add(ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(groups - 1);
+            }
+            L.last = last;
         }
     }
-}
-
-__global__ __launch_bounds__(256) void k_ssim_bwd(int W, int H, const float *__restrict__ x,
-                                                  const float *__restrict__ y, SsimWin win,
-                                                  const float *__restrict__ D, float w1, float w2, float ws,
-                                                  float *__restrict__ dL, const float *__restrict__ part,
-                                                  int nparts, double w1d, double w2d, double wsd,
-                                                  float *__restrict__ loss) {
-    const size_t plane = (size_t)W * H;
-    const double inv_n = 1.0 / (3.0 * (double)plane);
-    // 1-D grid: the tiles (x fastest, then y, then channel), then one more workgroup for the loss
-    const int gx = (W + kSsimTW - 1) / kSsimTW, gy = (H + kSsimTH - 1) / kSsimTH;
-    const int bid = blockIdx.x, per_ch = gx * gy;
-    if (bid == 3 * per_ch) {                              // the spare workgroup: the loss
-        __shared__ double sred[3][4];
-        double a[3] = {0.0, 0.0, 0.0};
-        for (int t = threadIdx.x; t < nparts; t += 256)
+    if (!loss) return;
+    __syncthreads();
+    if (!L.last) return;
+    // the last workgroup: every tile's partials, in tile order per thread, then a fixed tree
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    double a[3] = {0.0, 0.0, 0.0};
+    for (int t = tid; t < ntiles; t += kLossNT)
 #pragma unroll
-            for (int k = 0; k < 3; ++k) a[k] += (double)part[3 * t + k];
+        for (int k = 0; k < 3; ++k)
+            a[k] += (double)__hip_atomic_load(&part[3 * t + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) a[k] += __shfl_xor(a[k], d, 64);
+        if ((tid & 63) == 0) L.dred[k][tid >> 6] = a[k];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double s[3];
         for (int k = 0; k < 3; ++k) {
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) a[k] += __shfl_xor(a[k], d, 64);
-            if ((threadIdx.x & 63) == 0) sred[k][threadIdx.x >> 6] = a[k];
+            s[k] = 0.0;
+            for (int w = 0; w < kLossWaves; ++w) s[k] += L.dred[k][w];
         }
-        __syncthreads();
-        if (threadIdx.x == 0 && loss) {
-            double t[3];
-            for (int k = 0; k < 3; ++k) t[k] = ((sred[k][0] + sred[k][1]) + sred[k][2]) + sred[k][3];
-            loss[0] = (float)(w1d * t[1] * inv_n + w2d * t[2] * inv_n + wsd * (1.0 - t[0] * inv_n));
-        }
-        return;
-    }
-    __shared__ __align__(16) SsimBwdLds L;
-    const int tid = threadIdx.x, ch = bid / per_ch, rem = bid - ch * per_ch;
-    const int x0 = (rem % gx) * kSsimTW, y0 = (rem / gx) * kSsimTH;
-    // the four outputs' x and y load with the staging (column tid % 32, rows 4 (tid / 32) ..)
-    const int tx = tid & (kSsimTW - 1), ty0 = (tid / kSsimTW) * 4;
-    const int j = x0 + tx;
-    float xv[4], yv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = y0 + ty0 + q;
-        const bool in = i < H && j < W;
-        const size_t o = ch * plane + (in ? (size_t)i * W + j : 0);
-        xv[q] = x[o];
-        yv[q] = y[o];
-    }
-    ssim_stage<3>(D + ch * plane, 3 * plane, W, H, x0, y0, L.s);
-    __syncthreads();
-    // rows: four adjacent outputs per task, held in registers until every thread has read the
-    // staged maps (the results overwrite them)
-    float4 o1[3], o2[3];
-    ssim_bwd_rows(L, tid, win, o1);
-    const bool two = tid + 256 < kSsimRowTasks;
-    if (two) ssim_bwd_rows(L, tid + 256, win, o2);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        *reinterpret_cast<float4 *>(&L.h[k][tid / kSsimNG][(tid % kSsimNG) * 4]) = o1[k];
-        if (two) *reinterpret_cast<float4 *>(&L.h[k][(tid + 256) / kSsimNG][((tid + 256) % kSsimNG) * 4]) = o2[k];
-    }
-    __syncthreads();
-    float ss[4][3];
-    ssim_cols<3>(L.h, tx, ty0, win, ss);
-    // 1 / (3 H W) rounded once (the products below round like the divisions they replace, to 1 ulp)
-    const float inv_nf = (float)inv_n;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = y0 + ty0 + q;
-        if (i >= H || j >= W) continue;
-        const float e = xv[q] - yv[q];
-        const float dssim = fmaf(yv[q], ss[q][2], fmaf(2.0f * xv[q], ss[q][1], ss[q][0])) * inv_nf;
-        const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
-        dL[ch * plane + (size_t)i * W + j] = fmaf(w1, sg * inv_nf, fmaf(w2, 2.0f * e * inv_nf, -(ws * dssim)));
+        loss[0] = (float)(w1d * s[1] * inv_n + w2d * s[2] * inv_n + wsd * (1.0 - s[0] * inv_n));
+        __hip_atomic_store(done + kSsimCountStride * kSsimGroups, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -392,50 +498,56 @@ static SsimWin ssim_window() {
     return w;
 }
 
-static size_t ssim_tiles(int W, int H) {
-    return (size_t)((W + kSsimTW - 1) / kSsimTW) * ((H + kSsimTH - 1) / kSsimTH) * 3;
-}
+static int ssim_tiles(int W, int H) { return ((W + kTW - 1) / kTW) * ((H + kTH - 1) / kTH) * 3; }
 
-// Workspace: D (9 planes) | the target's statistics T (6 planes) | the tile partials.
+// Workspace: the target's statistics T (3 planes of float2) | the tile partials | the counts of
+// finished tiles (zeroed by k_ssim_target, left at zero by every loss call).
 struct SsimWs {
-    float *D, *T, *part;
+    float2 *T;
+    float *part;
+    unsigned *done;
 };
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 static SsimWs ssim_ws(int W, int H, void *ws) {
     const size_t plane = (size_t)W * H;
     char *b = static_cast<char *>(ws);
+    const size_t tb = align256(3 * plane * sizeof(float2)), pb = align256(3 * (size_t)ssim_tiles(W, H) * sizeof(float));
     SsimWs w;
-    w.D = reinterpret_cast<float *>(b);
-    w.T = reinterpret_cast<float *>(b + align256(9 * plane * sizeof(float)));
-    w.part = reinterpret_cast<float *>(b + align256(9 * plane * sizeof(float)) + align256(6 * plane * sizeof(float)));
+    w.T = reinterpret_cast<float2 *>(b);
+    w.part = reinterpret_cast<float *>(b + tb);
+    w.done = reinterpret_cast<unsigned *>(b + tb + pb);
     return w;
 }
 
 size_t ssim_workspace_bytes(int W, int H) {
     const size_t plane = (size_t)W * H;
-    return align256(9 * plane * sizeof(float)) + align256(6 * plane * sizeof(float)) +
-           3 * ssim_tiles(W, H) * sizeof(float);
+    return align256(3 * plane * sizeof(float2)) + align256(3 * (size_t)ssim_tiles(W, H) * sizeof(float)) +
+           (kSsimGroups + 1) * kSsimCountStride * sizeof(unsigned);
 }
 
 hipError_t launch_ssim_target(int W, int H, const float *y, void *ws_ptr, hipStream_t s) {
     const SsimWs w = ssim_ws(W, H, ws_ptr);
-    const dim3 grid((W + kSsimTW - 1) / kSsimTW, (H + kSsimTH - 1) / kSsimTH, 3);
-    k_ssim_fwd<kSsimTarget><<<grid, 256, 0, s>>>(W, H, nullptr, y, ssim_window(), nullptr, nullptr, w.T);
+    const dim3 grid((W + kSsimT - 1) / kSsimT, (H + kSsimT - 1) / kSsimT, 3);
+    k_ssim_target<<<grid, 256, 0, s>>>(W, H, y, ssim_window(), w.T, w.done);
     return hipGetLastError();
 }
 
 hipError_t launch_loss_ssim(int W, int H, const float *x, const float *y, float w1, float w2, float ws, float *dL,
                             float *loss, void *ws_ptr, bool target_prepared, hipStream_t s) {
+    if (!target_prepared) {
+        const hipError_t e = launch_ssim_target(W, H, y, ws_ptr, s);
+        if (e != hipSuccess) return e;
+    }
     const SsimWin win = ssim_window();
     const SsimWs w = ssim_ws(W, H, ws_ptr);
-    const dim3 grid((W + kSsimTW - 1) / kSsimTW, (H + kSsimTH - 1) / kSsimTH, 3);
-    const int nparts = (int)ssim_tiles(W, H);
-    if (target_prepared)
-        k_ssim_fwd<kSsimPrepared><<<grid, 256, 0, s>>>(W, H, x, y, win, w.D, w.part, w.T);
+    const int ntiles = ssim_tiles(W, H), nblk = (ntiles + 7) & ~7;
+    const bool vec = W % 4 == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+    if (vec)
+        k_ssim_loss<true><<<nblk, kLossNT, 0, s>>>(W, H, x, y, w.T, win, w1, w2, ws, dL, w.part, ntiles, nblk, (double)w1,
+                                               (double)w2, (double)ws, loss, w.done);
     else
-        k_ssim_fwd<kSsimFull><<<grid, 256, 0, s>>>(W, H, x, y, win, w.D, w.part, nullptr);
-    k_ssim_bwd<<<nparts + 1, 256, 0, s>>>(W, H, x, y, win, w.D, w1, w2, ws, dL, w.part, nparts, (double)w1,
-                                          (double)w2, (double)ws, loss);
+        k_ssim_loss<false><<<nblk, kLossNT, 0, s>>>(W, H, x, y, w.T, win, w1, w2, ws, dL, w.part, ntiles, nblk,
+                                                (double)w1, (double)w2, (double)ws, loss, w.done);
     return hipGetLastError();
 }
 

@@ -103,3 +103,43 @@ def test_fit_with_ssim_loss():
     last = float(fit.loss.item())
     print(f"ssim fit: loss {first:.4e} -> {last:.4e}")
     assert np.isfinite(last) and last < 0.8 * first
+
+
+def test_ssim_loss_pointer_optional_and_unaligned_planes():
+    """Calls without d_loss leave the workspace ready for calls with it (the loss is the same bits each
+    time), and planes that are not 16-byte aligned (element-wise staging) give the bits of aligned ones."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd import gi
+    W, H = 96, 70
+    rng = np.random.default_rng(903)
+    y = rng.uniform(0, 1, (3, H, W)).astype(np.float32)
+    x = np.clip(y + rng.normal(0, 0.1, y.shape), -0.2, 1.2).astype(np.float32)
+    X, Y = dev(x), dev(y)
+    ws = torch.empty(gi.gi_loss_ssim_workspace_bytes(W, H), dtype=torch.uint8, device="cuda")
+    gi.gi_loss_ssim_target(W, H, Y, ws)
+    w = (0.8, 0.1, 0.2)
+    losses, grads = [], []
+    for with_loss in (True, False, False, True, True):
+        dL = torch.empty_like(X)
+        loss = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+        gi.gi_loss_ssim(W, H, X, Y, *w, dL, loss if with_loss else None, ws, flags=gi.SSIM_TARGET_PREPARED)
+        torch.cuda.synchronize()
+        if with_loss:
+            losses.append(float(loss.item()))
+        else:
+            assert float(loss.item()) == -1.0
+        grads.append(dL.cpu().numpy())
+    assert losses[0] == losses[1] == losses[2]
+    for g in grads[1:]:
+        np.testing.assert_array_equal(g.view(np.uint32), grads[0].view(np.uint32))
+    # planes one element past a 16-byte boundary
+    xb = torch.zeros(X.numel() + 1, dtype=torch.float32, device="cuda")
+    xb[1:] = X.reshape(-1)
+    Xu = xb[1:].view(3, H, W)
+    assert Xu.data_ptr() % 16 != 0
+    dLu = torch.empty_like(X)
+    lu = torch.zeros(1, dtype=torch.float32, device="cuda")
+    gi.gi_loss_ssim(W, H, Xu, Y, *w, dLu, lu, ws, flags=gi.SSIM_TARGET_PREPARED)
+    torch.cuda.synchronize()
+    assert float(lu.item()) == losses[0]
+    np.testing.assert_array_equal(dLu.cpu().numpy().view(np.uint32), grads[0].view(np.uint32))
