@@ -30,8 +30,8 @@ namespace gi {
 constexpr int kSsimR = 5;                                   // window radius
 constexpr int kSsimT = 32;                                  // output tile (32 x 32)
 constexpr float kC1 = 0.0001f, kC2 = 0.0009f;
-constexpr int kSsimGroups = 8;                              // first-level ticket counters of the loss
-constexpr int kSsimCountStride = 64;                        // unsigned: one counter per 256 bytes
+constexpr int kTicketGroups = 16;                           // first-level ticket counters of the loss
+constexpr int kTicketStride = 64;                           // unsigned: one counter per 256 bytes
 
 struct SsimWin { float g[11]; };
 
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(256) void k_ssim_target(int W, int H, const float *
     const int x0 = blockIdx.x * kSsimT, y0 = blockIdx.y * kSsimT;
     const size_t plane = (size_t)W * H;
     const float *yc = y + ch * plane;
-    if (done && (blockIdx.x | blockIdx.y | blockIdx.z) == 0 && tid <= kSsimGroups)   // the loss's completion counts
-        done[kSsimCountStride * tid] = 0;
+    if (done && (blockIdx.x | blockIdx.y | blockIdx.z) == 0 && tid <= kTicketGroups)   // the loss's ticket counts
+        done[kTicketStride * tid] = 0;
     {
         // thread (tid / 64, tid % 64) stages column tid % 64 of rows tid / 64 + 4k
         const int c = tid & 63, r0 = tid >> 6, gx = x0 - kSsimR + c;
@@ -372,10 +372,42 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
             }
         }
     }
-    // the window sums of D0, D1, D2 at this thread's four outputs (tasks below 384: column tx, rows
-    // ty0 .. ty0 + 3 of the tile), one map at a time
+    // this thread's four outputs (tasks below 384): column tx, rows ty0 .. ty0 + 3 of the tile
     const bool outtask = tid < kOutTasks;
-    const int tx = tid % kTW, ty0 = 4 * (tid / kTW) % kTH;
+    const int tx = tid % kTW, ty0 = 4 * (tid / kTW) % kTH, j = x0 + tx;
+    // the tile's partial sums (SSIM over its pixels, |e| and e^2 at them), reduced in a fixed order
+    // now, so that the loss's ticket is taken while D is filtered
+    {
+        float l1 = 0.f, l2 = 0.f;
+        if (outtask) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (y0 + ty0 + q >= H || j >= W) continue;
+                const float e = L.s[0][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR] - L.s[1][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR];
+                l1 += fabsf(e);
+                l2 += e * e;
+            }
+        }
+        float v[3] = {f, l1, l2};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            float sm = v[k];
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) sm += __shfl_xor(sm, d, 64);
+            if ((tid & 63) == 0) L.red[k][tid >> 6] = sm;   // read after the next barrier
+        }
+    }
+    // The partials go out as device-scope stores (written through to the device's coherent level);
+    // once they have completed, the first wave takes a ticket of its group of tiles (one D map later,
+    // so neither wait holds the workgroup up); a group's last tile takes a ticket of the groups one
+    // map later again.  The workgroup with the last of those reads every partial back with
+    // device-scope loads at its end.  Nothing else is published, so no cache write-back is needed.
+    // Sixteen group counters on their own 256-byte lines keep the atomics on one address few.
+    const int gsize = (ntiles + kTicketGroups - 1) / kTicketGroups, grp = tile / gsize;
+    const int members = min(gsize, ntiles - grp * gsize), ngroups = (ntiles + gsize - 1) / gsize;
+    unsigned *cg = done + kTicketStride * grp, *ct = done + kTicketStride * kTicketGroups;
+    unsigned gticket = 0, tticket = 0;
+    // the window sums of D0, D1, D2 at the four outputs, one map at a time
     float ss[3][4];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -387,6 +419,12 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
                 if (!(i0[u] == kMR - 4 && q < 2)) L.d[i0[u] + q][jj[u]] = D[k][u][q];
         }
         __syncthreads();
+        if (k == 0 && loss && tid < 3) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < kLossWaves; ++w) t += L.red[tid][w];
+            __hip_atomic_store(&part[3 * tile + tid], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
         for (int u = 0; u < rounds(kBRowTasks); ++u) {
             const int t = tid + kLossNT * u;
@@ -399,13 +437,21 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
         }
         __syncthreads();
         if (outtask) ssim_col4<kBP>(&L.hb[ty0][tx], win, ss[k]);
+        if (k == 0 && loss && tid < 64) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);                  // the partials' stores have completed
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (tid == 0) gticket = __hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (k == 1 && loss && tid == 0 && gticket == (unsigned)(members - 1)) {
+            __hip_atomic_store(cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+            tticket = __hip_atomic_fetch_add(ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+        }
         if (k < 2) __syncthreads();                         // d and hb are rewritten next
     }
     const double inv_n = 1.0 / (3.0 * (double)plane);
     // 1 / (3 H W) rounded once (the products below round like the divisions they replace, to 1 ulp)
     const float inv_nf = (float)inv_n;
-    const int j = x0 + tx;
-    float l1 = 0.f, l2 = 0.f;
     if (outtask) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -413,53 +459,13 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
             if (i >= H || j >= W) continue;
             const float xo = L.s[0][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR], yo = L.s[1][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR];
             const float e = xo - yo;
-            l1 += fabsf(e);
-            l2 += e * e;
             const float dssim = fmaf(yo, ss[2][q], fmaf(2.0f * xo, ss[1][q], ss[0][q])) * inv_nf;
             const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
             dL[ch * plane + (size_t)i * W + j] = fmaf(w1, sg * inv_nf, fmaf(w2, 2.0f * e * inv_nf, -(ws * dssim)));
         }
     }
-    // the tile's partial sums, reduced in a fixed order
-    float v[3] = {f, l1, l2};
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        float s = v[k];
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
-        if ((tid & 63) == 0) L.red[k][tid >> 6] = s;
-    }
-    __syncthreads();
-    // The partials go out as device-scope stores (written through to the device's coherent level);
-    // once they have completed, the first wave takes a ticket.  The workgroup with the last ticket
-    // reads every partial back with device-scope loads.  Nothing else is published, so no cache
-    // write-back is needed on the way.
-    if (tid < 64) {
-        if (tid < 3) {
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < kLossWaves; ++w) t += L.red[tid][w];
-            __hip_atomic_store(&part[3 * tile + tid], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!loss) return;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);                      // the stores have completed
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (tid == 0) {
-            // tickets in two levels (eight groups of workgroups, each counter on its own 256-byte line,
-            // then the groups), so no single counter takes every workgroup's atomic
-            const int per = nblk / kSsimGroups, g = blockIdx.x % kSsimGroups;
-            const int members = min(per, ntiles - g * per), groups = (ntiles + per - 1) / per;
-            unsigned *cg = done + kSsimCountStride * g, *ct = done + kSsimCountStride * kSsimGroups;
-            bool last = false;
-            if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(members - 1)) {
-                __hip_atomic_store(cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
-                last = __hip_atomic_fetch_add(ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(groups - 1);
-            }
-            L.last = last;
-        }
-    }
     if (!loss) return;
+    if (tid == 0) L.last = tticket == (unsigned)ngroups;    // 0 unless this is a group's last tile
     __syncthreads();
     if (!L.last) return;
     // the last workgroup: every tile's partials, in tile order per thread, then a fixed tree
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
             for (int w = 0; w < kLossWaves; ++w) s[k] += L.dred[k][w];
         }
         loss[0] = (float)(w1d * s[1] * inv_n + w2d * s[2] * inv_n + wsd * (1.0 - s[0] * inv_n));
-        __hip_atomic_store(done + kSsimCountStride * kSsimGroups, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);      // ready for the next call
     }
 }
 
@@ -500,8 +506,8 @@ static SsimWin ssim_window() {
 
 static int ssim_tiles(int W, int H) { return ((W + kTW - 1) / kTW) * ((H + kTH - 1) / kTH) * 3; }
 
-// Workspace: the target's statistics T (3 planes of float2) | the tile partials | the counts of
-// finished tiles (zeroed by k_ssim_target, left at zero by every loss call).
+// Workspace: the target's statistics T (3 planes of float2) | the tile partials | the ticket counts
+// (zeroed by k_ssim_target, left at zero by every loss call).
 struct SsimWs {
     float2 *T;
     float *part;
@@ -522,7 +528,7 @@ static SsimWs ssim_ws(int W, int H, void *ws) {
 size_t ssim_workspace_bytes(int W, int H) {
     const size_t plane = (size_t)W * H;
     return align256(3 * plane * sizeof(float2)) + align256(3 * (size_t)ssim_tiles(W, H) * sizeof(float)) +
-           (kSsimGroups + 1) * kSsimCountStride * sizeof(unsigned);
+           (kTicketGroups + 1) * kTicketStride * sizeof(unsigned);
 }
 
 hipError_t launch_ssim_target(int W, int H, const float *y, void *ws_ptr, hipStream_t s) {
