@@ -490,6 +490,31 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
                           int32_t step, const int32_t *d_step, uint32_t flags, void *stream);
 
 /*
+ * gi_fit_step_sum_ssim -- gi_fit_step_sum with the pixel loss of gi_loss_ssim
+ *   (w1 mean|I - T| + w2 mean (I - T)^2 + ws (1 - SSIM); "Drawing with
+ *   Gaussians", 2D fitting; "FlashImgs", Training features / --loss) in place
+ *   of the L2 loss.  The SSIM gradient at a pixel needs the rendered image
+ *   around it, so the raster pass is the forward (finishing the sort as the
+ *   fused pass does), gi_loss_ssim with GI_SSIM_TARGET_PREPARED, and the
+ *   backward into the pair slots; the binning before and the Adam step with
+ *   the set-up for the next call after are gi_fit_step_sum's.  Every result
+ *   is bit-identical to the sequence gi_preprocess_bin_sort, gi_render_fwd,
+ *   gi_loss_ssim, gi_render_bwd (dparams = NULL), gi_adam_step_pairs.
+ *   b->loss_partials is not used (may be NULL); b->d_loss (or NULL) receives
+ *   the loss.  Flags, buffers and errors as gi_fit_step_sum, and:
+ *   w1, w2, ws      finite loss weights.
+ *   dL_dimage       device float [3][H][W] (scratch: dL/dI), 16-byte aligned,
+ *                   not the image or the target.
+ *   ssim_workspace  >= gi_loss_ssim_workspace_bytes(W, H) bytes, 256-byte
+ *                   aligned, holding b->target's statistics from
+ *                   gi_loss_ssim_target.
+ */
+gi_status gi_fit_step_sum_ssim(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
+                               float w1, float w2, float ws, float *dL_dimage, void *ssim_workspace,
+                               size_t ssim_workspace_bytes, int32_t step, const int32_t *d_step, uint32_t flags,
+                               void *stream);
+
+/*
  * Parameter forms ("GaussianImage", Overview and its training scripts: the
  * covariance as a Cholesky factor or as a rotation and two scales;
  * "FlashImgs", Library API: xy / scale / rot tensors, and rendering a trained

@@ -350,8 +350,17 @@ gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *reco
                                                   loss_partials, workspace, as_stream(stream)));
 }
 
-gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
-                          int32_t step, const int32_t *d_step, uint32_t flags, void *stream) {
+namespace {
+// The SSIM loss of gi_fit_step_sum_ssim (NULL: the L2 loss of gi_fit_step_sum).
+struct FitSsim {
+    float w1, w2, ws;
+    float *dL;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+gi_status fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
+                       int32_t step, const int32_t *d_step, uint32_t flags, void *stream, const FitSsim *ssim) {
     if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
     if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER | GI_FIT_NO_UPDATE |
                              GI_FIT_TRACK_MAX)) != 0u)
@@ -367,11 +376,18 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
                      b->bin_workspace, b->bin_workspace_bytes))
         return GI_ERR_INVALID_ARG;
     if ((flags & (GI_FIT_ORDER | GI_FIT_USE_ORDER)) && !b->tile_order) return GI_ERR_INVALID_ARG;
-    if (!b->target || !b->image || !aligned16(b->image) || !b->loss_partials || !b->bwd_workspace ||
+    if (!b->target || !b->image || !aligned16(b->image) || (!ssim && !b->loss_partials) || !b->bwd_workspace ||
         !aligned256(b->bwd_workspace))
         return GI_ERR_INVALID_ARG;
     const int W = desc->width, H = desc->height;
     if (b->bwd_workspace_bytes < gi::make_bwd_plan(W, H, b->capacity).bytes) return GI_ERR_INVALID_ARG;
+    if (ssim) {
+        if (!std::isfinite(ssim->w1) || !std::isfinite(ssim->w2) || !std::isfinite(ssim->ws)) return GI_ERR_INVALID_ARG;
+        if (!ssim->dL || !aligned16(ssim->dL) || ssim->dL == b->image || ssim->dL == b->target ||
+            !ssim->workspace || !aligned256(ssim->workspace) ||
+            ssim->workspace_bytes < gi::ssim_workspace_bytes(W, H))
+            return GI_ERR_INVALID_ARG;
+    }
     if (update && n > 0 && (!b->m || !b->v || !aligned16(b->m) || !aligned16(b->v))) return GI_ERR_INVALID_ARG;
     const gi::BinPlan plan = gi::make_bin_plan((int)n, W, H, b->capacity);
     const gi::BinHist hist = gi::bin_hist(plan, b->bin_workspace);
@@ -392,17 +408,43 @@ gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *
                                 b->bin_workspace, s, true, bucket, (flags & GI_FIT_TRACK_MAX) ? b->d_num + 1 : nullptr);
     if (e == hipSuccess) {
         const gi::BucketList bl = gi::bin_bucket_list(plan, b->bin_workspace, b->keys, b->vals, b->ranges);
-        e = gi::launch_render_sum_fused(W, H, b->records, b->pixbox, b->offsets, b->ranges, order, b->vals,
-                                        b->capacity, b->image, b->target, nullptr, b->loss_partials, b->bwd_workspace,
-                                        s, bucket ? &bl : nullptr);
+        if (!ssim) {
+            e = gi::launch_render_sum_fused(W, H, b->records, b->pixbox, b->offsets, b->ranges, order, b->vals,
+                                            b->capacity, b->image, b->target, nullptr, b->loss_partials,
+                                            b->bwd_workspace, s, bucket ? &bl : nullptr);
+        } else {
+            // the SSIM gradient needs the whole image: forward (finishing the sort), the loss, backward
+            e = gi::launch_render_sum_fwd(W, H, b->records, b->pixbox, b->ranges, order, b->vals, b->image, nullptr,
+                                          nullptr, nullptr, s, bucket ? &bl : nullptr);
+            if (e == hipSuccess)
+                e = gi::launch_loss_ssim(W, H, b->image, b->target, ssim->w1, ssim->w2, ssim->ws, ssim->dL, b->d_loss,
+                                         ssim->workspace, true, s);
+            if (e == hipSuccess)
+                e = gi::launch_render_sum_bwd(W, H, b->records, b->pixbox, b->offsets, b->ranges, order, b->vals,
+                                              b->capacity, ssim->dL, b->bwd_workspace, nullptr, 0, nullptr, s);
+        }
     }
     if (e == hipSuccess && bucket && (flags & GI_FIT_ORDER)) e = gi::launch_tile_order(plan, b->ranges, b->tile_order, s);
     if (e == hipSuccess && update)
         e = gi::launch_adam_preprocess((int)n, W, H, b->offsets, b->capacity, b->bwd_workspace, b->params, b->m, b->v,
                                        gi::make_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, step, d_step),
-                                       b->records, b->pixbox, b->counts, groups, b->ranges, hist, b->loss_partials,
-                                       3ll * W * H, b->d_loss, s);
+                                       b->records, b->pixbox, b->counts, groups, b->ranges, hist,
+                                       ssim ? nullptr : b->loss_partials, 3ll * W * H, ssim ? nullptr : b->d_loss, s);
     return hip_status(e);
+}
+}  // namespace
+
+gi_status gi_fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
+                          int32_t step, const int32_t *d_step, uint32_t flags, void *stream) {
+    return fit_step_sum(desc, n, b, hp, step, d_step, flags, stream, nullptr);
+}
+
+gi_status gi_fit_step_sum_ssim(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
+                               float w1, float w2, float ws, float *dL_dimage, void *ssim_workspace,
+                               size_t ssim_workspace_bytes, int32_t step, const int32_t *d_step, uint32_t flags,
+                               void *stream) {
+    const FitSsim f{w1, w2, ws, dL_dimage, ssim_workspace, ssim_workspace_bytes};
+    return fit_step_sum(desc, n, b, hp, step, d_step, flags, stream, &f);
 }
 
 size_t gi_loss_workspace_bytes(int64_t count) { return count < 1 ? 0 : gi::loss_workspace_bytes(count); }

@@ -109,6 +109,9 @@ def load():
                                      P], i32),
         "gi_fit_step_sum": ([D, i64, ctypes.POINTER(gi_fit_buffers), ctypes.POINTER(gi_adam_hparams), i32, P,
                              ctypes.c_uint32, P], i32),
+        "gi_fit_step_sum_ssim": ([D, i64, ctypes.POINTER(gi_fit_buffers), ctypes.POINTER(gi_adam_hparams),
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, sz, i32, P, ctypes.c_uint32,
+                                  P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -453,3 +456,12 @@ def gi_fit_step_sum(d, n, buffers: gi_fit_buffers, hparams: gi_adam_hparams, ste
     """One sum-mode training step (binning, fused raster, Adam + set-up of the next binning)."""
     _check(load().gi_fit_step_sum(ctypes.byref(d), int(n), ctypes.byref(buffers), ctypes.byref(hparams), int(step),
                                   _ptr(d_step), int(flags), _stream(stream)), "gi_fit_step_sum")
+
+
+def gi_fit_step_sum_ssim(d, n, buffers: gi_fit_buffers, hparams: gi_adam_hparams, w1, w2, ws, dL_dimage,
+                         ssim_workspace, step, d_step=None, flags=0, stream=None):
+    """gi_fit_step_sum with the SSIM pixel loss (forward, gi_loss_ssim, backward in the raster pass)."""
+    _check(load().gi_fit_step_sum_ssim(ctypes.byref(d), int(n), ctypes.byref(buffers), ctypes.byref(hparams),
+                                       float(w1), float(w2), float(ws), _ptr(dL_dimage), _ptr(ssim_workspace),
+                                       int(ssim_workspace.numel()), int(step), _ptr(d_step), int(flags),
+                                       _stream(stream)), "gi_fit_step_sum_ssim")

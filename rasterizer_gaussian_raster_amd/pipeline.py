@@ -7,7 +7,9 @@ the C ABI (through :mod:`.gi`):
            gi_preprocess_bin_sort -> gi_render_fwd)
   fit (sum mode)   : gi_fit_step_sum, one call per step: binning -> the fused per-tile forward, L2
                      gradient and backward -> Adam with the gathered gradient, which also sets up the
-                     updated parameters for the next step's binning (and reduces the loss)
+                     updated parameters for the next step's binning (and reduces the loss); with the
+                     SSIM loss gi_fit_step_sum_ssim, whose raster pass is forward -> gi_loss_ssim ->
+                     backward
   fit (alpha mode) : render -> gi_loss_l2 -> gi_render_bwd -> gi_adam_step (gradients cleared)
 
 Fitter.capture() records the sum-mode step as HIP graphs (torch.cuda.CUDAGraph over the same
@@ -424,7 +426,8 @@ class Fitter:
 
     def _sum_step(self, order, d_step=None):
         """The sum-mode step: one gi_fit_step_sum call (binning, fused raster, Adam + the set-up of the
-        updated parameters for the next call).  d_step: device step counter, advanced here (graph mode)."""
+        updated parameters for the next call), or gi_fit_step_sum_ssim with the SSIM loss (the raster
+        pass is then forward, loss, backward).  d_step: device step counter, advanced here (graph mode)."""
         r = self.raster
         if self._fb is None:
             self._fb = gi.fit_buffers(self.params, self.m, self.v, self.target, r.image, r.loss_partials, self.loss,
@@ -441,7 +444,11 @@ class Fitter:
                 r.has_order = True
         if d_step is not None:
             d_step.add_(1)
-        gi.gi_fit_step_sum(r.desc, self.n, self._fb, self._hp, self.step_count + 1, d_step=d_step, flags=flags)
+        if self.loss_w is None:
+            gi.gi_fit_step_sum(r.desc, self.n, self._fb, self._hp, self.step_count + 1, d_step=d_step, flags=flags)
+        else:
+            gi.gi_fit_step_sum_ssim(r.desc, self.n, self._fb, self._hp, *self.loss_w, self.dL, self.ssim_ws,
+                                    self.step_count + 1, d_step=d_step, flags=flags)
         self.prepared = True
 
     def capture(self, warmup=2):
@@ -485,7 +492,7 @@ class Fitter:
             self.step_count += 1
             return
         r = self.raster
-        if self.logit is None and self.loss_w is None:
+        if self.logit is None:
             self._sum_step(self.step_count % ORDER_EVERY == 0)
             self.step_count += 1
             return

@@ -143,3 +143,24 @@ def test_ssim_loss_pointer_optional_and_unaligned_planes():
     torch.cuda.synchronize()
     assert float(lu.item()) == losses[0]
     np.testing.assert_array_equal(dLu.cpu().numpy().view(np.uint32), grads[0].view(np.uint32))
+
+
+def test_ssim_fit_step_matches_separate_calls():
+    """gi_fit_step_sum_ssim (Fitter.step with the SSIM loss: binning, forward, loss, backward into the
+    pair slots, Adam with the set-up of the next binning) against the separate calls (binning,
+    forward, gi_loss_ssim, backward with the gather, gi_adam_step): the same bits every step."""
+    require_gpu()
+    from rasterizer_gaussian_raster_amd.pipeline import Fitter
+    p = synth.random_case(321, 96, 80, 600, sigma=(0.5, 8.0))
+    tgt = np.random.default_rng(322).uniform(0, 1, (3, 80, 96)).astype(np.float32)
+    w = (0.8, 0.1, 0.2)
+    a = Fitter(dev(tgt), dev(p), loss=w)
+    b = Fitter(dev(tgt), dev(p), loss=w)
+    for k in range(20):
+        a.step()
+        b.step_separate()
+        if k in (0, 19):
+            torch.cuda.synchronize()
+            for x, y in [(a.params, b.params), (a.m, b.m), (a.v, b.v), (a.loss, b.loss), (a.dL, b.dL)]:
+                np.testing.assert_array_equal(x.cpu().numpy().view(np.uint32), y.cpu().numpy().view(np.uint32))
+    print(f"ssim fit step: loss {a.loss.item():.6e} after 20 steps")
