@@ -413,7 +413,8 @@ def bench_ssim(args, w, target, params, dev):
         "final_loss": final_loss,
         "kernels_us": {"loss_ssim": st, "loss_ssim_target_unprepared": st_full},
         "roofline": {"bound": "alu", "kernel": "k_ssim_loss", "achieved": round(tfs, 2), "peak": PEAK_FP32,
-                     "unit": "TFLOP/s", "frac": round(tfs / PEAK_FP32, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tfs / PEAK_FP32, 4),
+                     "traffic": load_traffic("k_ssim.hip", "k_ssim_loss"),
                      "avg_launch_us": round(ssim_s * 1e6, 2), "flop_per_entry": 315,
                      "hbm": {"achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                              "frac": round(gbs / PEAK_HBM, 4), "bytes_per_entry": 20}},
