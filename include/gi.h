@@ -95,7 +95,7 @@ int64_t gi_num_tiles(const gi_desc *desc);
  *   Reading of "GaussianImage" (8 parameters, Cholesky covariance) and the
  *   fvdb config's eps_2d (pixel padding of the screen-space box).
  *
- *   n        number of Gaussians, 0 <= n < 2^31.
+ *   n        number of Gaussians, 0 <= n < 2^27 (every call that takes n).
  *   params   device float [n][8], as above.
  *   logit    device float [n] (alpha mode) or NULL (sum mode).
  *   records  device float [n][8] out: mux, muy, a, b, c, cr, cg, cb

@@ -11,6 +11,9 @@
 namespace {
 
 constexpr int kMaxDim = 32768;
+// Gaussians per call: the update kernels index up to 8 lanes and 4 float4 per Gaussian in 32-bit
+// arithmetic, which stays in range below 2^27 Gaussians.
+constexpr int64_t kMaxGaussians = 1ll << 27;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -51,7 +54,7 @@ int64_t gi_num_tiles(const gi_desc *desc) {
 namespace {
 bool preprocess_args_ok(const gi_desc *desc, int64_t n, const float *params, const float *logit,
                         const float *records, const float *opacity, const uint16_t *pixbox, const uint32_t *counts) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return false;
+    if (!desc_ok(desc) || n < 0 || n >= kMaxGaussians) return false;
     const bool alpha = desc->mode == GI_MODE_ALPHA;
     if (n > 0) {
         if (!params || !records || !pixbox || !counts) return false;
@@ -64,7 +67,7 @@ bool preprocess_args_ok(const gi_desc *desc, int64_t n, const float *params, con
 bool bin_args_ok(const gi_desc *desc, int64_t n, const uint16_t *pixbox, const uint32_t *counts,
                  const uint32_t *offsets, const uint32_t *keys, const uint32_t *vals, const uint32_t *ranges,
                  int64_t capacity, const uint32_t *d_num, const void *workspace, size_t workspace_bytes) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return false;
+    if (!desc_ok(desc) || n < 0 || n >= kMaxGaussians || capacity < 0 || capacity >= (1ll << 31)) return false;
     if (!offsets || !ranges || !d_num || !workspace || !aligned256(workspace)) return false;
     if (n > 0 && (!pixbox || !counts)) return false;
     if (capacity > 0 && (!keys || !vals)) return false;
@@ -92,7 +95,7 @@ gi_status gi_preprocess(const gi_desc *desc, int64_t n, const float *params, con
 }
 
 size_t gi_bin_sort_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return 0;
+    if (!desc_ok(desc) || n < 0 || n >= kMaxGaussians || capacity < 0 || capacity >= (1ll << 31)) return 0;
     return gi::make_bin_plan((int)n, desc->width, desc->height, capacity).bytes;
 }
 
@@ -257,7 +260,7 @@ gi_status gi_render_fwd(const gi_desc *desc, int64_t n, const float *records, co
                         const uint16_t *pixbox, const uint32_t *ranges, const uint32_t *tile_order,
                         const uint32_t *vals, const float *background, float *image, float *t_final, uint32_t *last,
                         void *stream) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!desc_ok(desc) || n < 0 || n >= kMaxGaussians) return GI_ERR_INVALID_ARG;
     if (!ranges || !vals || !image || !aligned16(image)) return GI_ERR_INVALID_ARG;
     if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
@@ -275,7 +278,7 @@ gi_status gi_render_fwd_l2(const gi_desc *desc, int64_t n, const float *records,
                            const uint32_t *ranges, const uint32_t *tile_order, const uint32_t *vals,
                            const float *target, float *image, float *dL_dimage, float *loss_partials,
                            void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians) return GI_ERR_INVALID_ARG;
     if (!ranges || !vals || !image || !target || !dL_dimage || !loss_partials || !aligned16(image))
         return GI_ERR_INVALID_ARG;
     if (n > 0 && (!records || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
@@ -289,7 +292,7 @@ gi_status gi_loss_reduce(int64_t nparts, const float *loss_partials, int64_t cou
 }
 
 size_t gi_render_bwd_workspace_bytes(const gi_desc *desc, int64_t n, int64_t capacity) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31)) return 0;
+    if (!desc_ok(desc) || n < 0 || n >= kMaxGaussians || capacity < 0 || capacity >= (1ll << 31)) return 0;
     if (desc->mode == GI_MODE_ALPHA) return gi::alpha_bwd_workspace_bytes(desc->width, desc->height, n, capacity);
     return gi::make_bwd_plan(desc->width, desc->height, capacity).bytes;
 }
@@ -301,7 +304,7 @@ gi_status gi_render_bwd(const gi_desc *desc, int64_t n, const float *records, co
                         const float *dL_dimage, float *dparams, float *dlogit, float *dbackground,
                         const float *loss_partials, int64_t loss_count, float *d_loss,
                         void *workspace, size_t workspace_bytes, void *stream) {
-    if (!desc_ok(desc) || n < 0 || n >= (1ll << 31) || capacity < 0 || capacity >= (1ll << 31))
+    if (!desc_ok(desc) || n < 0 || n >= kMaxGaussians || capacity < 0 || capacity >= (1ll << 31))
         return GI_ERR_INVALID_ARG;
     if (d_loss && (desc->mode != GI_MODE_SUM || !loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;
     if (!offsets || !ranges || !vals || !dL_dimage || !workspace || !aligned256(workspace))
@@ -337,7 +340,7 @@ gi_status gi_render_fwd_bwd_l2(const gi_desc *desc, int64_t n, const float *reco
                                const uint32_t *vals, int64_t capacity, const float *target, float *image,
                                float *dL_dimage, float *loss_partials, void *workspace, size_t workspace_bytes,
                                void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians || capacity < 0 ||
         capacity >= (1ll << 31))
         return GI_ERR_INVALID_ARG;
     if (!offsets || !ranges || !vals || !target || !image || !loss_partials || !aligned16(image) || !workspace ||
@@ -361,7 +364,7 @@ struct FitSsim {
 
 gi_status fit_step_sum(const gi_desc *desc, int64_t n, const gi_fit_buffers *b, const gi_adam_hparams *hp,
                        int32_t step, const int32_t *d_step, uint32_t flags, void *stream, const FitSsim *ssim) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || !b || n < 0 || n >= kMaxGaussians) return GI_ERR_INVALID_ARG;
     if ((flags & ~(uint32_t)(GI_FIT_PREPARED | GI_FIT_ORDER | GI_FIT_USE_ORDER | GI_FIT_NO_UPDATE |
                              GI_FIT_TRACK_MAX)) != 0u)
         return GI_ERR_INVALID_ARG;
@@ -462,7 +465,7 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
                              const float *lr, double beta1, double beta2, double eps, int32_t step,
                              const int32_t *d_step, const float *loss_partials, int64_t loss_count, float *d_loss,
                              void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians || capacity < 0 ||
         capacity >= (1ll << 31) || (!d_step && step < 1) || !lr)
         return GI_ERR_INVALID_ARG;
     if (d_loss && (!loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;
@@ -516,7 +519,7 @@ gi_status gi_params_to_cholesky_grad(int32_t kind, int64_t n, const float *param
 gi_status gi_grad_gather(const gi_desc *desc, int32_t kind, int64_t n, const float *params, float fx, float fy,
                          const float *records, const uint32_t *offsets, int64_t capacity, const void *workspace,
                          size_t workspace_bytes, float *dparams, void *stream) {
-    if (!desc_ok(desc) || (kind != GI_PARAMS_CHOLESKY && kind != GI_PARAMS_RS) || n < 0 || n >= (1ll << 31) ||
+    if (!desc_ok(desc) || (kind != GI_PARAMS_CHOLESKY && kind != GI_PARAMS_RS) || n < 0 || n >= kMaxGaussians ||
         capacity < 0 || capacity >= (1ll << 31))
         return GI_ERR_INVALID_ARG;
     if (!(fx > 0.0f) || !(fy > 0.0f) || !std::isfinite(fx) || !std::isfinite(fy)) return GI_ERR_INVALID_ARG;
@@ -560,7 +563,7 @@ gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *
                                 const float *lr, double beta1, double beta2, double eps, int32_t step,
                                 const float *loss_partials, int64_t loss_count, float *d_loss, float *chol_out,
                                 void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians || capacity < 0 ||
         capacity >= (1ll << 31) || step < 1 || !lr)
         return GI_ERR_INVALID_ARG;
     if (d_loss && (!loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;
@@ -576,7 +579,7 @@ gi_status gi_adam_step_pairs_rs(const gi_desc *desc, int64_t n, const uint32_t *
 
 gi_status gi_merge_pairs(int64_t n_pairs, const int32_t *pairs, int64_t n, const float *params, float *out,
                          void *stream) {
-    if (n_pairs < 0 || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (n_pairs < 0 || n < 0 || n >= kMaxGaussians) return GI_ERR_INVALID_ARG;
     if (n_pairs > 0 && (!pairs || !params || !out || !aligned16(params) || !aligned16(out) ||
                         (reinterpret_cast<uintptr_t>(pairs) & 7u) != 0 || out == params))
         return GI_ERR_INVALID_ARG;
@@ -670,14 +673,14 @@ gi_status gi_merge_to(const gi_desc *desc, int64_t n, const float *params, int64
 }
 
 size_t gi_adc_workspace_bytes(const gi_desc *desc, int64_t n) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return 0;
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians) return 0;
     return gi::adc_workspace_bytes(desc->width, desc->height, n);
 }
 
 gi_status gi_adc(const gi_desc *desc, int64_t n, float *params, float *m, float *v, const float *image,
                  const float *target, float s0, int32_t *flags, uint32_t *d_moved, void *workspace,
                  size_t workspace_bytes, void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians) return GI_ERR_INVALID_ARG;
     if ((int64_t)desc->width * desc->height >= (1ll << 31)) return GI_ERR_INVALID_ARG;
     if (!std::isfinite(s0) || !image || !target || !workspace || !aligned256(workspace)) return GI_ERR_INVALID_ARG;
     if (workspace_bytes < gi::adc_workspace_bytes(desc->width, desc->height, n)) return GI_ERR_INVALID_ARG;
@@ -691,7 +694,7 @@ gi_status gi_render_bwd_absgrad(const gi_desc *desc, int64_t n, const float *rec
                                 const uint32_t *offsets, const uint32_t *ranges, const uint32_t *tile_order,
                                 const uint32_t *vals, int64_t capacity, const float *dL_dimage, float *dparams,
                                 float *dabs, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+    if (!desc_ok(desc) || desc->mode != GI_MODE_SUM || n < 0 || n >= kMaxGaussians || capacity < 0 ||
         capacity >= (1ll << 31))
         return GI_ERR_INVALID_ARG;
     if (!offsets || !ranges || !vals || !dL_dimage || !workspace || !aligned256(workspace))
@@ -716,7 +719,7 @@ gi_status gi_render_fwd_alpha_l2(const gi_desc *desc, int64_t n, const float *re
                                  const uint32_t *vals, const float *background, const float *target, float *image,
                                  float *t_final, uint32_t *last, float *dL_dimage, float *loss_partials,
                                  void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_ALPHA || n < 0 || n >= (1ll << 31)) return GI_ERR_INVALID_ARG;
+    if (!desc_ok(desc) || desc->mode != GI_MODE_ALPHA || n < 0 || n >= kMaxGaussians) return GI_ERR_INVALID_ARG;
     if (!ranges || !vals || !background || !target || !image || !t_final || !last || !dL_dimage || !loss_partials)
         return GI_ERR_INVALID_ARG;
     if (n > 0 && (!records || !opacity || !pixbox || !aligned16(records))) return GI_ERR_INVALID_ARG;
@@ -732,7 +735,7 @@ gi_status gi_adam_step_pairs_alpha(const gi_desc *desc, int64_t n, const uint32_
                                    float *background, float *m_bg, float *v_bg, float lr_bg, double beta1,
                                    double beta2, double eps, int32_t step, const float *loss_partials,
                                    int64_t loss_count, float *d_loss, void *stream) {
-    if (!desc_ok(desc) || desc->mode != GI_MODE_ALPHA || n < 0 || n >= (1ll << 31) || capacity < 0 ||
+    if (!desc_ok(desc) || desc->mode != GI_MODE_ALPHA || n < 0 || n >= kMaxGaussians || capacity < 0 ||
         capacity >= (1ll << 31) || step < 1 || !lr)
         return GI_ERR_INVALID_ARG;
     if (d_loss && (!loss_partials || loss_count < 1)) return GI_ERR_INVALID_ARG;

@@ -83,6 +83,15 @@ def test_host_only_calls(lib):
                              None) == gi.GI_ERR_INVALID_ARG
     assert L.gi_fit_step_sum(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp), 0, None, 0,
                              None) == gi.GI_ERR_INVALID_ARG
+    # the SSIM step: as gi_fit_step_sum, plus its own buffers and weights
+    assert L.gi_fit_step_sum_ssim(ctypes.byref(d), 10, None, ctypes.byref(hp), 0.8, 0.0, 0.2, None, None, 0, 1,
+                                  None, 0, None) == gi.GI_ERR_INVALID_ARG
+    assert L.gi_fit_step_sum_ssim(ctypes.byref(d), 0, ctypes.byref(fb), ctypes.byref(hp), float("nan"), 0.0, 0.2,
+                                  None, None, 0, 1, None, 0, None) == gi.GI_ERR_INVALID_ARG
+    # Gaussian counts of 2^27 and more are refused before any device work
+    assert gi.gi_bin_sort_workspace_bytes(d, 1 << 27, 10) == 0
+    st = L.gi_preprocess(ctypes.byref(d), 1 << 27, None, None, None, None, None, None, None)
+    assert st == gi.GI_ERR_INVALID_ARG
     assert gi.status_string(gi.GI_ERR_CAPACITY) == "GI_ERR_CAPACITY"
 
 
