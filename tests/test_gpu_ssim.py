@@ -43,7 +43,8 @@ def _check(x, y, w, prepared=False):
 
 
 @pytest.mark.parametrize("W,H,w", [(64, 64, (0.8, 0.0, 0.2)), (100, 37, (0.0, 1.0, 0.2)), (17, 33, (0.7, 0.1, 0.3)),
-                                   (5, 3, (0.8, 0.0, 0.2)), (1, 1, (0.5, 0.5, 0.5)), (300, 200, (0.8, 0.0, 0.2))])
+                                   (5, 3, (0.8, 0.0, 0.2)), (1, 1, (0.5, 0.5, 0.5)), (300, 200, (0.8, 0.0, 0.2)),
+                                   (131, 97, (0.8, 0.1, 0.2))])
 def test_ssim_random(W, H, w):
     require_gpu()
     rng = np.random.default_rng(W * 1000 + H)
