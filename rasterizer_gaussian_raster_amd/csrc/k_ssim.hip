@@ -143,9 +143,9 @@ __global__ __launch_bounds__(256) void k_ssim_target(int W, int H, const float *
 //               in groups of four, the last two unused);
 //   D           the statistics region.
 // LDS holds the staged maps, ONE map's row pass at a time (x, then x^2, then x y; later D0, D1, D2
-// in turn) and one of D0..D2, about 51 KB.  Every row stride is an odd multiple of 4 floats, and the tasks that
-// read or write float4 runs give a wave's lanes consecutive rows of one column group, so each 8
-// lanes' float4 accesses cover the 32 banks once.
+// in turn) and one of D0..D2, about 51 KB.  Every row stride is an odd multiple of 4 floats, and
+// the tasks that read or write float4 runs give a wave's lanes consecutive rows of one column group,
+// so each 8 lanes' float4 accesses cover the 32 banks once.
 constexpr int kLossNT = 512;                                // threads per workgroup (8 waves)
 constexpr int kLossWaves = kLossNT / 64;
 constexpr int kTW = 48, kTH = 32;                           // output tile
@@ -304,12 +304,10 @@ __device__ __forceinline__ void ssim_loss_map(SsimLossLds &L, const SsimWin &win
 
 // three workgroups (24 waves) per CU: at most 80 VGPRs
 template <bool VEC>
-__global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) void k_ssim_loss(int W, int H, const float *__restrict__ x,
-                                                       const float *__restrict__ y, const float2 *__restrict__ T,
-                                                       SsimWin win, float w1, float w2, float ws,
-                                                       float *__restrict__ dL, float *__restrict__ part, int ntiles,
-                                                       int nblk, double w1d, double w2d, double wsd,
-                                                       float *__restrict__ loss, unsigned *__restrict__ done) {
+__global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) void k_ssim_loss(
+    int W, int H, const float *__restrict__ x, const float *__restrict__ y, const float2 *__restrict__ T, SsimWin win,
+    float w1, float w2, float ws, float *__restrict__ dL, float *__restrict__ part, int ntiles, int nblk, double w1d,
+    double w2d, double wsd, float *__restrict__ loss, unsigned *__restrict__ done) {
     __shared__ __align__(16) SsimLossLds L;
     const int tile = xcd_remap(blockIdx.x, nblk);           // an XCD takes neighbouring tiles
     if (tile >= ntiles) return;
@@ -383,7 +381,8 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (y0 + ty0 + q >= H || j >= W) continue;
-                const float e = L.s[0][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR] - L.s[1][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR];
+                const int r = ty0 + q + 2 * kSsimR, c = tx + 2 * kSsimR;
+                const float e = L.s[0][r][c] - L.s[1][r][c];
                 l1 += fabsf(e);
                 l2 += e * e;
             }
@@ -457,7 +456,8 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
         for (int q = 0; q < 4; ++q) {
             const int i = y0 + ty0 + q;
             if (i >= H || j >= W) continue;
-            const float xo = L.s[0][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR], yo = L.s[1][ty0 + q + 2 * kSsimR][tx + 2 * kSsimR];
+            const int r = ty0 + q + 2 * kSsimR, c = tx + 2 * kSsimR;
+            const float xo = L.s[0][r][c], yo = L.s[1][r][c];
             const float e = xo - yo;
             const float dssim = fmaf(yo, ss[2][q], fmaf(2.0f * xo, ss[1][q], ss[0][q])) * inv_nf;
             const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
@@ -517,7 +517,8 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 static SsimWs ssim_ws(int W, int H, void *ws) {
     const size_t plane = (size_t)W * H;
     char *b = static_cast<char *>(ws);
-    const size_t tb = align256(3 * plane * sizeof(float2)), pb = align256(3 * (size_t)ssim_tiles(W, H) * sizeof(float));
+    const size_t tb = align256(3 * plane * sizeof(float2));
+    const size_t pb = align256(3 * (size_t)ssim_tiles(W, H) * sizeof(float));
     SsimWs w;
     w.T = reinterpret_cast<float2 *>(b);
     w.part = reinterpret_cast<float *>(b + tb);
@@ -549,8 +550,8 @@ hipError_t launch_loss_ssim(int W, int H, const float *x, const float *y, float 
     const int ntiles = ssim_tiles(W, H), nblk = (ntiles + 7) & ~7;
     const bool vec = W % 4 == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
     if (vec)
-        k_ssim_loss<true><<<nblk, kLossNT, 0, s>>>(W, H, x, y, w.T, win, w1, w2, ws, dL, w.part, ntiles, nblk, (double)w1,
-                                               (double)w2, (double)ws, loss, w.done);
+        k_ssim_loss<true><<<nblk, kLossNT, 0, s>>>(W, H, x, y, w.T, win, w1, w2, ws, dL, w.part, ntiles, nblk,
+                                                   (double)w1, (double)w2, (double)ws, loss, w.done);
     else
         k_ssim_loss<false><<<nblk, kLossNT, 0, s>>>(W, H, x, y, w.T, win, w1, w2, ws, dL, w.part, ntiles, nblk,
                                                 (double)w1, (double)w2, (double)ws, loss, w.done);
