@@ -146,14 +146,21 @@ def test_ssim_loss_pointer_optional_and_unaligned_planes():
     np.testing.assert_array_equal(dLu.cpu().numpy().view(np.uint32), grads[0].view(np.uint32))
 
 
-def test_ssim_fit_step_matches_separate_calls():
+@pytest.mark.parametrize("case", ["small", "kodak_768x512_50k"])
+def test_ssim_fit_step_matches_separate_calls(case):
     """gi_fit_step_sum_ssim (Fitter.step with the SSIM loss: binning, forward, loss, backward into the
     pair slots, Adam with the set-up of the next binning) against the separate calls (binning,
-    forward, gi_loss_ssim, backward with the gather, gi_adam_step): the same bits every step."""
+    forward, gi_loss_ssim, backward with the gather, gi_adam_step): the same bits every step.  At
+    768x512 (more than 256 tiles) the forward finishes the sort per tile, and the 20 steps cross a
+    tile-order refresh."""
     require_gpu()
     from rasterizer_gaussian_raster_amd.pipeline import Fitter
-    p = synth.random_case(321, 96, 80, 600, sigma=(0.5, 8.0))
-    tgt = np.random.default_rng(322).uniform(0, 1, (3, 80, 96)).astype(np.float32)
+    if case == "small":
+        p = synth.random_case(321, 96, 80, 600, sigma=(0.5, 8.0))
+        tgt = np.random.default_rng(322).uniform(0, 1, (3, 80, 96)).astype(np.float32)
+    else:
+        wl = synth.make_workload(case)
+        p, tgt = wl["params"], wl["target"]
     w = (0.8, 0.1, 0.2)
     a = Fitter(dev(tgt), dev(p), loss=w)
     b = Fitter(dev(tgt), dev(p), loss=w)
