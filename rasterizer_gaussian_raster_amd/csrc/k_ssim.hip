@@ -46,6 +46,17 @@ __device__ __forceinline__ void lds_run14(const float *p, float (&v)[14]) {
     v[12] = d.x; v[13] = d.y;
 }
 
+// 18 consecutive floats of an LDS row from a 16-byte aligned start.
+__device__ __forceinline__ void lds_run18(const float *p, float (&v)[18]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 a = *reinterpret_cast<const float4 *>(p + 4 * k);
+        v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+    }
+    const float2 d = *reinterpret_cast<const float2 *>(p + 16);
+    v[16] = d.x; v[17] = d.y;
+}
+
 // The window over 14 consecutive inputs: four adjacent outputs (taps in a fixed order).
 __device__ __forceinline__ float4 win4(const float (&v)[14], const SsimWin &w) {
     float o[4];
@@ -156,19 +167,21 @@ constexpr int kSV = (kTW + 24) / 4;                         // float4 loads per 
 constexpr int kSN4 = kSR * kSV;                             // 936 per map
 constexpr int kMR = kTH + 2 * kSsimR;                       // 42 statistics rows
 constexpr int kMC = kTW + 2 * kSsimR;                       // 58 statistics columns
-constexpr int kMG = (kMC + 3) / 4;                          // 15 row-pass column groups
-constexpr int kHP = 4 * kMG;                                // 60: row-pass stride (28 mod 32)
-constexpr int kRowTasks = kSR * kMG;                        // 780
-constexpr int kColGroups = (kMR + 3) / 4;                   // 11 (the last one starts at row 38)
-constexpr int kColTasks = kMC * kColGroups;                 // 638
+constexpr int kMG = (kMC + 7) / 8;                          // 8 row-pass column groups of 8 outputs
+constexpr int kHP = 68;                                     // row-pass stride (4 mod 32; >= 8 kMG)
+constexpr int kRowTasks = kSR * kMG;                        // 416: one round
+constexpr int kColRows = 6;                                 // outputs per column task
+constexpr int kColGroups = kMR / kColRows;                  // 7
+constexpr int kColTasks = kMC * kColGroups;                 // 406: one round
 constexpr int kDP = 60;                                     // D stride (28 mod 32)
 constexpr int kBG = kTW / 4;                                // 12 D row-pass column groups
 constexpr int kBRowTasks = kMR * kBG;                       // 504
 constexpr int kBP = 52;                                     // D row-pass stride (20 mod 32)
 constexpr int kOutTasks = kTW * (kTH / 4);                  // 384 tasks of four outputs
 constexpr int rounds(int n) { return (n + kLossNT - 1) / kLossNT; }
-static_assert(kSP >= kSC && kDP >= kMC && kBP >= kTW, "strides");
-static_assert(4 * (kMG - 1) + 14 <= kSP + 2 && 4 * (kBG - 1) + 14 <= kMC, "row-pass reads");
+static_assert(kSP >= kSC && kHP >= 8 * kMG && kDP >= kMC && kBP >= kTW, "strides");
+static_assert(8 * (kMG - 1) + 18 <= kSP + 6 && 4 * (kBG - 1) + 14 <= kMC, "row-pass reads");
+static_assert(kColGroups * kColRows == kMR && kRowTasks <= kLossNT && kColTasks <= kLossNT, "one round");
 
 struct SsimLossLds {
     alignas(16) float s[2][kSR][kSP];                       // x, y staged (kept to the end)
@@ -181,8 +194,8 @@ struct SsimLossLds {
     double dred[3][kLossWaves];
     int last;
 };
-// the row pass's last column group reads two floats past the end of its row (for the two unused
-// outputs): the next row's, or for the last row of y the first two of d, which follows s
+// the row pass's last column group reads six floats past the end of its row (for the six unused
+// outputs): the next row's, or for the last row of y the first six of d, which follows s
 static_assert(offsetof(SsimLossLds, d) == sizeof(float) * 2 * kSR * kSP, "d follows s");
 
 // Stages x and y (one channel each) over the staged region into s (zero outside the image), in two
@@ -243,41 +256,49 @@ __device__ __forceinline__ void ssim_stage_store(const float4 (&vx)[kStageRounds
 }
 
 // Row pass task t of map MAP (0: x, 1: x^2, 2: x y): staged row t % 52, statistics columns
-// 4 (t / 52) .. + 3.
+// 8 (t / 52) .. + 7 from 18 consecutive staged values.
 template <int MAP>
 __device__ __forceinline__ void ssim_loss_rows(SsimLossLds &L, int t, const SsimWin &win) {
-    const int g = t / kSR, r = t - g * kSR, c0 = 4 * g;
-    float v[14];
-    lds_run14(&L.s[0][r][c0], v);
+    const int g = t / kSR, r = t - g * kSR, c0 = 8 * g;
+    float v[18];
+    lds_run18(&L.s[0][r][c0], v);
     if (MAP == 1) {
 #pragma unroll
-        for (int b = 0; b < 14; ++b) v[b] = v[b] * v[b];
+        for (int b = 0; b < 18; ++b) v[b] = v[b] * v[b];
     } else if (MAP == 2) {
-        float w[14];
-        lds_run14(&L.s[1][r][c0], w);
+        float w[18];
+        lds_run18(&L.s[1][r][c0], w);
 #pragma unroll
-        for (int b = 0; b < 14; ++b) v[b] = v[b] * w[b];
+        for (int b = 0; b < 18; ++b) v[b] = v[b] * w[b];
     }
-    *reinterpret_cast<float4 *>(&L.h[r][c0]) = win4(v, win);
+    float o[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], v[b + h], a);
+        o[h] = a;
+    }
+    *reinterpret_cast<float4 *>(&L.h[r][c0]) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4 *>(&L.h[r][c0 + 4]) = make_float4(o[4], o[5], o[6], o[7]);
 }
 
-// Column task u: statistics column u % 58, rows i0 .. i0 + 3, i0 = 4 (u / 58) (38 for the last
-// group, which keeps rows 40, 41 only).
+// Column task u: statistics column u % 58, rows 6 (u / 58) .. + 5.
 __device__ __forceinline__ void ssim_col_task(int u, int &jj, int &i0) {
     const int g = u / kMC;
     jj = u - g * kMC;
-    i0 = g < kColGroups - 1 ? 4 * g : kMR - 4;
+    i0 = kColRows * g;
 }
 
-// The 11-tap window down a column of an LDS map (row stride P) from its first row: four vertically
+// The 11-tap window down a column of an LDS map (row stride P) from its first row: N vertically
 // adjacent outputs.
-template <int P>
-__device__ __forceinline__ void ssim_col4(const float *col, const SsimWin &win, float (&o)[4]) {
-    float hv[14];
+template <int P, int N>
+__device__ __forceinline__ void ssim_col(const float *col, const SsimWin &win, float (&o)[N]) {
+    float hv[N + 10];
 #pragma unroll
-    for (int a = 0; a < 14; ++a) hv[a] = col[a * P];
+    for (int a = 0; a < N + 10; ++a) hv[a] = col[a * P];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < N; ++q) {
         float a = 0.f;
 #pragma unroll
         for (int b = 0; b < 11; ++b) a = fmaf(win.g[b], hv[b + q], a);
@@ -285,20 +306,14 @@ __device__ __forceinline__ void ssim_col4(const float *col, const SsimWin &win, 
     }
 }
 
-constexpr int kColRounds = rounds(kColTasks);               // 2
-
-// One statistics map: its row pass into h, then the column pass of this thread's column tasks.
+// One statistics map: its row pass into h, then the column pass of this thread's column task.
 template <int MAP>
-__device__ __forceinline__ void ssim_loss_map(SsimLossLds &L, const SsimWin &win, const int (&jj)[kColRounds],
-                                              const int (&i0)[kColRounds], float (&m)[kColRounds][4]) {
+__device__ __forceinline__ void ssim_loss_map(SsimLossLds &L, const SsimWin &win, bool coltask, int jj, int i0,
+                                              float (&m)[kColRows]) {
     const int tid = threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < rounds(kRowTasks); ++k)
-        if (tid + kLossNT * k < kRowTasks) ssim_loss_rows<MAP>(L, tid + kLossNT * k, win);
+    if (tid < kRowTasks) ssim_loss_rows<MAP>(L, tid, win);
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kColRounds; ++u)
-        if (tid + kLossNT * u < kColTasks) ssim_col4<kHP>(&L.h[i0[u]][jj[u]], win, m[u]);
+    if (coltask) ssim_col<kHP, kColRows>(&L.h[i0][jj], win, m);
     __syncthreads();                                        // h is rewritten next
 }
 
@@ -320,41 +335,38 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
     // (needed later; pixel 0 of the plane stands in outside the image, where they are not used)
     float4 vx[kStageRounds], vy[kStageRounds];
     ssim_stage_load<VEC>(x + ch * plane, y + ch * plane, W, H, x0, y0, vx, vy);
-    int jj[kColRounds], i0[kColRounds];
-    float2 tq[kColRounds][4];
+    // this thread's column task: statistics column jj, rows i0 .. i0 + 5
+    const bool coltask = tid < kColTasks;
+    int jj, i0;
+    ssim_col_task(tid, jj, i0);
+    const int px = x0 - kSsimR + jj;
+    float2 tq[kColRows];
 #pragma unroll
-    for (int u = 0; u < kColRounds; ++u) {
-        ssim_col_task(tid + kLossNT * u, jj[u], i0[u]);
-        const int px = x0 - kSsimR + jj[u];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int py = y0 - kSsimR + i0[u] + q;
-            const bool ok = tid + kLossNT * u < kColTasks && px >= 0 && px < W && py >= 0 && py < H;
-            tq[u][q] = T[ch * plane + (ok ? (size_t)py * W + px : 0)];
-        }
+    for (int q = 0; q < kColRows; ++q) {
+        const int py = y0 - kSsimR + i0 + q;
+        const bool ok = coltask && px >= 0 && px < W && py >= 0 && py < H;
+        tq[q] = T[ch * plane + (ok ? (size_t)py * W + px : 0)];
     }
     ssim_stage_store(vx, vy, L.s);
     __syncthreads();
-    // the statistics: mx, Exx, Exy at the column tasks' pixels
-    float mx[kColRounds][4], exx[kColRounds][4], exy[kColRounds][4];
-    ssim_loss_map<0>(L, win, jj, i0, mx);
-    ssim_loss_map<1>(L, win, jj, i0, exx);
-    ssim_loss_map<2>(L, win, jj, i0, exy);
+    // the statistics: mx, Exx, Exy at the column task's pixels
+    float mx[kColRows], exx[kColRows], exy[kColRows];
+    ssim_loss_map<0>(L, win, coltask, jj, i0, mx);
+    ssim_loss_map<1>(L, win, coltask, jj, i0, exx);
+    ssim_loss_map<2>(L, win, coltask, jj, i0, exy);
     // the map and D0..D2 there (zero outside the image)
-    float f = 0.f, D[3][kColRounds][4];
+    float f = 0.f, D[3][kColRows];
+    {
+        const bool colin = coltask && px >= 0 && px < W;
+        const bool colown = jj >= kSsimR && jj < kSsimR + kTW;
 #pragma unroll
-    for (int u = 0; u < kColRounds; ++u) {
-        const int px = x0 - kSsimR + jj[u];
-        const bool colin = tid + kLossNT * u < kColTasks && px >= 0 && px < W;
-        const bool colown = jj[u] >= kSsimR && jj[u] < kSsimR + kTW;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = i0[u] + q, py = y0 - kSsimR + i;
-            D[0][u][q] = D[1][u][q] = D[2][u][q] = 0.f;
+        for (int q = 0; q < kColRows; ++q) {
+            const int i = i0 + q, py = y0 - kSsimR + i;
+            D[0][q] = D[1][q] = D[2][q] = 0.f;
             if (colin && py >= 0 && py < H) {
-                const float a = mx[u][q], my = tq[u][q].x, eyy = tq[u][q].y;
+                const float a = mx[q], my = tq[q].x, eyy = tq[q].y;
                 const float xx = a * a, yy = my * my;
-                const float sxx = exx[u][q] - xx, syy = eyy - yy, sxy = exy[u][q] - a * my;
+                const float sxx = exx[q] - xx, syy = eyy - yy, sxy = exy[q] - a * my;
                 const float n1 = fmaf(2.0f * a, my, kC1), n2 = fmaf(2.0f, sxy, kC2);
                 const float d1 = (xx + yy) + kC1, d2 = (sxx + syy) + kC2;
                 // one hardware reciprocal (1 ulp) of d1 d2 (>= C1 C2) serves every quotient:
@@ -362,11 +374,10 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
                 //   dSSIM/dExx = -SSIM d1 r,  dSSIM/dExy = 2 n1 r,  r = 1 / (d1 d2)
                 const float r = __builtin_amdgcn_rcpf(d1 * d2);
                 const float fr = (n1 * n2) * r;
-                // the tile's own pixels (rows 38, 39 of the last group are the previous group's)
-                if (colown && i >= kSsimR && i < kSsimR + kTH) f += fr;
-                D[0][u][q] = (2.0f * r) * fmaf(a * fr, d1 - d2, my * (n2 - n1));
-                D[1][u][q] = -(fr * d1) * r;
-                D[2][u][q] = (2.0f * n1) * r;
+                if (colown && i >= kSsimR && i < kSsimR + kTH) f += fr;   // the tile's own pixels
+                D[0][q] = (2.0f * r) * fmaf(a * fr, d1 - d2, my * (n2 - n1));
+                D[1][q] = -(fr * d1) * r;
+                D[2][q] = (2.0f * n1) * r;
             }
         }
     }
@@ -410,12 +421,9 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
     float ss[3][4];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
+        if (coltask) {
 #pragma unroll
-        for (int u = 0; u < kColRounds; ++u) {
-            if (tid + kLossNT * u >= kColTasks) continue;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (!(i0[u] == kMR - 4 && q < 2)) L.d[i0[u] + q][jj[u]] = D[k][u][q];
+            for (int q = 0; q < kColRows; ++q) L.d[i0 + q][jj] = D[k][q];
         }
         __syncthreads();
         if (k == 0 && loss && tid < 3) {
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kLossNT) __attribute__((amdgpu_waves_per_eu(6))) vo
             }
         }
         __syncthreads();
-        if (outtask) ssim_col4<kBP>(&L.hb[ty0][tx], win, ss[k]);
+        if (outtask) ssim_col<kBP, 4>(&L.hb[ty0][tx], win, ss[k]);
         if (k == 0 && loss && tid < 64) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(0);                  // the partials' stores have completed
