@@ -222,12 +222,14 @@ __device__ __forceinline__ uint2 bucket_tile_list(const BucketList &B, int t, ui
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint64_t below = lanes_below();
     uint2 *ranges = reinterpret_cast<uint2 *>(B.ranges);
-    if (*B.m_eff == 0u) {                                 // nothing binned (or overflow): uniform
+    // the bucket's bounds (always in bounds to read) load together with M: the test below uses both,
+    // so the chain of dependent loads is tile -> (M, bounds) -> entries
+    const uint32_t b = (uint32_t)t >> B.lo_bits, tt = (uint32_t)t;
+    const uint32_t s0 = B.bstart[b], s1 = B.bstart[b + 1];
+    if (*B.m_eff == 0u || s1 < s0) {                      // nothing binned (or overflow): uniform
         if (tid == 0) ranges[t] = make_uint2(0u, 0u);
         return make_uint2(0u, 0u);
     }
-    const uint32_t b = (uint32_t)t >> B.lo_bits, tt = (uint32_t)t;
-    const uint32_t s0 = B.bstart[b], s1 = B.bstart[b + 1];
     constexpr uint32_t CH = 256u * kBucketPL;
     const bool one = s1 - s0 <= CH;                       // uniform: keep the chunk in registers
     uint32_t k[kBucketPL], v[kBucketPL];
