@@ -156,14 +156,18 @@ struct SegLds {
 
 // Pair `idx` (< excl[ns]) of a segment of ns Gaussians: its tile id and the
 // segment-local index of its Gaussian (the last l with excl[l] <= idx, which
-// never names a Gaussian without tiles).
+// never names a Gaussian without tiles).  The search has no branch: a probe
+// past the segment reads excl[ns] (> idx), so several searches of one thread
+// interleave their LDS reads.
 template <int S>
 __device__ __forceinline__ void regen_pair(const SegLds<S> &G, int ns, uint32_t idx, int tiles_x, uint32_t &key,
                                            int &lo) {
     int l = 0;
 #pragma unroll
-    for (int step = S >> 1; step > 0; step >>= 1)
-        if (l + step < ns && G.excl[l + step] <= idx) l += step;
+    for (int step = S >> 1; step > 0; step >>= 1) {
+        const int c = l + step;
+        l = G.excl[c < ns ? c : ns] <= idx ? c : l;
+    }
     const uint32_t r = idx - G.excl[l];
     const uint2 bx = G.box[l];
     const uint32_t tx0 = (bx.x & 0xffffu) >> 4, ty0 = (bx.x >> 16) >> 4;
@@ -710,14 +714,14 @@ __device__ __forceinline__ void wide_chunk_keys(WideLds<NT> &L, int ns, int firs
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int radix = 1 << bits, iters = span >> 6;
     const uint32_t dmask = (uint32_t)(radix - 1);
+    // every slot's search runs (slots past the span repeat the last key; they are not ranked), so the
+    // searches' LDS reads overlap instead of waiting on a branch per slot
 #pragma unroll
     for (int it = 0; it < kWPL; ++it) {
-        if (it < iters) {                                 // uniform
-            const int idx = wave * span + it * 64 + lane;
-            int lo;
-            regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
-            val[it] = (uint32_t)(first + lo);
-        }
+        const int idx = wave * span + it * 64 + lane;
+        int lo;
+        regen_pair<kBT>(L.G, ns, cs + (uint32_t)(idx < cc ? idx : cc - 1), tiles_x, key[it], lo);
+        val[it] = (uint32_t)(first + lo);
     }
     for (int d = lane; d < radix; d += 64) L.cnt[wave][d] = 0u;
     const uint64_t below = lanes_below();
@@ -810,34 +814,61 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
     int cc = (int)min((uint32_t)CH, tot);
     int span = ((cc + NT - 1) / NT) * 64;                 // keys per wave: a multiple of 64, NW * span >= cc
     if (tot > 0u) wide_chunk_keys<NT>(L, ns, first, 0u, cc, span, tiles_x, shift, bits, key, val, rk);
-    // the group sums (before this group, all) and the table's digit partials, reduced per wave
-    unsigned long long before = 0, all = 0;
+    // the group sums (before this group, all) and the table's digit partials, reduced per wave.  Each
+    // sum is split into its low 16 bits and the rest (capped at 2^20: a larger group sum overflows
+    // any pair buffer, and the capped total still does); over at most 2048 groups both parts stay
+    // within 32 bits, so four DPP wave sums replace 64-bit shuffles.
+    const int g = (int)blockIdx.x;
+    uint32_t blo = 0, bhi = 0, alo = 0, ahi = 0;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
         const int i = tid + k * NT;
         const unsigned long long x = i < ngroups ? v[k] : 0ull;
-        all += x;
-        before += i < (int)blockIdx.x ? x : 0ull;
+        const uint32_t lo = (uint32_t)x & 0xffffu;
+        const uint32_t hi = (uint32_t)min(x >> 16, 1ull << 20);
+        alo += lo;
+        ahi += hi;
+        blo += i < g ? lo : 0u;
+        bhi += i < g ? hi : 0u;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        before += __shfl_xor(before, o, 64);
-        all += __shfl_xor(all, o, 64);
-    }
+    blo = wave_scan_incl(blo);
+    bhi = wave_scan_incl(bhi);
+    alo = wave_scan_incl(alo);
+    ahi = wave_scan_incl(ahi);
     if (lane == 63) {
-        L.sm64[wave] = before;
-        L.sm64[NW + wave] = all;
+        L.sm64[wave] = ((unsigned long long)bhi << 16) + blo;
+        L.sm64[NW + wave] = ((unsigned long long)ahi << 16) + alo;
     }
     const int Q = radix >> 2;                             // digit quads (redundant tables: radix >= 4)
     if (table_redundant) {                                // uniform
+        // load k of this wave covers columns [cw0, cw1] + k cstep (cw1 - cw0 < cstep): rounds within
+        // the table and before this group are added whole (wave-uniform tests); the columns before
+        // this group are a prefix of the rounds, so their sum is the running total taken once, at
+        // the first round that reaches the group, plus that round's lanes before it
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int cw0 = (wv * 64) >> lq, cw1 = (wv * 64 + 63) >> lq;
         uint4 fb = make_uint4(0u, 0u, 0u, 0u), ft = fb;
+        bool taken = false;                               // wave-uniform: fb is final
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
-            const int col = cfirst + k * cstep;
-            if (col >= ncols_cap) continue;
-            ft.x += tv[k].x; ft.y += tv[k].y; ft.z += tv[k].z; ft.w += tv[k].w;
-            if (col < (int)blockIdx.x) { fb.x += tv[k].x; fb.y += tv[k].y; fb.z += tv[k].z; fb.w += tv[k].w; }
+            const int a0 = cw0 + k * cstep, a1 = cw1 + k * cstep, col = cfirst + k * cstep;
+            if (a0 >= ncols_cap) break;                   // uniform
+            uint4 x = tv[k];
+            if (a1 >= ncols_cap) {                        // uniform: the round that crosses the table's end
+                const bool in = col < ncols_cap;
+                x.x = in ? x.x : 0u; x.y = in ? x.y : 0u; x.z = in ? x.z : 0u; x.w = in ? x.w : 0u;
+            }
+            if (!taken && a1 >= g) {                      // uniform: the first round that reaches this group
+                fb = ft;
+                if (a0 < g) {
+                    const bool bf = col < g;
+                    fb.x += bf ? x.x : 0u; fb.y += bf ? x.y : 0u; fb.z += bf ? x.z : 0u; fb.w += bf ? x.w : 0u;
+                }
+                taken = true;
+            }
+            ft.x += x.x; ft.y += x.y; ft.z += x.z; ft.w += x.w;
         }
+        if (!taken) fb = ft;                              // every column of the wave is before this group
         // lanes with equal lane mod Q hold the same digits
         for (int o = Q; o < 64; o <<= 1) {
             fb.x += __shfl_xor(fb.x, o, 64); fb.y += __shfl_xor(fb.y, o, 64);
