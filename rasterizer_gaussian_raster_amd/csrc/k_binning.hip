@@ -686,8 +686,9 @@ __global__ __launch_bounds__(kBT) void k_scatter0(int n, int tiles_x, int shift,
 // flight; then each block forms its Gaussians' emission offsets, writes
 // offsets[], and workgroup 0 publishes M and the bucket starts.  Each key is
 // stored straight from its register: position = the block's next slot of the
-// digit + the chunk's keys of the digit in earlier waves + its rank among its
-// wave's keys of the digit (ballots, in key order), so the pass is stable.
+// digit + the chunk's keys of the digit in earlier waves (those two summed once
+// per wave and digit) + its rank among its wave's keys of the digit (ballots,
+// in key order), so the pass is stable.
 // (1024 threads per group measured slower: one such block per CU leaves a tail
 // once the groups outnumber the CUs.)
 constexpr int kWPL = 4;                        // keys per lane per chunk (at most)
@@ -697,8 +698,9 @@ template <int NT>
 struct WideLds {
     static constexpr int NW = NT / 64;
     SegLds<kBT> G;                             // the group's emission scan and boxes
-    uint32_t cnt[NW][256];                     // per wave and digit: the chunk's keys of the digit in the wave
-    uint32_t gbase[256];                       // output position of the block's next key of each digit
+    uint32_t cnt[NW][256];                     // per wave and digit: the chunk's keys of the digit in the wave,
+                                               // then the wave's first output slot of the digit
+    uint32_t gbase[256];                       // the block's first output slot of each digit
     uint4 fb[NW][64], ft[NW][64];              // per wave: digit-quad sums of the table (before, all)
     unsigned long long sm64[2 * NW];           // per wave: group sums before this group, all
     uint32_t sm32[NW];                         // per wave: its Gaussians' tile counts
@@ -740,6 +742,22 @@ __device__ __forceinline__ void wide_chunk_keys(WideLds<NT> &L, int ns, int firs
         const uint32_t before_w = valid ? L.cnt[wave][d] : 0u;
         rk[it] = before_w + (uint32_t)__popcll(peers & below);
         if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before_w + (uint32_t)__popcll(peers);
+    }
+}
+
+// Thread d < radix: each wave's key count of digit d in the chunk (L.cnt[w][d]) replaced by that
+// wave's first slot of the digit, from nb (the block's next slot of d), which moves past the chunk.
+template <int NT>
+__device__ __forceinline__ void wave_starts(WideLds<NT> &L, uint32_t &nb) {
+    constexpr int NW = NT / 64;
+    const int d = threadIdx.x;
+    uint32_t c[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c[w] = L.cnt[w][d];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        L.cnt[w][d] = nb;
+        nb += c[w];
     }
 }
 
@@ -892,7 +910,9 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
     if (blockIdx.x == 0 && tid == 0) publish_total(ta, capacity, n, hdr, offsets, d_num, d_max);
     const uint32_t M = ta <= (unsigned long long)capacity ? (uint32_t)ta : 0u;   // else nothing is emitted
     if (M == 0u) return;                                  // overflow or no pair: uniform
-    // digit bases: gbase[d] = (keys of smaller digits, all groups) + (keys of d in earlier groups)
+    // digit bases: gbase[d] = (keys of smaller digits, all groups) + (keys of d in earlier groups);
+    // nb: (thread d < radix) the block's next slot of digit d
+    uint32_t nb = 0u;
     if (table_redundant) {                                // uniform
         uint32_t sb = 0, st = 0;
         if (tid < radix) {
@@ -911,12 +931,16 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
             uint32_t dbase = 0;
 #pragma unroll
             for (int w = 0; w < 4; ++w) dbase += w < wave ? L.dsum[w] : 0u;
-            L.gbase[tid] = dbase + dinc - st + sb;
+            nb = dbase + dinc - st + sb;
         }
     } else {
-        if (tid < radix) L.gbase[tid] = tx;               // the scanned table holds the bases
+        nb = tx;                                          // the scanned table holds the bases
     }
-    __syncthreads();                                      // 5: gbase
+    if (tid < radix) {
+        L.gbase[tid] = nb;
+        wave_starts<NT>(L, nb);
+    }
+    __syncthreads();                                      // 5: gbase and the waves' first slots
     if (blockIdx.x == 0) {
         if (tid < radix) bucket_start[tid] = L.gbase[tid];
         if (tid == 0) bucket_start[radix] = M;
@@ -927,15 +951,14 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
     }
     for (uint32_t cs = 0; cs < tot;) {                    // the chunk's keys are ranked and the counts published
         const int iters = span >> 6;
-        // position = the block's next slot of the digit + its keys in earlier waves + the rank
+        // position = the wave's first slot of the digit + the rank
 #pragma unroll
         for (int it = 0; it < kWPL; ++it) {
             if (it >= iters) continue;                    // uniform
             const int idx = wave * span + it * 64 + lane;
             if (idx < cc) {
                 const uint32_t d = (key[it] >> shift) & dmask;
-                uint32_t pos = L.gbase[d] + rk[it];
-                for (int w = 0; w < wave; ++w) pos += L.cnt[w][d];
+                const uint32_t pos = L.cnt[wave][d] + rk[it];
                 if (pos < M) {                            // holds by construction; keeps a bad table in bounds
                     kout[pos] = key[it];
                     vout[pos] = val[it];
@@ -944,18 +967,13 @@ __global__ __launch_bounds__(NT, 2048 / NT) void k_scatter0w(int n, int tiles_x,
         }
         cs += (uint32_t)CH;
         if (cs >= tot) break;                             // uniform: the last chunk
-        __syncthreads();                                  // every wave has its positions
-        if (tid < radix) {
-            uint32_t t = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) t += L.cnt[w][tid];
-            L.gbase[tid] += t;
-        }
-        __syncthreads();                                  // the counts are read: the next chunk rewrites them
+        __syncthreads();                                  // every wave has its positions: the rows are free
         cc = (int)min((uint32_t)CH, tot - cs);
         span = ((cc + NT - 1) / NT) * 64;
         wide_chunk_keys<NT>(L, ns, first, cs, cc, span, tiles_x, shift, bits, key, val, rk);
         __syncthreads();                                  // the waves' counts
+        if (tid < radix) wave_starts<NT>(L, nb);
+        __syncthreads();                                  // the waves' first slots
     }
 }
 
