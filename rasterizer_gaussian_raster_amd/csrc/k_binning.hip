@@ -178,6 +178,22 @@ __device__ __forceinline__ void regen_pair(const SegLds<S> &G, int ns, uint32_t 
     lo = l;
 }
 
+// The lanes among `peers` whose digit equals this lane's d (digits of at most 8 bits: a bit above
+// the digit's width is clear in every lane and leaves the set as it is).  Per bit: its ballot m,
+// kept where this lane's bit is set and inverted where it is clear (~(m ^ spread bit)), in
+// straight-line code.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t peers) {
+    uint32_t lo = (uint32_t)peers, hi = (uint32_t)(peers >> 32);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint32_t sp = (uint32_t)((int32_t)(d << (31 - b)) >> 31);   // bit b spread over the word
+        const uint64_t m = __ballot(sp != 0u);
+        lo &= ~((uint32_t)m ^ sp);                        // lanes whose bit equals this lane's
+        hi &= ~((uint32_t)(m >> 32) ^ sp);
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // ---------------------------------------------------------------------------
 // digit bases of one sort block
 // ---------------------------------------------------------------------------
@@ -340,12 +356,7 @@ __device__ __forceinline__ void scatter_chunk(ChunkLds<PL> &L, int cc, int span,
         const int idx = wave * span + it * 64 + lane;
         const bool valid = idx < cc;
         const uint32_t d = (key[it] >> shift) & dmask;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < bits; ++b) {
-            const bool on = (d >> b) & 1u;
-            const uint64_t m = __ballot(on);
-            peers &= on ? m : ~m;
-        }
+        const uint64_t peers = match_digit(d, __ballot(valid));
         const uint32_t before = valid ? L.cnt[wave][d] : 0u;
         rk[it] = before + (uint32_t)__popcll(peers & below);
         if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before + (uint32_t)__popcll(peers);
@@ -473,19 +484,49 @@ __global__ __launch_bounds__(1024) void k_group_scan(int ngroups, int n, long lo
                                                      BinHeader *__restrict__ hdr, uint32_t *__restrict__ offsets,
                                                      uint32_t *__restrict__ d_num, uint32_t *__restrict__ d_max) {
     __shared__ unsigned long long sm[16];
+    constexpr int U = 8;                                  // sums held in registers (ngroups <= 8192: one round)
     const int per = (ngroups + 1023) / 1024;
     const int beg = threadIdx.x * per;
     unsigned long long s = 0;
-    for (int i = 0; i < per; ++i)
-        if (beg + i < ngroups) s += part[beg + i];
+    unsigned long long v[U];
+    // rounds of U loads issued together (a load per loop trip would wait for each in turn)
+    for (int i0 = 0; i0 < per; i0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = beg + i0 + u;
+            v[u] = (i0 + u < per && i < ngroups) ? part[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) s += v[u];
+    }
     unsigned long long tot;
     unsigned long long run = block_exclusive_scan<unsigned long long, 1024>(s, sm, &tot);
-    for (int i = 0; i < per; ++i)
-        if (beg + i < ngroups) {
-            const unsigned long long v = part[beg + i];
-            part[beg + i] = run;
-            run += v;
+    if (per <= U) {                                       // uniform: the sums are still in v
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = beg + u;
+            if (u < per && i < ngroups) {
+                part[i] = run;
+                run += v[u];
+            }
         }
+    } else {
+        for (int i0 = 0; i0 < per; i0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = beg + i0 + u;
+                v[u] = (i0 + u < per && i < ngroups) ? part[i] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = beg + i0 + u;
+                if (i0 + u < per && i < ngroups) {
+                    part[i] = run;
+                    run += v[u];
+                }
+            }
+        }
+    }
     if (threadIdx.x == 0) publish_total(tot, capacity, n, hdr, offsets, d_num, d_max);
 }
 
@@ -733,12 +774,7 @@ __device__ __forceinline__ void wide_chunk_keys(WideLds<NT> &L, int ns, int firs
         const int idx = wave * span + it * 64 + lane;
         const bool valid = idx < cc;
         const uint32_t d = (key[it] >> shift) & dmask;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < bits; ++b) {
-            const bool on = (d >> b) & 1u;
-            const uint64_t m = __ballot(on);
-            peers &= on ? m : ~m;
-        }
+        const uint64_t peers = match_digit(d, __ballot(valid));
         const uint32_t before_w = valid ? L.cnt[wave][d] : 0u;
         rk[it] = before_w + (uint32_t)__popcll(peers & below);
         if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before_w + (uint32_t)__popcll(peers);
@@ -1012,12 +1048,7 @@ __device__ __forceinline__ void bucketw_rank(BucketWLds &L, int cc, int span, in
         const int idx = wave * span + it * 64 + lane;
         const bool valid = idx < cc;
         const uint32_t d = key[it] & dmask;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < lo_bits; ++b) {
-            const bool on = (d >> b) & 1u;
-            const uint64_t m = __ballot(on);
-            peers &= on ? m : ~m;
-        }
+        const uint64_t peers = match_digit(d, __ballot(valid));
         const uint32_t before = valid ? L.cnt[wave][d] : 0u;
         rk[it] = before + (uint32_t)__popcll(peers & below);
         if (valid && (peers >> lane) == 1ull) L.cnt[wave][d] = before + (uint32_t)__popcll(peers);
@@ -1307,7 +1338,9 @@ __global__ __launch_bounds__(kBT) void k_bucket_sort(const uint32_t *__restrict_
 
 // ---------------------------------------------------------------------------
 // exclusive scan of a u32 array in place (large digit tables): one workgroup
-// when it is short, otherwise reduce -> scan of block sums -> rescan.
+// when it is short, otherwise block totals -> rescan, each rescan block adding
+// up the totals before it (a scan of the totals in between only past
+// kScanDownSums blocks).
 // count <= 1024 * kScanSingleItems for the single form.  Element r * 1024 + i
 // lives in thread i's register v[r] (coalesced loads, all issued together).
 // ---------------------------------------------------------------------------
@@ -1367,10 +1400,24 @@ __global__ __launch_bounds__(256) void k_scan_reduce(const uint32_t *__restrict_
     if (threadIdx.x == 0) sums[blockIdx.x] = tot;
 }
 
+// RAW: sums[] holds the raw block totals of k_scan_reduce and each block adds up those before it
+// itself (at most kScanDownSums of them; no scan of the totals runs in between); else sums[] is
+// their exclusive scan.
+constexpr int kScanDownSums = 4 * 256;
+template <bool RAW>
 __global__ __launch_bounds__(256) void k_scan_down(uint32_t *__restrict__ a, int count,
                                                    const uint32_t *__restrict__ sums) {
-    __shared__ uint32_t sm[4];
+    __shared__ uint32_t sm[4], pre[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int beg = blockIdx.x * kScanChunk + threadIdx.x * kScanItems;
+    uint32_t b = 0;                                       // RAW: totals of the blocks before this one
+    if (RAW) {
+#pragma unroll
+        for (int k = 0; k < kScanDownSums / 256; ++k) {
+            const int j = threadIdx.x + k * 256;
+            b += j < (int)blockIdx.x ? sums[j] : 0u;
+        }
+    }
     uint32_t v[kScanItems];
     uint32_t s = 0;
 #pragma unroll
@@ -1378,8 +1425,18 @@ __global__ __launch_bounds__(256) void k_scan_down(uint32_t *__restrict__ a, int
         v[i] = (beg + i < count) ? a[beg + i] : 0u;
         s += v[i];
     }
-    uint32_t tot;
-    uint32_t run = block_exclusive_scan<uint32_t, 256>(s, sm, &tot) + sums[blockIdx.x];
+    // one barrier: the wave totals of s (for the scan) and of b (for the block's base)
+    const uint32_t sinc = wave_scan_incl(s);
+    const uint32_t binc = RAW ? wave_scan_incl(b) : 0u;
+    if (lane == 63) {
+        sm[wave] = sinc;
+        pre[wave] = binc;
+    }
+    __syncthreads();
+    uint32_t run = sinc - s;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) run += (w < wave ? sm[w] : 0u) + (RAW ? pre[w] : 0u);
+    if (!RAW) run += sums[blockIdx.x];
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i)
         if (beg + i < count) {
@@ -1395,8 +1452,12 @@ static hipError_t scan_u32(uint32_t *a, int count, uint32_t *sums, hipStream_t s
     }
     const int nb = (count + kScanChunk - 1) / kScanChunk;
     k_scan_reduce<<<nb, 256, 0, s>>>(a, count, sums);
-    k_scan_single<<<1, 1024, 0, s>>>(sums, nb);
-    k_scan_down<<<nb, 256, 0, s>>>(a, count, sums);
+    if (nb > kScanDownSums) {                             // (beyond 4M entries) scan the block totals first
+        k_scan_single<<<1, 1024, 0, s>>>(sums, nb);
+        k_scan_down<false><<<nb, 256, 0, s>>>(a, count, sums);
+        return hipGetLastError();
+    }
+    k_scan_down<true><<<nb, 256, 0, s>>>(a, count, sums);
     return hipGetLastError();
 }
 
