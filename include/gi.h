@@ -451,8 +451,8 @@ gi_status gi_adam_step_pairs(const gi_desc *desc, int64_t n, const uint32_t *off
  *             read after many asynchronous steps tells whether any of their
  *             binnings overflowed (M > capacity renders nothing and gives a
  *             zero gradient for that step).
- *   When each first-pass bucket holds at most 16 tiles (up to 2^21 pairs of
- *   capacity and a low digit of <= 4 bits, e.g. 768x512), the raster's
+ *   When each first-pass bucket holds at most 16 tiles (plans whose low digit
+ *   has at most 4 bits, e.g. 768x512), the raster's
  *   workgroups finish the sort themselves -- each reads its tile's bucket and
  *   picks its entries out in bucket order, writing keys, vals and the range
  *   exactly where the bucket pass would -- and that pass is not launched.
