@@ -50,17 +50,11 @@ def test_bin_workloads_full(name):
     _check_bin(wl.width, wl.height, w["params"])
 
 
-@pytest.mark.parametrize("name", ["alpha_2048x2048_500k", "render_3840x2160_2m"])
-def test_bin_large_workloads(name):
-    """Full-size binning checked by its defining properties; a 5% subset checked bit-exactly."""
-    require_gpu()
+def _check_bin_properties(W, H, p, lg, got):
+    """A binning checked by its defining properties against the oracle's footprint: counts, M, offsets
+    (the exclusive scan of the counts), keys/vals (every (tile, index) pair of the boxes exactly once,
+    sorted by tile and stably by index) and the tile ranges."""
     import oracle
-    w = synth.make_workload(name)
-    wl = w["workload"]
-    W, H = wl.width, wl.height
-    p = w["params"]
-    lg = w["logit"]
-    r, got = gpu_bin(W, H, p, lg)
     box, cnt = oracle.footprint(W, H, p.astype(np.float64), None if lg is None else lg.astype(np.float64))
     np.testing.assert_array_equal(got["counts"], cnt)
     assert got["M"] == int(cnt.astype(np.int64).sum())
@@ -89,10 +83,33 @@ def test_bin_large_workloads(name):
     hi = np.searchsorted(keys, np.arange(T), "right")
     np.testing.assert_array_equal(rg[:, 0], np.where(hi > lo, lo, 0))
     np.testing.assert_array_equal(rg[:, 1], np.where(hi > lo, hi, 0))
+
+
+@pytest.mark.parametrize("name", ["alpha_2048x2048_500k", "render_3840x2160_2m"])
+def test_bin_large_workloads(name):
+    """Full-size binning checked by its defining properties; a 5% subset checked bit-exactly."""
+    require_gpu()
+    w = synth.make_workload(name)
+    wl = w["workload"]
+    W, H = wl.width, wl.height
+    p = w["params"]
+    lg = w["logit"]
+    r, got = gpu_bin(W, H, p, lg)
+    _check_bin_properties(W, H, p, lg, got)
     # bit-exact against the oracle's definition on a 5% subset
     sub = np.random.default_rng(7).choice(wl.n, size=wl.n // 20, replace=False)
     sub.sort()
     _check_bin(W, H, p[sub], None if lg is None else lg[sub])
+
+
+def test_bin_more_than_8192_groups():
+    """2,200,000 small Gaussians: more than 8192 groups of 256, so the single-workgroup scan of the
+    group sums takes more than one round of its register-held loads."""
+    require_gpu()
+    W, H, n = 512, 512, 2_200_000
+    p = synth.random_case(211, W, H, n, sigma=(0.3, 1.5), margin=4)
+    _, got = gpu_bin(W, H, p, None)
+    _check_bin_properties(W, H, p, None, got)
 
 
 @pytest.mark.parametrize("fused", [False, True])
